@@ -1,0 +1,209 @@
+"""Benchmark of the FlashIPA forward (lift + fused attention + epilogue) on one
+MI355X.
+
+Prints ONE JSON line.  A step is one forward of the whole path over one batch
+of synthetic, seeded inputs already resident in HBM.  The headline workload is
+the long-sequence case B=1, N=16384, H=8, D=Dv=16, P=4, Q=8, Cz=64, R=2,
+Cout=128, bf16 inputs (random-walk frames, 3.8 angstrom steps, all masks
+valid); the other sequence lengths of the sweep (and the short-chain batch at
+N=512) are reported under "sweep".
+
+value = effective TFLOP/s = 2 H (d_qk + d_v) sum_b L_b^2 / time per forward,
+with d_qk = D + 3P + 2 + R Cz and d_v = Dv + 3Q + R Cz (the lifted inner
+product and value widths of the method; padding and split columns are not
+counted).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "IPA fwd ms/call + effective TFLOP/s (% MFMA peak) at N=512..16384; peak mem"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_mfma_traffic.json")
+KERNEL_SOURCES = ("flash_mfma.hip", "mfma_tile.h", "common.h")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rna_structure_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def eff_flops(shape, mask) -> float:
+    L = mask.sum(axis=1).astype(float)
+    return 2.0 * shape.H * (shape.d_qk + shape.d_v) * float((L ** 2).sum())
+
+
+def make_workload(name):
+    from rna_structure_amd.synth import make_config
+    return make_config(name)
+
+
+def time_forward(inp, steps, warmup, per_kernel=True):
+    import torch
+    from rna_structure_amd import _lib
+    shape = inp["shape"]
+    t = _lib.device_inputs(inp, "cuda")
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base_mem = torch.cuda.memory_allocated()
+    f = _lib.FlashIPA(shape, eps=inp["eps"], with_pair_mask=t["pair_mask"] is not None)
+    for _ in range(warmup):
+        f.forward(t)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        f.forward(t)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    res = dict(ms=ms, peak_mem_mb=torch.cuda.max_memory_allocated() / 2**20,
+               work_mem_mb=(torch.cuda.max_memory_allocated() - base_mem) / 2**20)
+    if per_kernel:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for k in range(steps):
+            ev[k][0].record(st)
+            f.lift(t)
+            ev[k][1].record(st)
+            f.attend()
+            ev[k][2].record(st)
+            f.epilogue(t)
+            ev[k][3].record(st)
+        torch.cuda.synchronize()
+        res["lift_ms"] = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+        res["flash_ms"] = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+        res["epilogue_ms"] = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    del f, t
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(inp, flops, budget_s=12.0):
+    """Time the float64 oracle on a bounded sample of query rows and scale to
+    the whole forward (per-row cost is the same for every row at fixed N)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ipa_factored
+    shape = inp["shape"]
+    N = shape.N
+    rng = np.random.default_rng(0)
+    with threadpool_limits(limits=1):
+        rows = np.sort(rng.choice(N, size=4, replace=False))
+        t0 = time.perf_counter()
+        ipa_factored(inp, rows=rows, keep=("update", "local_points"))
+        per_row = (time.perf_counter() - t0) / (len(rows) * shape.B)
+        n = int(max(4, min(N, budget_s / max(per_row * shape.B, 1e-9))))
+        rows = np.sort(rng.choice(N, size=n, replace=False))
+        t0 = time.perf_counter()
+        ipa_factored(inp, rows=rows, keep=("update", "local_points"))
+        el = time.perf_counter() - t0
+    per_call_s = el * N / n
+    return dict(value=flops / per_call_s / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"{n} of {N} query rows x all {shape.B} samples, float64 NumPy oracle, "
+                       f"{el:.1f} s measured, scaled by N/rows to {per_call_s:.1f} s per forward",
+                seconds_per_call=per_call_s)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sweep_16384")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    inp = make_workload(args.workload)
+    shape = inp["shape"]
+    flops = eff_flops(shape, inp["mask"])
+    print(f"# workload {args.workload} {shape}", file=sys.stderr, flush=True)
+    r = time_forward(inp, args.steps, args.warmup)
+    value = flops / (r["ms"] * 1e-3) / 1e12
+    achieved = flops / (r["flash_ms"] * 1e-3) / 1e12
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == args.workload:
+            traffic = tr["fetch_bytes"] + tr["write_bytes"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"long-sequence IPA forward {args.workload}", "B": shape.B, "N": shape.N,
+                   "H": shape.H, "D": shape.D, "Dv": shape.Dv, "P": shape.P, "Q": shape.Q, "Cz": shape.Cz,
+                   "R": shape.R, "Cout": shape.Cout, "inputs": "bf16", "accumulate": "fp32"},
+        "kernels_ms": {"lift": round(r["lift_ms"], 4), "flash": round(r["flash_ms"], 4),
+                       "epilogue": round(r["epilogue_ms"], 4)},
+        "peak_mem_mb": round(r["peak_mem_mb"], 1),
+        "roofline": {"bound": "mfma", "kernel": "flash_mfma_kernel", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    print(json.dumps({"partial": out}), file=sys.stderr, flush=True)
+    if not args.no_sweep:
+        sweep = []
+        for name in ("short_batch", "sweep_4096", "sweep_8192", "sweep_16384", "sweep_32768"):
+            if name == args.workload:
+                rr, sh, fl = r, shape, flops
+            else:
+                w = make_workload(name)
+                sh = w["shape"]
+                fl = eff_flops(sh, w["mask"])
+                rr = time_forward(w, max(3, args.steps // 4), 2)
+            sweep.append({"workload": name, "B": sh.B, "N": sh.N, "H": sh.H, "ms": round(rr["ms"], 4),
+                          "eff_tflops": round(fl / (rr["ms"] * 1e-3) / 1e12, 2),
+                          "flash_ms": round(rr["flash_ms"], 4),
+                          "flash_frac_mfma": round(fl / (rr["flash_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "lift_ms": round(rr["lift_ms"], 4), "epilogue_ms": round(rr["epilogue_ms"], 4),
+                          "peak_mem_mb": round(rr["peak_mem_mb"], 1), "work_mem_mb": round(rr["work_mem_mb"], 1)})
+            print(f"# sweep {sweep[-1]}", file=sys.stderr, flush=True)
+        pts = [s for s in sweep if s["workload"].startswith("sweep_")]
+        if len(pts) >= 2:
+            import numpy as np
+            x = np.log([p["N"] for p in pts])
+            for key, name in (("ms", "time_exponent"), ("work_mem_mb", "mem_exponent")):
+                y = np.log([max(p[key], 1e-9) for p in pts])
+                out[name] = round(float(np.polyfit(x, y, 1)[0]), 3)
+        out["sweep"] = sweep
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, flops)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * flashipa.h -- C ABI of the MI355X (gfx950) FlashIPA forward library.
+ *
+ * The library computes the aggregation core of monomer-style Invariant Point
+ * Attention exactly as the "Invariant point attention (IPA)" problem page
+ * (biotorch) states it in "Required behavior", with the pair representation
+ * given as rank-R factors z_ij = sum_r zl_ir * zr_jr and a per-head pair bias
+ * sum_c w_pair[h,c] z_ij[c] (FlashIPA rebuttal, paperhub page, answers to Q4
+ * and Q5).  The whole logit -- scalar term, pair bias and the expanded squared
+ * point distance (FlashIPA verdict page, key_machinery) -- is evaluated as one
+ * inner product of lifted query and key rows inside a fused attention kernel,
+ * so no [B,H,N,N] logit, bias, attention or pair tensor ever exists in memory.
+ *
+ * Three calls make one forward:
+ *   ipa_lift      frames -> global points, point weight, lifted Q/K/V rows
+ *   ipa_flash_fwd fused masked online-softmax attention over lifted rows
+ *   ipa_epilogue  inverse frame transform, pair expansion, point lengths,
+ *                 head-major feature concat and the output projection
+ *
+ * Conventions shared by every call
+ *  - All device pointers refer to memory of the current HIP device; tensors
+ *    are dense, row-major (C order) with the layouts stated below.
+ *  - Floating inputs all have the dtype named in ipa_shape.dtype (IEEE fp32,
+ *    or bfloat16 stored as 16-bit words).  Masks are bytes (0 = invalid,
+ *    nonzero = valid).  Outputs are fp32.
+ *  - Every device pointer must be 16-byte aligned.
+ *  - Ownership: the caller allocates and frees every buffer.  The library
+ *    never allocates, frees, retains a pointer after returning, or
+ *    synchronises; all work is enqueued on `stream` (a hipStream_t, NULL for
+ *    the default stream) and completes in stream order.
+ *  - Errors: each call validates its arguments on the host and returns
+ *    IPA_OK or an ipa_status code without enqueuing anything; kernel launch
+ *    failures are reported as IPA_ERR_LAUNCH.  Finite inputs are a
+ *    precondition and are not checked.
+ */
+#ifndef FLASHIPA_H
+#define FLASHIPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IPA_OK = 0,
+  IPA_ERR_NULL = 1,        /* a required pointer is NULL */
+  IPA_ERR_SHAPE = 2,       /* a dimension is <= 0, or eps <= 0 */
+  IPA_ERR_UNSUPPORTED = 3, /* dims beyond the compiled kernel limits, or unknown dtype */
+  IPA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  IPA_ERR_LAUNCH = 5,      /* a kernel launch failed (hipGetLastError) */
+  IPA_ERR_DEVICE = 6       /* HIP runtime / device query failed */
+} ipa_status;
+
+typedef enum { IPA_F32 = 0, IPA_BF16 = 1 } ipa_dtype;
+
+/* Problem sizes, all positive (IPA page, "Required behavior").
+ *   B batch, N residues, H heads, D scalar q/k width, Dv scalar value width,
+ *   P query/key points per head, Q value points per head, Cz pair channels,
+ *   R factor rank, Cout output width.  F = H*(Dv+4Q+Cz).
+ * dtype: IPA_F32 runs the fp32 path (fp32 storage and fp32 arithmetic
+ * throughout); IPA_BF16 runs the matrix-core path (bf16/fp16 MFMA operands,
+ * fp32 accumulation, see ipa_flash_fwd).
+ * eps: added under the output point-length square root only. */
+typedef struct {
+  int64_t B, N, H, D, Dv, P, Q, Cz, R, Cout;
+  int32_t dtype;
+  float eps;
+} ipa_shape;
+
+/* Inputs of ipa_lift (IPA page, "Required behavior"; factors per the
+ * FlashIPA rebuttal, Q4/Q5).  Layouts:
+ *   q, k              [B,N,H,D]      projected scalar queries / keys
+ *   v                 [B,N,H,Dv]     projected scalar values
+ *   q_points,k_points [B,N,H,P,3]    LOCAL query / key points
+ *   v_points          [B,N,H,Q,3]    LOCAL value points
+ *   rotation          [B,N,3,3]      R_i, column-vector convention
+ *                                     T_i(x) = R_i @ x + t_i
+ *   translation       [B,N,3]        t_i
+ *   point_weight_raw  [H]            softplus is applied inside
+ *   w_pair            [H,Cz]         per-head pair-bias weights:
+ *                                     pair_bias_ijh = sum_c w_pair[h,c] z_ij[c]
+ *   zl, zr            [B,N,R,Cz]     pair factors, z_ij[c] = sum_r zl[i,r,c] zr[j,r,c]
+ *   mask              [B,N] bytes    residue mask
+ *   pair_mask         [B,N,N] bytes  or NULL (all valid); key j is permitted
+ *                                     for query i iff mask_i && mask_j && pair_mask_ij */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* q_points;
+  const void* k_points;
+  const void* v_points;
+  const void* rotation;
+  const void* translation;
+  const void* point_weight_raw;
+  const void* w_pair;
+  const void* zl;
+  const void* zr;
+  const uint8_t* mask;
+  const uint8_t* pair_mask;
+} ipa_lift_in;
+
+/* Inputs of ipa_epilogue besides the attention output.  Layouts:
+ *   zl [B,N,R,Cz], rotation [B,N,3,3], translation [B,N,3],
+ *   w_out [F,Cout] (update = features @ w_out + b_out), b_out [Cout]. */
+typedef struct {
+  const void* zl;
+  const void* rotation;
+  const void* translation;
+  const void* w_out;
+  const void* b_out;
+} ipa_epi_in;
+
+/* Size in bytes of the opaque "lifted" workspace that ipa_lift fills and
+ * ipa_flash_fwd reads (lifted query rows, key/value tiles, per-tile
+ * centroids, point weights, packed masks).  with_pair_mask != 0 reserves
+ * room for a bit-packed pair mask (B*N*ceil(N/64)*8 bytes, the only part
+ * that grows as N^2/8); pass 0 when ipa_lift will get pair_mask == NULL.
+ * Returns 0 for an invalid or unsupported shape. */
+size_t ipa_lifted_bytes(const ipa_shape* s, int with_pair_mask);
+
+/* Width of one (residue, head) row of the attention output O:
+ * Dv + R*Cz + 3*Q. */
+int64_t ipa_o_width(const ipa_shape* s);
+
+/* Kernel 1 (lift).  Applies the frames to every point (T_i(x) = R_i x + t_i),
+ * forms the per-head point weight gamma_h = 1/2 softplus(w_h) sqrt(2/(27P)),
+ * and writes the lifted rows whose inner products give
+ *   L_ijh = q.k/sqrt(3D) + pair_bias_ijh/sqrt(3) - gamma_h sum_p |T_i q_p - T_j k_p|^2
+ * (IPA page, "Required behavior"; lifting per the FlashIPA verdict page,
+ * key_machinery).  Distances are expanded about a per-key-tile centroid so
+ * that the expanded form keeps its accuracy for long chains.
+ * `lifted` (lifted_bytes bytes, at least ipa_lifted_bytes(s, pair_mask != NULL))
+ * is overwritten; IPA_ERR_SHAPE if it is too small. */
+ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, size_t lifted_bytes,
+                    void* stream);
+
+/* Kernel 2 (fused attention).  For every (b, h, i), masked stable softmax
+ * over the permitted keys j of L_ijh (IPA page: key j permitted iff
+ * mask_i && mask_j && pair_mask_ij; an empty neighbourhood gives an all-zero
+ * attention row) followed by the aggregations, written per (b, i, h) as
+ *   o[b,i,h, 0:Dv]              sum_j a_hij v_jh
+ *   o[b,i,h, Dv:Dv+R*Cz]        sum_j a_hij zr_j          (layout [R,Cz])
+ *   o[b,i,h, Dv+R*Cz: +3Q]      sum_j a_hij T_j(v_points_jhq)   (global, [Q,3])
+ * o is [B,N,H,ipa_o_width(s)] fp32; rows with an empty neighbourhood are 0.
+ * lse [B,H,N] fp32 receives log sum_j exp(L_ijh) over permitted keys
+ * (natural log; -inf for an empty neighbourhood), so that the attention row
+ * is a_hij = exp(L_ijh - lse_hi).
+ * `lifted` must come from ipa_lift with the same shape, mask and pair_mask.
+ * bf16 path: bf16 MFMA for the scalar and pair columns, fp16 hi/lo split
+ * MFMA for the centred point columns, fp32 softmax and accumulation. */
+ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream);
+
+/* Kernel 3 (epilogue).  Per residue i: local_points = R_i^T (g - t_i) for
+ * every head and value point, lengths sqrt(|local|^2 + eps), pair features
+ * o_pair = sum_r zl_ir * o_zr_r, head-major concat
+ * [scalar (H,Dv) | x (H,Q) | y | z | length (H,Q) | pair (H,Cz)], and
+ * update = features @ w_out + b_out; everything zero for an empty
+ * neighbourhood (IPA page, "Required behavior").
+ *   o, lse       from ipa_flash_fwd
+ *   update       [B,N,Cout] fp32 (written)
+ *   local_points [B,N,H,Q,3] fp32 (written) */
+ipa_status ipa_epilogue(const ipa_shape* s, const float* o, const float* lse, const ipa_epi_in* in,
+                        float* update, float* local_points, void* stream);
+
+/* Diagnostic (tests only): the logits the fused kernel uses, for query rows
+ * row0 .. row0+nrows-1 of (b, h), recomputed from the lifted rows with the
+ * fused kernel's operand rounding, in natural-log units; -inf where the key is
+ * not permitted.  out is [nrows, N] fp32. */
+ipa_status ipa_logit_rows(const ipa_shape* s, const void* lifted, int64_t b, int64_t h, int64_t row0,
+                          int64_t nrows, float* out, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* ipa_status_string(int status);
+
+/* Library version string (static). */
+const char* ipa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHIPA_H */

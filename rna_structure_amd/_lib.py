@@ -1,0 +1,196 @@
+"""ctypes binding of libflashipa.so (the C ABI in include/flashipa.h).
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels; torch provides device memory and the current stream.  There is
+no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflashipa.so")
+
+IPA_F32, IPA_BF16 = 0, 1
+STATUS = {0: "IPA_OK", 1: "IPA_ERR_NULL", 2: "IPA_ERR_SHAPE", 3: "IPA_ERR_UNSUPPORTED",
+          4: "IPA_ERR_ALIGN", 5: "IPA_ERR_LAUNCH", 6: "IPA_ERR_DEVICE"}
+EXPORTS = ("ipa_lifted_bytes", "ipa_o_width", "ipa_lift", "ipa_flash_fwd", "ipa_epilogue",
+           "ipa_logit_rows", "ipa_status_string", "ipa_version")
+
+
+class IpaShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "N", "H", "D", "Dv", "P", "Q", "Cz", "R", "Cout")] + \
+               [("dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class IpaLiftIn(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "q_points", "k_points", "v_points", "rotation",
+                                                "translation", "point_weight_raw", "w_pair", "zl", "zr",
+                                                "mask", "pair_mask")]
+
+
+class IpaEpiIn(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("zl", "rotation", "translation", "w_out", "b_out")]
+
+
+class IPAError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}")
+        self.code = code
+
+
+_LIB = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it first (python -m rna_structure_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    sp = ctypes.POINTER(IpaShape)
+    lib.ipa_lifted_bytes.argtypes = [sp, ctypes.c_int]
+    lib.ipa_lifted_bytes.restype = sz
+    lib.ipa_o_width.argtypes = [sp]
+    lib.ipa_o_width.restype = i64
+    lib.ipa_lift.argtypes = [sp, ctypes.POINTER(IpaLiftIn), vp, sz, vp]
+    lib.ipa_lift.restype = ctypes.c_int
+    lib.ipa_flash_fwd.argtypes = [sp, vp, vp, vp, vp]
+    lib.ipa_flash_fwd.restype = ctypes.c_int
+    lib.ipa_epilogue.argtypes = [sp, vp, vp, ctypes.POINTER(IpaEpiIn), vp, vp, vp]
+    lib.ipa_epilogue.restype = ctypes.c_int
+    lib.ipa_logit_rows.argtypes = [sp, vp, i64, i64, i64, i64, vp, vp]
+    lib.ipa_logit_rows.restype = ctypes.c_int
+    lib.ipa_status_string.argtypes = [ctypes.c_int]
+    lib.ipa_status_string.restype = ctypes.c_char_p
+    lib.ipa_version.argtypes = []
+    lib.ipa_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def make_shape(shape, eps: float = 1e-8) -> IpaShape:
+    """IpaShape from an object with B,N,H,D,Dv,P,Q,Cz,R,Cout and dtype ('f32'/'bf16')."""
+    dt = {"f32": IPA_F32, "bf16": IPA_BF16}[shape.dtype]
+    return IpaShape(shape.B, shape.N, shape.H, shape.D, shape.Dv, shape.P, shape.Q, shape.Cz, shape.R,
+                    shape.Cout, dt, float(eps))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn, code):
+    if code != 0:
+        raise IPAError(fn, code)
+
+
+def lifted_bytes(s: IpaShape, with_pair_mask: bool) -> int:
+    return int(load().ipa_lifted_bytes(ctypes.byref(s), int(bool(with_pair_mask))))
+
+
+def o_width(s: IpaShape) -> int:
+    return int(load().ipa_o_width(ctypes.byref(s)))
+
+
+def ipa_lift(s: IpaShape, t: dict, lifted, stream=None):
+    lib = load()
+    li = IpaLiftIn(*[_ptr(t.get(n)) for n in ("q", "k", "v", "q_points", "k_points", "v_points", "rotation",
+                                              "translation", "point_weight_raw", "w_pair", "zl", "zr",
+                                              "mask", "pair_mask")])
+    _check("ipa_lift", lib.ipa_lift(ctypes.byref(s), ctypes.byref(li), _ptr(lifted), lifted.numel() *
+                                    lifted.element_size(), _stream(stream)))
+
+
+def ipa_flash_fwd(s: IpaShape, lifted, o, lse, stream=None):
+    _check("ipa_flash_fwd", load().ipa_flash_fwd(ctypes.byref(s), _ptr(lifted), _ptr(o), _ptr(lse),
+                                                 _stream(stream)))
+
+
+def ipa_epilogue(s: IpaShape, o, lse, t: dict, update, local_points, stream=None):
+    ei = IpaEpiIn(*[_ptr(t[n]) for n in ("zl", "rotation", "translation", "w_out", "b_out")])
+    _check("ipa_epilogue", load().ipa_epilogue(ctypes.byref(s), _ptr(o), _ptr(lse), ctypes.byref(ei),
+                                               _ptr(update), _ptr(local_points), _stream(stream)))
+
+
+def ipa_logit_rows(s: IpaShape, lifted, b: int, h: int, row0: int, nrows: int, out, stream=None):
+    _check("ipa_logit_rows", load().ipa_logit_rows(ctypes.byref(s), _ptr(lifted), b, h, row0, nrows,
+                                                   _ptr(out), _stream(stream)))
+
+
+_FLOAT_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "translation",
+               "point_weight_raw", "w_pair", "zl", "zr", "w_out", "b_out")
+
+
+def device_inputs(inp: dict, device="cuda") -> dict:
+    """Copy a host input set (numpy arrays) to device tensors of the run dtype."""
+    import torch
+    dt = torch.bfloat16 if inp["shape"].dtype == "bf16" else torch.float32
+    out = {}
+    for key in _FLOAT_KEYS:
+        a = np.ascontiguousarray(inp[key], dtype=np.float32)
+        out[key] = torch.from_numpy(a).to(device=device).to(dt).contiguous()
+    out["mask"] = torch.from_numpy(np.ascontiguousarray(inp["mask"]).astype(np.uint8)).to(device)
+    pm = inp.get("pair_mask")
+    out["pair_mask"] = None if pm is None else torch.from_numpy(np.ascontiguousarray(pm).astype(np.uint8)).to(device)
+    return out
+
+
+class FlashIPA:
+    """Buffers and the three calls of one forward for a fixed problem shape."""
+
+    def __init__(self, shape, eps: float = 1e-8, with_pair_mask: bool = False, device="cuda"):
+        import torch
+        load()
+        self.shape = shape
+        self.s = make_shape(shape, eps)
+        nbytes = lifted_bytes(self.s, with_pair_mask)
+        if nbytes == 0:
+            raise IPAError("ipa_lifted_bytes", 3)
+        self.lifted = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        B, N, H, Q = shape.B, shape.N, shape.H, shape.Q
+        self.o = torch.empty(B, N, H, o_width(self.s), dtype=torch.float32, device=device)
+        self.lse = torch.empty(B, H, N, dtype=torch.float32, device=device)
+        self.update = torch.empty(B, N, shape.Cout, dtype=torch.float32, device=device)
+        self.local_points = torch.empty(B, N, H, Q, 3, dtype=torch.float32, device=device)
+
+    def lift(self, t: dict, stream=None):
+        ipa_lift(self.s, t, self.lifted, stream)
+
+    def attend(self, stream=None):
+        ipa_flash_fwd(self.s, self.lifted, self.o, self.lse, stream)
+
+    def epilogue(self, t: dict, stream=None):
+        ipa_epilogue(self.s, self.o, self.lse, t, self.update, self.local_points, stream)
+
+    def forward(self, t: dict, stream=None):
+        self.lift(t, stream)
+        self.attend(stream)
+        self.epilogue(t, stream)
+        return dict(update=self.update, local_points=self.local_points, o=self.o, lse=self.lse)
+
+    def logit_rows(self, b: int, h: int, row0: int, nrows: int, stream=None):
+        import torch
+        out = torch.empty(nrows, self.shape.N, dtype=torch.float32, device=self.o.device)
+        ipa_logit_rows(self.s, self.lifted, b, h, row0, nrows, out, stream)
+        return out
+
+
+def forward(inp_dev: dict, shape, eps: float = 1e-8) -> dict:
+    """One forward on device tensors (see device_inputs)."""
+    f = FlashIPA(shape, eps, with_pair_mask=inp_dev.get("pair_mask") is not None,
+                 device=inp_dev["q"].device)
+    return f.forward(inp_dev)

@@ -1,0 +1,124 @@
+// C ABI of the FlashIPA library: argument validation, workspace layout and
+// kernel launches.  No allocation, no synchronisation: every kernel is
+// enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace fipa {
+hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStream_t st);
+hipError_t launch_flash_f32(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st);
+hipError_t launch_flash_mfma(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st);
+hipError_t launch_epilogue(const Layout& L, const float* o, const float* lse, const ipa_epi_in* in, float eps,
+                           float* update, float* local, hipStream_t st);
+hipError_t launch_logit_rows(const Layout& L, const void* ws, int b, int h, int row0, int nrows, float* out,
+                             hipStream_t st);
+}  // namespace fipa
+
+using fipa::Layout;
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static ipa_status shape_status(const ipa_shape* s, int with_pm, Layout* L) {
+  if (!s) return IPA_ERR_NULL;
+  if (s->B <= 0 || s->N <= 0 || s->H <= 0 || s->D <= 0 || s->Dv <= 0 || s->P <= 0 || s->Q <= 0 || s->Cz <= 0 ||
+      s->R <= 0 || s->Cout <= 0 || !(s->eps > 0.0f))
+    return IPA_ERR_SHAPE;
+  if (s->dtype != IPA_F32 && s->dtype != IPA_BF16) return IPA_ERR_UNSUPPORTED;
+  if (!fipa::make_layout(s, with_pm, L)) return IPA_ERR_UNSUPPORTED;
+  return IPA_OK;
+}
+
+static ipa_status launch_status(hipError_t e) { return e == hipSuccess ? IPA_OK : IPA_ERR_LAUNCH; }
+
+extern "C" {
+
+size_t ipa_lifted_bytes(const ipa_shape* s, int with_pair_mask) {
+  Layout L;
+  if (shape_status(s, with_pair_mask, &L) != IPA_OK) return 0;
+  return L.total;
+}
+
+int64_t ipa_o_width(const ipa_shape* s) {
+  if (!s) return 0;
+  return s->Dv + s->R * s->Cz + 3 * s->Q;
+}
+
+ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, size_t lifted_bytes, void* stream) {
+  if (!s || !in || !lifted) return IPA_ERR_NULL;
+  Layout L;
+  const int with_pm = in->pair_mask != nullptr;
+  ipa_status st = shape_status(s, with_pm, &L);
+  if (st != IPA_OK) return st;
+  const void* req[] = {in->q, in->k, in->v, in->q_points, in->k_points, in->v_points, in->rotation,
+                       in->translation, in->point_weight_raw, in->w_pair, in->zl, in->zr, in->mask};
+  for (const void* p : req)
+    if (!p) return IPA_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return IPA_ERR_ALIGN;
+  if (!aligned16(lifted) || (in->pair_mask && !aligned16(in->pair_mask))) return IPA_ERR_ALIGN;
+  if (lifted_bytes < L.total) return IPA_ERR_SHAPE;
+  return launch_status(fipa::launch_lift(L, in, lifted, reinterpret_cast<hipStream_t>(stream)));
+}
+
+ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream) {
+  if (!s || !lifted || !o || !lse) return IPA_ERR_NULL;
+  Layout L;
+  // the pair-mask region is at the end of the workspace; its presence is
+  // recorded in the workspace header by ipa_lift
+  ipa_status st = shape_status(s, 0, &L);
+  if (st != IPA_OK) return st;
+  if (!aligned16(lifted) || !aligned16(o) || !aligned16(lse)) return IPA_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  return launch_status(L.mfma ? fipa::launch_flash_mfma(L, lifted, o, lse, hs)
+                              : fipa::launch_flash_f32(L, lifted, o, lse, hs));
+}
+
+ipa_status ipa_epilogue(const ipa_shape* s, const float* o, const float* lse, const ipa_epi_in* in, float* update,
+                        float* local_points, void* stream) {
+  if (!s || !o || !lse || !in || !update || !local_points) return IPA_ERR_NULL;
+  Layout L;
+  ipa_status st = shape_status(s, 0, &L);
+  if (st != IPA_OK) return st;
+  const void* req[] = {in->zl, in->rotation, in->translation, in->w_out, in->b_out};
+  for (const void* p : req)
+    if (!p) return IPA_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return IPA_ERR_ALIGN;
+  if (!aligned16(o) || !aligned16(lse) || !aligned16(update) || !aligned16(local_points)) return IPA_ERR_ALIGN;
+  const int64_t F = s->H * (s->Dv + 4 * s->Q + s->Cz);
+  if (L.mfma ? (32 * ((F + 15) / 16 * 16 + 8) * 2 > 160 * 1024) : (16 * (F + 1) * 4 > 160 * 1024))
+    return IPA_ERR_UNSUPPORTED;
+  return launch_status(fipa::launch_epilogue(L, o, lse, in, s->eps, update, local_points,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+ipa_status ipa_logit_rows(const ipa_shape* s, const void* lifted, int64_t b, int64_t h, int64_t row0, int64_t nrows,
+                          float* out, void* stream) {
+  if (!s || !lifted || !out) return IPA_ERR_NULL;
+  Layout L;
+  ipa_status st = shape_status(s, 0, &L);
+  if (st != IPA_OK) return st;
+  if (b < 0 || b >= s->B || h < 0 || h >= s->H || row0 < 0 || nrows <= 0 || row0 + nrows > s->N || nrows > 65535)
+    return IPA_ERR_SHAPE;
+  if (!aligned16(lifted) || !aligned16(out)) return IPA_ERR_ALIGN;
+  return launch_status(fipa::launch_logit_rows(L, lifted, (int)b, (int)h, (int)row0, (int)nrows, out,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* ipa_status_string(int status) {
+  switch (status) {
+    case IPA_OK: return "ok";
+    case IPA_ERR_NULL: return "a required pointer is NULL";
+    case IPA_ERR_SHAPE: return "invalid shape or workspace size";
+    case IPA_ERR_UNSUPPORTED: return "dimensions or dtype not supported by the compiled kernels";
+    case IPA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case IPA_ERR_LAUNCH: return "kernel launch failed";
+    case IPA_ERR_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ipa_version(void) { return "flashipa-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,197 @@
+// Internal definitions shared by the FlashIPA HIP sources: the layout of the
+// opaque "lifted" workspace, tile constants and small conversion helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/flashipa.h"
+
+namespace fipa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Key tile: 64 keys.  Query tile of the matrix-core kernel: 4 waves x 32.
+constexpr int kKeyTile = 64;
+constexpr int kQueryTile = 128;
+// Geometric columns of a lifted key row on the matrix-core path: 3 MFMA
+// K-steps of 16.  Fixed positions for up to 5 points (15 coordinates):
+//   [w_hi (15) | w_lo (15) | w_hi (15) | nb_hi | nb_lo | 0]
+// against the query's [u_hi | u_hi | u_lo | kNormScale | kNormScale | 0],
+// where w = b - c and u = 2 gamma log2(e) (a - c) are split into fp16
+// high and low parts and nb = -gamma log2(e) |b - c|^2 / kNormScale.
+constexpr int kGeoCols = 48;
+constexpr int kGeoW = 15;
+// The squared-norm column of a key is stored divided by this power of two
+// (and the matching query column holds it), extending its fp16 range.
+constexpr float kNormScale = 16.0f;
+// Padding (in 16-bit elements) appended to every LDS row so that the
+// 16-byte fragment reads of 16 consecutive rows hit distinct banks.
+constexpr int kRowPad = 8;
+constexpr int kVCols = kKeyTile + kRowPad;  // 72 elements = 144 bytes
+constexpr uint32_t kMagic = 0x46495041u;    // "FIPA"
+
+// Matrix-core kernel instances: (NQS, NVB) = number of 16-wide bf16 K-steps
+// of the scalar+pair query columns, number of 32-row bf16 value blocks.
+struct MfmaDims {
+  int NQS, NVB;
+};
+
+// Workspace header, first 256 bytes of the lifted buffer.
+struct Header {
+  uint32_t magic;
+  uint32_t has_pair_mask;
+  uint32_t pad[62];
+};
+
+// Everything a kernel needs to find its rows in the lifted workspace.
+struct Layout {
+  int B, N, H, D, Dv, P, Q, Cz, R, Cout;
+  int RCz;   // R*Cz
+  int NT;    // key tiles of 64
+  int NKpad; // NT*64 key rows
+  int NQpad; // query rows rounded up to 128
+  int mfma;  // 1: matrix-core path (bf16 input), 0: fp32 path
+  int NQS, NVB;
+  int QW;     // query scalar+pair width (elements)
+  int KROW;   // elements per key row (mfma: QW + 48 + pad; fp32: DKP)
+  int VROWS;  // mfma: rows of the transposed value tile; fp32: DVP (row stride)
+  int DQP;    // fp32 path: padded query row width
+  int DO;     // attention output width Dv + R*Cz + 3Q
+  int has_pm;
+  size_t off_ql, off_qa, off_kt, off_vt, off_ck, off_gam, off_km, off_pm, total;
+};
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Choose the smallest compiled matrix-core instance that holds the shape.
+// Returns false when none does.
+static inline bool pick_mfma_dims(int D, int Dv, int RCz, int P, int Q, MfmaDims* out) {
+  static const MfmaDims inst[] = {{3, 2}, {5, 3}, {9, 5}};
+  if (P > 5) return false;
+  if (3 * Q + 4 > 32) return false;
+  for (const MfmaDims& m : inst) {
+    if (D + RCz <= 16 * m.NQS && Dv + RCz + 1 <= 32 * m.NVB) {
+      *out = m;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Limits of the fp32 kernels (registers sized at compile time).
+constexpr int kF32MaxDQ = 160;   // D + R*Cz
+constexpr int kF32MaxDV = 192;   // Dv + R*Cz + 3Q (4 threads x 48)
+constexpr int kMaxP = 5;   // 3P <= 15 point coordinates per lifted row
+constexpr int kMaxQ = 10;  // 3Q <= 30 value-point coordinates
+
+static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
+  if (!s) return false;
+  if (s->B <= 0 || s->N <= 0 || s->H <= 0 || s->D <= 0 || s->Dv <= 0 || s->P <= 0 || s->Q <= 0 ||
+      s->Cz <= 0 || s->R <= 0 || s->Cout <= 0)
+    return false;
+  if (s->N > (1 << 24) || s->B > (1 << 20) || s->H > 64 || s->Cout > 4096) return false;
+  L->B = (int)s->B; L->N = (int)s->N; L->H = (int)s->H; L->D = (int)s->D; L->Dv = (int)s->Dv;
+  L->P = (int)s->P; L->Q = (int)s->Q; L->Cz = (int)s->Cz; L->R = (int)s->R; L->Cout = (int)s->Cout;
+  L->RCz = L->R * L->Cz;
+  L->NT = (L->N + kKeyTile - 1) / kKeyTile;
+  L->NKpad = L->NT * kKeyTile;
+  L->NQpad = round_up(L->N, kQueryTile);
+  L->DO = L->Dv + L->RCz + 3 * L->Q;
+  L->has_pm = with_pm ? 1 : 0;
+  if (L->P > kMaxP || L->Q > kMaxQ) return false;
+  const size_t B = L->B, H = L->H, NT = L->NT, NQ = L->NQpad, NK = L->NKpad;
+  if (s->dtype == IPA_BF16) {
+    MfmaDims md;
+    if (!pick_mfma_dims(L->D, L->Dv, L->RCz, L->P, L->Q, &md)) return false;
+    L->mfma = 1;
+    L->NQS = md.NQS; L->NVB = md.NVB;
+    L->QW = 16 * md.NQS;
+    L->KROW = L->QW + kGeoCols + kRowPad;
+    L->VROWS = 32 * (md.NVB + 1);
+    L->DQP = L->QW;
+  } else if (s->dtype == IPA_F32) {
+    if (L->D + L->RCz > kF32MaxDQ || L->DO > kF32MaxDV) return false;
+    L->mfma = 0;
+    L->NQS = L->NVB = 0;
+    L->DQP = round_up(L->D + L->RCz, 4);
+    L->QW = L->DQP;
+    L->KROW = round_up(L->D + L->RCz + 3 * L->P + 1, 4);
+    L->VROWS = round_up(L->DO, 4);
+  } else {
+    return false;
+  }
+  size_t off = 256;  // header
+  L->off_ql = off;
+  off = align256(off + B * H * NQ * L->QW * (L->mfma ? 2 : 4));
+  L->off_qa = off;
+  off = align256(off + B * H * NQ * 16 * 4);
+  L->off_kt = off;
+  off = align256(off + B * H * NK * L->KROW * (L->mfma ? 2 : 4));
+  L->off_vt = off;
+  if (L->mfma)
+    off = align256(off + B * H * NT * (size_t)L->VROWS * kVCols * 2);
+  else
+    off = align256(off + B * H * NK * (size_t)L->VROWS * 4);
+  L->off_ck = off;
+  off = align256(off + B * NT * 4 * 4);
+  L->off_gam = off;
+  off = align256(off + H * 4);
+  L->off_km = off;
+  off = align256(off + B * NT * 2 * 4);
+  L->off_pm = off;
+  if (with_pm) off = align256(off + B * NQ * NT * 2 * 4);
+  L->total = off;
+  return true;
+}
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) {
+  return __uint_as_float(((uint32_t)u) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t u) {
+  return (float)__builtin_bit_cast(_Float16, u);
+}
+
+// Load element i of an input tensor stored as fp32 or bf16.
+template <bool BF>
+__device__ __forceinline__ float ld(const void* p, size_t i) {
+  if constexpr (BF) {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  } else {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+}
+
+// Key index inside a 64-key tile that lives in column kappa of a transposed
+// value tile.  Within every 16 keys the order is [0-3, 8-11, 4-7, 12-15]:
+// this is the order in which an MFMA 32x32 accumulator lane holds the
+// probabilities it feeds back as the B operand of the value product.
+__host__ __device__ __forceinline__ int vt_key_of_col(int kappa) {
+  const int g = kappa >> 4, half = (kappa >> 3) & 1, e = kappa & 7;
+  return 16 * g + 8 * (e >> 2) + 4 * half + (e & 3);
+}
+
+// Mask words: every 64-key tile has two 32-bit words, one per half of a
+// wavefront.  A lane of half h of a 32x32 accumulator holds keys
+// kb*32 + 8*(r/4) + 4*h + r%4 (kb = 0..1, r = 0..15) and reads them as bit
+// kb*16 + r of word h.  Returns that bit and sets *half_out = h for key jj.
+__host__ __device__ __forceinline__ int mask_bit_of_key(int jj, int* half_out) {
+  const int kb = jj >> 5, rem = jj & 31;
+  *half_out = (rem >> 2) & 1;
+  return kb * 16 + 4 * (rem >> 3) + (rem & 3);
+}
+
+}  // namespace fipa

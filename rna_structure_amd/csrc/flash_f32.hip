@@ -1,0 +1,176 @@
+// Kernel 2, fp32 path: fused masked online-softmax attention over the lifted
+// rows, fp32 arithmetic throughout (VALU, no matrix cores).
+//
+// Logit (log2 units) for query i, key j in key tile t with centroid c_t:
+//   s_ij = Qs_i . Ks_j                       scalar + pair columns
+//        + u_it . w_j                        u = 2 gamma log2e (a_i - c_t), w = b_j - c_t
+//        + nb_j - gamma log2e |a_i - c_t|^2  nb = -gamma log2e |b_j - c_t|^2
+// which equals log2(e) * L_ijh of the IPA page ("Required behavior").
+// Softmax over the permitted keys uses a running maximum (FlashAttention
+// style); value points are aggregated relative to the tile centroid and the
+// centroid term sum_j p_j c_t is carried separately.
+//
+// Grid (ceil(N/64), H, B), 256 threads: 64 queries x 4 column groups.
+#include "common.h"
+
+namespace fipa {
+
+struct FlashF32Args {
+  Layout L;
+  const char* ws;
+  float* o;
+  float* lse;
+};
+
+constexpr int kF32Keys = 32;  // keys staged per step
+constexpr int kF32DvPer = kF32MaxDV / 4;
+
+__global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
+  const Layout& L = a.L;
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int qi = tid & 63, part = tid >> 6;
+  const int i = qb * 64 + qi;
+  const int N = L.N, H = L.H, P3 = 3 * L.P, DQ = L.D + L.RCz, KROW = L.KROW, DVP = L.VROWS;
+  const int DO = L.DO, DPT = L.Dv + L.RCz;  // points start at DPT
+
+  extern __shared__ float smem[];
+  float* sk = smem;                       // [32][KROW]
+  float* sv = smem + kF32Keys * KROW;     // [32][DVP]
+
+  const Header* hd = reinterpret_cast<const Header*>(a.ws);
+  const bool has_pm = hd->has_pair_mask != 0;
+  const float gam = reinterpret_cast<const float*>(a.ws + L.off_gam)[h];
+  const float gl = gam * kLog2e;
+  const bool qin = i < N;
+
+  float qv[kF32MaxDQ];
+  const float* qrow = reinterpret_cast<const float*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + i) * L.DQP;
+#pragma unroll
+  for (int d = 0; d < kF32MaxDQ; ++d) qv[d] = (qin && d < DQ) ? qrow[d] : 0.f;
+  float av[15];
+  const float* arow = reinterpret_cast<const float*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + i) * 16;
+#pragma unroll
+  for (int g = 0; g < 15; ++g) av[g] = (qin && g < P3) ? arow[g] : 0.f;
+
+  float ov[kF32DvPer];
+#pragma unroll
+  for (int e = 0; e < kF32DvPer; ++e) ov[e] = 0.f;
+  float cs0 = 0.f, cs1 = 0.f, cs2 = 0.f;  // sum_j p_j c_t
+  float m = -INFINITY, l = 0.f;
+
+  const uint32_t* km = reinterpret_cast<const uint32_t*>(a.ws + L.off_km);
+  const uint32_t* pmw = reinterpret_cast<const uint32_t*>(a.ws + L.off_pm);
+  const float4* ck = reinterpret_cast<const float4*>(a.ws + L.off_ck);
+  const float* kbase = reinterpret_cast<const float*>(a.ws + L.off_kt) + ((size_t)b * H + h) * L.NKpad * KROW;
+  const float* vbase = reinterpret_cast<const float*>(a.ws + L.off_vt) + ((size_t)b * H + h) * L.NKpad * DVP;
+
+  // query validity: bit of residue i in the key-mask words of its tile
+  bool qvalid = false;
+  if (qin) {
+    int hf;
+    const int bit = mask_bit_of_key(i & 63, &hf);
+    qvalid = (km[((size_t)b * L.NT + (i >> 6)) * 2 + hf] >> bit) & 1u;
+  }
+
+  float u[15];
+  float na = 0.f;
+  float4 c4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint32_t w0 = 0, w1 = 0;
+  const int nsteps = L.NKpad / kF32Keys;
+  for (int st = 0; st < nsteps; ++st) {
+    const int t = st >> 1;
+    if ((st & 1) == 0) {
+      c4 = ck[(size_t)b * L.NT + t];
+      na = 0.f;
+#pragma unroll
+      for (int g = 0; g < 15; ++g) {
+        const float cc = (g % 3 == 0) ? c4.x : ((g % 3 == 1) ? c4.y : c4.z);
+        const float d = (g < P3) ? av[g] - cc : 0.f;
+        na += d * d;
+        u[g] = 2.f * gl * d;
+      }
+      na *= gl;
+      if (has_pm) {
+        const size_t o = (((size_t)b * L.NQpad + i) * L.NT + t) * 2;
+        w0 = qin ? pmw[o] : 0u;
+        w1 = qin ? pmw[o + 1] : 0u;
+      } else {
+        w0 = qvalid ? km[((size_t)b * L.NT + t) * 2] : 0u;
+        w1 = qvalid ? km[((size_t)b * L.NT + t) * 2 + 1] : 0u;
+      }
+    }
+    __syncthreads();
+    const float* kt = kbase + (size_t)st * kF32Keys * KROW;
+    const float* vt = vbase + (size_t)st * kF32Keys * DVP;
+    for (int x = tid; x < kF32Keys * KROW / 4; x += 256)
+      reinterpret_cast<float4*>(sk)[x] = reinterpret_cast<const float4*>(kt)[x];
+    for (int x = tid; x < kF32Keys * DVP / 4; x += 256)
+      reinterpret_cast<float4*>(sv)[x] = reinterpret_cast<const float4*>(vt)[x];
+    __syncthreads();
+    for (int jl = 0; jl < kF32Keys; ++jl) {
+      const int jj = (st & 1) * kF32Keys + jl;
+      int hf;
+      const int bit = mask_bit_of_key(jj, &hf);
+      const bool perm = (((hf ? w1 : w0) >> bit) & 1u) != 0;
+      if (!perm) continue;
+      const float* kr = sk + jl * KROW;
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < kF32MaxDQ; ++d)
+        if (d < DQ) s = fmaf(qv[d], kr[d], s);
+#pragma unroll
+      for (int g = 0; g < 15; ++g)
+        if (g < P3) s = fmaf(u[g], kr[DQ + g], s);
+      s += kr[DQ + P3] - na;
+      if (s > m) {
+        const float alpha = exp2f(m - s);  // m = -inf -> 0
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < kF32DvPer; ++e) ov[e] *= alpha;
+        cs0 *= alpha; cs1 *= alpha; cs2 *= alpha;
+        m = s;
+      }
+      const float p = exp2f(s - m);
+      l += p;
+      const float* vr = sv + jl * DVP;
+#pragma unroll
+      for (int e = 0; e < kF32DvPer; ++e) {
+        const int d = e * 4 + part;
+        if (d < DO) ov[e] = fmaf(p, vr[d], ov[e]);
+      }
+      cs0 = fmaf(p, c4.x, cs0); cs1 = fmaf(p, c4.y, cs1); cs2 = fmaf(p, c4.z, cs2);
+    }
+  }
+  if (!qin) return;
+  const bool nonempty = l > 0.f;
+  const float inv = nonempty ? 1.0f / l : 0.f;
+  float* orow = a.o + (((size_t)b * N + i) * H + h) * DO;
+#pragma unroll
+  for (int e = 0; e < kF32DvPer; ++e) {
+    const int d = e * 4 + part;
+    if (d < DO) {
+      float val = ov[e];
+      if (d >= DPT) {
+        const int x = (d - DPT) % 3;
+        val += (x == 0) ? cs0 : ((x == 1) ? cs1 : cs2);
+      }
+      orow[d] = val * inv;
+    }
+  }
+  if (part == 0) a.lse[((size_t)b * H + h) * N + i] = nonempty ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_flash_f32(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st) {
+  FlashF32Args a;
+  a.L = L;
+  a.ws = reinterpret_cast<const char*>(ws);
+  a.o = o;
+  a.lse = lse;
+  const size_t shm = (size_t)kF32Keys * (L.KROW + L.VROWS) * sizeof(float);
+  dim3 grid((L.N + 63) / 64, L.H, L.B);
+  hipLaunchKernelGGL(flash_f32_kernel, grid, dim3(256), shm, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fipa

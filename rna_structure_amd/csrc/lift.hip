@@ -1,0 +1,354 @@
+// Kernel 1 (lift): frames -> global points, per-head point weight, and the
+// lifted rows whose inner products are the IPA logits.
+//
+// Logit of the "Invariant point attention (IPA)" page ("Required behavior"):
+//   L_ijh = q.k/sqrt(3D) + pair_bias_ijh/sqrt(3) - gamma_h sum_p |a_ip - b_jp|^2
+// with a = T_i(q_points), b = T_j(k_points), gamma_h = 1/2 softplus(w_h)
+// sqrt(2/(27P)), pair_bias_ijh = sum_c w_pair[h,c] sum_r zl_irc zr_jrc.
+// Expanding the squared distance (FlashIPA verdict page, key_machinery)
+// about the centroid c of the key tile that holds j,
+//   -gamma |a-b|^2 = 2 gamma (a-c).(b-c) - gamma |b-c|^2 - gamma |a-c|^2,
+// every term but the last is an inner product of a query-side and a
+// key-side vector; the last depends on (i, tile) only and is added by the
+// fused kernel.  All logits are carried in log2 units (times log2 e) so that
+// the softmax can use exp2.
+//
+// One workgroup per (key tile t, head h, batch b), 64 residues.
+#include "common.h"
+
+namespace fipa {
+
+struct LiftArgs {
+  Layout L;
+  const void *q, *k, *v, *qp, *kp, *vp, *rot, *trans, *pwr, *wpair, *zl, *zr;
+  const uint8_t* mask;
+  const uint8_t* pm;
+  char* ws;
+};
+
+__device__ __forceinline__ float softplus_f(float x) {
+  // log(1 + exp(x)) without overflow
+  return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+}
+
+__device__ __forceinline__ float clamp_f16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
+
+__device__ __forceinline__ uint16_t hi16(float x) { return f32_to_f16_bits(clamp_f16(x)); }
+__device__ __forceinline__ uint16_t lo16(float x) {
+  const float c = clamp_f16(x);
+  return f32_to_f16_bits(c - f16_bits_to_f32(f32_to_f16_bits(c)));
+}
+
+template <bool BF>
+__global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
+  const Layout& L = a.L;
+  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int N = L.N, H = L.H, P = L.P, Q = L.Q, D = L.D, Dv = L.Dv, RCz = L.RCz, Cz = L.Cz;
+
+  __shared__ float s_tr[64][3];
+  __shared__ int s_valid[64];
+  __shared__ float s_w[64][16];    // b - c (key points, centred)
+  __shared__ float s_x[64][32];    // x - c (value points, centred)
+  __shared__ float s_a[64][16];    // a (query points, global)
+  __shared__ float s_nb[64];       // -gamma log2e |b - c|^2
+  __shared__ float s_c[4];
+  __shared__ float s_gam;
+
+  // --- residues of this tile: validity, translation
+  if (tid < 64) {
+    const int j = t * 64 + tid;
+    int valid = 0;
+    float tx = 0.f, ty = 0.f, tz = 0.f;
+    if (j < N) {
+      valid = a.mask[(size_t)b * N + j] != 0;
+      const size_t o = ((size_t)b * N + j) * 3;
+      tx = ld<BF>(a.trans, o); ty = ld<BF>(a.trans, o + 1); tz = ld<BF>(a.trans, o + 2);
+    }
+    s_valid[tid] = valid;
+    s_tr[tid][0] = tx; s_tr[tid][1] = ty; s_tr[tid][2] = tz;
+    // centroid of the valid translations (wave 0 holds the 64 residues)
+    float sx = valid ? tx : 0.f, sy = valid ? ty : 0.f, sz = valid ? tz : 0.f, sn = valid ? 1.f : 0.f;
+    for (int off = 32; off > 0; off >>= 1) {
+      sx += __shfl_xor(sx, off);
+      sy += __shfl_xor(sy, off);
+      sz += __shfl_xor(sz, off);
+      sn += __shfl_xor(sn, off);
+    }
+    if (tid == 0) {
+      float cx = 0.f, cy = 0.f, cz = 0.f;
+      if (sn > 0.f) { cx = sx / sn; cy = sy / sn; cz = sz / sn; }
+      if (L.mfma) {
+        // the centroid only has to be some fixed point; keep it exactly
+        // representable in fp16 so that it can ride in an fp16 value column
+        cx = f16_bits_to_f32(hi16(cx)); cy = f16_bits_to_f32(hi16(cy)); cz = f16_bits_to_f32(hi16(cz));
+      }
+      s_c[0] = cx; s_c[1] = cy; s_c[2] = cz; s_c[3] = 0.f;
+      const float g = 0.5f * softplus_f(ld<BF>(a.pwr, h)) * sqrtf(2.0f / (27.0f * (float)P));
+      s_gam = g;
+    }
+  }
+  __syncthreads();
+  const float cx = s_c[0], cy = s_c[1], cz = s_c[2];
+  const float gam = s_gam;
+  const float gl = gam * kLog2e;
+
+  // --- global points of the 64 residues for head h
+  if (tid < 64) {
+    const int j = t * 64 + tid;
+    float Rm[9];
+    const bool in = j < N;
+    for (int e = 0; e < 9; ++e) Rm[e] = in ? ld<BF>(a.rot, ((size_t)b * N + j) * 9 + e) : 0.f;
+    const float tx = s_tr[tid][0], ty = s_tr[tid][1], tz = s_tr[tid][2];
+    float nb = 0.f;
+    for (int p = 0; p < 16; ++p) { s_w[tid][p] = 0.f; s_a[tid][p] = 0.f; }
+    for (int p = 0; p < 32; ++p) s_x[tid][p] = 0.f;
+    if (in) {
+      const size_t base_k = (((size_t)b * N + j) * H + h) * P * 3;
+      for (int p = 0; p < P; ++p) {
+        const float lx = ld<BF>(a.kp, base_k + 3 * p), ly = ld<BF>(a.kp, base_k + 3 * p + 1),
+                    lz = ld<BF>(a.kp, base_k + 3 * p + 2);
+        const float gx = Rm[0] * lx + Rm[1] * ly + Rm[2] * lz + tx;
+        const float gy = Rm[3] * lx + Rm[4] * ly + Rm[5] * lz + ty;
+        const float gz = Rm[6] * lx + Rm[7] * ly + Rm[8] * lz + tz;
+        const float wx = gx - cx, wy = gy - cy, wz = gz - cz;
+        s_w[tid][3 * p] = wx; s_w[tid][3 * p + 1] = wy; s_w[tid][3 * p + 2] = wz;
+        nb += wx * wx + wy * wy + wz * wz;
+        const float qx = ld<BF>(a.qp, base_k + 3 * p), qy = ld<BF>(a.qp, base_k + 3 * p + 1),
+                    qz = ld<BF>(a.qp, base_k + 3 * p + 2);
+        s_a[tid][3 * p] = Rm[0] * qx + Rm[1] * qy + Rm[2] * qz + tx;
+        s_a[tid][3 * p + 1] = Rm[3] * qx + Rm[4] * qy + Rm[5] * qz + ty;
+        s_a[tid][3 * p + 2] = Rm[6] * qx + Rm[7] * qy + Rm[8] * qz + tz;
+      }
+      const size_t base_v = (((size_t)b * N + j) * H + h) * Q * 3;
+      for (int q = 0; q < Q && q < 10; ++q) {
+        const float lx = ld<BF>(a.vp, base_v + 3 * q), ly = ld<BF>(a.vp, base_v + 3 * q + 1),
+                    lz = ld<BF>(a.vp, base_v + 3 * q + 2);
+        s_x[tid][3 * q] = Rm[0] * lx + Rm[1] * ly + Rm[2] * lz + tx - cx;
+        s_x[tid][3 * q + 1] = Rm[3] * lx + Rm[4] * ly + Rm[5] * lz + ty - cy;
+        s_x[tid][3 * q + 2] = Rm[6] * lx + Rm[7] * ly + Rm[8] * lz + tz - cz;
+      }
+    }
+    s_nb[tid] = -gl * nb;
+  }
+  // --- small per-tile / per-head records
+  if (tid == 0) {
+    if (b == 0 && t == 0) reinterpret_cast<float*>(a.ws + L.off_gam)[h] = gam;
+    if (h == 0) {
+      float4* ck = reinterpret_cast<float4*>(a.ws + L.off_ck);
+      ck[(size_t)b * L.NT + t] = make_float4(cx, cy, cz, 0.f);
+      if (b == 0 && t == 0) {
+        Header* hd = reinterpret_cast<Header*>(a.ws);
+        hd->magic = kMagic;
+        hd->has_pair_mask = a.pm != nullptr;
+      }
+    }
+  }
+  __syncthreads();
+  if (h == 0 && tid < 2) {
+    uint32_t w = 0;
+    for (int jj = 0; jj < 64; ++jj) {
+      int hf;
+      const int bit = mask_bit_of_key(jj, &hf);
+      if (hf == tid && s_valid[jj]) w |= 1u << bit;
+    }
+    reinterpret_cast<uint32_t*>(a.ws + L.off_km)[((size_t)b * L.NT + t) * 2 + tid] = w;
+  }
+
+  const float sq = kLog2e / sqrtf(3.0f * (float)D);
+  const float sp = kLog2e / sqrtf(3.0f);
+
+  if constexpr (BF) {
+    // ---------------- matrix-core layouts
+    const int QW = L.QW, KROW = L.KROW, P3 = 3 * P;
+    // key rows of tile (b,h,t): [k | zr | 0 | geo(48) | pad]
+    uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * KROW;
+    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(a.k);
+    const uint16_t* zr16 = reinterpret_cast<const uint16_t*>(a.zr);
+    const uint16_t* v16 = reinterpret_cast<const uint16_t*>(a.v);
+    const int kchunks = KROW / 8;
+    for (int ch = tid; ch < 64 * kchunks; ch += 256) {
+      const int row = ch / kchunks, c0 = (ch % kchunks) * 8;
+      const int j = t * 64 + row;
+      uint16_t out[8];
+      for (int e = 0; e < 8; ++e) {
+        const int c = c0 + e;
+        uint16_t val = 0;
+        if (s_valid[row]) {
+          if (c < D) {
+            val = k16[(((size_t)b * N + j) * H + h) * D + c];
+          } else if (c < D + RCz) {
+            val = zr16[((size_t)b * N + j) * RCz + (c - D)];
+          } else if (c >= QW && c < QW + kGeoCols) {
+            const int g = c - QW;
+            (void)P3;
+            if (g < kGeoW) val = hi16(s_w[row][g]);
+            else if (g < 2 * kGeoW) val = lo16(s_w[row][g - kGeoW]);
+            else if (g < 3 * kGeoW) val = hi16(s_w[row][g - 2 * kGeoW]);
+            else if (g == 3 * kGeoW) val = hi16(s_nb[row] * (1.0f / kNormScale));
+            else if (g == 3 * kGeoW + 1) val = lo16(s_nb[row] * (1.0f / kNormScale));
+          }
+        }
+        out[e] = val;
+      }
+      uint4 pk;
+      pk.x = out[0] | ((uint32_t)out[1] << 16);
+      pk.y = out[2] | ((uint32_t)out[3] << 16);
+      pk.z = out[4] | ((uint32_t)out[5] << 16);
+      pk.w = out[6] | ((uint32_t)out[7] << 16);
+      reinterpret_cast<uint4*>(kt + (size_t)row * KROW + c0)[0] = pk;
+    }
+    // transposed value tile (b,h,t): rows d, columns kappa (permuted keys)
+    const int VROWS = L.VROWS, NVB = L.NVB;
+    uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + L.off_vt) + (((size_t)b * H + h) * L.NT + t) * VROWS * kVCols;
+    const int vchunks = kVCols / 8;
+    for (int ch = tid; ch < VROWS * vchunks; ch += 256) {
+      const int d = ch / vchunks, k0 = (ch % vchunks) * 8;
+      uint16_t out[8];
+      for (int e = 0; e < 8; ++e) {
+        const int kappa = k0 + e;
+        uint16_t val = 0;
+        if (kappa < 64) {
+          const int jj = vt_key_of_col(kappa);
+          const int j = t * 64 + jj;
+          if (s_valid[jj]) {
+            if (d < 32 * NVB) {
+              if (d < Dv) val = v16[(((size_t)b * N + j) * H + h) * Dv + d];
+              else if (d < Dv + RCz) val = zr16[((size_t)b * N + j) * RCz + (d - Dv)];
+              else if (d == Dv + RCz) val = 0x3F80;  // bf16 1.0: weight sum
+            } else {
+              const int dd = d - 32 * NVB;
+              if (dd < 3 * Q) val = hi16(s_x[jj][dd]);
+              else if (dd == 3 * Q) val = 0x3C00;  // fp16 1.0: weight sum
+              else if (dd <= 3 * Q + 3) val = hi16(s_c[dd - 3 * Q - 1]);
+            }
+          }
+        }
+        out[e] = val;
+      }
+      uint4 pk;
+      pk.x = out[0] | ((uint32_t)out[1] << 16);
+      pk.y = out[2] | ((uint32_t)out[3] << 16);
+      pk.z = out[4] | ((uint32_t)out[5] << 16);
+      pk.w = out[6] | ((uint32_t)out[7] << 16);
+      reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + k0)[0] = pk;
+    }
+    // lifted query rows: [q sq | w_pair * zl * sp | 0] for the tile's residues
+    uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql);
+    const int qchunks = QW / 8;
+    for (int ch = tid; ch < 64 * qchunks; ch += 256) {
+      const int row = ch / qchunks, c0 = (ch % qchunks) * 8;
+      const int i = t * 64 + row;
+      uint16_t out[8];
+      for (int e = 0; e < 8; ++e) {
+        const int c = c0 + e;
+        float val = 0.f;
+        if (i < N) {
+          if (c < D) {
+            val = ld<true>(a.q, (((size_t)b * N + i) * H + h) * D + c) * sq;
+          } else if (c < D + RCz) {
+            const int cc = (c - D) % Cz;
+            val = ld<true>(a.wpair, (size_t)h * Cz + cc) * ld<true>(a.zl, ((size_t)b * N + i) * RCz + (c - D)) * sp;
+          }
+        }
+        out[e] = f32_to_bf16_bits(val);
+      }
+      uint4 pk;
+      pk.x = out[0] | ((uint32_t)out[1] << 16);
+      pk.y = out[2] | ((uint32_t)out[3] << 16);
+      pk.z = out[4] | ((uint32_t)out[5] << 16);
+      pk.w = out[6] | ((uint32_t)out[7] << 16);
+      reinterpret_cast<uint4*>(ql + (((size_t)b * H + h) * L.NQpad + i) * QW + c0)[0] = pk;
+    }
+  } else {
+    // ---------------- fp32 layouts (row-major per key / query)
+    const int KROW = L.KROW, DVP = L.VROWS, DQP = L.DQP, P3 = 3 * P;
+    float* kr = reinterpret_cast<float*>(a.ws + L.off_kt);
+    float* vr = reinterpret_cast<float*>(a.ws + L.off_vt);
+    float* qr = reinterpret_cast<float*>(a.ws + L.off_ql);
+    for (int idx = tid; idx < 64 * KROW; idx += 256) {
+      const int row = idx / KROW, c = idx % KROW;
+      const int j = t * 64 + row;
+      float val = 0.f;
+      if (s_valid[row]) {
+        if (c < D) val = ld<false>(a.k, (((size_t)b * N + j) * H + h) * D + c);
+        else if (c < D + RCz) val = ld<false>(a.zr, ((size_t)b * N + j) * RCz + (c - D));
+        else if (c < D + RCz + P3) val = s_w[row][c - D - RCz];
+        else if (c == D + RCz + P3) val = s_nb[row];
+      }
+      kr[(((size_t)b * H + h) * L.NKpad + j) * KROW + c] = val;
+    }
+    for (int idx = tid; idx < 64 * DVP; idx += 256) {
+      const int row = idx / DVP, d = idx % DVP;
+      const int j = t * 64 + row;
+      float val = 0.f;
+      if (s_valid[row]) {
+        if (d < Dv) val = ld<false>(a.v, (((size_t)b * N + j) * H + h) * Dv + d);
+        else if (d < Dv + RCz) val = ld<false>(a.zr, ((size_t)b * N + j) * RCz + (d - Dv));
+        else if (d < Dv + RCz + 3 * Q) val = s_x[row][d - Dv - RCz];
+      }
+      vr[(((size_t)b * H + h) * L.NKpad + j) * DVP + d] = val;
+    }
+    for (int idx = tid; idx < 64 * DQP; idx += 256) {
+      const int row = idx / DQP, c = idx % DQP;
+      const int i = t * 64 + row;
+      float val = 0.f;
+      if (i < N) {
+        if (c < D) {
+          val = ld<false>(a.q, (((size_t)b * N + i) * H + h) * D + c) * sq;
+        } else if (c < D + RCz) {
+          const int cc = (c - D) % Cz;
+          val = ld<false>(a.wpair, (size_t)h * Cz + cc) * ld<false>(a.zl, ((size_t)b * N + i) * RCz + (c - D)) * sp;
+        }
+      }
+      qr[(((size_t)b * H + h) * L.NQpad + i) * DQP + c] = val;
+    }
+  }
+  // query global points (both paths): 16 floats per (b,h,i)
+  float* qa = reinterpret_cast<float*>(a.ws + L.off_qa);
+  for (int idx = tid; idx < 64 * 16; idx += 256) {
+    const int row = idx / 16, c = idx % 16;
+    const int i = t * 64 + row;
+    qa[(((size_t)b * H + h) * L.NQpad + i) * 16 + c] = (i < N && c < 3 * P) ? s_a[row][c] : 0.f;
+  }
+  // packed permitted-key words for every query row and this key tile:
+  // mask_i && mask_j && pair_mask_ij
+  if (a.pm != nullptr && h == 0) {
+    uint32_t* pmw = reinterpret_cast<uint32_t*>(a.ws + L.off_pm);
+    for (int i = tid; i < L.NQpad; i += 256) {
+      uint32_t w0 = 0, w1 = 0;
+      if (i < N && a.mask[(size_t)b * N + i]) {
+        const uint8_t* row = a.pm + ((size_t)b * N + i) * N + (size_t)t * 64;
+        for (int jj = 0; jj < 64; ++jj) {
+          if (t * 64 + jj >= N) break;
+          if (s_valid[jj] && row[jj]) {
+            int hf;
+            const int bit = mask_bit_of_key(jj, &hf);
+            if (hf) w1 |= 1u << bit; else w0 |= 1u << bit;
+          }
+        }
+      }
+      pmw[(((size_t)b * L.NQpad + i) * L.NT + t) * 2] = w0;
+      pmw[(((size_t)b * L.NQpad + i) * L.NT + t) * 2 + 1] = w1;
+    }
+  }
+}
+
+hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStream_t st) {
+  LiftArgs a;
+  a.L = L;
+  a.q = in->q; a.k = in->k; a.v = in->v;
+  a.qp = in->q_points; a.kp = in->k_points; a.vp = in->v_points;
+  a.rot = in->rotation; a.trans = in->translation; a.pwr = in->point_weight_raw;
+  a.wpair = in->w_pair; a.zl = in->zl; a.zr = in->zr;
+  a.mask = in->mask; a.pm = in->pair_mask;
+  a.ws = reinterpret_cast<char*>(ws);
+  dim3 grid(L.NT, L.H, L.B);
+  if (L.mfma)
+    hipLaunchKernelGGL(lift_kernel<true>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(lift_kernel<false>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fipa

@@ -1,0 +1,111 @@
+"""C-ABI library: loads, exports what include/flashipa.h declares, and the
+host-side argument validation (runs without a GPU: invalid arguments are
+rejected before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rna_structure_amd import _lib
+from rna_structure_amd.synth import IPAShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashipa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from rna_structure_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ipa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("ipa_lift", "ipa_flash_fwd", "ipa_epilogue"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ipa_version().startswith(b"flashipa")
+    for code in range(7):
+        assert lib.ipa_status_string(code)
+    assert lib.ipa_status_string(99) == b"unknown status"
+
+
+def test_struct_sizes_match_c():
+    assert ctypes.sizeof(_lib.IpaShape) == 88
+    assert ctypes.sizeof(_lib.IpaLiftIn) == 14 * 8
+    assert ctypes.sizeof(_lib.IpaEpiIn) == 5 * 8
+
+
+def _shape(**kw):
+    base = dict(B=2, N=300, H=8, D=16, Dv=16, P=4, Q=8, Cz=64, R=2, Cout=128, dtype="bf16")
+    base.update(kw)
+    return _lib.make_shape(IPAShape(**base))
+
+
+def test_lifted_bytes_linear_in_n_without_pair_mask(lib):
+    b1 = _lib.lifted_bytes(_shape(N=4096, B=1), False)
+    b2 = _lib.lifted_bytes(_shape(N=8192, B=1), False)
+    assert b1 > 0 and 1.9 < b2 / b1 < 2.1
+    with_pm = _lib.lifted_bytes(_shape(N=4096, B=1), True)
+    assert with_pm - b1 >= 4096 * 64 * 8
+
+
+def test_lifted_bytes_rejects(lib):
+    assert _lib.lifted_bytes(_shape(N=0), False) == 0
+    assert _lib.lifted_bytes(_shape(H=-1), False) == 0
+    assert _lib.lifted_bytes(_shape(P=6), False) == 0          # beyond compiled point columns
+    assert _lib.lifted_bytes(_shape(Cz=200), False) == 0       # beyond the widest mfma instance
+    s = _shape()
+    s.dtype = 7
+    assert _lib.lifted_bytes(s, False) == 0
+    assert _lib.lifted_bytes(_shape(dtype="f32"), False) > 0
+
+
+def test_o_width(lib):
+    assert _lib.o_width(_shape()) == 16 + 2 * 64 + 3 * 8
+
+
+def test_validation_before_launch(lib):
+    s = _shape()
+    li = _lib.IpaLiftIn()
+    # NULL arguments
+    assert lib.ipa_lift(None, ctypes.byref(li), 256, 1 << 30, None) == 1
+    assert lib.ipa_lift(ctypes.byref(s), ctypes.byref(li), 256, 1 << 30, None) == 1
+    # misaligned pointers (never dereferenced: validation fails first)
+    fields = [n for n, _ in _lib.IpaLiftIn._fields_ if n != "pair_mask"]
+    li2 = _lib.IpaLiftIn(**{n: 4096 for n in fields})
+    li2.q = 4100
+    assert lib.ipa_lift(ctypes.byref(s), ctypes.byref(li2), 4096, 1 << 40, None) == 4
+    # workspace too small
+    li3 = _lib.IpaLiftIn(**{n: 4096 for n in fields})
+    assert lib.ipa_lift(ctypes.byref(s), ctypes.byref(li3), 4096, 16, None) == 2
+    # shape errors
+    bad = _shape(N=0)
+    assert lib.ipa_lift(ctypes.byref(bad), ctypes.byref(li3), 4096, 1 << 40, None) == 2
+    eps0 = _shape()
+    eps0.eps = 0.0
+    assert lib.ipa_flash_fwd(ctypes.byref(eps0), 4096, 4096, 4096, None) == 2
+    assert lib.ipa_flash_fwd(ctypes.byref(_shape(P=9)), 4096, 4096, 4096, None) == 3
+    assert lib.ipa_flash_fwd(ctypes.byref(s), None, 4096, 4096, None) == 1
+    assert lib.ipa_flash_fwd(ctypes.byref(s), 4096, 4100, 4096, None) == 4
+    ei = _lib.IpaEpiIn(4096, 4096, 4096, 4096, None)
+    assert lib.ipa_epilogue(ctypes.byref(s), 4096, 4096, ctypes.byref(ei), 4096, 4096, None) == 1
+    assert lib.ipa_logit_rows(ctypes.byref(s), 4096, 5, 0, 0, 1, 4096, None) == 2   # b out of range
+    assert lib.ipa_logit_rows(ctypes.byref(s), 4096, 0, 0, 299, 2, 4096, None) == 2  # rows past N

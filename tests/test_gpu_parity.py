@@ -1,0 +1,158 @@
+"""GPU parity: the HIP path against the float64 CPU oracle on the same seeded
+inputs.  Tolerance (max |gpu - ref| / max |ref| per output tensor): 1e-4 for
+the fp32 path, 2e-2 for the bf16 matrix-core path; attention rows sum to
+1 +- 1e-5."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import ipa_factored
+from rna_structure_amd.synth import IPAShape, make_config, make_inputs
+
+from gpu_helpers import compare, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _case(name, shape, seed, **kw):
+    return pytest.param(shape, seed, kw, id=name)
+
+
+SMALL = [
+    _case("tiny-f32", IPAShape(B=1, N=16, H=4, Cz=16, dtype="f32"), 1016,
+          frames="gauss", trans_sigma=10.0, masked_keys=(5,)),
+    _case("ragged-bf16", IPAShape(B=2, N=200, H=4), 7, frames="walk", step=3.8, lengths=(100, 200),
+          pair_dropout=0.1, empty_row=True),
+    _case("ragged-f32", IPAShape(B=2, N=200, H=4, dtype="f32"), 8, frames="walk", step=3.8, lengths=(100, 200),
+          pair_dropout=0.1, empty_row=True),
+    _case("one-residue-bf16", IPAShape(B=3, N=1, H=2), 9, frames="gauss"),
+    _case("one-residue-f32", IPAShape(B=3, N=1, H=2, dtype="f32"), 9, frames="gauss"),
+    _case("n64-bf16", IPAShape(B=1, N=64, H=3), 10, frames="walk", step=3.8),
+    _case("n65-bf16", IPAShape(B=1, N=65, H=3), 11, frames="walk", step=3.8, masked_keys=(64,)),
+    _case("n129-f32", IPAShape(B=2, N=129, H=2, dtype="f32"), 12, frames="gauss", trans_sigma=20.0),
+    _case("small-dims-bf16", IPAShape(B=2, N=70, H=3, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6), 13, frames="gauss"),
+    _case("small-dims-f32", IPAShape(B=2, N=70, H=3, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6, dtype="f32"), 13,
+          frames="gauss"),
+    _case("mid-instance-bf16", IPAShape(B=1, N=150, H=2, D=16, Dv=16, P=4, Q=8, Cz=32, R=2), 14, frames="walk"),
+    _case("rank1-p5-q9-bf16", IPAShape(B=1, N=100, H=2, D=8, Dv=8, P=5, Q=9, Cz=48, R=1, Cout=64), 15,
+          frames="walk"),
+]
+
+
+@pytest.mark.parametrize("shape,seed,kw", SMALL)
+def test_parity_small(shape, seed, kw):
+    say(f"case {shape} seed={seed}")
+    inp = make_inputs(shape, seed, **kw)
+    _, _, gpu = run_gpu(inp)
+    compare(inp, gpu, tol=TOL[shape.dtype])
+
+
+def test_all_masked_batch_is_zero():
+    s = IPAShape(B=2, N=90, H=2)
+    inp = make_inputs(s, 21, frames="walk")
+    inp["mask"][1, :] = False
+    say("case all-masked sample")
+    _, _, gpu = run_gpu(inp)
+    assert np.all(gpu["update"][1] == 0) and np.all(gpu["local_points"][1] == 0)
+    assert np.all(np.isneginf(gpu["lse"][1]))
+    compare(inp, gpu, tol=TOL["bf16"])
+
+
+def _sample_rows(N, k, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, size=min(k, N), replace=False).tolist()) | {0, N - 1} | set(extra)
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+@pytest.mark.parametrize("name", ["tiny", "protein"])
+def test_parity_configs_full(name):
+    inp = make_config(name)
+    say(f"config {name} {inp['shape']}")
+    _, _, gpu = run_gpu(inp)
+    compare(inp, gpu, tol=TOL[inp["shape"].dtype])
+
+
+def test_parity_rna_sampled():
+    inp = make_config("rna")
+    say(f"config rna {inp['shape']}")
+    _, _, gpu = run_gpu(inp)
+    compare(inp, gpu, rows=_sample_rows(2048, 48, 1), tol=TOL["bf16"])
+
+
+def test_parity_short_batch_sampled():
+    inp = make_config("short_batch")
+    L0 = int(inp["mask"][0].sum())
+    say(f"config short_batch {inp['shape']} empty row {L0 // 2}")
+    _, _, gpu = run_gpu(inp)
+    compare(inp, gpu, rows=_sample_rows(512, 24, 2, extra=(L0 // 2, L0 - 1, L0)), tol=TOL["bf16"])
+
+
+@pytest.mark.parametrize("n", [4096, 8192, 16384, 32768])
+def test_parity_sweep_sampled(n):
+    inp = make_config(f"sweep_{n}")
+    say(f"config sweep N={n}")
+    _, _, gpu = run_gpu(inp)
+    compare(inp, gpu, rows=_sample_rows(n, 6, 3, extra=(n // 2, n - 64, 63, 64)), tol=TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_rows_sum_to_one(dtype):
+    """Attention rows a_ij = exp(L_ij - lse_i), from the logits the kernel uses and
+    the kernel's log-sum-exp: they match the oracle's attention and sum to 1."""
+    import torch
+    s = IPAShape(B=2, N=300, H=3, dtype=dtype)
+    inp = make_inputs(s, 31, frames="walk", step=3.8, lengths=(200, 300), pair_dropout=0.05, empty_row=True)
+    say(f"case attention rows {dtype}")
+    f, _, gpu = run_gpu(inp)
+    rows = np.array([0, 7, 63, 64, 150, 199])
+    ref = ipa_factored(inp, rows=rows, keep=("attention", "logits", "lse", "empty"))
+    tol = TOL[dtype]
+    for b in range(2):
+        for h in range(3):
+            L = f.logit_rows(b, h, int(rows[0]), int(rows[-1] - rows[0] + 1)).cpu().numpy().astype(np.float64)
+            L = L[rows - rows[0]]
+            lse = gpu["lse"][b, h, rows]
+            for k, i in enumerate(rows):
+                if ref["empty"][b, k]:
+                    assert np.isneginf(lse[k]) and np.all(np.isneginf(L[k]))
+                    continue
+                a = np.exp(L[k] - lse[k])
+                assert abs(a.sum() - 1.0) <= 1e-5, (b, h, i, a.sum())
+                ra = ref["attention"][b, h, k]
+                assert np.max(np.abs(a - ra)) <= tol * max(np.max(ra), 1e-30) + 1e-7, (b, h, i)
+                perm = np.isfinite(L[k])
+                lr = ref["logits"][b, h, k][perm]
+                assert np.max(np.abs(L[k][perm] - lr)) <= (5e-2 if dtype == "bf16" else 1e-4) * max(1.0, np.abs(lr).max())
+
+
+def test_deterministic():
+    inp = make_config("protein")
+    say("case determinism")
+    _, _, g1 = run_gpu(inp)
+    _, _, g2 = run_gpu(inp)
+    for k in ("update", "local_points", "o", "lse"):
+        assert np.array_equal(g1[k], g2[k], equal_nan=True), k
+
+
+def test_rigid_invariance_gpu_f32():
+    s = IPAShape(B=1, N=150, H=4, dtype="f32")
+    inp = make_inputs(s, 41, frames="walk", step=3.8)
+    say("case invariance f32")
+    _, _, g1 = run_gpu(inp)
+    rng = np.random.default_rng(5)
+    qt = rng.standard_normal(4)
+    qt /= np.linalg.norm(qt)
+    w, x, y, z = qt
+    G = np.array([[1 - 2 * (y * y + z * z), 2 * (x * y - z * w), 2 * (x * z + y * w)],
+                  [2 * (x * y + z * w), 1 - 2 * (x * x + z * z), 2 * (y * z - x * w)],
+                  [2 * (x * z - y * w), 2 * (y * z + x * w), 1 - 2 * (x * x + y * y)]])
+    moved = dict(inp)
+    moved["rotation"] = np.einsum("xy,bnyz->bnxz", G, inp["rotation"]).astype(np.float32).astype(np.float64)
+    moved["translation"] = (np.einsum("xy,bny->bnx", G, inp["translation"]) + 100.0).astype(np.float32).astype(np.float64)
+    _, _, g2 = run_gpu(moved)
+    for k in ("update", "local_points"):
+        err = np.max(np.abs(g1[k] - g2[k])) / np.max(np.abs(g1[k]))
+        assert err <= 1e-4, (k, err)
