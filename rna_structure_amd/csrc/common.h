@@ -16,27 +16,35 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Key tile: 64 keys.  Query tile of the matrix-core kernel: 4 waves x 32.
 constexpr int kKeyTile = 64;
 constexpr int kQueryTile = 128;
-// Geometric columns of a lifted key row on the matrix-core path: 3 MFMA
-// K-steps of 16.  Fixed positions for up to 5 points (15 coordinates):
-//   [w_hi (15) | w_lo (15) | w_hi (15) | nb_hi | nb_lo | 0]
-// against the query's [u_hi | u_hi | u_lo | kNormScale | kNormScale | 0],
-// where w = b - c and u = 2 gamma log2(e) (a - c) are split into fp16
-// high and low parts and nb = -gamma log2(e) |b - c|^2 / kNormScale.
-constexpr int kGeoCols = 48;
-constexpr int kGeoW = 15;
-// The squared-norm column of a key is stored divided by this power of two
-// (and the matching query column holds it), extending its fp16 range.
+// Geometric columns of a lifted key row on the matrix-core path: GS MFMA
+// K-steps of 16 (GS = 3 for P <= 4, 4 for P = 5).  With c_t the centroid of
+// key tile t and c_w the centroid of the queries of one wavefront (both on a
+// 4-angstrom grid, so delta = c_t - c_w is exact in fp16), A = a - c_w and
+// w = b - c_t, the point term of the logit (log2 units, gl = gamma log2 e) is
+//   -gl sum_p |a_p - b_p|^2 = 2 gl A.w  - gl |w|^2  - 2 gl delta.W  + t'
+// with W = sum_p w_p and t' = -gl sum_p |a_p - c_t|^2 (per query and tile).
+// Columns 0 .. 16(GS-1)+3 hold the 9P cross products of the fp16 hi/lo
+// splits (u = 2 gl A against w): pairs [u_hi.w_hi | u_hi.w_lo | u_lo.w_hi].
+// The last K-step holds, with base = 16(GS-1) (query value x key value):
+//   base+4:  16 x nb_hi      base+12: 16 x nb_lo     (nb = -gl|w|^2 / 16)
+//   base+5..7: -delta x WW_hi  base+13..15: -delta x WW_lo  (WW = 2 gl W)
+//   base+9..11: t'/16 in three fp16 parts x 16
+// so that the MFMA itself returns the complete logit.
+constexpr int kCentGrid = 4;  // angstrom
 constexpr float kNormScale = 16.0f;
+__host__ __device__ __forceinline__ int geo_steps(int P) { return P <= 4 ? 3 : 4; }
+
 // Padding (in 16-bit elements) appended to every LDS row so that the
 // 16-byte fragment reads of 16 consecutive rows hit distinct banks.
 constexpr int kRowPad = 8;
 constexpr int kVCols = kKeyTile + kRowPad;  // 72 elements = 144 bytes
 constexpr uint32_t kMagic = 0x46495041u;    // "FIPA"
 
-// Matrix-core kernel instances: (NQS, NVB) = number of 16-wide bf16 K-steps
-// of the scalar+pair query columns, number of 32-row bf16 value blocks.
+// Matrix-core kernel instances: (NQS, NVB, GS) = number of 16-wide bf16
+// K-steps of the scalar+pair query columns, number of 32-row bf16 value
+// blocks, number of fp16 geometric K-steps.
 struct MfmaDims {
-  int NQS, NVB;
+  int NQS, NVB, GS;
 };
 
 // Workspace header, first 256 bytes of the lifted buffer.
@@ -54,9 +62,9 @@ struct Layout {
   int NKpad; // NT*64 key rows
   int NQpad; // query rows rounded up to 128
   int mfma;  // 1: matrix-core path (bf16 input), 0: fp32 path
-  int NQS, NVB;
+  int NQS, NVB, GS;
   int QW;     // query scalar+pair width (elements)
-  int KROW;   // elements per key row (mfma: QW + 48 + pad; fp32: DKP)
+  int KROW;   // elements per key row (mfma: QW + 16 GS + pad; fp32: DKP)
   int VROWS;  // mfma: rows of the transposed value tile; fp32: DVP (row stride)
   int DQP;    // fp32 path: padded query row width
   int DO;     // attention output width Dv + R*Cz + 3Q
@@ -70,12 +78,13 @@ static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 // Choose the smallest compiled matrix-core instance that holds the shape.
 // Returns false when none does.
 static inline bool pick_mfma_dims(int D, int Dv, int RCz, int P, int Q, MfmaDims* out) {
-  static const MfmaDims inst[] = {{3, 2}, {5, 3}, {9, 5}};
+  static const MfmaDims inst[] = {{3, 2, 0}, {5, 3, 0}, {9, 5, 0}};
   if (P > 5) return false;
   if (3 * Q + 4 > 32) return false;
   for (const MfmaDims& m : inst) {
     if (D + RCz <= 16 * m.NQS && Dv + RCz + 1 <= 32 * m.NVB) {
       *out = m;
+      out->GS = geo_steps(P);
       return true;
     }
   }
@@ -108,15 +117,15 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
     MfmaDims md;
     if (!pick_mfma_dims(L->D, L->Dv, L->RCz, L->P, L->Q, &md)) return false;
     L->mfma = 1;
-    L->NQS = md.NQS; L->NVB = md.NVB;
+    L->NQS = md.NQS; L->NVB = md.NVB; L->GS = md.GS;
     L->QW = 16 * md.NQS;
-    L->KROW = L->QW + kGeoCols + kRowPad;
+    L->KROW = L->QW + 16 * md.GS + kRowPad;
     L->VROWS = 32 * (md.NVB + 1);
     L->DQP = L->QW;
   } else if (s->dtype == IPA_F32) {
     if (L->D + L->RCz > kF32MaxDQ || L->DO > kF32MaxDV) return false;
     L->mfma = 0;
-    L->NQS = L->NVB = 0;
+    L->NQS = L->NVB = L->GS = 0;
     L->DQP = round_up(L->D + L->RCz, 4);
     L->QW = L->DQP;
     L->KROW = round_up(L->D + L->RCz + 3 * L->P + 1, 4);

@@ -1,8 +1,8 @@
 // Diagnostic kernel (tests only): the logits the fused kernel forms, for a
 // few query rows, in natural-log units, -inf where the key is not permitted.
 // The matrix-core variant runs the fused kernel's own MFMA fragment sequence
-// (mfma_tile.h) on the same lifted operands, so its logits are bit-identical
-// to the ones the fused kernel exponentiates; together with the fused
+// (mfma_tile.h) on the same lifted operands and the same query grouping, so
+// its logits are bit-identical to the ones the fused kernel exponentiates; together with the fused
 // kernel's log-sum-exp they give the attention rows exp(L - lse).  The fp32
 // variant repeats the fp32 kernel's expression order.
 #include "mfma_tile.h"
@@ -16,15 +16,18 @@ struct DiagArgs {
   float* out;
 };
 
-template <int NQS>
+// One wavefront per aligned group of 32 query rows (the grouping of the
+// fused kernel's wavefronts, which sets the query centroid), all key tiles.
+template <int NQS, int GS>
 __global__ __launch_bounds__(64) void logit_rows_mfma_kernel(DiagArgs a) {
   constexpr int QW = 16 * NQS;
-  constexpr int KROW = QW + kGeoCols + kRowPad;
+  constexpr int KROW = QW + 16 * GS + kRowPad;
   const Layout& L = a.L;
   const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
   const int b = a.b, h = a.h, N = L.N, H = L.H, NT = L.NT;
-  const int i = a.row0 + blockIdx.x * 32 + l32;
-  const bool qin = i < N && i < a.row0 + a.nrows;
+  const int i = (a.row0 / 32 + (int)blockIdx.x) * 32 + l32;
+  const bool qin = i < N;
+  const bool out_row = qin && i >= a.row0 && i < a.row0 + a.nrows;
   const Header* hd = reinterpret_cast<const Header*>(a.ws);
   const bool has_pm = hd->has_pair_mask != 0;
   const float gl = reinterpret_cast<const float*>(a.ws + L.off_gam)[h] * kLog2e;
@@ -32,27 +35,28 @@ __global__ __launch_bounds__(64) void logit_rows_mfma_kernel(DiagArgs a) {
   bf16x8_t bq[NQS];
   load_q_frag<NQS>(reinterpret_cast<const uint4*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + i) * (QW / 8),
                    qin, half, bq);
-  float av[15];
-  load_qa(reinterpret_cast<const float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + i) * 4, qin, av);
   const bool qvalid = query_valid(L, a.ws, b, i, qin);
+  f16x8_t bg[GS];
+  QueryGeo qg;
+  {
+    float av[15];
+    load_qa(reinterpret_cast<const float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + i) * 4, qin, av);
+    build_geo<GS>(L.P, av, qvalid, gl, half, bg, &qg);
+  }
   const char* kt0 = a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)(64 * KROW * 2);
   for (int t = 0; t < NT; ++t) {
     const uint32_t mw = perm_word(L, a.ws, has_pm, b, i, qin, qvalid, t, half);
-    f16x8_t bg[3];
-    float na;
-    geo_frag(av, ck[(size_t)b * NT + t], gl, 3 * L.P, half, bg, &na);
+    geo_tile<GS>(qg, ck[(size_t)b * NT + t], gl, (float)L.P, half, bg);
     f32x16_t sacc[2];
-    s_tile<NQS>(kt0 + (size_t)t * 64 * KROW * 2, bq, bg, l32, half, sacc);
-    if (!qin) continue;
+    s_tile<NQS, GS>(kt0 + (size_t)t * 64 * KROW * 2, bq, bg, l32, half, sacc);
+    if (!out_row) continue;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = t * 64 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (j < N) {
-          const float s = sacc[kb][r] - na;
-          a.out[(size_t)(i - a.row0) * N + j] = ((mw >> (kb * 16 + r)) & 1u) ? s * kLn2 : -INFINITY;
-        }
+        if (j < N)
+          a.out[(size_t)(i - a.row0) * N + j] = ((mw >> (kb * 16 + r)) & 1u) ? sacc[kb][r] * kLn2 : -INFINITY;
       }
   }
 }
@@ -92,9 +96,10 @@ __global__ __launch_bounds__(256) void logit_rows_f32_kernel(DiagArgs a) {
   *outp = s * kLn2;
 }
 
-template <int NQS>
+template <int NQS, int GS>
 static void launch_m(const DiagArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(logit_rows_mfma_kernel<NQS>, dim3((a.nrows + 31) / 32), dim3(64), 0, st, a);
+  const int groups = (a.row0 + a.nrows - 1) / 32 - a.row0 / 32 + 1;
+  hipLaunchKernelGGL((logit_rows_mfma_kernel<NQS, GS>), dim3(groups), dim3(64), 0, st, a);
 }
 
 hipError_t launch_logit_rows(const Layout& L, const void* ws, int b, int h, int row0, int nrows, float* out,
@@ -104,9 +109,12 @@ hipError_t launch_logit_rows(const Layout& L, const void* ws, int b, int h, int 
   a.ws = reinterpret_cast<const char*>(ws);
   a.b = b; a.h = h; a.row0 = row0; a.nrows = nrows; a.out = out;
   if (L.mfma) {
-    if (L.NQS == 3) launch_m<3>(a, st);
-    else if (L.NQS == 5) launch_m<5>(a, st);
-    else if (L.NQS == 9) launch_m<9>(a, st);
+    if (L.GS == 3 && L.NQS == 3) launch_m<3, 3>(a, st);
+    else if (L.GS == 3 && L.NQS == 5) launch_m<5, 3>(a, st);
+    else if (L.GS == 3 && L.NQS == 9) launch_m<9, 3>(a, st);
+    else if (L.GS == 4 && L.NQS == 3) launch_m<3, 4>(a, st);
+    else if (L.GS == 4 && L.NQS == 5) launch_m<5, 4>(a, st);
+    else if (L.GS == 4 && L.NQS == 9) launch_m<9, 4>(a, st);
     else return hipErrorInvalidValue;
   } else {
     dim3 grid((L.N + 255) / 256, nrows);

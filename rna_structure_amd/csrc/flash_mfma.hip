@@ -7,9 +7,11 @@
 //                                         scalar + pair columns,
 //                                         v_mfma_f32_32x32x16_f16 over the
 //                                         centred point columns (fp16 hi/lo
-//                                         split: 3 products per coordinate)
-//   s = S - gamma log2e |a_i - c_t|^2     (row term of the expanded distance)
-//   masked online softmax in fp32 with exp2 (logits carry a log2 e factor),
+//                                         split: 3 products per coordinate,
+//                                         plus the tile offset and row terms,
+//                                         see common.h), so S is the complete
+//                                         logit times log2 e
+//   masked online softmax in fp32 with exp2,
 //   a running maximum that is only raised when it grows by more than 8
 //   (probabilities stay below 2^8) and an fp32 row sum for the log-sum-exp
 //   O^T += V~^T P^T                       bf16 probabilities against the
@@ -23,6 +25,9 @@
 // Normalisation uses the ones rows, i.e. the sums of the rounded
 // probabilities actually multiplied into O, so the weights applied to the
 // values sum to one to fp32 rounding and the centroid cancels exactly.
+// Key and value tiles are copied global -> LDS with direct-to-LDS loads; the
+// next key tile is fetched while the softmax and value product of the current
+// tile run, the next value tile while the next key product runs.
 #include "mfma_tile.h"
 
 namespace fipa {
@@ -44,46 +49,73 @@ __device__ __forceinline__ float pick16(const V& acc, int r) {
   return v;
 }
 
-template <int NQS, int NVB>
-__global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
+// Uniform read-only data (per-tile centroids, key-mask words, point
+// weights) is read through the constant address space so that it goes
+// through scalar loads and never adds to the vector-memory counter that the
+// tile copies below are synchronised with.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return *(const __attribute__((address_space(4))) T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float4 ld_uniform4(const float4* p) {
+  const float* f = reinterpret_cast<const float*>(p);
+  return make_float4(ld_uniform(f), ld_uniform(f + 1), ld_uniform(f + 2), ld_uniform(f + 3));
+}
+
+// Number of direct-to-LDS copy instructions each of the 4 wavefronts issues
+// for a tile of BYTES bytes (1 KiB per instruction).
+template <int BYTES>
+constexpr int dma_per_wave() { return ((BYTES + 1023) / 1024 + 3) / 4; }
+
+// Copy a tile (BYTES, a multiple of 16) global -> LDS with
+// global_load_lds_dwordx4: lane l of a wavefront moves bytes 16l .. 16l+15 of
+// one KiB chunk to M0 + 16l.  Every wavefront issues the same number of
+// instructions (dma_per_wave) so that the vmcnt waits below are
+// compile-time constants; a wavefront with fewer chunks repeats its last one
+// (same bytes to the same place).  The copies are issued from inline
+// assembly: the compiler does not track them, and the kernel waits for them
+// explicitly (vmcnt) before the barrier that precedes the LDS reads.
+template <int BYTES>
+__device__ __forceinline__ void dma_tile(const char* g, const char* s, int w, int lane) {
+  constexpr int nch = (BYTES + 1023) / 1024;
+  const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(s);
+#pragma unroll
+  for (int k = 0; k < dma_per_wave<BYTES>(); ++k) {
+    int ch = w + 4 * k;
+    ch = ch < nch ? ch : nch - 1;
+    const uint32_t off = (uint32_t)ch * 1024u + (uint32_t)lane * 16u;
+    const uint32_t voff = off < (uint32_t)BYTES ? off : (uint32_t)(BYTES - 16);
+    const uint32_t m0 = lbase + (uint32_t)ch * 1024u;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(g), "s"(m0)
+                 : "memory", "m0");
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Main loop over the key tiles and the final normalisation for one
+// wavefront's 32 queries; PM selects the per-query pair-mask words (a vector
+// load per tile) over the per-tile key-mask words (scalar loads).
+template <int NQS, int NVB, int GS, bool PM>
+__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* sv, int b, int h, int i, bool qin,
+                                       bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
+                                       const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
   constexpr int QW = 16 * NQS;
-  constexpr int KROW = QW + kGeoCols + kRowPad;
+  constexpr int KROW = QW + 16 * GS + kRowPad;
   constexpr int KT_BYTES = 64 * KROW * 2;
   constexpr int VROWS = 32 * (NVB + 1);
   constexpr int VT_BYTES = VROWS * kVCols * 2;
-  __shared__ __attribute__((aligned(16))) char smem[KT_BYTES + VT_BYTES];
-
   const Layout& L = a.L;
   const int N = L.N, H = L.H, NT = L.NT;
-  // Consecutive workgroup ids go round-robin over the 8 XCDs; remap so each
-  // XCD works through a contiguous range of (b, h, query tile), keeping the
-  // key/value tiles of a head in one L2.
-  const int wg = blockIdx.x;
-  int logical = wg;
-  if ((a.nwg & 7) == 0) logical = (wg & 7) * (a.nwg >> 3) + (wg >> 3);
-  const int qt = logical % a.qtiles;
-  const int bh = logical / a.qtiles;
-  const int h = bh % H, b = bh / H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, half = lane >> 5;
-  const int i = qt * kQueryTile + w * 32 + l32;
-  const bool qin = i < N;
-
-  const Header* hd = reinterpret_cast<const Header*>(a.ws);
-  const bool has_pm = hd->has_pair_mask != 0;
-  const float gl = reinterpret_cast<const float*>(a.ws + L.off_gam)[h] * kLog2e;
+  const bool has_pm = PM;
   const uint32_t* km = reinterpret_cast<const uint32_t*>(a.ws + L.off_km);
   const float4* ck = reinterpret_cast<const float4*>(a.ws + L.off_ck);
-
-  // query operand (B of S^T): lane holds query l32, columns half*8 .. +7 of each K-step
-  bf16x8_t bq[NQS];
-  load_q_frag<NQS>(reinterpret_cast<const uint4*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + i) * (QW / 8),
-                   qin, half, bq);
-  float av[15];
-  load_qa(reinterpret_cast<const float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + i) * 4, qin, av);
-  const int P3 = 3 * L.P;
-  const bool qvalid = query_valid(L, a.ws, b, i, qin);
-
   f32x16_t oacc[NVB + 1];
 #pragma unroll
   for (int vb = 0; vb <= NVB; ++vb) oacc[vb] = f32x16_t{};
@@ -91,34 +123,45 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
 
   const char* ktg0 = a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)KT_BYTES;
   const char* vtg0 = a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES;
+  const uint32_t* kmb = km + (size_t)b * NT * 2;
+  auto next_tile = [&](int t) {
+    for (++t; t < NT; ++t)
+      if ((ld_uniform(kmb + 2 * t) | ld_uniform(kmb + 2 * t + 1)) != 0u) break;  // skip tiles without a valid key
+    return __builtin_amdgcn_readfirstlane(t);
+  };
+  constexpr int kDK = dma_per_wave<KT_BYTES>(), kDV = dma_per_wave<VT_BYTES>();
 
-  for (int t = 0; t < NT; ++t) {
-    const uint32_t k0 = km[((size_t)b * NT + t) * 2], k1 = km[((size_t)b * NT + t) * 2 + 1];
-    if ((k0 | k1) == 0u) continue;  // no valid key in this tile (uniform)
-    const uint32_t mw = perm_word(L, a.ws, has_pm, b, i, qin, qvalid, t, half);
-
-    __syncthreads();
-    {
-      const uint4* kg = reinterpret_cast<const uint4*>(ktg0 + (size_t)t * KT_BYTES);
-      const uint4* vg = reinterpret_cast<const uint4*>(vtg0 + (size_t)t * VT_BYTES);
-      uint4* s4 = reinterpret_cast<uint4*>(smem);
-      for (int c = tid; c < KT_BYTES / 16; c += 256) s4[c] = kg[c];
-      for (int c = tid; c < VT_BYTES / 16; c += 256) s4[KT_BYTES / 16 + c] = vg[c];
+  int t = next_tile(-1);
+  if (t < NT) {
+    dma_tile<KT_BYTES>(ktg0 + (size_t)t * KT_BYTES, sk, w, lane);
+    dma_tile<VT_BYTES>(vtg0 + (size_t)t * VT_BYTES, sv, w, lane);
+  }
+  while (t < NT) {
+    const int tn = next_tile(t);
+    uint32_t mw;
+    if constexpr (PM) {
+      mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
+    } else {
+      const uint32_t k0 = ld_uniform(kmb + 2 * t), k1 = ld_uniform(kmb + 2 * t + 1);
+      mw = qvalid ? (half ? k1 : k0) : 0u;
     }
-    __syncthreads();
+    geo_tile<GS>(qg, ld_uniform4(ck + (size_t)b * NT + t), gl, Pf, half, bg);
 
-    // query geometric operand for this key tile (centroid c_t), then S^T = K~ Q~^T
-    f16x8_t bg[3];
-    float na;
-    geo_frag(av, ck[(size_t)b * NT + t], gl, P3, half, bg, &na);
+    // key tile t in LDS: this wave's copies are done once only the value-tile
+    // copies issued after them may still be in flight; then all waves' are
+    if (has_pm) wait_vmcnt<0>(); else wait_vmcnt<kDV>();
+    __syncthreads();
     f32x16_t sacc[2];
-    s_tile<NQS>(smem, bq, bg, l32, half, sacc);
+    s_tile<NQS, GS>(sk, bq, bg, l32, half, sacc);
+    asm volatile("" ::"v"(mw));  // the mask word is in registers before the next copies are issued
+    __syncthreads();  // every wave has read key tile t
+    if (tn < NT) dma_tile<KT_BYTES>(ktg0 + (size_t)tn * KT_BYTES, sk, w, lane);
 
     float s[32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb * 16 + r] = sacc[kb][r] - na;
+      for (int r = 0; r < 16; ++r) s[kb * 16 + r] = sacc[kb][r];
     if (!__all(mw == 0xFFFFFFFFu)) {
 #pragma unroll
       for (int x = 0; x < 32; ++x) s[x] = ((mw >> x) & 1u) ? s[x] : -INFINITY;
@@ -128,6 +171,8 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
     for (int x = 1; x < 32; ++x) mt = fmaxf(mt, s[x]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mnew = fmaxf(m, mt);
+    // raise the running maximum only when it grows by more than 8 (log2
+    // units): probabilities stay below 2^8, rescaling is rare
     if (__any(mnew > m + 8.0f)) {
       const float alpha = (mnew > m) ? exp2f(m - mnew) : 1.0f;
 #pragma unroll
@@ -140,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
     float ps = 0.f;
 #pragma unroll
     for (int x = 0; x < 32; ++x) {
-      p[x] = exp2f(s[x] - mu);
+      p[x] = __builtin_amdgcn_exp2f(s[x] - mu);
       ps += p[x];
     }
     l += ps;
@@ -155,27 +200,25 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
         ph[ks][e] = (_Float16)v;
       }
 
-    // O^T += V~^T P^T
-    const char* vbase = smem + KT_BYTES;
+    // value tile t in LDS: only the next key tile's copies may be in flight
+    if (has_pm || tn >= NT) wait_vmcnt<0>(); else wait_vmcnt<kDK>();
+    __syncthreads();
+    // O^T += V~^T P^T, value blocks interleaved so consecutive MFMAs are independent
+    const char* vrow = sv + (size_t)(l32 * kVCols) * 2 + half * 16;
 #pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      const char* vrow = vbase + (size_t)((vb * 32 + l32) * kVCols) * 2;
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(vrow + (ks * 16 + half * 8) * 2);
+      for (int vb = 0; vb < NVB; ++vb) {
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(vrow + (size_t)(vb * 32 * kVCols) * 2 + ks * 32);
         oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[ks], oacc[vb], 0, 0, 0);
       }
+      const f16x8_t af = *reinterpret_cast<const f16x8_t*>(vrow + (size_t)(NVB * 32 * kVCols) * 2 + ks * 32);
+      oacc[NVB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, ph[ks], oacc[NVB], 0, 0, 0);
     }
-    {
-      const char* vrow = vbase + (size_t)((NVB * 32 + l32) * kVCols) * 2;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f16x8_t af = *reinterpret_cast<const f16x8_t*>(vrow + (ks * 16 + half * 8) * 2);
-        oacc[NVB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, ph[ks], oacc[NVB], 0, 0, 0);
-      }
-    }
+    __syncthreads();  // every wave has read value tile t
+    if (tn < NT) dma_tile<VT_BYTES>(vtg0 + (size_t)tn * VT_BYTES, sv, w, lane);
+    t = tn;
   }
-
   // ---- finalise
   const float ltot = l + __shfl_xor(l, 32);
   const bool nonempty = qvalid && ltot > 0.f;
@@ -228,7 +271,59 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
   }
 }
 
-template <int NQS, int NVB>
+template <int NQS, int NVB, int GS>
+__global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
+  constexpr int QW = 16 * NQS;
+  constexpr int KROW = QW + 16 * GS + kRowPad;
+  constexpr int KT_BYTES = 64 * KROW * 2;
+  constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
+  // rounded up to whole KiB: the last copy chunk of a tile may be partial and
+  // its upper lanes then land in this padding
+  __shared__ __attribute__((aligned(1024))) char sk[(KT_BYTES + 1023) / 1024 * 1024];
+  __shared__ __attribute__((aligned(1024))) char sv[(VT_BYTES + 1023) / 1024 * 1024];
+
+  const Layout& L = a.L;
+  const int N = L.N, H = L.H;
+  // Consecutive workgroup ids go round-robin over the 8 XCDs; remap so each
+  // XCD works through a contiguous range of (b, h, query tile), keeping the
+  // key/value tiles of a head in one L2.
+  const int wg = blockIdx.x;
+  int logical = wg;
+  if ((a.nwg & 7) == 0) logical = (wg & 7) * (a.nwg >> 3) + (wg >> 3);
+  const int qt = logical % a.qtiles;
+  const int bh = logical / a.qtiles;
+  const int h = bh % H, b = bh / H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
+  const int l32 = lane & 31, half = lane >> 5;
+  const int i = qt * kQueryTile + w * 32 + l32;
+  const bool qin = i < N;
+
+  const Header* hd = reinterpret_cast<const Header*>(a.ws);
+  const bool has_pm = ld_uniform(&hd->has_pair_mask) != 0;
+  const float gl = ld_uniform(reinterpret_cast<const float*>(a.ws + L.off_gam) + h) * kLog2e;
+  const float Pf = (float)L.P;
+
+  // query operand (B of S^T): lane holds query l32, columns half*8 .. +7 of each K-step
+  bf16x8_t bq[NQS];
+  load_q_frag<NQS>(reinterpret_cast<const uint4*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + i) * (QW / 8),
+                   qin, half, bq);
+  const bool qvalid = query_valid(L, a.ws, b, i, qin);
+  f16x8_t bg[GS];
+  QueryGeo qg;
+  {
+    float av[15];
+    load_qa(reinterpret_cast<const float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + i) * 4, qin, av);
+    build_geo<GS>(L.P, av, qvalid, gl, half, bg, &qg);
+  }
+
+  if (has_pm)
+    attend<NQS, NVB, GS, true>(a, sk, sv, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+  else
+    attend<NQS, NVB, GS, false>(a, sk, sv, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+}
+
+template <int NQS, int NVB, int GS>
 static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st) {
   FlashMfmaArgs a;
   a.L = L;
@@ -237,14 +332,20 @@ static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* 
   a.lse = lse;
   a.qtiles = (L.N + kQueryTile - 1) / kQueryTile;
   a.nwg = a.qtiles * L.H * L.B;
-  hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB>), dim3(a.nwg), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS>), dim3(a.nwg), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_flash_mfma(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st) {
-  if (L.NQS == 3 && L.NVB == 2) return launch_inst<3, 2>(L, ws, o, lse, st);
-  if (L.NQS == 5 && L.NVB == 3) return launch_inst<5, 3>(L, ws, o, lse, st);
-  if (L.NQS == 9 && L.NVB == 5) return launch_inst<9, 5>(L, ws, o, lse, st);
+  if (L.GS == 3) {
+    if (L.NQS == 3 && L.NVB == 2) return launch_inst<3, 2, 3>(L, ws, o, lse, st);
+    if (L.NQS == 5 && L.NVB == 3) return launch_inst<5, 3, 3>(L, ws, o, lse, st);
+    if (L.NQS == 9 && L.NVB == 5) return launch_inst<9, 5, 3>(L, ws, o, lse, st);
+  } else if (L.GS == 4) {
+    if (L.NQS == 3 && L.NVB == 2) return launch_inst<3, 2, 4>(L, ws, o, lse, st);
+    if (L.NQS == 5 && L.NVB == 3) return launch_inst<5, 3, 4>(L, ws, o, lse, st);
+    if (L.NQS == 9 && L.NVB == 5) return launch_inst<9, 5, 4>(L, ws, o, lse, st);
+  }
   return hipErrorInvalidValue;
 }
 

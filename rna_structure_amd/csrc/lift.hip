@@ -5,13 +5,14 @@
 //   L_ijh = q.k/sqrt(3D) + pair_bias_ijh/sqrt(3) - gamma_h sum_p |a_ip - b_jp|^2
 // with a = T_i(q_points), b = T_j(k_points), gamma_h = 1/2 softplus(w_h)
 // sqrt(2/(27P)), pair_bias_ijh = sum_c w_pair[h,c] sum_r zl_irc zr_jrc.
-// Expanding the squared distance (FlashIPA verdict page, key_machinery)
-// about the centroid c of the key tile that holds j,
-//   -gamma |a-b|^2 = 2 gamma (a-c).(b-c) - gamma |b-c|^2 - gamma |a-c|^2,
-// every term but the last is an inner product of a query-side and a
-// key-side vector; the last depends on (i, tile) only and is added by the
-// fused kernel.  All logits are carried in log2 units (times log2 e) so that
-// the softmax can use exp2.
+// The squared distance is expanded (FlashIPA verdict page, key_machinery)
+// about two centroids, that of the key tile holding j and that of the query's
+// wavefront (see common.h for the column layout), so that every term is an
+// inner product of a query-side and a key-side vector of small magnitude.
+// This kernel writes the key side: centred key points w = b - c_t split into
+// fp16 high/low parts, -gamma log2e |w|^2, 2 gamma log2e sum_p w_p, and the
+// value rows (centred value points, a ones row and the centroid).  All logits
+// are carried in log2 units (times log2 e) so that the softmax can use exp2.
 //
 // One workgroup per (key tile t, head h, batch b), 64 residues.
 #include "common.h"
@@ -52,6 +53,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
   __shared__ float s_x[64][32];    // x - c (value points, centred)
   __shared__ float s_a[64][16];    // a (query points, global)
   __shared__ float s_nb[64];       // -gamma log2e |b - c|^2
+  __shared__ float s_ww[64][4];    // 2 gamma log2e sum_p (b_p - c)
   __shared__ float s_c[4];
   __shared__ float s_gam;
 
@@ -78,11 +80,13 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
     if (tid == 0) {
       float cx = 0.f, cy = 0.f, cz = 0.f;
       if (sn > 0.f) { cx = sx / sn; cy = sy / sn; cz = sz / sn; }
-      if (L.mfma) {
-        // the centroid only has to be some fixed point; keep it exactly
-        // representable in fp16 so that it can ride in an fp16 value column
-        cx = f16_bits_to_f32(hi16(cx)); cy = f16_bits_to_f32(hi16(cy)); cz = f16_bits_to_f32(hi16(cz));
-      }
+      // The centroid only has to be some fixed point near the tile.  It is
+      // put on a 4-angstrom grid, exactly representable in fp16, so that it
+      // can ride in an fp16 value column and so that differences of two
+      // centroids are exact in fp16.
+      const float grid = (float)kCentGrid;
+      cx = grid * rintf(cx / grid); cy = grid * rintf(cy / grid); cz = grid * rintf(cz / grid);
+      cx = f16_bits_to_f32(hi16(cx)); cy = f16_bits_to_f32(hi16(cy)); cz = f16_bits_to_f32(hi16(cz));
       s_c[0] = cx; s_c[1] = cy; s_c[2] = cz; s_c[3] = 0.f;
       const float g = 0.5f * softplus_f(ld<BF>(a.pwr, h)) * sqrtf(2.0f / (27.0f * (float)P));
       s_gam = g;
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
     const bool in = j < N;
     for (int e = 0; e < 9; ++e) Rm[e] = in ? ld<BF>(a.rot, ((size_t)b * N + j) * 9 + e) : 0.f;
     const float tx = s_tr[tid][0], ty = s_tr[tid][1], tz = s_tr[tid][2];
-    float nb = 0.f;
+    float nb = 0.f, Wx = 0.f, Wy = 0.f, Wz = 0.f;
     for (int p = 0; p < 16; ++p) { s_w[tid][p] = 0.f; s_a[tid][p] = 0.f; }
     for (int p = 0; p < 32; ++p) s_x[tid][p] = 0.f;
     if (in) {
@@ -114,6 +118,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
         const float wx = gx - cx, wy = gy - cy, wz = gz - cz;
         s_w[tid][3 * p] = wx; s_w[tid][3 * p + 1] = wy; s_w[tid][3 * p + 2] = wz;
         nb += wx * wx + wy * wy + wz * wz;
+        Wx += wx; Wy += wy; Wz += wz;
         const float qx = ld<BF>(a.qp, base_k + 3 * p), qy = ld<BF>(a.qp, base_k + 3 * p + 1),
                     qz = ld<BF>(a.qp, base_k + 3 * p + 2);
         s_a[tid][3 * p] = Rm[0] * qx + Rm[1] * qy + Rm[2] * qz + tx;
@@ -130,6 +135,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
       }
     }
     s_nb[tid] = -gl * nb;
+    s_ww[tid][0] = 2.f * gl * Wx; s_ww[tid][1] = 2.f * gl * Wy; s_ww[tid][2] = 2.f * gl * Wz; s_ww[tid][3] = 0.f;
   }
   // --- small per-tile / per-head records
   if (tid == 0) {
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
 
   if constexpr (BF) {
     // ---------------- matrix-core layouts
-    const int QW = L.QW, KROW = L.KROW, P3 = 3 * P;
+    const int QW = L.QW, KROW = L.KROW, P3 = 3 * P, GS = L.GS;
     // key rows of tile (b,h,t): [k | zr | 0 | geo(48) | pad]
     uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * KROW;
     const uint16_t* k16 = reinterpret_cast<const uint16_t*>(a.k);
@@ -179,14 +185,21 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
             val = k16[(((size_t)b * N + j) * H + h) * D + c];
           } else if (c < D + RCz) {
             val = zr16[((size_t)b * N + j) * RCz + (c - D)];
-          } else if (c >= QW && c < QW + kGeoCols) {
-            const int g = c - QW;
-            (void)P3;
-            if (g < kGeoW) val = hi16(s_w[row][g]);
-            else if (g < 2 * kGeoW) val = lo16(s_w[row][g - kGeoW]);
-            else if (g < 3 * kGeoW) val = hi16(s_w[row][g - 2 * kGeoW]);
-            else if (g == 3 * kGeoW) val = hi16(s_nb[row] * (1.0f / kNormScale));
-            else if (g == 3 * kGeoW + 1) val = lo16(s_nb[row] * (1.0f / kNormScale));
+          } else if (c >= QW && c < QW + 16 * GS) {
+            // geometric columns, layout in common.h
+            const int g = c - QW, base = 16 * (GS - 1);
+            if (g < base + 4) {
+              if (g < P3) val = hi16(s_w[row][g]);
+              else if (g < 2 * P3) val = lo16(s_w[row][g - P3]);
+              else if (g < 3 * P3) val = hi16(s_w[row][g - 2 * P3]);
+            } else {
+              const int x = g - base;
+              if (x == 4) val = hi16(s_nb[row] * (1.0f / kNormScale));
+              else if (x == 12) val = lo16(s_nb[row] * (1.0f / kNormScale));
+              else if (x >= 5 && x <= 7) val = hi16(s_ww[row][x - 5]);
+              else if (x >= 13) val = lo16(s_ww[row][x - 13]);
+              else if (x >= 9 && x <= 11) val = 0x4C00;  // fp16 16.0, multiplies the query's t'/16 parts
+            }
           }
         }
         out[e] = val;

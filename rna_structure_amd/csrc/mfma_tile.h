@@ -15,13 +15,13 @@ __device__ __forceinline__ float f16_round(float x) {
   return (float)(_Float16)fminf(fmaxf(x, -65504.0f), 65504.0f);
 }
 
-// value of geometric query column g (0..47) given the split parts
-__device__ __forceinline__ float geo_q(int g, const float* uh, const float* ul) {
-  if (g < kGeoW) return uh[g];
-  if (g < 2 * kGeoW) return uh[g - kGeoW];
-  if (g < 3 * kGeoW) return ul[g - 2 * kGeoW];
-  if (g < 3 * kGeoW + 2) return kNormScale;
-  return 0.f;
+// A centroid on the 4-angstrom grid, exactly representable in fp16.
+__device__ __forceinline__ float grid_round(float x) {
+  return f16_round((float)kCentGrid * rintf(x * (1.0f / (float)kCentGrid)));
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
 }
 
 // Query operand of S^T = K~ Q~^T (B operand): lane (l32, half) holds columns
@@ -46,54 +46,137 @@ __device__ __forceinline__ void load_qa(const float4* arow, bool qin, float* av)
   }
 }
 
-// Query-side geometric operand for a key tile with centroid c:
-//   u = 2 gamma log2e (a - c) split into fp16 high/low parts,
-//   na = gamma log2e |a - c|^2 (the row term, subtracted after the product).
-__device__ __forceinline__ void geo_frag(const float* av, float4 c4, float gl, int P3, int half, f16x8_t* bg,
-                                         float* na_out) {
-  float uh[15], ul[15];
-  float na = 0.f;
+// Per-wavefront query geometry: centroid c_w of the valid queries (32
+// consecutive residues), split operand u = 2 gl (a - c_w), and the sums
+// U = sum_p (a_p - c_w), SA = sum_p |a_p - c_w|^2 used by the per-tile row
+// term t' = -gl sum_p |a_p - c_t|^2 = 2 gl delta.U - gl (P |delta|^2 + SA).
+struct QueryGeo {
+  float cw[3];
+  float U[3];
+  float SA;
+  uint32_t fix0, fix1;  // fixed first two dwords of the last geometric K-step
+};
+
+template <int P, int GS>
+__device__ __forceinline__ void build_geo_P(const float* av, bool qvalid, float gl, int half, f16x8_t* bg,
+                                            QueryGeo* qg) {
+  constexpr int P3 = 3 * P;
+  constexpr int base = 16 * (GS - 1);
+  // centroid of the valid queries of this wavefront (each half holds the same 32)
+  float sx = 0.f, sy = 0.f, sz = 0.f, cnt = qvalid ? 1.f : 0.f;
+  if (qvalid) {
 #pragma unroll
-  for (int g = 0; g < 15; ++g) {
-    const float cc = (g % 3 == 0) ? c4.x : ((g % 3 == 1) ? c4.y : c4.z);
-    const float d = (g < P3) ? av[g] - cc : 0.f;
-    na = fmaf(d, d, na);
-    const float u = 2.f * gl * d;
+    for (int p = 0; p < P; ++p) { sx += av[3 * p]; sy += av[3 * p + 1]; sz += av[3 * p + 2]; }
+    sx *= 1.0f / P; sy *= 1.0f / P; sz *= 1.0f / P;
+  }
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    sx += __shfl_xor(sx, off);
+    sy += __shfl_xor(sy, off);
+    sz += __shfl_xor(sz, off);
+    cnt += __shfl_xor(cnt, off);
+  }
+  const float inv = cnt > 0.f ? 1.0f / cnt : 0.f;
+  qg->cw[0] = grid_round(sx * inv);
+  qg->cw[1] = grid_round(sy * inv);
+  qg->cw[2] = grid_round(sz * inv);
+  float uh[P3], ul[P3];
+  float U0 = 0.f, U1 = 0.f, U2 = 0.f, SA = 0.f;
+#pragma unroll
+  for (int g = 0; g < P3; ++g) {
+    const float A = av[g] - qg->cw[g % 3];
+    if (g % 3 == 0) U0 += A; else if (g % 3 == 1) U1 += A; else U2 += A;
+    SA = fmaf(A, A, SA);
+    const float u = 2.f * gl * A;
     uh[g] = f16_round(u);
     ul[g] = f16_round(u - uh[g]);
   }
-  *na_out = na * gl;
+  qg->U[0] = U0; qg->U[1] = U1; qg->U[2] = U2; qg->SA = SA;
+  auto qval = [&](int g) -> float {
+    if (g < base + 4) {
+      const int c = g;
+      if (c < P3) return uh[c];
+      if (c < 2 * P3) return uh[c - P3];
+      if (c < 3 * P3) return ul[c - 2 * P3];
+      return 0.f;
+    }
+    if (g == base + 4 || g == base + 12) return kNormScale;
+    return 0.f;  // delta and t' slots, set per key tile
+  };
 #pragma unroll
-  for (int s = 0; s < 3; ++s) {
+  for (int s = 0; s < GS; ++s) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v0 = geo_q(s * 16 + e, uh, ul), v1 = geo_q(s * 16 + 8 + e, uh, ul);
+      const float v0 = qval(16 * s + e), v1 = qval(16 * s + 8 + e);
       bg[s][e] = (_Float16)(half ? v1 : v0);
     }
   }
+  const uint4 last = __builtin_bit_cast(uint4, bg[GS - 1]);
+  qg->fix0 = last.x;
+  qg->fix1 = last.y;
+}
+
+template <int GS>
+__device__ __forceinline__ void build_geo(int P, const float* av, bool qvalid, float gl, int half, f16x8_t* bg,
+                                          QueryGeo* qg) {
+  if constexpr (GS == 3) {
+    switch (P) {
+      case 1: build_geo_P<1, 3>(av, qvalid, gl, half, bg, qg); break;
+      case 2: build_geo_P<2, 3>(av, qvalid, gl, half, bg, qg); break;
+      case 3: build_geo_P<3, 3>(av, qvalid, gl, half, bg, qg); break;
+      default: build_geo_P<4, 3>(av, qvalid, gl, half, bg, qg); break;
+    }
+  } else {
+    build_geo_P<5, 4>(av, qvalid, gl, half, bg, qg);
+  }
+}
+
+// Per key tile: -delta (exact in fp16) in the last K-step, and the row term
+// t' (three fp16 parts of t'/16) in the slots of half 1.
+template <int GS>
+__device__ __forceinline__ void geo_tile(const QueryGeo& qg, float4 ct, float gl, float Pf, int half, f16x8_t* bg) {
+  const float dx = ct.x - qg.cw[0], dy = ct.y - qg.cw[1], dz = ct.z - qg.cw[2];
+  const float dU = fmaf(dx, qg.U[0], fmaf(dy, qg.U[1], dz * qg.U[2]));
+  const float d2 = fmaf(dx, dx, fmaf(dy, dy, dz * dz));
+  const float tp = 2.f * gl * dU - gl * fmaf(Pf, d2, qg.SA);
+  const float x = fminf(fmaxf(tp * (1.0f / kNormScale), -65504.0f), 65504.0f);
+  const float h1 = f16_round(x);
+  const float r1 = x - h1;
+  const float h2 = f16_round(r1);
+  const float h3 = f16_round(r1 - h2);
+  uint4 last;
+  last.x = half ? pack_f16(0.f, h1) : qg.fix0;
+  last.y = half ? pack_f16(h2, h3) : qg.fix1;
+  last.z = pack_f16(kNormScale, -dx);
+  last.w = pack_f16(-dy, -dz);
+  bg[GS - 1] = __builtin_bit_cast(f16x8_t, last);
 }
 
 // S^T for one 64-key tile: sacc[kb] (keys kb*32 .. +31) x 32 queries.
 // ktile points at 64 rows of KROW 16-bit elements (LDS or global memory).
-template <int NQS>
+// The two key blocks are interleaved so consecutive MFMAs are independent.
+template <int NQS, int GS>
 __device__ __forceinline__ void s_tile(const char* ktile, const bf16x8_t* bq, const f16x8_t* bg, int l32, int half,
                                        f32x16_t* sacc) {
   constexpr int QW = 16 * NQS;
-  constexpr int KROW = QW + kGeoCols + kRowPad;
+  constexpr int KROW = QW + 16 * GS + kRowPad;
+  const char* k0 = ktile + (size_t)(l32 * KROW) * 2 + half * 16;
+  const char* k1 = k0 + (size_t)(32 * KROW) * 2;
+  sacc[0] = f32x16_t{};
+  sacc[1] = f32x16_t{};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    sacc[kb] = f32x16_t{};
-    const char* krow = ktile + (size_t)((kb * 32 + l32) * KROW) * 2;
+  for (int ks = 0; ks < NQS; ++ks) {
+    const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(k0 + ks * 32);
+    const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(k1 + ks * 32);
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[ks], sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[ks], sacc[1], 0, 0, 0);
+  }
 #pragma unroll
-    for (int ks = 0; ks < NQS; ++ks) {
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(krow + (ks * 16 + half * 8) * 2);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bq[ks], sacc[kb], 0, 0, 0);
-    }
-#pragma unroll
-    for (int gs = 0; gs < 3; ++gs) {
-      const f16x8_t af = *reinterpret_cast<const f16x8_t*>(krow + (QW + gs * 16 + half * 8) * 2);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bg[gs], sacc[kb], 0, 0, 0);
-    }
+  for (int gs = 0; gs < GS; ++gs) {
+    const f16x8_t a0 = *reinterpret_cast<const f16x8_t*>(k0 + (QW + gs * 16) * 2);
+    const f16x8_t a1 = *reinterpret_cast<const f16x8_t*>(k1 + (QW + gs * 16) * 2);
+    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bg[gs], sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bg[gs], sacc[1], 0, 0, 0);
   }
 }
 
