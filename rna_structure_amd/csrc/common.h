@@ -128,7 +128,7 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
     L->NQS = L->NVB = L->GS = 0;
     L->DQP = round_up(L->D + L->RCz, 4);
     L->QW = L->DQP;
-    L->KROW = round_up(L->D + L->RCz + 3 * L->P + 1, 4);
+    L->KROW = round_up(L->D + L->RCz + 3 * L->P, 4);
     L->VROWS = round_up(L->DO, 4);
   } else {
     return false;

@@ -4,7 +4,7 @@
 // (mfma_tile.h) on the same lifted operands and the same query grouping, so
 // its logits are bit-identical to the ones the fused kernel exponentiates; together with the fused
 // kernel's log-sum-exp they give the attention rows exp(L - lse).  The fp32
-// variant repeats the fp32 kernel's expression order.
+// variant repeats the fp32 kernel's expressions in the same order.
 #include "mfma_tile.h"
 
 namespace fipa {
@@ -81,18 +81,19 @@ __global__ __launch_bounds__(256) void logit_rows_f32_kernel(DiagArgs a) {
   const int P3 = 3 * L.P, DQ = L.D + L.RCz;
   const float* q = reinterpret_cast<const float*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + i) * L.DQP;
   const float* k = reinterpret_cast<const float*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NKpad + j) * L.KROW;
-  float na = 0.f, u[15];
+  float dA[15];
   for (int g = 0; g < 15; ++g) {
     const float cc = (g % 3 == 0) ? c4.x : ((g % 3 == 1) ? c4.y : c4.z);
-    const float d = (g < P3) ? arow[g] - cc : 0.f;
-    na += d * d;
-    u[g] = 2.f * gl * d;
+    dA[g] = (g < P3) ? arow[g] - cc : 0.f;
   }
-  na *= gl;
   float s = 0.f;
   for (int c = 0; c < DQ; ++c) s = fmaf(q[c], k[c], s);
-  for (int g = 0; g < P3; ++g) s = fmaf(u[g], k[DQ + g], s);
-  s += k[DQ + P3] - na;
+  float dist = 0.f;
+  for (int g = 0; g < P3; ++g) {
+    const float df = dA[g] - k[DQ + g];
+    dist = fmaf(df, df, dist);
+  }
+  s = fmaf(-gl, dist, s);
   *outp = s * kLn2;
 }
 

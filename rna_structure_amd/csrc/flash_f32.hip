@@ -2,10 +2,12 @@
 // rows, fp32 arithmetic throughout (VALU, no matrix cores).
 //
 // Logit (log2 units) for query i, key j in key tile t with centroid c_t:
-//   s_ij = Qs_i . Ks_j                       scalar + pair columns
-//        + u_it . w_j                        u = 2 gamma log2e (a_i - c_t), w = b_j - c_t
-//        + nb_j - gamma log2e |a_i - c_t|^2  nb = -gamma log2e |b_j - c_t|^2
-// which equals log2(e) * L_ijh of the IPA page ("Required behavior").
+//   s_ij = Qs_i . Ks_j                       scalar + pair columns (lifted rows)
+//        - gamma log2e sum_p |(a_ip - c_t) - (b_jp - c_t)|^2
+// which equals log2(e) * L_ijh of the IPA page ("Required behavior").  On
+// this fp32 VALU path the point term is formed as a difference, then
+// squared, from coordinates centred on the key tile: no expansion, hence no
+// cancellation between large terms.
 // Softmax over the permitted keys uses a running maximum (FlashAttention
 // style); value points are aggregated relative to the tile centroid and the
 // centroid term sum_j p_j c_t is carried separately.
@@ -73,8 +75,7 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
     qvalid = (km[((size_t)b * L.NT + (i >> 6)) * 2 + hf] >> bit) & 1u;
   }
 
-  float u[15];
-  float na = 0.f;
+  float dA[15];  // a - c_t for the current key tile
   float4 c4 = make_float4(0.f, 0.f, 0.f, 0.f);
   uint32_t w0 = 0, w1 = 0;
   const int nsteps = L.NKpad / kF32Keys;
@@ -82,15 +83,11 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
     const int t = st >> 1;
     if ((st & 1) == 0) {
       c4 = ck[(size_t)b * L.NT + t];
-      na = 0.f;
 #pragma unroll
       for (int g = 0; g < 15; ++g) {
         const float cc = (g % 3 == 0) ? c4.x : ((g % 3 == 1) ? c4.y : c4.z);
-        const float d = (g < P3) ? av[g] - cc : 0.f;
-        na += d * d;
-        u[g] = 2.f * gl * d;
+        dA[g] = (g < P3) ? av[g] - cc : 0.f;
       }
-      na *= gl;
       if (has_pm) {
         const size_t o = (((size_t)b * L.NQpad + i) * L.NT + t) * 2;
         w0 = qin ? pmw[o] : 0u;
@@ -119,10 +116,14 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
 #pragma unroll
       for (int d = 0; d < kF32MaxDQ; ++d)
         if (d < DQ) s = fmaf(qv[d], kr[d], s);
+      float dist = 0.f;
 #pragma unroll
       for (int g = 0; g < 15; ++g)
-        if (g < P3) s = fmaf(u[g], kr[DQ + g], s);
-      s += kr[DQ + P3] - na;
+        if (g < P3) {
+          const float df = dA[g] - kr[DQ + g];
+          dist = fmaf(df, df, dist);
+        }
+      s = fmaf(-gl, dist, s);
       if (s > m) {
         const float alpha = exp2f(m - s);  // m = -inf -> 0
         l *= alpha;

@@ -287,7 +287,6 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
         if (c < D) val = ld<false>(a.k, (((size_t)b * N + j) * H + h) * D + c);
         else if (c < D + RCz) val = ld<false>(a.zr, ((size_t)b * N + j) * RCz + (c - D));
         else if (c < D + RCz + P3) val = s_w[row][c - D - RCz];
-        else if (c == D + RCz + P3) val = s_nb[row];
       }
       kr[(((size_t)b * H + h) * L.NKpad + j) * KROW + c] = val;
     }
