@@ -13,7 +13,8 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libflashipa.so")
+# FLASHIPA_LIBRARY may name another build of the same library (same ABI)
+LIB_PATH = os.environ.get("FLASHIPA_LIBRARY", os.path.join(HERE, "libflashipa.so"))
 
 IPA_F32, IPA_BF16 = 0, 1
 STATUS = {0: "IPA_OK", 1: "IPA_ERR_NULL", 2: "IPA_ERR_SHAPE", 3: "IPA_ERR_UNSUPPORTED",

@@ -152,7 +152,11 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
     if (has_pm) wait_vmcnt<0>(); else wait_vmcnt<kDV>();
     __syncthreads();
     f32x16_t sacc[2];
+    // raised wave priority while issuing MFMAs: the other wavefront on the
+    // SIMD (another workgroup) fills the gaps with its VALU work
+    __builtin_amdgcn_s_setprio(1);
     s_tile<NQS, GS>(sk, bq, bg, l32, half, sacc);
+    __builtin_amdgcn_s_setprio(0);
     asm volatile("" ::"v"(mw));  // the mask word is in registers before the next copies are issued
     __syncthreads();  // every wave has read key tile t
     if (tn < NT) dma_tile<KT_BYTES>(ktg0 + (size_t)tn * KT_BYTES, sk, w, lane);
@@ -205,6 +209,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
     __syncthreads();
     // O^T += V~^T P^T, value blocks interleaved so consecutive MFMAs are independent
     const char* vrow = sv + (size_t)(l32 * kVCols) * 2 + half * 16;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -215,6 +220,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
       const f16x8_t af = *reinterpret_cast<const f16x8_t*>(vrow + (size_t)(NVB * 32 * kVCols) * 2 + ks * 32);
       oacc[NVB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, ph[ks], oacc[NVB], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // every wave has read value tile t
     if (tn < NT) dma_tile<VT_BYTES>(vtg0 + (size_t)tn * VT_BYTES, sv, w, lane);
     t = tn;

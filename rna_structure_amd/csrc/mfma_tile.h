@@ -154,29 +154,49 @@ __device__ __forceinline__ void geo_tile(const QueryGeo& qg, float4 ct, float gl
 
 // S^T for one 64-key tile: sacc[kb] (keys kb*32 .. +31) x 32 queries.
 // ktile points at 64 rows of KROW 16-bit elements (LDS or global memory).
-// The two key blocks are interleaved so consecutive MFMAs are independent.
+// The two key blocks are interleaved so consecutive MFMAs are independent,
+// and the operand fragments are fetched DEPTH K-steps ahead of their MFMA so
+// that the reads' latency hides behind the preceding MFMAs.
 template <int NQS, int GS>
 __device__ __forceinline__ void s_tile(const char* ktile, const bf16x8_t* bq, const f16x8_t* bg, int l32, int half,
                                        f32x16_t* sacc) {
   constexpr int QW = 16 * NQS;
   constexpr int KROW = QW + 16 * GS + kRowPad;
+  constexpr int NS = NQS + GS;
+  constexpr int DEPTH = 3;
   const char* k0 = ktile + (size_t)(l32 * KROW) * 2 + half * 16;
   const char* k1 = k0 + (size_t)(32 * KROW) * 2;
+  auto off = [](int st) { return st < NQS ? st * 32 : (QW + (st - NQS) * 16) * 2; };
+  uint4 f0[DEPTH], f1[DEPTH];
+#pragma unroll
+  for (int st = 0; st < DEPTH && st < NS; ++st) {
+    f0[st] = *reinterpret_cast<const uint4*>(k0 + off(st));
+    f1[st] = *reinterpret_cast<const uint4*>(k1 + off(st));
+  }
   sacc[0] = f32x16_t{};
   sacc[1] = f32x16_t{};
 #pragma unroll
-  for (int ks = 0; ks < NQS; ++ks) {
-    const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(k0 + ks * 32);
-    const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(k1 + ks * 32);
-    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[ks], sacc[0], 0, 0, 0);
-    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[ks], sacc[1], 0, 0, 0);
+  for (int st = 0; st < NS; ++st) {
+    const uint4 c0 = f0[st % DEPTH], c1 = f1[st % DEPTH];
+    if (st + DEPTH < NS) {
+      f0[st % DEPTH] = *reinterpret_cast<const uint4*>(k0 + off(st + DEPTH));
+      f1[st % DEPTH] = *reinterpret_cast<const uint4*>(k1 + off(st + DEPTH));
+    }
+    if (st < NQS) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c0), bq[st], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c1), bq[st], sacc[1], 0, 0, 0);
+    } else {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c0), bg[st - NQS], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c1), bg[st - NQS], sacc[1], 0, 0, 0);
+    }
   }
+  // keep the fetch-ahead order through scheduling: the first DEPTH steps'
+  // reads, then per step two MFMAs followed by the reads DEPTH steps ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * DEPTH, 0);
 #pragma unroll
-  for (int gs = 0; gs < GS; ++gs) {
-    const f16x8_t a0 = *reinterpret_cast<const f16x8_t*>(k0 + (QW + gs * 16) * 2);
-    const f16x8_t a1 = *reinterpret_cast<const f16x8_t*>(k1 + (QW + gs * 16) * 2);
-    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bg[gs], sacc[0], 0, 0, 0);
-    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bg[gs], sacc[1], 0, 0, 0);
+  for (int st = 0; st < NS; ++st) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (st + DEPTH < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
 }
 
