@@ -159,10 +159,14 @@ ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float
  * [scalar (H,Dv) | x (H,Q) | y | z | length (H,Q) | pair (H,Cz)], and
  * update = features @ w_out + b_out; everything zero for an empty
  * neighbourhood (IPA page, "Required behavior").
+ *   lifted       the workspace of ipa_lift (a region of it receives w_out
+ *                transposed; the lifted rows are not touched)
  *   o, lse       from ipa_flash_fwd
  *   update       [B,N,Cout] fp32 (written)
- *   local_points [B,N,H,Q,3] fp32 (written) */
-ipa_status ipa_epilogue(const ipa_shape* s, const float* o, const float* lse, const ipa_epi_in* in,
+ *   local_points [B,N,H,Q,3] fp32 (written)
+ * IPA_ERR_UNSUPPORTED if the feature row F does not fit the kernel's LDS
+ * staging (bf16 path: F <= 2544; fp32 path: F <= 2559). */
+ipa_status ipa_epilogue(const ipa_shape* s, void* lifted, const float* o, const float* lse, const ipa_epi_in* in,
                         float* update, float* local_points, void* stream);
 
 /* Diagnostic (tests only): the logits the fused kernel uses, for query rows

@@ -65,7 +65,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipa_lift.restype = ctypes.c_int
     lib.ipa_flash_fwd.argtypes = [sp, vp, vp, vp, vp]
     lib.ipa_flash_fwd.restype = ctypes.c_int
-    lib.ipa_epilogue.argtypes = [sp, vp, vp, ctypes.POINTER(IpaEpiIn), vp, vp, vp]
+    lib.ipa_epilogue.argtypes = [sp, vp, vp, vp, ctypes.POINTER(IpaEpiIn), vp, vp, vp]
     lib.ipa_epilogue.restype = ctypes.c_int
     lib.ipa_logit_rows.argtypes = [sp, vp, i64, i64, i64, i64, vp, vp]
     lib.ipa_logit_rows.restype = ctypes.c_int
@@ -121,9 +121,9 @@ def ipa_flash_fwd(s: IpaShape, lifted, o, lse, stream=None):
                                                  _stream(stream)))
 
 
-def ipa_epilogue(s: IpaShape, o, lse, t: dict, update, local_points, stream=None):
+def ipa_epilogue(s: IpaShape, lifted, o, lse, t: dict, update, local_points, stream=None):
     ei = IpaEpiIn(*[_ptr(t[n]) for n in ("zl", "rotation", "translation", "w_out", "b_out")])
-    _check("ipa_epilogue", load().ipa_epilogue(ctypes.byref(s), _ptr(o), _ptr(lse), ctypes.byref(ei),
+    _check("ipa_epilogue", load().ipa_epilogue(ctypes.byref(s), _ptr(lifted), _ptr(o), _ptr(lse), ctypes.byref(ei),
                                                _ptr(update), _ptr(local_points), _stream(stream)))
 
 
@@ -175,7 +175,7 @@ class FlashIPA:
         ipa_flash_fwd(self.s, self.lifted, self.o, self.lse, stream)
 
     def epilogue(self, t: dict, stream=None):
-        ipa_epilogue(self.s, self.o, self.lse, t, self.update, self.local_points, stream)
+        ipa_epilogue(self.s, self.lifted, self.o, self.lse, t, self.update, self.local_points, stream)
 
     def forward(self, t: dict, stream=None):
         self.lift(t, stream)

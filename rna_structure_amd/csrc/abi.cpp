@@ -9,8 +9,9 @@ namespace fipa {
 hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStream_t st);
 hipError_t launch_flash_f32(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st);
 hipError_t launch_flash_mfma(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st);
-hipError_t launch_epilogue(const Layout& L, const float* o, const float* lse, const ipa_epi_in* in, float eps,
+hipError_t launch_epilogue(const Layout& L, void* ws, const float* o, const float* lse, const ipa_epi_in* in, float eps,
                            float* update, float* local, hipStream_t st);
+bool epilogue_supported(const Layout& L);
 hipError_t launch_logit_rows(const Layout& L, const void* ws, int b, int h, int row0, int nrows, float* out,
                              hipStream_t st);
 }  // namespace fipa
@@ -74,9 +75,9 @@ ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float
                               : fipa::launch_flash_f32(L, lifted, o, lse, hs));
 }
 
-ipa_status ipa_epilogue(const ipa_shape* s, const float* o, const float* lse, const ipa_epi_in* in, float* update,
-                        float* local_points, void* stream) {
-  if (!s || !o || !lse || !in || !update || !local_points) return IPA_ERR_NULL;
+ipa_status ipa_epilogue(const ipa_shape* s, void* lifted, const float* o, const float* lse, const ipa_epi_in* in,
+                        float* update, float* local_points, void* stream) {
+  if (!s || !lifted || !o || !lse || !in || !update || !local_points) return IPA_ERR_NULL;
   Layout L;
   ipa_status st = shape_status(s, 0, &L);
   if (st != IPA_OK) return st;
@@ -85,11 +86,10 @@ ipa_status ipa_epilogue(const ipa_shape* s, const float* o, const float* lse, co
     if (!p) return IPA_ERR_NULL;
   for (const void* p : req)
     if (!aligned16(p)) return IPA_ERR_ALIGN;
-  if (!aligned16(o) || !aligned16(lse) || !aligned16(update) || !aligned16(local_points)) return IPA_ERR_ALIGN;
-  const int64_t F = s->H * (s->Dv + 4 * s->Q + s->Cz);
-  if (L.mfma ? (32 * ((F + 15) / 16 * 16 + 8) * 2 > 160 * 1024) : (16 * (F + 1) * 4 > 160 * 1024))
-    return IPA_ERR_UNSUPPORTED;
-  return launch_status(fipa::launch_epilogue(L, o, lse, in, s->eps, update, local_points,
+  if (!aligned16(lifted) || !aligned16(o) || !aligned16(lse) || !aligned16(update) || !aligned16(local_points))
+    return IPA_ERR_ALIGN;
+  if (!fipa::epilogue_supported(L)) return IPA_ERR_UNSUPPORTED;
+  return launch_status(fipa::launch_epilogue(L, lifted, o, lse, in, s->eps, update, local_points,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -69,7 +69,8 @@ struct Layout {
   int DQP;    // fp32 path: padded query row width
   int DO;     // attention output width Dv + R*Cz + 3Q
   int has_pm;
-  size_t off_ql, off_qa, off_kt, off_vt, off_ck, off_gam, off_km, off_pm, total;
+  int F, FP;  // epilogue feature count, padded to 16
+  size_t off_ql, off_qa, off_kt, off_vt, off_ck, off_gam, off_km, off_wt, off_pm, total;
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -110,6 +111,8 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
   L->NKpad = L->NT * kKeyTile;
   L->NQpad = round_up(L->N, kQueryTile);
   L->DO = L->Dv + L->RCz + 3 * L->Q;
+  L->F = L->H * (L->Dv + 4 * L->Q + L->Cz);
+  L->FP = round_up(L->F, 16);
   L->has_pm = with_pm ? 1 : 0;
   if (L->P > kMaxP || L->Q > kMaxQ) return false;
   const size_t B = L->B, H = L->H, NT = L->NT, NQ = L->NQpad, NK = L->NKpad;
@@ -151,6 +154,9 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
   off = align256(off + H * 4);
   L->off_km = off;
   off = align256(off + B * NT * 2 * 4);
+  // output projection transposed to [Cout][FP] bf16 (matrix-core path)
+  L->off_wt = off;
+  if (L->mfma) off = align256(off + (size_t)L->Cout * L->FP * 2);
   L->off_pm = off;
   if (with_pm) off = align256(off + B * NQ * NT * 2 * 4);
   L->total = off;

@@ -5,9 +5,11 @@
 //   pair_ih = sum_r zl_ir * o_zr_ihr            pair features from the factors
 //   features = [scalar (H,Dv) | x (H,Q) | y | z | length (H,Q) | pair (H,Cz)]
 //   update = features @ w_out + b_out, zero for an empty neighbourhood.
-// Features of a block of residues are staged in LDS; the projection runs on
-// MFMA (bf16 operands, fp32 accumulation) on the matrix-core path and on
-// fp32 VALU on the fp32 path.
+// Matrix-core path: the features of a block of residues are built in LDS
+// (bf16) by coalesced work items and multiplied by w_out on MFMA (bf16
+// operands, fp32 accumulation); w_out is first transposed once per call into
+// the workspace so that every MFMA operand fragment is one 16-byte load.
+// fp32 path: the same features in fp32 and a VALU product.
 #include "common.h"
 
 namespace fipa {
@@ -20,119 +22,340 @@ struct EpiArgs {
   const float* o;
   const float* lse;
   const void *zl, *rot, *trans, *w_out, *b_out;
+  const uint16_t* wt;  // [Cout][FP] bf16 (matrix-core path)
   float* update;
   float* local;
   float eps;
-  int F, FP;  // feature count, LDS row pitch (elements)
+  int FP;  // LDS row pitch of the features (elements)
 };
 
-// Features of (residue row, head h) into an LDS row (element type T).
+__device__ __forceinline__ bool row_empty(const EpiArgs& a, int row) {
+  const Layout& L = a.L;
+  const int b = row / L.N, i = row % L.N;
+  return !(a.lse[((size_t)b * L.H) * L.N + i] > -INFINITY);
+}
+
+// ---------------------------------------------------------------- w_out transpose
+// wt[c][f] = w_out[f][c] (bf16 bits), zero for f in [F, FP).
+__global__ __launch_bounds__(256) void transpose_wout_kernel(const uint16_t* w, uint16_t* wt, int F, int FP, int Cout) {
+  __shared__ uint16_t tile[64][65];
+  const int f0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int f = f0 + r, c = c0 + tx;
+    tile[r][tx] = (f < F && c < Cout) ? w[(size_t)f * Cout + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int c = c0 + r, f = f0 + tx;
+    if (c < Cout && f < FP) wt[(size_t)c * FP + f] = tile[tx][r];
+  }
+}
+
+// ---------------------------------------------------------------- features
+// Work items of one (row, head): ceil(Dv/4) scalar chunks, ceil(Cz/4) pair
+// chunks, Q points; consecutive items read consecutive parts of the row's O.
 template <bool BF, typename T>
-__device__ void build_features(const EpiArgs& a, int row, int h, bool empty, T* frow) {
+__device__ __forceinline__ void feature_item(const EpiArgs& a, int row, int h, int it, bool empty, T* frow) {
   const Layout& L = a.L;
   const int H = L.H, Dv = L.Dv, Q = L.Q, Cz = L.Cz, R = L.R, RCz = L.RCz, DO = L.DO;
+  const int nS = (Dv + 3) / 4, nP = (Cz + 3) / 4;
   const int offx = H * Dv, offy = offx + H * Q, offz = offy + H * Q, offl = offz + H * Q, offp = offl + H * Q;
   const float* orow = a.o + ((size_t)row * H + h) * DO;
   auto put = [&](int f, float v) {
     if constexpr (sizeof(T) == 2) frow[f] = __builtin_bit_cast(T, f32_to_bf16_bits(v));
     else frow[f] = v;
   };
-  for (int d = 0; d < Dv; ++d) put(h * Dv + d, empty ? 0.f : orow[d]);
-  float Rm[9], tr[3];
-  for (int e = 0; e < 9; ++e) Rm[e] = ld<BF>(a.rot, (size_t)row * 9 + e);
-  for (int e = 0; e < 3; ++e) tr[e] = ld<BF>(a.trans, (size_t)row * 3 + e);
-  float* lrow = a.local + ((size_t)row * H + h) * Q * 3;
-  for (int q = 0; q < Q; ++q) {
-    const float gx = orow[Dv + RCz + 3 * q] - tr[0];
-    const float gy = orow[Dv + RCz + 3 * q + 1] - tr[1];
-    const float gz = orow[Dv + RCz + 3 * q + 2] - tr[2];
+  if (it < nS) {
+    const int d0 = 4 * it;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (d0 + e < Dv) put(h * Dv + d0 + e, empty ? 0.f : orow[d0 + e]);
+  } else if (it < nS + nP) {
+    const int c0 = 4 * (it - nS);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c0 + e < Cz)
+          acc[e] = fmaf(ld<BF>(a.zl, (size_t)row * RCz + r * Cz + c0 + e), orow[Dv + r * Cz + c0 + e], acc[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c0 + e < Cz) put(offp + h * Cz + c0 + e, empty ? 0.f : acc[e]);
+  } else {
+    const int q = it - nS - nP;
+    const float gx = orow[Dv + RCz + 3 * q] - ld<BF>(a.trans, (size_t)row * 3);
+    const float gy = orow[Dv + RCz + 3 * q + 1] - ld<BF>(a.trans, (size_t)row * 3 + 1);
+    const float gz = orow[Dv + RCz + 3 * q + 2] - ld<BF>(a.trans, (size_t)row * 3 + 2);
+    float Rm[9];
+#pragma unroll
+    for (int e = 0; e < 9; ++e) Rm[e] = ld<BF>(a.rot, (size_t)row * 9 + e);
     // R^T (g - t): column x of R dotted with (g - t)
     float x = Rm[0] * gx + Rm[3] * gy + Rm[6] * gz;
     float y = Rm[1] * gx + Rm[4] * gy + Rm[7] * gz;
     float z = Rm[2] * gx + Rm[5] * gy + Rm[8] * gz;
     float len = sqrtf(x * x + y * y + z * z + a.eps);
     if (empty) { x = y = z = len = 0.f; }
-    lrow[3 * q] = x; lrow[3 * q + 1] = y; lrow[3 * q + 2] = z;
+    float* lp = a.local + (((size_t)row * H + h) * Q + q) * 3;
+    lp[0] = x; lp[1] = y; lp[2] = z;
     put(offx + h * Q + q, x);
     put(offy + h * Q + q, y);
     put(offz + h * Q + q, z);
     put(offl + h * Q + q, len);
   }
-  for (int c = 0; c < Cz; ++c) {
-    float acc = 0.f;
-    for (int r = 0; r < R; ++r) acc = fmaf(ld<BF>(a.zl, (size_t)row * RCz + r * Cz + c), orow[Dv + r * Cz + c], acc);
-    put(offp + h * Cz + c, empty ? 0.f : acc);
+}
+
+// Features of one (row, head) for the standard dimensions Dv=16, Cz=64,
+// Q=8, R=2: the whole attention-output row (168 floats) is read with 42
+// independent 16-byte loads and the features go to LDS as 16-byte stores.
+constexpr int kFDv = 16, kFCz = 64, kFQ = 8, kFR = 2, kFDO = kFDv + kFR * kFCz + 3 * kFQ;
+__device__ __forceinline__ bool fast_dims(const Layout& L) {
+  return L.Dv == kFDv && L.Cz == kFCz && L.Q == kFQ && L.R == kFR;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ void features_fast(const EpiArgs& a, int row, int h, bool empty, uint16_t* frow) {
+  const int H = a.L.H;
+  const float4* __restrict__ o4 = reinterpret_cast<const float4*>(a.o + ((size_t)row * H + h) * kFDO);
+  float ov[kFDO];
+#pragma unroll
+  for (int k = 0; k < kFDO / 4; ++k) {
+    const float4 v = o4[k];
+    ov[4 * k] = v.x; ov[4 * k + 1] = v.y; ov[4 * k + 2] = v.z; ov[4 * k + 3] = v.w;
   }
+  const uint4* __restrict__ z4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.zl) +
+                                                                (size_t)row * kFR * kFCz);
+  uint4 zv[kFR * kFCz / 8];
+#pragma unroll
+  for (int k = 0; k < kFR * kFCz / 8; ++k) zv[k] = z4[k];
+  const uint16_t* __restrict__ rt = reinterpret_cast<const uint16_t*>(a.rot) + (size_t)row * 9;
+  const uint16_t* __restrict__ tt = reinterpret_cast<const uint16_t*>(a.trans) + (size_t)row * 3;
+  float Rm[9], tr[3];
+#pragma unroll
+  for (int e = 0; e < 9; ++e) Rm[e] = bf16_bits_to_f32(rt[e]);
+#pragma unroll
+  for (int e = 0; e < 3; ++e) tr[e] = bf16_bits_to_f32(tt[e]);
+  const float keep = empty ? 0.f : 1.f;
+  const int offx = H * kFDv, offy = offx + H * kFQ, offz = offy + H * kFQ, offl = offz + H * kFQ,
+            offp = offl + H * kFQ;
+  // scalar
+#pragma unroll
+  for (int k = 0; k < kFDv / 8; ++k) {
+    uint4 v;
+    v.x = pack_bf16(keep * ov[8 * k], keep * ov[8 * k + 1]);
+    v.y = pack_bf16(keep * ov[8 * k + 2], keep * ov[8 * k + 3]);
+    v.z = pack_bf16(keep * ov[8 * k + 4], keep * ov[8 * k + 5]);
+    v.w = pack_bf16(keep * ov[8 * k + 6], keep * ov[8 * k + 7]);
+    *reinterpret_cast<uint4*>(frow + h * kFDv + 8 * k) = v;
+  }
+  // pair: sum_r zl_r * o_zr_r
+#pragma unroll
+  for (int k = 0; k < kFCz / 8; ++k) {
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = 8 * k + e;
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 0; r < kFR; ++r) {
+        const uint4 zz = zv[(r * kFCz + c) / 8];
+        const uint32_t wd = (e >> 1) == 0 ? zz.x : ((e >> 1) == 1 ? zz.y : ((e >> 1) == 2 ? zz.z : zz.w));
+        const float zlv = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+        acc = fmaf(zlv, ov[kFDv + r * kFCz + c], acc);
+      }
+      pv[e] = keep * acc;
+    }
+    uint4 v;
+    v.x = pack_bf16(pv[0], pv[1]); v.y = pack_bf16(pv[2], pv[3]);
+    v.z = pack_bf16(pv[4], pv[5]); v.w = pack_bf16(pv[6], pv[7]);
+    *reinterpret_cast<uint4*>(frow + offp + h * kFCz + 8 * k) = v;
+  }
+  // points: R^T (g - t), lengths
+  float lx[kFQ], ly[kFQ], lz[kFQ], ll[kFQ];
+#pragma unroll
+  for (int q = 0; q < kFQ; ++q) {
+    const float gx = ov[kFDv + kFR * kFCz + 3 * q] - tr[0];
+    const float gy = ov[kFDv + kFR * kFCz + 3 * q + 1] - tr[1];
+    const float gz = ov[kFDv + kFR * kFCz + 3 * q + 2] - tr[2];
+    const float x = Rm[0] * gx + Rm[3] * gy + Rm[6] * gz;
+    const float y = Rm[1] * gx + Rm[4] * gy + Rm[7] * gz;
+    const float z = Rm[2] * gx + Rm[5] * gy + Rm[8] * gz;
+    lx[q] = keep * x; ly[q] = keep * y; lz[q] = keep * z;
+    ll[q] = keep * sqrtf(x * x + y * y + z * z + a.eps);
+  }
+  float4* __restrict__ lp = reinterpret_cast<float4*>(a.local + ((size_t)row * H + h) * kFQ * 3);
+#pragma unroll
+  for (int k = 0; k < kFQ * 3 / 4; ++k) {
+    float t4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = 4 * k + e, q = idx / 3, c = idx % 3;
+      t4[e] = c == 0 ? lx[q] : (c == 1 ? ly[q] : lz[q]);
+    }
+    lp[k] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+  }
+  auto st8 = [&](int off, const float* v) {
+    uint4 u;
+    u.x = pack_bf16(v[0], v[1]); u.y = pack_bf16(v[2], v[3]);
+    u.z = pack_bf16(v[4], v[5]); u.w = pack_bf16(v[6], v[7]);
+    *reinterpret_cast<uint4*>(frow + off) = u;
+  };
+  st8(offx + h * kFQ, lx);
+  st8(offy + h * kFQ, ly);
+  st8(offz + h * kFQ, lz);
+  st8(offl + h * kFQ, ll);
 }
 
 // ---------------------------------------------------------------- matrix-core path
-constexpr int kEpiRows = 32;
-
-__global__ __launch_bounds__(256) void epilogue_mfma_kernel(EpiArgs a) {
+// RPW residues per workgroup, 8 RPW threads (RPW / 8 wavefronts).  Phase 1
+// builds the features; phase 2 streams w_out^T through LDS in chunks of 64
+// features (double-buffered, loaded cooperatively with 16-byte loads) and
+// every wavefront accumulates 32x32 output tiles.
+constexpr int kWChunk = 64;                 // features per w_out chunk
+constexpr int kWPitch = kWChunk + 8;        // LDS pitch (elements) of a chunk row
+template <int RPW>
+__global__ __launch_bounds__(RPW * 8) void epilogue_mfma_kernel(EpiArgs a) {
+  constexpr int NT_ = RPW * 8;     // threads
+  constexpr int NW = NT_ / 64;     // wavefronts
+  constexpr int RB = RPW / 32;     // 32-row blocks
   const Layout& L = a.L;
-  extern __shared__ __attribute__((aligned(16))) uint16_t efeat[];  // [32][FP] bf16
-  __shared__ int s_empty[kEpiRows];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
-  const int row0 = blockIdx.x * kEpiRows;
-  const int total = L.B * L.N, H = L.H, F = a.F, FP = a.FP;
-  if (tid < kEpiRows) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t efeat[];  // [RPW][FP] then 2 x [Cout][kWPitch]
+  __shared__ int s_empty[RPW];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row0 = blockIdx.x * RPW;
+  const int total = L.B * L.N, H = L.H, F = L.F, FP = a.FP, LP = L.FP, Cout = L.Cout;
+  uint16_t* wbuf = efeat + (size_t)RPW * FP;
+  const uint16_t* __restrict__ wt = a.wt;
+  if (tid < RPW) {
     const int row = row0 + tid;
-    int e = 1;
-    if (row < total) {
-      const int b = row / L.N, i = row % L.N;
-      e = !(a.lse[((size_t)b * H) * L.N + i] > -INFINITY);
-    }
-    s_empty[tid] = e;
+    s_empty[tid] = row < total ? (int)row_empty(a, row) : 1;
   }
-  // zero the padded tail columns of every row
-  for (int x = tid; x < kEpiRows * (FP - F); x += 256) efeat[(x / (FP - F)) * FP + F + x % (FP - F)] = 0;
+  // padding columns [F, LP) of every row are zero
+  for (int x = tid; x < RPW * (LP - F); x += NT_) efeat[(x / (LP - F)) * FP + F + x % (LP - F)] = 0;
+  // first w_out chunk in flight while the features are built
+  const int nchunk = LP / kWChunk + (LP % kWChunk != 0);
+  const int cpr = kWChunk / 8;  // 16-byte pieces per chunk row
+  auto load_chunk = [&](int c, uint4* reg) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int x = tid + k * NT_;  // piece index
+      const int col = x / cpr, f = c * kWChunk + (x % cpr) * 8;
+      reg[k] = (col < Cout && f < LP && x < Cout * cpr) ? *reinterpret_cast<const uint4*>(wt + (size_t)col * LP + f)
+                                                         : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_chunk = [&](int buf, const uint4* reg) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int x = tid + k * NT_;
+      if (x < Cout * cpr)
+        *reinterpret_cast<uint4*>(wbuf + (size_t)buf * Cout * kWPitch + (x / cpr) * kWPitch + (x % cpr) * 8) = reg[k];
+    }
+  };
+  // three chunks of w_out in flight in registers (ring), two in LDS
+  uint4 wr0[4], wr1[4], wr2[4];
+  load_chunk(0, wr0);
+  load_chunk(1, wr1);
+  load_chunk(2, wr2);
   __syncthreads();
-  for (int pr = tid; pr < kEpiRows * H; pr += 256) {
-    const int r = pr / H, h = pr % H, row = row0 + r;
+  if (fast_dims(L)) {
+    for (int x = tid; x < RPW * H; x += NT_) {
+      const int r = x / H, h = x % H, row = row0 + r;
+      uint16_t* frow = efeat + (size_t)r * FP;
+      if (row < total) {
+        features_fast(a, row, h, s_empty[r] != 0, frow);
+      } else {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        for (int k = 0; k < kFDv / 8; ++k) *reinterpret_cast<uint4*>(frow + h * kFDv + 8 * k) = z;
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(frow + H * kFDv + k * H * kFQ + h * kFQ) = z;
+        for (int k = 0; k < kFCz / 8; ++k)
+          *reinterpret_cast<uint4*>(frow + H * (kFDv + 4 * kFQ) + h * kFCz + 8 * k) = z;
+      }
+    }
+  } else {
+  const int nI = (L.Dv + 3) / 4 + (L.Cz + 3) / 4 + L.Q;
+  const int items = RPW * H * nI;
+#pragma unroll 4
+  for (int x = tid; x < items; x += NT_) {
+    const int it = x % nI, rh = x / nI;
+    const int r = rh / H, h = rh % H, row = row0 + r;
     uint16_t* frow = efeat + (size_t)r * FP;
     if (row < total) {
-      build_features<true, uint16_t>(a, row, h, s_empty[r] != 0, frow);
+      feature_item<true, uint16_t>(a, row, h, it, s_empty[r] != 0, frow);
     } else {
-      const int Dv = L.Dv, Q = L.Q, Cz = L.Cz;
-      const int offx = H * Dv, offp = offx + 4 * H * Q;
-      for (int d = 0; d < Dv; ++d) frow[h * Dv + d] = 0;
-      for (int q = 0; q < Q; ++q)
-        for (int k = 0; k < 4; ++k) frow[offx + k * H * Q + h * Q + q] = 0;
-      for (int c = 0; c < Cz; ++c) frow[offp + h * Cz + c] = 0;
+      // rows past the end: zero features (their update is not written)
+      const int nS = (L.Dv + 3) / 4, nP = (L.Cz + 3) / 4;
+      const int offx = H * L.Dv, offp = offx + 4 * H * L.Q;
+      if (it < nS) {
+        for (int e = 0; e < 4; ++e) if (4 * it + e < L.Dv) frow[h * L.Dv + 4 * it + e] = 0;
+      } else if (it < nS + nP) {
+        for (int e = 0; e < 4; ++e) if (4 * (it - nS) + e < L.Cz) frow[offp + h * L.Cz + 4 * (it - nS) + e] = 0;
+      } else {
+        const int q = it - nS - nP;
+        for (int k = 0; k < 4; ++k) frow[offx + k * H * L.Q + h * L.Q + q] = 0;
+      }
     }
   }
+  }
+  store_chunk(0, wr0);
   __syncthreads();
-  // update[32 x Cout] = feat[32 x F] @ w_out[F x Cout]; wave w takes column blocks w, w+4, ...
-  const int Cout = L.Cout;
-  const uint16_t* wo = reinterpret_cast<const uint16_t*>(a.w_out);
-  const int nks = FP / 16;
-  for (int cb = w; cb * 32 < Cout; cb += 4) {
-    const int col = cb * 32 + l32;
-    const bool cin = col < Cout;
-    f32x16_t acc = f32x16_t{};
-    for (int ks = 0; ks < nks; ++ks) {
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(efeat + (size_t)l32 * FP + ks * 16 + half * 8);
-      uint16_t bw[8];
+  // output tiles: (row block, 32-column block), wavefront w takes tiles w, w+NW, ...
+  const int ncb = (Cout + 31) / 32;
+  const int ntiles = RB * ncb;
+  constexpr int MAXT = 2;  // tiles per wavefront held in registers
+  f32x16_t acc[MAXT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int f = ks * 16 + half * 8 + e;
-        bw[e] = (cin && f < F) ? wo[(size_t)f * Cout + col] : (uint16_t)0;
+  for (int k = 0; k < MAXT; ++k) acc[k] = f32x16_t{};
+  auto compute_chunk = [&](int c) {
+    const uint16_t* wb = wbuf + (size_t)(c & 1) * Cout * kWPitch;
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k) {
+      const int ti = w + k * NW;
+      if (ti < ntiles) {
+        const int rb = ti % RB, cb = ti / RB;
+        const int colr = min(cb * 32 + l32, Cout - 1);
+#pragma unroll
+        for (int ks = 0; ks < kWChunk / 16; ++ks) {
+          const int f = c * kWChunk + ks * 16;
+          if (f < LP) {
+            const bf16x8_t af =
+                *reinterpret_cast<const bf16x8_t*>(efeat + (size_t)(rb * 32 + l32) * FP + f + half * 8);
+            const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t*>(wb + (size_t)colr * kWPitch + ks * 16 + half * 8);
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[k], 0, 0, 0);
+          }
+        }
       }
-      uint4 pk;
-      pk.x = bw[0] | ((uint32_t)bw[1] << 16);
-      pk.y = bw[2] | ((uint32_t)bw[3] << 16);
-      pk.z = bw[4] | ((uint32_t)bw[5] << 16);
-      pk.w = bw[6] | ((uint32_t)bw[7] << 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8_t, pk), acc, 0, 0, 0);
     }
-    if (cin) {
-      const float bo = ld<true>(a.b_out, col);
+  };
+  // chunk c is in LDS buffer c & 1; chunk c+1 waits in the ring register set
+  // (c+1) % 3 and is stored after chunk c's products; chunk c+3 is then
+  // fetched into the set chunk c used
+  auto step = [&](int c, uint4* next, uint4* mine) {
+    compute_chunk(c);
+    if (c + 1 < nchunk) store_chunk((c + 1) & 1, next);
+    if (c + 3 < nchunk) load_chunk(c + 3, mine);
+    __syncthreads();
+  };
+  for (int c = 0; c < nchunk; c += 3) {
+    step(c, wr1, wr0);
+    if (c + 1 < nchunk) step(c + 1, wr2, wr1);
+    if (c + 2 < nchunk) step(c + 2, wr0, wr2);
+  }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = 8 * (r >> 2) + 4 * half + (r & 3);
-        const int row = row0 + rr;
-        if (row < total) a.update[(size_t)row * Cout + col] = s_empty[rr] ? 0.f : acc[r] + bo;
-      }
+  for (int k = 0; k < MAXT; ++k) {
+    const int ti = w + k * NW;
+    if (ti >= ntiles) continue;
+    const int rb = ti % RB, cb = ti / RB;
+    const int col = cb * 32 + l32;
+    if (col >= Cout) continue;
+    const float bo = ld<true>(a.b_out, col);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int row = row0 + rr;
+      if (row < total) a.update[(size_t)row * Cout + col] = s_empty[rr] ? 0.f : acc[k][r] + bo;
     }
   }
 }
@@ -146,20 +369,17 @@ __global__ __launch_bounds__(256) void epilogue_f32_kernel(EpiArgs a) {
   __shared__ int s_empty[kEpiRowsF32];
   const int tid = threadIdx.x;
   const int row0 = blockIdx.x * kEpiRowsF32;
-  const int total = L.B * L.N, H = L.H, F = a.F, FP = a.FP;
+  const int total = L.B * L.N, H = L.H, F = L.F, FP = a.FP;
   if (tid < kEpiRowsF32) {
     const int row = row0 + tid;
-    int e = 1;
-    if (row < total) {
-      const int b = row / L.N, i = row % L.N;
-      e = !(a.lse[((size_t)b * H) * L.N + i] > -INFINITY);
-    }
-    s_empty[tid] = e;
+    s_empty[tid] = row < total ? (int)row_empty(a, row) : 1;
   }
   __syncthreads();
-  for (int pr = tid; pr < kEpiRowsF32 * H; pr += 256) {
-    const int r = pr / H, h = pr % H, row = row0 + r;
-    if (row < total) build_features<false, float>(a, row, h, s_empty[r] != 0, ffeat + (size_t)r * FP);
+  const int nI = (L.Dv + 3) / 4 + (L.Cz + 3) / 4 + L.Q;
+  for (int x = tid; x < kEpiRowsF32 * H * nI; x += 256) {
+    const int it = x % nI, rh = x / nI;
+    const int r = rh / H, h = rh % H, row = row0 + r;
+    if (row < total) feature_item<false, float>(a, row, h, it, s_empty[r] != 0, ffeat + (size_t)r * FP);
   }
   __syncthreads();
   const int Cout = L.Cout;
@@ -176,39 +396,70 @@ __global__ __launch_bounds__(256) void epilogue_f32_kernel(EpiArgs a) {
   }
 }
 
-hipError_t launch_epilogue(const Layout& L, const float* o, const float* lse, const ipa_epi_in* in, float eps,
+template <typename K>
+static hipError_t allow_lds(K kernel, size_t shm, size_t* done) {
+  if (shm > 64 * 1024 && shm > *done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    *done = shm;
+  }
+  return hipSuccess;
+}
+
+// LDS bytes of the matrix-core epilogue for RPW residues per workgroup:
+// features plus two w_out chunks
+static inline size_t epi_lds_bytes(const Layout& L, int rpw) {
+  return (size_t)rpw * (L.FP + 8) * 2 + 2 * (size_t)L.Cout * kWPitch * 2;
+}
+
+// the output tiles of a workgroup must fit MAXT (2) per wavefront, and the
+// chunk loads 4 pieces per thread
+static inline bool epi_fits(const Layout& L, int rpw) {
+  const int nw = rpw / 8, ntiles = (rpw / 32) * ((L.Cout + 31) / 32);
+  return epi_lds_bytes(L, rpw) <= 160 * 1024 && ntiles <= 2 * nw && L.Cout * (kWChunk / 8) <= 4 * rpw * 8;
+}
+
+bool epilogue_supported(const Layout& L) {
+  if (L.mfma) return epi_fits(L, 32) || epi_fits(L, 64);
+  return (size_t)kEpiRowsF32 * (L.F + 1) * 4 <= 160 * 1024;
+}
+
+hipError_t launch_epilogue(const Layout& L, void* ws, const float* o, const float* lse, const ipa_epi_in* in, float eps,
                            float* update, float* local, hipStream_t st) {
   EpiArgs a;
   a.L = L;
   a.o = o; a.lse = lse;
   a.zl = in->zl; a.rot = in->rotation; a.trans = in->translation; a.w_out = in->w_out; a.b_out = in->b_out;
   a.update = update; a.local = local; a.eps = eps;
-  a.F = L.H * (L.Dv + 4 * L.Q + L.Cz);
+  a.wt = nullptr;
   const int total = L.B * L.N;
   if (L.mfma) {
-    a.FP = round_up(a.F, 16) + 8;  // +8 elements: 16-byte row skew for conflict-free fragment reads
-    // the tail [F, FP) is zeroed in the kernel; the MFMA loop reads FP - 8 columns
-    const size_t shm = (size_t)kEpiRows * a.FP * 2;
-    if (shm > 160 * 1024) return hipErrorInvalidValue;
-    static size_t attr_set = 0;  // largest dynamic LDS size enabled so far
-    if (shm > 64 * 1024 && shm > attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&epilogue_mfma_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    uint16_t* wt = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.off_wt);
+    hipLaunchKernelGGL(transpose_wout_kernel, dim3((L.FP + 63) / 64, (L.Cout + 63) / 64), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(in->w_out), wt, L.F, L.FP, L.Cout);
+    a.wt = wt;
+    a.FP = L.FP + 8;  // +8 elements: 16-byte row skew for conflict-free fragment reads
+    // 64 residues per workgroup when that still gives every CU a workgroup
+    if (epi_fits(L, 64) && (total + 63) / 64 >= 256) {
+      static size_t done = 0;
+      const size_t shm = epi_lds_bytes(L, 64);
+      hipError_t e = allow_lds(&epilogue_mfma_kernel<64>, shm, &done);
       if (e != hipSuccess) return e;
-      attr_set = shm;
+      hipLaunchKernelGGL(epilogue_mfma_kernel<64>, dim3((total + 63) / 64), dim3(512), shm, st, a);
+    } else {
+      static size_t done = 0;
+      const size_t shm = epi_lds_bytes(L, 32);
+      hipError_t e = allow_lds(&epilogue_mfma_kernel<32>, shm, &done);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(epilogue_mfma_kernel<32>, dim3((total + 31) / 32), dim3(256), shm, st, a);
     }
-    hipLaunchKernelGGL(epilogue_mfma_kernel, dim3((total + kEpiRows - 1) / kEpiRows), dim3(256), shm, st, a);
   } else {
-    a.FP = a.F + 1;
+    a.FP = L.F + 1;
     const size_t shm = (size_t)kEpiRowsF32 * a.FP * 4;
-    if (shm > 160 * 1024) return hipErrorInvalidValue;
-    static size_t attr_set = 0;
-    if (shm > 64 * 1024 && shm > attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&epilogue_f32_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-      if (e != hipSuccess) return e;
-      attr_set = shm;
-    }
+    static size_t done = 0;
+    hipError_t e = allow_lds(&epilogue_f32_kernel, shm, &done);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(epilogue_f32_kernel, dim3((total + kEpiRowsF32 - 1) / kEpiRowsF32), dim3(256), shm, st, a);
   }
   return hipGetLastError();
