@@ -120,6 +120,20 @@ def cpu_baseline(inp, flops, budget_s=12.0):
                 seconds_per_call=per_call_s)
 
 
+def copy_calibration(mib: int, reps: int = 3) -> None:
+    """Plain device-to-device copies of a known size: the HBM counters
+    (FETCH_SIZE, WRITE_SIZE) read for this kernel calibrate those read for
+    the FlashIPA kernels in the same profiling pass."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +142,8 @@ def main():
     ap.add_argument("--workload", default="sweep_16384")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run only plain copies of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -135,6 +151,9 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     inp = make_workload(args.workload)
     shape = inp["shape"]
     flops = eff_flops(shape, inp["mask"])

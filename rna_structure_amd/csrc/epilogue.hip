@@ -41,14 +41,19 @@ __global__ __launch_bounds__(256) void transpose_wout_kernel(const uint16_t* w, 
   __shared__ uint16_t tile[64][65];
   const int f0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int f = f0 + r, c = c0 + tx;
-    tile[r][tx] = (f < F && c < Cout) ? w[(size_t)f * Cout + c] : (uint16_t)0;
+  uint16_t v[16];  // all 16 loads of a thread in flight together
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int f = f0 + ty + 4 * k, c = c0 + tx;
+    v[k] = (f < F && c < Cout) ? w[(size_t)f * Cout + c] : (uint16_t)0;
   }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) tile[ty + 4 * k][tx] = v[k];
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
-    const int c = c0 + r, f = f0 + tx;
-    if (c < Cout && f < FP) wt[(size_t)c * FP + f] = tile[tx][r];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = c0 + ty + 4 * k, f = f0 + tx;
+    if (c < Cout && f < FP) wt[(size_t)c * FP + f] = tile[tx][ty + 4 * k];
   }
 }
 

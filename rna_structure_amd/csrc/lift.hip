@@ -346,6 +346,404 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- vectorised matrix-core lift
+// Same output as lift_kernel<true> for shapes whose D, Dv and Cz are
+// multiples of 8, so that every 8-column chunk of a lifted row comes from one
+// 16-byte piece of one input row.  Every global load of a workgroup is issued
+// up front into registers (one memory latency per workgroup instead of one
+// per loop trip); key and pair rows are then copied with 16-byte stores, the
+// value tile is transposed through LDS, the query rows are scaled and rounded
+// 8 columns at a time, and one thread per key writes that key's geometric
+// columns (their layout is fixed by P at compile time).  LDS rows are padded
+// to odd word strides where lanes walk down a column.  Units (b, t, h) are
+// handed out so that the H heads of one key tile run back to back on one XCD
+// and share its L2 for zr, zl and the frames.
+constexpr int kFastVRows = 160;      // Dv + R Cz <= 32 NVB - 1 <= 159
+constexpr int kFastVPitch = 66;      // 16-bit elements per transposed LDS row (33 words)
+constexpr int kFastStage = 8;        // 16-byte pieces of [k | zr | v] per thread: 64 (D+RCz+Dv)/8 <= 2048
+constexpr int kFastQL = 5;           // pieces of a query row per thread: 64 QW/8 <= 1280
+constexpr int kFastPts = 5;          // points per thread: 64 (2P + Q) <= 1280
+
+// x / d for 0 <= x < 2^16 and 0 < d < 2^16: m = ceil(2^32 / d)
+struct FastDiv {
+  uint32_t m;
+  int d;
+};
+static inline FastDiv make_fastdiv(int d) {
+  return FastDiv{(uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d), d};
+}
+__device__ __forceinline__ int fdiv(int x, FastDiv f) { return (int)__umulhi((uint32_t)x, f.m); }
+
+__device__ __forceinline__ uint4 pack8(const uint16_t* v) {
+  uint4 pk;
+  pk.x = v[0] | ((uint32_t)v[1] << 16);
+  pk.y = v[2] | ((uint32_t)v[3] << 16);
+  pk.z = v[4] | ((uint32_t)v[5] << 16);
+  pk.w = v[6] | ((uint32_t)v[7] << 16);
+  return pk;
+}
+
+struct LiftFastArgs {
+  int units, per_xcd, pm_vec;
+  FastDiv nch, qch;
+};
+
+static inline bool lift_fast_fits(const Layout& L) {
+  return L.mfma && L.D % 8 == 0 && L.Dv % 8 == 0 && L.Cz % 8 == 0 && L.Dv + L.RCz <= kFastVRows &&
+         L.Cz <= 160 && 64 * ((L.D + L.RCz + L.Dv) / 8) <= 256 * kFastStage &&
+         64 * (L.QW / 8) <= 256 * kFastQL && 64 * (2 * L.P + L.Q) <= 256 * kFastPts;
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs f) {
+  constexpr int P3 = 3 * P;
+  constexpr int GS = P <= 4 ? 3 : 4;
+  const Layout& L = a.L;
+  const int N = L.N, H = L.H, Q = L.Q, D = L.D, Dv = L.Dv, RCz = L.RCz, Cz = L.Cz;
+  const int u = (int)(blockIdx.x % 8) * f.per_xcd + (int)(blockIdx.x / 8);
+  if (u >= f.units) return;
+  const int h = u % H, t = (u / H) % L.NT, b = u / (H * L.NT);
+  const int tid = threadIdx.x;
+  const int nk = D / 8, nz = RCz / 8, nv = Dv / 8, nch = f.nch.d;
+  const int QW = L.QW, qch = f.qch.d;
+  const int npt = 2 * P + Q;
+
+  __shared__ float s_rot[64][9];
+  __shared__ float s_tr[64][3];
+  __shared__ int s_valid[64];
+  __shared__ uint32_t s_vmask[2];  // valid keys, bit jj of word jj / 32
+  __shared__ float s_w[64][P3 % 2 ? P3 : P3 + 1];  // b - c (key points, centred), odd row stride
+  __shared__ float s_a[64][17];        // a (query points, global)
+  __shared__ __attribute__((aligned(16))) float s_xT[32][64];  // x - c of valid keys, coordinate-major
+  __shared__ float s_wp[160];          // w_pair[h, :]
+  __shared__ __attribute__((aligned(16))) uint16_t s_vzT[kFastVRows][kFastVPitch];  // [v | zr] of valid keys
+  __shared__ float s_c[4];
+  __shared__ float s_gam;
+
+  // ---- 1. every global load of the workgroup
+  float fr[13];  // threads 0..63: translation, rotation, mask of residue tid
+  if (tid < 64) {
+    const int j = t * 64 + tid;
+    if (j < N) {
+      const size_t o = ((size_t)b * N + j) * 3;
+#pragma unroll
+      for (int e = 0; e < 3; ++e) fr[e] = ld<true>(a.trans, o + e);
+#pragma unroll
+      for (int e = 0; e < 9; ++e) fr[3 + e] = ld<true>(a.rot, ((size_t)b * N + j) * 9 + e);
+      fr[12] = a.mask[(size_t)b * N + j] != 0 ? 1.f : 0.f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 13; ++e) fr[e] = 0.f;
+    }
+  }
+  const float wp_raw = tid < Cz ? ld<true>(a.wpair, (size_t)h * Cz + tid) : 0.f;
+  const float pwr = ld<true>(a.pwr, h);
+  uint4 stg[kFastStage];
+#pragma unroll
+  for (int k = 0; k < kFastStage; ++k) {
+    const int x = tid + 256 * k, r = fdiv(x, f.nch), c = x - r * nch, j = t * 64 + r;
+    stg[k] = make_uint4(0, 0, 0, 0);
+    if (x < 64 * nch && j < N) {
+      if (c < nk)
+        stg[k] = reinterpret_cast<const uint4*>(a.k)[(((size_t)b * N + j) * H + h) * nk + c];
+      else if (c < nk + nz)
+        stg[k] = reinterpret_cast<const uint4*>(a.zr)[((size_t)b * N + j) * nz + (c - nk)];
+      else
+        stg[k] = reinterpret_cast<const uint4*>(a.v)[(((size_t)b * N + j) * H + h) * nv + (c - nk - nz)];
+    }
+  }
+  uint4 qlr[kFastQL];
+#pragma unroll
+  for (int k = 0; k < kFastQL; ++k) {
+    const int x = tid + 256 * k, r = fdiv(x, f.qch), c = x - r * qch, i = t * 64 + r;
+    qlr[k] = make_uint4(0, 0, 0, 0);
+    if (x < 64 * qch && i < N) {
+      if (c < nk)
+        qlr[k] = reinterpret_cast<const uint4*>(a.q)[(((size_t)b * N + i) * H + h) * nk + c];
+      else if (c < nk + nz)
+        qlr[k] = reinterpret_cast<const uint4*>(a.zl)[((size_t)b * N + i) * nz + (c - nk)];
+    }
+  }
+  float pts[kFastPts][3];
+#pragma unroll
+  for (int k = 0; k < kFastPts; ++k) {
+    const int x = tid + 256 * k, r = x % 64, it = x / 64, j = t * 64 + r;
+    pts[k][0] = pts[k][1] = pts[k][2] = 0.f;
+    if (x < 64 * npt && j < N) {
+      const void* src;
+      size_t o;
+      if (it < P) { src = a.kp; o = ((((size_t)b * N + j) * H + h) * P + it) * 3; }
+      else if (it < 2 * P) { src = a.qp; o = ((((size_t)b * N + j) * H + h) * P + (it - P)) * 3; }
+      else { src = a.vp; o = ((((size_t)b * N + j) * H + h) * Q + (it - 2 * P)) * 3; }
+      pts[k][0] = ld<true>(src, o); pts[k][1] = ld<true>(src, o + 1); pts[k][2] = ld<true>(src, o + 2);
+    }
+  }
+
+  // ---- 2. frames, validity and the tile centroid (wavefront 0)
+  if (tid < Cz) s_wp[tid] = wp_raw;
+  if (tid < 64) {
+    const int valid = fr[12] != 0.f;
+    const float tx = fr[0], ty = fr[1], tz = fr[2];
+    s_valid[tid] = valid;
+    const uint64_t vm = __ballot(valid);
+    if (tid == 0) { s_vmask[0] = (uint32_t)vm; s_vmask[1] = (uint32_t)(vm >> 32); }
+    s_tr[tid][0] = tx; s_tr[tid][1] = ty; s_tr[tid][2] = tz;
+#pragma unroll
+    for (int e = 0; e < 9; ++e) s_rot[tid][e] = fr[3 + e];
+    float sx = valid ? tx : 0.f, sy = valid ? ty : 0.f, sz = valid ? tz : 0.f, sn = valid ? 1.f : 0.f;
+    for (int off = 32; off > 0; off >>= 1) {
+      sx += __shfl_xor(sx, off);
+      sy += __shfl_xor(sy, off);
+      sz += __shfl_xor(sz, off);
+      sn += __shfl_xor(sn, off);
+    }
+    if (tid == 0) {
+      float cx = 0.f, cy = 0.f, cz = 0.f;
+      if (sn > 0.f) { cx = sx / sn; cy = sy / sn; cz = sz / sn; }
+      // any fixed point near the tile will do; on the 4-angstrom grid it is
+      // exact in fp16 and differences of two centroids are exact too
+      const float grid = (float)kCentGrid;
+      cx = grid * rintf(cx / grid); cy = grid * rintf(cy / grid); cz = grid * rintf(cz / grid);
+      cx = f16_bits_to_f32(hi16(cx)); cy = f16_bits_to_f32(hi16(cy)); cz = f16_bits_to_f32(hi16(cz));
+      s_c[0] = cx; s_c[1] = cy; s_c[2] = cz; s_c[3] = 0.f;
+      s_gam = 0.5f * softplus_f(pwr) * sqrtf(2.0f / (27.0f * (float)P));
+    }
+  }
+  __syncthreads();
+  const float cx = s_c[0], cy = s_c[1], cz = s_c[2];
+  const float gam = s_gam;
+  const float gl = gam * kLog2e;
+
+  // ---- 3. [k | zr] straight into the key tile, [v | zr] transposed into LDS
+  uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * L.KROW;
+#pragma unroll
+  for (int k = 0; k < kFastStage; ++k) {
+    const int x = tid + 256 * k, r = fdiv(x, f.nch), c = x - r * nch;
+    if (x < 64 * nch) {
+      const uint4 val = s_valid[r] ? stg[k] : make_uint4(0, 0, 0, 0);
+      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
+      if (c < nk) {
+        *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + 8 * c) = val;
+      } else if (c < nk + nz) {
+        const int cz8 = c - nk;
+        *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + D + 8 * cz8) = val;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_vzT[Dv + 8 * cz8 + e][r] = e16[e];
+      } else {
+        const int cv = c - nk - nz;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][r] = e16[e];
+      }
+    }
+  }
+  // global points: key points (centred), query points, value points (centred,
+  // zero for keys that are masked or past the end)
+#pragma unroll
+  for (int k = 0; k < kFastPts; ++k) {
+    const int x = tid + 256 * k, r = x % 64, it = x / 64;
+    if (x < 64 * npt) {
+      const bool in = t * 64 + r < N;
+      const float* Rm = s_rot[r];
+      const float tx = s_tr[r][0], ty = s_tr[r][1], tz = s_tr[r][2];
+      const float lx = pts[k][0], ly = pts[k][1], lz = pts[k][2];
+      const float gx = Rm[0] * lx + Rm[1] * ly + Rm[2] * lz + tx;
+      const float gy = Rm[3] * lx + Rm[4] * ly + Rm[5] * lz + ty;
+      const float gz = Rm[6] * lx + Rm[7] * ly + Rm[8] * lz + tz;
+      if (it < P) {
+        s_w[r][3 * it] = in ? gx - cx : 0.f;
+        s_w[r][3 * it + 1] = in ? gy - cy : 0.f;
+        s_w[r][3 * it + 2] = in ? gz - cz : 0.f;
+      } else if (it < 2 * P) {
+        const int p = it - P;
+        s_a[r][3 * p] = gx; s_a[r][3 * p + 1] = gy; s_a[r][3 * p + 2] = gz;
+      } else {
+        const int q = it - 2 * P;
+        const bool v = in && s_valid[r];
+        s_xT[3 * q][r] = v ? gx - cx : 0.f;
+        s_xT[3 * q + 1][r] = v ? gy - cy : 0.f;
+        s_xT[3 * q + 2][r] = v ? gz - cz : 0.f;
+      }
+    }
+  }
+  // lifted query rows [q sq | w_pair zl sp | 0]
+  {
+    const float sq = kLog2e / sqrtf(3.0f * (float)D);
+    const float sp = kLog2e / sqrtf(3.0f);
+    uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql);
+#pragma unroll
+    for (int k = 0; k < kFastQL; ++k) {
+      const int x = tid + 256 * k, r = fdiv(x, f.qch), c = x - r * qch;
+      if (x < 64 * qch) {
+        const int i = t * 64 + r;
+        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&qlr[k]);
+        uint16_t out[8];
+        if (c < nk) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[e] = f32_to_bf16_bits(bf16_bits_to_f32(e16[e]) * sq);
+        } else if (c < nk + nz) {
+          const int c0 = (8 * (c - nk)) % Cz;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[e] = f32_to_bf16_bits(s_wp[c0 + e] * bf16_bits_to_f32(e16[e]) * sp);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[e] = 0;
+        }
+        *reinterpret_cast<uint4*>(ql + (((size_t)b * H + h) * L.NQpad + i) * QW + 8 * c) = pack8(out);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. key rows past [k | zr] (one thread per key): zeros up to QW, the
+  // geometric columns (layout in common.h), 8 pad columns
+  const int VROWS = L.VROWS, NVB = L.NVB, DZ = Dv + RCz;
+  if (tid < 64) {
+    const int r = tid;
+    const bool valid = s_valid[r] != 0;
+    float w[P3];
+#pragma unroll
+    for (int g = 0; g < P3; ++g) w[g] = s_w[r][g];
+    float nb = 0.f, Wx = 0.f, Wy = 0.f, Wz = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      nb += w[3 * p] * w[3 * p] + w[3 * p + 1] * w[3 * p + 1] + w[3 * p + 2] * w[3 * p + 2];
+      Wx += w[3 * p]; Wy += w[3 * p + 1]; Wz += w[3 * p + 2];
+    }
+    nb = -gl * nb;
+    const float ww[3] = {2.f * gl * Wx, 2.f * gl * Wy, 2.f * gl * Wz};
+    uint16_t* krow = kt + (size_t)r * L.KROW;
+    for (int c = D + RCz; c < QW; c += 8) *reinterpret_cast<uint4*>(krow + c) = make_uint4(0, 0, 0, 0);
+    constexpr int base = 16 * (GS - 1);
+    uint16_t g16[16 * GS + 8];
+#pragma unroll
+    for (int g = 0; g < 16 * GS + 8; ++g) {
+      uint16_t val = 0;
+      if (g < base + 4) {
+        if (g < P3) val = hi16(w[g]);
+        else if (g < 2 * P3) val = lo16(w[g - P3]);
+        else if (g < 3 * P3) val = hi16(w[g - 2 * P3]);
+      } else if (g < 16 * GS) {
+        const int y = g - base;
+        if (y == 4) val = hi16(nb * (1.0f / kNormScale));
+        else if (y == 12) val = lo16(nb * (1.0f / kNormScale));
+        else if (y >= 5 && y <= 7) val = hi16(ww[y - 5]);
+        else if (y >= 13) val = lo16(ww[y - 13]);
+        else if (y >= 9 && y <= 11) val = 0x4C00;  // fp16 16.0, multiplies the query's t'/16 parts
+      }
+      g16[g] = valid ? val : (uint16_t)0;
+    }
+#pragma unroll
+    for (int c = 0; c < (16 * GS + 8) / 8; ++c) *reinterpret_cast<uint4*>(krow + QW + 8 * c) = pack8(g16 + 8 * c);
+  } else if (tid == 64) {
+    if (b == 0 && t == 0) reinterpret_cast<float*>(a.ws + L.off_gam)[h] = gam;
+    if (h == 0) {
+      float4* ck = reinterpret_cast<float4*>(a.ws + L.off_ck);
+      ck[(size_t)b * L.NT + t] = make_float4(cx, cy, cz, 0.f);
+      if (b == 0 && t == 0) {
+        Header* hd = reinterpret_cast<Header*>(a.ws);
+        hd->magic = kMagic;
+        hd->has_pair_mask = a.pm != nullptr;
+      }
+    }
+  } else if (tid >= 128 && tid < 130 && h == 0) {
+    const int hw = tid - 128;
+    uint32_t w = 0;
+    for (int jj = 0; jj < 64; ++jj) {
+      int hf;
+      const int bit = mask_bit_of_key(jj, &hf);
+      if (hf == hw && s_valid[jj]) w |= 1u << bit;
+    }
+    reinterpret_cast<uint32_t*>(a.ws + L.off_km)[((size_t)b * L.NT + t) * 2 + hw] = w;
+  }
+  // query global points: 16 floats per (b, h, i)
+  {
+    float4* qa = reinterpret_cast<float4*>(a.ws + L.off_qa);
+    const int row = tid / 4, c = (tid % 4) * 4;
+    const int i = t * 64 + row;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (i < N && c + e < P3) ? s_a[row][c + e] : 0.f;
+    qa[(((size_t)b * H + h) * L.NQpad + i) * 4 + tid % 4] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  // transposed value tile: rows d, columns kappa; columns k0 .. k0+7 hold keys
+  // j0 .. j0+3 and j0+8 .. j0+11 (j0 = vt_key_of_col(k0)), columns 64 .. 71 are zero
+  uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + L.off_vt) + (((size_t)b * H + h) * L.NT + t) * VROWS * kVCols;
+  constexpr int vch = kVCols / 8;
+  const uint32_t vm0 = s_vmask[0], vm1 = s_vmask[1];
+  for (int x = tid; x < VROWS * vch; x += 256) {
+    const int d = x / vch, kc = x % vch;
+    uint4 pk = make_uint4(0, 0, 0, 0);
+    if (kc < 8) {
+      const int j0 = vt_key_of_col(8 * kc);
+      if (d < DZ) {
+        const uint32_t* row = reinterpret_cast<const uint32_t*>(&s_vzT[d][0]);
+        pk = make_uint4(row[j0 / 2], row[j0 / 2 + 1], row[j0 / 2 + 4], row[j0 / 2 + 5]);
+      } else {
+        // valid bits of the 8 keys, in column order
+        const uint32_t word = j0 < 32 ? vm0 : vm1;
+        const uint32_t bits = ((word >> (j0 & 31)) & 0xFu) | (((word >> ((j0 & 31) + 8)) & 0xFu) << 4);
+        uint16_t one = 0;
+        const int dd = d - 32 * NVB;
+        if (d == DZ) one = 0x3F80;                          // bf16 1.0: weight sum
+        else if (dd == 3 * Q) one = 0x3C00;                 // fp16 1.0: weight sum
+        else if (dd > 3 * Q && dd <= 3 * Q + 3) one = hi16(s_c[dd - 3 * Q - 1]);  // centroid
+        uint16_t out[8];
+        if (dd >= 0 && dd < 3 * Q) {
+          const float4 lo = *reinterpret_cast<const float4*>(&s_xT[dd][j0]);
+          const float4 hi = *reinterpret_cast<const float4*>(&s_xT[dd][j0 + 8]);
+          out[0] = hi16(lo.x); out[1] = hi16(lo.y); out[2] = hi16(lo.z); out[3] = hi16(lo.w);
+          out[4] = hi16(hi.x); out[5] = hi16(hi.y); out[6] = hi16(hi.z); out[7] = hi16(hi.w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[e] = ((bits >> e) & 1u) ? one : (uint16_t)0;
+        }
+        pk = pack8(out);
+      }
+    }
+    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * kc) = pk;
+  }
+
+  // ---- 5. permitted-key words of every query row for this key tile
+  if (a.pm != nullptr && h == 0) {
+    uint32_t* pmw = reinterpret_cast<uint32_t*>(a.ws + L.off_pm);
+    for (int i = tid; i < L.NQpad; i += 256) {
+      uint32_t w[2] = {0u, 0u};
+      if (i < N && a.mask[(size_t)b * N + i]) {
+        const uint8_t* row = a.pm + ((size_t)b * N + i) * N + (size_t)t * 64;
+        if (f.pm_vec) {
+          // N is a multiple of 16 and the rows are 16-byte aligned
+          uint4 v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            v[q] = t * 64 + 16 * q < N ? *reinterpret_cast<const uint4*>(row + 16 * q) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t wd[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int jj = 16 * q + e;
+              int hf;
+              const int bit = mask_bit_of_key(jj, &hf);
+              if (((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) && s_valid[jj]) w[hf] |= 1u << bit;
+            }
+          }
+        } else {
+          for (int jj = 0; jj < 64; ++jj) {
+            if (t * 64 + jj >= N) break;
+            if (s_valid[jj] && row[jj]) {
+              int hf;
+              const int bit = mask_bit_of_key(jj, &hf);
+              w[hf] |= 1u << bit;
+            }
+          }
+        }
+      }
+      pmw[(((size_t)b * L.NQpad + i) * L.NT + t) * 2] = w[0];
+      pmw[(((size_t)b * L.NQpad + i) * L.NT + t) * 2 + 1] = w[1];
+    }
+  }
+}
+
 hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStream_t st) {
   LiftArgs a;
   a.L = L;
@@ -356,7 +754,25 @@ hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStre
   a.mask = in->mask; a.pm = in->pair_mask;
   a.ws = reinterpret_cast<char*>(ws);
   dim3 grid(L.NT, L.H, L.B);
-  if (L.mfma)
+  const bool aligned = (reinterpret_cast<uintptr_t>(in->q) | reinterpret_cast<uintptr_t>(in->k) |
+                        reinterpret_cast<uintptr_t>(in->v) | reinterpret_cast<uintptr_t>(in->zl) |
+                        reinterpret_cast<uintptr_t>(in->zr)) % 16 == 0;
+  if (aligned && lift_fast_fits(L)) {
+    LiftFastArgs f;
+    f.units = L.B * L.NT * L.H;
+    f.per_xcd = (f.units + 7) / 8;
+    f.pm_vec = in->pair_mask != nullptr && L.N % 16 == 0 && reinterpret_cast<uintptr_t>(in->pair_mask) % 16 == 0;
+    f.nch = make_fastdiv((L.D + L.RCz + L.Dv) / 8);
+    f.qch = make_fastdiv(L.QW / 8);
+    const dim3 g(8 * f.per_xcd), blk(256);
+    switch (L.P) {
+      case 1: hipLaunchKernelGGL(lift_fast_kernel<1>, g, blk, 0, st, a, f); break;
+      case 2: hipLaunchKernelGGL(lift_fast_kernel<2>, g, blk, 0, st, a, f); break;
+      case 3: hipLaunchKernelGGL(lift_fast_kernel<3>, g, blk, 0, st, a, f); break;
+      case 4: hipLaunchKernelGGL(lift_fast_kernel<4>, g, blk, 0, st, a, f); break;
+      default: hipLaunchKernelGGL(lift_fast_kernel<5>, g, blk, 0, st, a, f); break;
+    }
+  } else if (L.mfma)
     hipLaunchKernelGGL(lift_kernel<true>, grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(lift_kernel<false>, grid, dim3(256), 0, st, a);

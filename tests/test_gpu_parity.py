@@ -39,6 +39,13 @@ SMALL = [
     _case("mid-instance-bf16", IPAShape(B=1, N=150, H=2, D=16, Dv=16, P=4, Q=8, Cz=32, R=2), 14, frames="walk"),
     _case("rank1-p5-q9-bf16", IPAShape(B=1, N=100, H=2, D=8, Dv=8, P=5, Q=9, Cz=48, R=1, Cout=64), 15,
           frames="walk"),
+    # one point per head up to three: every geometric-column layout of the lift
+    _case("p1-q1-bf16", IPAShape(B=1, N=130, H=2, D=8, Dv=8, P=1, Q=1, Cz=16, R=1, Cout=32), 16, frames="walk",
+          pair_dropout=0.1),
+    _case("p2-q3-bf16", IPAShape(B=2, N=96, H=3, D=16, Dv=8, P=2, Q=3, Cz=24, R=2, Cout=48), 17, frames="walk",
+          lengths=(50, 96)),
+    _case("p3-q4-bf16", IPAShape(B=1, N=192, H=2, D=8, Dv=16, P=3, Q=4, Cz=40, R=2, Cout=64), 18, frames="gauss",
+          trans_sigma=15.0, pair_dropout=0.05),
 ]
 
 
