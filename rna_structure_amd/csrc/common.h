@@ -27,11 +27,19 @@ constexpr int kQueryTile = 128;
 // splits (u = 2 gl A against w): pairs [u_hi.w_hi | u_hi.w_lo | u_lo.w_hi].
 // The last K-step holds, with base = 16(GS-1) (query value x key value):
 //   base+4:  16 x nb_hi      base+12: 16 x nb_lo     (nb = -gl|w|^2 / 16)
+//   base+8:  16 x (-65504 for a masked key, 0 otherwise)
 //   base+5..7: -delta x WW_hi  base+13..15: -delta x WW_lo  (WW = 2 gl W)
-//   base+9..11: t'/16 in three fp16 parts x 16
+//   base+9..11: (t' - m)/16 in three fp16 parts x 16 (m: the query's running
+//               maximum in the fused kernel, 0 for plain logits)
 // so that the MFMA itself returns the complete logit.
 constexpr int kCentGrid = 4;  // angstrom
 constexpr float kNormScale = 16.0f;
+// The value tile is fp16 throughout (the probabilities multiply it as fp16).
+// Values and pair factors enter it times 2^-8: every bf16 value of magnitude
+// up to 1.6e7 stays in range, those of magnitude >= 2^-6 convert exactly and
+// smaller ones with an absolute error below 2^-17; the fused kernel's
+// normalisation multiplies the 2^8 back.
+constexpr float kVScale = 1.0f / 256.0f;
 __host__ __device__ __forceinline__ int geo_steps(int P) { return P <= 4 ? 3 : 4; }
 
 // Padding (in 16-bit elements) appended to every LDS row so that the

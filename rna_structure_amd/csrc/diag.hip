@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64) void logit_rows_mfma_kernel(DiagArgs a) {
   const char* kt0 = a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)(64 * KROW * 2);
   for (int t = 0; t < NT; ++t) {
     const uint32_t mw = perm_word(L, a.ws, has_pm, b, i, qin, qvalid, t, half);
-    geo_tile<GS>(qg, ck[(size_t)b * NT + t], gl, (float)L.P, half, bg);
+    geo_tile<GS>(qg, ck[(size_t)b * NT + t], gl, (float)L.P, 0.f, half, bg);
     f32x16_t sacc[2];
     s_tile<NQS, GS>(kt0 + (size_t)t * 64 * KROW * 2, bq, bg, l32, half, sacc);
     if (!out_row) continue;

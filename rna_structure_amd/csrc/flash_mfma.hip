@@ -82,6 +82,13 @@ template <int BYTES>
 __device__ __forceinline__ void dma_tile(const char* g, const char* s, int w, int lane) {
   constexpr int nch = (BYTES + 1023) / 1024;
   const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(s);
+  // the tile address is uniform; make that explicit for the SGPR operand
+  // (readfirstlane returns int: each half goes through uint32_t so that the
+  // low word is zero-extended, not sign-extended, when the halves are joined)
+  const uint64_t ga = (uint64_t)(uintptr_t)g;
+  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ga);
+  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
+  g = (const char*)(uintptr_t)(((uint64_t)ghi << 32) | (uint64_t)glo);
 #pragma unroll
   for (int k = 0; k < dma_per_wave<BYTES>(); ++k) {
     int ch = w + 4 * k;
@@ -99,9 +106,88 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// O^T += V~^T P^T for one 64-key value tile in LDS: 4 K-steps x (NVB + 1)
+// value blocks, consecutive MFMAs on different blocks (independent), value
+// fragments fetched DEPTH MFMAs ahead of their use so that the LDS latency
+// hides behind the preceding MFMAs.
+template <int NVB>
+__device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* ph, f32x16_t* oacc) {
+  constexpr int NB = NVB + 1;
+  constexpr int NS = 4 * NB;
+  constexpr int DEPTH = 4;
+  auto off = [](int st) { return (size_t)((st % NB) * 32 * kVCols) * 2 + (st / NB) * 32; };
+  uint4 f[DEPTH];
+#pragma unroll
+  for (int st = 0; st < DEPTH; ++st) f[st] = *reinterpret_cast<const uint4*>(vrow + off(st));
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const uint4 c = f[st % DEPTH];
+    if (st + DEPTH < NS) f[st % DEPTH] = *reinterpret_cast<const uint4*>(vrow + off(st + DEPTH));
+    oacc[st % NB] =
+        __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c), ph[st / NB], oacc[st % NB], 0, 0, 0);
+  }
+  // the first DEPTH reads, then per step its MFMA followed by the read DEPTH ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, DEPTH, 0);
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (st + DEPTH < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// One tile of the online softmax for the 32 queries of a wavefront.  S
+// arrives relative to the running maximum m of each query (m rides in the row
+// term of the last geometric K-step); keys that are masked out arrive as
+// -16 x 65504 (key-mask column) or are set to -inf here (pair-mask bits).
+// m is raised only when a row maximum exceeds it by more than 8 (log2 units),
+// so the probabilities stay below 2^8 and rescaling is rare.  Returns the
+// factor by which O and l have been scaled.
+template <bool PM>
+__device__ __forceinline__ float softmax_tile(const f32x16_t* sacc, uint32_t mw, float& m, bool& init, float& l,
+                                              f16x8_t* ph) {
+  float s[32];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb * 16 + r] = sacc[kb][r];
+  if constexpr (PM) {
+    if (!__all(mw == 0xFFFFFFFFu)) {
+#pragma unroll
+      for (int x = 0; x < 32; ++x) s[x] = ((mw >> x) & 1u) ? s[x] : -INFINITY;
+    }
+  }
+  float mt = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int x = 2; x < 32; ++x) mt = fmaxf(mt, s[x]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  // first permitted key of the row (masked keys are below -1e6), or a
+  // maximum that grew by more than 8
+  const bool need = init ? (mt > 8.0f) : (mt > -5.0e5f);
+  const float shift = need ? mt : 0.f;
+  const float alpha = (need && init) ? __builtin_amdgcn_exp2f(-mt) : 1.0f;
+  if (__any(need)) {
+#pragma unroll
+    for (int x = 0; x < 32; ++x) s[x] -= shift;
+  }
+  m += shift;
+  init = init || need;
+  float ps = 0.f;
+#pragma unroll
+  for (int x = 0; x < 32; ++x) {
+    s[x] = __builtin_amdgcn_exp2f(s[x]);
+    ps += s[x];
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ph[ks][e] = (_Float16)s[(ks >> 1) * 16 + (ks & 1) * 8 + e];
+  l = l * alpha + ps;
+  return alpha;
+}
+
 // Main loop over the key tiles and the final normalisation for one
-// wavefront's 32 queries; PM selects the per-query pair-mask words (a vector
-// load per tile) over the per-tile key-mask words (scalar loads).
+// wavefront's 32 queries.  PM selects the per-query pair-mask words (a vector
+// load per tile); without a pair mask the key mask is inside the key product.
 template <int NQS, int NVB, int GS, bool PM>
 __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* sv, int b, int h, int i, bool qin,
                                        bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
@@ -113,13 +199,13 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
   constexpr int VT_BYTES = VROWS * kVCols * 2;
   const Layout& L = a.L;
   const int N = L.N, H = L.H, NT = L.NT;
-  const bool has_pm = PM;
   const uint32_t* km = reinterpret_cast<const uint32_t*>(a.ws + L.off_km);
   const float4* ck = reinterpret_cast<const float4*>(a.ws + L.off_ck);
   f32x16_t oacc[NVB + 1];
 #pragma unroll
   for (int vb = 0; vb <= NVB; ++vb) oacc[vb] = f32x16_t{};
-  float m = -INFINITY, l = 0.f;
+  float m = 0.f, l = 0.f;
+  bool init = false;
 
   const char* ktg0 = a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)KT_BYTES;
   const char* vtg0 = a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES;
@@ -130,6 +216,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
     return __builtin_amdgcn_readfirstlane(t);
   };
   constexpr int kDK = dma_per_wave<KT_BYTES>(), kDV = dma_per_wave<VT_BYTES>();
+  const char* vrow = sv + (size_t)(l32 * kVCols) * 2 + half * 16;
 
   int t = next_tile(-1);
   if (t < NT) {
@@ -138,88 +225,35 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
   }
   while (t < NT) {
     const int tn = next_tile(t);
-    uint32_t mw;
-    if constexpr (PM) {
-      mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
-    } else {
-      const uint32_t k0 = ld_uniform(kmb + 2 * t), k1 = ld_uniform(kmb + 2 * t + 1);
-      mw = qvalid ? (half ? k1 : k0) : 0u;
-    }
-    geo_tile<GS>(qg, ld_uniform4(ck + (size_t)b * NT + t), gl, Pf, half, bg);
+    uint32_t mw = 0xFFFFFFFFu;
+    if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
+    geo_tile<GS>(qg, ld_uniform4(ck + (size_t)b * NT + t), gl, Pf, m, half, bg);
 
     // key tile t in LDS: this wave's copies are done once only the value-tile
     // copies issued after them may still be in flight; then all waves' are
-    if (has_pm) wait_vmcnt<0>(); else wait_vmcnt<kDV>();
+    if constexpr (PM) wait_vmcnt<0>(); else wait_vmcnt<kDV>();
     __syncthreads();
     f32x16_t sacc[2];
-    // raised wave priority while issuing MFMAs: the other wavefront on the
-    // SIMD (another workgroup) fills the gaps with its VALU work
+    // raised wave priority while issuing MFMAs
     __builtin_amdgcn_s_setprio(1);
     s_tile<NQS, GS>(sk, bq, bg, l32, half, sacc);
     __builtin_amdgcn_s_setprio(0);
-    asm volatile("" ::"v"(mw));  // the mask word is in registers before the next copies are issued
+    if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
     __syncthreads();  // every wave has read key tile t
     if (tn < NT) dma_tile<KT_BYTES>(ktg0 + (size_t)tn * KT_BYTES, sk, w, lane);
 
-    float s[32];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb * 16 + r] = sacc[kb][r];
-    if (!__all(mw == 0xFFFFFFFFu)) {
-#pragma unroll
-      for (int x = 0; x < 32; ++x) s[x] = ((mw >> x) & 1u) ? s[x] : -INFINITY;
-    }
-    float mt = s[0];
-#pragma unroll
-    for (int x = 1; x < 32; ++x) mt = fmaxf(mt, s[x]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m, mt);
-    // raise the running maximum only when it grows by more than 8 (log2
-    // units): probabilities stay below 2^8, rescaling is rare
-    if (__any(mnew > m + 8.0f)) {
-      const float alpha = (mnew > m) ? exp2f(m - mnew) : 1.0f;
+    f16x8_t ph[4];
+    const float alpha = softmax_tile<PM>(sacc, mw, m, init, l, ph);
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int vb = 0; vb <= NVB; ++vb) oacc[vb] *= alpha;
-      l *= alpha;
-      m = mnew;
     }
-    const float mu = (m == -INFINITY) ? 0.f : m;
-    float p[32];
-    float ps = 0.f;
-#pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      p[x] = __builtin_amdgcn_exp2f(s[x] - mu);
-      ps += p[x];
-    }
-    l += ps;
-    bf16x8_t pb[4];
-    f16x8_t ph[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = p[(ks >> 1) * 16 + (ks & 1) * 8 + e];
-        pb[ks][e] = (__bf16)v;
-        ph[ks][e] = (_Float16)v;
-      }
 
     // value tile t in LDS: only the next key tile's copies may be in flight
-    if (has_pm || tn >= NT) wait_vmcnt<0>(); else wait_vmcnt<kDK>();
+    if (PM || tn >= NT) wait_vmcnt<0>(); else wait_vmcnt<kDK>();
     __syncthreads();
-    // O^T += V~^T P^T, value blocks interleaved so consecutive MFMAs are independent
-    const char* vrow = sv + (size_t)(l32 * kVCols) * 2 + half * 16;
     __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(vrow + (size_t)(vb * 32 * kVCols) * 2 + ks * 32);
-        oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[ks], oacc[vb], 0, 0, 0);
-      }
-      const f16x8_t af = *reinterpret_cast<const f16x8_t*>(vrow + (size_t)(NVB * 32 * kVCols) * 2 + ks * 32);
-      oacc[NVB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, ph[ks], oacc[NVB], 0, 0, 0);
-    }
+    pv_tile<NVB>(vrow, ph, oacc);
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // every wave has read value tile t
     if (tn < NT) dma_tile<VT_BYTES>(vtg0 + (size_t)tn * VT_BYTES, sv, w, lane);
@@ -227,10 +261,9 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
   }
   // ---- finalise
   const float ltot = l + __shfl_xor(l, 32);
-  const bool nonempty = qvalid && ltot > 0.f;
-  const float mu = (m == -INFINITY) ? 0.f : m;
+  const bool nonempty = qvalid && init && ltot > 0.f;
   if (qin && half == 0)
-    a.lse[((size_t)b * H + h) * N + i] = nonempty ? (mu + log2f(ltot)) * kLn2 : -INFINITY;
+    a.lse[((size_t)b * H + h) * N + i] = nonempty ? (m + log2f(ltot)) * kLn2 : -INFINITY;
 
   // row d of a 32-row block sits in register 4*(d/8) + d%4 of the lane half (d%8)/4
   const int Dv = L.Dv, RCz = L.RCz, Q3 = 3 * L.Q, DO = L.DO;
@@ -256,7 +289,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
     }
   }
   if (!qin) return;
-  const float ib = nonempty ? 1.0f / lbf : 0.f;
+  const float ib = nonempty ? (1.0f / kVScale) / lbf : 0.f;  // the value rows hold v 2^-8
   const float ih = nonempty ? 1.0f / lh : 0.f;
   float* orow = a.o + (((size_t)b * N + i) * H + h) * DO;
 #pragma unroll

@@ -201,6 +201,8 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
               else if (x >= 9 && x <= 11) val = 0x4C00;  // fp16 16.0, multiplies the query's t'/16 parts
             }
           }
+        } else if (c == QW + 16 * (GS - 1) + 8) {
+          val = 0xFBFF;  // fp16 -65504 in the key-mask column of a masked key
         }
         out[e] = val;
       }
@@ -226,9 +228,9 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
           const int j = t * 64 + jj;
           if (s_valid[jj]) {
             if (d < 32 * NVB) {
-              if (d < Dv) val = v16[(((size_t)b * N + j) * H + h) * Dv + d];
-              else if (d < Dv + RCz) val = zr16[((size_t)b * N + j) * RCz + (d - Dv)];
-              else if (d == Dv + RCz) val = 0x3F80;  // bf16 1.0: weight sum
+              if (d < Dv) val = f32_to_f16_bits(bf16_bits_to_f32(v16[(((size_t)b * N + j) * H + h) * Dv + d]) * kVScale);
+              else if (d < Dv + RCz) val = f32_to_f16_bits(bf16_bits_to_f32(zr16[((size_t)b * N + j) * RCz + (d - Dv)]) * kVScale);
+              else if (d == Dv + RCz) val = 0x3C00;  // fp16 1.0: weight sum
             } else {
               const int dd = d - 32 * NVB;
               if (dd < 3 * Q) val = hi16(s_x[jj][dd]);
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
   __shared__ float s_a[64][17];        // a (query points, global)
   __shared__ __attribute__((aligned(16))) float s_xT[32][64];  // x - c of valid keys, coordinate-major
   __shared__ float s_wp[160];          // w_pair[h, :]
-  __shared__ __attribute__((aligned(16))) uint16_t s_vzT[kFastVRows][kFastVPitch];  // [v | zr] of valid keys
+  __shared__ __attribute__((aligned(16))) uint16_t s_vzT[kFastVRows][kFastVPitch];  // [v | zr] 2^-8 (fp16) of valid keys
   __shared__ float s_c[4];
   __shared__ float s_gam;
 
@@ -522,17 +524,19 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
     if (x < 64 * nch) {
       const uint4 val = s_valid[r] ? stg[k] : make_uint4(0, 0, 0, 0);
       const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
+      // value-tile entries: fp16 of the bf16 input times 2^-8
+      auto vh = [&](int e) { return f32_to_f16_bits(bf16_bits_to_f32(e16[e]) * kVScale); };
       if (c < nk) {
         *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + 8 * c) = val;
       } else if (c < nk + nz) {
         const int cz8 = c - nk;
         *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + D + 8 * cz8) = val;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_vzT[Dv + 8 * cz8 + e][r] = e16[e];
+        for (int e = 0; e < 8; ++e) s_vzT[Dv + 8 * cz8 + e][r] = vh(e);
       } else {
         const int cv = c - nk - nz;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][r] = e16[e];
+        for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][r] = vh(e);
       }
     }
   }
@@ -630,7 +634,9 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
         else if (y >= 13) val = lo16(ww[y - 13]);
         else if (y >= 9 && y <= 11) val = 0x4C00;  // fp16 16.0, multiplies the query's t'/16 parts
       }
-      g16[g] = valid ? val : (uint16_t)0;
+      // a masked key (or one past the end) is all zeros but for -65504 in
+      // the key-mask column, which the query side multiplies by 16
+      g16[g] = valid ? val : (g == base + 8 ? (uint16_t)0xFBFF : (uint16_t)0);
     }
 #pragma unroll
     for (int c = 0; c < (16 * GS + 8) / 8; ++c) *reinterpret_cast<uint4*>(krow + QW + 8 * c) = pack8(g16 + 8 * c);
@@ -684,7 +690,7 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
         const uint32_t bits = ((word >> (j0 & 31)) & 0xFu) | (((word >> ((j0 & 31) + 8)) & 0xFu) << 4);
         uint16_t one = 0;
         const int dd = d - 32 * NVB;
-        if (d == DZ) one = 0x3F80;                          // bf16 1.0: weight sum
+        if (d == DZ) one = 0x3C00;                          // fp16 1.0: weight sum
         else if (dd == 3 * Q) one = 0x3C00;                 // fp16 1.0: weight sum
         else if (dd > 3 * Q && dd <= 3 * Q + 3) one = hi16(s_c[dd - 3 * Q - 1]);  // centroid
         uint16_t out[8];

@@ -100,7 +100,7 @@ __device__ __forceinline__ void build_geo_P(const float* av, bool qvalid, float 
       if (c < 3 * P3) return ul[c - 2 * P3];
       return 0.f;
     }
-    if (g == base + 4 || g == base + 12) return kNormScale;
+    if (g == base + 4 || g == base + 8 || g == base + 12) return kNormScale;
     return 0.f;  // delta and t' slots, set per key tile
   };
 #pragma unroll
@@ -132,20 +132,23 @@ __device__ __forceinline__ void build_geo(int P, const float* av, bool qvalid, f
 }
 
 // Per key tile: -delta (exact in fp16) in the last K-step, and the row term
-// t' (three fp16 parts of t'/16) in the slots of half 1.
+// t' - msub (three fp16 parts of (t' - msub)/16) in the slots of half 1, so
+// that the product returns the logit minus msub (the running maximum of the
+// query in the fused kernel, 0 for plain logits).
 template <int GS>
-__device__ __forceinline__ void geo_tile(const QueryGeo& qg, float4 ct, float gl, float Pf, int half, f16x8_t* bg) {
+__device__ __forceinline__ void geo_tile(const QueryGeo& qg, float4 ct, float gl, float Pf, float msub, int half,
+                                         f16x8_t* bg) {
   const float dx = ct.x - qg.cw[0], dy = ct.y - qg.cw[1], dz = ct.z - qg.cw[2];
   const float dU = fmaf(dx, qg.U[0], fmaf(dy, qg.U[1], dz * qg.U[2]));
   const float d2 = fmaf(dx, dx, fmaf(dy, dy, dz * dz));
-  const float tp = 2.f * gl * dU - gl * fmaf(Pf, d2, qg.SA);
+  const float tp = 2.f * gl * dU - gl * fmaf(Pf, d2, qg.SA) - msub;
   const float x = fminf(fmaxf(tp * (1.0f / kNormScale), -65504.0f), 65504.0f);
   const float h1 = f16_round(x);
   const float r1 = x - h1;
   const float h2 = f16_round(r1);
   const float h3 = f16_round(r1 - h2);
   uint4 last;
-  last.x = half ? pack_f16(0.f, h1) : qg.fix0;
+  last.x = half ? pack_f16(kNormScale, h1) : qg.fix0;
   last.y = half ? pack_f16(h2, h3) : qg.fix1;
   last.z = pack_f16(kNormScale, -dx);
   last.w = pack_f16(-dy, -dz);
