@@ -1,33 +1,34 @@
 // Kernel 2, matrix-core path: fused masked online-softmax attention over the
 // lifted IPA rows on gfx950 MFMA.  No [N,N] tensor is written anywhere.
 //
-// Per (batch b, head h, 128-query tile): 4 waves, each owning 32 queries.
-// Per 64-key tile staged in LDS by the whole workgroup:
+// Per (batch b, head h, query tile): W wavefronts (4 or 8), each owning 32
+// queries.  Per 64-key tile staged in LDS by the whole workgroup:
 //   S^T (keys x queries) = K~ Q~^T        v_mfma_f32_32x32x16_bf16 over the
 //                                         scalar + pair columns,
 //                                         v_mfma_f32_32x32x16_f16 over the
 //                                         centred point columns (fp16 hi/lo
 //                                         split: 3 products per coordinate,
-//                                         plus the tile offset and row terms,
-//                                         see common.h), so S is the complete
-//                                         logit times log2 e
-//   masked online softmax in fp32 with exp2,
-//   a running maximum that is only raised when it grows by more than 8
-//   (probabilities stay below 2^8) and an fp32 row sum for the log-sum-exp
-//   O^T += V~^T P^T                       bf16 probabilities against the
-//                                         value and pair-factor rows, fp16
-//                                         probabilities against the centred
-//                                         value points, the centroid and a
-//                                         ones row
+//                                         plus the tile offset, the row term
+//                                         minus the running maximum and the
+//                                         key mask, see common.h), so S is
+//                                         the complete logit times log2 e
+//                                         relative to the running maximum
+//   masked online softmax in fp32 with exp2, a running maximum that is only
+//   raised when it grows by more than 8 (probabilities stay below 2^8) and
+//   an fp32 row sum for the log-sum-exp
+//   O^T += V~^T P^T                       fp16 probabilities against the fp16
+//                                         value tile: values and pair factors
+//                                         (times 2^-8), centred value points,
+//                                         the centroid and ones rows
 // The accumulator layout of S^T gives every lane one query and 16 keys, so
 // the probabilities feed the value product from registers; the value tile is
 // stored transposed with its keys permuted to match (lift kernel).
 // Normalisation uses the ones rows, i.e. the sums of the rounded
 // probabilities actually multiplied into O, so the weights applied to the
 // values sum to one to fp32 rounding and the centroid cancels exactly.
-// Key and value tiles are copied global -> LDS with direct-to-LDS loads; the
-// next key tile is fetched while the softmax and value product of the current
-// tile run, the next value tile while the next key product runs.
+// Key and value tiles are copied global -> LDS with direct-to-LDS loads into
+// two buffers: the copies of the next tile run during the whole of the
+// current tile, and one barrier per tile separates the two.
 #include "mfma_tile.h"
 
 namespace fipa {
@@ -65,10 +66,10 @@ __device__ __forceinline__ float4 ld_uniform4(const float4* p) {
   return make_float4(ld_uniform(f), ld_uniform(f + 1), ld_uniform(f + 2), ld_uniform(f + 3));
 }
 
-// Number of direct-to-LDS copy instructions each of the 4 wavefronts issues
+// Number of direct-to-LDS copy instructions each of the W wavefronts issues
 // for a tile of BYTES bytes (1 KiB per instruction).
-template <int BYTES>
-constexpr int dma_per_wave() { return ((BYTES + 1023) / 1024 + 3) / 4; }
+template <int BYTES, int W>
+constexpr int dma_per_wave() { return ((BYTES + 1023) / 1024 + W - 1) / W; }
 
 // Copy a tile (BYTES, a multiple of 16) global -> LDS with
 // global_load_lds_dwordx4: lane l of a wavefront moves bytes 16l .. 16l+15 of
@@ -78,7 +79,7 @@ constexpr int dma_per_wave() { return ((BYTES + 1023) / 1024 + 3) / 4; }
 // (same bytes to the same place).  The copies are issued from inline
 // assembly: the compiler does not track them, and the kernel waits for them
 // explicitly (vmcnt) before the barrier that precedes the LDS reads.
-template <int BYTES>
+template <int BYTES, int W>
 __device__ __forceinline__ void dma_tile(const char* g, const char* s, int w, int lane) {
   constexpr int nch = (BYTES + 1023) / 1024;
   const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(s);
@@ -90,8 +91,8 @@ __device__ __forceinline__ void dma_tile(const char* g, const char* s, int w, in
   const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
   g = (const char*)(uintptr_t)(((uint64_t)ghi << 32) | (uint64_t)glo);
 #pragma unroll
-  for (int k = 0; k < dma_per_wave<BYTES>(); ++k) {
-    int ch = w + 4 * k;
+  for (int k = 0; k < dma_per_wave<BYTES, W>(); ++k) {
+    int ch = w + W * k;
     ch = ch < nch ? ch : nch - 1;
     const uint32_t off = (uint32_t)ch * 1024u + (uint32_t)lane * 16u;
     const uint32_t voff = off < (uint32_t)BYTES ? off : (uint32_t)(BYTES - 16);
@@ -106,12 +107,29 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// O^T += V~^T P^T for one 64-key value tile in LDS: 4 K-steps x (NVB + 1)
+// Second half of the online softmax: p = 2^s (s already relative to the
+// running maximum), its fp32 row sum (returned) and the fp16 operand ph of
+// the value product.
+__device__ __forceinline__ float exp_tile(float* s, f16x8_t* ph) {
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int x = 0; x < 32; ++x) {
+    s[x] = __builtin_amdgcn_exp2f(s[x]);
+    ps[x & 3] += s[x];
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ph[ks][e] = (_Float16)s[(ks >> 1) * 16 + (ks & 1) * 8 + e];
+  return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+
+// O^T += V~^T P^T over one 64-key value tile in LDS: 4 K-steps x (NVB + 1)
 // value blocks, consecutive MFMAs on different blocks (independent), value
 // fragments fetched DEPTH MFMAs ahead of their use so that the LDS latency
 // hides behind the preceding MFMAs.
 template <int NVB>
-__device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* ph, f32x16_t* oacc) {
+__device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* pc, f32x16_t* oacc) {
   constexpr int NB = NVB + 1;
   constexpr int NS = 4 * NB;
   constexpr int DEPTH = 4;
@@ -124,9 +142,8 @@ __device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* ph, f32
     const uint4 c = f[st % DEPTH];
     if (st + DEPTH < NS) f[st % DEPTH] = *reinterpret_cast<const uint4*>(vrow + off(st + DEPTH));
     oacc[st % NB] =
-        __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c), ph[st / NB], oacc[st % NB], 0, 0, 0);
+        __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c), pc[st / NB], oacc[st % NB], 0, 0, 0);
   }
-  // the first DEPTH reads, then per step its MFMA followed by the read DEPTH ahead
   __builtin_amdgcn_sched_group_barrier(0x100, DEPTH, 0);
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
@@ -135,17 +152,16 @@ __device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* ph, f32
   }
 }
 
-// One tile of the online softmax for the 32 queries of a wavefront.  S
-// arrives relative to the running maximum m of each query (m rides in the row
-// term of the last geometric K-step); keys that are masked out arrive as
-// -16 x 65504 (key-mask column) or are set to -inf here (pair-mask bits).
-// m is raised only when a row maximum exceeds it by more than 8 (log2 units),
-// so the probabilities stay below 2^8 and rescaling is rare.  Returns the
-// factor by which O and l have been scaled.
+// First half of the online softmax of one tile for the 32 queries of a
+// wavefront.  S arrives relative to the running maximum m of each query (m
+// rides in the row term of the last geometric K-step); keys that are masked
+// out arrive as -16 x 65504 (key-mask column) or are set to -inf here
+// (pair-mask bits).  m is raised only when a row maximum exceeds it by more
+// than 8 (log2 units), so the probabilities stay below 2^8 and rescaling is
+// rare.  Leaves s relative to the new m and returns the factor by which O
+// and l are to be scaled.
 template <bool PM>
-__device__ __forceinline__ float softmax_tile(const f32x16_t* sacc, uint32_t mw, float& m, bool& init, float& l,
-                                              f16x8_t* ph) {
-  float s[32];
+__device__ __forceinline__ float softmax_max(const f32x16_t* sacc, uint32_t mw, float& m, bool& init, float* s) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -171,25 +187,18 @@ __device__ __forceinline__ float softmax_tile(const f32x16_t* sacc, uint32_t mw,
   }
   m += shift;
   init = init || need;
-  float ps = 0.f;
-#pragma unroll
-  for (int x = 0; x < 32; ++x) {
-    s[x] = __builtin_amdgcn_exp2f(s[x]);
-    ps += s[x];
-  }
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ph[ks][e] = (_Float16)s[(ks >> 1) * 16 + (ks & 1) * 8 + e];
-  l = l * alpha + ps;
   return alpha;
 }
 
 // Main loop over the key tiles and the final normalisation for one
-// wavefront's 32 queries.  PM selects the per-query pair-mask words (a vector
-// load per tile); without a pair mask the key mask is inside the key product.
-template <int NQS, int NVB, int GS, bool PM>
-__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* sv, int b, int h, int i, bool qin,
+// wavefront's 32 queries.  Key/value tiles alternate between two LDS buffers:
+// at the top of tile t the copies of t (issued one tile earlier) are waited
+// for, one barrier makes them visible and frees the other buffer, and the
+// copies of the next tile go out before the products of t start.  PM selects
+// the per-query pair-mask words (a vector load per tile); without a pair mask
+// the key mask is inside the key product.
+template <int NQS, int NVB, int GS, int W, bool PM>
+__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* sv0, int b, int h, int i, bool qin,
                                        bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
                                        const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
   constexpr int QW = 16 * NQS;
@@ -197,6 +206,8 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
   constexpr int KT_BYTES = 64 * KROW * 2;
   constexpr int VROWS = 32 * (NVB + 1);
   constexpr int VT_BYTES = VROWS * kVCols * 2;
+  constexpr int KT_LDS = (KT_BYTES + 1023) / 1024 * 1024;
+  constexpr int VT_LDS = (VT_BYTES + 1023) / 1024 * 1024;
   const Layout& L = a.L;
   const int N = L.N, H = L.H, NT = L.NT;
   const uint32_t* km = reinterpret_cast<const uint32_t*>(a.ws + L.off_km);
@@ -215,48 +226,46 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
       if ((ld_uniform(kmb + 2 * t) | ld_uniform(kmb + 2 * t + 1)) != 0u) break;  // skip tiles without a valid key
     return __builtin_amdgcn_readfirstlane(t);
   };
-  constexpr int kDK = dma_per_wave<KT_BYTES>(), kDV = dma_per_wave<VT_BYTES>();
-  const char* vrow = sv + (size_t)(l32 * kVCols) * 2 + half * 16;
+  auto copy_tile = [&](int t, int buf) {
+    dma_tile<KT_BYTES, W>(ktg0 + (size_t)t * KT_BYTES, sk0 + buf * KT_LDS, w, lane);
+    dma_tile<VT_BYTES, W>(vtg0 + (size_t)t * VT_BYTES, sv0 + buf * VT_LDS, w, lane);
+  };
 
   int t = next_tile(-1);
-  if (t < NT) {
-    dma_tile<KT_BYTES>(ktg0 + (size_t)t * KT_BYTES, sk, w, lane);
-    dma_tile<VT_BYTES>(vtg0 + (size_t)t * VT_BYTES, sv, w, lane);
-  }
+  int buf = 0;
+  if (t < NT) copy_tile(t, 0);
   while (t < NT) {
     const int tn = next_tile(t);
     uint32_t mw = 0xFFFFFFFFu;
     if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
     geo_tile<GS>(qg, ld_uniform4(ck + (size_t)b * NT + t), gl, Pf, m, half, bg);
-
-    // key tile t in LDS: this wave's copies are done once only the value-tile
-    // copies issued after them may still be in flight; then all waves' are
-    if constexpr (PM) wait_vmcnt<0>(); else wait_vmcnt<kDV>();
+    // tile t in LDS buffer buf; every wave is done with tile t-1 (buffer buf^1)
+    wait_vmcnt<0>();
     __syncthreads();
+    if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
+    if (tn < NT) copy_tile(tn, buf ^ 1);
+    const char* sk = sk0 + buf * KT_LDS;
+    const char* sv = sv0 + buf * VT_LDS;
+
     f32x16_t sacc[2];
-    // raised wave priority while issuing MFMAs
     __builtin_amdgcn_s_setprio(1);
     s_tile<NQS, GS>(sk, bq, bg, l32, half, sacc);
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
-    __syncthreads();  // every wave has read key tile t
-    if (tn < NT) dma_tile<KT_BYTES>(ktg0 + (size_t)tn * KT_BYTES, sk, w, lane);
 
+    float s32[32];
+    const float alpha = softmax_max<PM>(sacc, mw, m, init, s32);
     f16x8_t ph[4];
-    const float alpha = softmax_tile<PM>(sacc, mw, m, init, l, ph);
+    const float ps = exp_tile(s32, ph);
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int vb = 0; vb <= NVB; ++vb) oacc[vb] *= alpha;
     }
+    l = l * alpha + ps;
 
-    // value tile t in LDS: only the next key tile's copies may be in flight
-    if (PM || tn >= NT) wait_vmcnt<0>(); else wait_vmcnt<kDK>();
-    __syncthreads();
     __builtin_amdgcn_s_setprio(1);
-    pv_tile<NVB>(vrow, ph, oacc);
+    pv_tile<NVB>(sv + (size_t)(l32 * kVCols) * 2 + half * 16, ph, oacc);
     __builtin_amdgcn_s_setprio(0);
-    __syncthreads();  // every wave has read value tile t
-    if (tn < NT) dma_tile<VT_BYTES>(vtg0 + (size_t)tn * VT_BYTES, sv, w, lane);
+    buf ^= 1;
     t = tn;
   }
   // ---- finalise
@@ -310,16 +319,16 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk, char* s
   }
 }
 
-template <int NQS, int NVB, int GS>
-__global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
+template <int NQS, int NVB, int GS, int W>
+__global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   constexpr int QW = 16 * NQS;
   constexpr int KROW = QW + 16 * GS + kRowPad;
   constexpr int KT_BYTES = 64 * KROW * 2;
   constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
-  // rounded up to whole KiB: the last copy chunk of a tile may be partial and
-  // its upper lanes then land in this padding
-  __shared__ __attribute__((aligned(1024))) char sk[(KT_BYTES + 1023) / 1024 * 1024];
-  __shared__ __attribute__((aligned(1024))) char sv[(VT_BYTES + 1023) / 1024 * 1024];
+  // two buffers each, rounded up to whole KiB: the last copy chunk of a
+  // tile may be partial and its upper lanes then land in this padding
+  __shared__ __attribute__((aligned(1024))) char sk[2 * ((KT_BYTES + 1023) / 1024 * 1024)];
+  __shared__ __attribute__((aligned(1024))) char sv[2 * ((VT_BYTES + 1023) / 1024 * 1024)];
 
   const Layout& L = a.L;
   const int N = L.N, H = L.H;
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
   const int l32 = lane & 31, half = lane >> 5;
-  const int i = qt * kQueryTile + w * 32 + l32;
+  const int i = qt * (W * 32) + w * 32 + l32;
   const bool qin = i < N;
 
   const Header* hd = reinterpret_cast<const Header*>(a.ws);
@@ -357,11 +366,13 @@ __global__ __launch_bounds__(256, 2) void flash_mfma_kernel(FlashMfmaArgs a) {
   }
 
   if (has_pm)
-    attend<NQS, NVB, GS, true>(a, sk, sv, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, true>(a, sk, sv, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
   else
-    attend<NQS, NVB, GS, false>(a, sk, sv, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, false>(a, sk, sv, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
 }
 
+// 8 wavefronts (256 queries) per workgroup when that still gives every CU a
+// workgroup, else 4 (128 queries).
 template <int NQS, int NVB, int GS>
 static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st) {
   FlashMfmaArgs a;
@@ -369,9 +380,16 @@ static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* 
   a.ws = reinterpret_cast<const char*>(ws);
   a.o = o;
   a.lse = lse;
-  a.qtiles = (L.N + kQueryTile - 1) / kQueryTile;
-  a.nwg = a.qtiles * L.H * L.B;
-  hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS>), dim3(a.nwg), dim3(256), 0, st, a);
+  const int q8 = (L.N + 255) / 256;
+  if ((long)q8 * L.H * L.B >= 256) {
+    a.qtiles = q8;
+    a.nwg = a.qtiles * L.H * L.B;
+    hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 8>), dim3(a.nwg), dim3(512), 0, st, a);
+  } else {
+    a.qtiles = (L.N + 127) / 128;
+    a.nwg = a.qtiles * L.H * L.B;
+    hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4>), dim3(a.nwg), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
