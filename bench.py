@@ -46,6 +46,40 @@ def eff_flops(shape, mask) -> float:
     return 2.0 * shape.H * (shape.d_qk + shape.d_v) * float((L ** 2).sum())
 
 
+def _mfma_dims(shape):
+    """(NQS, NVB, GS) of the compiled matrix-core instance used for a shape."""
+    rcz = shape.R * shape.Cz
+    for nqs, nvb in ((3, 2), (5, 3), (9, 5)):
+        if shape.D + rcz <= 16 * nqs and shape.Dv + rcz + 1 <= 32 * nvb:
+            return nqs, nvb, (3 if shape.P <= 4 else 4)
+    raise ValueError("no matrix-core instance for this shape")
+
+
+def lift_bytes(shape, with_pm: bool) -> float:
+    """Algorithmic HBM bytes of the lift kernel: every input read once, every
+    lifted row written once (per residue: q, k, v, the points, frames, zl, zr,
+    mask; key rows, transposed value tiles, query rows, query points)."""
+    nqs, nvb, gs = _mfma_dims(shape)
+    H, R, Cz = shape.H, shape.R, shape.Cz
+    rd = 2 * H * (2 * shape.D + shape.Dv) + 2 * 3 * H * (2 * shape.P + shape.Q) + 2 * 12 + 2 * 2 * R * Cz + 1
+    kt = H * (16 * nqs + 16 * gs + 8) * 2
+    vt = H * 32 * (nvb + 1) * 72 * 2 / 64
+    wr = kt + vt + H * 16 * nqs * 2 + H * 16 * 4
+    per_res = rd + wr
+    extra = shape.B * shape.N * shape.N if with_pm else 0
+    return shape.B * shape.N * per_res + extra
+
+
+def epilogue_bytes(shape) -> float:
+    """Algorithmic HBM bytes of the epilogue: O, lse, zl and frames read, the
+    update and local points written, per residue (w_out once)."""
+    H = shape.H
+    do = shape.Dv + shape.R * shape.Cz + 3 * shape.Q
+    rd = H * do * 4 + H * 4 + 2 * shape.R * shape.Cz + 2 * 12
+    wr = shape.Cout * 4 + H * shape.Q * 3 * 4
+    return shape.B * shape.N * (rd + wr) + 2 * shape.F * shape.Cout
+
+
 def make_workload(name):
     from rna_structure_amd.synth import make_config
     return make_config(name)
@@ -138,7 +172,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="sweep_16384")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -188,6 +222,11 @@ def main():
         "kernels_ms": {"lift": round(r["lift_ms"], 4), "flash": round(r["flash_ms"], 4),
                        "epilogue": round(r["epilogue_ms"], 4)},
         "peak_mem_mb": round(r["peak_mem_mb"], 1),
+        "hbm_kernels": {
+            name: {"bytes": round(nb), "achieved_GBs": round(nb / (ms * 1e-3) / 1e9, 1),
+                   "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            for name, nb, ms in (("lift", lift_bytes(shape, inp["pair_mask"] is not None), r["lift_ms"]),
+                                 ("epilogue", epilogue_bytes(shape), r["epilogue_ms"]))},
         "roofline": {"bound": "mfma", "kernel": "flash_mfma_kernel", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
