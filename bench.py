@@ -168,6 +168,34 @@ def copy_calibration(mib: int, reps: int = 3) -> None:
     print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}), flush=True)
 
 
+def hbm_calibration(mib: int = 2048, reps: int = 10) -> dict:
+    """Achievable HBM rates of plain device kernels: a fill (writes only), a
+    copy (read + write) and a sum (reads only) over MIB MiB, event-timed."""
+    import torch
+    n = mib * 2**20 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    res = {}
+    for name, fn, nbytes in (("fill", lambda: y.fill_(1.0), 4 * n),
+                             ("copy", lambda: y.copy_(x), 8 * n),
+                             ("sum", lambda: x.sum(), 4 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4)}
+    del x, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +206,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only plain copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--hbm-calibration", action="store_true",
+                    help="print the fill / copy / sum rates of plain device kernels and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -187,6 +217,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.hbm_calibration:
+        print(json.dumps({"hbm_calibration": hbm_calibration()}), flush=True)
         return
     inp = make_workload(args.workload)
     shape = inp["shape"]

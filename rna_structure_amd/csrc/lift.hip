@@ -362,19 +362,20 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
 // and share its L2 for zr, zl and the frames.
 constexpr int kFastVRows = 160;      // Dv + R Cz <= 32 NVB - 1 <= 159
 constexpr int kFastVPitch = 66;      // 16-bit elements per transposed LDS row (33 words)
-constexpr int kFastStage = 8;        // 16-byte pieces of [k | zr | v] per thread: 64 (D+RCz+Dv)/8 <= 2048
-constexpr int kFastQL = 5;           // pieces of a query row per thread: 64 QW/8 <= 1280
+constexpr int kFastZ = 5;            // 16-byte pieces of a zr / zl tile per thread: 64 R Cz/8 <= 1280
+constexpr int kFastK = 2;            // pieces of a k / v / q tile per thread: 64 D/8 <= 512
 constexpr int kFastPts = 5;          // points per thread: 64 (2P + Q) <= 1280
 
-// x / d for 0 <= x < 2^16 and 0 < d < 2^16: m = ceil(2^32 / d)
+// x / d for 0 <= x < 2^16 and 0 < d < 2^16: m = ceil(2^32 / d), which fits
+// in 32 bits for d >= 2; d = 1 is passed through
 struct FastDiv {
   uint32_t m;
   int d;
 };
 static inline FastDiv make_fastdiv(int d) {
-  return FastDiv{(uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d), d};
+  return FastDiv{d > 1 ? (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d) : 0u, d};
 }
-__device__ __forceinline__ int fdiv(int x, FastDiv f) { return (int)__umulhi((uint32_t)x, f.m); }
+__device__ __forceinline__ int fdiv(int x, FastDiv f) { return f.d == 1 ? x : (int)__umulhi((uint32_t)x, f.m); }
 
 __device__ __forceinline__ uint4 pack8(const uint16_t* v) {
   uint4 pk;
@@ -387,17 +388,24 @@ __device__ __forceinline__ uint4 pack8(const uint16_t* v) {
 
 struct LiftFastArgs {
   int units, per_xcd, pm_vec;
-  FastDiv nch, qch;
+  FastDiv nz, nk, nv;
 };
+
+// Two floats to packed bf16 (round to nearest even, the hardware conversion).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 static inline bool lift_fast_fits(const Layout& L) {
   return L.mfma && L.D % 8 == 0 && L.Dv % 8 == 0 && L.Cz % 8 == 0 && L.Dv + L.RCz <= kFastVRows &&
-         L.Cz <= 160 && 64 * ((L.D + L.RCz + L.Dv) / 8) <= 256 * kFastStage &&
-         64 * (L.QW / 8) <= 256 * kFastQL && 64 * (2 * L.P + L.Q) <= 256 * kFastPts;
+         L.Cz <= 160 && 64 * (L.RCz / 8) <= 256 * kFastZ && 64 * (L.D / 8) <= 256 * kFastK &&
+         64 * (L.Dv / 8) <= 256 * kFastK && 64 * (2 * L.P + L.Q) <= 256 * kFastPts;
 }
 
 template <int P>
-__global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs f) {
+__global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastArgs f) {
   constexpr int P3 = 3 * P;
   constexpr int GS = P <= 4 ? 3 : 4;
   const Layout& L = a.L;
@@ -406,8 +414,8 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
   if (u >= f.units) return;
   const int h = u % H, t = (u / H) % L.NT, b = u / (H * L.NT);
   const int tid = threadIdx.x;
-  const int nk = D / 8, nz = RCz / 8, nv = Dv / 8, nch = f.nch.d;
-  const int QW = L.QW, qch = f.qch.d;
+  const int nk = D / 8, nz = RCz / 8, nv = Dv / 8;
+  const int QW = L.QW;
   const int npt = 2 * P + Q;
 
   __shared__ float s_rot[64][9];
@@ -415,24 +423,37 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
   __shared__ int s_valid[64];
   __shared__ uint32_t s_vmask[2];  // valid keys, bit jj of word jj / 32
   __shared__ float s_w[64][P3 % 2 ? P3 : P3 + 1];  // b - c (key points, centred), odd row stride
-  __shared__ float s_a[64][17];        // a (query points, global)
+  __shared__ float s_a[64][P3 % 2 ? P3 : P3 + 1];  // a (query points, global), odd row stride
   __shared__ __attribute__((aligned(16))) float s_xT[32][64];  // x - c of valid keys, coordinate-major
   __shared__ float s_wp[160];          // w_pair[h, :]
   __shared__ __attribute__((aligned(16))) uint16_t s_vzT[kFastVRows][kFastVPitch];  // [v | zr] 2^-8 (fp16) of valid keys
   __shared__ float s_c[4];
   __shared__ float s_gam;
 
-  // ---- 1. every global load of the workgroup
+  // ---- 1. every global load of the workgroup.  Addresses: one 64-bit base
+  // per tensor for the tile's first residue (uniform), plus 32-bit offsets
+  // within the tile.
+  const size_t row0 = (size_t)b * N + (size_t)t * 64;     // first residue of the tile
+  const size_t rh0 = row0 * H + h;                         // its (residue, head) row
+  const uint4* kb4 = reinterpret_cast<const uint4*>(a.k) + rh0 * nk;
+  const uint4* vb4 = reinterpret_cast<const uint4*>(a.v) + rh0 * nv;
+  const uint4* qb4 = reinterpret_cast<const uint4*>(a.q) + rh0 * nk;
+  const uint4* zrb4 = reinterpret_cast<const uint4*>(a.zr) + row0 * nz;
+  const uint4* zlb4 = reinterpret_cast<const uint4*>(a.zl) + row0 * nz;
+  const uint16_t* kpb = reinterpret_cast<const uint16_t*>(a.kp) + rh0 * (3 * P);
+  const uint16_t* qpb = reinterpret_cast<const uint16_t*>(a.qp) + rh0 * (3 * P);
+  const uint16_t* vpb = reinterpret_cast<const uint16_t*>(a.vp) + rh0 * (3 * Q);
+  const int nrow = min(64, N - t * 64);                    // residues of the tile inside the chain
   float fr[13];  // threads 0..63: translation, rotation, mask of residue tid
   if (tid < 64) {
-    const int j = t * 64 + tid;
-    if (j < N) {
-      const size_t o = ((size_t)b * N + j) * 3;
+    if (tid < nrow) {
+      const uint16_t* tr16 = reinterpret_cast<const uint16_t*>(a.trans) + (row0 + tid) * 3;
+      const uint16_t* ro16 = reinterpret_cast<const uint16_t*>(a.rot) + (row0 + tid) * 9;
 #pragma unroll
-      for (int e = 0; e < 3; ++e) fr[e] = ld<true>(a.trans, o + e);
+      for (int e = 0; e < 3; ++e) fr[e] = bf16_bits_to_f32(tr16[e]);
 #pragma unroll
-      for (int e = 0; e < 9; ++e) fr[3 + e] = ld<true>(a.rot, ((size_t)b * N + j) * 9 + e);
-      fr[12] = a.mask[(size_t)b * N + j] != 0 ? 1.f : 0.f;
+      for (int e = 0; e < 9; ++e) fr[3 + e] = bf16_bits_to_f32(ro16[e]);
+      fr[12] = a.mask[row0 + tid] != 0 ? 1.f : 0.f;
     } else {
 #pragma unroll
       for (int e = 0; e < 13; ++e) fr[e] = 0.f;
@@ -440,44 +461,40 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
   }
   const float wp_raw = tid < Cz ? ld<true>(a.wpair, (size_t)h * Cz + tid) : 0.f;
   const float pwr = ld<true>(a.pwr, h);
-  uint4 stg[kFastStage];
+  // each loop below covers one tensor, so the lanes of a wavefront never
+  // diverge over which tensor a piece comes from
+  uint4 zr_r[kFastZ], zl_r[kFastZ];
 #pragma unroll
-  for (int k = 0; k < kFastStage; ++k) {
-    const int x = tid + 256 * k, r = fdiv(x, f.nch), c = x - r * nch, j = t * 64 + r;
-    stg[k] = make_uint4(0, 0, 0, 0);
-    if (x < 64 * nch && j < N) {
-      if (c < nk)
-        stg[k] = reinterpret_cast<const uint4*>(a.k)[(((size_t)b * N + j) * H + h) * nk + c];
-      else if (c < nk + nz)
-        stg[k] = reinterpret_cast<const uint4*>(a.zr)[((size_t)b * N + j) * nz + (c - nk)];
-      else
-        stg[k] = reinterpret_cast<const uint4*>(a.v)[(((size_t)b * N + j) * H + h) * nv + (c - nk - nz)];
-    }
+  for (int k = 0; k < kFastZ; ++k) {
+    const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+    const bool in = x < 64 * nz && r < nrow;
+    zr_r[k] = in ? zrb4[r * nz + c] : make_uint4(0, 0, 0, 0);
+    zl_r[k] = in ? zlb4[r * nz + c] : make_uint4(0, 0, 0, 0);
   }
-  uint4 qlr[kFastQL];
+  uint4 k_r[kFastK], q_r[kFastK], v_r[kFastK];
 #pragma unroll
-  for (int k = 0; k < kFastQL; ++k) {
-    const int x = tid + 256 * k, r = fdiv(x, f.qch), c = x - r * qch, i = t * 64 + r;
-    qlr[k] = make_uint4(0, 0, 0, 0);
-    if (x < 64 * qch && i < N) {
-      if (c < nk)
-        qlr[k] = reinterpret_cast<const uint4*>(a.q)[(((size_t)b * N + i) * H + h) * nk + c];
-      else if (c < nk + nz)
-        qlr[k] = reinterpret_cast<const uint4*>(a.zl)[((size_t)b * N + i) * nz + (c - nk)];
-    }
+  for (int k = 0; k < kFastK; ++k) {
+    const int x = tid + 256 * k;
+    const int rk = fdiv(x, f.nk), ck = x - rk * nk;
+    const bool ink = x < 64 * nk && rk < nrow;
+    k_r[k] = ink ? kb4[rk * H * nk + ck] : make_uint4(0, 0, 0, 0);
+    q_r[k] = ink ? qb4[rk * H * nk + ck] : make_uint4(0, 0, 0, 0);
+    const int rv = fdiv(x, f.nv), cv = x - rv * nv;
+    v_r[k] = (x < 64 * nv && rv < nrow) ? vb4[rv * H * nv + cv] : make_uint4(0, 0, 0, 0);
   }
   float pts[kFastPts][3];
 #pragma unroll
   for (int k = 0; k < kFastPts; ++k) {
-    const int x = tid + 256 * k, r = x % 64, it = x / 64, j = t * 64 + r;
+    const int x = tid + 256 * k, r = x % 64, it = x / 64;
     pts[k][0] = pts[k][1] = pts[k][2] = 0.f;
-    if (x < 64 * npt && j < N) {
-      const void* src;
-      size_t o;
-      if (it < P) { src = a.kp; o = ((((size_t)b * N + j) * H + h) * P + it) * 3; }
-      else if (it < 2 * P) { src = a.qp; o = ((((size_t)b * N + j) * H + h) * P + (it - P)) * 3; }
-      else { src = a.vp; o = ((((size_t)b * N + j) * H + h) * Q + (it - 2 * P)) * 3; }
-      pts[k][0] = ld<true>(src, o); pts[k][1] = ld<true>(src, o + 1); pts[k][2] = ld<true>(src, o + 2);
+    if (x < 64 * npt && r < nrow) {
+      const uint16_t* src;
+      if (it < P) src = kpb + r * H * 3 * P + 3 * it;
+      else if (it < 2 * P) src = qpb + r * H * 3 * P + 3 * (it - P);
+      else src = vpb + r * H * 3 * Q + 3 * (it - 2 * P);
+      pts[k][0] = bf16_bits_to_f32(src[0]);
+      pts[k][1] = bf16_bits_to_f32(src[1]);
+      pts[k][2] = bf16_bits_to_f32(src[2]);
     }
   }
 
@@ -518,26 +535,31 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
 
   // ---- 3. [k | zr] straight into the key tile, [v | zr] transposed into LDS
   uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * L.KROW;
+  auto vh = [](uint16_t bits) { return f32_to_f16_bits(bf16_bits_to_f32(bits) * kVScale); };
 #pragma unroll
-  for (int k = 0; k < kFastStage; ++k) {
-    const int x = tid + 256 * k, r = fdiv(x, f.nch), c = x - r * nch;
-    if (x < 64 * nch) {
-      const uint4 val = s_valid[r] ? stg[k] : make_uint4(0, 0, 0, 0);
-      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
+  for (int k = 0; k < kFastZ; ++k) {
+    const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+    if (x < 64 * nz) {
+      const uint4 val = s_valid[r] ? zr_r[k] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + D + 8 * c) = val;
       // value-tile entries: fp16 of the bf16 input times 2^-8
-      auto vh = [&](int e) { return f32_to_f16_bits(bf16_bits_to_f32(e16[e]) * kVScale); };
-      if (c < nk) {
-        *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + 8 * c) = val;
-      } else if (c < nk + nz) {
-        const int cz8 = c - nk;
-        *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + D + 8 * cz8) = val;
+      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_vzT[Dv + 8 * cz8 + e][r] = vh(e);
-      } else {
-        const int cv = c - nk - nz;
+      for (int e = 0; e < 8; ++e) s_vzT[Dv + 8 * c + e][r] = vh(e16[e]);
+    }
+  }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][r] = vh(e);
-      }
+  for (int k = 0; k < kFastK; ++k) {
+    const int x = tid + 256 * k;
+    const int rk = fdiv(x, f.nk), ck = x - rk * nk;
+    if (x < 64 * nk)
+      *reinterpret_cast<uint4*>(kt + (size_t)rk * L.KROW + 8 * ck) = s_valid[rk] ? k_r[k] : make_uint4(0, 0, 0, 0);
+    const int rv = fdiv(x, f.nv), cv = x - rv * nv;
+    if (x < 64 * nv) {
+      const uint4 val = s_valid[rv] ? v_r[k] : make_uint4(0, 0, 0, 0);
+      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][rv] = vh(e16[e]);
     }
   }
   // global points: key points (centred), query points, value points (centred,
@@ -573,28 +595,38 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
   {
     const float sq = kLog2e / sqrtf(3.0f * (float)D);
     const float sp = kLog2e / sqrtf(3.0f);
-    uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql);
+    uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + (size_t)t * 64) * QW;
 #pragma unroll
-    for (int k = 0; k < kFastQL; ++k) {
-      const int x = tid + 256 * k, r = fdiv(x, f.qch), c = x - r * qch;
-      if (x < 64 * qch) {
-        const int i = t * 64 + r;
-        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&qlr[k]);
-        uint16_t out[8];
-        if (c < nk) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) out[e] = f32_to_bf16_bits(bf16_bits_to_f32(e16[e]) * sq);
-        } else if (c < nk + nz) {
-          const int c0 = (8 * (c - nk)) % Cz;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) out[e] = f32_to_bf16_bits(s_wp[c0 + e] * bf16_bits_to_f32(e16[e]) * sp);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) out[e] = 0;
-        }
-        *reinterpret_cast<uint4*>(ql + (((size_t)b * H + h) * L.NQpad + i) * QW + 8 * c) = pack8(out);
+    for (int k = 0; k < kFastZ; ++k) {
+      const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+      if (x < 64 * nz) {
+        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&zl_r[k]);
+        const float* wp = s_wp + (8 * c) % Cz;
+        uint4 pk;
+        pk.x = pack_bf16x2(wp[0] * bf16_bits_to_f32(e16[0]) * sp, wp[1] * bf16_bits_to_f32(e16[1]) * sp);
+        pk.y = pack_bf16x2(wp[2] * bf16_bits_to_f32(e16[2]) * sp, wp[3] * bf16_bits_to_f32(e16[3]) * sp);
+        pk.z = pack_bf16x2(wp[4] * bf16_bits_to_f32(e16[4]) * sp, wp[5] * bf16_bits_to_f32(e16[5]) * sp);
+        pk.w = pack_bf16x2(wp[6] * bf16_bits_to_f32(e16[6]) * sp, wp[7] * bf16_bits_to_f32(e16[7]) * sp);
+        *reinterpret_cast<uint4*>(ql + (size_t)r * QW + D + 8 * c) = pk;
       }
     }
+#pragma unroll
+    for (int k = 0; k < kFastK; ++k) {
+      const int x = tid + 256 * k, r = fdiv(x, f.nk), c = x - r * nk;
+      if (x < 64 * nk) {
+        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&q_r[k]);
+        uint4 pk;
+        pk.x = pack_bf16x2(bf16_bits_to_f32(e16[0]) * sq, bf16_bits_to_f32(e16[1]) * sq);
+        pk.y = pack_bf16x2(bf16_bits_to_f32(e16[2]) * sq, bf16_bits_to_f32(e16[3]) * sq);
+        pk.z = pack_bf16x2(bf16_bits_to_f32(e16[4]) * sq, bf16_bits_to_f32(e16[5]) * sq);
+        pk.w = pack_bf16x2(bf16_bits_to_f32(e16[6]) * sq, bf16_bits_to_f32(e16[7]) * sq);
+        *reinterpret_cast<uint4*>(ql + (size_t)r * QW + 8 * c) = pk;
+      }
+    }
+    // zero columns [D + R Cz, QW)
+    const int nzero = (QW - D - RCz) / 8;
+    for (int x = tid; x < 64 * nzero; x += 256)
+      *reinterpret_cast<uint4*>(ql + (size_t)(x / nzero) * QW + D + RCz + 8 * (x % nzero)) = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 
@@ -663,51 +695,51 @@ __global__ __launch_bounds__(256) void lift_fast_kernel(LiftArgs a, LiftFastArgs
   }
   // query global points: 16 floats per (b, h, i)
   {
-    float4* qa = reinterpret_cast<float4*>(a.ws + L.off_qa);
+    float4* qa = reinterpret_cast<float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + (size_t)t * 64) * 4;
     const int row = tid / 4, c = (tid % 4) * 4;
-    const int i = t * 64 + row;
     float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (i < N && c + e < P3) ? s_a[row][c + e] : 0.f;
-    qa[(((size_t)b * H + h) * L.NQpad + i) * 4 + tid % 4] = make_float4(v[0], v[1], v[2], v[3]);
+    for (int e = 0; e < 4; ++e) v[e] = (row < nrow && c + e < P3) ? s_a[row][c + e] : 0.f;
+    qa[tid] = make_float4(v[0], v[1], v[2], v[3]);
   }
   // transposed value tile: rows d, columns kappa; columns k0 .. k0+7 hold keys
   // j0 .. j0+3 and j0+8 .. j0+11 (j0 = vt_key_of_col(k0)), columns 64 .. 71 are zero
   uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + L.off_vt) + (((size_t)b * H + h) * L.NT + t) * VROWS * kVCols;
-  constexpr int vch = kVCols / 8;
   const uint32_t vm0 = s_vmask[0], vm1 = s_vmask[1];
-  for (int x = tid; x < VROWS * vch; x += 256) {
-    const int d = x / vch, kc = x % vch;
-    uint4 pk = make_uint4(0, 0, 0, 0);
-    if (kc < 8) {
-      const int j0 = vt_key_of_col(8 * kc);
-      if (d < DZ) {
-        const uint32_t* row = reinterpret_cast<const uint32_t*>(&s_vzT[d][0]);
-        pk = make_uint4(row[j0 / 2], row[j0 / 2 + 1], row[j0 / 2 + 4], row[j0 / 2 + 5]);
-      } else {
-        // valid bits of the 8 keys, in column order
-        const uint32_t word = j0 < 32 ? vm0 : vm1;
-        const uint32_t bits = ((word >> (j0 & 31)) & 0xFu) | (((word >> ((j0 & 31) + 8)) & 0xFu) << 4);
-        uint16_t one = 0;
-        const int dd = d - 32 * NVB;
-        if (d == DZ) one = 0x3C00;                          // fp16 1.0: weight sum
-        else if (dd == 3 * Q) one = 0x3C00;                 // fp16 1.0: weight sum
-        else if (dd > 3 * Q && dd <= 3 * Q + 3) one = hi16(s_c[dd - 3 * Q - 1]);  // centroid
-        uint16_t out[8];
-        if (dd >= 0 && dd < 3 * Q) {
-          const float4 lo = *reinterpret_cast<const float4*>(&s_xT[dd][j0]);
-          const float4 hi = *reinterpret_cast<const float4*>(&s_xT[dd][j0 + 8]);
-          out[0] = hi16(lo.x); out[1] = hi16(lo.y); out[2] = hi16(lo.z); out[3] = hi16(lo.w);
-          out[4] = hi16(hi.x); out[5] = hi16(hi.y); out[6] = hi16(hi.z); out[7] = hi16(hi.w);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) out[e] = ((bits >> e) & 1u) ? one : (uint16_t)0;
-        }
-        pk = pack8(out);
-      }
-    }
-    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * kc) = pk;
+  // rows [v | zr]: 8 column chunks each, straight from the transposed LDS copy
+  for (int x = tid; x < DZ * 8; x += 256) {
+    const int d = x >> 3, j0 = vt_key_of_col(8 * (x & 7));
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(&s_vzT[d][0]);
+    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * (x & 7)) =
+        make_uint4(row[j0 / 2], row[j0 / 2 + 1], row[j0 / 2 + 4], row[j0 / 2 + 5]);
   }
+  // the other rows: the weight-sum row, zero rows, centred value points, the
+  // ones row and the centroid (valid keys only)
+  for (int x = tid; x < (VROWS - DZ) * 8; x += 256) {
+    const int d = DZ + (x >> 3), j0 = vt_key_of_col(8 * (x & 7));
+    // valid bits of the 8 keys, in column order
+    const uint32_t word = j0 < 32 ? vm0 : vm1;
+    const uint32_t bits = ((word >> (j0 & 31)) & 0xFu) | (((word >> ((j0 & 31) + 8)) & 0xFu) << 4);
+    uint16_t one = 0;
+    const int dd = d - 32 * NVB;
+    if (d == DZ) one = 0x3C00;                          // fp16 1.0: weight sum
+    else if (dd == 3 * Q) one = 0x3C00;                 // fp16 1.0: weight sum
+    else if (dd > 3 * Q && dd <= 3 * Q + 3) one = hi16(s_c[dd - 3 * Q - 1]);  // centroid
+    uint16_t out[8];
+    if (dd >= 0 && dd < 3 * Q) {
+      const float4 lo = *reinterpret_cast<const float4*>(&s_xT[dd][j0]);
+      const float4 hi = *reinterpret_cast<const float4*>(&s_xT[dd][j0 + 8]);
+      out[0] = hi16(lo.x); out[1] = hi16(lo.y); out[2] = hi16(lo.z); out[3] = hi16(lo.w);
+      out[4] = hi16(hi.x); out[5] = hi16(hi.y); out[6] = hi16(hi.z); out[7] = hi16(hi.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = ((bits >> e) & 1u) ? one : (uint16_t)0;
+    }
+    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * (x & 7)) = pack8(out);
+  }
+  // pad columns 64 .. 71 of every row
+  for (int d = tid; d < VROWS; d += 256)
+    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 64) = make_uint4(0, 0, 0, 0);
 
   // ---- 5. permitted-key words of every query row for this key tile
   if (a.pm != nullptr && h == 0) {
@@ -768,8 +800,9 @@ hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStre
     f.units = L.B * L.NT * L.H;
     f.per_xcd = (f.units + 7) / 8;
     f.pm_vec = in->pair_mask != nullptr && L.N % 16 == 0 && reinterpret_cast<uintptr_t>(in->pair_mask) % 16 == 0;
-    f.nch = make_fastdiv((L.D + L.RCz + L.Dv) / 8);
-    f.qch = make_fastdiv(L.QW / 8);
+    f.nz = make_fastdiv(L.RCz / 8);
+    f.nk = make_fastdiv(L.D / 8);
+    f.nv = make_fastdiv(L.Dv / 8);
     const dim3 g(8 * f.per_xcd), blk(256);
     switch (L.P) {
       case 1: hipLaunchKernelGGL(lift_fast_kernel<1>, g, blk, 0, st, a, f); break;
