@@ -633,8 +633,10 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   // ---- 4. key rows past [k | zr] (one thread per key): zeros up to QW, the
   // geometric columns (layout in common.h), 8 pad columns
   const int VROWS = L.VROWS, NVB = L.NVB, DZ = Dv + RCz;
-  if (tid < 64) {
-    const int r = tid;
+  {
+    // every wavefront: lane = key, chunks w, w + 4, ... of the 16 GS + 8
+    // columns after QW; each lane recomputes its key's point sums
+    const int r = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool valid = s_valid[r] != 0;
     float w[P3];
 #pragma unroll
@@ -648,11 +650,12 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     nb = -gl * nb;
     const float ww[3] = {2.f * gl * Wx, 2.f * gl * Wy, 2.f * gl * Wz};
     uint16_t* krow = kt + (size_t)r * L.KROW;
-    for (int c = D + RCz; c < QW; c += 8) *reinterpret_cast<uint4*>(krow + c) = make_uint4(0, 0, 0, 0);
+    if (wv == 0)
+      for (int c = D + RCz; c < QW; c += 8) *reinterpret_cast<uint4*>(krow + c) = make_uint4(0, 0, 0, 0);
     constexpr int base = 16 * (GS - 1);
-    uint16_t g16[16 * GS + 8];
-#pragma unroll
-    for (int g = 0; g < 16 * GS + 8; ++g) {
+    constexpr int NCH = (16 * GS + 8) / 8;
+    // value of geometric column g of this key (layout in common.h)
+    auto geo = [&](int g) -> uint16_t {
       uint16_t val = 0;
       if (g < base + 4) {
         if (g < P3) val = hi16(w[g]);
@@ -668,11 +671,18 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       }
       // a masked key (or one past the end) is all zeros but for -65504 in
       // the key-mask column, which the query side multiplies by 16
-      g16[g] = valid ? val : (g == base + 8 ? (uint16_t)0xFBFF : (uint16_t)0);
-    }
+      return valid ? val : (g == base + 8 ? (uint16_t)0xFBFF : (uint16_t)0);
+    };
 #pragma unroll
-    for (int c = 0; c < (16 * GS + 8) / 8; ++c) *reinterpret_cast<uint4*>(krow + QW + 8 * c) = pack8(g16 + 8 * c);
-  } else if (tid == 64) {
+    for (int c = 0; c < NCH; ++c) {
+      if (c % 4 != wv) continue;
+      uint16_t g16[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g16[e] = geo(8 * c + e);
+      *reinterpret_cast<uint4*>(krow + QW + 8 * c) = pack8(g16);
+    }
+  }
+  if (tid == 64) {
     if (b == 0 && t == 0) reinterpret_cast<float*>(a.ws + L.off_gam)[h] = gam;
     if (h == 0) {
       float4* ck = reinterpret_cast<float4*>(a.ws + L.off_ck);
@@ -683,14 +693,15 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
         hd->has_pair_mask = a.pm != nullptr;
       }
     }
-  } else if (tid >= 128 && tid < 130 && h == 0) {
+  }
+  if (tid >= 128 && tid < 130 && h == 0) {
+    // word hw holds the keys of the 4-key groups 2k + hw (k = 0..7), group by
+    // group (the bit order of mask_bit_of_key)
     const int hw = tid - 128;
+    const uint64_t vm = (uint64_t)s_vmask[0] | ((uint64_t)s_vmask[1] << 32);
     uint32_t w = 0;
-    for (int jj = 0; jj < 64; ++jj) {
-      int hf;
-      const int bit = mask_bit_of_key(jj, &hf);
-      if (hf == hw && s_valid[jj]) w |= 1u << bit;
-    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w |= (uint32_t)((vm >> (4 * (2 * k + hw))) & 0xFu) << (4 * k);
     reinterpret_cast<uint32_t*>(a.ws + L.off_km)[((size_t)b * L.NT + t) * 2 + hw] = w;
   }
   // query global points: 16 floats per (b, h, i)
@@ -742,9 +753,10 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 64) = make_uint4(0, 0, 0, 0);
 
   // ---- 5. permitted-key words of every query row for this key tile
-  if (a.pm != nullptr && h == 0) {
+  // (the H workgroups of the tile share the query rows: rows h, h + H, ...)
+  if (a.pm != nullptr) {
     uint32_t* pmw = reinterpret_cast<uint32_t*>(a.ws + L.off_pm);
-    for (int i = tid; i < L.NQpad; i += 256) {
+    for (int i = tid * H + h; i < L.NQpad; i += 256 * H) {
       uint32_t w[2] = {0u, 0u};
       if (i < N && a.mask[(size_t)b * N + i]) {
         const uint8_t* row = a.pm + ((size_t)b * N + i) * N + (size_t)t * 64;
