@@ -297,25 +297,51 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
       cxyz[x] = __shfl(pick16(oacc[NVB], 4 * (rr >> 3) + (rr & 3)), l32 + 32 * ((rr & 7) >> 2));
     }
   }
-  if (!qin) return;
   const float ib = nonempty ? (1.0f / kVScale) / lbf : 0.f;  // the value rows hold v 2^-8
   const float ih = nonempty ? 1.0f / lh : 0.f;
-  float* orow = a.o + (((size_t)b * N + i) * H + h) * DO;
+  // O is written through LDS (the tile buffers are free now), in passes of
+  // PW columns: every wavefront puts its 32 x PW block in a slot of its own,
+  // then writes the 32 query rows with 16-byte stores (consecutive lanes,
+  // consecutive addresses) instead of 4-byte stores spread over 32 rows.
+  constexpr int SLOTS = W / 2;  // slots per buffer array
+  constexpr int PW = ((KT_LDS * 2 < VT_LDS * 2 ? KT_LDS * 2 : VT_LDS * 2) / (SLOTS * 32 * 4) - 1) / 4 * 4;
+  static_assert(PW >= 16, "LDS slots too small for the output staging");
+  float* slot = reinterpret_cast<float*>((w < SLOTS ? sk0 : sv0) + (size_t)(w % SLOTS) * 32 * (PW + 1) * 4);
+  const int i0 = i - l32;  // first query of this wavefront
+  __syncthreads();  // every wave is done with the tile buffers
+  for (int c0 = 0; c0 < DO; c0 += PW) {
+    const int c1 = min(DO, c0 + PW);
 #pragma unroll
-  for (int vb = 0; vb < NVB; ++vb)
+    for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = vb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (d < d1 && d >= c0 && d < c1) slot[l32 * (PW + 1) + d - c0] = oacc[vb][r] * ib;
+      }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int d = vb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (d < d1) orow[d] = oacc[vb][r] * ib;
+      const int dd = 8 * (r >> 2) + 4 * half + (r & 3);
+      const int d = d1 + dd;
+      if (dd < Q3 && d >= c0 && d < c1) {
+        const int x = dd % 3;
+        const float c = (x == 0) ? cxyz[0] : ((x == 1) ? cxyz[1] : cxyz[2]);
+        slot[l32 * (PW + 1) + d - c0] = (oacc[NVB][r] + c) * ih;
+      }
     }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int dd = 8 * (r >> 2) + 4 * half + (r & 3);
-    if (dd < Q3) {
-      const int x = dd % 3;
-      const float c = (x == 0) ? cxyz[0] : ((x == 1) ? cxyz[1] : cxyz[2]);
-      orow[d1 + dd] = (oacc[NVB][r] + c) * ih;
+    __builtin_amdgcn_wave_barrier();
+    const int nc = c1 - c0, n4 = (nc + 3) / 4;
+    for (int x = lane; x < 32 * n4; x += 64) {
+      const int q = x / n4, j = x % n4, iq = i0 + q;
+      if (iq >= N) continue;
+      const float* sr = slot + q * (PW + 1) + 4 * j;
+      float* dst = a.o + (((size_t)b * N + iq) * H + h) * DO + c0 + 4 * j;
+      if (4 * j + 4 <= nc && (DO & 3) == 0) {
+        *reinterpret_cast<float4*>(dst) = make_float4(sr[0], sr[1], sr[2], sr[3]);
+      } else {
+        for (int e = 0; e < 4 && 4 * j + e < nc; ++e) dst[e] = sr[e];
+      }
     }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
