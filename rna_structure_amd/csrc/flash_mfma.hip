@@ -102,6 +102,26 @@ __device__ __forceinline__ void dma_tile(const char* g, const char* s, int w, in
   }
 }
 
+// First key tile after t with at least one valid key (NT if none); kmb
+// points at the key-mask words of the batch element.
+__device__ __forceinline__ int next_valid_tile(const uint32_t* kmb, int t, int NT) {
+  for (++t; t < NT; ++t)
+    if ((ld_uniform(kmb + 2 * t) | ld_uniform(kmb + 2 * t + 1)) != 0u) break;
+  return __builtin_amdgcn_readfirstlane(t);
+}
+
+// Key and value tile t of one (batch, head) into LDS buffer buf.
+template <int NQS, int NVB, int GS, int W>
+__device__ __forceinline__ void copy_kv_tile(const char* ktg0, const char* vtg0, char* sk0, char* sv0, int t, int buf,
+                                             int w, int lane) {
+  constexpr int KT_BYTES = 64 * (16 * NQS + 16 * GS + kRowPad) * 2;
+  constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
+  constexpr int KT_LDS = (KT_BYTES + 1023) / 1024 * 1024;
+  constexpr int VT_LDS = (VT_BYTES + 1023) / 1024 * 1024;
+  dma_tile<KT_BYTES, W>(ktg0 + (size_t)t * KT_BYTES, sk0 + buf * KT_LDS, w, lane);
+  dma_tile<VT_BYTES, W>(vtg0 + (size_t)t * VT_BYTES, sv0 + buf * VT_LDS, w, lane);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -191,14 +211,15 @@ __device__ __forceinline__ float softmax_max(const f32x16_t* sacc, uint32_t mw, 
 }
 
 // Main loop over the key tiles and the final normalisation for one
-// wavefront's 32 queries.  Key/value tiles alternate between two LDS buffers:
+// wavefront's 32 queries.  The copy of the first tile t (into buffer 0) was
+// issued by the caller.  Key/value tiles alternate between two LDS buffers:
 // at the top of tile t the copies of t (issued one tile earlier) are waited
 // for, one barrier makes them visible and frees the other buffer, and the
 // copies of the next tile go out before the products of t start.  PM selects
 // the per-query pair-mask words (a vector load per tile); without a pair mask
 // the key mask is inside the key product.
 template <int NQS, int NVB, int GS, int W, bool PM>
-__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* sv0, int b, int h, int i, bool qin,
+__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* sv0, int t, int b, int h, int i, bool qin,
                                        bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
                                        const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
   constexpr int QW = 16 * NQS;
@@ -221,21 +242,9 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   const char* ktg0 = a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)KT_BYTES;
   const char* vtg0 = a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES;
   const uint32_t* kmb = km + (size_t)b * NT * 2;
-  auto next_tile = [&](int t) {
-    for (++t; t < NT; ++t)
-      if ((ld_uniform(kmb + 2 * t) | ld_uniform(kmb + 2 * t + 1)) != 0u) break;  // skip tiles without a valid key
-    return __builtin_amdgcn_readfirstlane(t);
-  };
-  auto copy_tile = [&](int t, int buf) {
-    dma_tile<KT_BYTES, W>(ktg0 + (size_t)t * KT_BYTES, sk0 + buf * KT_LDS, w, lane);
-    dma_tile<VT_BYTES, W>(vtg0 + (size_t)t * VT_BYTES, sv0 + buf * VT_LDS, w, lane);
-  };
-
-  int t = next_tile(-1);
   int buf = 0;
-  if (t < NT) copy_tile(t, 0);
   while (t < NT) {
-    const int tn = next_tile(t);
+    const int tn = next_valid_tile(kmb, t, NT);
     uint32_t mw = 0xFFFFFFFFu;
     if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
     geo_tile<GS>(qg, ld_uniform4(ck + (size_t)b * NT + t), gl, Pf, m, half, bg);
@@ -243,7 +252,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
     wait_vmcnt<0>();
     __syncthreads();
     if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
-    if (tn < NT) copy_tile(tn, buf ^ 1);
+    if (tn < NT) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, tn, buf ^ 1, w, lane);
     const char* sk = sk0 + buf * KT_LDS;
     const char* sv = sv0 + buf * VT_LDS;
 
@@ -299,46 +308,70 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   }
   const float ib = nonempty ? (1.0f / kVScale) / lbf : 0.f;  // the value rows hold v 2^-8
   const float ih = nonempty ? 1.0f / lh : 0.f;
-  // O is written through LDS (the tile buffers are free now), in passes of
-  // PW columns: every wavefront puts its 32 x PW block in a slot of its own,
-  // then writes the 32 query rows with 16-byte stores (consecutive lanes,
-  // consecutive addresses) instead of 4-byte stores spread over 32 rows.
+  // O is written through LDS (the tile buffers are free now), BPP
+  // accumulator blocks per pass: every wavefront stores its 32 queries x
+  // 32 BPP rows (scaled) in a slot of its own, register by register, then
+  // writes the pass's output columns, one contiguous range, 16 bytes per lane
+  // with consecutive lanes on consecutive addresses.
+  constexpr int NB = NVB + 1;
   constexpr int SLOTS = W / 2;  // slots per buffer array
-  constexpr int PW = ((KT_LDS * 2 < VT_LDS * 2 ? KT_LDS * 2 : VT_LDS * 2) / (SLOTS * 32 * 4) - 1) / 4 * 4;
-  static_assert(PW >= 16, "LDS slots too small for the output staging");
-  float* slot = reinterpret_cast<float*>((w < SLOTS ? sk0 : sv0) + (size_t)(w % SLOTS) * 32 * (PW + 1) * 4);
+  constexpr int BUF = KT_LDS * 2 < VT_LDS * 2 ? KT_LDS * 2 : VT_LDS * 2;
+  constexpr int BPP0 = (BUF / (SLOTS * 32 * 4) - 1) / 32;
+  constexpr int BPP = BPP0 < NB ? BPP0 : NB;
+  static_assert(BPP >= 1, "LDS slots too small for the output staging");
+  constexpr int PITCH = 32 * BPP + 1;  // floats per staged query row
+  float* slot = reinterpret_cast<float*>((w < SLOTS ? sk0 : sv0) + (size_t)(w % SLOTS) * 32 * PITCH * 4);
   const int i0 = i - l32;  // first query of this wavefront
   __syncthreads();  // every wave is done with the tile buffers
-  for (int c0 = 0; c0 < DO; c0 += PW) {
-    const int c1 = min(DO, c0 + PW);
 #pragma unroll
-    for (int vb = 0; vb < NVB; ++vb)
+  for (int p = 0; p < (NB + BPP - 1) / BPP; ++p) {
+    const int vb0 = p * BPP;
+    const int vb1 = vb0 + BPP < NB ? vb0 + BPP : NB;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = vb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (d < d1 && d >= c0 && d < c1) slot[l32 * (PW + 1) + d - c0] = oacc[vb][r] * ib;
-      }
+    for (int j = 0; j < BPP; ++j) {
+      const int vb = vb0 + j;
+      if (vb < NB) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int dd = 8 * (r >> 2) + 4 * half + (r & 3);
-      const int d = d1 + dd;
-      if (dd < Q3 && d >= c0 && d < c1) {
-        const int x = dd % 3;
-        const float c = (x == 0) ? cxyz[0] : ((x == 1) ? cxyz[1] : cxyz[2]);
-        slot[l32 * (PW + 1) + d - c0] = (oacc[NVB][r] + c) * ih;
+        for (int r = 0; r < 16; ++r) {
+          // row of register r in a 32-row block: 8 (r/4) + 4 half + r%4
+          const int rb = 8 * (r >> 2) + (r & 3);
+          float v;
+          if (vb < NVB) {
+            v = oacc[vb][r] * ib;
+          } else {
+            // value-point row dd = rb + 4 half: add back the centroid coordinate dd % 3
+            const int x0 = rb % 3, x1 = (rb + 4) % 3;
+            const float c0 = x0 == 0 ? cxyz[0] : (x0 == 1 ? cxyz[1] : cxyz[2]);
+            const float c1 = x1 == 0 ? cxyz[0] : (x1 == 1 ? cxyz[1] : cxyz[2]);
+            v = (oacc[NVB][r] + (half ? c1 : c0)) * ih;
+          }
+          slot[l32 * PITCH + 32 * j + rb + 4 * half] = v;
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    const int nc = c1 - c0, n4 = (nc + 3) / 4;
+    // output columns of this pass: values [32 vb0, min(32 vb1, d1)), then the
+    // value points [d1, d1 + 3Q) if the point block is in the pass
+    const int cs = vb0 < NVB ? min(32 * vb0, d1) : d1;
+    const int ce = vb1 > NVB ? d1 + Q3 : min(32 * vb1, d1);
+    const int nc = ce - cs, n4 = (nc + 3) >> 2;
+    const bool vec = ((DO | cs) & 3) == 0;
     for (int x = lane; x < 32 * n4; x += 64) {
-      const int q = x / n4, j = x % n4, iq = i0 + q;
+      const int q = x / n4, jj = x - q * n4, iq = i0 + q;
       if (iq >= N) continue;
-      const float* sr = slot + q * (PW + 1) + 4 * j;
-      float* dst = a.o + (((size_t)b * N + iq) * H + h) * DO + c0 + 4 * j;
-      if (4 * j + 4 <= nc && (DO & 3) == 0) {
-        *reinterpret_cast<float4*>(dst) = make_float4(sr[0], sr[1], sr[2], sr[3]);
+      const float* sr = slot + q * PITCH;
+      float e4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = cs + 4 * jj + e;
+        const int loc = c < d1 ? c - 32 * vb0 : 32 * (NVB - vb0) + (c - d1);
+        e4[e] = c < ce ? sr[loc] : 0.f;
+      }
+      float* dst = a.o + (((size_t)b * N + iq) * H + h) * DO + cs + 4 * jj;
+      if (vec && 4 * jj + 4 <= nc) {
+        *reinterpret_cast<float4*>(dst) = make_float4(e4[0], e4[1], e4[2], e4[3]);
       } else {
-        for (int e = 0; e < 4 && 4 * j + e < nc; ++e) dst[e] = sr[e];
+        for (int e = 0; e < 4 && 4 * jj + e < nc; ++e) dst[e] = e4[e];
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -373,6 +406,14 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   const int i = qt * (W * 32) + w * 32 + l32;
   const bool qin = i < N;
 
+  // the copy of the first key tile goes out before the query rows are loaded
+  const int NT = L.NT;
+  const int t0 = next_valid_tile(reinterpret_cast<const uint32_t*>(a.ws + L.off_km) + (size_t)b * NT * 2, -1, NT);
+  if (t0 < NT)
+    copy_kv_tile<NQS, NVB, GS, W>(a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)KT_BYTES,
+                                  a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES, sk, sv, t0, 0, w,
+                                  lane);
+
   const Header* hd = reinterpret_cast<const Header*>(a.ws);
   const bool has_pm = ld_uniform(&hd->has_pair_mask) != 0;
   const float gl = ld_uniform(reinterpret_cast<const float*>(a.ws + L.off_gam) + h) * kLog2e;
@@ -392,9 +433,9 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   }
 
   if (has_pm)
-    attend<NQS, NVB, GS, W, true>(a, sk, sv, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, true>(a, sk, sv, t0, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
   else
-    attend<NQS, NVB, GS, W, false>(a, sk, sv, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, false>(a, sk, sv, t0, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
 }
 
 // 8 wavefronts (256 queries) per workgroup when that still gives every CU a
