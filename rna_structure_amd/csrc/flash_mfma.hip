@@ -195,7 +195,11 @@ __device__ __forceinline__ float softmax_max(const f32x16_t* sacc, uint32_t mw, 
   float mt = fmaxf(s[0], s[1]);
 #pragma unroll
   for (int x = 2; x < 32; ++x) mt = fmaxf(mt, s[x]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  {
+    // the other half of the wavefront holds the same queries' other 32 keys
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+    mt = fmaxf(mt, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+  }
   // first permitted key of the row (masked keys are below -1e6), or a
   // maximum that grew by more than 8
   const bool need = init ? (mt > 8.0f) : (mt > -5.0e5f);
