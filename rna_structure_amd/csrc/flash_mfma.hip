@@ -214,6 +214,27 @@ __device__ __forceinline__ float softmax_max(const f32x16_t* sacc, uint32_t mw, 
   return alpha;
 }
 
+// Output of 32 queries i0 .. i0+31 none of which is valid: zero rows of O
+// and a log-sum-exp of -inf.
+__device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, int i0, int lane) {
+  const Layout& L = a.L;
+  const int N = L.N, H = L.H, DO = L.DO;
+  if (lane < 32 && i0 + lane < N) a.lse[((size_t)b * H + h) * N + i0 + lane] = -INFINITY;
+  if ((DO & 3) == 0) {
+    const int n4 = DO >> 2;
+    for (int x = lane; x < 32 * n4; x += 64) {
+      const int q = x / n4, j = x - q * n4;
+      if (i0 + q < N)
+        reinterpret_cast<float4*>(a.o + (((size_t)b * N + i0 + q) * H + h) * DO)[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+    for (int x = lane; x < 32 * DO; x += 64) {
+      const int q = x / DO, c = x - q * DO;
+      if (i0 + q < N) a.o[(((size_t)b * N + i0 + q) * H + h) * DO + c] = 0.f;
+    }
+  }
+}
+
 // Main loop over the key tiles and the final normalisation for one
 // wavefront's 32 queries.  The copy of the first tile t (into buffer 0) was
 // issued by the caller.  Key/value tiles alternate between two LDS buffers:
@@ -247,6 +268,9 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   const char* vtg0 = a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES;
   const uint32_t* kmb = km + (size_t)b * NT * 2;
   int buf = 0;
+  // a wavefront without a valid query keeps copying tiles and meeting the
+  // barriers, but does no products
+  const bool active = __any(qvalid);
   while (t < NT) {
     const int tn = next_valid_tile(kmb, t, NT);
     uint32_t mw = 0xFFFFFFFFu;
@@ -259,6 +283,11 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
     if (tn < NT) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, tn, buf ^ 1, w, lane);
     const char* sk = sk0 + buf * KT_LDS;
     const char* sv = sv0 + buf * VT_LDS;
+    if (!active) {
+      buf ^= 1;
+      t = tn;
+      continue;
+    }
 
     f32x16_t sacc[2];
     __builtin_amdgcn_s_setprio(1);
@@ -410,13 +439,25 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   const int i = qt * (W * 32) + w * 32 + l32;
   const bool qin = i < N;
 
-  // the copy of the first key tile goes out before the query rows are loaded
   const int NT = L.NT;
-  const int t0 = next_valid_tile(reinterpret_cast<const uint32_t*>(a.ws + L.off_km) + (size_t)b * NT * 2, -1, NT);
+  const uint32_t* kmb = reinterpret_cast<const uint32_t*>(a.ws + L.off_km) + (size_t)b * NT * 2;
+  // the copy of the first key tile goes out before anything else is loaded
+  const int t0 = next_valid_tile(kmb, -1, NT);
   if (t0 < NT)
     copy_kv_tile<NQS, NVB, GS, W>(a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)KT_BYTES,
                                   a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES, sk, sv, t0, 0, w,
                                   lane);
+  {
+    // a workgroup none of whose queries is valid (padding) only writes zeros
+    const int tq0 = (qt * W * 32) >> 6, tq1 = min(NT, tq0 + W / 2);
+    uint32_t any = 0;
+    for (int tq = tq0; tq < tq1; ++tq) any |= ld_uniform(kmb + 2 * tq) | ld_uniform(kmb + 2 * tq + 1);
+    if (any == 0) {
+      wait_vmcnt<0>();  // the tile copy lands before the workgroup's LDS is released
+      zero_rows(a, b, h, qt * (W * 32) + w * 32, lane);
+      return;
+    }
+  }
 
   const Header* hd = reinterpret_cast<const Header*>(a.ws);
   const bool has_pm = ld_uniform(&hd->has_pair_mask) != 0;

@@ -533,155 +533,6 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   const float gam = s_gam;
   const float gl = gam * kLog2e;
 
-  // ---- 3. [k | zr] straight into the key tile, [v | zr] transposed into LDS
-  uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * L.KROW;
-  auto vh = [](uint16_t bits) { return f32_to_f16_bits(bf16_bits_to_f32(bits) * kVScale); };
-#pragma unroll
-  for (int k = 0; k < kFastZ; ++k) {
-    const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
-    if (x < 64 * nz) {
-      const uint4 val = s_valid[r] ? zr_r[k] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + D + 8 * c) = val;
-      // value-tile entries: fp16 of the bf16 input times 2^-8
-      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_vzT[Dv + 8 * c + e][r] = vh(e16[e]);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kFastK; ++k) {
-    const int x = tid + 256 * k;
-    const int rk = fdiv(x, f.nk), ck = x - rk * nk;
-    if (x < 64 * nk)
-      *reinterpret_cast<uint4*>(kt + (size_t)rk * L.KROW + 8 * ck) = s_valid[rk] ? k_r[k] : make_uint4(0, 0, 0, 0);
-    const int rv = fdiv(x, f.nv), cv = x - rv * nv;
-    if (x < 64 * nv) {
-      const uint4 val = s_valid[rv] ? v_r[k] : make_uint4(0, 0, 0, 0);
-      const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][rv] = vh(e16[e]);
-    }
-  }
-  // global points: key points (centred), query points, value points (centred,
-  // zero for keys that are masked or past the end)
-#pragma unroll
-  for (int k = 0; k < kFastPts; ++k) {
-    const int x = tid + 256 * k, r = x % 64, it = x / 64;
-    if (x < 64 * npt) {
-      const bool in = t * 64 + r < N;
-      const float* Rm = s_rot[r];
-      const float tx = s_tr[r][0], ty = s_tr[r][1], tz = s_tr[r][2];
-      const float lx = pts[k][0], ly = pts[k][1], lz = pts[k][2];
-      const float gx = Rm[0] * lx + Rm[1] * ly + Rm[2] * lz + tx;
-      const float gy = Rm[3] * lx + Rm[4] * ly + Rm[5] * lz + ty;
-      const float gz = Rm[6] * lx + Rm[7] * ly + Rm[8] * lz + tz;
-      if (it < P) {
-        s_w[r][3 * it] = in ? gx - cx : 0.f;
-        s_w[r][3 * it + 1] = in ? gy - cy : 0.f;
-        s_w[r][3 * it + 2] = in ? gz - cz : 0.f;
-      } else if (it < 2 * P) {
-        const int p = it - P;
-        s_a[r][3 * p] = gx; s_a[r][3 * p + 1] = gy; s_a[r][3 * p + 2] = gz;
-      } else {
-        const int q = it - 2 * P;
-        const bool v = in && s_valid[r];
-        s_xT[3 * q][r] = v ? gx - cx : 0.f;
-        s_xT[3 * q + 1][r] = v ? gy - cy : 0.f;
-        s_xT[3 * q + 2][r] = v ? gz - cz : 0.f;
-      }
-    }
-  }
-  // lifted query rows [q sq | w_pair zl sp | 0]
-  {
-    const float sq = kLog2e / sqrtf(3.0f * (float)D);
-    const float sp = kLog2e / sqrtf(3.0f);
-    uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + (size_t)t * 64) * QW;
-#pragma unroll
-    for (int k = 0; k < kFastZ; ++k) {
-      const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
-      if (x < 64 * nz) {
-        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&zl_r[k]);
-        const float* wp = s_wp + (8 * c) % Cz;
-        uint4 pk;
-        pk.x = pack_bf16x2(wp[0] * bf16_bits_to_f32(e16[0]) * sp, wp[1] * bf16_bits_to_f32(e16[1]) * sp);
-        pk.y = pack_bf16x2(wp[2] * bf16_bits_to_f32(e16[2]) * sp, wp[3] * bf16_bits_to_f32(e16[3]) * sp);
-        pk.z = pack_bf16x2(wp[4] * bf16_bits_to_f32(e16[4]) * sp, wp[5] * bf16_bits_to_f32(e16[5]) * sp);
-        pk.w = pack_bf16x2(wp[6] * bf16_bits_to_f32(e16[6]) * sp, wp[7] * bf16_bits_to_f32(e16[7]) * sp);
-        *reinterpret_cast<uint4*>(ql + (size_t)r * QW + D + 8 * c) = pk;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kFastK; ++k) {
-      const int x = tid + 256 * k, r = fdiv(x, f.nk), c = x - r * nk;
-      if (x < 64 * nk) {
-        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&q_r[k]);
-        uint4 pk;
-        pk.x = pack_bf16x2(bf16_bits_to_f32(e16[0]) * sq, bf16_bits_to_f32(e16[1]) * sq);
-        pk.y = pack_bf16x2(bf16_bits_to_f32(e16[2]) * sq, bf16_bits_to_f32(e16[3]) * sq);
-        pk.z = pack_bf16x2(bf16_bits_to_f32(e16[4]) * sq, bf16_bits_to_f32(e16[5]) * sq);
-        pk.w = pack_bf16x2(bf16_bits_to_f32(e16[6]) * sq, bf16_bits_to_f32(e16[7]) * sq);
-        *reinterpret_cast<uint4*>(ql + (size_t)r * QW + 8 * c) = pk;
-      }
-    }
-    // zero columns [D + R Cz, QW)
-    const int nzero = (QW - D - RCz) / 8;
-    for (int x = tid; x < 64 * nzero; x += 256)
-      *reinterpret_cast<uint4*>(ql + (size_t)(x / nzero) * QW + D + RCz + 8 * (x % nzero)) = make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-
-  // ---- 4. key rows past [k | zr] (one thread per key): zeros up to QW, the
-  // geometric columns (layout in common.h), 8 pad columns
-  const int VROWS = L.VROWS, NVB = L.NVB, DZ = Dv + RCz;
-  {
-    // every wavefront: lane = key, chunks w, w + 4, ... of the 16 GS + 8
-    // columns after QW; each lane recomputes its key's point sums
-    const int r = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool valid = s_valid[r] != 0;
-    float w[P3];
-#pragma unroll
-    for (int g = 0; g < P3; ++g) w[g] = s_w[r][g];
-    float nb = 0.f, Wx = 0.f, Wy = 0.f, Wz = 0.f;
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      nb += w[3 * p] * w[3 * p] + w[3 * p + 1] * w[3 * p + 1] + w[3 * p + 2] * w[3 * p + 2];
-      Wx += w[3 * p]; Wy += w[3 * p + 1]; Wz += w[3 * p + 2];
-    }
-    nb = -gl * nb;
-    const float ww[3] = {2.f * gl * Wx, 2.f * gl * Wy, 2.f * gl * Wz};
-    uint16_t* krow = kt + (size_t)r * L.KROW;
-    if (wv == 0)
-      for (int c = D + RCz; c < QW; c += 8) *reinterpret_cast<uint4*>(krow + c) = make_uint4(0, 0, 0, 0);
-    constexpr int base = 16 * (GS - 1);
-    constexpr int NCH = (16 * GS + 8) / 8;
-    // value of geometric column g of this key (layout in common.h)
-    auto geo = [&](int g) -> uint16_t {
-      uint16_t val = 0;
-      if (g < base + 4) {
-        if (g < P3) val = hi16(w[g]);
-        else if (g < 2 * P3) val = lo16(w[g - P3]);
-        else if (g < 3 * P3) val = hi16(w[g - 2 * P3]);
-      } else if (g < 16 * GS) {
-        const int y = g - base;
-        if (y == 4) val = hi16(nb * (1.0f / kNormScale));
-        else if (y == 12) val = lo16(nb * (1.0f / kNormScale));
-        else if (y >= 5 && y <= 7) val = hi16(ww[y - 5]);
-        else if (y >= 13) val = lo16(ww[y - 13]);
-        else if (y >= 9 && y <= 11) val = 0x4C00;  // fp16 16.0, multiplies the query's t'/16 parts
-      }
-      // a masked key (or one past the end) is all zeros but for -65504 in
-      // the key-mask column, which the query side multiplies by 16
-      return valid ? val : (g == base + 8 ? (uint16_t)0xFBFF : (uint16_t)0);
-    };
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (c % 4 != wv) continue;
-      uint16_t g16[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) g16[e] = geo(8 * c + e);
-      *reinterpret_cast<uint4*>(krow + QW + 8 * c) = pack8(g16);
-    }
-  }
   if (tid == 64) {
     if (b == 0 && t == 0) reinterpret_cast<float*>(a.ws + L.off_gam)[h] = gam;
     if (h == 0) {
@@ -704,53 +555,207 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     for (int k = 0; k < 8; ++k) w |= (uint32_t)((vm >> (4 * (2 * k + hw))) & 0xFu) << (4 * k);
     reinterpret_cast<uint32_t*>(a.ws + L.off_km)[((size_t)b * L.NT + t) * 2 + hw] = w;
   }
-  // query global points: 16 floats per (b, h, i)
-  {
-    float4* qa = reinterpret_cast<float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + (size_t)t * 64) * 4;
-    const int row = tid / 4, c = (tid % 4) * 4;
-    float v[4];
+  // a tile without a valid residue is never read: the fused kernel skips
+  // key tiles without a valid key and writes padding queries as zeros
+  const bool tile_any = (s_vmask[0] | s_vmask[1]) != 0u;
+  if (tile_any) {
+    // ---- 3. [k | zr] straight into the key tile, [v | zr] transposed into LDS
+    uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * L.KROW;
+    auto vh = [](uint16_t bits) { return f32_to_f16_bits(bf16_bits_to_f32(bits) * kVScale); };
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (row < nrow && c + e < P3) ? s_a[row][c + e] : 0.f;
-    qa[tid] = make_float4(v[0], v[1], v[2], v[3]);
-  }
-  // transposed value tile: rows d, columns kappa; columns k0 .. k0+7 hold keys
-  // j0 .. j0+3 and j0+8 .. j0+11 (j0 = vt_key_of_col(k0)), columns 64 .. 71 are zero
-  uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + L.off_vt) + (((size_t)b * H + h) * L.NT + t) * VROWS * kVCols;
-  const uint32_t vm0 = s_vmask[0], vm1 = s_vmask[1];
-  // rows [v | zr]: 8 column chunks each, straight from the transposed LDS copy
-  for (int x = tid; x < DZ * 8; x += 256) {
-    const int d = x >> 3, j0 = vt_key_of_col(8 * (x & 7));
-    const uint32_t* row = reinterpret_cast<const uint32_t*>(&s_vzT[d][0]);
-    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * (x & 7)) =
-        make_uint4(row[j0 / 2], row[j0 / 2 + 1], row[j0 / 2 + 4], row[j0 / 2 + 5]);
-  }
-  // the other rows: the weight-sum row, zero rows, centred value points, the
-  // ones row and the centroid (valid keys only)
-  for (int x = tid; x < (VROWS - DZ) * 8; x += 256) {
-    const int d = DZ + (x >> 3), j0 = vt_key_of_col(8 * (x & 7));
-    // valid bits of the 8 keys, in column order
-    const uint32_t word = j0 < 32 ? vm0 : vm1;
-    const uint32_t bits = ((word >> (j0 & 31)) & 0xFu) | (((word >> ((j0 & 31) + 8)) & 0xFu) << 4);
-    uint16_t one = 0;
-    const int dd = d - 32 * NVB;
-    if (d == DZ) one = 0x3C00;                          // fp16 1.0: weight sum
-    else if (dd == 3 * Q) one = 0x3C00;                 // fp16 1.0: weight sum
-    else if (dd > 3 * Q && dd <= 3 * Q + 3) one = hi16(s_c[dd - 3 * Q - 1]);  // centroid
-    uint16_t out[8];
-    if (dd >= 0 && dd < 3 * Q) {
-      const float4 lo = *reinterpret_cast<const float4*>(&s_xT[dd][j0]);
-      const float4 hi = *reinterpret_cast<const float4*>(&s_xT[dd][j0 + 8]);
-      out[0] = hi16(lo.x); out[1] = hi16(lo.y); out[2] = hi16(lo.z); out[3] = hi16(lo.w);
-      out[4] = hi16(hi.x); out[5] = hi16(hi.y); out[6] = hi16(hi.z); out[7] = hi16(hi.w);
-    } else {
+    for (int k = 0; k < kFastZ; ++k) {
+      const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+      if (x < 64 * nz) {
+        const uint4 val = s_valid[r] ? zr_r[k] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + D + 8 * c) = val;
+        // value-tile entries: fp16 of the bf16 input times 2^-8
+        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = ((bits >> e) & 1u) ? one : (uint16_t)0;
+        for (int e = 0; e < 8; ++e) s_vzT[Dv + 8 * c + e][r] = vh(e16[e]);
+      }
     }
-    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * (x & 7)) = pack8(out);
+#pragma unroll
+    for (int k = 0; k < kFastK; ++k) {
+      const int x = tid + 256 * k;
+      const int rk = fdiv(x, f.nk), ck = x - rk * nk;
+      if (x < 64 * nk)
+        *reinterpret_cast<uint4*>(kt + (size_t)rk * L.KROW + 8 * ck) = s_valid[rk] ? k_r[k] : make_uint4(0, 0, 0, 0);
+      const int rv = fdiv(x, f.nv), cv = x - rv * nv;
+      if (x < 64 * nv) {
+        const uint4 val = s_valid[rv] ? v_r[k] : make_uint4(0, 0, 0, 0);
+        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][rv] = vh(e16[e]);
+      }
+    }
+    // global points: key points (centred), query points, value points (centred,
+    // zero for keys that are masked or past the end)
+#pragma unroll
+    for (int k = 0; k < kFastPts; ++k) {
+      const int x = tid + 256 * k, r = x % 64, it = x / 64;
+      if (x < 64 * npt) {
+        const bool in = t * 64 + r < N;
+        const float* Rm = s_rot[r];
+        const float tx = s_tr[r][0], ty = s_tr[r][1], tz = s_tr[r][2];
+        const float lx = pts[k][0], ly = pts[k][1], lz = pts[k][2];
+        const float gx = Rm[0] * lx + Rm[1] * ly + Rm[2] * lz + tx;
+        const float gy = Rm[3] * lx + Rm[4] * ly + Rm[5] * lz + ty;
+        const float gz = Rm[6] * lx + Rm[7] * ly + Rm[8] * lz + tz;
+        if (it < P) {
+          s_w[r][3 * it] = in ? gx - cx : 0.f;
+          s_w[r][3 * it + 1] = in ? gy - cy : 0.f;
+          s_w[r][3 * it + 2] = in ? gz - cz : 0.f;
+        } else if (it < 2 * P) {
+          const int p = it - P;
+          s_a[r][3 * p] = gx; s_a[r][3 * p + 1] = gy; s_a[r][3 * p + 2] = gz;
+        } else {
+          const int q = it - 2 * P;
+          const bool v = in && s_valid[r];
+          s_xT[3 * q][r] = v ? gx - cx : 0.f;
+          s_xT[3 * q + 1][r] = v ? gy - cy : 0.f;
+          s_xT[3 * q + 2][r] = v ? gz - cz : 0.f;
+        }
+      }
+    }
+    // lifted query rows [q sq | w_pair zl sp | 0]
+    {
+      const float sq = kLog2e / sqrtf(3.0f * (float)D);
+      const float sp = kLog2e / sqrtf(3.0f);
+      uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + (size_t)t * 64) * QW;
+#pragma unroll
+      for (int k = 0; k < kFastZ; ++k) {
+        const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+        if (x < 64 * nz) {
+          const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&zl_r[k]);
+          const float* wp = s_wp + (8 * c) % Cz;
+          uint4 pk;
+          pk.x = pack_bf16x2(wp[0] * bf16_bits_to_f32(e16[0]) * sp, wp[1] * bf16_bits_to_f32(e16[1]) * sp);
+          pk.y = pack_bf16x2(wp[2] * bf16_bits_to_f32(e16[2]) * sp, wp[3] * bf16_bits_to_f32(e16[3]) * sp);
+          pk.z = pack_bf16x2(wp[4] * bf16_bits_to_f32(e16[4]) * sp, wp[5] * bf16_bits_to_f32(e16[5]) * sp);
+          pk.w = pack_bf16x2(wp[6] * bf16_bits_to_f32(e16[6]) * sp, wp[7] * bf16_bits_to_f32(e16[7]) * sp);
+          *reinterpret_cast<uint4*>(ql + (size_t)r * QW + D + 8 * c) = pk;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kFastK; ++k) {
+        const int x = tid + 256 * k, r = fdiv(x, f.nk), c = x - r * nk;
+        if (x < 64 * nk) {
+          const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&q_r[k]);
+          uint4 pk;
+          pk.x = pack_bf16x2(bf16_bits_to_f32(e16[0]) * sq, bf16_bits_to_f32(e16[1]) * sq);
+          pk.y = pack_bf16x2(bf16_bits_to_f32(e16[2]) * sq, bf16_bits_to_f32(e16[3]) * sq);
+          pk.z = pack_bf16x2(bf16_bits_to_f32(e16[4]) * sq, bf16_bits_to_f32(e16[5]) * sq);
+          pk.w = pack_bf16x2(bf16_bits_to_f32(e16[6]) * sq, bf16_bits_to_f32(e16[7]) * sq);
+          *reinterpret_cast<uint4*>(ql + (size_t)r * QW + 8 * c) = pk;
+        }
+      }
+      // zero columns [D + R Cz, QW)
+      const int nzero = (QW - D - RCz) / 8;
+      for (int x = tid; x < 64 * nzero; x += 256)
+        *reinterpret_cast<uint4*>(ql + (size_t)(x / nzero) * QW + D + RCz + 8 * (x % nzero)) = make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    // ---- 4. key rows past [k | zr] (one thread per key): zeros up to QW, the
+    // geometric columns (layout in common.h), 8 pad columns
+    const int VROWS = L.VROWS, NVB = L.NVB, DZ = Dv + RCz;
+    {
+      // every wavefront: lane = key, chunks w, w + 4, ... of the 16 GS + 8
+      // columns after QW; each lane recomputes its key's point sums
+      const int r = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const bool valid = s_valid[r] != 0;
+      float w[P3];
+#pragma unroll
+      for (int g = 0; g < P3; ++g) w[g] = s_w[r][g];
+      float nb = 0.f, Wx = 0.f, Wy = 0.f, Wz = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        nb += w[3 * p] * w[3 * p] + w[3 * p + 1] * w[3 * p + 1] + w[3 * p + 2] * w[3 * p + 2];
+        Wx += w[3 * p]; Wy += w[3 * p + 1]; Wz += w[3 * p + 2];
+      }
+      nb = -gl * nb;
+      const float ww[3] = {2.f * gl * Wx, 2.f * gl * Wy, 2.f * gl * Wz};
+      uint16_t* krow = kt + (size_t)r * L.KROW;
+      if (wv == 0)
+        for (int c = D + RCz; c < QW; c += 8) *reinterpret_cast<uint4*>(krow + c) = make_uint4(0, 0, 0, 0);
+      constexpr int base = 16 * (GS - 1);
+      constexpr int NCH = (16 * GS + 8) / 8;
+      // value of geometric column g of this key (layout in common.h)
+      auto geo = [&](int g) -> uint16_t {
+        uint16_t val = 0;
+        if (g < base + 4) {
+          if (g < P3) val = hi16(w[g]);
+          else if (g < 2 * P3) val = lo16(w[g - P3]);
+          else if (g < 3 * P3) val = hi16(w[g - 2 * P3]);
+        } else if (g < 16 * GS) {
+          const int y = g - base;
+          if (y == 4) val = hi16(nb * (1.0f / kNormScale));
+          else if (y == 12) val = lo16(nb * (1.0f / kNormScale));
+          else if (y >= 5 && y <= 7) val = hi16(ww[y - 5]);
+          else if (y >= 13) val = lo16(ww[y - 13]);
+          else if (y >= 9 && y <= 11) val = 0x4C00;  // fp16 16.0, multiplies the query's t'/16 parts
+        }
+        // a masked key (or one past the end) is all zeros but for -65504 in
+        // the key-mask column, which the query side multiplies by 16
+        return valid ? val : (g == base + 8 ? (uint16_t)0xFBFF : (uint16_t)0);
+      };
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (c % 4 != wv) continue;
+        uint16_t g16[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) g16[e] = geo(8 * c + e);
+        *reinterpret_cast<uint4*>(krow + QW + 8 * c) = pack8(g16);
+      }
+    }
+    // query global points: 16 floats per (b, h, i)
+    {
+      float4* qa = reinterpret_cast<float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + (size_t)t * 64) * 4;
+      const int row = tid / 4, c = (tid % 4) * 4;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (row < nrow && c + e < P3) ? s_a[row][c + e] : 0.f;
+      qa[tid] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    // transposed value tile: rows d, columns kappa; columns k0 .. k0+7 hold keys
+    // j0 .. j0+3 and j0+8 .. j0+11 (j0 = vt_key_of_col(k0)), columns 64 .. 71 are zero
+    uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + L.off_vt) + (((size_t)b * H + h) * L.NT + t) * VROWS * kVCols;
+    const uint32_t vm0 = s_vmask[0], vm1 = s_vmask[1];
+    // rows [v | zr]: 8 column chunks each, straight from the transposed LDS copy
+    for (int x = tid; x < DZ * 8; x += 256) {
+      const int d = x >> 3, j0 = vt_key_of_col(8 * (x & 7));
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(&s_vzT[d][0]);
+      *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * (x & 7)) =
+          make_uint4(row[j0 / 2], row[j0 / 2 + 1], row[j0 / 2 + 4], row[j0 / 2 + 5]);
+    }
+    // the other rows: the weight-sum row, zero rows, centred value points, the
+    // ones row and the centroid (valid keys only)
+    for (int x = tid; x < (VROWS - DZ) * 8; x += 256) {
+      const int d = DZ + (x >> 3), j0 = vt_key_of_col(8 * (x & 7));
+      // valid bits of the 8 keys, in column order
+      const uint32_t word = j0 < 32 ? vm0 : vm1;
+      const uint32_t bits = ((word >> (j0 & 31)) & 0xFu) | (((word >> ((j0 & 31) + 8)) & 0xFu) << 4);
+      uint16_t one = 0;
+      const int dd = d - 32 * NVB;
+      if (d == DZ) one = 0x3C00;                          // fp16 1.0: weight sum
+      else if (dd == 3 * Q) one = 0x3C00;                 // fp16 1.0: weight sum
+      else if (dd > 3 * Q && dd <= 3 * Q + 3) one = hi16(s_c[dd - 3 * Q - 1]);  // centroid
+      uint16_t out[8];
+      if (dd >= 0 && dd < 3 * Q) {
+        const float4 lo = *reinterpret_cast<const float4*>(&s_xT[dd][j0]);
+        const float4 hi = *reinterpret_cast<const float4*>(&s_xT[dd][j0 + 8]);
+        out[0] = hi16(lo.x); out[1] = hi16(lo.y); out[2] = hi16(lo.z); out[3] = hi16(lo.w);
+        out[4] = hi16(hi.x); out[5] = hi16(hi.y); out[6] = hi16(hi.z); out[7] = hi16(hi.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = ((bits >> e) & 1u) ? one : (uint16_t)0;
+      }
+      *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * (x & 7)) = pack8(out);
+    }
+    // pad columns 64 .. 71 of every row
+    for (int d = tid; d < VROWS; d += 256)
+      *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 64) = make_uint4(0, 0, 0, 0);
   }
-  // pad columns 64 .. 71 of every row
-  for (int d = tid; d < VROWS; d += 256)
-    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 64) = make_uint4(0, 0, 0, 0);
 
   // ---- 5. permitted-key words of every query row for this key tile
   // (the H workgroups of the tile share the query rows: rows h, h + H, ...)
@@ -758,7 +763,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     uint32_t* pmw = reinterpret_cast<uint32_t*>(a.ws + L.off_pm);
     for (int i = tid * H + h; i < L.NQpad; i += 256 * H) {
       uint32_t w[2] = {0u, 0u};
-      if (i < N && a.mask[(size_t)b * N + i]) {
+      if (tile_any && i < N && a.mask[(size_t)b * N + i]) {
         const uint8_t* row = a.pm + ((size_t)b * N + i) * N + (size_t)t * 64;
         if (f.pm_vec) {
           // N is a multiple of 16 and the rows are 16-byte aligned
