@@ -78,8 +78,23 @@ struct Layout {
   int DO;     // attention output width Dv + R*Cz + 3Q
   int has_pm;
   int F, FP;  // epilogue feature count, padded to 16
-  size_t off_ql, off_qa, off_kt, off_vt, off_ck, off_gam, off_km, off_wt, off_pm, total;
+  int KS;     // matrix-core path: key ranges the fused kernel splits a query tile over
+  int PREC;   // floats per partial-result record (KS > 1): DO values + 4 statistics, padded to 4
+  size_t off_ql, off_qa, off_kt, off_vt, off_ck, off_gam, off_km, off_wt, off_part, off_pm, total;
 };
+
+// Key ranges per query tile of the fused kernel: when (b, h, 256-query tile)
+// workgroups do not fill the 256 compute units, the keys are split into KS
+// ranges (at most 4, of at least 4 tiles each), one workgroup per range, and
+// a combine kernel merges the partial results.
+static inline int key_splits(int B, int N, int H, int NT) {
+  const long n8 = (long)((N + 255) / 256) * H * B;
+  if (n8 >= 256) return 1;
+  int ks = (int)((256 + n8 - 1) / n8);
+  ks = ks < 4 ? ks : 4;
+  ks = ks < NT / 4 ? ks : NT / 4;
+  return ks > 1 ? ks : 1;
+}
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -133,10 +148,12 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
     L->KROW = L->QW + 16 * md.GS + kRowPad;
     L->VROWS = 32 * (md.NVB + 1);
     L->DQP = L->QW;
+    L->KS = key_splits(L->B, L->N, L->H, L->NT);
   } else if (s->dtype == IPA_F32) {
     if (L->D + L->RCz > kF32MaxDQ || L->DO > kF32MaxDV) return false;
     L->mfma = 0;
     L->NQS = L->NVB = L->GS = 0;
+    L->KS = 1;
     L->DQP = round_up(L->D + L->RCz, 4);
     L->QW = L->DQP;
     L->KROW = round_up(L->D + L->RCz + 3 * L->P, 4);
@@ -165,6 +182,11 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
   // output projection transposed to [Cout][FP] bf16 (matrix-core path)
   L->off_wt = off;
   if (L->mfma) off = align256(off + (size_t)L->Cout * L->FP * 2);
+  // partial results of the key ranges: [KS][B][H][NQpad][PREC] fp32 (before
+  // the pair-mask region, whose presence does not move it)
+  L->PREC = round_up(L->DO + 4, 4);
+  L->off_part = off;
+  if (L->KS > 1) off = align256(off + (size_t)L->KS * B * H * NQ * L->PREC * 4);
   L->off_pm = off;
   if (with_pm) off = align256(off + B * NQ * NT * 2 * 4);
   L->total = off;

@@ -40,6 +40,7 @@ struct FlashMfmaArgs {
   float* lse;
   int qtiles;
   int nwg;
+  int ks;  // key ranges per query tile (partial results when > 1)
 };
 
 template <typename V>
@@ -216,9 +217,18 @@ __device__ __forceinline__ float softmax_max(const f32x16_t* sacc, uint32_t mw, 
 
 // Output of 32 queries i0 .. i0+31 none of which is valid: zero rows of O
 // and a log-sum-exp of -inf.
-__device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, int i0, int lane) {
+__device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, int s, int i0, int lane) {
   const Layout& L = a.L;
   const int N = L.N, H = L.H, DO = L.DO;
+  if (a.ks > 1) {
+    // partial result: empty statistics (the combine reads no values then)
+    if (lane < 32 && i0 + lane < N) {
+      float* rec = reinterpret_cast<float*>(const_cast<char*>(a.ws) + L.off_part) +
+                   ((((size_t)s * L.B + b) * H + h) * L.NQpad + i0 + lane) * L.PREC + DO;
+      rec[0] = -INFINITY; rec[1] = 0.f; rec[2] = 0.f; rec[3] = 0.f;
+    }
+    return;
+  }
   if (lane < 32 && i0 + lane < N) a.lse[((size_t)b * H + h) * N + i0 + lane] = -INFINITY;
   if ((DO & 3) == 0) {
     const int n4 = DO >> 2;
@@ -235,7 +245,8 @@ __device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, 
   }
 }
 
-// Main loop over the key tiles and the final normalisation for one
+// Main loop over the key tiles [t, tend) of key range sp and the final
+// normalisation (or, with several key ranges, the partial result) for one
 // wavefront's 32 queries.  The copy of the first tile t (into buffer 0) was
 // issued by the caller.  Key/value tiles alternate between two LDS buffers:
 // at the top of tile t the copies of t (issued one tile earlier) are waited
@@ -244,8 +255,8 @@ __device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, 
 // the per-query pair-mask words (a vector load per tile); without a pair mask
 // the key mask is inside the key product.
 template <int NQS, int NVB, int GS, int W, bool PM>
-__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* sv0, int t, int b, int h, int i, bool qin,
-                                       bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
+__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* sv0, int t, int tend, int sp, int b,
+                                       int h, int i, bool qin, bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
                                        const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
   constexpr int QW = 16 * NQS;
   constexpr int KROW = QW + 16 * GS + kRowPad;
@@ -271,8 +282,8 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   // a wavefront without a valid query keeps copying tiles and meeting the
   // barriers, but does no products
   const bool active = __any(qvalid);
-  while (t < NT) {
-    const int tn = next_valid_tile(kmb, t, NT);
+  while (t < tend) {
+    const int tn = next_valid_tile(kmb, t, tend);
     uint32_t mw = 0xFFFFFFFFu;
     if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
     geo_tile<GS>(qg, ld_uniform4(ck + (size_t)b * NT + t), gl, Pf, m, half, bg);
@@ -280,7 +291,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
     wait_vmcnt<0>();
     __syncthreads();
     if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
-    if (tn < NT) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, tn, buf ^ 1, w, lane);
+    if (tn < tend) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, tn, buf ^ 1, w, lane);
     const char* sk = sk0 + buf * KT_LDS;
     const char* sv = sv0 + buf * VT_LDS;
     if (!active) {
@@ -313,7 +324,8 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   // ---- finalise
   const float ltot = l + __shfl_xor(l, 32);
   const bool nonempty = qvalid && init && ltot > 0.f;
-  if (qin && half == 0)
+  const bool partial = a.ks > 1;
+  if (qin && half == 0 && !partial)
     a.lse[((size_t)b * H + h) * N + i] = nonempty ? (m + log2f(ltot)) * kLn2 : -INFINITY;
 
   // row d of a 32-row block sits in register 4*(d/8) + d%4 of the lane half (d%8)/4
@@ -339,8 +351,19 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
       cxyz[x] = __shfl(pick16(oacc[NVB], 4 * (rr >> 3) + (rr & 3)), l32 + 32 * ((rr & 7) >> 2));
     }
   }
-  const float ib = nonempty ? (1.0f / kVScale) / lbf : 0.f;  // the value rows hold v 2^-8
-  const float ih = nonempty ? 1.0f / lh : 0.f;
+  // a partial result keeps the unnormalised sums (values times 2^-8) and
+  // its statistics; the combine normalises
+  const float ib = nonempty ? (partial ? 1.0f : (1.0f / kVScale) / lbf) : 0.f;  // the value rows hold v 2^-8
+  const float ih = nonempty ? (partial ? 1.0f : 1.0f / lh) : 0.f;
+  float* prec = reinterpret_cast<float*>(const_cast<char*>(a.ws) + L.off_part) +
+                (((size_t)sp * L.B + b) * H + h) * L.NQpad * L.PREC;
+  if (partial && qin && half == 0) {
+    float* st = prec + (size_t)i * L.PREC + DO;
+    st[0] = nonempty ? m : -INFINITY;
+    st[1] = nonempty ? ltot : 0.f;
+    st[2] = nonempty ? lbf : 0.f;
+    st[3] = nonempty ? lh : 0.f;
+  }
   // O is written through LDS (the tile buffers are free now), BPP
   // accumulator blocks per pass: every wavefront stores its 32 queries x
   // 32 BPP rows (scaled) in a slot of its own, register by register, then
@@ -388,7 +411,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
     const int cs = vb0 < NVB ? min(32 * vb0, d1) : d1;
     const int ce = vb1 > NVB ? d1 + Q3 : min(32 * vb1, d1);
     const int nc = ce - cs, n4 = (nc + 3) >> 2;
-    const bool vec = ((DO | cs) & 3) == 0;
+    const bool vec = (((partial ? L.PREC : DO) | cs) & 3) == 0;
     for (int x = lane; x < 32 * n4; x += 64) {
       const int q = x / n4, jj = x - q * n4, iq = i0 + q;
       if (iq >= N) continue;
@@ -400,7 +423,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
         const int loc = c < d1 ? c - 32 * vb0 : 32 * (NVB - vb0) + (c - d1);
         e4[e] = c < ce ? sr[loc] : 0.f;
       }
-      float* dst = a.o + (((size_t)b * N + iq) * H + h) * DO + cs + 4 * jj;
+      float* dst = (partial ? prec + (size_t)iq * L.PREC : a.o + (((size_t)b * N + iq) * H + h) * DO) + cs + 4 * jj;
       if (vec && 4 * jj + 4 <= nc) {
         *reinterpret_cast<float4*>(dst) = make_float4(e4[0], e4[1], e4[2], e4[3]);
       } else {
@@ -431,7 +454,8 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   int logical = wg;
   if ((a.nwg & 7) == 0) logical = (wg & 7) * (a.nwg >> 3) + (wg >> 3);
   const int qt = logical % a.qtiles;
-  const int bh = logical / a.qtiles;
+  const int sp = (logical / a.qtiles) % a.ks;  // key range
+  const int bh = logical / (a.qtiles * a.ks);
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
@@ -441,9 +465,11 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
 
   const int NT = L.NT;
   const uint32_t* kmb = reinterpret_cast<const uint32_t*>(a.ws + L.off_km) + (size_t)b * NT * 2;
-  // the copy of the first key tile goes out before anything else is loaded
-  const int t0 = next_valid_tile(kmb, -1, NT);
-  if (t0 < NT)
+  // key tiles [tb, te) of key range sp; the copy of the first goes out
+  // before anything else is loaded
+  const int tb = (int)(((long)NT * sp) / a.ks), te = (int)(((long)NT * (sp + 1)) / a.ks);
+  const int t0 = next_valid_tile(kmb, tb - 1, te);
+  if (t0 < te)
     copy_kv_tile<NQS, NVB, GS, W>(a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)KT_BYTES,
                                   a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES, sk, sv, t0, 0, w,
                                   lane);
@@ -454,7 +480,7 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
     for (int tq = tq0; tq < tq1; ++tq) any |= ld_uniform(kmb + 2 * tq) | ld_uniform(kmb + 2 * tq + 1);
     if (any == 0) {
       wait_vmcnt<0>();  // the tile copy lands before the workgroup's LDS is released
-      zero_rows(a, b, h, qt * (W * 32) + w * 32, lane);
+      zero_rows(a, b, h, sp, qt * (W * 32) + w * 32, lane);
       return;
     }
   }
@@ -478,13 +504,62 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   }
 
   if (has_pm)
-    attend<NQS, NVB, GS, W, true>(a, sk, sv, t0, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, true>(a, sk, sv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
   else
-    attend<NQS, NVB, GS, W, false>(a, sk, sv, t0, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, false>(a, sk, sv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+}
+
+// Merge the partial results of the KS key ranges of every (b, h, query):
+// weights 2^(m_s - m) for the range maxima m_s, values divided by the merged
+// ones-row sums, log-sum-exp from the merged fp32 sums.  One thread per four
+// output columns of a row.
+__global__ __launch_bounds__(256) void combine_kernel(Layout L, const float* part, float* o, float* lse) {
+  const int DO = L.DO, n4 = (DO + 3) >> 2, H = L.H, N = L.N, KS = L.KS;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)L.B * N * H * n4) return;
+  const long row = idx / n4;  // output row (b, i, h)
+  const int c4 = (int)(idx - row * n4);
+  const int h = (int)(row % H), i = (int)((row / H) % N), b = (int)(row / ((long)H * N));
+  const size_t sstride = (size_t)L.B * H * L.NQpad * L.PREC;
+  const float* rec0 = part + (((size_t)b * H + h) * L.NQpad + i) * L.PREC;
+  float m = -INFINITY;
+  for (int s = 0; s < KS; ++s) {
+    const float* st = rec0 + s * sstride + DO;
+    if (st[1] > 0.f) m = fmaxf(m, st[0]);
+  }
+  float ls = 0.f, lbf = 0.f, lh = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (m > -INFINITY) {
+    for (int s = 0; s < KS; ++s) {
+      const float* rec = rec0 + s * sstride;
+      const float* st = rec + DO;
+      if (!(st[1] > 0.f)) continue;  // an empty range holds no values
+      const float wgt = __builtin_amdgcn_exp2f(st[0] - m);
+      ls = fmaf(wgt, st[1], ls);
+      lbf = fmaf(wgt, st[2], lbf);
+      lh = fmaf(wgt, st[3], lh);
+      const float4 v = *reinterpret_cast<const float4*>(rec + 4 * c4);
+      acc[0] = fmaf(wgt, v.x, acc[0]); acc[1] = fmaf(wgt, v.y, acc[1]);
+      acc[2] = fmaf(wgt, v.z, acc[2]); acc[3] = fmaf(wgt, v.w, acc[3]);
+    }
+  }
+  const bool nonempty = ls > 0.f;
+  const int d1 = L.Dv + L.RCz;
+  const float ib = nonempty ? (1.0f / kVScale) / lbf : 0.f, ih = nonempty ? 1.0f / lh : 0.f;
+  float* orow = o + (size_t)row * DO;
+  float r4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r4[e] = acc[e] * (4 * c4 + e < d1 ? ib : ih);
+  if ((DO & 3) == 0) {
+    reinterpret_cast<float4*>(orow)[c4] = make_float4(r4[0], r4[1], r4[2], r4[3]);
+  } else {
+    for (int e = 0; e < 4 && 4 * c4 + e < DO; ++e) orow[4 * c4 + e] = r4[e];
+  }
+  if (c4 == 0) lse[((size_t)b * H + h) * N + i] = nonempty ? (m + log2f(ls)) * kLn2 : -INFINITY;
 }
 
 // 8 wavefronts (256 queries) per workgroup when that still gives every CU a
-// workgroup, else 4 (128 queries).
+// workgroup, or when the keys are split into ranges (then KS workgroups per
+// query tile and the combine kernel after); else 4 (128 queries).
 template <int NQS, int NVB, int GS>
 static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st) {
   FlashMfmaArgs a;
@@ -492,15 +567,21 @@ static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* 
   a.ws = reinterpret_cast<const char*>(ws);
   a.o = o;
   a.lse = lse;
+  a.ks = L.KS;
   const int q8 = (L.N + 255) / 256;
-  if ((long)q8 * L.H * L.B >= 256) {
+  if ((long)q8 * L.H * L.B >= 256 || L.KS > 1) {
     a.qtiles = q8;
-    a.nwg = a.qtiles * L.H * L.B;
+    a.nwg = a.qtiles * L.H * L.B * L.KS;
     hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 8>), dim3(a.nwg), dim3(512), 0, st, a);
   } else {
     a.qtiles = (L.N + 127) / 128;
     a.nwg = a.qtiles * L.H * L.B;
     hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4>), dim3(a.nwg), dim3(256), 0, st, a);
+  }
+  if (L.KS > 1) {
+    const long n = (long)L.B * L.N * L.H * ((L.DO + 3) / 4);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, L,
+                       reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + L.off_part), o, lse);
   }
   return hipGetLastError();
 }

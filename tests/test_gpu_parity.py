@@ -46,6 +46,11 @@ SMALL = [
           lengths=(50, 96)),
     _case("p3-q4-bf16", IPAShape(B=1, N=192, H=2, D=8, Dv=16, P=3, Q=4, Cz=40, R=2, Cout=64), 18, frames="gauss",
           trans_sigma=15.0, pair_dropout=0.05),
+    # grids too small for the GPU: keys split into 4 and 2 ranges per query
+    # tile, partial results merged by the combine kernel
+    _case("split4-bf16", IPAShape(B=1, N=1024, H=2), 19, frames="walk", step=3.8, masked_keys=(5, 300, 1023)),
+    _case("split2-ragged-bf16", IPAShape(B=2, N=600, H=3), 20, frames="walk", step=3.8, lengths=(300, 600),
+          pair_dropout=0.05, empty_row=True),
 ]
 
 
@@ -105,14 +110,15 @@ def test_parity_sweep_sampled(n):
     compare(inp, gpu, rows=_sample_rows(n, 6, 3, extra=(n // 2, n - 64, 63, 64)), tol=TOL["bf16"])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_attention_rows_sum_to_one(dtype):
+@pytest.mark.parametrize("dtype,N", [("bf16", 300), ("f32", 300), ("bf16", 1100)])
+def test_attention_rows_sum_to_one(dtype, N):
     """Attention rows a_ij = exp(L_ij - lse_i), from the logits the kernel uses and
-    the kernel's log-sum-exp: they match the oracle's attention and sum to 1."""
+    the kernel's log-sum-exp: they match the oracle's attention and sum to 1
+    (N = 1100: log-sum-exp merged from 4 key ranges)."""
     import torch
-    s = IPAShape(B=2, N=300, H=3, dtype=dtype)
-    inp = make_inputs(s, 31, frames="walk", step=3.8, lengths=(200, 300), pair_dropout=0.05, empty_row=True)
-    say(f"case attention rows {dtype}")
+    s = IPAShape(B=2, N=N, H=3, dtype=dtype)
+    inp = make_inputs(s, 31, frames="walk", step=3.8, lengths=(2 * N // 3, N), pair_dropout=0.05, empty_row=True)
+    say(f"case attention rows {dtype} N={N}")
     f, _, gpu = run_gpu(inp)
     rows = np.array([0, 7, 63, 64, 150, 199])
     ref = ipa_factored(inp, rows=rows, keep=("attention", "logits", "lse", "empty"))
