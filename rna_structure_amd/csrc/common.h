@@ -115,6 +115,11 @@ static inline bool pick_mfma_dims(int D, int Dv, int RCz, int P, int Q, MfmaDims
   return false;
 }
 
+// Epilogue per-head product: the features of one head (Dv=16, 4 x Q=8,
+// Cz=64) and their row pitch in LDS and in the packed w_out (elements).
+constexpr int kHeadFeat = 112;
+constexpr int kHeadFeatPitch = 120;
+
 // Limits of the fp32 kernels (registers sized at compile time).
 constexpr int kF32MaxDQ = 160;   // D + R*Cz
 constexpr int kF32MaxDV = 192;   // Dv + R*Cz + 3Q (4 threads x 48)
@@ -179,9 +184,13 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
   off = align256(off + H * 4);
   L->off_km = off;
   off = align256(off + B * NT * 2 * 4);
-  // output projection transposed to [Cout][FP] bf16 (matrix-core path)
+  // output projection transposed to [Cout][FP] bf16, or per head to
+  // [H][Cout][kHeadFeatPitch] bf16 (matrix-core path)
   L->off_wt = off;
-  if (L->mfma) off = align256(off + (size_t)L->Cout * L->FP * 2);
+  if (L->mfma) {
+    const size_t a1 = (size_t)L->Cout * L->FP, a2 = (size_t)L->H * L->Cout * kHeadFeatPitch;
+    off = align256(off + (a1 > a2 ? a1 : a2) * 2);
+  }
   // partial results of the key ranges: [KS][B][H][NQpad][PREC] fp32 (before
   // the pair-mask region, whose presence does not move it)
   L->PREC = round_up(L->DO + 4, 4);

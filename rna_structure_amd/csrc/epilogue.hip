@@ -114,7 +114,7 @@ __device__ __forceinline__ void feature_item(const EpiArgs& a, int row, int h, i
 // Q=8, R=2: the whole attention-output row (168 floats) is read with 42
 // independent 16-byte loads and the features go to LDS as 16-byte stores.
 constexpr int kFDv = 16, kFCz = 64, kFQ = 8, kFR = 2, kFDO = kFDv + kFR * kFCz + 3 * kFQ;
-__device__ __forceinline__ bool fast_dims(const Layout& L) {
+__host__ __device__ __forceinline__ bool fast_dims(const Layout& L) {
   return L.Dv == kFDv && L.Cz == kFCz && L.Q == kFQ && L.R == kFR;
 }
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -365,6 +365,221 @@ __global__ __launch_bounds__(RPW * 8) void epilogue_mfma_kernel(EpiArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- per-head matrix-core path
+// For the standard dimensions (Dv=16, Cz=64, Q=8, R=2) and Cout <= 128 the
+// product is summed over heads: update = sum_h features_h @ W_h + b_out with
+// W_h the 112 rows of w_out that multiply head h's features.  w_out is packed
+// once per call to wh[h][c][k] (k in the head's feature order [scalar 16 |
+// x 8 | y 8 | z 8 | length 8 | pair 64], pitch kHeadFeatPitch).  A workgroup
+// of 8 M threads takes M residues; per head, 8 lanes read one residue's
+// 672-byte block of O with 16-byte loads on consecutive addresses (whole
+// cache lines), build its 112 features in LDS, and the wavefronts multiply
+// them by W_h on MFMA.  O and W of head h+1 are loaded into registers while
+// head h is processed.
+constexpr int kHeadCoutMax = 128;
+__host__ __device__ __forceinline__ bool head_path(const Layout& L) {
+  return L.mfma && fast_dims(L) && L.Cout % 32 == 0 && L.Cout <= kHeadCoutMax;
+}
+
+// wh[h][c][k] = w_out[f(h, k)][c] (bf16 bits), zero in the pitch padding.
+__global__ __launch_bounds__(256) void pack_wout_heads_kernel(const uint16_t* w, uint16_t* wh, int H, int Cout) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)H * Cout * kHeadFeatPitch) return;
+  const int k = (int)(idx % kHeadFeatPitch);
+  const long hc = idx / kHeadFeatPitch;
+  const int c = (int)(hc % Cout), h = (int)(hc / Cout);
+  const int offx = H * kFDv, offy = offx + H * kFQ, offz = offy + H * kFQ, offl = offz + H * kFQ,
+            offp = offl + H * kFQ;
+  int f = -1;
+  if (k < 16) f = h * kFDv + k;
+  else if (k < 24) f = offx + h * kFQ + (k - 16);
+  else if (k < 32) f = offy + h * kFQ + (k - 24);
+  else if (k < 40) f = offz + h * kFQ + (k - 32);
+  else if (k < 48) f = offl + h * kFQ + (k - 40);
+  else if (k < kHeadFeat) f = offp + h * kFCz + (k - 48);
+  wh[idx] = f >= 0 ? w[(size_t)f * Cout + c] : (uint16_t)0;
+}
+
+template <int M>
+__global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
+  constexpr int NT_ = 8 * M;                 // threads
+  constexpr int KP = kHeadFeatPitch;
+  constexpr int WBYTES = kHeadCoutMax * KP * 2;
+  constexpr int WPT = (WBYTES / 16 + NT_ - 1) / NT_;  // 16-byte pieces of W_h per thread
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kHeadCoutMax * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sF[M * KP];
+  __shared__ __attribute__((aligned(16))) float sP[M][28];
+  __shared__ int s_empty[M];
+  const Layout& L = a.L;
+  const int H = L.H, Cout = L.Cout, total = L.B * L.N;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = tid >> 3, j = tid & 7;  // residue of the workgroup, lane within its 8
+  const int row0 = blockIdx.x * M, row = row0 + r;
+  int nonempty = 0;
+  if (tid < M) {
+    s_empty[tid] = row0 + tid < total ? (int)row_empty(a, row0 + tid) : 1;
+    nonempty = !s_empty[tid];
+  }
+  if (!__syncthreads_or(nonempty)) {
+    // every residue is padding or has an empty neighbourhood: zeros only
+    const int nr = min(M, total - row0);
+    const int HQ3 = H * kFQ * 3;
+    float4* up = reinterpret_cast<float4*>(a.update + (size_t)row0 * Cout);
+    for (int x = tid; x < nr * Cout / 4; x += NT_) up[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4* lp = reinterpret_cast<float4*>(a.local + (size_t)row0 * HQ3);
+    for (int x = tid; x < nr * HQ3 / 4; x += NT_) lp[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const bool empty = s_empty[r] != 0;  // also true past the end
+
+  // W_h pieces: 16-byte loads into registers, stored to LDS one head ahead
+  const uint4* whg = reinterpret_cast<const uint4*>(a.wt);
+  const int wpieces = Cout * KP / 8;  // per head
+  uint4 wreg[WPT];
+  auto load_w = [&](int h) {
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int x = tid + k * NT_;
+      wreg[k] = x < wpieces ? whg[(size_t)h * wpieces + x] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int x = tid + k * NT_;
+      if (x < wpieces) reinterpret_cast<uint4*>(sW[buf])[x] = wreg[k];
+    }
+  };
+
+  // per-residue constants, the same for every head: frame, and the zl values
+  // of this lane's two pair chunks (chunks qa, qb of 4 channels)
+  float Rm[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, tr[3] = {0.f, 0.f, 0.f};
+  const int qa = j >= 4 ? j - 4 : j + 12, qb = j + 4;
+  uint2 zla0 = make_uint2(0, 0), zla1 = make_uint2(0, 0), zlb0 = make_uint2(0, 0), zlb1 = make_uint2(0, 0);
+  if (!empty) {
+    const uint16_t* rt = reinterpret_cast<const uint16_t*>(a.rot) + (size_t)row * 9;
+    const uint16_t* tt = reinterpret_cast<const uint16_t*>(a.trans) + (size_t)row * 3;
+#pragma unroll
+    for (int e = 0; e < 9; ++e) Rm[e] = bf16_bits_to_f32(rt[e]);
+#pragma unroll
+    for (int e = 0; e < 3; ++e) tr[e] = bf16_bits_to_f32(tt[e]);
+    const uint2* z2 = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.zl) + (size_t)row * kFR * kFCz);
+    zla0 = z2[qa]; zla1 = z2[16 + qa];  // channel 4q of r = 0 and r = 1
+    zlb0 = z2[qb]; zlb1 = z2[16 + qb];
+  }
+  // this lane's float4 pieces j, j+8, ..., j+40 of a 42-piece O block
+  float4 cur[6], nxt[6];
+  auto load_o = [&](int h, float4* v) {
+    const float4* o4 = reinterpret_cast<const float4*>(a.o + ((size_t)row * H + h) * kFDO);
+#pragma unroll
+    for (int k = 0; k < 6; ++k)
+      v[k] = (!empty && j + 8 * k < kFDO / 4) ? o4[j + 8 * k] : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto zl4 = [](uint2 u, int e) {
+    const uint32_t wd = (e >> 1) ? u.y : u.x;
+    return __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+  };
+  auto f4 = [](const float4& v, int e) { return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w)); };
+
+  load_w(0);
+  load_o(0, cur);
+  store_w(0);
+  // output tile of this wavefront: rows rb*32.., columns cb*32..
+  constexpr int RB = M / 32;
+  const int ncb = Cout / 32;
+  const int ntiles = RB * ncb;
+  const int NW = NT_ / 64;
+  f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+  uint16_t* frow = sF + r * KP;
+  for (int h = 0; h < H; ++h) {
+    if (h + 1 < H) {
+      load_o(h + 1, nxt);
+      load_w(h + 1);
+    }
+    // ---- features of head h for residue r (8 lanes)
+    if (j < 4) {  // scalar: piece j
+      uint2 u;
+      u.x = pack_bf16(cur[0].x, cur[0].y);
+      u.y = pack_bf16(cur[0].z, cur[0].w);
+      *reinterpret_cast<uint2*>(frow + 4 * j) = u;
+    }
+    {
+      // pair chunk qa: pieces 4+qa (r=0) and 20+qa (r=1); chunk qb: 4+qb, 20+qb
+      const float4& a0 = j >= 4 ? cur[0] : cur[2];
+      const float4& a1 = j >= 4 ? cur[2] : cur[4];
+      const float4& b0 = cur[1];
+      const float4& b1 = cur[3];
+      float pa[4], pb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pa[e] = fmaf(zl4(zla1, e), f4(a1, e), zl4(zla0, e) * f4(a0, e));
+        pb[e] = fmaf(zl4(zlb1, e), f4(b1, e), zl4(zlb0, e) * f4(b0, e));
+      }
+      uint2 u;
+      u.x = pack_bf16(pa[0], pa[1]); u.y = pack_bf16(pa[2], pa[3]);
+      *reinterpret_cast<uint2*>(frow + 48 + 4 * qa) = u;
+      u.x = pack_bf16(pb[0], pb[1]); u.y = pack_bf16(pb[2], pb[3]);
+      *reinterpret_cast<uint2*>(frow + 48 + 4 * qb) = u;
+    }
+    // points: pieces 36..41 through LDS, then lane j takes point j
+    if (j >= 4) *reinterpret_cast<float4*>(&sP[r][4 * (j - 4)]) = cur[4];
+    if (j < 2) *reinterpret_cast<float4*>(&sP[r][16 + 4 * j]) = cur[5];
+    __builtin_amdgcn_wave_barrier();
+    {
+      const float gx = sP[r][3 * j] - tr[0], gy = sP[r][3 * j + 1] - tr[1], gz = sP[r][3 * j + 2] - tr[2];
+      // R^T (g - t): column x of R dotted with (g - t)
+      float x = Rm[0] * gx + Rm[3] * gy + Rm[6] * gz;
+      float y = Rm[1] * gx + Rm[4] * gy + Rm[7] * gz;
+      float z = Rm[2] * gx + Rm[5] * gy + Rm[8] * gz;
+      float len = sqrtf(x * x + y * y + z * z + a.eps);
+      if (empty) { x = y = z = len = 0.f; }
+      frow[16 + j] = f32_to_bf16_bits(x);
+      frow[24 + j] = f32_to_bf16_bits(y);
+      frow[32 + j] = f32_to_bf16_bits(z);
+      frow[40 + j] = f32_to_bf16_bits(len);
+      if (row < total) {
+        float* lp = a.local + (((size_t)row * H + h) * kFQ + j) * 3;
+        lp[0] = x; lp[1] = y; lp[2] = z;
+      }
+    }
+    __syncthreads();  // features of head h and W_h in LDS; W buffer (h+1)&1 free
+    // ---- update += features_h @ W_h
+    const uint16_t* wb = sW[h & 1];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ti = w + k * NW;
+      if (ti < ntiles) {
+        const int rb = ti % RB, cb = ti / RB;
+#pragma unroll
+        for (int ks = 0; ks < kHeadFeat / 16; ++ks) {
+          const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(sF + (rb * 32 + l32) * KP + ks * 16 + half * 8);
+          const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(wb + (cb * 32 + l32) * KP + ks * 16 + half * 8);
+          acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw, acc[k], 0, 0, 0);
+        }
+      }
+    }
+    if (h + 1 < H) store_w((h + 1) & 1);
+    __syncthreads();  // everyone done with the features of head h; W_(h+1) in LDS
+#pragma unroll
+    for (int k = 0; k < 6; ++k) cur[k] = nxt[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int ti = w + k * NW;
+    if (ti >= ntiles) continue;
+    const int rb = ti % RB, cb = ti / RB;
+    const int col = cb * 32 + l32;
+    const float bo = ld<true>(a.b_out, col);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int rr = rb * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+      const int orow = row0 + rr;
+      if (orow < total) a.update[(size_t)orow * Cout + col] = s_empty[rr] ? 0.f : acc[k][q] + bo;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 constexpr int kEpiRowsF32 = 16;
 
@@ -426,6 +641,7 @@ static inline bool epi_fits(const Layout& L, int rpw) {
 }
 
 bool epilogue_supported(const Layout& L) {
+  if (head_path(L)) return true;
   if (L.mfma) return epi_fits(L, 32) || epi_fits(L, 64);
   return (size_t)kEpiRowsF32 * (L.F + 1) * 4 <= 160 * 1024;
 }
@@ -439,7 +655,15 @@ hipError_t launch_epilogue(const Layout& L, void* ws, const float* o, const floa
   a.update = update; a.local = local; a.eps = eps;
   a.wt = nullptr;
   const int total = L.B * L.N;
-  if (L.mfma) {
+  if (head_path(L)) {
+    uint16_t* wh = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.off_wt);
+    const long n = (long)L.H * L.Cout * kHeadFeatPitch;
+    hipLaunchKernelGGL(pack_wout_heads_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(in->w_out), wh, L.H, L.Cout);
+    a.wt = wh;
+    a.FP = kHeadFeatPitch;
+    hipLaunchKernelGGL(epilogue_head_kernel<32>, dim3((total + 31) / 32), dim3(256), 0, st, a);
+  } else if (L.mfma) {
     uint16_t* wt = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.off_wt);
     hipLaunchKernelGGL(transpose_wout_kernel, dim3((L.FP + 63) / 64, (L.Cout + 63) / 64), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(in->w_out), wt, L.F, L.FP, L.Cout);

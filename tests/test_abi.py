@@ -115,7 +115,10 @@ def test_validation_before_launch(lib):
     ei2 = _lib.IpaEpiIn(4096, 4096, 4096, 4096, 4096)
     assert lib.ipa_epilogue(ctypes.byref(s), None, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 1
     assert lib.ipa_epilogue(ctypes.byref(s), 4096, 4096, 4100, ctypes.byref(ei2), 4096, 4096, None) == 4
-    big = _shape(H=40, Cz=64)  # F = 40*(16+32+64) = 4480: beyond the epilogue's LDS staging
+    # F = 40*(16+32+56) = 4160 with non-standard dimensions: beyond the LDS
+    # staging of the general epilogue (the per-head path takes any H, but only
+    # Dv=16, Q=8, Cz=64, R=2)
+    big = _shape(H=40, Cz=56)
     assert lib.ipa_epilogue(ctypes.byref(big), 4096, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 3
     assert lib.ipa_logit_rows(ctypes.byref(s), 4096, 5, 0, 0, 1, 4096, None) == 2   # b out of range
     assert lib.ipa_logit_rows(ctypes.byref(s), 4096, 0, 0, 299, 2, 4096, None) == 2  # rows past N
