@@ -11,6 +11,7 @@
 // the workspace so that every MFMA operand fragment is one 16-byte load.
 // fp32 path: the same features in fp32 and a VALU product.
 #include "common.h"
+#include "lds_copy.h"
 
 namespace fipa {
 
@@ -374,8 +375,7 @@ __global__ __launch_bounds__(RPW * 8) void epilogue_mfma_kernel(EpiArgs a) {
 // of 8 M threads takes M residues; per head, 8 lanes read one residue's
 // 672-byte block of O with 16-byte loads on consecutive addresses (whole
 // cache lines), build its 112 features in LDS, and the wavefronts multiply
-// them by W_h on MFMA.  O and W of head h+1 are loaded into registers while
-// head h is processed.
+// them by W_h on MFMA.  O is loaded two heads ahead, W_h one head ahead.
 constexpr int kHeadCoutMax = 128;
 __host__ __device__ __forceinline__ bool head_path(const Layout& L) {
   return L.mfma && fast_dims(L) && L.Cout % 32 == 0 && L.Cout <= kHeadCoutMax;
@@ -400,18 +400,25 @@ __global__ __launch_bounds__(256) void pack_wout_heads_kernel(const uint16_t* w,
   wh[idx] = f >= 0 ? w[(size_t)f * Cout + c] : (uint16_t)0;
 }
 
-template <int M>
+// HT > 0: H = HT at compile time (the head loop is unrolled completely, and
+// the compiler's waits for the O loads then follow the two-head prefetch).
+template <int M, int COUT, int HT>
 __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
-  constexpr int NT_ = 8 * M;                 // threads
+  constexpr int NT_ = 8 * M;  // threads
+  constexpr int NW = NT_ / 64;
   constexpr int KP = kHeadFeatPitch;
-  constexpr int WBYTES = kHeadCoutMax * KP * 2;
-  constexpr int WPT = (WBYTES / 16 + NT_ - 1) / NT_;  // 16-byte pieces of W_h per thread
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kHeadCoutMax * KP];
+  constexpr int WBYTES = COUT * KP * 2;                  // W_h
+  constexpr int WLDS = (WBYTES + 1023) / 1024 * 1024;    // room for a partial last copy chunk
+  constexpr int WDMA = dma_per_wave<WBYTES, NW>();       // copy instructions per wavefront
+  constexpr int RB = M / 32;
+  constexpr int NTILE = RB * (COUT / 32);                // 32x32 output tiles
+  static_assert(NTILE <= 2 * NW, "two output tiles per wavefront at most");
+  __shared__ __attribute__((aligned(1024))) char sW[2 * WLDS];
   __shared__ __attribute__((aligned(16))) uint16_t sF[M * KP];
   __shared__ __attribute__((aligned(16))) float sP[M][28];
   __shared__ int s_empty[M];
   const Layout& L = a.L;
-  const int H = L.H, Cout = L.Cout, total = L.B * L.N;
+  const int H = HT > 0 ? HT : L.H, total = L.B * L.N;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = tid >> 3, j = tid & 7;  // residue of the workgroup, lane within its 8
@@ -425,32 +432,13 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
     // every residue is padding or has an empty neighbourhood: zeros only
     const int nr = min(M, total - row0);
     const int HQ3 = H * kFQ * 3;
-    float4* up = reinterpret_cast<float4*>(a.update + (size_t)row0 * Cout);
-    for (int x = tid; x < nr * Cout / 4; x += NT_) up[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4* up = reinterpret_cast<float4*>(a.update + (size_t)row0 * COUT);
+    for (int x = tid; x < nr * COUT / 4; x += NT_) up[x] = make_float4(0.f, 0.f, 0.f, 0.f);
     float4* lp = reinterpret_cast<float4*>(a.local + (size_t)row0 * HQ3);
     for (int x = tid; x < nr * HQ3 / 4; x += NT_) lp[x] = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
   const bool empty = s_empty[r] != 0;  // also true past the end
-
-  // W_h pieces: 16-byte loads into registers, stored to LDS one head ahead
-  const uint4* whg = reinterpret_cast<const uint4*>(a.wt);
-  const int wpieces = Cout * KP / 8;  // per head
-  uint4 wreg[WPT];
-  auto load_w = [&](int h) {
-#pragma unroll
-    for (int k = 0; k < WPT; ++k) {
-      const int x = tid + k * NT_;
-      wreg[k] = x < wpieces ? whg[(size_t)h * wpieces + x] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_w = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < WPT; ++k) {
-      const int x = tid + k * NT_;
-      if (x < wpieces) reinterpret_cast<uint4*>(sW[buf])[x] = wreg[k];
-    }
-  };
 
   // per-residue constants, the same for every head: frame, and the zl values
   // of this lane's two pair chunks (chunks qa, qb of 4 channels)
@@ -468,13 +456,17 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
     zla0 = z2[qa]; zla1 = z2[16 + qa];  // channel 4q of r = 0 and r = 1
     zlb0 = z2[qb]; zlb1 = z2[16 + qb];
   }
-  // this lane's float4 pieces j, j+8, ..., j+40 of a 42-piece O block
-  float4 cur[6], nxt[6];
+  // W_h straight into LDS buffer h&1 (direct copies, waited for explicitly);
+  // O of a head: this lane's 16-byte pieces j, j+8, ..., j+40 of the
+  // residue's 42-piece block, unconditional loads (clamped indices) so that
+  // the compiler's own waits count them exactly
+  const char* whg = reinterpret_cast<const char*>(a.wt);
+  auto copy_w = [&](int h) { dma_tile<WBYTES, NW>(whg + (size_t)h * WBYTES, sW + (h & 1) * WLDS, w, lane); };
+  const int rowc = min(row, total - 1);
   auto load_o = [&](int h, float4* v) {
-    const float4* o4 = reinterpret_cast<const float4*>(a.o + ((size_t)row * H + h) * kFDO);
+    const float4* o4 = reinterpret_cast<const float4*>(a.o + ((size_t)rowc * H + h) * kFDO);
 #pragma unroll
-    for (int k = 0; k < 6; ++k)
-      v[k] = (!empty && j + 8 * k < kFDO / 4) ? o4[j + 8 * k] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < 6; ++k) v[k] = o4[min(j + 8 * k, kFDO / 4 - 1)];
   };
   auto zl4 = [](uint2 u, int e) {
     const uint32_t wd = (e >> 1) ? u.y : u.x;
@@ -482,22 +474,19 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
   };
   auto f4 = [](const float4& v, int e) { return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w)); };
 
-  load_w(0);
-  load_o(0, cur);
-  store_w(0);
-  // output tile of this wavefront: rows rb*32.., columns cb*32..
-  constexpr int RB = M / 32;
-  const int ncb = Cout / 32;
-  const int ntiles = RB * ncb;
-  const int NW = NT_ / 64;
   f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
   uint16_t* frow = sF + r * KP;
-  for (int h = 0; h < H; ++h) {
-    if (h + 1 < H) {
-      load_o(h + 1, nxt);
-      load_w(h + 1);
+  // head h: O in cur (loaded two heads ahead), W_h in LDS buffer h&1 (copy
+  // issued one head ahead); issues the copy of W_(h+1), then O of head h+2
+  // into nb
+  auto step = [&](int h, float4(&cur)[6], float4(&nb)[6]) {
+    if (h + 1 < H) copy_w(h + 1);
+    if (h + 2 < H) load_o(h + 2, nb);
+    // ---- features of head h for residue r (8 lanes); an empty row's O is zero
+    if (empty) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k) cur[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    // ---- features of head h for residue r (8 lanes)
     if (j < 4) {  // scalar: piece j
       uint2 u;
       u.x = pack_bf16(cur[0].x, cur[0].y);
@@ -543,13 +532,18 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
         lp[0] = x; lp[1] = y; lp[2] = z;
       }
     }
-    __syncthreads();  // features of head h and W_h in LDS; W buffer (h+1)&1 free
+    // W_h has landed: at most the copies and loads issued after it (O of
+    // h+1, the copy of W_(h+1), O of h+2) may still be in flight
+    if (h + 2 < H) wait_vmcnt<12 + WDMA>();
+    else if (h + 1 < H) wait_vmcnt<6 + WDMA>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // features of head h and W_h visible
     // ---- update += features_h @ W_h
-    const uint16_t* wb = sW[h & 1];
+    const uint16_t* wb = reinterpret_cast<const uint16_t*>(sW + (h & 1) * WLDS);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int ti = w + k * NW;
-      if (ti < ntiles) {
+      if (ti < NTILE) {
         const int rb = ti % RB, cb = ti / RB;
 #pragma unroll
         for (int ks = 0; ks < kHeadFeat / 16; ++ks) {
@@ -559,15 +553,24 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
         }
       }
     }
-    if (h + 1 < H) store_w((h + 1) & 1);
-    __syncthreads();  // everyone done with the features of head h; W_(h+1) in LDS
+    __syncthreads();  // everyone done with the features of head h and W buffer h&1
+  };
+  float4 oa[6], ob[6], oc[6];
+  copy_w(0);
+  load_o(0, oa);
+  if (H > 1) load_o(1, ob);
 #pragma unroll
-    for (int k = 0; k < 6; ++k) cur[k] = nxt[k];
+  for (int h = 0; h < H; h += 3) {
+    step(h, oa, oc);
+    if (h + 1 >= H) break;
+    step(h + 1, ob, oa);
+    if (h + 2 >= H) break;
+    step(h + 2, oc, ob);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int ti = w + k * NW;
-    if (ti >= ntiles) continue;
+    if (ti >= NTILE) continue;
     const int rb = ti % RB, cb = ti / RB;
     const int col = cb * 32 + l32;
     const float bo = ld<true>(a.b_out, col);
@@ -575,7 +578,7 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
     for (int q = 0; q < 16; ++q) {
       const int rr = rb * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
       const int orow = row0 + rr;
-      if (orow < total) a.update[(size_t)orow * Cout + col] = s_empty[rr] ? 0.f : acc[k][q] + bo;
+      if (orow < total) a.update[(size_t)orow * COUT + col] = s_empty[rr] ? 0.f : acc[k][q] + bo;
     }
   }
 }
@@ -662,7 +665,19 @@ hipError_t launch_epilogue(const Layout& L, void* ws, const float* o, const floa
                        reinterpret_cast<const uint16_t*>(in->w_out), wh, L.H, L.Cout);
     a.wt = wh;
     a.FP = kHeadFeatPitch;
-    hipLaunchKernelGGL(epilogue_head_kernel<32>, dim3((total + 31) / 32), dim3(256), 0, st, a);
+    const dim3 g((total + 31) / 32), blk(256);
+    if (L.Cout == 128 && L.H == 8) {
+      hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 8>), g, blk, 0, st, a);
+    } else if (L.Cout == 128 && L.H == 12) {
+      hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 12>), g, blk, 0, st, a);
+    } else {
+      switch (L.Cout) {
+        case 32: hipLaunchKernelGGL((epilogue_head_kernel<32, 32, 0>), g, blk, 0, st, a); break;
+        case 64: hipLaunchKernelGGL((epilogue_head_kernel<32, 64, 0>), g, blk, 0, st, a); break;
+        case 96: hipLaunchKernelGGL((epilogue_head_kernel<32, 96, 0>), g, blk, 0, st, a); break;
+        default: hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 0>), g, blk, 0, st, a); break;
+      }
+    }
   } else if (L.mfma) {
     uint16_t* wt = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.off_wt);
     hipLaunchKernelGGL(transpose_wout_kernel, dim3((L.FP + 63) / 64, (L.Cout + 63) / 64), dim3(256), 0, st,
