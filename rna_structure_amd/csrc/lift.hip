@@ -365,6 +365,8 @@ constexpr int kFastVPitch = 66;      // 16-bit elements per transposed LDS row (
 constexpr int kFastZ = 5;            // 16-byte pieces of a zr / zl tile per thread: 64 R Cz/8 <= 1280
 constexpr int kFastK = 2;            // pieces of a k / v / q tile per thread: 64 D/8 <= 512
 constexpr int kFastPts = 5;          // points per thread: 64 (2P + Q) <= 1280
+constexpr int kFastPc = 4;           // 8-byte point pieces per thread: 64 (6 + 3Q/4) <= 1024
+constexpr int kPrPitch = 13;         // 8-byte pieces per staged point row (odd: rows spread over banks)
 
 // x / d for 0 <= x < 2^16 and 0 < d < 2^16: m = ceil(2^32 / d), which fits
 // in 32 bits for d >= 2; d = 1 is passed through
@@ -388,7 +390,8 @@ __device__ __forceinline__ uint4 pack8(const uint16_t* v) {
 
 struct LiftFastArgs {
   int units, per_xcd, pm_vec;
-  FastDiv nz, nk, nv;
+  int pts_vec;  // P = 4 and Q % 4 == 0: points loaded as 8-byte pieces of whole rows
+  FastDiv nz, nk, nv, npc;
 };
 
 // Two floats to packed bf16 (round to nearest even, the hardware conversion).
@@ -482,7 +485,21 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     const int rv = fdiv(x, f.nv), cv = x - rv * nv;
     v_r[k] = (x < 64 * nv && rv < nrow) ? vb4[rv * H * nv + cv] : make_uint4(0, 0, 0, 0);
   }
+  // points: with pts_vec, 8-byte pieces of each row's [kp | qp | vp] (3 + 3 +
+  // 3Q/4 pieces, consecutive lanes on consecutive pieces), staged in LDS
+  // below; else one point (3 x bf16) per thread and item
+  const int npc = 6 + 3 * Q / 4;
+  uint2 ppc[kFastPc];
   float pts[kFastPts][3];
+  if (P == 4 && f.pts_vec) {
+#pragma unroll
+    for (int k = 0; k < kFastPc; ++k) {
+      const int x = tid + 256 * k, r = fdiv(x, f.npc), c = x - r * npc;
+      const uint16_t* src = c < 3 ? kpb + r * H * 12 + 4 * c
+                                  : (c < 6 ? qpb + r * H * 12 + 4 * (c - 3) : vpb + r * H * 3 * Q + 4 * (c - 6));
+      ppc[k] = (x < 64 * npc && r < nrow) ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+    }
+  } else {
 #pragma unroll
   for (int k = 0; k < kFastPts; ++k) {
     const int x = tid + 256 * k, r = x % 64, it = x / 64;
@@ -496,6 +513,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       pts[k][1] = bf16_bits_to_f32(src[1]);
       pts[k][2] = bf16_bits_to_f32(src[2]);
     }
+  }
   }
 
   // ---- 2. frames, validity and the tile centroid (wavefront 0)
@@ -526,6 +544,16 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       cx = f16_bits_to_f32(hi16(cx)); cy = f16_bits_to_f32(hi16(cy)); cz = f16_bits_to_f32(hi16(cz));
       s_c[0] = cx; s_c[1] = cy; s_c[2] = cz; s_c[3] = 0.f;
       s_gam = 0.5f * softplus_f(pwr) * sqrtf(2.0f / (27.0f * (float)P));
+    }
+  }
+  // raw point rows in LDS (the value-tile staging array is free until the
+  // points are done): row r at s_praw + kPrPitch r, as bf16 [kp | qp | vp]
+  uint2* s_praw = reinterpret_cast<uint2*>(&s_vzT[0][0]);
+  if (P == 4 && f.pts_vec) {
+#pragma unroll
+    for (int k = 0; k < kFastPc; ++k) {
+      const int x = tid + 256 * k, r = fdiv(x, f.npc), c = x - r * npc;
+      if (x < 64 * npc) s_praw[r * kPrPitch + c] = ppc[k];
     }
   }
   __syncthreads();
@@ -559,7 +587,46 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   // key tiles without a valid key and writes padding queries as zeros
   const bool tile_any = (s_vmask[0] | s_vmask[1]) != 0u;
   if (tile_any) {
-    // ---- 3. [k | zr] straight into the key tile, [v | zr] transposed into LDS
+    // ---- 3. points, then [k | zr] straight into the key tile and [v | zr]
+    // transposed into LDS
+    // global points: key points (centred), query points, value points (centred,
+    // zero for keys that are masked or past the end)
+#pragma unroll
+    for (int k = 0; k < kFastPts; ++k) {
+      const int x = tid + 256 * k, r = x % 64, it = x / 64;
+      if (x < 64 * npt) {
+        const bool in = t * 64 + r < N;
+        const float* Rm = s_rot[r];
+        const float tx = s_tr[r][0], ty = s_tr[r][1], tz = s_tr[r][2];
+        float lx, ly, lz;
+        if (P == 4 && f.pts_vec) {
+          // point it of the row is at bf16 3 it of [kp | qp | vp] (3P = 12)
+          const uint16_t* pr = reinterpret_cast<const uint16_t*>(s_praw + r * kPrPitch) + 3 * it;
+          lx = bf16_bits_to_f32(pr[0]); ly = bf16_bits_to_f32(pr[1]); lz = bf16_bits_to_f32(pr[2]);
+          if (r >= nrow) lx = ly = lz = 0.f;
+        } else {
+          lx = pts[k][0]; ly = pts[k][1]; lz = pts[k][2];
+        }
+        const float gx = Rm[0] * lx + Rm[1] * ly + Rm[2] * lz + tx;
+        const float gy = Rm[3] * lx + Rm[4] * ly + Rm[5] * lz + ty;
+        const float gz = Rm[6] * lx + Rm[7] * ly + Rm[8] * lz + tz;
+        if (it < P) {
+          s_w[r][3 * it] = in ? gx - cx : 0.f;
+          s_w[r][3 * it + 1] = in ? gy - cy : 0.f;
+          s_w[r][3 * it + 2] = in ? gz - cz : 0.f;
+        } else if (it < 2 * P) {
+          const int p = it - P;
+          s_a[r][3 * p] = gx; s_a[r][3 * p + 1] = gy; s_a[r][3 * p + 2] = gz;
+        } else {
+          const int q = it - 2 * P;
+          const bool v = in && s_valid[r];
+          s_xT[3 * q][r] = v ? gx - cx : 0.f;
+          s_xT[3 * q + 1][r] = v ? gy - cy : 0.f;
+          s_xT[3 * q + 2][r] = v ? gz - cz : 0.f;
+        }
+      }
+    }
+    __syncthreads();  // the raw point rows are read; the staging array is free
     uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * L.KROW;
     auto vh = [](uint16_t bits) { return f32_to_f16_bits(bf16_bits_to_f32(bits) * kVScale); };
 #pragma unroll
@@ -586,35 +653,6 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
         const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][rv] = vh(e16[e]);
-      }
-    }
-    // global points: key points (centred), query points, value points (centred,
-    // zero for keys that are masked or past the end)
-#pragma unroll
-    for (int k = 0; k < kFastPts; ++k) {
-      const int x = tid + 256 * k, r = x % 64, it = x / 64;
-      if (x < 64 * npt) {
-        const bool in = t * 64 + r < N;
-        const float* Rm = s_rot[r];
-        const float tx = s_tr[r][0], ty = s_tr[r][1], tz = s_tr[r][2];
-        const float lx = pts[k][0], ly = pts[k][1], lz = pts[k][2];
-        const float gx = Rm[0] * lx + Rm[1] * ly + Rm[2] * lz + tx;
-        const float gy = Rm[3] * lx + Rm[4] * ly + Rm[5] * lz + ty;
-        const float gz = Rm[6] * lx + Rm[7] * ly + Rm[8] * lz + tz;
-        if (it < P) {
-          s_w[r][3 * it] = in ? gx - cx : 0.f;
-          s_w[r][3 * it + 1] = in ? gy - cy : 0.f;
-          s_w[r][3 * it + 2] = in ? gz - cz : 0.f;
-        } else if (it < 2 * P) {
-          const int p = it - P;
-          s_a[r][3 * p] = gx; s_a[r][3 * p + 1] = gy; s_a[r][3 * p + 2] = gz;
-        } else {
-          const int q = it - 2 * P;
-          const bool v = in && s_valid[r];
-          s_xT[3 * q][r] = v ? gx - cx : 0.f;
-          s_xT[3 * q + 1][r] = v ? gy - cy : 0.f;
-          s_xT[3 * q + 2][r] = v ? gz - cz : 0.f;
-        }
       }
     }
     // lifted query rows [q sq | w_pair zl sp | 0]
@@ -820,6 +858,8 @@ hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStre
     f.nz = make_fastdiv(L.RCz / 8);
     f.nk = make_fastdiv(L.D / 8);
     f.nv = make_fastdiv(L.Dv / 8);
+    f.pts_vec = L.P == 4 && L.Q % 4 == 0 && 6 + 3 * L.Q / 4 <= kPrPitch;
+    f.npc = make_fastdiv(6 + 3 * L.Q / 4);
     const dim3 g(8 * f.per_xcd), blk(256);
     switch (L.P) {
       case 1: hipLaunchKernelGGL(lift_fast_kernel<1>, g, blk, 0, st, a, f); break;
