@@ -49,7 +49,7 @@ def eff_flops(shape, mask) -> float:
 def _mfma_dims(shape):
     """(NQS, NVB, GS) of the compiled matrix-core instance used for a shape."""
     rcz = shape.R * shape.Cz
-    for nqs, nvb in ((3, 2), (5, 3), (9, 5)):
+    for nqs, nvb in ((3, 2), (5, 3), (9, 5), (13, 7)):
         if shape.D + rcz <= 16 * nqs and shape.Dv + rcz + 1 <= 32 * nvb:
             return nqs, nvb, (3 if shape.P <= 4 else 4)
     raise ValueError("no matrix-core instance for this shape")
@@ -290,6 +290,22 @@ def main():
                 y = np.log([max(p[key], 1e-9) for p in pts])
                 out[name] = round(float(np.polyfit(x, y, 1)[0]), 3)
         out["sweep"] = sweep
+        # rank sweep of the pair factors (R = 1, 2, 3) at N = 8192: R = 3 runs
+        # on the widest matrix-core instance
+        from rna_structure_amd.synth import IPAShape, make_inputs
+        ranks = []
+        for R in (1, 2, 3):
+            sh = IPAShape(B=1, N=8192, H=8, R=R)
+            w = make_inputs(sh, 6000 + R, frames="walk", step=3.8)
+            fl = eff_flops(sh, w["mask"])
+            rr = time_forward(w, max(3, args.steps // 4), 2)
+            ranks.append({"R": R, "N": sh.N, "H": sh.H, "ms": round(rr["ms"], 4),
+                          "eff_tflops": round(fl / (rr["ms"] * 1e-3) / 1e12, 2),
+                          "flash_ms": round(rr["flash_ms"], 4),
+                          "flash_frac_mfma": round(fl / (rr["flash_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "lift_ms": round(rr["lift_ms"], 4), "epilogue_ms": round(rr["epilogue_ms"], 4)})
+            print(f"# rank sweep {ranks[-1]}", file=sys.stderr, flush=True)
+        out["rank_sweep"] = ranks
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, flops)

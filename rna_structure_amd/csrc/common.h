@@ -102,7 +102,7 @@ static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 // Choose the smallest compiled matrix-core instance that holds the shape.
 // Returns false when none does.
 static inline bool pick_mfma_dims(int D, int Dv, int RCz, int P, int Q, MfmaDims* out) {
-  static const MfmaDims inst[] = {{3, 2, 0}, {5, 3, 0}, {9, 5, 0}};
+  static const MfmaDims inst[] = {{3, 2, 0}, {5, 3, 0}, {9, 5, 0}, {13, 7, 0}};
   if (P > 5) return false;
   if (3 * Q + 4 > 32) return false;
   for (const MfmaDims& m : inst) {

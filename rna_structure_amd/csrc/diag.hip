@@ -113,9 +113,11 @@ hipError_t launch_logit_rows(const Layout& L, const void* ws, int b, int h, int 
     if (L.GS == 3 && L.NQS == 3) launch_m<3, 3>(a, st);
     else if (L.GS == 3 && L.NQS == 5) launch_m<5, 3>(a, st);
     else if (L.GS == 3 && L.NQS == 9) launch_m<9, 3>(a, st);
+    else if (L.GS == 3 && L.NQS == 13) launch_m<13, 3>(a, st);
     else if (L.GS == 4 && L.NQS == 3) launch_m<3, 4>(a, st);
     else if (L.GS == 4 && L.NQS == 5) launch_m<5, 4>(a, st);
     else if (L.GS == 4 && L.NQS == 9) launch_m<9, 4>(a, st);
+    else if (L.GS == 4 && L.NQS == 13) launch_m<13, 4>(a, st);
     else return hipErrorInvalidValue;
   } else {
     dim3 grid((L.N + 255) / 256, nrows);

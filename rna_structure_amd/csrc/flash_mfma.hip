@@ -530,14 +530,22 @@ static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* 
   a.lse = lse;
   a.ks = L.KS;
   const int q8 = (L.N + 255) / 256;
-  if ((long)q8 * L.H * L.B >= 256 || L.KS > 1) {
-    a.qtiles = q8;
-    a.nwg = a.qtiles * L.H * L.B * L.KS;
-    hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 8>), dim3(a.nwg), dim3(512), 0, st, a);
-  } else {
+  if constexpr (NQS > 9) {
+    // the widest rows (rank-3 pair factors): four wavefronts, one per SIMD,
+    // with the whole register file each
     a.qtiles = (L.N + 127) / 128;
-    a.nwg = a.qtiles * L.H * L.B;
+    a.nwg = a.qtiles * L.H * L.B * L.KS;
     hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4>), dim3(a.nwg), dim3(256), 0, st, a);
+  } else {
+    if ((long)q8 * L.H * L.B >= 256 || L.KS > 1) {
+      a.qtiles = q8;
+      a.nwg = a.qtiles * L.H * L.B * L.KS;
+      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 8>), dim3(a.nwg), dim3(512), 0, st, a);
+    } else {
+      a.qtiles = (L.N + 127) / 128;
+      a.nwg = a.qtiles * L.H * L.B;
+      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4>), dim3(a.nwg), dim3(256), 0, st, a);
+    }
   }
   if (L.KS > 1) {
     const long n = (long)L.B * L.N * L.H * ((L.DO + 3) / 4);
@@ -552,10 +560,12 @@ hipError_t launch_flash_mfma(const Layout& L, const void* ws, float* o, float* l
     if (L.NQS == 3 && L.NVB == 2) return launch_inst<3, 2, 3>(L, ws, o, lse, st);
     if (L.NQS == 5 && L.NVB == 3) return launch_inst<5, 3, 3>(L, ws, o, lse, st);
     if (L.NQS == 9 && L.NVB == 5) return launch_inst<9, 5, 3>(L, ws, o, lse, st);
+    if (L.NQS == 13 && L.NVB == 7) return launch_inst<13, 7, 3>(L, ws, o, lse, st);
   } else if (L.GS == 4) {
     if (L.NQS == 3 && L.NVB == 2) return launch_inst<3, 2, 4>(L, ws, o, lse, st);
     if (L.NQS == 5 && L.NVB == 3) return launch_inst<5, 3, 4>(L, ws, o, lse, st);
     if (L.NQS == 9 && L.NVB == 5) return launch_inst<9, 5, 4>(L, ws, o, lse, st);
+    if (L.NQS == 13 && L.NVB == 7) return launch_inst<13, 7, 4>(L, ws, o, lse, st);
   }
   return hipErrorInvalidValue;
 }

@@ -51,6 +51,11 @@ SMALL = [
     _case("split4-bf16", IPAShape(B=1, N=1024, H=2), 19, frames="walk", step=3.8, masked_keys=(5, 300, 1023)),
     _case("split2-ragged-bf16", IPAShape(B=2, N=600, H=3), 20, frames="walk", step=3.8, lengths=(300, 600),
           pair_dropout=0.05, empty_row=True),
+    # rank-3 pair factors: the widest matrix-core instance (13 query K-steps,
+    # 7 value blocks), once whole and once split into key ranges
+    _case("rank3-bf16", IPAShape(B=2, N=300, H=3, R=3), 22, frames="walk", step=3.8, lengths=(200, 300),
+          pair_dropout=0.05, empty_row=True),
+    _case("rank3-split-bf16", IPAShape(B=1, N=1100, H=2, R=3), 23, frames="walk", step=3.8),
 ]
 
 
