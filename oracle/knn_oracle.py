@@ -49,21 +49,22 @@ def sqdist_f32(ti: np.ndarray, tj: np.ndarray) -> np.ndarray:
     ti [..., 3] and tj [..., 3] broadcast against each other."""
     ti = np.asarray(ti, dtype=np.float32)
     tj = np.asarray(tj, dtype=np.float32)
-    dx = tj[..., 0] - ti[..., 0]
-    dy = tj[..., 1] - ti[..., 1]
-    dz = tj[..., 2] - ti[..., 2]
-    return (dx * dx + dy * dy) + dz * dz
+    with np.errstate(over="ignore"):      # an overflow to +inf is a value like any other
+        dx = tj[..., 0] - ti[..., 0]
+        dy = tj[..., 1] - ti[..., 1]
+        dz = tj[..., 2] - ti[..., 2]
+        return (dx * dx + dy * dy) + dz * dz
 
 
 def distance_bins(dist: np.ndarray, nbins: int, dmax: float) -> np.ndarray:
-    """Bin of each fp32 distance: floor(fl32(d / w)) clamped to nbins-1; -1 for +inf slots."""
+    """Bin of each fp32 distance: floor(fl32(d / w)), clamped to nbins-1 (an
+    overflowed d = +inf of a real neighbour included)."""
     d = np.asarray(dist, dtype=np.float32)
     w = bin_width(dmax, nbins)
     with np.errstate(over="ignore", invalid="ignore"):
         q = d / w
     out = np.where(q >= np.float32(nbins), nbins - 1, np.floor(np.where(np.isfinite(q), q, 0.0)))
-    out = out.astype(np.int32)
-    return np.where(np.isinf(d), -1, out).astype(np.int32)
+    return out.astype(np.int32)
 
 
 def one_hot(bins: np.ndarray, nbins: int) -> np.ndarray:
@@ -101,7 +102,7 @@ def knn_distogram(translation: np.ndarray, mask: Optional[np.ndarray] = None, k:
                 n = len(order)
                 index[b, r0 + a, :n] = order
                 dist[b, r0 + a, :n] = np.sqrt(d2[a, order])
-    bins = distance_bins(dist, nbins, dmax)
+    bins = np.where(index >= 0, distance_bins(dist, nbins, dmax), -1).astype(np.int32)
     return dict(index=index, dist=dist, bins=bins, dgram=one_hot(bins, nbins))
 
 
@@ -122,9 +123,10 @@ def knn_loops(translation, mask=None, k: int = 20, nbins: int = 20, dmax: float 
             for j in range(N):
                 if j == i or not valid[b, j]:
                     continue
-                parts = [np.float32(t[b, j, c] - t[b, i, c]) for c in range(3)]
-                s = np.float32(np.float32(parts[0] * parts[0]) + np.float32(parts[1] * parts[1]))
-                s = np.float32(s + np.float32(parts[2] * parts[2]))
+                with np.errstate(over="ignore"):
+                    parts = [np.float32(t[b, j, c] - t[b, i, c]) for c in range(3)]
+                    s = np.float32(np.float32(parts[0] * parts[0]) + np.float32(parts[1] * parts[1]))
+                    s = np.float32(s + np.float32(parts[2] * parts[2]))
                 keyed.append((s, j))
             keyed.sort()
             for slot, (s, j) in enumerate(keyed[:k]):

@@ -146,13 +146,13 @@ def test_rows_subset_and_row_blocks():
 
 def test_bins_at_edges():
     """floor(d / w) with w = dmax / nbins: exact edges go up, just below stays, d >= dmax
-    and huge d clamp to the last bin, +inf (no neighbour) has no bin."""
+    and huge d (even an overflowed +inf) clamp to the last bin."""
     nb, dmax = 20, 20.0
     assert bin_width(dmax, nb) == np.float32(1.0)
     d = np.array([0.0, 0.5, 1.0, np.nextafter(np.float32(1.0), np.float32(0.0)), 19.0,
                   np.nextafter(np.float32(20.0), np.float32(0.0)), 20.0, 250.0, 3e38, np.inf],
                  dtype=np.float32)
-    assert distance_bins(d, nb, dmax).tolist() == [0, 0, 1, 0, 19, 19, 19, 19, 19, -1]
+    assert distance_bins(d, nb, dmax).tolist() == [0, 0, 1, 0, 19, 19, 19, 19, 19, 19]
     # a width that is not a power of two: bins of 3.0 are floor(fl32(d / fl32(0.6)))
     w = bin_width(6.0, 10)
     assert w == np.float32(0.6)
@@ -213,3 +213,11 @@ def test_empty_and_tiny():
     out = knn_distogram(t, None, k=5, nbins=4, dmax=4.0)
     assert out["index"][0].tolist() == [[1, 2, -1, -1, -1], [0, 2, -1, -1, -1], [0, 1, -1, -1, -1]]
     assert out["bins"][0, 1].tolist() == [1, 2, -1, -1, -1]
+    # a real neighbour whose squared distance overflows fp32 keeps its index, has
+    # distance +inf and falls in the last bin
+    t = np.array([[[0, 0, 0], [3e19, 0, 0]]], dtype=np.float32)
+    for fn in (knn_distogram, knn_loops):
+        out = fn(t, None, k=2, nbins=4, dmax=4.0)
+        assert out["index"][0].tolist() == [[1, -1], [0, -1]]
+        assert np.all(np.isinf(out["dist"][0]))
+        assert out["bins"][0].tolist() == [[3, -1], [3, -1]]
