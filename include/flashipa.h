@@ -176,6 +176,52 @@ ipa_status ipa_epilogue(const ipa_shape* s, void* lifted, const float* o, const 
 ipa_status ipa_logit_rows(const ipa_shape* s, const void* lifted, int64_t b, int64_t h, int64_t row0,
                           int64_t nrows, float* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * k-nearest-neighbour distogram (pair-feature preprocessing)
+ *
+ * FlashIPA rebuttal, paperhub page, answer to Q6: per residue only the
+ * distances to its k nearest neighbours are kept, as a (B, L, k, n_bins)
+ * distogram rather than (B, L, L, n_bins), the neighbours being found from
+ * the full L x L distance matrix; the answer also allows computing them
+ * block-wise in a streaming fashion, which is what this call does: no L x L
+ * array exists, memory is O(L k).
+ *
+ * Definition (the page leaves the arithmetic open; this is the reading):
+ *  - the position of residue i is its frame translation t_i (fp32);
+ *  - d2(i,j) = ((dx*dx + dy*dy) + dz*dz) in fp32 with dx = t_j.x - t_i.x
+ *    etc., every operation rounded to nearest, no fused multiply-add;
+ *    the distance is the correctly rounded fp32 square root of d2;
+ *  - the candidates of a valid residue i are the valid residues j != i of
+ *    the same sample, ordered by d2, equal d2 by the lower j first; the
+ *    first k are kept (slot 0 = nearest);
+ *  - bins: w = fl32(dmax / nbins); bin = floor(fl32(d / w)), and any d
+ *    with fl32(d / w) >= nbins is in bin nbins-1.
+ * Slots beyond the number of candidates, and every slot of an invalid
+ * residue, hold index -1, distance +inf and an all-zero one-hot row.
+ * The result is exact: the same bits as the definition above, whatever the
+ * data (ties, duplicate positions, masks).  Finite coordinates are a
+ * precondition. */
+typedef struct {
+  int64_t B, N;        /* samples, residues per sample (both > 0) */
+  int64_t k;           /* neighbours kept per residue, 1 .. 64 */
+  int64_t nbins;       /* distance bins, 1 .. 4096 */
+  float dmax;          /* > 0 and finite: the bins split [0, dmax) evenly */
+  int32_t dgram_dtype; /* IPA_F32 or IPA_BF16: element type of dgram */
+} ipa_knn_shape;
+
+/* translation [B,N,3] fp32 (the same array ipa_lift takes), mask [B,N]
+ * bytes or NULL (all valid).  Outputs, all written in full:
+ *   nn_index [B,N,k] int32   neighbour indices within the sample (required)
+ *   nn_dist  [B,N,k] fp32    their distances (NULL to skip)
+ *   dgram    [B,N,k,nbins]   one-hot bins, 1.0 / 0.0 in dgram_dtype (NULL
+ *                            to skip)
+ * Returns IPA_ERR_NULL (translation or nn_index NULL), IPA_ERR_SHAPE
+ * (B, N <= 0, k or nbins out of range, dmax not positive and finite),
+ * IPA_ERR_UNSUPPORTED (unknown dgram_dtype), IPA_ERR_ALIGN (a pointer not
+ * 16-byte aligned) before enqueuing anything, or IPA_ERR_LAUNCH. */
+ipa_status ipa_knn_distogram(const ipa_knn_shape* s, const float* translation, const uint8_t* mask,
+                             int32_t* nn_index, float* nn_dist, void* dgram, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* ipa_status_string(int status);
 

@@ -20,7 +20,7 @@ IPA_F32, IPA_BF16 = 0, 1
 STATUS = {0: "IPA_OK", 1: "IPA_ERR_NULL", 2: "IPA_ERR_SHAPE", 3: "IPA_ERR_UNSUPPORTED",
           4: "IPA_ERR_ALIGN", 5: "IPA_ERR_LAUNCH", 6: "IPA_ERR_DEVICE"}
 EXPORTS = ("ipa_lifted_bytes", "ipa_o_width", "ipa_lift", "ipa_flash_fwd", "ipa_epilogue",
-           "ipa_logit_rows", "ipa_status_string", "ipa_version")
+           "ipa_logit_rows", "ipa_knn_distogram", "ipa_status_string", "ipa_version")
 
 
 class IpaShape(ctypes.Structure):
@@ -36,6 +36,11 @@ class IpaLiftIn(ctypes.Structure):
 
 class IpaEpiIn(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("zl", "rotation", "translation", "w_out", "b_out")]
+
+
+class IpaKnnShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "N", "k", "nbins")] + \
+               [("dmax", ctypes.c_float), ("dgram_dtype", ctypes.c_int32)]
 
 
 class IPAError(RuntimeError):
@@ -69,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipa_epilogue.restype = ctypes.c_int
     lib.ipa_logit_rows.argtypes = [sp, vp, i64, i64, i64, i64, vp, vp]
     lib.ipa_logit_rows.restype = ctypes.c_int
+    lib.ipa_knn_distogram.argtypes = [ctypes.POINTER(IpaKnnShape), vp, vp, vp, vp, vp, vp]
+    lib.ipa_knn_distogram.restype = ctypes.c_int
     lib.ipa_status_string.argtypes = [ctypes.c_int]
     lib.ipa_status_string.restype = ctypes.c_char_p
     lib.ipa_version.argtypes = []
@@ -130,6 +137,35 @@ def ipa_epilogue(s: IpaShape, lifted, o, lse, t: dict, update, local_points, str
 def ipa_logit_rows(s: IpaShape, lifted, b: int, h: int, row0: int, nrows: int, out, stream=None):
     _check("ipa_logit_rows", load().ipa_logit_rows(ctypes.byref(s), _ptr(lifted), b, h, row0, nrows,
                                                    _ptr(out), _stream(stream)))
+
+
+def ipa_knn_distogram(s: IpaKnnShape, translation, mask, nn_index, nn_dist=None, dgram=None, stream=None):
+    _check("ipa_knn_distogram", load().ipa_knn_distogram(ctypes.byref(s), _ptr(translation), _ptr(mask),
+                                                         _ptr(nn_index), _ptr(nn_dist), _ptr(dgram),
+                                                         _stream(stream)))
+
+
+class KnnDistogram:
+    """Output buffers and the call of the kNN distogram for a fixed shape.
+
+    translation [B,N,3] fp32 and mask [B,N] uint8 (or None) are device tensors;
+    nn_index [B,N,k] int32, nn_dist [B,N,k] fp32 and dgram [B,N,k,nbins]
+    (fp32 or bf16) are allocated here and rewritten by every call."""
+
+    def __init__(self, B: int, N: int, k: int = 20, nbins: int = 20, dmax: float = 20.0,
+                 dgram_dtype: str = "f32", with_dist: bool = True, with_dgram: bool = True, device="cuda"):
+        import torch
+        load()
+        dt = {"f32": IPA_F32, "bf16": IPA_BF16}[dgram_dtype]
+        self.s = IpaKnnShape(B, N, k, nbins, float(dmax), dt)
+        self.nn_index = torch.empty(B, N, k, dtype=torch.int32, device=device)
+        self.nn_dist = torch.empty(B, N, k, dtype=torch.float32, device=device) if with_dist else None
+        tdt = torch.bfloat16 if dgram_dtype == "bf16" else torch.float32
+        self.dgram = torch.empty(B, N, k, nbins, dtype=tdt, device=device) if with_dgram else None
+
+    def __call__(self, translation, mask=None, stream=None) -> dict:
+        ipa_knn_distogram(self.s, translation, mask, self.nn_index, self.nn_dist, self.dgram, stream)
+        return dict(index=self.nn_index, dist=self.nn_dist, dgram=self.dgram)
 
 
 _FLOAT_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "translation",

@@ -14,6 +14,8 @@ hipError_t launch_epilogue(const Layout& L, void* ws, const float* o, const floa
 bool epilogue_supported(const Layout& L);
 hipError_t launch_logit_rows(const Layout& L, const void* ws, int b, int h, int row0, int nrows, float* out,
                              hipStream_t st);
+hipError_t launch_knn(const ipa_knn_shape* s, const float* t, const uint8_t* mask, int32_t* idx, float* dist,
+                      void* dgram, hipStream_t st);
 }  // namespace fipa
 
 using fipa::Layout;
@@ -104,6 +106,21 @@ ipa_status ipa_logit_rows(const ipa_shape* s, const void* lifted, int64_t b, int
   if (!aligned16(lifted) || !aligned16(out)) return IPA_ERR_ALIGN;
   return launch_status(fipa::launch_logit_rows(L, lifted, (int)b, (int)h, (int)row0, (int)nrows, out,
                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+ipa_status ipa_knn_distogram(const ipa_knn_shape* s, const float* translation, const uint8_t* mask,
+                             int32_t* nn_index, float* nn_dist, void* dgram, void* stream) {
+  if (!s || !translation || !nn_index) return IPA_ERR_NULL;
+  if (s->B <= 0 || s->N <= 0 || s->k < 1 || s->k > 64 || s->nbins < 1 || s->nbins > 4096 ||
+      !(s->dmax > 0.0f) || !(s->dmax <= 3.4028235e38f))
+    return IPA_ERR_SHAPE;
+  // query groups of 8 per wavefront must fit the 32-bit wavefront count
+  if (s->N > (int64_t)1 << 30 || s->B * ((s->N + 7) / 8) > ((int64_t)1 << 31) - 4) return IPA_ERR_SHAPE;
+  if (s->dgram_dtype != IPA_F32 && s->dgram_dtype != IPA_BF16) return IPA_ERR_UNSUPPORTED;
+  if (!aligned16(translation) || !aligned16(nn_index) || (mask && !aligned16(mask)) ||
+      (nn_dist && !aligned16(nn_dist)) || (dgram && !aligned16(dgram)))
+    return IPA_ERR_ALIGN;
+  return launch_status(fipa::launch_knn(s, translation, mask, nn_index, nn_dist, dgram, (hipStream_t)stream));
 }
 
 const char* ipa_status_string(int status) {

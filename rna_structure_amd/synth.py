@@ -118,6 +118,39 @@ def _distogram_channels(trans: np.ndarray, R: int, nbins: int = 20, dmax: float 
     return out
 
 
+def make_positions(B: int, N: int, seed: int, *, frames: str = "walk", step: float = 3.8,
+                   trans_sigma: float = 10.0, box: int = 3, lengths: Optional[tuple] = None,
+                   dropout: float = 0.0) -> dict:
+    """Seeded residue positions and masks for the kNN distogram.
+
+    frames: "walk" (random walk of `step` angstrom), "gauss" (N(0, trans_sigma^2)),
+    "lattice" (integer coordinates uniform in [-box, box]^3: many exact ties and
+    duplicates) or "same" (every residue at the origin).
+    lengths: (lo, hi) -> per-sample valid prefix L_b ~ U{lo..hi}; dropout: i.i.d.
+    probability that a residue inside the prefix is invalid.
+    Returns translation [B,N,3] fp32 and mask [B,N] bool."""
+    rng = np.random.default_rng(seed)
+    if frames == "walk":
+        t = _random_walk(rng, B, N, step)
+    elif frames == "gauss":
+        t = trans_sigma * rng.standard_normal((B, N, 3))
+    elif frames == "lattice":
+        t = rng.integers(-box, box + 1, size=(B, N, 3)).astype(np.float64)
+    elif frames == "same":
+        t = np.zeros((B, N, 3))
+    else:
+        raise ValueError(frames)
+    mask = np.ones((B, N), dtype=bool)
+    if lengths is not None:
+        lo, hi = lengths
+        L = rng.integers(lo, hi + 1, size=B)
+        for b in range(B):
+            mask[b, L[b]:] = False
+    if dropout > 0.0:
+        mask &= rng.random((B, N)) >= dropout
+    return dict(translation=t.astype(np.float32), mask=mask)
+
+
 def make_inputs(shape: IPAShape, seed: int, *, frames: str = "walk", step: float = 3.8,
                 trans_sigma: float = 10.0, lengths: Optional[tuple] = None,
                 masked_keys: tuple = (), pair_dropout: float = 0.0,

@@ -122,3 +122,28 @@ def test_validation_before_launch(lib):
     assert lib.ipa_epilogue(ctypes.byref(big), 4096, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 3
     assert lib.ipa_logit_rows(ctypes.byref(s), 4096, 5, 0, 0, 1, 4096, None) == 2   # b out of range
     assert lib.ipa_logit_rows(ctypes.byref(s), 4096, 0, 0, 299, 2, 4096, None) == 2  # rows past N
+
+
+def test_knn_struct_size_matches_c():
+    assert ctypes.sizeof(_lib.IpaKnnShape) == 4 * 8 + 4 + 4
+
+
+def test_knn_validation_before_launch(lib):
+    def ks(**kw):
+        base = dict(B=2, N=300, k=20, nbins=20, dmax=20.0, dgram_dtype=0)
+        base.update(kw)
+        return _lib.IpaKnnShape(base["B"], base["N"], base["k"], base["nbins"], base["dmax"], base["dgram_dtype"])
+
+    call = lambda s, t=4096, m=None, i=4096, d=4096, g=4096: lib.ipa_knn_distogram(ctypes.byref(s), t, m, i, d, g, None)
+    assert lib.ipa_knn_distogram(None, 4096, None, 4096, None, None, None) == 1
+    assert call(ks(), t=None) == 1
+    assert call(ks(), i=None) == 1
+    for bad in (dict(B=0), dict(N=0), dict(k=0), dict(k=65), dict(nbins=0), dict(nbins=5000), dict(dmax=0.0),
+                dict(dmax=-1.0), dict(dmax=float("inf")), dict(dmax=float("nan")), dict(N=(1 << 30) + 1)):
+        assert call(ks(**bad)) == 2, bad
+    assert call(ks(dgram_dtype=5)) == 3
+    assert call(ks(), t=4100) == 4
+    assert call(ks(), m=4097) == 4
+    assert call(ks(), i=4104) == 4
+    assert call(ks(), d=4104) == 4
+    assert call(ks(), g=4104) == 4

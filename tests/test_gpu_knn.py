@@ -1,0 +1,87 @@
+"""GPU parity of the kNN distogram: the HIP kernel against the CPU oracle on the
+same seeded positions.  Integer and byte work, so the bar is bit-exact:
+neighbour indices, fp32 distances (compared as bits) and the one-hot rows,
+in every slot of every residue, including padding slots and invalid rows."""
+import numpy as np
+import pytest
+
+from oracle import knn_distogram
+from rna_structure_amd.synth import make_positions
+
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(pos, k, nbins, dmax, dgram_dtype="f32", with_mask=True, prefill=True):
+    import torch
+    from rna_structure_amd import _lib
+    B, N, _ = pos["translation"].shape
+    t = torch.from_numpy(np.ascontiguousarray(pos["translation"])).cuda()
+    m = torch.from_numpy(pos["mask"].astype(np.uint8)).cuda() if with_mask else None
+    kd = _lib.KnnDistogram(B, N, k, nbins, dmax, dgram_dtype=dgram_dtype)
+    if prefill:   # every element must be written by the call
+        kd.nn_index.fill_(12345)
+        kd.nn_dist.fill_(-7.0)
+        kd.dgram.fill_(3.0)
+    out = kd(t, m)
+    torch.cuda.synchronize()
+    return {key: v.float().cpu().numpy() if key == "dgram" else v.cpu().numpy() for key, v in out.items()}
+
+
+def _compare(got, ref, rows=None):
+    sel = (lambda a: a) if rows is None else (lambda a: a[:, rows])
+    gi, gd, gg = sel(got["index"]), sel(got["dist"]), sel(got["dgram"])
+    assert np.array_equal(gi, ref["index"]), np.argwhere(gi != ref["index"])[:5]
+    assert np.array_equal(gd.view(np.uint32), ref["dist"].view(np.uint32)), np.argwhere(gd != ref["dist"])[:5]
+    assert np.array_equal(gg, ref["dgram"]), np.argwhere(gg != ref["dgram"])[:5]
+
+
+CASES = [
+    # name, B, N, seed, positions kw, k, nbins, dmax, dgram dtype
+    ("walk-ragged", 2, 300, 1, dict(frames="walk", step=3.8, lengths=(200, 300), dropout=0.03), 20, 20, 20.0, "f32"),
+    ("walk-6A-bin-edges", 1, 500, 2, dict(frames="walk", step=6.0), 20, 20, 20.0, "bf16"),
+    ("gauss-k64-odd-bins", 1, 1100, 3, dict(frames="gauss", trans_sigma=12.0, dropout=0.05), 64, 37, 25.0, "bf16"),
+    ("k1-batch", 3, 100, 4, dict(frames="gauss", lengths=(1, 100)), 1, 8, 10.0, "f32"),
+    ("lattice-ties", 2, 400, 5, dict(frames="lattice", box=3, dropout=0.1), 20, 6, 3.0, "f32"),
+    ("all-same-position", 1, 300, 6, dict(frames="same"), 20, 4, 1.0, "f32"),
+    ("fewer-than-k", 2, 7, 7, dict(frames="gauss", lengths=(1, 7)), 20, 20, 20.0, "f32"),
+    ("one-residue", 2, 1, 8, dict(frames="gauss"), 5, 3, 3.0, "bf16"),
+    ("n65-ragged-tail", 1, 65, 9, dict(frames="walk"), 20, 64, 16.0, "f32"),
+    ("many-bins", 1, 200, 10, dict(frames="walk", step=3.8), 16, 300, 30.0, "f32"),
+]
+
+
+@pytest.mark.parametrize("name,B,N,seed,kw,k,nbins,dmax,dt", CASES, ids=[c[0] for c in CASES])
+def test_knn_small(name, B, N, seed, kw, k, nbins, dmax, dt):
+    say(f"case knn {name} B={B} N={N} k={k} nbins={nbins}")
+    pos = make_positions(B, N, seed, **kw)
+    ref = knn_distogram(pos["translation"], pos["mask"], k=k, nbins=nbins, dmax=dmax)
+    _compare(_run(pos, k, nbins, dmax, dt), ref)
+
+
+def test_knn_mask_none_equals_all_valid():
+    say("case knn mask None")
+    pos = make_positions(2, 257, 11, frames="walk")
+    a = _run(pos, 20, 20, 20.0, with_mask=False)
+    ref = knn_distogram(pos["translation"], None, k=20)
+    _compare(a, ref)
+
+
+@pytest.mark.parametrize("B,N,frames", [(1, 16384, "walk"), (1, 8192, "gauss"), (39, 512, "walk")])
+def test_knn_full_size_sampled_rows(B, N, frames):
+    """Full-size inputs in the launch the benchmark times; the oracle computes a
+    sample of rows (first, last, block edges, random) one by one."""
+    say(f"case knn full B={B} N={N} {frames}")
+    pos = make_positions(B, N, 100 + N, frames=frames, step=3.8, trans_sigma=30.0)
+    got = _run(pos, 20, 20, 20.0, prefill=False)
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.concatenate([[0, 1, 7, 8, 63, 64, N - 65, N - 1], rng.integers(0, N, 40)]))
+    ref = knn_distogram(pos["translation"], pos["mask"], k=20, rows=rows)
+    _compare(got, ref, rows)
+    # properties that hold for every row: sorted distances, no self, in range
+    idx, dist = got["index"], got["dist"]
+    assert np.all(np.diff(dist, axis=-1) >= 0)
+    assert np.all((idx >= 0) & (idx < N))
+    assert not np.any(idx == np.arange(N)[None, :, None])
+    assert np.array_equal(got["dgram"].sum(-1), np.ones_like(dist))
