@@ -142,6 +142,76 @@ def time_forward(inp, steps, warmup, per_kernel=True, min_warm_ms=40.0):
     return res
 
 
+# kNN distogram (pair-feature preprocessing): 8 fp32 operations per ordered
+# pair (3 differences, 3 squares, 2 sums) against the rate of unfused,
+# unpacked fp32 vector operations: 256 CUs x 64 lanes x 2.4 GHz.
+KNN_FLOPS_PER_PAIR = 8
+PEAK_VALU_TOPS = 256 * 64 * 2.4e9 / 1e12
+KNN_WORKLOADS = (
+    ("knn_16384", 1, 16384, dict(frames="walk", step=3.8)),
+    ("knn_rna_2048", 1, 2048, dict(frames="walk", step=6.0)),
+    ("knn_short_batch", 39, 512, dict(frames="walk", step=3.8)),
+    ("knn_gauss_8192", 1, 8192, dict(frames="gauss", trans_sigma=30.0)),
+)
+
+
+def time_knn(name, B, N, kw, steps, k=20, nbins=20, dmax=20.0, min_warm_ms=40.0):
+    """Time ipa_knn_distogram on resident positions: warm-up of at least
+    min_warm_ms of GPU time, then `steps` timed calls."""
+    import numpy as np
+    import torch
+    from rna_structure_amd import _lib
+    from rna_structure_amd.synth import make_positions
+    pos = make_positions(B, N, 7000 + N, **kw)
+    t = torch.from_numpy(np.ascontiguousarray(pos["translation"])).cuda()
+    m = torch.from_numpy(pos["mask"].astype(np.uint8)).cuda()
+    kd = _lib.KnnDistogram(B, N, k, nbins, dmax)
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    warm = 0.0
+    while warm < min_warm_ms:
+        e0.record(st)
+        for _ in range(5):
+            kd(t, m)
+        e1.record(st)
+        torch.cuda.synchronize()
+        warm += e0.elapsed_time(e1)
+    e0.record(st)
+    for _ in range(steps):
+        kd(t, m)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = B * N * N
+    tops = KNN_FLOPS_PER_PAIR * pairs / (ms * 1e-3) / 1e12
+    out_bytes = B * N * k * (4 + 4 + 4 * nbins)
+    return {"workload": name, "B": B, "N": N, "k": k, "nbins": nbins, "frames": kw["frames"], "ms": round(ms, 4),
+            "gpairs_per_s": round(pairs / (ms * 1e-3) / 1e9, 1), "alu_tflops": round(tops, 2),
+            "alu_frac": round(tops / PEAK_VALU_TOPS, 4), "out_bytes": out_bytes,
+            "out_GBs": round(out_bytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def knn_cpu_baseline(N=16384, budget_s=3.0):
+    """The kNN oracle on a sample of rows of the N-residue walk, scaled to all rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import knn_distogram
+    from rna_structure_amd.synth import make_positions
+    pos = make_positions(1, N, 7000 + N, frames="walk", step=3.8)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        knn_distogram(pos["translation"], pos["mask"], k=20, rows=np.arange(16))
+        per_row = (time.perf_counter() - t0) / 16
+        n = int(max(16, min(N, budget_s / max(per_row, 1e-9))))
+        t0 = time.perf_counter()
+        knn_distogram(pos["translation"], pos["mask"], k=20, rows=np.arange(n))
+        el = time.perf_counter() - t0
+    return {"workload": f"knn_{N}", "ms_per_call": round(el * N / n * 1e3, 1), "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {N} rows, fp32 NumPy oracle, {el:.1f} s measured, scaled by N/rows"}
+
+
 def cpu_baseline(inp, flops, budget_s=12.0):
     """Time the float64 oracle on a bounded sample of query rows and scale to
     the whole forward (per-row cost is the same for every row at fixed N)."""
@@ -211,6 +281,17 @@ def hbm_calibration(mib: int = 2048, reps: int = 10) -> dict:
     return res
 
 
+def knn_section(args):
+    res = []
+    for name, B, N, kw in KNN_WORKLOADS:
+        res.append(time_knn(name, B, N, kw, max(5, args.steps)))
+        print(f"# knn {res[-1]}", file=sys.stderr, flush=True)
+    sec = {"peak_alu_tflops": round(PEAK_VALU_TOPS, 2), "flops_per_pair": KNN_FLOPS_PER_PAIR, "runs": res}
+    if not args.no_cpu_baseline:
+        sec["cpu_baseline"] = knn_cpu_baseline()
+    return sec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +300,9 @@ def main():
     ap.add_argument("--workload", default="sweep_16384")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-knn", action="store_true", help="skip the kNN distogram section")
+    ap.add_argument("--knn-only", action="store_true",
+                    help="run only the kNN distogram section and print it as the JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only plain copies of MIB MiB (counter calibration) and exit")
     ap.add_argument("--hbm-calibration", action="store_true",
@@ -235,6 +319,9 @@ def main():
         return
     if args.hbm_calibration:
         print(json.dumps({"hbm_calibration": hbm_calibration()}), flush=True)
+        return
+    if args.knn_only:
+        print(json.dumps({"knn_distogram": knn_section(args)}), flush=True)
         return
     inp = make_workload(args.workload)
     shape = inp["shape"]
@@ -321,6 +408,8 @@ def main():
                           "lift_ms": round(rr["lift_ms"], 4), "epilogue_ms": round(rr["epilogue_ms"], 4)})
             print(f"# rank sweep {ranks[-1]}", file=sys.stderr, flush=True)
         out["rank_sweep"] = ranks
+    if not args.no_sweep and not args.no_knn:
+        out["knn_distogram"] = knn_section(args)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, flops)

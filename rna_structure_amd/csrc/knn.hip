@@ -17,11 +17,12 @@
 // order and lowers tau to the k-th one.  Candidates arrive in increasing
 // index order, so a later candidate with the same d2 as the k-th kept one
 // loses the tie: after a selection the test is d2 < d2_k, written as
-// d2 <= tau with tau the float just below d2_k.  Before the walk, tau is the
-// k-th smallest d2 of a 64-residue window around the queries, taken
-// inclusively (any k candidates bound the final k-th distance from above);
-// for chain molecules it is already close to the final value, so the walk
-// buffers few candidates.  A last selection orders the survivors.
+// d2 <= tau with tau the float just below d2_k.  Before the walk, tau is
+// (just above) the k-th smallest d2 among the candidates of a 64-residue
+// window around the queries, taken inclusively (any k candidates bound the final k-th distance
+// from above); for chain molecules sequence neighbours are spatial
+// neighbours, so this is close to the final value and the walk buffers few
+// candidates.  A last selection orders the survivors.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,7 +44,7 @@ struct KnnArgs {
   void* dgram;           // [B,N,k,nbins] or null
   int N, k, nbins;
   int groups;            // ceil(N / G) query groups per sample
-  int waves;             // B * groups
+  int waves;             // B * groups: query groups in the grid
   float width;           // fl32(dmax / nbins)
   int bf16;              // dgram element type
 };
@@ -58,10 +59,13 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Order key of a buffered candidate: (d2 bits, index).  d2 >= 0, so its bits
-// order like the value; a d2 word of ~0u marks an entry that is not a
-// candidate (the query itself) and sorts after every candidate.
-__device__ __forceinline__ uint64_t key_of(uint2 e) { return ((uint64_t)e.x << 32) | e.y; }
+// A buffered candidate is its order key, (d2 bits) << 32 | index: d2 >= 0,
+// so the key orders like (d2, index).  A d2 word of ~0u marks an entry that
+// is not a candidate (the query itself, or padding) and sorts after every
+// candidate.
+constexpr uint64_t kDeadKey = ~0ull;
+__device__ __forceinline__ uint64_t make_key(uint32_t d2bits, uint32_t j) { return ((uint64_t)d2bits << 32) | j; }
+__device__ __forceinline__ bool key_live(uint64_t key) { return (uint32_t)(key >> 32) != ~0u; }
 
 // fp32 squared distance of candidate (x,y,z) from query (qx,qy,qz):
 // ((dx*dx + dy*dy) + dz*dz), each operation rounded on its own.
@@ -71,33 +75,80 @@ __device__ __forceinline__ float sqdist(float x, float y, float z, float qx, flo
   return (dx * dx + dy * dy) + dz * dz;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+// k-th smallest (1 <= k <= 64) of the 64 lanes' values v[g] < 2^BITS, for
+// G value sets at once: the smallest T with #{v <= T} >= k, found bit by bit
+// from the top with one ballot per bit and set (the G searches are
+// independent, so their ballots overlap).  Wave-uniform results.
+template <int BITS>
+__device__ __forceinline__ void kth_smallest(const uint32_t (&v)[kKnnG], int k, uint32_t (&res)[kKnnG]) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int g = 0; g < kKnnG; ++g) res[g] = 0;
+#pragma unroll
+  for (int bit = BITS - 1; bit >= 0; --bit) {
+    // all G ballots first, then the scalar updates: the vector compares and
+    // the scalar counts of different sets overlap
+    uint64_t bl[kKnnG];
+#pragma unroll
+    for (int g = 0; g < kKnnG; ++g) bl[g] = __ballot(v[g] <= (res[g] | ((1u << bit) - 1u)));
+#pragma unroll
+    for (int g = 0; g < kKnnG; ++g)
+      if (__popcll(bl[g]) < k) res[g] |= 1u << bit;
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t w = (uint32_t)__shfl_xor((int)v, o);
+    v = w > v ? w : v;
+  }
   return v;
 }
 
 // Keeps the (at most k) smallest candidate keys of buf[0..n), n <= 256,
-// sorted at buf[0..); returns how many were kept (wave-uniform).
-__device__ int select_topk(uint2* buf, int n, int k, int lane) {
-  uint2 e[4];
+// sorted at buf[0..); returns how many were kept (wave-uniform).  Every lane
+// ranks its (up to four) entries against all n keys, read as broadcasts.
+__device__ __forceinline__ int select_topk(uint64_t* buf, int n, int k, int lane) {
   uint64_t ke[4];
   int rank[4];
   bool live[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int p = lane + 64 * r;
-    e[r] = p < n ? buf[p] : make_uint2(~0u, ~0u);
-    ke[r] = key_of(e[r]);
-    live[r] = p < n && e[r].x != ~0u;
+    const uint64_t v = buf[p];
+    ke[r] = p < n ? v : kDeadKey;
+    live[r] = key_live(ke[r]);
     rank[r] = 0;
   }
-  const int rows = (n + 63) >> 6;
-  if (rows <= 1) {
-    for (int f = 0; f < n; ++f) rank[0] += key_of(buf[f]) < ke[0] ? 1 : 0;
+  const uint4* b4 = reinterpret_cast<const uint4*>(buf);
+  if (n <= 64) {
+    // one entry per lane: entries n..63 become dead keys (they rank nothing),
+    // then all 64 broadcasts are in flight at once
+    if (lane >= n) buf[lane] = kDeadKey;
+    wave_sync();
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const uint4 w = b4[q];
+      rank[0] += (((uint64_t)w.y << 32) | w.x) < ke[0] ? 1 : 0;
+      rank[0] += (((uint64_t)w.w << 32) | w.z) < ke[0] ? 1 : 0;
+    }
   } else {
-    for (int f = 0; f < n; ++f) {
-      const uint64_t v = key_of(buf[f]);
+    int f = 0;
+    for (; f + 8 <= n; f += 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 w = b4[(f >> 1) + u];
+        v[2 * u] = ((uint64_t)w.y << 32) | w.x;
+        v[2 * u + 1] = ((uint64_t)w.w << 32) | w.z;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rank[r] += v[u] < ke[r] ? 1 : 0;
+    }
+    for (; f < n; ++f) {
+      const uint64_t v = buf[f];
 #pragma unroll
       for (int r = 0; r < 4; ++r) rank[r] += v < ke[r] ? 1 : 0;
     }
@@ -108,148 +159,259 @@ __device__ int select_topk(uint2* buf, int n, int k, int lane) {
   wave_sync();
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    if (live[r] && rank[r] < k) buf[rank[r]] = e[r];
+    if (live[r] && rank[r] < k) buf[rank[r]] = ke[r];
   wave_sync();
   return __builtin_amdgcn_readfirstlane(nlive < k ? nlive : k);
 }
 
-__device__ __forceinline__ void load_candidate(const float* tb, const uint8_t* mb, int j, int N, float& x, float& y,
-                                               float& z) {
-  const float qnan = __int_as_float(0x7fc00000);
-  x = y = z = qnan;  // NaN: fails every d2 <= tau test
-  if (j < N && (!mb || mb[j])) {
-    const float* p = tb + 3 * (size_t)j;
-    x = p[0];
-    y = p[1];
-    z = p[2];
-  }
+// Candidate j's position, NaN (fails every d2 <= tau test) when j is past the
+// end or masked.  The loads are issued unconditionally for j < N so that the
+// mask does not serialise them.
+struct Cand {
+  float x, y, z;
+  uint32_t m;   // mask byte (ignored without a mask)
+  bool inb;     // j < N
+};
+
+// mp is the mask, or any readable byte array when there is no mask.  The
+// loads are issued unconditionally (clamped index) and their results are only
+// looked at in use_candidate, so that a prefetch is not waited for at once.
+__device__ __forceinline__ Cand fetch_candidate(const float* tb, const uint8_t* mp, int j, int N) {
+  const int jc = j < N ? j : N - 1;
+  const float* p = tb + 3 * (size_t)jc;
+  Cand c;
+  c.x = p[0];
+  c.y = p[1];
+  c.z = p[2];
+  c.m = mp[jc];
+  c.inb = j < N;
+  return c;
 }
 
+__device__ __forceinline__ void use_candidate(const Cand& c, bool has_mask, float& x, float& y, float& z) {
+  const float qnan = __int_as_float(0x7fc00000);
+  const bool ok = c.inb & (!has_mask | (c.m != 0u));
+  x = ok ? c.x : qnan;
+  y = ok ? c.y : qnan;
+  z = ok ? c.z : qnan;
+}
+
+// S wavefronts share one group of G query residues, each walking 1/S of the
+// candidate blocks (S = 1, 2, 4; more splits when the grid is small), then
+// their per-split best k are merged.  A workgroup holds 4 / S groups.
+// Per-query state (position, tau, buffer fill) lives in LDS: the hot loop
+// keeps the positions in vector registers (loaded once) and re-reads the
+// eight thresholds each step; the rare append path walks the queries in a
+// plain loop.
+template <int S>
 __global__ __launch_bounds__(256) void knn_distogram_kernel(KnnArgs a) {
-  __shared__ uint2 s_buf[kKnnWaves][kKnnG][kKnnCap];
-  __shared__ int s_bin[kKnnWaves][kKnnMaxK];
+  constexpr int GPW = kKnnWaves / S;
+  __shared__ uint64_t s_buf[kKnnWaves][kKnnG][kKnnCap];
+  __shared__ int s_cnt[kKnnWaves][kKnnG];
+  __shared__ __align__(16) float s_tau[kKnnWaves][kKnnG];
+  __shared__ int s_bin[kKnnWaves][kKnnG * kKnnMaxK];
+  __shared__ float4 s_q[kKnnWaves][kKnnG];
   const int lane = threadIdx.x & 63;
   const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wid = blockIdx.x * kKnnWaves + wl;
-  if (wid >= a.waves) return;
+  const int gl = wl / S, split = wl - gl * S;
+  const int grp = blockIdx.x * GPW + gl;
+  const bool live = grp < a.waves;
+  if (S == 1 && !live) return;
   const int N = a.N, k = a.k;
-  const int b = wid / a.groups;
-  const int i0 = (wid - b * a.groups) * kKnnG;
+  const int b = live ? grp / a.groups : 0;
+  const int i0 = (grp - b * a.groups) * kKnnG;
   const float* tb = a.t + (size_t)b * N * 3;
   const uint8_t* mb = a.mask ? a.mask + (size_t)b * N : nullptr;
+  const bool has_mask = mb != nullptr;
+  const uint8_t* mp = has_mask ? mb : (const uint8_t*)tb;
   const float inf = __int_as_float(0x7f800000);
 
-  float qx[kKnnG], qy[kKnnG], qz[kKnnG], tau[kKnnG];
-  int cnt[kKnnG];
-  bool act[kKnnG];
-#pragma unroll
-  for (int g = 0; g < kKnnG; ++g) {
-    const int i = i0 + g;
-    act[g] = i < N && (!mb || mb[i]);
-    qx[g] = qy[g] = qz[g] = 0.0f;
-    if (act[g]) {
-      qx[g] = tb[3 * (size_t)i];
-      qy[g] = tb[3 * (size_t)i + 1];
-      qz[g] = tb[3 * (size_t)i + 2];
+  // Lane g < G loads query g; act has bit g set when query g is a valid residue.
+  uint32_t act = 0;
+  if (live) {
+    bool ok = false;
+    if (lane < kKnnG) {
+      const int i = i0 + lane;
+      ok = i < N && (!mb || mb[i]);
+      float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (ok) q = make_float4(tb[3 * (size_t)i], tb[3 * (size_t)i + 1], tb[3 * (size_t)i + 2], 0.0f);
+      s_q[wl][lane] = q;
+      s_tau[wl][lane] = ok ? inf : -1.0f;
+      s_cnt[wl][lane] = 0;
     }
-    tau[g] = act[g] ? inf : -1.0f;
-    cnt[g] = 0;
+    act = (uint32_t)__ballot(ok);
+    wave_sync();
   }
-
-  // Seed: tau = k-th smallest d2 over the window's candidates (+inf if fewer).
-  {
+  // Seed from a 64-residue window around the queries.
+  if (live) {
     int w0 = i0 + kKnnG / 2 - 32;
     w0 = w0 < N - 64 ? w0 : N - 64;
     w0 = w0 > 0 ? w0 : 0;
     const int j = w0 + lane;
     float x, y, z;
-    load_candidate(tb, mb, j, N, x, y, z);
+    use_candidate(fetch_candidate(tb, mp, j, N), has_mask, x, y, z);
+    // Per query: tau = the k-th smallest d2 among the window's candidates
+    // (+inf when it holds fewer than k), rounded up to the top 12 bits of its
+    // encoding (exponent and 4 mantissa bits: at most 1/16 above): an upper
+    // bound of the final k-th d2.
+    constexpr int kLow = 19;
+    uint32_t v[kKnnG], t[kKnnG];
 #pragma unroll
     for (int g = 0; g < kKnnG; ++g) {
-      if (!act[g]) continue;
-      const float d2 = sqdist(x, y, z, qx[g], qy[g], qz[g]);
-      const float v = (j == i0 + g || d2 != d2) ? inf : d2;
-      int lt = 0;
-      for (int c = 0; c < 64; ++c) lt += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c)) < v ? 1 : 0;
-      const float m = wave_max(lt < k ? v : -inf);
-      tau[g] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(m)));
+      const float4 q = s_q[wl][g];
+      const float d2 = sqdist(x, y, z, q.x, q.y, q.z);
+      v[g] = __float_as_uint((j == i0 + g || d2 != d2) ? inf : d2) >> kLow;
     }
+    kth_smallest<31 - kLow>(v, k, t);
+    uint32_t tl = 0;
+#pragma unroll
+    for (int g = 0; g < kKnnG; ++g) tl = lane == g ? t[g] : tl;
+    tl = (tl << kLow) | ((1u << kLow) - 1u);
+    if (tl >= 0x7f800000u) tl = 0x7f800000u;  // an infinite k-th value stays +inf
+    if (lane < kKnnG && ((act >> lane) & 1u)) s_tau[wl][lane] = __uint_as_float(tl);
   }
 
-  // Walk all candidates in increasing index order, one block of 64 per step.
-  float cx, cy, cz;
-  load_candidate(tb, mb, lane, N, cx, cy, cz);
-  for (int c0 = 0; c0 < N; c0 += 64) {
-    const int j = c0 + lane;
-    const float x = cx, y = cy, z = cz;
-    load_candidate(tb, mb, j + 64, N, cx, cy, cz);  // next block, in flight during this one
+  if (live) {
+    wave_sync();
+    float qx[kKnnG], qy[kKnnG], qz[kKnnG];
 #pragma unroll
     for (int g = 0; g < kKnnG; ++g) {
-      const float d2 = sqdist(x, y, z, qx[g], qy[g], qz[g]);
-      const bool pass = d2 <= tau[g];
-      const uint64_t m = __ballot(pass);
-      if (m) {
-        uint2* buf = &s_buf[wl][g][0];
-        if (pass) buf[cnt[g] + lanes_below(m)] = make_uint2(j == i0 + g ? ~0u : __float_as_uint(d2), (uint32_t)j);
-        cnt[g] = __builtin_amdgcn_readfirstlane(cnt[g] + __popcll(m));
-        if (cnt[g] > kKnnCap - 64) {
+      const float4 q = s_q[wl][g];
+      qx[g] = q.x;
+      qy[g] = q.y;
+      qz[g] = q.z;
+    }
+    // Walk this split's candidate blocks in increasing index order.
+    const int nblk = (N + 63) >> 6;
+    const int cb = (split * nblk / S) * 64, ce = ((split + 1) * nblk / S) * 64;
+    Cand nx = fetch_candidate(tb, mp, cb + lane, N);
+    for (int c0 = cb; c0 < ce; c0 += 64) {
+      const int j = c0 + lane;
+      float x, y, z;
+      use_candidate(nx, has_mask, x, y, z);
+      nx = fetch_candidate(tb, mp, j + 64, N);  // next block, in flight during this one
+      const float4 ta = *(const float4*)&s_tau[wl][0];
+      const float4 tc = *(const float4*)&s_tau[wl][4];
+      const float tau[kKnnG] = {ta.x, ta.y, ta.z, ta.w, tc.x, tc.y, tc.z, tc.w};
+      uint64_t any = 0;
+#pragma unroll
+      for (int g = 0; g < kKnnG; ++g) any |= __ballot(sqdist(x, y, z, qx[g], qy[g], qz[g]) <= tau[g]);
+      if (!any) continue;
+      // Append path: the same distances again, one query at a time.
+#pragma unroll 1
+      for (int g = 0; g < kKnnG; ++g) {
+        const float4 q = s_q[wl][g];
+        const float d2 = sqdist(x, y, z, q.x, q.y, q.z);
+        const bool pass = d2 <= s_tau[wl][g];
+        const uint64_t m = __ballot(pass);
+        if (!m) continue;
+        uint64_t* buf = &s_buf[wl][g][0];
+        int n = __builtin_amdgcn_readfirstlane(s_cnt[wl][g]);
+        if (pass) buf[n + lanes_below(m)] = make_key(j == i0 + g ? ~0u : __float_as_uint(d2), (uint32_t)j);
+        n += __popcll(m);
+        if (n > kKnnCap - 64) {
           wave_sync();
-          cnt[g] = select_topk(buf, cnt[g], k, lane);
-          if (cnt[g] == k) {
-            const uint32_t kb = __builtin_amdgcn_readfirstlane(buf[k - 1].x);
-            tau[g] = kb == 0u ? -1.0f : __uint_as_float(kb - 1u);
+          n = select_topk(buf, n, k, lane);
+          if (n == k) {
+            const uint32_t kb = __builtin_amdgcn_readfirstlane((uint32_t)(buf[k - 1] >> 32));
+            if (lane == 0) s_tau[wl][g] = kb == 0u ? -1.0f : __uint_as_float(kb - 1u);
           }
         }
+        if (lane == 0) s_cnt[wl][g] = n;
+        wave_sync();
       }
     }
-  }
-
-  // Order the survivors and write the k slots of every query residue.
-  const int nb = a.nbins;
-  const int tot = k * nb;
-  const int q64 = 64 / nb, r64 = 64 - q64 * nb;
-  const int s_first = lane / nb, c_first = lane - s_first * nb;
-#pragma unroll
-  for (int g = 0; g < kKnnG; ++g) {
-    const int i = i0 + g;
-    if (i >= N) break;
-    uint2* buf = &s_buf[wl][g][0];
+    // This split's best k of every query, in order.
     wave_sync();
-    const int n = act[g] ? select_topk(buf, cnt[g], k, lane) : 0;
-    const size_t row = (size_t)b * N + i;
-    int jj = -1, bin = -1;
-    float d = inf;
-    if (lane < n) {
-      const uint2 e = buf[lane];
-      d = sqrtf(__uint_as_float(e.x));
-      jj = (int)e.y;
-      const float q = d / a.width;
-      bin = q >= (float)nb ? nb - 1 : (int)q;
+#pragma unroll 1
+    for (int g = 0; g < kKnnG; ++g) {
+      if (!((act >> g) & 1u)) continue;
+      const int n = select_topk(&s_buf[wl][g][0], __builtin_amdgcn_readfirstlane(s_cnt[wl][g]), k, lane);
+      if (lane == 0) s_cnt[wl][g] = n;
     }
-    if (lane < k) {
-      a.idx[row * k + lane] = jj;
-      if (a.dist) a.dist[row * k + lane] = d;
-      s_bin[wl][lane] = bin;
+  }
+  if constexpr (S > 1) {
+    // Merge: split s takes the queries g with g % S == s and gathers the
+    // other splits' best k behind its own before a last selection.
+    __syncthreads();
+    if (live) {
+#pragma unroll 1
+      for (int g = split; g < kKnnG; g += S) {
+        if (!((act >> g) & 1u)) continue;
+        uint64_t* buf = &s_buf[wl][g][0];
+        int n = __builtin_amdgcn_readfirstlane(s_cnt[wl][g]);
+        for (int o = 1; o < S; ++o) {
+          const int src = gl * S + (split + o) % S;
+          const int no = __builtin_amdgcn_readfirstlane(s_cnt[src][g]);
+          if (lane < no) buf[n + lane] = s_buf[src][g][lane];
+          n += no;
+        }
+        wave_sync();
+        n = select_topk(buf, n, k, lane);
+        if (lane == 0) s_cnt[wl][g] = n;
+      }
     }
-    if (a.dgram) {
-      wave_sync();
-      int s = s_first, c = c_first;
-      if (a.bf16) {
-        uint16_t* out = (uint16_t*)a.dgram + row * tot;
-        for (int e2 = lane; e2 < tot; e2 += 64) {
-          out[e2] = s_bin[wl][s] == c ? (uint16_t)0x3F80 : (uint16_t)0;
-          c += r64;
-          s += q64;
-          if (c >= nb) { c -= nb; ++s; }
-        }
-      } else {
-        float* out = (float*)a.dgram + row * tot;
-        for (int e2 = lane; e2 < tot; e2 += 64) {
-          out[e2] = s_bin[wl][s] == c ? 1.0f : 0.0f;
-          c += r64;
-          s += q64;
-          if (c >= nb) { c -= nb; ++s; }
-        }
+    __syncthreads();
+  }
+  if (!live) return;
+  wave_sync();
+
+  // Outputs of the group's rows i0 .. i0+gv-1, contiguous in every output
+  // array; the S wavefronts of the group share them.  Query g's final list
+  // sits in the buffer of split g % S.
+  const int gv = N - i0 < kKnnG ? N - i0 : kKnnG;
+  const int nb = a.nbins;
+  const size_t row0 = (size_t)b * N + i0;
+  int* bins = &s_bin[gl][0];
+  {
+    const int np = gv * k;  // (query, slot) pairs
+    int p = split * 64 + lane;
+    int g = p / k, sl = p - g * k;
+    const int gstep = (S * 64) / k, sstep = S * 64 - gstep * k;
+    for (; p < np; p += S * 64) {
+      const int owner = gl * S + g % S;
+      const int n = ((act >> g) & 1u) ? s_cnt[owner][g] : 0;
+      int jj = -1, bin = -1;
+      float d = inf;
+      if (sl < n) {
+        const uint64_t e = s_buf[owner][g][sl];
+        d = sqrtf(__uint_as_float((uint32_t)(e >> 32)));
+        jj = (int)(uint32_t)e;
+        const float q = d / a.width;
+        bin = q >= (float)nb ? nb - 1 : (int)q;
+      }
+      a.idx[row0 * k + p] = jj;
+      if (a.dist) a.dist[row0 * k + p] = d;
+      bins[p] = bin;
+      g += gstep;
+      sl += sstep;
+      if (sl >= k) { sl -= k; ++g; }
+    }
+  }
+  if (!a.dgram) return;
+  if constexpr (S > 1) __syncthreads(); else wave_sync();
+  {
+    const int ne = gv * k * nb;  // one-hot elements
+    int e = split * 64 + lane;
+    int p = e / nb, c = e - p * nb;
+    const int pstep = (S * 64) / nb, cstep = S * 64 - pstep * nb;
+    if (a.bf16) {
+      uint16_t* out = (uint16_t*)a.dgram + row0 * k * nb;
+#pragma unroll 4
+      for (; e < ne; e += S * 64) {
+        out[e] = bins[p] == c ? (uint16_t)0x3F80 : (uint16_t)0;
+        p += pstep;
+        c += cstep;
+        if (c >= nb) { c -= nb; ++p; }
+      }
+    } else {
+      float* out = (float*)a.dgram + row0 * k * nb;
+#pragma unroll 4
+      for (; e < ne; e += S * 64) {
+        out[e] = bins[p] == c ? 1.0f : 0.0f;
+        p += pstep;
+        c += cstep;
+        if (c >= nb) { c -= nb; ++p; }
       }
     }
   }
@@ -269,11 +431,23 @@ hipError_t launch_knn(const ipa_knn_shape* s, const float* t, const uint8_t* mas
   a.k = (int)s->k;
   a.nbins = (int)s->nbins;
   a.groups = (int)((s->N + kKnnG - 1) / kKnnG);
-  a.waves = (int)(s->B * a.groups);
+  a.waves = (int)(s->B * a.groups);  // query groups in the grid
   a.width = s->dmax / (float)s->nbins;  // fp32 division, correctly rounded
   a.bf16 = s->dgram_dtype == IPA_BF16;
-  const int blocks = (a.waves + kKnnWaves - 1) / kKnnWaves;
-  hipLaunchKernelGGL(knn_distogram_kernel, dim3(blocks), dim3(64 * kKnnWaves), 0, st, a);
+  // split the candidate walk of a group over several wavefronts while the
+  // grid has fewer than ~2048 wavefronts (8 per CU) and every split keeps at
+  // least 4 blocks of candidates
+  const int64_t nblk = (s->N + 63) / 64;
+  int S = 1;
+  while (S < 4 && (int64_t)a.waves * S * 2 <= 2048 && nblk >= 8 * S) S *= 2;
+  const int gpw = kKnnWaves / S;
+  const int blocks = (a.waves + gpw - 1) / gpw;
+  if (S == 1)
+    hipLaunchKernelGGL(knn_distogram_kernel<1>, dim3(blocks), dim3(64 * kKnnWaves), 0, st, a);
+  else if (S == 2)
+    hipLaunchKernelGGL(knn_distogram_kernel<2>, dim3(blocks), dim3(64 * kKnnWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL(knn_distogram_kernel<4>, dim3(blocks), dim3(64 * kKnnWaves), 0, st, a);
   return hipGetLastError();
 }
 

@@ -49,6 +49,10 @@ CASES = [
     ("one-residue", 2, 1, 8, dict(frames="gauss"), 5, 3, 3.0, "bf16"),
     ("n65-ragged-tail", 1, 65, 9, dict(frames="walk"), 20, 64, 16.0, "f32"),
     ("many-bins", 1, 200, 10, dict(frames="walk", step=3.8), 16, 300, 30.0, "f32"),
+    # small grids split each group's candidate walk over 2 or 4 wavefronts
+    ("rna-2048-split4", 1, 2048, 12, dict(frames="walk", step=6.0), 20, 20, 20.0, "f32"),
+    ("lattice-2048-split4", 1, 2048, 13, dict(frames="lattice", box=4, dropout=0.1), 20, 9, 4.5, "bf16"),
+    ("gauss-4096-split2", 1, 4096, 14, dict(frames="gauss", trans_sigma=25.0, dropout=0.02), 32, 20, 40.0, "f32"),
 ]
 
 
