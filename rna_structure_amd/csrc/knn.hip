@@ -75,36 +75,6 @@ __device__ __forceinline__ float sqdist(float x, float y, float z, float qx, flo
   return (dx * dx + dy * dy) + dz * dz;
 }
 
-// k-th smallest (1 <= k <= 64) of the 64 lanes' values v[g] < 2^BITS, for
-// G value sets at once: the smallest T with #{v <= T} >= k, found bit by bit
-// from the top with one ballot per bit and set (the G searches are
-// independent, so their ballots overlap).  Wave-uniform results.
-template <int BITS>
-__device__ __forceinline__ void kth_smallest(const uint32_t (&v)[kKnnG], int k, uint32_t (&res)[kKnnG]) {
-#pragma unroll
-  for (int g = 0; g < kKnnG; ++g) res[g] = 0;
-#pragma unroll
-  for (int bit = BITS - 1; bit >= 0; --bit) {
-    // all G ballots first, then the scalar updates: the vector compares and
-    // the scalar counts of different sets overlap
-    uint64_t bl[kKnnG];
-#pragma unroll
-    for (int g = 0; g < kKnnG; ++g) bl[g] = __ballot(v[g] <= (res[g] | ((1u << bit) - 1u)));
-#pragma unroll
-    for (int g = 0; g < kKnnG; ++g)
-      if (__popcll(bl[g]) < k) res[g] |= 1u << bit;
-  }
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t w = (uint32_t)__shfl_xor((int)v, o);
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
 // Keeps the (at most k) smallest candidate keys of buf[0..n), n <= 256,
 // sorted at buf[0..); returns how many were kept (wave-uniform).  Every lane
 // ranks its (up to four) entries against all n keys, read as broadcasts.
@@ -121,9 +91,18 @@ __device__ __forceinline__ int select_topk(uint64_t* buf, int n, int k, int lane
     rank[r] = 0;
   }
   const uint4* b4 = reinterpret_cast<const uint4*>(buf);
-  if (n <= 64) {
-    // one entry per lane: entries n..63 become dead keys (they rank nothing),
-    // then all 64 broadcasts are in flight at once
+  if (n <= 32) {
+    // one entry per lane: entries n..31 become dead keys (they rank nothing),
+    // then all 32 broadcasts are in flight at once
+    if (lane >= n && lane < 32) buf[lane] = kDeadKey;
+    wave_sync();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint4 w = b4[q];
+      rank[0] += (((uint64_t)w.y << 32) | w.x) < ke[0] ? 1 : 0;
+      rank[0] += (((uint64_t)w.w << 32) | w.z) < ke[0] ? 1 : 0;
+    }
+  } else if (n <= 64) {
     if (lane >= n) buf[lane] = kDeadKey;
     wave_sync();
 #pragma unroll
@@ -253,22 +232,40 @@ __global__ __launch_bounds__(256) void knn_distogram_kernel(KnnArgs a) {
     // Per query: tau = the k-th smallest d2 among the window's candidates
     // (+inf when it holds fewer than k), rounded up to the top 12 bits of its
     // encoding (exponent and 4 mantissa bits: at most 1/16 above): an upper
-    // bound of the final k-th d2.
+    // bound of the final k-th d2.  The 8 x 64 keys go through this wave's
+    // part of the output-bin area so that 16 lanes serve each query (4 keys
+    // per lane, two passes of 4 queries); counts are summed over the 16 lanes
+    // of a row with DPP.
     constexpr int kLow = 19;
-    uint32_t v[kKnnG], t[kKnnG];
+    uint32_t* sv = reinterpret_cast<uint32_t*>(&s_bin[wl][0]);
 #pragma unroll
     for (int g = 0; g < kKnnG; ++g) {
       const float4 q = s_q[wl][g];
       const float d2 = sqdist(x, y, z, q.x, q.y, q.z);
-      v[g] = __float_as_uint((j == i0 + g || d2 != d2) ? inf : d2) >> kLow;
+      sv[g * 64 + lane] = __float_as_uint((j == i0 + g || d2 != d2) ? inf : d2) >> kLow;
     }
-    kth_smallest<31 - kLow>(v, k, t);
-    uint32_t tl = 0;
+    wave_sync();
+    const int row = lane >> 4, part = lane & 15;
 #pragma unroll
-    for (int g = 0; g < kKnnG; ++g) tl = lane == g ? t[g] : tl;
-    tl = (tl << kLow) | ((1u << kLow) - 1u);
-    if (tl >= 0x7f800000u) tl = 0x7f800000u;  // an infinite k-th value stays +inf
-    if (lane < kKnnG && ((act >> lane) & 1u)) s_tau[wl][lane] = __uint_as_float(tl);
+    for (int pass = 0; pass < 2; ++pass) {
+      const int g = pass * 4 + row;
+      const uint4 w = *reinterpret_cast<const uint4*>(&sv[g * 64 + part * 4]);
+      uint32_t res = 0;
+#pragma unroll
+      for (int bit = 30 - kLow; bit >= 0; --bit) {
+        const uint32_t lo = res | ((1u << bit) - 1u);
+        int c = (w.x <= lo ? 1 : 0) + (w.y <= lo ? 1 : 0) + (w.z <= lo ? 1 : 0) + (w.w <= lo ? 1 : 0);
+        c += __builtin_amdgcn_update_dpp(0, c, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+        c += __builtin_amdgcn_update_dpp(0, c, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+        c += __builtin_amdgcn_update_dpp(0, c, 0x124, 0xF, 0xF, false);  // row_ror:4
+        c += __builtin_amdgcn_update_dpp(0, c, 0x128, 0xF, 0xF, false);  // row_ror:8 -> row total
+        res = c < k ? (res | (1u << bit)) : res;
+      }
+      uint32_t tl = (res << kLow) | ((1u << kLow) - 1u);
+      if (tl >= 0x7f800000u) tl = 0x7f800000u;  // an infinite k-th value stays +inf
+      if (part == 0 && ((act >> g) & 1u)) s_tau[wl][g] = __uint_as_float(tl);
+    }
+    wave_sync();
   }
 
   if (live) {
@@ -321,38 +318,44 @@ __global__ __launch_bounds__(256) void knn_distogram_kernel(KnnArgs a) {
         wave_sync();
       }
     }
-    // This split's best k of every query, in order.
+  }
+  // Final lists.  S = 1: one selection per query.  S > 1: split s takes the
+  // queries g with g % S == s and gathers the other splits' buffers behind
+  // its own (first cutting every buffer to its best k if they would not fit)
+  // before one selection.
+  if constexpr (S > 1) __syncthreads();
+  if (live) {
     wave_sync();
 #pragma unroll 1
-    for (int g = 0; g < kKnnG; ++g) {
+    for (int g = split; g < kKnnG; g += S) {
       if (!((act >> g) & 1u)) continue;
-      const int n = select_topk(&s_buf[wl][g][0], __builtin_amdgcn_readfirstlane(s_cnt[wl][g]), k, lane);
-      if (lane == 0) s_cnt[wl][g] = n;
-    }
-  }
-  if constexpr (S > 1) {
-    // Merge: split s takes the queries g with g % S == s and gathers the
-    // other splits' best k behind its own before a last selection.
-    __syncthreads();
-    if (live) {
-#pragma unroll 1
-      for (int g = split; g < kKnnG; g += S) {
-        if (!((act >> g) & 1u)) continue;
-        uint64_t* buf = &s_buf[wl][g][0];
-        int n = __builtin_amdgcn_readfirstlane(s_cnt[wl][g]);
+      uint64_t* buf = &s_buf[wl][g][0];
+      int n = __builtin_amdgcn_readfirstlane(s_cnt[wl][g]);
+      if (S > 1) {
+        int tot = n;
+        for (int o = 1; o < S; ++o) tot += __builtin_amdgcn_readfirstlane(s_cnt[gl * S + (split + o) % S][g]);
+        if (tot > kKnnCap) {
+          n = select_topk(buf, n, k, lane);
+          for (int o = 1; o < S; ++o) {
+            const int src = gl * S + (split + o) % S;
+            const int ns = select_topk(&s_buf[src][g][0], __builtin_amdgcn_readfirstlane(s_cnt[src][g]), k, lane);
+            if (lane == 0) s_cnt[src][g] = ns;
+          }
+          wave_sync();
+        }
         for (int o = 1; o < S; ++o) {
           const int src = gl * S + (split + o) % S;
           const int no = __builtin_amdgcn_readfirstlane(s_cnt[src][g]);
-          if (lane < no) buf[n + lane] = s_buf[src][g][lane];
+          for (int e = lane; e < no; e += 64) buf[n + e] = s_buf[src][g][e];
           n += no;
         }
         wave_sync();
-        n = select_topk(buf, n, k, lane);
-        if (lane == 0) s_cnt[wl][g] = n;
       }
+      n = select_topk(buf, n, k, lane);
+      if (lane == 0) s_cnt[wl][g] = n;
     }
-    __syncthreads();
   }
+  if constexpr (S > 1) __syncthreads();
   if (!live) return;
   wave_sync();
 
