@@ -1,0 +1,98 @@
+"""Gradients of the IPA forward: a plain PyTorch float64 restatement of the
+forward definition on the CPU, differentiated by autograd.
+
+TEST INFRASTRUCTURE ONLY.  This file is imported by tests/, by
+__graft_entry__.smoke() and by the cpu_baseline leg of bench.py, and by
+nothing else.  It shares no code with the HIP library and does not import it.
+
+The forward restated here is the aggregation core of the "Invariant point
+attention (IPA)" problem page (biotorch), section "Required behavior", with
+the pair representation given as rank-R factors (FlashIPA rebuttal, paperhub
+page, answers to Q4 and Q5): z_ij[c] = sum_r zl[i,r,c] zr[j,r,c], per-head
+pair bias sum_c w_pair[h,c] z_ij[c], pair values z.  The page's starter code
+states that its test suite grades gradients; the readings for them are:
+
+  * the scalar loss is <update, d_update> + <local_points, d_local_points>,
+    i.e. d_update and d_local_points are the upstream gradients;
+  * rotation is differentiated as a free 3x3 matrix (the formula uses R and
+    R^T linearly; no projection onto SO(3));
+  * masks and the pair mask are not differentiable; an empty neighbourhood
+    passes no gradient (its outputs are constants);
+  * the stable-softmax shift is a constant (the softmax does not depend on
+    it).
+
+Pinned by tests/test_backward_oracle.py: the forward equals the NumPy oracle
+(oracle/ipa_oracle.py), every gradient equals central finite differences on
+tiny inputs, gradients transform correctly under a common rigid motion of
+the frames, and with the point and pair terms switched off the q/k/v
+gradients equal those of torch's scaled_dot_product_attention.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+GRAD_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "translation",
+             "point_weight_raw", "w_pair", "zl", "zr", "w_out", "b_out")
+
+
+def ipa_forward_torch(t: dict, mask: torch.Tensor, pair_mask, eps: float = 1e-8) -> dict:
+    """The forward on float64 tensors t[key] for key in GRAD_KEYS; mask [B,N]
+    bool, pair_mask [B,N,N] bool or None.  Returns update [B,N,Cout] and
+    local_points [B,N,H,Q,3]."""
+    q, k, v = t["q"], t["k"], t["v"]
+    B, N, H, D = q.shape
+    P = t["q_points"].shape[3]
+    R = t["rotation"]
+    tr = t["translation"]
+
+    def to_global(x):                                   # T_i(x) = R_i @ x + t_i
+        return torch.einsum("bnxy,bnhpy->bnhpx", R, x) + tr[:, :, None, None, :]
+
+    Xq, Xk, Xv = to_global(t["q_points"]), to_global(t["k_points"]), to_global(t["v_points"])
+    z = torch.einsum("birc,bjrc->bijc", t["zl"], t["zr"])               # [B,N,N,Cz]
+    pair_bias = torch.einsum("bijc,hc->bhij", z, t["w_pair"])
+    scalar = torch.einsum("bihd,bjhd->bhij", q, k) / math.sqrt(3.0 * D)
+    diff = Xq[:, :, None] - Xk[:, None, :]                               # [B,N,N,H,P,3]
+    dist = (diff * diff).sum(dim=(-1, -2)).permute(0, 3, 1, 2)           # [B,H,N,N]
+    gamma = 0.5 * torch.nn.functional.softplus(t["point_weight_raw"]) * math.sqrt(2.0 / (27.0 * P))
+    logits = scalar + pair_bias / math.sqrt(3.0) - gamma[None, :, None, None] * dist
+
+    permitted = mask[:, :, None] & mask[:, None, :]
+    if pair_mask is not None:
+        permitted = permitted & pair_mask
+    perm_h = permitted[:, None].expand_as(logits)
+    empty = ~permitted.any(dim=-1)                                        # [B,N]
+    shift = torch.where(perm_h, logits, torch.full_like(logits, -math.inf)).amax(dim=-1, keepdim=True)
+    shift = torch.where(torch.isfinite(shift), shift, torch.zeros_like(shift)).detach()
+    e = torch.exp(torch.where(perm_h, logits - shift, torch.full_like(logits, -math.inf)))
+    s = e.sum(dim=-1, keepdim=True)
+    attention = e / torch.where(s > 0, s, torch.ones_like(s))
+
+    o_scalar = torch.einsum("bhij,bjhd->bihd", attention, v)
+    o_pair = torch.einsum("bhij,bijc->bihc", attention, z)
+    g = torch.einsum("bhij,bjhqx->bihqx", attention, Xv)
+    local = torch.einsum("biyx,bihqy->bihqx", R, g - tr[:, :, None, None, :])
+    keep = (~empty)[:, :, None, None, None].to(local.dtype)
+    local = local * keep
+    length = torch.sqrt((local * local).sum(-1) + eps) * keep[..., 0]
+    features = torch.cat([o_scalar.reshape(B, N, -1), local[..., 0].reshape(B, N, -1),
+                          local[..., 1].reshape(B, N, -1), local[..., 2].reshape(B, N, -1),
+                          length.reshape(B, N, -1), o_pair.reshape(B, N, -1)], dim=-1)
+    update = (features @ t["w_out"] + t["b_out"]) * (~empty)[:, :, None].to(features.dtype)
+    return dict(update=update, local_points=local)
+
+
+def ipa_gradients(inp: dict, d_update, d_local, keys=GRAD_KEYS) -> dict:
+    """Gradients (float64 NumPy) of <update, d_update> + <local_points, d_local>
+    with respect to the inputs of a synth.make_inputs() set."""
+    t = {key: torch.tensor(inp[key], dtype=torch.float64, requires_grad=key in keys) for key in GRAD_KEYS}
+    mask = torch.tensor(inp["mask"], dtype=torch.bool)
+    pm = inp.get("pair_mask")
+    pm = None if pm is None else torch.tensor(pm, dtype=torch.bool)
+    out = ipa_forward_torch(t, mask, pm, inp["eps"])
+    loss = (out["update"] * torch.tensor(d_update, dtype=torch.float64)).sum() + \
+           (out["local_points"] * torch.tensor(d_local, dtype=torch.float64)).sum()
+    loss.backward()
+    return {key: t[key].grad.numpy() for key in keys}
