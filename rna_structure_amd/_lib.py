@@ -20,7 +20,10 @@ IPA_F32, IPA_BF16 = 0, 1
 STATUS = {0: "IPA_OK", 1: "IPA_ERR_NULL", 2: "IPA_ERR_SHAPE", 3: "IPA_ERR_UNSUPPORTED",
           4: "IPA_ERR_ALIGN", 5: "IPA_ERR_LAUNCH", 6: "IPA_ERR_DEVICE"}
 EXPORTS = ("ipa_lifted_bytes", "ipa_o_width", "ipa_lift", "ipa_flash_fwd", "ipa_epilogue",
-           "ipa_logit_rows", "ipa_knn_distogram", "ipa_status_string", "ipa_version")
+           "ipa_logit_rows", "ipa_backward_workspace_bytes", "ipa_backward", "ipa_knn_distogram",
+           "ipa_status_string", "ipa_version")
+GRAD_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "translation",
+             "point_weight_raw", "w_pair", "zl", "zr", "w_out", "b_out")
 
 
 class IpaShape(ctypes.Structure):
@@ -36,6 +39,10 @@ class IpaLiftIn(ctypes.Structure):
 
 class IpaEpiIn(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("zl", "rotation", "translation", "w_out", "b_out")]
+
+
+class IpaGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_KEYS]
 
 
 class IpaKnnShape(ctypes.Structure):
@@ -74,6 +81,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipa_epilogue.restype = ctypes.c_int
     lib.ipa_logit_rows.argtypes = [sp, vp, i64, i64, i64, i64, vp, vp]
     lib.ipa_logit_rows.restype = ctypes.c_int
+    lib.ipa_backward_workspace_bytes.argtypes = [sp]
+    lib.ipa_backward_workspace_bytes.restype = sz
+    lib.ipa_backward.argtypes = [sp, ctypes.POINTER(IpaLiftIn), ctypes.POINTER(IpaEpiIn), vp, vp, vp, sz,
+                                 ctypes.POINTER(IpaGrads), vp]
+    lib.ipa_backward.restype = ctypes.c_int
     lib.ipa_knn_distogram.argtypes = [ctypes.POINTER(IpaKnnShape), vp, vp, vp, vp, vp, vp]
     lib.ipa_knn_distogram.restype = ctypes.c_int
     lib.ipa_status_string.argtypes = [ctypes.c_int]
@@ -143,6 +155,49 @@ def ipa_knn_distogram(s: IpaKnnShape, translation, mask, nn_index, nn_dist=None,
     _check("ipa_knn_distogram", load().ipa_knn_distogram(ctypes.byref(s), _ptr(translation), _ptr(mask),
                                                          _ptr(nn_index), _ptr(nn_dist), _ptr(dgram),
                                                          _stream(stream)))
+
+
+def backward_workspace_bytes(s: IpaShape) -> int:
+    return int(load().ipa_backward_workspace_bytes(ctypes.byref(s)))
+
+
+def ipa_backward(s: IpaShape, t: dict, d_update, d_local, workspace, grads: dict, stream=None):
+    lib = load()
+    li = IpaLiftIn(*[_ptr(t.get(n)) for n in ("q", "k", "v", "q_points", "k_points", "v_points", "rotation",
+                                              "translation", "point_weight_raw", "w_pair", "zl", "zr",
+                                              "mask", "pair_mask")])
+    ei = IpaEpiIn(*[_ptr(t[n]) for n in ("zl", "rotation", "translation", "w_out", "b_out")])
+    gr = IpaGrads(*[_ptr(grads[n]) for n in GRAD_KEYS])
+    _check("ipa_backward", lib.ipa_backward(ctypes.byref(s), ctypes.byref(li), ctypes.byref(ei), _ptr(d_update),
+                                            _ptr(d_local), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            ctypes.byref(gr), _stream(stream)))
+
+
+class IPABackward:
+    """Workspace, gradient buffers and the backward call for a fixed fp32 shape.
+
+    t are fp32 device inputs (device_inputs of an 'f32' input set); every call
+    rewrites the gradient tensors, each shaped like its input."""
+
+    def __init__(self, shape, eps: float = 1e-8, device="cuda"):
+        import torch
+        load()
+        if shape.dtype != "f32":
+            raise ValueError("the backward runs on fp32 inputs")
+        self.shape = shape
+        self.s = make_shape(shape, eps)
+        nbytes = backward_workspace_bytes(self.s)
+        if nbytes == 0:
+            raise IPAError("ipa_backward_workspace_bytes", 3)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.grads = None
+
+    def __call__(self, t: dict, d_update, d_local, stream=None) -> dict:
+        import torch
+        if self.grads is None:
+            self.grads = {n: torch.empty_like(t[n], dtype=torch.float32) for n in GRAD_KEYS}
+        ipa_backward(self.s, t, d_update, d_local, self.ws, self.grads, stream)
+        return self.grads
 
 
 class KnnDistogram:

@@ -16,6 +16,9 @@ hipError_t launch_logit_rows(const Layout& L, const void* ws, int b, int h, int 
                              hipStream_t st);
 hipError_t launch_knn(const ipa_knn_shape* s, const float* t, const uint8_t* mask, int32_t* idx, float* dist,
                       void* dgram, hipStream_t st);
+size_t bw_workspace_bytes(const ipa_shape* s);
+hipError_t launch_backward(const ipa_shape* s, const ipa_lift_in* in, const ipa_epi_in* ep, const float* dupd,
+                           const float* dloc, void* ws, ipa_grads* gr, hipStream_t st);
 }  // namespace fipa
 
 using fipa::Layout;
@@ -106,6 +109,44 @@ ipa_status ipa_logit_rows(const ipa_shape* s, const void* lifted, int64_t b, int
   if (!aligned16(lifted) || !aligned16(out)) return IPA_ERR_ALIGN;
   return launch_status(fipa::launch_logit_rows(L, lifted, (int)b, (int)h, (int)row0, (int)nrows, out,
                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+static ipa_status bw_shape_status(const ipa_shape* s) {
+  if (!s) return IPA_ERR_NULL;
+  if (s->B <= 0 || s->N <= 0 || s->H <= 0 || s->D <= 0 || s->Dv <= 0 || s->P <= 0 || s->Q <= 0 || s->Cz <= 0 ||
+      s->R <= 0 || s->Cout <= 0 || !(s->eps > 0.0f))
+    return IPA_ERR_SHAPE;
+  if (s->dtype != IPA_F32) return IPA_ERR_UNSUPPORTED;
+  if (s->N > (1 << 26) || s->B * s->N > (1 << 28) || s->H > 1024 || s->Cout > (1 << 16)) return IPA_ERR_UNSUPPORTED;
+  return fipa::bw_workspace_bytes(s) ? IPA_OK : IPA_ERR_UNSUPPORTED;
+}
+
+size_t ipa_backward_workspace_bytes(const ipa_shape* s) {
+  if (bw_shape_status(s) != IPA_OK) return 0;
+  return fipa::bw_workspace_bytes(s);
+}
+
+ipa_status ipa_backward(const ipa_shape* s, const ipa_lift_in* in, const ipa_epi_in* epi, const float* d_update,
+                        const float* d_local, void* workspace, size_t workspace_bytes, ipa_grads* g, void* stream) {
+  if (!s || !in || !epi || !d_update || !d_local || !workspace || !g) return IPA_ERR_NULL;
+  const ipa_status st = bw_shape_status(s);
+  if (st != IPA_OK) return st;
+  const size_t need = fipa::bw_workspace_bytes(s);
+  const void* req[] = {in->q, in->k, in->v, in->q_points, in->k_points, in->v_points, in->rotation,
+                       in->translation, in->point_weight_raw, in->w_pair, in->zl, in->zr, in->mask,
+                       epi->w_out, epi->b_out, g->q, g->k, g->v, g->q_points, g->k_points, g->v_points,
+                       g->rotation, g->translation, g->point_weight_raw, g->w_pair, g->zl, g->zr, g->w_out,
+                       g->b_out};
+  for (const void* p : req)
+    if (!p) return IPA_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return IPA_ERR_ALIGN;
+  if (!aligned16(d_update) || !aligned16(d_local) || !aligned16(workspace) ||
+      (in->pair_mask && !aligned16(in->pair_mask)))
+    return IPA_ERR_ALIGN;
+  if (workspace_bytes < need) return IPA_ERR_SHAPE;
+  return launch_status(
+      fipa::launch_backward(s, in, epi, d_update, d_local, workspace, g, (hipStream_t)stream));
 }
 
 ipa_status ipa_knn_distogram(const ipa_knn_shape* s, const float* translation, const uint8_t* mask,

@@ -147,3 +147,34 @@ def test_knn_validation_before_launch(lib):
     assert call(ks(), i=4104) == 4
     assert call(ks(), d=4104) == 4
     assert call(ks(), g=4104) == 4
+
+
+def test_backward_validation_before_launch(lib):
+    s = _shape(dtype="f32")
+    assert _lib.backward_workspace_bytes(s) > 0
+    assert _lib.backward_workspace_bytes(_shape(dtype="bf16")) == 0        # fp32 inputs only
+    assert _lib.backward_workspace_bytes(_shape(dtype="f32", P=6)) == 0     # 3P > 16
+    assert _lib.backward_workspace_bytes(_shape(dtype="f32", Cz=200)) == 0  # D + R Cz > 256
+    assert _lib.backward_workspace_bytes(_shape(dtype="f32", N=0)) == 0
+    # grows linearly with N (no N^2 array)
+    w1 = _lib.backward_workspace_bytes(_shape(dtype="f32", B=1, N=8192))
+    w2 = _lib.backward_workspace_bytes(_shape(dtype="f32", B=1, N=16384))
+    assert 1.9 < w2 / w1 < 2.1
+    fields = [n for n, _ in _lib.IpaLiftIn._fields_ if n != "pair_mask"]
+    li = _lib.IpaLiftIn(**{n: 4096 for n in fields})
+    ei = _lib.IpaEpiIn(4096, 4096, 4096, 4096, 4096)
+    gr = _lib.IpaGrads(*[4096] * len(_lib.GRAD_KEYS))
+    big = 1 << 40
+    call = lambda s, li=li, ei=ei, gr=gr, du=4096, ws=4096, n=big: lib.ipa_backward(
+        ctypes.byref(s), ctypes.byref(li), ctypes.byref(ei), du, 4096, ws, n, ctypes.byref(gr), None)
+    assert call(s, du=None) == 1
+    assert call(s, ws=None) == 1
+    gr0 = _lib.IpaGrads(*[4096] * len(_lib.GRAD_KEYS))
+    gr0.zr = None
+    assert call(s, gr=gr0) == 1
+    assert call(_shape(dtype="bf16")) == 3
+    assert call(_shape(dtype="f32", N=0)) == 2
+    gr1 = _lib.IpaGrads(*[4096] * len(_lib.GRAD_KEYS))
+    gr1.q = 4100
+    assert call(s, gr=gr1) == 4
+    assert call(s, n=16) == 2                                            # workspace too small

@@ -1,0 +1,85 @@
+"""GPU parity of the backward pass (ipa_backward, fp32): every input gradient
+against the float64 autograd oracle (oracle/ipa_backward.py) on the same
+seeded inputs and upstream gradients.  Tolerance: max-abs-rel 1e-4 per
+gradient tensor (max |gpu - ref| / max |ref|), the fp32 bar.  At a length the
+oracle cannot differentiate densely, properties that hold at any size are
+checked instead (a common translation or rotation of the frames changes
+nothing; d b_out is the sum of the upstream gradient over non-empty rows)."""
+import numpy as np
+import pytest
+
+from oracle.ipa_backward import GRAD_KEYS, ipa_gradients
+from rna_structure_amd.synth import IPAShape, make_inputs
+
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _upstream(shape, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((shape.B, shape.N, shape.Cout)).astype(np.float32),
+            rng.standard_normal((shape.B, shape.N, shape.H, shape.Q, 3)).astype(np.float32))
+
+
+def _run(inp, du, dl):
+    import torch
+    from rna_structure_amd import _lib
+    shape = inp["shape"]
+    t = _lib.device_inputs(inp, "cuda")
+    bw = _lib.IPABackward(shape, eps=inp["eps"])
+    g = bw(t, torch.from_numpy(du).cuda(), torch.from_numpy(dl).cuda())
+    torch.cuda.synchronize()
+    return {key: v.cpu().numpy().astype(np.float64) for key, v in g.items()}
+
+
+CASES = [
+    ("small-masks", IPAShape(B=2, N=37, H=3, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6, dtype="f32"), 1,
+     dict(frames="gauss", trans_sigma=3.0, masked_keys=(4,), pair_dropout=0.2, empty_row=True, lengths=(20, 37))),
+    ("standard-ragged", IPAShape(B=1, N=150, H=4, dtype="f32"), 2,
+     dict(frames="walk", step=3.8, masked_keys=(149,), pair_dropout=0.05)),
+    ("standard-n65", IPAShape(B=2, N=65, H=2, dtype="f32"), 3,
+     dict(frames="walk", step=3.8, lengths=(40, 65), empty_row=True)),
+    ("rank1-p5-q9", IPAShape(B=1, N=70, H=2, D=8, Dv=8, P=5, Q=9, Cz=48, R=1, Cout=64, dtype="f32"), 4,
+     dict(frames="gauss", trans_sigma=6.0)),
+    ("rank3", IPAShape(B=1, N=90, H=2, D=16, Dv=16, P=4, Q=8, Cz=64, R=3, Cout=128, dtype="f32"), 5,
+     dict(frames="walk", step=3.8, pair_dropout=0.1)),
+    ("one-residue", IPAShape(B=2, N=1, H=2, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6, dtype="f32"), 6,
+     dict(frames="gauss")),
+]
+
+
+@pytest.mark.parametrize("name,shape,seed,kw", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_autograd(name, shape, seed, kw):
+    say(f"case backward {name} {shape}")
+    inp = make_inputs(shape, seed, **kw)
+    du, dl = _upstream(shape, seed + 100)
+    got = _run(inp, du, dl)
+    ref = ipa_gradients(inp, du.astype(np.float64), dl.astype(np.float64))
+    errs = {}
+    for key in GRAD_KEYS:
+        scale = np.max(np.abs(ref[key]))
+        errs[key] = np.max(np.abs(got[key] - ref[key])) / scale if scale > 0 else np.max(np.abs(got[key]))
+    say("  max-abs-rel " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    for key, v in errs.items():
+        assert v <= 1e-4, (key, v)
+
+
+def test_backward_properties_at_length_4096():
+    """Standard dimensions, N=4096: the frame gradients obey the rigid-motion
+    invariance of the forward, db is the row sum of d_update, and the
+    gradients are finite."""
+    shape = IPAShape(B=1, N=4096, H=8, dtype="f32")
+    say(f"case backward properties {shape}")
+    inp = make_inputs(shape, 7, frames="walk", step=3.8, trans_sigma=10.0)
+    du, dl = _upstream(shape, 8)
+    g = _run(inp, du, dl)
+    for key in GRAD_KEYS:
+        assert np.all(np.isfinite(g[key])), key
+    dt = g["translation"][0]
+    assert np.max(np.abs(dt.sum(axis=0))) <= 1e-4 * np.sum(np.abs(dt)), "common translation"
+    R, t = inp["rotation"][0], inp["translation"][0]
+    M = np.einsum("nxy,nzy->xz", g["rotation"][0], R) + np.einsum("nx,nz->xz", dt, t)
+    scale = np.sum(np.abs(np.einsum("nxy,nzy->nxz", g["rotation"][0], R))) + np.sum(np.abs(np.einsum("nx,nz->nxz", dt, t)))
+    assert np.max(np.abs(M - M.T)) <= 1e-4 * scale, "common rotation"
+    np.testing.assert_allclose(g["b_out"], du[0].astype(np.float64).sum(axis=0), rtol=1e-5, atol=1e-3)
