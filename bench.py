@@ -192,6 +192,72 @@ def time_knn(name, B, N, kw, steps, k=20, nbins=20, dmax=20.0, min_warm_ms=40.0)
             "out_GBs": round(out_bytes / (ms * 1e-3) / 1e9, 1)}
 
 
+# Backward (fp32, vector ALU): algorithmic flops per (query, key, head) of the
+# attention core without recomputation -- logit 2 d_k + 9P, output 2 d_v,
+# dP 2 d_v, dQ and dK 2 d_k each, dV 2 d_v, point gradients 12P -- against the
+# unpacked fp32 FMA rate 256 CUs x 64 lanes x 2 x 2.4 GHz = 78.6 TFLOP/s.
+PEAK_FP32_FMA_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+BACKWARD_WORKLOADS = (
+    ("backward_rna_2048", 1, 2048, dict(frames="walk", step=6.0), 10),
+    ("backward_4096", 1, 4096, dict(frames="walk", step=3.8), 5),
+    ("backward_16384", 1, 16384, dict(frames="walk", step=3.8), 2),
+)
+
+
+def backward_flops(shape, mask) -> float:
+    import numpy as np
+    dk = shape.D + shape.R * shape.Cz
+    dv = shape.Dv + shape.R * shape.Cz + 3 * shape.Q
+    per_pair = 6 * dk + 6 * dv + 21 * shape.P
+    L = np.asarray(mask).sum(axis=1).astype(np.float64)
+    return float(shape.H * per_pair * np.sum(L * L))
+
+
+def time_backward(name, B, N, kw, steps, min_warm_ms=40.0):
+    import numpy as np
+    import torch
+    from rna_structure_amd import _lib
+    from rna_structure_amd.synth import IPAShape, make_inputs
+    shape = IPAShape(B=B, N=N, H=8, dtype="f32")
+    inp = make_inputs(shape, 8000 + N, **kw)
+    t = _lib.device_inputs(inp, "cuda")
+    rng = np.random.default_rng(N)
+    du = torch.from_numpy(rng.standard_normal((B, N, shape.Cout)).astype(np.float32)).cuda()
+    dl = torch.from_numpy(rng.standard_normal((B, N, shape.H, shape.Q, 3)).astype(np.float32)).cuda()
+    bw = _lib.IPABackward(shape, eps=inp["eps"])
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    warm = 0.0
+    while warm < min_warm_ms:
+        e0.record(st)
+        bw(t, du, dl)
+        e1.record(st)
+        torch.cuda.synchronize()
+        warm += e0.elapsed_time(e1)
+    e0.record(st)
+    for _ in range(steps):
+        bw(t, du, dl)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = backward_flops(shape, inp["mask"])
+    tf = fl / (ms * 1e-3) / 1e12
+    ws_mb = bw.ws.numel() / 2**20
+    del bw, t
+    torch.cuda.empty_cache()
+    return {"workload": name, "B": B, "N": N, "H": shape.H, "ms": round(ms, 3), "alu_tflops": round(tf, 2),
+            "alu_frac": round(tf / PEAK_FP32_FMA_TFLOPS, 4), "workspace_mb": round(ws_mb, 1)}
+
+
+def backward_section(args):
+    res = []
+    for name, B, N, kw, steps in BACKWARD_WORKLOADS:
+        res.append(time_backward(name, B, N, kw, steps))
+        print(f"# backward {res[-1]}", file=sys.stderr, flush=True)
+    return {"peak_fp32_fma_tflops": round(PEAK_FP32_FMA_TFLOPS, 1), "inputs": "fp32", "runs": res}
+
+
 def knn_cpu_baseline(N=16384, budget_s=3.0):
     """The kNN oracle on a sample of rows of the N-residue walk, scaled to all rows."""
     import numpy as np
@@ -301,6 +367,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-knn", action="store_true", help="skip the kNN distogram section")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward section")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="run only the backward section and print it as the JSON line")
     ap.add_argument("--knn-only", action="store_true",
                     help="run only the kNN distogram section and print it as the JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -322,6 +391,9 @@ def main():
         return
     if args.knn_only:
         print(json.dumps({"knn_distogram": knn_section(args)}), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps({"backward": backward_section(args)}), flush=True)
         return
     inp = make_workload(args.workload)
     shape = inp["shape"]
@@ -410,6 +482,8 @@ def main():
         out["rank_sweep"] = ranks
     if not args.no_sweep and not args.no_knn:
         out["knn_distogram"] = knn_section(args)
+    if not args.no_sweep and not args.no_backward:
+        out["backward"] = backward_section(args)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, flops)

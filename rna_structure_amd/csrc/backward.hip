@@ -32,7 +32,6 @@ namespace fipa {
 
 namespace {
 
-constexpr int kBwRows = 64;   // rows (queries or keys) per workgroup, 4 lanes each
 constexpr int kBwTile = 32;   // partner rows staged in LDS per step
 
 struct BwLayout {
@@ -40,7 +39,8 @@ struct BwLayout {
   int DK, DV, P3, NK4, NV4, DKp, DVp;
   int ksplit;
   size_t off_gam, off_qv, off_kv, off_vv, off_qa, off_kb, off_o, off_lse, off_do, off_dd, off_feat, off_dfeat,
-      off_dqv, off_dqa, off_dgam, off_dkv, off_dkb, off_dvv, off_dzle, off_dre, off_dte, off_dwpart, total;
+      off_dqv, off_dqa, off_dgam, off_dkv, off_dkb, off_dvv, off_dzle, off_dre, off_dte, off_dwpart, off_ppart,
+      total;
 };
 
 struct BwArgs {
@@ -189,8 +189,8 @@ __device__ __forceinline__ float logit_q(const float4 (&own)[NK4], const float* 
 }
 
 // Forward: per query, O and the natural-log lse over the permitted keys.
-template <int NK4, int NV4>
-__global__ __launch_bounds__(256) void bw_fwd_kernel(BwArgs a) {
+template <int NK4, int NV4, int ROWS>
+__global__ __launch_bounds__(4 * ROWS) void bw_fwd_kernel(BwArgs a) {
   const BwLayout& L = a.L;
   constexpr int KW = 16 * NK4, VW = 16 * NV4;
   __shared__ __align__(16) float sK[kBwTile][KW];
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void bw_fwd_kernel(BwArgs a) {
   __shared__ float sM[kBwTile];
   const int tid = threadIdx.x, part = tid & 3, r = tid >> 2;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int i = blockIdx.x * kBwRows + r;
+  const int i = blockIdx.x * ROWS + r;
   const bool qin = i < L.N;
   const int ic = qin ? i : L.N - 1;
   const size_t ri = rowidx(L, b, h, ic);
@@ -215,17 +215,17 @@ __global__ __launch_bounds__(256) void bw_fwd_kernel(BwArgs a) {
   const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + ic) * L.N : nullptr;
   for (int j0 = 0; j0 < L.N; j0 += kBwTile) {
     __syncthreads();
-    for (int e = tid; e < kBwTile * (KW / 4); e += 256) {
+    for (int e = tid; e < kBwTile * (KW / 4); e += 4 * ROWS) {
       const int jj = e / (KW / 4), c4 = e - jj * (KW / 4);
       const int j = min(j0 + jj, L.N - 1);
       reinterpret_cast<float4*>(&sK[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, j) * L.DKp)[c4];
     }
-    for (int e = tid; e < kBwTile * (VW / 4); e += 256) {
+    for (int e = tid; e < kBwTile * (VW / 4); e += 4 * ROWS) {
       const int jj = e / (VW / 4), c4 = e - jj * (VW / 4);
       const int j = min(j0 + jj, L.N - 1);
       reinterpret_cast<float4*>(&sV[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_vv) + rowidx(L, b, h, j) * L.DVp)[c4];
     }
-    for (int e = tid; e < kBwTile * 4; e += 256) {
+    for (int e = tid; e < kBwTile * 4; e += 4 * ROWS) {
       const int jj = e >> 2, c4 = e & 3;
       const int j = min(j0 + jj, L.N - 1);
       reinterpret_cast<float4*>(&sB[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_kb) + rowidx(L, b, h, j) * 16)[c4];
@@ -273,8 +273,8 @@ __global__ __launch_bounds__(256) void bw_fwd_kernel(BwArgs a) {
 }
 
 // dQ pass: per query, loop over all keys.
-template <int NK4, int NV4>
-__global__ __launch_bounds__(256) void bw_query_kernel(BwArgs a) {
+template <int NK4, int NV4, int ROWS>
+__global__ __launch_bounds__(4 * ROWS) void bw_query_kernel(BwArgs a) {
   const BwLayout& L = a.L;
   constexpr int KW = 16 * NK4, VW = 16 * NV4;
   __shared__ __align__(16) float sK[kBwTile][KW];
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void bw_query_kernel(BwArgs a) {
   __shared__ float sM[kBwTile];
   const int tid = threadIdx.x, part = tid & 3, r = tid >> 2;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int i = blockIdx.x * kBwRows + r;
+  const int i = blockIdx.x * ROWS + r;
   const bool qin = i < L.N;
   const int ic = qin ? i : L.N - 1;
   const size_t ri = rowidx(L, b, h, ic);
@@ -303,17 +303,17 @@ __global__ __launch_bounds__(256) void bw_query_kernel(BwArgs a) {
   const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + ic) * L.N : nullptr;
   for (int j0 = 0; j0 < L.N; j0 += kBwTile) {
     __syncthreads();
-    for (int e = tid; e < kBwTile * (KW / 4); e += 256) {
+    for (int e = tid; e < kBwTile * (KW / 4); e += 4 * ROWS) {
       const int jj = e / (KW / 4), c4 = e - jj * (KW / 4);
       const int j = min(j0 + jj, L.N - 1);
       reinterpret_cast<float4*>(&sK[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, j) * L.DKp)[c4];
     }
-    for (int e = tid; e < kBwTile * (VW / 4); e += 256) {
+    for (int e = tid; e < kBwTile * (VW / 4); e += 4 * ROWS) {
       const int jj = e / (VW / 4), c4 = e - jj * (VW / 4);
       const int j = min(j0 + jj, L.N - 1);
       reinterpret_cast<float4*>(&sV[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_vv) + rowidx(L, b, h, j) * L.DVp)[c4];
     }
-    for (int e = tid; e < kBwTile * 4; e += 256) {
+    for (int e = tid; e < kBwTile * 4; e += 4 * ROWS) {
       const int jj = e >> 2, c4 = e & 3;
       const int j = min(j0 + jj, L.N - 1);
       reinterpret_cast<float4*>(&sB[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_kb) + rowidx(L, b, h, j) * 16)[c4];
@@ -350,18 +350,18 @@ __global__ __launch_bounds__(256) void bw_query_kernel(BwArgs a) {
 }
 
 // dK / dV pass: per key, loop over all queries.
-template <int NK4, int NV4>
-__global__ __launch_bounds__(256) void bw_key_kernel(BwArgs a) {
+template <int NK4, int NV4, int ROWS>
+__global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
   const BwLayout& L = a.L;
   constexpr int KW = 16 * NK4, VW = 16 * NV4;
   __shared__ __align__(16) float sQ[kBwTile][KW];
   __shared__ __align__(16) float sA[kBwTile][16];
   __shared__ __align__(16) float sD[kBwTile][VW];
   __shared__ float sL[kBwTile], sS[kBwTile];
-  __shared__ uint8_t sPM[kBwTile][kBwRows];
+  __shared__ uint8_t sPM[kBwTile][ROWS];
   const int tid = threadIdx.x, part = tid & 3, r = tid >> 2;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int j = blockIdx.x * kBwRows + r;
+  const int j = blockIdx.x * ROWS + r;
   const bool kin = j < L.N;
   const int jc = kin ? j : L.N - 1;
   const size_t rj = rowidx(L, b, h, jc);
@@ -377,20 +377,20 @@ __global__ __launch_bounds__(256) void bw_key_kernel(BwArgs a) {
 #pragma unroll
   for (int u = 0; u < NV4; ++u) dv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 db = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int kbase = blockIdx.x * kBwRows;
+  const int kbase = blockIdx.x * ROWS;
   for (int i0 = 0; i0 < L.N; i0 += kBwTile) {
     __syncthreads();
-    for (int e = tid; e < kBwTile * (KW / 4); e += 256) {
+    for (int e = tid; e < kBwTile * (KW / 4); e += 4 * ROWS) {
       const int ii = e / (KW / 4), c4 = e - ii * (KW / 4);
       const int i = min(i0 + ii, L.N - 1);
       reinterpret_cast<float4*>(&sQ[ii][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_qv) + rowidx(L, b, h, i) * L.DKp)[c4];
     }
-    for (int e = tid; e < kBwTile * (VW / 4); e += 256) {
+    for (int e = tid; e < kBwTile * (VW / 4); e += 4 * ROWS) {
       const int ii = e / (VW / 4), c4 = e - ii * (VW / 4);
       const int i = min(i0 + ii, L.N - 1);
       reinterpret_cast<float4*>(&sD[ii][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_do) + rowidx(L, b, h, i) * L.DVp)[c4];
     }
-    for (int e = tid; e < kBwTile * 4; e += 256) {
+    for (int e = tid; e < kBwTile * 4; e += 4 * ROWS) {
       const int ii = e >> 2, c4 = e & 3;
       const int i = min(i0 + ii, L.N - 1);
       reinterpret_cast<float4*>(&sA[ii][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_qa) + rowidx(L, b, h, i) * 16)[c4];
@@ -403,8 +403,8 @@ __global__ __launch_bounds__(256) void bw_key_kernel(BwArgs a) {
       sL[tid] = ok ? lse : INFINITY;  // +inf marks a query that takes no key
       sS[tid] = wsf(a, L.off_dd)[rowidx(L, b, h, icl)];
     }
-    for (int e = tid; e < kBwTile * kBwRows; e += 256) {
-      const int ii = e / kBwRows, jj = e - ii * kBwRows;
+    for (int e = tid; e < kBwTile * ROWS; e += 4 * ROWS) {
+      const int ii = e / ROWS, jj = e - ii * ROWS;
       const int i = min(i0 + ii, L.N - 1), jn = min(kbase + jj, L.N - 1);
       sPM[ii][jj] = a.pmask ? a.pmask[((size_t)b * L.N + i) * L.N + jn] : (uint8_t)1;
     }
@@ -668,20 +668,25 @@ __global__ __launch_bounds__(64) void bw_inputs_kernel(BwArgs a) {
 }
 
 // Per-head parameters: dw_pair[h][c] = sum_{b,i,r} zl[b,i,r,c] dQV[b,h,i,D+rCz+c] / sqrt(3)
-// and dgamma[h] = sum_{b,i} dgam[b,h,i] -> d point_weight_raw.  One workgroup
-// per head, threads over c, then over rows in four groups.
-__global__ __launch_bounds__(256) void bw_params_kernel(BwArgs a) {
+// and dgamma[h] = sum_{b,i} dgam[b,h,i] -> d point_weight_raw.  Stage 1: one
+// workgroup per (head, chunk of rows) writes partial sums; stage 2 adds the
+// chunks of a head.
+constexpr int kBwParamChunks = 64;
+
+__global__ __launch_bounds__(256) void bw_params_part_kernel(BwArgs a) {
   const BwLayout& L = a.L;
-  const int h = blockIdx.x;
+  const int h = blockIdx.x, ch = blockIdx.y;
   const int tid = threadIdx.x;
   const int BN = L.B * L.N, Cz = L.Cz, R = L.R, D = L.D;
-  const float s3 = 1.0f / sqrtf(3.0f);
+  const int per = (BN + kBwParamChunks - 1) / kBwParamChunks;
+  const int r0 = ch * per, r1 = min(BN, r0 + per);
+  float* part = wsf(a, L.off_ppart) + ((size_t)h * kBwParamChunks + ch) * (Cz + 1);
   __shared__ float red[256];
   for (int c0 = 0; c0 < Cz; c0 += 64) {
     const int c = c0 + (tid & 63), grp = tid >> 6;
     float s = 0.f;
     if (c < Cz) {
-      for (int bn = grp; bn < BN; bn += 4) {
+      for (int bn = r0 + grp; bn < r1; bn += 4) {
         const int b = bn / L.N, n = bn - b * L.N;
         const size_t ri = rowidx(L, b, h, n);
         for (int r = 0; r < R; ++r)
@@ -690,11 +695,11 @@ __global__ __launch_bounds__(256) void bw_params_kernel(BwArgs a) {
     }
     red[tid] = s;
     __syncthreads();
-    if (tid < 64 && c < Cz) a.gwpair[h * Cz + c] = (red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192]) * s3;
+    if (tid < 64 && c < Cz) part[c] = red[tid] + red[tid + 64] + red[tid + 128] + red[tid + 192];
     __syncthreads();
   }
   float s = 0.f;
-  for (int bn = tid; bn < BN; bn += 256) {
+  for (int bn = r0 + tid; bn < r1; bn += 256) {
     const int b = bn / L.N, n = bn - b * L.N;
     s += wsf(a, L.off_dgam)[rowidx(L, b, h, n)];
   }
@@ -704,10 +709,25 @@ __global__ __launch_bounds__(256) void bw_params_kernel(BwArgs a) {
     if (tid < o) red[tid] += red[tid + o];
     __syncthreads();
   }
-  if (tid == 0) {
-    const float w = a.wraw[h];
-    const float sig = 1.f / (1.f + expf(-w));
-    a.gwraw[h] = red[0] * 0.5f * sig * sqrtf(2.0f / (27.0f * (float)L.P));
+  if (tid == 0) part[Cz] = red[0];
+}
+
+__global__ __launch_bounds__(256) void bw_params_kernel(BwArgs a) {
+  const BwLayout& L = a.L;
+  const int h = blockIdx.x;
+  const int Cz = L.Cz;
+  const float s3 = 1.0f / sqrtf(3.0f);
+  const float* part = wsf(a, L.off_ppart) + (size_t)h * kBwParamChunks * (Cz + 1);
+  for (int c = threadIdx.x; c <= Cz; c += 256) {
+    float s = 0.f;
+    for (int ch = 0; ch < kBwParamChunks; ++ch) s += part[(size_t)ch * (Cz + 1) + c];
+    if (c < Cz) {
+      a.gwpair[h * Cz + c] = s * s3;
+    } else {
+      const float w = a.wraw[h];
+      const float sig = 1.f / (1.f + expf(-w));
+      a.gwraw[h] = s * 0.5f * sig * sqrtf(2.0f / (27.0f * (float)L.P));
+    }
   }
 }
 
@@ -716,14 +736,22 @@ struct BwInst {
 };
 constexpr BwInst kBwInst[] = {{1, 2}, {4, 4}, {9, 11}, {16, 16}};
 
+template <int NK4, int NV4, int ROWS>
+hipError_t launch_pairs_rows(const BwArgs& a, int which, hipStream_t st) {
+  const BwLayout& L = a.L;
+  dim3 grid((L.N + ROWS - 1) / ROWS, L.H, L.B);
+  if (which == 0) hipLaunchKernelGGL((bw_fwd_kernel<NK4, NV4, ROWS>), grid, dim3(4 * ROWS), 0, st, a);
+  if (which == 1) hipLaunchKernelGGL((bw_query_kernel<NK4, NV4, ROWS>), grid, dim3(4 * ROWS), 0, st, a);
+  if (which == 2) hipLaunchKernelGGL((bw_key_kernel<NK4, NV4, ROWS>), grid, dim3(4 * ROWS), 0, st, a);
+  return hipGetLastError();
+}
+
+// 64 rows (256 threads) per workgroup.  (32-row workgroups for small grids
+// were measured slower: the staging per row doubles and the key pass is held
+// to one wavefront per SIMD by its registers either way.)
 template <int NK4, int NV4>
 hipError_t launch_pairs(const BwArgs& a, int which, hipStream_t st) {
-  const BwLayout& L = a.L;
-  dim3 grid((L.N + kBwRows - 1) / kBwRows, L.H, L.B);
-  if (which == 0) hipLaunchKernelGGL((bw_fwd_kernel<NK4, NV4>), grid, dim3(256), 0, st, a);
-  if (which == 1) hipLaunchKernelGGL((bw_query_kernel<NK4, NV4>), grid, dim3(256), 0, st, a);
-  if (which == 2) hipLaunchKernelGGL((bw_key_kernel<NK4, NV4>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch_pairs_rows<NK4, NV4, 64>(a, which, st);
 }
 
 hipError_t launch_pairs_inst(const BwArgs& a, int which, hipStream_t st) {
@@ -799,6 +827,7 @@ bool bw_layout(const ipa_shape* s, BwLayout* L) {
   L->off_dre = take(bn * 9);
   L->off_dte = take(bn * 3);
   L->off_dwpart = take((size_t)L->ksplit * (L->F + 1) * L->Cout);
+  L->off_ppart = take((size_t)L->H * kBwParamChunks * (L->Cz + 1));
   L->total = off;
   return true;
 }
@@ -872,6 +901,8 @@ hipError_t launch_backward(const ipa_shape* s, const ipa_lift_in* in, const ipa_
   if ((e = launch_pairs_inst(a, 1, st)) != hipSuccess) return e;
   if ((e = launch_pairs_inst(a, 2, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(bw_inputs_kernel, dim3((BN + 63) / 64), dim3(64), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bw_params_part_kernel, dim3(L.H, kBwParamChunks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bw_params_kernel, dim3(L.H), dim3(256), 0, st, a);
   return hipGetLastError();
