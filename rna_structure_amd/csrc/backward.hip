@@ -612,59 +612,85 @@ __global__ __launch_bounds__(64) void bw_epi_kernel(BwArgs a) {
 }
 
 // ------------------------------------------------------------------ input gradients
-// One thread per (b, residue): frames, points, q/k/v, factors.
+// One wavefront per (b, residue): q/k/v, frames, points, factors.  A global
+// point gradient g of local point x gives d x = R^T g, dR += g x^T, dt += g.
 __global__ __launch_bounds__(64) void bw_inputs_kernel(BwArgs a) {
   const BwLayout& L = a.L;
-  const int bn = blockIdx.x * 64 + threadIdx.x;
-  if (bn >= L.B * L.N) return;
+  const int bn = blockIdx.x, lane = threadIdx.x;
   const int b = bn / L.N, n = bn - b * L.N;
   const int H = L.H, D = L.D, Dv = L.Dv, P = L.P, Q = L.Q, Cz = L.Cz, R = L.R;
   const float* Rm = a.rot + (size_t)bn * 9;
   const float sq = 1.0f / sqrtf(3.0f * (float)D), s3 = 1.0f / sqrtf(3.0f);
-  float dr[9], dt[3];
-  for (int e = 0; e < 9; ++e) dr[e] = wsf(a, L.off_dre)[(size_t)bn * 9 + e];
-  for (int e = 0; e < 3; ++e) dt[e] = wsf(a, L.off_dte)[(size_t)bn * 3 + e];
-  // global-point gradient g (3) of local point x (3): d x = R^T g, dR += g x^T, dt += g
-  auto point = [&](const float* g, const float* x, float* dx) {
-    for (int c = 0; c < 3; ++c) dx[c] = Rm[0 * 3 + c] * g[0] + Rm[1 * 3 + c] * g[1] + Rm[2 * 3 + c] * g[2];
-    for (int m = 0; m < 3; ++m) {
-      dt[m] += g[m];
-      for (int c = 0; c < 3; ++c) dr[m * 3 + c] += g[m] * x[c];
-    }
-  };
-  for (int h = 0; h < H; ++h) {
+  for (int e = lane; e < H * D; e += 64) {
+    const int h = e / D, d = e - h * D;
     const size_t ri = rowidx(L, b, h, n);
-    const float* dqv = wsf(a, L.off_dqv) + ri * L.DKp;
-    const float* dkv = wsf(a, L.off_dkv) + ri * L.DKp;
-    const float* dvv = wsf(a, L.off_dvv) + ri * L.DVp;
-    const float* dqa = wsf(a, L.off_dqa) + ri * 16;
-    const float* dkb = wsf(a, L.off_dkb) + ri * 16;
-    const size_t bnh = (size_t)bn * H + h;
-    for (int d = 0; d < D; ++d) {
-      a.gq[bnh * D + d] = dqv[d] * sq;
-      a.gk[bnh * D + d] = dkv[d];
-    }
-    for (int d = 0; d < Dv; ++d) a.gv[bnh * Dv + d] = dvv[d];
-    for (int p = 0; p < P; ++p) {
-      point(dqa + 3 * p, a.qp + (bnh * P + p) * 3, a.gqp + (bnh * P + p) * 3);
-      point(dkb + 3 * p, a.kp + (bnh * P + p) * 3, a.gkp + (bnh * P + p) * 3);
-    }
-    for (int qq = 0; qq < Q; ++qq) point(dvv + Dv + R * Cz + 3 * qq, a.vp + (bnh * Q + qq) * 3, a.gvp + (bnh * Q + qq) * 3);
+    a.gq[(size_t)bn * H * D + e] = wsf(a, L.off_dqv)[ri * L.DKp + d] * sq;
+    a.gk[(size_t)bn * H * D + e] = wsf(a, L.off_dkv)[ri * L.DKp + d];
   }
-  for (int e = 0; e < 9; ++e) a.grot[(size_t)bn * 9 + e] = dr[e];
-  for (int e = 0; e < 3; ++e) a.gtr[(size_t)bn * 3 + e] = dt[e];
-  for (int r = 0; r < R; ++r)
-    for (int c = 0; c < Cz; ++c) {
-      float gl = wsf(a, L.off_dzle)[(size_t)bn * R * Cz + r * Cz + c];
-      float gr = 0.f;
-      for (int h = 0; h < H; ++h) {
-        const size_t ri = rowidx(L, b, h, n);
-        gl += wsf(a, L.off_dqv)[ri * L.DKp + D + r * Cz + c] * a.wpair[h * Cz + c] * s3;
-        gr += wsf(a, L.off_dkv)[ri * L.DKp + D + r * Cz + c] + wsf(a, L.off_dvv)[ri * L.DVp + Dv + r * Cz + c];
-      }
-      a.gzl[(size_t)bn * R * Cz + r * Cz + c] = gl;
-      a.gzr[(size_t)bn * R * Cz + r * Cz + c] = gr;
+  for (int e = lane; e < H * Dv; e += 64) {
+    const int h = e / Dv, d = e - h * Dv;
+    a.gv[(size_t)bn * H * Dv + e] = wsf(a, L.off_dvv)[rowidx(L, b, h, n) * L.DVp + d];
+  }
+  float dr[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float dt[3] = {0.f, 0.f, 0.f};
+  // tasks: (h, p) query points, (h, p) key points, (h, q) value points
+  const int nq = H * P, nv = H * Q;
+  for (int e = lane; e < 2 * nq + nv; e += 64) {
+    const float* g;
+    const float* x;
+    float* dx;
+    if (e < nq) {
+      const int h = e / P, pp = e - h * P;
+      g = wsf(a, L.off_dqa) + rowidx(L, b, h, n) * 16 + 3 * pp;
+      const size_t o = (((size_t)bn * H + h) * P + pp) * 3;
+      x = a.qp + o;
+      dx = a.gqp + o;
+    } else if (e < 2 * nq) {
+      const int f = e - nq, h = f / P, pp = f - h * P;
+      g = wsf(a, L.off_dkb) + rowidx(L, b, h, n) * 16 + 3 * pp;
+      const size_t o = (((size_t)bn * H + h) * P + pp) * 3;
+      x = a.kp + o;
+      dx = a.gkp + o;
+    } else {
+      const int f = e - 2 * nq, h = f / Q, qq = f - h * Q;
+      g = wsf(a, L.off_dvv) + rowidx(L, b, h, n) * L.DVp + Dv + R * Cz + 3 * qq;
+      const size_t o = (((size_t)bn * H + h) * Q + qq) * 3;
+      x = a.vp + o;
+      dx = a.gvp + o;
     }
+    const float g0 = g[0], g1 = g[1], g2 = g[2];
+    const float x0 = x[0], x1 = x[1], x2 = x[2];
+    for (int c = 0; c < 3; ++c) dx[c] = Rm[0 * 3 + c] * g0 + Rm[1 * 3 + c] * g1 + Rm[2 * 3 + c] * g2;
+    const float gg[3] = {g0, g1, g2}, xx[3] = {x0, x1, x2};
+    for (int m = 0; m < 3; ++m) {
+      dt[m] += gg[m];
+      for (int c = 0; c < 3; ++c) dr[m * 3 + c] += gg[m] * xx[c];
+    }
+  }
+  for (int e = 0; e < 9; ++e) {
+    float v = dr[e];
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    dr[e] = v;
+  }
+  for (int e = 0; e < 3; ++e) {
+    float v = dt[e];
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    dt[e] = v;
+  }
+  if (lane < 9) a.grot[(size_t)bn * 9 + lane] = dr[lane] + wsf(a, L.off_dre)[(size_t)bn * 9 + lane];
+  if (lane < 3) a.gtr[(size_t)bn * 3 + lane] = dt[lane] + wsf(a, L.off_dte)[(size_t)bn * 3 + lane];
+  for (int e = lane; e < R * Cz; e += 64) {
+    const int r = e / Cz, c = e - r * Cz;
+    float gl = wsf(a, L.off_dzle)[(size_t)bn * R * Cz + e];
+    float gr = 0.f;
+    for (int h = 0; h < H; ++h) {
+      const size_t ri = rowidx(L, b, h, n);
+      gl += wsf(a, L.off_dqv)[ri * L.DKp + D + r * Cz + c] * a.wpair[h * Cz + c] * s3;
+      gr += wsf(a, L.off_dkv)[ri * L.DKp + D + r * Cz + c] + wsf(a, L.off_dvv)[ri * L.DVp + Dv + r * Cz + c];
+    }
+    a.gzl[(size_t)bn * R * Cz + e] = gl;
+    a.gzr[(size_t)bn * R * Cz + e] = gr;
+  }
 }
 
 // Per-head parameters: dw_pair[h][c] = sum_{b,i,r} zl[b,i,r,c] dQV[b,h,i,D+rCz+c] / sqrt(3)
@@ -900,7 +926,7 @@ hipError_t launch_backward(const ipa_shape* s, const ipa_lift_in* in, const ipa_
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_pairs_inst(a, 1, st)) != hipSuccess) return e;
   if ((e = launch_pairs_inst(a, 2, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bw_inputs_kernel, dim3((BN + 63) / 64), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(bw_inputs_kernel, dim3(BN), dim3(64), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bw_params_part_kernel, dim3(L.H, kBwParamChunks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
