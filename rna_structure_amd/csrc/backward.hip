@@ -350,7 +350,11 @@ __global__ __launch_bounds__(4 * ROWS) void bw_query_kernel(BwArgs a) {
 }
 
 // dK / dV pass: per key, loop over all queries.
-template <int NK4, int NV4, int ROWS>
+// MODE 0 accumulates dKV and dB (needs dP, hence the key's VV quarter);
+// MODE 1 accumulates dVV (needs only p); MODE 2 does both in one pass.  On
+// large grids the two launches of modes 0 and 1 win (each holds few enough
+// registers for two wavefronts per SIMD); on small grids the single pass does.
+template <int NK4, int NV4, int ROWS, int MODE>
 __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
   const BwLayout& L = a.L;
   constexpr int KW = 16 * NK4, VW = 16 * NV4;
@@ -367,15 +371,20 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
   const size_t rj = rowidx(L, b, h, jc);
   const float gam = wsf(a, L.off_gam)[h];
   const bool mk = kin && a.mask[(size_t)b * L.N + jc] != 0;
-  float4 kv[NK4], dk[NK4];
+  constexpr bool kDS = MODE != 1, kDV = MODE != 0;
+  float4 kv[NK4], dk[kDS ? NK4 : 1];
   load_quarter<NK4>(wsf(a, L.off_kv) + rj * L.DKp, part, kv);
-  float4 vv[NV4], dv[NV4];
-  load_quarter<NV4>(wsf(a, L.off_vv) + rj * L.DVp, part, vv);
+  float4 vv[kDS ? NV4 : 1], dv[kDV ? NV4 : 1];
+  if constexpr (kDS) load_quarter<NV4>(wsf(a, L.off_vv) + rj * L.DVp, part, vv);
   const float4 kb = reinterpret_cast<const float4*>(wsf(a, L.off_kb) + rj * 16)[part];
+  if constexpr (kDS) {
 #pragma unroll
-  for (int u = 0; u < NK4; ++u) dk[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < NK4; ++u) dk[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if constexpr (kDV) {
 #pragma unroll
-  for (int u = 0; u < NV4; ++u) dv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < NV4; ++u) dv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float4 db = make_float4(0.f, 0.f, 0.f, 0.f);
   const int kbase = blockIdx.x * ROWS;
   for (int i0 = 0; i0 < L.N; i0 += kBwTile) {
@@ -413,25 +422,33 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
     for (int ii = 0; ii < ni; ++ii) {
       float d2;
       const float lg = logit_q<NK4>(kv, &sQ[ii][part * 4 * NK4], kb, &sA[ii][part * 4], gam, false, d2);
-      const float dp = quad_sum(dot_quarter<NV4>(vv, &sD[ii][0], part));
-      const bool ok = mk && sL[ii] < INFINITY && sPM[ii][r] != 0;
-      if (!ok) continue;
-      const float p = expf(lg - sL[ii]);
-      const float ds = p * (dp - sS[ii]);
-      axpy_quarter<NK4>(dk, ds, &sQ[ii][0], part);
-      axpy_quarter<NV4>(dv, p, &sD[ii][0], part);
-      const float4 x = *reinterpret_cast<const float4*>(&sA[ii][part * 4]);
-      const float w = 2.f * gam * ds;
-      db.x = fmaf(w, x.x - kb.x, db.x);
-      db.y = fmaf(w, x.y - kb.y, db.y);
-      db.z = fmaf(w, x.z - kb.z, db.z);
-      db.w = fmaf(w, x.w - kb.w, db.w);
+      if constexpr (kDS) {
+        const float dp = quad_sum(dot_quarter<NV4>(vv, &sD[ii][0], part));
+        const bool ok = mk && sL[ii] < INFINITY && sPM[ii][r] != 0;
+        if (!ok) continue;
+        const float p = expf(lg - sL[ii]);
+        const float ds = p * (dp - sS[ii]);
+        axpy_quarter<NK4>(dk, ds, &sQ[ii][0], part);
+        if constexpr (kDV) axpy_quarter<NV4>(dv, p, &sD[ii][0], part);
+        const float4 x = *reinterpret_cast<const float4*>(&sA[ii][part * 4]);
+        const float w = 2.f * gam * ds;
+        db.x = fmaf(w, x.x - kb.x, db.x);
+        db.y = fmaf(w, x.y - kb.y, db.y);
+        db.z = fmaf(w, x.z - kb.z, db.z);
+        db.w = fmaf(w, x.w - kb.w, db.w);
+      } else {
+        const bool ok = mk && sL[ii] < INFINITY && sPM[ii][r] != 0;
+        if (!ok) continue;
+        axpy_quarter<NV4>(dv, expf(lg - sL[ii]), &sD[ii][0], part);
+      }
     }
   }
   if (!kin) return;
-  store_quarter<NK4>(wsf(a, L.off_dkv) + rj * L.DKp, part, dk);
-  store_quarter<NV4>(wsf(a, L.off_dvv) + rj * L.DVp, part, dv);
-  reinterpret_cast<float4*>(wsf(a, L.off_dkb) + rj * 16)[part] = db;
+  if constexpr (kDS) {
+    store_quarter<NK4>(wsf(a, L.off_dkv) + rj * L.DKp, part, dk);
+    reinterpret_cast<float4*>(wsf(a, L.off_dkb) + rj * 16)[part] = db;
+  }
+  if constexpr (kDV) store_quarter<NV4>(wsf(a, L.off_dvv) + rj * L.DVp, part, dv);
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -768,7 +785,14 @@ hipError_t launch_pairs_rows(const BwArgs& a, int which, hipStream_t st) {
   dim3 grid((L.N + ROWS - 1) / ROWS, L.H, L.B);
   if (which == 0) hipLaunchKernelGGL((bw_fwd_kernel<NK4, NV4, ROWS>), grid, dim3(4 * ROWS), 0, st, a);
   if (which == 1) hipLaunchKernelGGL((bw_query_kernel<NK4, NV4, ROWS>), grid, dim3(4 * ROWS), 0, st, a);
-  if (which == 2) hipLaunchKernelGGL((bw_key_kernel<NK4, NV4, ROWS>), grid, dim3(4 * ROWS), 0, st, a);
+  if (which == 2) {
+    if ((long)grid.x * grid.y * grid.z >= 512) {
+      hipLaunchKernelGGL((bw_key_kernel<NK4, NV4, ROWS, 0>), grid, dim3(4 * ROWS), 0, st, a);
+      hipLaunchKernelGGL((bw_key_kernel<NK4, NV4, ROWS, 1>), grid, dim3(4 * ROWS), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((bw_key_kernel<NK4, NV4, ROWS, 2>), grid, dim3(4 * ROWS), 0, st, a);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -46,6 +46,9 @@ CASES = [
      dict(frames="walk", step=3.8, pair_dropout=0.1)),
     ("one-residue", IPAShape(B=2, N=1, H=2, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6, dtype="f32"), 6,
      dict(frames="gauss")),
+    # 512 workgroups per pass: the key pass runs as two launches (dK/dB, then dV)
+    ("split-key-pass", IPAShape(B=16, N=256, H=8, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6, dtype="f32"), 9,
+     dict(frames="walk", step=3.8, lengths=(200, 256), pair_dropout=0.05)),
 ]
 
 
