@@ -190,8 +190,9 @@ ipa_status ipa_logit_rows(const ipa_shape* s, const void* lifted, int64_t b, int
  * and query pairs with recomputed probabilities (FlashAttention style, no
  * [B,H,N,N] array), and maps the row gradients back to the inputs.
  *
- * s->dtype must be IPA_F32: every floating input is fp32 (a bf16 model
- * converts its inputs first).  Limits: P <= 5, D + R*Cz <= 256,
+ * s->dtype names the inputs' type as for the forward (IPA_F32 or IPA_BF16;
+ * bf16 inputs are widened to fp32 copies in the workspace first, so the
+ * gradients are those at the bf16 values, computed in fp32).  Limits: P <= 5, D + R*Cz <= 256,
  * Dv + R*Cz + 3Q <= 256.  in / epi are the forward's input structs (the
  * pair mask may be NULL); d_update [B,N,Cout] and d_local [B,N,H,Q,3] are
  * fp32.  Every gradient pointer of ipa_grads is required; each array has its

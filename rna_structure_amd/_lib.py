@@ -174,16 +174,14 @@ def ipa_backward(s: IpaShape, t: dict, d_update, d_local, workspace, grads: dict
 
 
 class IPABackward:
-    """Workspace, gradient buffers and the backward call for a fixed fp32 shape.
+    """Workspace, gradient buffers and the backward call for a fixed shape.
 
-    t are fp32 device inputs (device_inputs of an 'f32' input set); every call
-    rewrites the gradient tensors, each shaped like its input."""
+    t are device inputs in the shape's dtype (device_inputs); gradients are
+    fp32, each shaped like its input, and rewritten by every call."""
 
     def __init__(self, shape, eps: float = 1e-8, device="cuda"):
         import torch
         load()
-        if shape.dtype != "f32":
-            raise ValueError("the backward runs on fp32 inputs")
         self.shape = shape
         self.s = make_shape(shape, eps)
         nbytes = backward_workspace_bytes(self.s)

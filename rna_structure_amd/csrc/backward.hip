@@ -41,6 +41,9 @@ struct BwLayout {
   size_t off_gam, off_qv, off_kv, off_vv, off_qa, off_kb, off_o, off_lse, off_do, off_dd, off_feat, off_dfeat,
       off_dqv, off_dqa, off_dgam, off_dkv, off_dkb, off_dvv, off_dzle, off_dre, off_dte, off_dwpart, off_ppart,
       total;
+  int bf16;               // inputs are bf16: converted into fp32 copies first
+  size_t off_cvt[14];     // fp32 copies of the 14 inputs (bf16 inputs only)
+  size_t cvt_n[14];
 };
 
 struct BwArgs {
@@ -506,6 +509,12 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(GemmArgs g) {
     }
 }
 
+// fp32 copy of a bf16 array
+__global__ __launch_bounds__(256) void bw_widen_kernel(const uint16_t* src, float* dst, size_t n) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) dst[e] = bf16_bits_to_f32(src[e]);
+}
+
 // out[e] = sum_z part[z*slab + e]
 __global__ __launch_bounds__(256) void bw_sum_slabs_kernel(const float* part, float* out, size_t n, int nz, size_t slab) {
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -878,6 +887,15 @@ bool bw_layout(const ipa_shape* s, BwLayout* L) {
   L->off_dte = take(bn * 3);
   L->off_dwpart = take((size_t)L->ksplit * (L->F + 1) * L->Cout);
   L->off_ppart = take((size_t)L->H * kBwParamChunks * (L->Cz + 1));
+  L->bf16 = s->dtype == IPA_BF16;
+  const size_t bnh = bn * L->H;
+  const size_t cn[14] = {bnh * L->D, bnh * L->D, bnh * L->Dv, bnh * L->P * 3, bnh * L->P * 3, bnh * L->Q * 3, bn * 9,
+                         bn * 3, (size_t)L->H, (size_t)L->H * L->Cz, bn * L->R * L->Cz, bn * L->R * L->Cz,
+                         (size_t)L->F * L->Cout, (size_t)L->Cout};
+  for (int e = 0; e < 14; ++e) {
+    L->cvt_n[e] = cn[e];
+    L->off_cvt[e] = L->bf16 ? take(cn[e]) : 0;
+  }
   L->total = off;
   return true;
 }
@@ -894,20 +912,33 @@ hipError_t launch_backward(const ipa_shape* s, const ipa_lift_in* in, const ipa_
   if (!bw_layout(s, &a.L)) return hipErrorInvalidValue;
   const BwLayout& L = a.L;
   a.ws = (char*)ws;
-  a.q = (const float*)in->q;
-  a.k = (const float*)in->k;
-  a.v = (const float*)in->v;
-  a.qp = (const float*)in->q_points;
-  a.kp = (const float*)in->k_points;
-  a.vp = (const float*)in->v_points;
-  a.rot = (const float*)in->rotation;
-  a.tr = (const float*)in->translation;
-  a.wraw = (const float*)in->point_weight_raw;
-  a.wpair = (const float*)in->w_pair;
-  a.zl = (const float*)in->zl;
-  a.zr = (const float*)in->zr;
-  a.wout = (const float*)ep->w_out;
-  a.bout = (const float*)ep->b_out;
+  if (L.bf16) {
+    // bf16 inputs: widen every input into its fp32 copy, then run the fp32 backward on the copies
+    const void* src[14] = {in->q, in->k, in->v, in->q_points, in->k_points, in->v_points, in->rotation,
+                           in->translation, in->point_weight_raw, in->w_pair, in->zl, in->zr, ep->w_out, ep->b_out};
+    for (int e = 0; e < 14; ++e) {
+      const size_t n = L.cvt_n[e];
+      hipLaunchKernelGGL(bw_widen_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                         (const uint16_t*)src[e], (float*)(a.ws + L.off_cvt[e]), n);
+    }
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
+  auto inp = [&](int e, const void* p) { return L.bf16 ? (const float*)(a.ws + L.off_cvt[e]) : (const float*)p; };
+  a.q = inp(0, in->q);
+  a.k = inp(1, in->k);
+  a.v = inp(2, in->v);
+  a.qp = inp(3, in->q_points);
+  a.kp = inp(4, in->k_points);
+  a.vp = inp(5, in->v_points);
+  a.rot = inp(6, in->rotation);
+  a.tr = inp(7, in->translation);
+  a.wraw = inp(8, in->point_weight_raw);
+  a.wpair = inp(9, in->w_pair);
+  a.zl = inp(10, in->zl);
+  a.zr = inp(11, in->zr);
+  a.wout = inp(12, ep->w_out);
+  a.bout = inp(13, ep->b_out);
   a.mask = in->mask;
   a.pmask = in->pair_mask;
   a.dupd = dupd;

@@ -152,7 +152,11 @@ def test_knn_validation_before_launch(lib):
 def test_backward_validation_before_launch(lib):
     s = _shape(dtype="f32")
     assert _lib.backward_workspace_bytes(s) > 0
-    assert _lib.backward_workspace_bytes(_shape(dtype="bf16")) == 0        # fp32 inputs only
+    # bf16 inputs: the workspace also holds their fp32 copies
+    assert _lib.backward_workspace_bytes(_shape(dtype="bf16")) > _lib.backward_workspace_bytes(s)
+    bad_dt = _shape(dtype="f32")
+    bad_dt.dtype = 7
+    assert _lib.backward_workspace_bytes(bad_dt) == 0
     assert _lib.backward_workspace_bytes(_shape(dtype="f32", P=6)) == 0     # 3P > 16
     assert _lib.backward_workspace_bytes(_shape(dtype="f32", Cz=200)) == 0  # D + R Cz > 256
     assert _lib.backward_workspace_bytes(_shape(dtype="f32", N=0)) == 0
@@ -172,7 +176,7 @@ def test_backward_validation_before_launch(lib):
     gr0 = _lib.IpaGrads(*[4096] * len(_lib.GRAD_KEYS))
     gr0.zr = None
     assert call(s, gr=gr0) == 1
-    assert call(_shape(dtype="bf16")) == 3
+    assert call(bad_dt) == 3
     assert call(_shape(dtype="f32", N=0)) == 2
     gr1 = _lib.IpaGrads(*[4096] * len(_lib.GRAD_KEYS))
     gr1.q = 4100

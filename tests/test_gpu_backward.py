@@ -1,6 +1,7 @@
-"""GPU parity of the backward pass (ipa_backward, fp32): every input gradient
-against the float64 autograd oracle (oracle/ipa_backward.py) on the same
-seeded inputs and upstream gradients.  Tolerance: max-abs-rel 1e-4 per
+"""GPU parity of the backward pass (ipa_backward, fp32 arithmetic): every
+input gradient against the float64 autograd oracle (oracle/ipa_backward.py)
+on the same seeded inputs (fp32, or bf16-rounded for bf16 inputs) and
+upstream gradients.  Tolerance: max-abs-rel 1e-4 per
 gradient tensor (max |gpu - ref| / max |ref|), the fp32 bar.  At a length the
 oracle cannot differentiate densely, properties that hold at any size are
 checked instead (a common translation or rotation of the frames changes
@@ -46,6 +47,9 @@ CASES = [
      dict(frames="walk", step=3.8, pair_dropout=0.1)),
     ("one-residue", IPAShape(B=2, N=1, H=2, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6, dtype="f32"), 6,
      dict(frames="gauss")),
+    # bf16 inputs: widened to fp32 inside, gradients at the bf16 values
+    ("standard-bf16-inputs", IPAShape(B=1, N=120, H=4, dtype="bf16"), 10,
+     dict(frames="walk", step=3.8, pair_dropout=0.05, empty_row=True)),
     # 512 workgroups per pass: the key pass runs as two launches (dK/dB, then dV)
     ("split-key-pass", IPAShape(B=16, N=256, H=8, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6, dtype="f32"), 9,
      dict(frames="walk", step=3.8, lengths=(200, 256), pair_dropout=0.05)),
