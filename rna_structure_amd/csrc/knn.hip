@@ -4,25 +4,27 @@
 // neighbours may be found block-wise in a streaming fashion).  No L x L
 // array exists; memory is the O(L k) output.
 //
-// One wavefront owns G = 8 consecutive query residues of one sample.  Its 64
-// lanes walk the candidates of that sample 64 at a time in increasing index
-// order; the G query positions are wave-uniform, so each lane forms the G
-// squared distances of its candidate with scalar operands (ALU bound: the
-// candidate block is read once per wavefront and reused G times).
+// A group of G = 8 consecutive query residues of one sample is owned by S
+// wavefronts (S = 1, 2 or 4; more on small grids), each walking 1/S of the
+// candidate blocks.  The 64 lanes of a wavefront take the candidates 64 at a
+// time in increasing index order and form the 8 squared distances of their
+// candidate against the query positions held in registers (ALU bound: a
+// candidate block is read once and used 8 times).
 //
-// Per query the wavefront keeps a threshold tau and an LDS buffer of up to
-// 256 candidates that passed it.  A step appends every lane whose d2 passes
-// (ballot + prefix count inside one uniform branch per query).  When a buffer
-// fills, an exact rank selection keeps its k best keys (d2, then index) in
-// order and lowers tau to the k-th one.  Candidates arrive in increasing
-// index order, so a later candidate with the same d2 as the k-th kept one
-// loses the tie: after a selection the test is d2 < d2_k, written as
-// d2 <= tau with tau the float just below d2_k.  Before the walk, tau is
-// (just above) the k-th smallest d2 among the candidates of a 64-residue
-// window around the queries, taken inclusively (any k candidates bound the final k-th distance
-// from above); for chain molecules sequence neighbours are spatial
-// neighbours, so this is close to the final value and the walk buffers few
-// candidates.  A last selection orders the survivors.
+// Per query a wavefront keeps a threshold tau and an LDS buffer of up to 256
+// candidate keys (d2 bits << 32 | index) that passed it.  One ballot per
+// query and step finds the passing lanes; only when some lane passes does the
+// step append (prefix count), and a buffer past 192 entries is cut by an exact
+// rank selection to its k best keys, which lowers tau to the float just below
+// the k-th d2: later candidates have larger indices, so an equal d2 loses the
+// tie and the strict test stays exact.  Before the walk tau is (just above)
+// the k-th smallest d2 among the candidates of a 64-residue window around the
+// queries, taken inclusively -- any k candidates bound the final k-th
+// distance from above -- found by a bitwise search with 16 lanes per query
+// and DPP row sums; for chain molecules sequence neighbours are spatial
+// neighbours, so few candidates are ever buffered.  At the end the S buffers
+// of a query are gathered and one selection orders them; the rows of the
+// group are contiguous in every output and written by flat loops.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
