@@ -117,7 +117,9 @@ static ipa_status bw_shape_status(const ipa_shape* s) {
       s->R <= 0 || s->Cout <= 0 || !(s->eps > 0.0f))
     return IPA_ERR_SHAPE;
   if (s->dtype != IPA_F32 && s->dtype != IPA_BF16) return IPA_ERR_UNSUPPORTED;
-  if (s->N > (1 << 26) || s->B * s->N > (1 << 28) || s->H > 1024 || s->Cout > (1 << 16)) return IPA_ERR_UNSUPPORTED;
+  // grid limits: samples on the z dimension (<= 65535), heads on y
+  if (s->N > (1 << 26) || s->B > 65535 || s->B * s->N > (1 << 28) || s->H > 1024 || s->Cout > (1 << 16))
+    return IPA_ERR_UNSUPPORTED;
   return fipa::bw_workspace_bytes(s) ? IPA_OK : IPA_ERR_UNSUPPORTED;
 }
 

@@ -471,7 +471,7 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(GemmArgs g) {
   __shared__ float As[16][65];
   __shared__ float Bs[16][65];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
   const int kchunk = (g.K + g.ksplit - 1) / g.ksplit;
   const int kb = blockIdx.z * kchunk, ke = min(g.K, kb + kchunk);
   float acc[4][4] = {};
@@ -822,7 +822,7 @@ hipError_t launch_pairs_inst(const BwArgs& a, int which, hipStream_t st) {
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
-  dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, g.ksplit);
+  dim3 grid((g.M + 63) / 64, (g.N + 63) / 64, g.ksplit);  // rows on x (up to 2^31 tiles)
   hipLaunchKernelGGL(bw_gemm_kernel, grid, dim3(256), 0, st, g);
   return hipGetLastError();
 }
