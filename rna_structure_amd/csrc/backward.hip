@@ -32,6 +32,8 @@ namespace fipa {
 
 namespace {
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 constexpr int kBwTile = 32;   // partner rows staged in LDS per step
 
 struct BwLayout {
@@ -454,6 +456,160 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
   if constexpr (kDV) store_quarter<NV4>(wsf(a, L.off_dvv) + rj * L.DVp, part, dv);
 }
 
+// ------------------------------------------------------------------ matrix-core forward recomputation
+// The same O and lse on fp32 matrix cores (v_mfma_f32_32x32x2f32, full fp32
+// operands).  A workgroup of four wavefronts takes 128 queries of one
+// (b, h); each wavefront owns 32 queries and walks key tiles of 32 staged in
+// LDS.  S^T (32 keys x 32 queries) = KV_t QV^T on the matrix cores (DKp/2
+// steps of K = 2); the point term -gamma sum |A - B|^2 is added per element
+// on the vector ALU from differences (an expanded form on fp32 matrix cores
+// loses ~1e-4 of a logit to cancellation), overlapping the matrix work.  The
+// accumulator gives each lane one query and 16 keys, so the softmax row work
+// stays in the lane (and its partner 32 lanes away); the running maximum is
+// raised lazily.  O^T (32 value columns x 32 queries per block) += VV_t^T P^T
+// takes the probabilities straight from the accumulator registers: at step s
+// lane half h supplies key kappa(s, h) = 8 (s / 4) + 4 h + s % 4, the key its
+// register s holds, and reads the value row of that key.
+constexpr int kBwKT = 32;  // keys per tile of the matrix-core passes
+
+__device__ __forceinline__ int kappa(int s, int h) { return 8 * (s >> 2) + 4 * h + (s & 3); }
+
+template <int DKH, int NVB>
+__global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
+  const BwLayout& L = a.L;
+  constexpr int DKp = 2 * DKH;
+  constexpr int VW = 32 * NVB;  // value columns staged (DVp padded with zeros)
+  __shared__ float sKT[DKp][kBwKT];
+  __shared__ __align__(16) float sBp[kBwKT][16];
+  __shared__ float sV[kBwKT][VW];
+  __shared__ float sM[kBwKT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int q = blockIdx.x * 128 + 32 * w + l32;
+  const bool qin = q < L.N;
+  const int qc = qin ? q : L.N - 1;
+  const size_t rq = rowidx(L, b, h, qc);
+  const float gam = wsf(a, L.off_gam)[h];
+  const bool mq = qin && a.mask[(size_t)b * L.N + qc] != 0;
+  // query operand: QV[q][s + DKH hf], s < DKH; point coordinates 8 hf .. +7
+  float qv[DKH];
+  {
+    const float* row = wsf(a, L.off_qv) + rq * L.DKp + DKH * hf;
+#pragma unroll
+    for (int s4 = 0; s4 < DKH / 4; ++s4) {
+      const float4 v = reinterpret_cast<const float4*>(row)[s4];
+      qv[4 * s4] = v.x;
+      qv[4 * s4 + 1] = v.y;
+      qv[4 * s4 + 2] = v.z;
+      qv[4 * s4 + 3] = v.w;
+    }
+#pragma unroll
+    for (int s = 4 * (DKH / 4); s < DKH; ++s) qv[s] = row[s];
+  }
+  float qa[16];  // this lane's query points (both halves of the pair hold all 16)
+  {
+    const float* row = wsf(a, L.off_qa) + rq * 16;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) qa[u] = row[u];
+  }
+  f32x16_t oacc[NVB];
+#pragma unroll
+  for (int v = 0; v < NVB; ++v) oacc[v] = f32x16_t{};
+  float m = -INFINITY, lsum = 0.f;
+  const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + qc) * L.N : nullptr;
+  const int P3 = L.P3;  // coordinates past 3P are zero on both sides
+  for (int j0 = 0; j0 < L.N; j0 += kBwKT) {
+    __syncthreads();
+    // stage the tile: KV transposed, VV rows (zero past DVp), centred key points
+    for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
+      const int jj = e / (DKp / 4), c4 = e - jj * (DKp / 4);
+      const int j = min(j0 + jj, L.N - 1);
+      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, j) * L.DKp)[c4];
+      sKT[4 * c4][jj] = v.x;
+      sKT[4 * c4 + 1][jj] = v.y;
+      sKT[4 * c4 + 2][jj] = v.z;
+      sKT[4 * c4 + 3][jj] = v.w;
+    }
+    for (int e = tid; e < kBwKT * (VW / 4); e += 256) {
+      const int jj = e / (VW / 4), c4 = e - jj * (VW / 4);
+      const int j = min(j0 + jj, L.N - 1);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * c4 < L.DVp) v = reinterpret_cast<const float4*>(wsf(a, L.off_vv) + rowidx(L, b, h, j) * L.DVp)[c4];
+      reinterpret_cast<float4*>(&sV[jj][0])[c4] = v;
+    }
+    for (int e = tid; e < kBwKT * 4; e += 256) {
+      const int jj = e >> 2, c4 = e & 3;
+      const int j = min(j0 + jj, L.N - 1);
+      reinterpret_cast<float4*>(&sBp[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_kb) + rowidx(L, b, h, j) * 16)[c4];
+    }
+    if (tid < kBwKT) {
+      const int j = j0 + tid;
+      sM[tid] = (j < L.N && a.mask[(size_t)b * L.N + j] != 0) ? 1.f : 0.f;
+    }
+    __syncthreads();
+    // S^T: A = key tile (row = key l32, k = hf), B = query (k = hf, column = query l32)
+    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < DKH; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(sKT[s + DKH * hf][l32], qv[s], sacc, 0, 0, 0);
+    // logits of this lane's 16 keys (point term from differences), masks, tile maximum
+    float lg[16];
+    float tmax = -INFINITY;
+    const int nj = min(kBwKT, L.N - j0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kappa(r, hf);
+      const bool ok = mq && kk < nj && sM[kk] != 0.f && (!pmrow || pmrow[j0 + kk] != 0);
+      float d2 = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        if (4 * c4 >= P3) break;
+        const float4 y = reinterpret_cast<const float4*>(&sBp[kk][0])[c4];
+        const float dx = qa[4 * c4] - y.x, dy = qa[4 * c4 + 1] - y.y, dz = qa[4 * c4 + 2] - y.z, dw = qa[4 * c4 + 3] - y.w;
+        d2 += dx * dx + dy * dy + dz * dz + dw * dw;
+      }
+      lg[r] = ok ? sacc[r] - gam * d2 : -INFINITY;
+      tmax = fmaxf(tmax, lg[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (tmax > m + 5.0f) {  // raise the running maximum (lazily: values up to e^5 are fine)
+      const float c = expf(m - tmax);
+      lsum *= c;
+#pragma unroll
+      for (int v = 0; v < NVB; ++v) oacc[v] *= c;
+      m = tmax;
+    }
+    float pr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = lg[r] > -INFINITY ? expf(lg[r] - m) : 0.f;
+      lsum += pr[r];
+    }
+    // O^T += VV^T P^T
+#pragma unroll
+    for (int v = 0; v < NVB; ++v)
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        oacc[v] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[kappa(s, hf)][32 * v + l32], pr[s], oacc[v], 0, 0, 0);
+  }
+  lsum += __shfl_xor(lsum, 32);
+  if (!qin) return;
+  const bool empty = !(lsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / lsum;
+  float* orow = wsf(a, L.off_o) + rq * L.DVp;
+#pragma unroll
+  for (int v = 0; v < NVB; ++v)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * v + 8 * g + 4 * hf;
+      if (c < L.DVp)
+        *reinterpret_cast<float4*>(orow + c) =
+            make_float4(oacc[v][4 * g] * inv, oacc[v][4 * g + 1] * inv, oacc[v][4 * g + 2] * inv, oacc[v][4 * g + 3] * inv);
+    }
+  if (hf == 0) wsf(a, L.off_lse)[rq] = empty ? -INFINITY : m + logf(lsum);
+}
+
 // ------------------------------------------------------------------ GEMM
 // C[m][n] (+)= sum_k A(m,k) B(k,n), fp32, 64x64 tiles, 256 threads x 4x4.
 // A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn].  blockIdx.z splits K
@@ -815,6 +971,11 @@ hipError_t launch_pairs(const BwArgs& a, int which, hipStream_t st) {
 
 hipError_t launch_pairs_inst(const BwArgs& a, int which, hipStream_t st) {
   const BwLayout& L = a.L;
+  if (which == 0 && L.NK4 == 9) {
+    // standard shape (D + R Cz <= 144, Dv + R Cz + 3Q <= 176): matrix cores
+    hipLaunchKernelGGL((bw_fwd_mfma_kernel<72, 6>), dim3((L.N + 127) / 128, L.H, L.B), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (L.NK4 == 1) return launch_pairs<1, 2>(a, which, st);
   if (L.NK4 == 4) return launch_pairs<4, 4>(a, which, st);
   if (L.NK4 == 9) return launch_pairs<9, 11>(a, which, st);
