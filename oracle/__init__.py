@@ -1,4 +1,5 @@
-"""CPU oracles for the IPA forward and the kNN distogram (test infrastructure only).
+"""CPU oracles for the IPA forward, the kNN distogram and attention with a
+low-rank bias (test infrastructure only).
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
 import anything from this package; the library path never does.
@@ -11,3 +12,9 @@ from .knn_oracle import (bin_width, sqdist_f32, distance_bins, one_hot, knn_dist
 __all__ = ["softplus", "point_weight", "to_global", "ipa_dense", "ipa_factored",
            "ipa_loops", "pair_from_factors", "bin_width", "sqdist_f32", "distance_bins",
            "one_hot", "knn_distogram", "knn_loops"]
+from .flashbias_oracle import (alibi_slopes, alibi_bias, alibi_factors, sqdist_factors,
+                               attention_with_bias, flashbias_attention, flashbias_rows,
+                               attention_loops)
+
+__all__ += ["alibi_slopes", "alibi_bias", "alibi_factors", "sqdist_factors",
+            "attention_with_bias", "flashbias_attention", "flashbias_rows", "attention_loops"]
