@@ -271,6 +271,60 @@ typedef struct {
 ipa_status ipa_knn_distogram(const ipa_knn_shape* s, const float* translation, const uint8_t* mask,
                              int32_t* nn_index, float* nn_dist, void* dgram, void* stream);
 
+/* ------------------------------------------------------------------
+ * Attention with a low-rank bias (FlashBias: Fast Computation of Attention
+ * with Bias, atlas.scime.ai summary, Problem and Approach).  A dense bias
+ * b_ij = phi_q(i) . phi_k(j) is given by its two factor tensors, which are
+ * concatenated onto the queries and keys, so the [N, M] bias is never formed:
+ *
+ *   L_ij  = scale q_i . k_j + phi_q(i) . phi_k(j)      (natural-log units)
+ *   O_i   = sum_j softmax_j(L_ij) v_j,  lse_i = log sum_j exp(L_ij)
+ *
+ * over the permitted keys j of the same sample: key_mask[b, j] != 0 (all
+ * when key_mask is NULL) and, when causal, j <= i.  A row with no permitted
+ * key gets O_i = 0 and lse_i = -inf.
+ *
+ * Arithmetic: bf16 matrix-core operands with fp32 accumulation.  The q.k
+ * part uses bf16 q scale log2(e) and bf16 k; every factor product is taken
+ * as hi.hi + hi.lo + lo.hi of bf16 hi/lo pairs (~16 significant bits per
+ * factor, so large exact factors such as ALiBi positions stay exact to
+ * ~1e-5 relative); probabilities are rounded to bf16 against bf16 values;
+ * softmax statistics in fp32.  fp32 q, k, v are rounded to bf16 in the same
+ * way; fp32 factors keep the ~16 bits of their hi/lo pairs. 
+ * ------------------------------------------------------------------ */
+typedef struct {
+  int64_t B, N, M, H; /* samples (<= 65535), queries, keys, heads (<= 65535); all >= 1 */
+  int64_t D;          /* q / k width (>= 1) */
+  int64_t Dv;         /* value width, 1 .. 256 */
+  int64_t R;          /* bias rank (>= 0); D + 3 R <= 256 */
+  int32_t dtype;      /* IPA_F32 or IPA_BF16: q, k, v */
+  int32_t phi_dtype;  /* IPA_F32 or IPA_BF16: phi_q, phi_k (fp32 keeps exact factors exact) */
+  int32_t causal;     /* nonzero: key j permitted for query i only if j <= i (needs N == M) */
+  float scale;        /* multiplies q . k (finite), e.g. 1/sqrt(D) */
+} ipa_bias_shape;
+
+/* Workspace bytes ipa_bias_attention needs for this shape (lifted rows,
+ * transposed value tiles and mask words, O(B H (N + M)(D + 3R + Dv))); 0 if
+ * the shape is invalid or beyond the compiled limits. */
+size_t ipa_bias_workspace_bytes(const ipa_bias_shape* s);
+
+/* Inputs (device pointers, row-major, all 16-byte aligned):
+ *   q [B,N,H,D], k [B,M,H,D], v [B,M,H,Dv]          in s->dtype
+ *   phi_q [B,N,H,R], phi_k [B,M,H,R]                in s->phi_dtype (may be NULL if R == 0)
+ *   key_mask [B,M] bytes, or NULL (every key permitted)
+ * Outputs (written in full): o [B,N,H,Dv] fp32, lse [B,H,N] fp32.
+ * workspace: device memory of at least ipa_bias_workspace_bytes(s) bytes,
+ * owned by the caller, overwritten.  Enqueued on `stream` (hipStream_t, NULL
+ * for the default stream); no allocation, no synchronisation.
+ * Returns IPA_ERR_NULL (a required pointer NULL), IPA_ERR_SHAPE (a dimension
+ * out of range, scale not finite, causal with N != M, B H max(N, M) beyond
+ * ~6.7e7, workspace too small),
+ * IPA_ERR_UNSUPPORTED (unknown dtype or phi_dtype, D + 3R > 256 or Dv > 256), IPA_ERR_ALIGN
+ * before enqueuing anything, or IPA_ERR_LAUNCH. */
+ipa_status ipa_bias_attention(const ipa_bias_shape* s, const void* q, const void* k, const void* v,
+                              const void* phi_q, const void* phi_k, const uint8_t* key_mask, float* o, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* ipa_status_string(int status);
 

@@ -21,7 +21,7 @@ STATUS = {0: "IPA_OK", 1: "IPA_ERR_NULL", 2: "IPA_ERR_SHAPE", 3: "IPA_ERR_UNSUPP
           4: "IPA_ERR_ALIGN", 5: "IPA_ERR_LAUNCH", 6: "IPA_ERR_DEVICE"}
 EXPORTS = ("ipa_lifted_bytes", "ipa_o_width", "ipa_lift", "ipa_flash_fwd", "ipa_epilogue",
            "ipa_logit_rows", "ipa_backward_workspace_bytes", "ipa_backward", "ipa_knn_distogram",
-           "ipa_status_string", "ipa_version")
+           "ipa_bias_workspace_bytes", "ipa_bias_attention", "ipa_status_string", "ipa_version")
 GRAD_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "translation",
              "point_weight_raw", "w_pair", "zl", "zr", "w_out", "b_out")
 
@@ -48,6 +48,12 @@ class IpaGrads(ctypes.Structure):
 class IpaKnnShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("B", "N", "k", "nbins")] + \
                [("dmax", ctypes.c_float), ("dgram_dtype", ctypes.c_int32)]
+
+
+class IpaBiasShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "N", "M", "H", "D", "Dv", "R")] + \
+               [("dtype", ctypes.c_int32), ("phi_dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
 
 
 class IPAError(RuntimeError):
@@ -88,6 +94,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipa_backward.restype = ctypes.c_int
     lib.ipa_knn_distogram.argtypes = [ctypes.POINTER(IpaKnnShape), vp, vp, vp, vp, vp, vp]
     lib.ipa_knn_distogram.restype = ctypes.c_int
+    lib.ipa_bias_workspace_bytes.argtypes = [ctypes.POINTER(IpaBiasShape)]
+    lib.ipa_bias_workspace_bytes.restype = sz
+    lib.ipa_bias_attention.argtypes = [ctypes.POINTER(IpaBiasShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ipa_bias_attention.restype = ctypes.c_int
     lib.ipa_status_string.argtypes = [ctypes.c_int]
     lib.ipa_status_string.restype = ctypes.c_char_p
     lib.ipa_version.argtypes = []
@@ -219,6 +229,41 @@ class KnnDistogram:
     def __call__(self, translation, mask=None, stream=None) -> dict:
         ipa_knn_distogram(self.s, translation, mask, self.nn_index, self.nn_dist, self.dgram, stream)
         return dict(index=self.nn_index, dist=self.nn_dist, dgram=self.dgram)
+
+
+def ipa_bias_workspace_bytes(s: IpaBiasShape) -> int:
+    return int(load().ipa_bias_workspace_bytes(ctypes.byref(s)))
+
+
+def ipa_bias_attention(s: IpaBiasShape, q, k, v, phi_q, phi_k, key_mask, o, lse, workspace, stream=None):
+    _check("ipa_bias_attention", load().ipa_bias_attention(
+        ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(phi_q), _ptr(phi_k), _ptr(key_mask), _ptr(o), _ptr(lse),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class BiasAttention:
+    """Workspace, output buffers and the call of attention with a low-rank
+    bias for a fixed shape.  q [B,N,H,D], k [B,M,H,D], v [B,M,H,Dv],
+    (device tensors in `dtype`), phi_q [B,N,H,R], phi_k [B,M,H,R] (in
+    `phi_dtype`) and key_mask [B,M] uint8 (or None); o [B,N,H,Dv] and
+    lse [B,H,N] (fp32) are allocated here and rewritten by every call."""
+
+    def __init__(self, B: int, N: int, M: int, H: int, D: int, Dv: int, R: int, scale: float,
+                 causal: bool = False, dtype: str = "bf16", phi_dtype: str = "f32", device="cuda"):
+        import torch
+        load()
+        dts = {"f32": IPA_F32, "bf16": IPA_BF16}
+        self.s = IpaBiasShape(B, N, M, H, D, Dv, R, dts[dtype], dts[phi_dtype], int(bool(causal)), float(scale))
+        nbytes = ipa_bias_workspace_bytes(self.s)
+        if nbytes == 0:
+            raise IPAError("ipa_bias_workspace_bytes", 3)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.o = torch.empty(B, N, H, Dv, dtype=torch.float32, device=device)
+        self.lse = torch.empty(B, H, N, dtype=torch.float32, device=device)
+
+    def __call__(self, q, k, v, phi_q=None, phi_k=None, key_mask=None, stream=None) -> dict:
+        ipa_bias_attention(self.s, q, k, v, phi_q, phi_k, key_mask, self.o, self.lse, self.workspace, stream)
+        return dict(o=self.o, lse=self.lse)
 
 
 _FLOAT_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "translation",

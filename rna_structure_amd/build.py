@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libflashipa.so")
-SOURCES = ["abi.cpp", "lift.hip", "flash_f32.hip", "flash_mfma.hip", "epilogue.hip", "diag.hip", "knn.hip", "backward.hip"]
+SOURCES = ["abi.cpp", "lift.hip", "flash_f32.hip", "flash_mfma.hip", "epilogue.hip", "diag.hip", "knn.hip", "backward.hip", "flashbias.hip"]
 ARCH = os.environ.get("FLASHIPA_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # no packed fp32 VALU instructions anywhere in the device code

@@ -17,6 +17,10 @@ hipError_t launch_logit_rows(const Layout& L, const void* ws, int b, int h, int 
 hipError_t launch_knn(const ipa_knn_shape* s, const float* t, const uint8_t* mask, int32_t* idx, float* dist,
                       void* dgram, hipStream_t st);
 size_t bw_workspace_bytes(const ipa_shape* s);
+size_t bias_workspace_bytes(const ipa_bias_shape* s);
+hipError_t launch_bias_attention(const ipa_bias_shape* s, const void* q, const void* k, const void* v,
+                                 const void* phi_q, const void* phi_k, const uint8_t* key_mask, float* o, float* lse,
+                                 void* ws, hipStream_t st);
 hipError_t launch_backward(const ipa_shape* s, const ipa_lift_in* in, const ipa_epi_in* ep, const float* dupd,
                            const float* dloc, void* ws, ipa_grads* gr, hipStream_t st);
 }  // namespace fipa
@@ -164,6 +168,44 @@ ipa_status ipa_knn_distogram(const ipa_knn_shape* s, const float* translation, c
       (nn_dist && !aligned16(nn_dist)) || (dgram && !aligned16(dgram)))
     return IPA_ERR_ALIGN;
   return launch_status(fipa::launch_knn(s, translation, mask, nn_index, nn_dist, dgram, (hipStream_t)stream));
+}
+
+static ipa_status bias_shape_status(const ipa_bias_shape* s) {
+  if (!s) return IPA_ERR_NULL;
+  if (s->B <= 0 || s->N <= 0 || s->M <= 0 || s->H <= 0 || s->D <= 0 || s->Dv <= 0 || s->R < 0 ||
+      !(s->scale > -3.4028235e38f && s->scale < 3.4028235e38f))
+    return IPA_ERR_SHAPE;
+  if (s->causal && s->N != s->M) return IPA_ERR_SHAPE;
+  // grid: query tiles of 128 on x, heads on y, samples on z
+  if (s->N > (1 << 30) || s->M > (1 << 30) || s->H > 65535 || s->B > 65535) return IPA_ERR_SHAPE;
+  // lift grids: one thread per 8 lifted columns (at most 32 per row) of every padded row
+  const int64_t rows = (s->N > s->M ? s->N : s->M) + 127;
+  if (s->B * s->H * rows > ((int64_t)1 << 26)) return IPA_ERR_SHAPE;
+  if (s->dtype != IPA_F32 && s->dtype != IPA_BF16) return IPA_ERR_UNSUPPORTED;
+  if (s->phi_dtype != IPA_F32 && s->phi_dtype != IPA_BF16) return IPA_ERR_UNSUPPORTED;
+  if (s->Dv > 256 || s->D + 3 * s->R > 256) return IPA_ERR_UNSUPPORTED;
+  return IPA_OK;
+}
+
+size_t ipa_bias_workspace_bytes(const ipa_bias_shape* s) {
+  if (bias_shape_status(s) != IPA_OK) return 0;
+  return fipa::bias_workspace_bytes(s);
+}
+
+ipa_status ipa_bias_attention(const ipa_bias_shape* s, const void* q, const void* k, const void* v,
+                              const void* phi_q, const void* phi_k, const uint8_t* key_mask, float* o, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const ipa_status st = bias_shape_status(s);
+  if (st != IPA_OK) return st;
+  if (!q || !k || !v || !o || !lse || !workspace || (s->R > 0 && (!phi_q || !phi_k))) return IPA_ERR_NULL;
+  const size_t need = fipa::bias_workspace_bytes(s);
+  if (need == 0) return IPA_ERR_UNSUPPORTED;
+  if (workspace_bytes < need) return IPA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
+      (phi_q && !aligned16(phi_q)) || (phi_k && !aligned16(phi_k)) || (key_mask && !aligned16(key_mask)))
+    return IPA_ERR_ALIGN;
+  return launch_status(fipa::launch_bias_attention(s, q, k, v, phi_q, phi_k, key_mask, o, lse, workspace,
+                                                   (hipStream_t)stream));
 }
 
 const char* ipa_status_string(int status) {

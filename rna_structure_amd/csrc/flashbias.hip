@@ -1,0 +1,386 @@
+// Attention with a low-rank bias on gfx950 matrix cores (FlashBias: Fast
+// Computation of Attention with Bias, atlas.scime.ai summary, Approach: the
+// dense bias b_ij = phi_q(i) . phi_k(j) is carried by two factor tensors
+// concatenated onto the queries and keys, so a flash-attention kernel over
+// the widened rows never reads an [N, M] bias).
+//
+//   L_ij = scale q_i . k_j + phi_q(i) . phi_k(j),  O_i = softmax_j(L_ij) v_j
+//
+// Lift (one pass over the inputs, written to the workspace):
+//   Q~_i = [scale log2(e) q_i | per factor r: hi, hi, lo of log2(e) phi_q,r(i)]
+//   K~_j = [k_j               | per factor r: hi, lo, hi of phi_k,r(j)]
+// in bf16, zero-padded to W = 16 NQS columns, so that Q~_i . K~_j is L_ij in
+// log2 units with every factor product taken as hi.hi + hi.lo + lo.hi
+// (hi = bf16(x), lo = bf16(x - hi)): a factor keeps ~16 significant bits, so
+// exact factors with large entries (ALiBi's key position, squared norms of
+// coordinates) stay exact to ~1e-5 relative instead of bf16's 4e-3.  Values
+// are stored transposed per 64-key tile, keys permuted within every 16 as
+// [0-3, 8-11, 4-7, 12-15] (the order in which a 32x32 accumulator lane holds
+// them), plus one mask word per tile and wavefront half.
+//
+// Attention: a workgroup of four wavefronts takes 128 queries of one
+// (batch, head); each wavefront owns 32.  Per 64-key tile staged in LDS:
+//   S^T (keys x queries) = K~ Q~^T     v_mfma_f32_32x32x16_bf16, NQS K-steps
+//                                      per 32-key block
+//   online softmax in fp32 with exp2; the running maximum is raised only
+//   when a row maximum exceeds it by more than 8 (log2 units), so the
+//   probabilities stay below 2^8 and rescaling is rare
+//   O^T += V~^T P^T                    v_mfma_f32_32x32x16_bf16, the
+//                                      probabilities (rounded to bf16) taken
+//                                      straight from the S^T accumulators
+// The next tile's global loads are issued before the current tile's
+// arithmetic and land in LDS after it.  Causal attention stops at the tile
+// that holds the workgroup's last query.
+#include "mfma_tile.h"
+
+namespace fipa {
+
+namespace {
+
+constexpr float kBiasLog2e = 1.4426950408889634f;
+constexpr float kBiasLn2 = 0.6931471805599453f;
+
+struct BiasLayout {
+  int B, N, M, H, D, Dv, R, causal, bf, bfp;
+  float scale;
+  int NQS, NVB, W, DVP, Npad, Mpad, MT;
+  size_t off_q, off_k, off_v, off_m, total;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int pick_nqs(int w16) {
+  const int opts[] = {2, 3, 5, 9, 16};
+  for (int o : opts)
+    if (w16 <= o) return o;
+  return 0;
+}
+int pick_nvb(int v32) {
+  const int opts[] = {1, 2, 4, 8};
+  for (int o : opts)
+    if (v32 <= o) return o;
+  return 0;
+}
+
+bool make_bias_layout(const ipa_bias_shape* s, BiasLayout* L) {
+  // dimensions were range-checked by the caller (N, M <= 2^30, D + 3R <= 256, Dv <= 256)
+  L->B = (int)s->B; L->N = (int)s->N; L->M = (int)s->M; L->H = (int)s->H;
+  L->D = (int)s->D; L->Dv = (int)s->Dv; L->R = (int)s->R; L->causal = s->causal != 0;
+  L->bf = s->dtype == IPA_BF16;
+  L->bfp = s->phi_dtype == IPA_BF16;
+  L->scale = s->scale;
+  L->NQS = pick_nqs((L->D + 3 * L->R + 15) / 16);
+  L->NVB = pick_nvb((L->Dv + 31) / 32);
+  if (L->NQS == 0 || L->NVB == 0) return false;
+  L->W = 16 * L->NQS;
+  L->DVP = 32 * L->NVB;
+  L->Npad = (s->N + 127) / 128 * 128;
+  L->Mpad = (s->M + 63) / 64 * 64;
+  L->MT = L->Mpad / 64;
+  const size_t BH = (size_t)s->B * s->H;
+  size_t off = 0;
+  L->off_q = off; off = al256(off + BH * L->Npad * L->W * 2);
+  L->off_k = off; off = al256(off + BH * L->Mpad * L->W * 2);
+  L->off_v = off; off = al256(off + BH * L->Mpad * L->DVP * 2);
+  L->off_m = off; off = al256(off + (size_t)s->B * L->MT * 2 * 4);
+  L->total = off;
+  return true;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Column c of a lifted row.  side 0: query row (q scaled, factors hi hi lo),
+// side 1: key row (k, factors hi lo hi).
+template <bool BF, bool BFP>
+__device__ __forceinline__ float lifted(const BiasLayout& L, int side, const void* x, const void* phi, size_t xrow,
+                                        size_t prow, int c) {
+  if (c < L.D) {
+    const float v = ld<BF>(x, xrow + c);
+    return side == 0 ? v * (L.scale * kBiasLog2e) : v;
+  }
+  const int idx = c - L.D;
+  if (idx >= 3 * L.R) return 0.f;
+  const int r = idx / 3, part = idx - 3 * r;
+  const float f = ld<BFP>(phi, prow + r) * (side == 0 ? kBiasLog2e : 1.0f);
+  const float hi = bf16_bits_to_f32(f32_to_bf16_bits(f));
+  const bool want_lo = side == 0 ? part == 2 : part == 1;
+  return want_lo ? f - hi : hi;
+}
+
+// Lifted query (side 0) or key (side 1) rows: one thread per 8 columns.
+template <bool BF, bool BFP>
+__global__ __launch_bounds__(256) void bias_lift_rows_kernel(BiasLayout L, int side, const void* x, const void* phi,
+                                                             char* ws) {
+  const int rows = side == 0 ? L.Npad : L.Mpad, n = side == 0 ? L.N : L.M;
+  const int c8 = L.W / 8;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)L.B * L.H * rows * c8) return;
+  const int cc = (int)(idx % c8);
+  const long rr = idx / c8;
+  const int i = (int)(rr % rows);
+  const int h = (int)((rr / rows) % L.H), b = (int)(rr / ((long)rows * L.H));
+  uint4 out = make_uint4(0, 0, 0, 0);
+  if (i < n) {
+    const size_t xrow = (((size_t)b * n + i) * L.H + h) * L.D;
+    const size_t prow = (((size_t)b * n + i) * L.H + h) * L.R;
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = lifted<BF, BFP>(L, side, x, phi, xrow, prow, 8 * cc + e);
+    out = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
+  }
+  char* base = ws + (side == 0 ? L.off_q : L.off_k);
+  reinterpret_cast<uint4*>(base)[(((size_t)b * L.H + h) * rows + i) * c8 + cc] = out;
+}
+
+// Transposed value tiles [b][h][t][c][64], keys permuted within every 16
+// (column kappa holds key vt_key_of_col(kappa)); one thread per 8 columns of
+// one value row.
+template <bool BF>
+__global__ __launch_bounds__(256) void bias_lift_v_kernel(BiasLayout L, const void* v, char* ws) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)L.B * L.H * L.MT * L.DVP * 8) return;
+  const int k8 = (int)(idx & 7);
+  const long r = idx >> 3;
+  const int c = (int)(r % L.DVP);
+  const long r2 = r / L.DVP;
+  const int t = (int)(r2 % L.MT);
+  const int h = (int)((r2 / L.MT) % L.H), b = (int)(r2 / ((long)L.MT * L.H));
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = t * 64 + vt_key_of_col(8 * k8 + e);
+    f[e] = (c < L.Dv && j < L.M) ? ld<BF>(v, (((size_t)b * L.M + j) * L.H + h) * L.Dv + c) : 0.f;
+  }
+  reinterpret_cast<uint4*>(ws + L.off_v)[idx] =
+      make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
+}
+
+// Key-mask words: per (b, tile) two words; bit kb*16 + r of word h is key
+// kb*32 + 8*(r/4) + 4*h + r%4 (the key that lane half h holds in register r
+// of key block kb).
+__global__ __launch_bounds__(256) void bias_mask_kernel(BiasLayout L, const uint8_t* km, char* ws) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)L.B * L.MT * 2) return;
+  const int hw = (int)(idx & 1);
+  const long bt = idx >> 1;
+  const int t = (int)(bt % L.MT), b = (int)(bt / L.MT);
+  uint32_t w = 0;
+  for (int x = 0; x < 32; ++x) {
+    const int kb = x >> 4, r = x & 15;
+    const int j = t * 64 + kb * 32 + 8 * (r >> 2) + 4 * hw + (r & 3);
+    const bool ok = j < L.M && (km == nullptr || km[(size_t)b * L.M + j] != 0);
+    w |= (uint32_t)ok << x;
+  }
+  reinterpret_cast<uint32_t*>(ws + L.off_m)[idx] = w;
+}
+
+template <int NQS, int NVB>
+__global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
+  constexpr int W = 16 * NQS, DVP = 32 * NVB;
+  constexpr int KP = W + 8;   // LDS row pitch of the key tile (bf16)
+  constexpr int VP = 64 + 8;  // LDS row pitch of the transposed value tile (bf16)
+  constexpr int KCH = 64 * W / 8, VCH = DVP * 8;  // 16-byte chunks per tile
+  constexpr int KPT = (KCH + 255) / 256, VPT = VCH / 256;
+  __shared__ __align__(16) uint16_t sK[64 * KP];
+  __shared__ __align__(16) uint16_t sV[DVP * VP];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int q0 = blockIdx.x * 128, i = q0 + w * 32 + l32;
+  const size_t bh = (size_t)b * L.H + h;
+
+  const uint4* qrow = reinterpret_cast<const uint4*>(ws + L.off_q) + (bh * L.Npad + i) * (W / 8);
+  bf16x8_t bq[NQS];
+#pragma unroll
+  for (int ks = 0; ks < NQS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8_t, qrow[2 * ks + hf]);
+
+  const uint4* kg = reinterpret_cast<const uint4*>(ws + L.off_k) + bh * L.Mpad * (W / 8);
+  const uint4* vg = reinterpret_cast<const uint4*>(ws + L.off_v) + bh * L.MT * (DVP * 8);
+  const uint32_t* mw = reinterpret_cast<const uint32_t*>(ws + L.off_m) + (size_t)b * L.MT * 2;
+  const int tend = L.causal ? min(L.MT, (min(q0 + 127, L.N - 1) >> 6) + 1) : L.MT;
+
+  uint4 pk[KPT], pv[VPT];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+      const int ch = tid + 256 * x;
+      if (ch < KCH) pk[x] = kg[(size_t)t * KCH + ch];
+    }
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) pv[x] = vg[(size_t)t * VCH + tid + 256 * x];
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+      const int ch = tid + 256 * x;
+      if (ch < KCH) *reinterpret_cast<uint4*>(&sK[(ch / (W / 8)) * KP + (ch % (W / 8)) * 8]) = pk[x];
+    }
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+      const int ch = tid + 256 * x;
+      *reinterpret_cast<uint4*>(&sV[(ch >> 3) * VP + (ch & 7) * 8]) = pv[x];
+    }
+  };
+
+  f32x16_t oacc[NVB];
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[vb][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  if (tend > 0) fetch(0);
+  for (int t = 0; t < tend; ++t) {
+    __syncthreads();  // every wavefront is done with the previous tile
+    stage();
+    __syncthreads();
+    if (t + 1 < tend) fetch(t + 1);
+
+    // S^T for the tile's two 32-key blocks
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      const uint16_t* krow = &sK[(kb * 32 + l32) * KP + 8 * hf];
+#pragma unroll
+      for (int ks = 0; ks < NQS; ++ks)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + 16 * ks)), bq[ks], sacc[kb], 0, 0, 0);
+    }
+
+    // masks: key mask word of this lane half; causal keys beyond the query
+    const uint32_t w0 = __builtin_amdgcn_readfirstlane(mw[2 * t]), w1 = __builtin_amdgcn_readfirstlane(mw[2 * t + 1]);
+    const uint32_t word = hf ? w1 : w0;
+    const bool diag = L.causal && t * 64 + 63 > q0 + w * 32;
+    float s[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int x = kb * 16 + r;
+        bool ok = (word >> x) & 1u;
+        if (diag) ok = ok && (t * 64 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) <= i);
+        s[x] = ok ? sacc[kb][r] : -INFINITY;
+      }
+    float mt = s[0];
+#pragma unroll
+    for (int x = 1; x < 32; ++x) mt = fmaxf(mt, s[x]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if (mt > m + 8.0f) {
+      // first permitted key of the row, or a maximum that grew by more than 8
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mt);
+      m = mt;
+      l *= alpha;
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[vb][r] *= alpha;
+    }
+    bf16x8_t pb[4];
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) {
+      const float p = s[x] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[x] - m);
+      if (x & 1) ps1 += p; else ps0 += p;
+      pb[x >> 3][x & 7] = (__bf16)p;
+    }
+    l += ps0 + ps1;
+
+    // O^T += V~^T P^T: K-step j covers keys 16 j .. 16 j + 15 of the tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&sV[(32 * vb + l32) * VP + 16 * j + 8 * hf]);
+        oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb[j], oacc[vb], 0, 0, 0);
+      }
+  }
+
+  l += __shfl_xor(l, 32);
+  if (i >= L.N) return;
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.0f / l;
+  if (hf == 0) lse[bh * L.N + i] = empty ? -INFINITY : (m + log2f(l)) * kBiasLn2;
+  float* orow = o + (((size_t)b * L.N + i) * L.H + h) * L.Dv;
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * vb + 8 * g + 4 * hf;
+      const float4 v4 = make_float4(oacc[vb][4 * g] * inv, oacc[vb][4 * g + 1] * inv, oacc[vb][4 * g + 2] * inv,
+                                    oacc[vb][4 * g + 3] * inv);
+      if ((L.Dv & 3) == 0 && c + 3 < L.Dv) {
+        *reinterpret_cast<float4*>(orow + c) = v4;
+      } else {
+        if (c < L.Dv) orow[c] = v4.x;
+        if (c + 1 < L.Dv) orow[c + 1] = v4.y;
+        if (c + 2 < L.Dv) orow[c + 2] = v4.z;
+        if (c + 3 < L.Dv) orow[c + 3] = v4.w;
+      }
+    }
+}
+
+template <int NQS, int NVB>
+void launch_attn(const BiasLayout& L, const char* ws, float* o, float* lse, hipStream_t st) {
+  hipLaunchKernelGGL((bias_attn_kernel<NQS, NVB>), dim3(L.Npad / 128, L.H, L.B), dim3(256), 0, st, L, ws, o, lse);
+}
+
+template <int NQS>
+bool dispatch_nvb(const BiasLayout& L, const char* ws, float* o, float* lse, hipStream_t st) {
+  switch (L.NVB) {
+    case 1: launch_attn<NQS, 1>(L, ws, o, lse, st); return true;
+    case 2: launch_attn<NQS, 2>(L, ws, o, lse, st); return true;
+    case 4: launch_attn<NQS, 4>(L, ws, o, lse, st); return true;
+    case 8: launch_attn<NQS, 8>(L, ws, o, lse, st); return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+size_t bias_workspace_bytes(const ipa_bias_shape* s) {
+  BiasLayout L;
+  return make_bias_layout(s, &L) ? L.total : 0;
+}
+
+bool bias_supported(const ipa_bias_shape* s) {
+  BiasLayout L;
+  return make_bias_layout(s, &L);
+}
+
+hipError_t launch_bias_attention(const ipa_bias_shape* s, const void* q, const void* k, const void* v,
+                                 const void* phi_q, const void* phi_k, const uint8_t* key_mask, float* o, float* lse,
+                                 void* ws, hipStream_t st) {
+  BiasLayout L;
+  if (!make_bias_layout(s, &L)) return hipErrorInvalidValue;
+  char* w = reinterpret_cast<char*>(ws);
+  const long nq = (long)L.B * L.H * L.Npad * (L.W / 8), nk = (long)L.B * L.H * L.Mpad * (L.W / 8);
+  const long nv = (long)L.B * L.H * L.MT * L.DVP * 8, nm = (long)L.B * L.MT * 2;
+  auto rows = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, L, 0, q, phi_q, w);
+    hipLaunchKernelGGL(kern, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, st, L, 1, k, phi_k, w);
+  };
+  if (L.bf) {
+    if (L.bfp) rows(bias_lift_rows_kernel<true, true>); else rows(bias_lift_rows_kernel<true, false>);
+    hipLaunchKernelGGL(bias_lift_v_kernel<true>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, L, v, w);
+  } else {
+    if (L.bfp) rows(bias_lift_rows_kernel<false, true>); else rows(bias_lift_rows_kernel<false, false>);
+    hipLaunchKernelGGL(bias_lift_v_kernel<false>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, L, v, w);
+  }
+  hipLaunchKernelGGL(bias_mask_kernel, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, st, L, key_mask, w);
+  bool ok = false;
+  switch (L.NQS) {
+    case 2: ok = dispatch_nvb<2>(L, w, o, lse, st); break;
+    case 3: ok = dispatch_nvb<3>(L, w, o, lse, st); break;
+    case 5: ok = dispatch_nvb<5>(L, w, o, lse, st); break;
+    case 9: ok = dispatch_nvb<9>(L, w, o, lse, st); break;
+    case 16: ok = dispatch_nvb<16>(L, w, o, lse, st); break;
+  }
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace fipa

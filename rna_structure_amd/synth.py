@@ -256,3 +256,67 @@ def make_config(name: str, seed: Optional[int] = None) -> dict:
     if seed is None:
         seed = 1000 * _CONFIG_INDEX[name] + shape.N
     return make_inputs(shape, seed, **cfg["kw"])
+
+
+def make_bias_inputs(B: int, N: int, M: int, H: int, D: int, Dv: int, R: int, seed: int, *,
+                     kind: str = "random", dtype: str = "bf16", phi_dtype: str = "f32", masked_keys=(),
+                     empty_sample: bool = False,
+                     box: float = 1.0, gamma=None) -> dict:
+    """Inputs of attention with a low-rank bias: q [B,N,H,D], k [B,M,H,D],
+    v [B,M,H,Dv] (standard normal, rounded to `dtype`, "f32" or "bf16"), bias
+    factors phi_q [B,N,H,R], phi_k [B,M,H,R] (rounded to `phi_dtype`) and
+    key_mask [B,M] (True = permitted).  The factors are inputs here, written out from
+    the bias they stand for:
+
+      kind "random": standard normal factors;
+      kind "alibi":  R = 2, phi_q(i) = [-m_h i, m_h], phi_k(j) = [1, j] with
+                     m_h = 2^(-8 (h+1) / H) (with causal attention this is the
+                     ALiBi bias -m_h (i - j));
+      kind "sqdist": R = 5, points x_i, y_j uniform in a cube of side `box`,
+                     phi_q(i) = [-g_h |x_i|^2, 2 g_h x_i, -g_h],
+                     phi_k(j) = [1, y_j, |y_j|^2] (the bias -g_h |x_i - y_j|^2);
+                     g_h from `gamma` (default: H values spread over
+                     [0.5, 4] / box^2).
+
+    `masked_keys` lists key indices masked in every sample; `empty_sample`
+    masks every key of the last sample."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, N, H, D))
+    k = rng.standard_normal((B, M, H, D))
+    v = rng.standard_normal((B, M, H, Dv))
+    if kind == "random":
+        pq = rng.standard_normal((B, N, H, R))
+        pk = rng.standard_normal((B, M, H, R))
+    elif kind == "alibi":
+        assert R == 2
+        m = 2.0 ** (-8.0 * (np.arange(H) + 1) / H)
+        i = np.arange(N, dtype=np.float64)[None, :, None]
+        j = np.arange(M, dtype=np.float64)[None, :, None]
+        pq = np.stack(np.broadcast_arrays(-m * i, m * np.ones_like(i)), -1)
+        pk = np.stack(np.broadcast_arrays(np.ones_like(j) * np.ones(H), j * np.ones(H)), -1)
+        pq = np.broadcast_to(pq, (B, N, H, 2))
+        pk = np.broadcast_to(pk, (B, M, H, 2))
+    elif kind == "sqdist":
+        assert R == 5
+        x = box * rng.random((B, N, 3))
+        y = x[:, :M] if M <= N and N == M else box * rng.random((B, M, 3))
+        g = np.asarray(gamma if gamma is not None else np.linspace(0.5, 4.0, H) / box ** 2, np.float64)
+        xx = np.sum(x * x, -1)[..., None, None]
+        yy = np.sum(y * y, -1)[..., None, None]
+        gg = g[None, None, :, None]
+        pq = np.concatenate([-gg * xx, 2.0 * gg * x[:, :, None, :], np.broadcast_to(-gg, (B, N, H, 1))], -1)
+        pk = np.concatenate([np.ones((B, M, H, 1)), np.broadcast_to(y[:, :, None, :], (B, M, H, 3)),
+                             np.broadcast_to(yy, (B, M, H, 1))], -1)
+    else:
+        raise ValueError(kind)
+    km = np.ones((B, M), bool)
+    for j0 in masked_keys:
+        km[:, j0] = False
+    if empty_sample:
+        km[-1] = False
+    out = {n: round_to(np.ascontiguousarray(a, dtype=np.float32), dtype) for n, a in (("q", q), ("k", k), ("v", v))}
+    for n, a in (("phi_q", pq), ("phi_k", pk)):
+        out[n] = round_to(np.ascontiguousarray(a, dtype=np.float32), phi_dtype)
+    out["key_mask"] = km
+    out["dims"] = dict(B=B, N=N, M=M, H=H, D=D, Dv=Dv, R=R, dtype=dtype, phi_dtype=phi_dtype)
+    return out

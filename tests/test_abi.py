@@ -182,3 +182,46 @@ def test_backward_validation_before_launch(lib):
     gr1.q = 4100
     assert call(s, gr=gr1) == 4
     assert call(s, n=16) == 2                                            # workspace too small
+
+
+def test_bias_struct_size_matches_c():
+    assert ctypes.sizeof(_lib.IpaBiasShape) == 7 * 8 + 4 * 4
+
+
+def test_bias_attention_validation_before_launch(lib):
+    def bs(**kw):
+        base = dict(B=2, N=300, M=300, H=4, D=64, Dv=64, R=2, dtype=1, phi_dtype=0, causal=0, scale=0.125)
+        base.update(kw)
+        return _lib.IpaBiasShape(*[base[n] for n, _ in _lib.IpaBiasShape._fields_])
+
+    ws = _lib.ipa_bias_workspace_bytes(bs())
+    assert ws > 0
+    # linear in the sequence lengths (no [N, M] array)
+    w1 = _lib.ipa_bias_workspace_bytes(bs(N=8192, M=8192))
+    w2 = _lib.ipa_bias_workspace_bytes(bs(N=16384, M=16384))
+    assert 1.9 < w2 / w1 < 2.1
+    for bad in (dict(B=0), dict(N=0), dict(M=0), dict(H=0), dict(D=0), dict(Dv=0), dict(R=-1),
+                dict(scale=float("inf")), dict(scale=float("nan")), dict(causal=1, M=301), dict(H=70000)):
+        assert _lib.ipa_bias_workspace_bytes(bs(**bad)) == 0, bad
+    for unsup in (dict(dtype=3), dict(phi_dtype=2), dict(Dv=257), dict(D=250, R=3)):
+        assert _lib.ipa_bias_workspace_bytes(bs(**unsup)) == 0, unsup
+    assert _lib.ipa_bias_workspace_bytes(bs(D=247, R=3)) > 0          # D + 3R = 256
+    assert _lib.ipa_bias_workspace_bytes(bs(R=0)) > 0
+
+    big = 1 << 40
+    def call(s, q=4096, k=4096, v=4096, pq=4096, pk=4096, km=None, o=4096, lse=4096, w=4096, n=big):
+        return lib.ipa_bias_attention(ctypes.byref(s), q, k, v, pq, pk, km, o, lse, w, n, None)
+    assert lib.ipa_bias_attention(None, 4096, 4096, 4096, 4096, 4096, None, 4096, 4096, 4096, big, None) == 1
+    for name in ("q", "k", "v", "pq", "pk", "o", "lse", "w"):
+        assert call(bs(), **{name: None}) == 1, name
+    # factors are optional without a bias: the call gets past the pointer checks
+    # (and stops at the misaligned q, before any launch)
+    assert call(bs(R=0), q=4100, pq=None, pk=None) == 4
+    assert call(bs(N=0)) == 2
+    assert call(bs(causal=1, M=200)) == 2
+    assert call(bs(dtype=5)) == 3
+    assert call(bs(Dv=300)) == 3
+    assert call(bs(), n=ws - 1) == 2                                  # workspace too small
+    for name in ("q", "k", "v", "pq", "pk", "o", "lse", "w"):
+        assert call(bs(), **{name: 4100}) == 4, name
+    assert call(bs(), km=4097) == 4

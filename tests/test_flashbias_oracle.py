@@ -121,3 +121,22 @@ def test_row_constant_bias_only_shifts_lse():
     f1 = flashbias_attention(q, k, v, c, np.ones((B, N, H, 1)), 0.5)
     np.testing.assert_allclose(f1["o"], f0["o"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(f1["lse"], f0["lse"] + c[..., 0].transpose(0, 2, 1), rtol=1e-12)
+
+
+def test_synthetic_factors_are_the_oracle_biases():
+    """The input generator's ALiBi and squared-distance factors are the biases
+    the oracle's factor functions define (so GPU cases test those biases)."""
+    from rna_structure_amd.synth import make_bias_inputs
+    inp = make_bias_inputs(1, 50, 50, 3, 4, 4, 2, seed=1, kind="alibi")
+    pq, pk = alibi_factors(1, 50, 3)
+    np.testing.assert_allclose(np.einsum("bihr,bjhr->bhij", inp["phi_q"], inp["phi_k"]),
+                               np.einsum("bihr,bjhr->bhij", pq, pk), rtol=1e-6, atol=1e-5)
+    inp = make_bias_inputs(2, 30, 30, 2, 4, 4, 5, seed=2, kind="sqdist", box=5.0, phi_dtype="f32")
+    prod = np.einsum("bihr,bjhr->bhij", inp["phi_q"], inp["phi_k"])
+    # recover the points from the key factors and compare with the definition
+    y = inp["phi_k"][:, :, 0, 1:4]
+    g = -inp["phi_q"][0, 0, :, 4]
+    for b in range(2):
+        d2 = cdist(y[b], y[b], "sqeuclidean")
+        for h in range(2):
+            np.testing.assert_allclose(prod[b, h], -g[h] * d2, rtol=1e-4, atol=1e-3 * g[h] * 75)
