@@ -347,6 +347,64 @@ def hbm_calibration(mib: int = 2048, reps: int = 10) -> dict:
     return res
 
 
+# Attention with a low-rank bias (bf16 matrix cores): algorithmic flops per
+# (query, permitted key, head) 2 (D + R) for the logit with its bias and 2 Dv
+# for the output, against the dense bf16 MFMA peak.  Workloads named after the
+# FlashBias page's settings: a GPT-2-style causal ALiBi layer at N = 2048 (25
+# heads of 64, the 1.5B model's), and a squared-distance bias over the 32186
+# points of the PDE case (8 heads of 32, points in the unit cube).
+FLASHBIAS_WORKLOADS = (
+    ("alibi_gpt2_2048", dict(B=8, N=2048, M=2048, H=25, D=64, Dv=64, R=2), "alibi", True, 10),
+    ("sqdist_pde_32186", dict(B=1, N=32186, M=32186, H=8, D=32, Dv=32, R=5), "sqdist", False, 5),
+)
+
+
+def time_flashbias(name, dims, kind, causal, steps, min_warm_ms=40.0):
+    import numpy as np
+    import torch
+    from rna_structure_amd import _lib
+    from rna_structure_amd.synth import make_bias_inputs
+    inp = make_bias_inputs(**dims, seed=8000 + dims["N"], kind=kind)
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(dt).contiguous()
+    q, k, v = (dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    pq, pk = (dev(inp[n], torch.float32) for n in ("phi_q", "phi_k"))
+    km = torch.from_numpy(inp["key_mask"].astype(np.uint8)).cuda()
+    f = _lib.BiasAttention(dims["B"], dims["N"], dims["M"], dims["H"], dims["D"], dims["Dv"], dims["R"],
+                           1.0 / math.sqrt(dims["D"]), causal, "bf16", "f32")
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    warm = 0.0
+    while warm < min_warm_ms:
+        e0.record(st)
+        for _ in range(3):
+            f(q, k, v, pq, pk, km, stream=st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        warm += e0.elapsed_time(e1)
+    e0.record(st)
+    for _ in range(steps):
+        f(q, k, v, pq, pk, km, stream=st)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    B, N, M, H = dims["B"], dims["N"], dims["M"], dims["H"]
+    pairs = B * H * (N * (N + 1) // 2 if causal else N * M)
+    flops = pairs * (2 * (dims["D"] + dims["R"]) + 2 * dims["Dv"])
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": name, **dims, "kind": kind, "causal": causal, "inputs": "bf16 q/k/v, fp32 factors",
+            "ms": round(ms, 4), "pair_heads": pairs, "flops_per_pair_head": 2 * (dims["D"] + dims["R"]) + 2 * dims["Dv"],
+            "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def flashbias_section(args):
+    res = []
+    for name, dims, kind, causal, steps in FLASHBIAS_WORKLOADS:
+        res.append(time_flashbias(name, dims, kind, causal, max(steps, args.steps // 2)))
+        print(f"# flashbias {res[-1]}", file=sys.stderr, flush=True)
+    return {"peak_bf16_tflops": PEAK_BF16_TFLOPS, "runs": res}
+
+
 def knn_section(args):
     res = []
     for name, B, N, kw in KNN_WORKLOADS:
@@ -370,6 +428,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward section")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only the backward section and print it as the JSON line")
+    ap.add_argument("--no-flashbias", action="store_true", help="skip the low-rank-bias attention section")
+    ap.add_argument("--flashbias-only", action="store_true",
+                    help="run only the low-rank-bias attention section and print it as the JSON line")
     ap.add_argument("--knn-only", action="store_true",
                     help="run only the kNN distogram section and print it as the JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -394,6 +455,9 @@ def main():
         return
     if args.backward_only:
         print(json.dumps({"backward": backward_section(args)}), flush=True)
+        return
+    if args.flashbias_only:
+        print(json.dumps({"flashbias": flashbias_section(args)}), flush=True)
         return
     inp = make_workload(args.workload)
     shape = inp["shape"]
@@ -484,6 +548,8 @@ def main():
         out["knn_distogram"] = knn_section(args)
     if not args.no_sweep and not args.no_backward:
         out["backward"] = backward_section(args)
+    if not args.no_sweep and not args.no_flashbias:
+        out["flashbias"] = flashbias_section(args)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, flops)

@@ -37,6 +37,7 @@ namespace fipa {
 
 namespace {
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kBiasLog2e = 1.4426950408889634f;
 constexpr float kBiasLn2 = 0.6931471805599453f;
 
@@ -50,7 +51,7 @@ struct BiasLayout {
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int pick_nqs(int w16) {
-  const int opts[] = {2, 3, 5, 9, 16};
+  const int opts[] = {2, 3, 4, 5, 8, 9, 16};
   for (int o : opts)
     if (w16 <= o) return o;
   return 0;
@@ -196,33 +197,20 @@ __global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char
 #pragma unroll
   for (int ks = 0; ks < NQS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8_t, qrow[2 * ks + hf]);
 
-  const uint4* kg = reinterpret_cast<const uint4*>(ws + L.off_k) + bh * L.Mpad * (W / 8);
-  const uint4* vg = reinterpret_cast<const uint4*>(ws + L.off_v) + bh * L.MT * (DVP * 8);
+  const u32x4_t* kg = reinterpret_cast<const u32x4_t*>(ws + L.off_k) + bh * L.Mpad * (W / 8);
+  const u32x4_t* vg = reinterpret_cast<const u32x4_t*>(ws + L.off_v) + bh * L.MT * (DVP * 8);
   const uint32_t* mw = reinterpret_cast<const uint32_t*>(ws + L.off_m) + (size_t)b * L.MT * 2;
   const int tend = L.causal ? min(L.MT, (min(q0 + 127, L.N - 1) >> 6) + 1) : L.MT;
 
-  uint4 pk[KPT], pv[VPT];
-  auto fetch = [&](int t) {
+  u32x4_t pk[KPT], pv[VPT];
+  // tile 0 into registers
 #pragma unroll
-    for (int x = 0; x < KPT; ++x) {
-      const int ch = tid + 256 * x;
-      if (ch < KCH) pk[x] = kg[(size_t)t * KCH + ch];
-    }
+  for (int x = 0; x < KPT; ++x) {
+    const int ch = tid + 256 * x;
+    pk[x] = kg[ch < KCH ? ch : 0];
+  }
 #pragma unroll
-    for (int x = 0; x < VPT; ++x) pv[x] = vg[(size_t)t * VCH + tid + 256 * x];
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int x = 0; x < KPT; ++x) {
-      const int ch = tid + 256 * x;
-      if (ch < KCH) *reinterpret_cast<uint4*>(&sK[(ch / (W / 8)) * KP + (ch % (W / 8)) * 8]) = pk[x];
-    }
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) {
-      const int ch = tid + 256 * x;
-      *reinterpret_cast<uint4*>(&sV[(ch >> 3) * VP + (ch & 7) * 8]) = pv[x];
-    }
-  };
+  for (int x = 0; x < VPT; ++x) pv[x] = vg[tid + 256 * x];
 
   f32x16_t oacc[NVB];
 #pragma unroll
@@ -231,12 +219,29 @@ __global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char
     for (int r = 0; r < 16; ++r) oacc[vb][r] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  if (tend > 0) fetch(0);
   for (int t = 0; t < tend; ++t) {
     __syncthreads();  // every wavefront is done with the previous tile
-    stage();
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+      const int ch = tid + 256 * x;
+      if (ch < KCH) *reinterpret_cast<u32x4_t*>(&sK[(ch / (W / 8)) * KP + (ch % (W / 8)) * 8]) = pk[x];
+    }
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+      const int ch = tid + 256 * x;
+      *reinterpret_cast<u32x4_t*>(&sV[(ch >> 3) * VP + (ch & 7) * 8]) = pv[x];
+    }
     __syncthreads();
-    if (t + 1 < tend) fetch(t + 1);
+    if (t + 1 < tend) {
+      // the next tile's loads run during this tile's arithmetic
+#pragma unroll
+      for (int x = 0; x < KPT; ++x) {
+        const int ch = tid + 256 * x;
+        pk[x] = kg[(size_t)(t + 1) * KCH + (ch < KCH ? ch : 0)];
+      }
+#pragma unroll
+      for (int x = 0; x < VPT; ++x) pv[x] = vg[(size_t)(t + 1) * VCH + tid + 256 * x];
+    }
 
     // S^T for the tile's two 32-key blocks
     f32x16_t sacc[2];
@@ -259,12 +264,18 @@ __global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int x = kb * 16 + r;
-        bool ok = (word >> x) & 1u;
-        if (diag) ok = ok && (t * 64 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) <= i);
-        s[x] = ok ? sacc[kb][r] : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r) s[kb * 16 + r] = sacc[kb][r];
+    if ((w0 & w1) != 0xFFFFFFFFu || diag) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int x = kb * 16 + r;
+          bool ok = (word >> x) & 1u;
+          if (diag) ok = ok && (t * 64 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) <= i);
+          s[x] = ok ? s[x] : -INFINITY;
+        }
+    }
     float mt = s[0];
 #pragma unroll
     for (int x = 1; x < 32; ++x) mt = fmaxf(mt, s[x]);
@@ -279,11 +290,14 @@ __global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[vb][r] *= alpha;
     }
+    // while no key of the row has been permitted, m is -inf and so is every s:
+    // subtracting 0 instead keeps exp2(-inf) = 0
+    const float ms = m == -INFINITY ? 0.f : m;
     bf16x8_t pb[4];
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int x = 0; x < 32; ++x) {
-      const float p = s[x] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[x] - m);
+      const float p = __builtin_amdgcn_exp2f(s[x] - ms);
       if (x & 1) ps1 += p; else ps0 += p;
       pb[x >> 3][x & 7] = (__bf16)p;
     }
@@ -375,7 +389,9 @@ hipError_t launch_bias_attention(const ipa_bias_shape* s, const void* q, const v
   switch (L.NQS) {
     case 2: ok = dispatch_nvb<2>(L, w, o, lse, st); break;
     case 3: ok = dispatch_nvb<3>(L, w, o, lse, st); break;
+    case 4: ok = dispatch_nvb<4>(L, w, o, lse, st); break;
     case 5: ok = dispatch_nvb<5>(L, w, o, lse, st); break;
+    case 8: ok = dispatch_nvb<8>(L, w, o, lse, st); break;
     case 9: ok = dispatch_nvb<9>(L, w, o, lse, st); break;
     case 16: ok = dispatch_nvb<16>(L, w, o, lse, st); break;
   }

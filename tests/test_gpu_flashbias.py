@@ -63,6 +63,7 @@ CASES = [
     ("widest", dict(B=1, N=130, M=200, H=1, D=128, Dv=256, R=40), 5, "random", False, dict()),
     ("d128", dict(B=1, N=200, M=200, H=2, D=128, Dv=128, R=2), 6, "random", True, dict()),
     ("no-bias", dict(B=1, N=190, M=190, H=2, D=64, Dv=64, R=0), 7, "random", False, dict()),
+    ("no-bias-d128", dict(B=1, N=150, M=150, H=1, D=128, Dv=64, R=0), 10, "random", True, dict()),
     ("bf16-factors", dict(B=1, N=129, M=129, H=2, D=32, Dv=32, R=3), 8, "random", False, dict(phi_dtype="bf16")),
     ("one-query", dict(B=1, N=1, M=1, H=1, D=4, Dv=4, R=1), 9, "random", True, dict(dtype="f32")),
 ]
