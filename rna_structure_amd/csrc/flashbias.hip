@@ -114,48 +114,73 @@ __device__ __forceinline__ float lifted(const BiasLayout& L, int side, const voi
 template <bool BF, bool BFP>
 __global__ __launch_bounds__(256) void bias_lift_rows_kernel(BiasLayout L, int side, const void* x, const void* phi,
                                                              char* ws) {
-  const int rows = side == 0 ? L.Npad : L.Mpad, n = side == 0 ? L.N : L.M;
-  const int c8 = L.W / 8;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)L.B * L.H * rows * c8) return;
-  const int cc = (int)(idx % c8);
-  const long rr = idx / c8;
-  const int i = (int)(rr % rows);
-  const int h = (int)((rr / rows) % L.H), b = (int)(rr / ((long)rows * L.H));
+  // 32-bit indices: B H rows c8 < 2^31 (checked on the host)
+  const uint32_t rows = side == 0 ? L.Npad : L.Mpad, n = side == 0 ? L.N : L.M;
+  const uint32_t c8 = L.W / 8;
+  const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+  if (idx >= (uint32_t)L.B * L.H * rows * c8) return;
+  const uint32_t rr = idx / c8, cc = idx - rr * c8;
+  const uint32_t bh = rr / rows, i = rr - bh * rows;
+  const uint32_t b = bh / L.H, h = bh - b * L.H;
   uint4 out = make_uint4(0, 0, 0, 0);
   if (i < n) {
     const size_t xrow = (((size_t)b * n + i) * L.H + h) * L.D;
     const size_t prow = (((size_t)b * n + i) * L.H + h) * L.R;
+    const int c0 = 8 * cc;
     float f[8];
+    if ((L.D & 7) == 0 && c0 + 8 <= L.D) {
+      // eight q or k columns: one 16-byte (bf16) or two 16-byte (fp32) loads
+      const float mul = side == 0 ? L.scale * kBiasLog2e : 1.0f;
+      if constexpr (BF) {
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + xrow + c0);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = lifted<BF, BFP>(L, side, x, phi, xrow, prow, 8 * cc + e);
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = __uint_as_float(w4[e] << 16) * mul;
+          f[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u) * mul;
+        }
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + xrow + c0);
+        const float4 c = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + xrow + c0 + 4);
+        f[0] = a.x * mul; f[1] = a.y * mul; f[2] = a.z * mul; f[3] = a.w * mul;
+        f[4] = c.x * mul; f[5] = c.y * mul; f[6] = c.z * mul; f[7] = c.w * mul;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = lifted<BF, BFP>(L, side, x, phi, xrow, prow, c0 + e);
+    }
     out = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
   }
   char* base = ws + (side == 0 ? L.off_q : L.off_k);
-  reinterpret_cast<uint4*>(base)[(((size_t)b * L.H + h) * rows + i) * c8 + cc] = out;
+  reinterpret_cast<uint4*>(base)[idx] = out;
 }
 
 // Transposed value tiles [b][h][t][c][64], keys permuted within every 16
-// (column kappa holds key vt_key_of_col(kappa)); one thread per 8 columns of
-// one value row.
+// (column kappa holds key vt_key_of_col(kappa)).  A workgroup takes one
+// 64-key tile and 32 value columns of one (b, h): it reads the 64 rows'
+// 32-column pieces, transposes them in LDS and writes 32 rows of 64 keys
+// (8 threads per row, 16 bytes each).
 template <bool BF>
 __global__ __launch_bounds__(256) void bias_lift_v_kernel(BiasLayout L, const void* v, char* ws) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)L.B * L.H * L.MT * L.DVP * 8) return;
-  const int k8 = (int)(idx & 7);
-  const long r = idx >> 3;
-  const int c = (int)(r % L.DVP);
-  const long r2 = r / L.DVP;
-  const int t = (int)(r2 % L.MT);
-  const int h = (int)((r2 / L.MT) % L.H), b = (int)(r2 / ((long)L.MT * L.H));
+  __shared__ float sT[64][33];
+  const int cb = blockIdx.x % (L.DVP / 32);
+  const int t = (blockIdx.x / (L.DVP / 32)) % L.MT;
+  const int bh = blockIdx.x / ((L.DVP / 32) * L.MT);
+  const int h = bh % L.H, b = bh / L.H;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const int e = tid + 256 * x;  // 64 keys x 32 columns, columns fastest
+    const int jj = e >> 5, c = 32 * cb + (e & 31), j = t * 64 + jj;
+    sT[jj][e & 31] = (c < L.Dv && j < L.M) ? ld<BF>(v, (((size_t)b * L.M + j) * L.H + h) * L.Dv + c) : 0.f;
+  }
+  __syncthreads();
+  const int cl = tid >> 3, k8 = tid & 7;
   float f[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int j = t * 64 + vt_key_of_col(8 * k8 + e);
-    f[e] = (c < L.Dv && j < L.M) ? ld<BF>(v, (((size_t)b * L.M + j) * L.H + h) * L.Dv + c) : 0.f;
-  }
-  reinterpret_cast<uint4*>(ws + L.off_v)[idx] =
-      make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
+  for (int e = 0; e < 8; ++e) f[e] = sT[vt_key_of_col(8 * k8 + e)][cl];
+  uint4* dst = reinterpret_cast<uint4*>(ws + L.off_v) + (((size_t)bh * L.MT + t) * L.DVP + 32 * cb + cl) * 8 + k8;
+  *dst = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
 }
 
 // Key-mask words: per (b, tile) two words; bit kb*16 + r of word h is key
@@ -177,19 +202,31 @@ __global__ __launch_bounds__(256) void bias_mask_kernel(BiasLayout L, const uint
   reinterpret_cast<uint32_t*>(ws + L.off_m)[idx] = w;
 }
 
+// Three wavefronts per SIMD where the instance's registers fit (168 each)
+// without spilling, else no occupancy constraint.
+constexpr int bias_waves(int nqs, int nvb) {
+  return ((nvb <= 2 && nqs <= 5) || (nvb == 1 && nqs <= 9) || (nvb == 4 && nqs == 2)) ? 3 : 1;
+}
+
 template <int NQS, int NVB>
-__global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bias_waves(NQS, NVB))))
+void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
   constexpr int W = 16 * NQS, DVP = 32 * NVB;
   constexpr int KP = W + 8;   // LDS row pitch of the key tile (bf16)
   constexpr int VP = 64 + 8;  // LDS row pitch of the transposed value tile (bf16)
   constexpr int KCH = 64 * W / 8, VCH = DVP * 8;  // 16-byte chunks per tile
   constexpr int KPT = (KCH + 255) / 256, VPT = VCH / 256;
-  __shared__ __align__(16) uint16_t sK[64 * KP];
-  __shared__ __align__(16) uint16_t sV[DVP * VP];
+  // key tile, value tile; after the last tile, 32x36-float output blocks per wavefront
+  constexpr int KB = 64 * KP * 2, VB = DVP * VP * 2, SB = 4 * 32 * 36 * 4;
+  __shared__ __align__(16) char smem[KB + VB > SB ? KB + VB : SB];
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + KB);
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int q0 = blockIdx.x * 128, i = q0 + w * 32 + l32;
+  // causal: the query tiles with the most key tiles are launched first
+  const int qt = L.causal ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const int q0 = qt * 128, i = q0 + w * 32 + l32;
   const size_t bh = (size_t)b * L.H + h;
 
   const uint4* qrow = reinterpret_cast<const uint4*>(ws + L.off_q) + (bh * L.Npad + i) * (W / 8);
@@ -243,6 +280,9 @@ __global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char
       for (int x = 0; x < VPT; ++x) pv[x] = vg[(size_t)(t + 1) * VCH + tid + 256 * x];
     }
 
+    // causal: a tile whose first key is past the wavefront's last query adds nothing
+    if (L.causal && t * 64 > q0 + w * 32 + 31) continue;
+
     // S^T for the tile's two 32-key blocks
     f32x16_t sacc[2];
 #pragma unroll
@@ -265,16 +305,18 @@ __global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb * 16 + r] = sacc[kb][r];
-    if ((w0 & w1) != 0xFFFFFFFFu || diag) {
+    if ((w0 & w1) != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int x = 0; x < 32; ++x) s[x] = ((word >> x) & 1u) ? s[x] : -INFINITY;
+    }
+    if (diag) {
+      // key kb*32 + 8*(r/4) + 4*hf + r%4 of the tile is permitted up to query i
+      const int lim = i - t * 64 - 4 * hf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int x = kb * 16 + r;
-          bool ok = (word >> x) & 1u;
-          if (diag) ok = ok && (t * 64 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3) <= i);
-          s[x] = ok ? s[x] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          s[kb * 16 + r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? s[kb * 16 + r] : -INFINITY;
     }
     float mt = s[0];
 #pragma unroll
@@ -314,27 +356,41 @@ __global__ __launch_bounds__(256) void bias_attn_kernel(BiasLayout L, const char
   }
 
   l += __shfl_xor(l, 32);
-  if (i >= L.N) return;
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.0f / l;
-  if (hf == 0) lse[bh * L.N + i] = empty ? -INFINITY : (m + log2f(l)) * kBiasLn2;
-  float* orow = o + (((size_t)b * L.N + i) * L.H + h) * L.Dv;
+  if (hf == 0 && i < L.N) lse[bh * L.N + i] = empty ? -INFINITY : (m + log2f(l)) * kBiasLn2;
+  // O^T (value columns x this wavefront's 32 queries) through LDS, one block
+  // of 32 columns at a time, so that every query row is written as whole
+  // 128-byte pieces of consecutive columns
+  __syncthreads();  // the last tile's LDS reads are done in every wavefront
+  float* so = reinterpret_cast<float*>(smem) + w * 32 * 36;
+  const int cq = lane & 7;  // 16-byte piece of a row
 #pragma unroll
-  for (int vb = 0; vb < NVB; ++vb)
+  for (int vb = 0; vb < NVB; ++vb) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int c = 32 * vb + 8 * g + 4 * hf;
-      const float4 v4 = make_float4(oacc[vb][4 * g] * inv, oacc[vb][4 * g + 1] * inv, oacc[vb][4 * g + 2] * inv,
-                                    oacc[vb][4 * g + 3] * inv);
-      if ((L.Dv & 3) == 0 && c + 3 < L.Dv) {
-        *reinterpret_cast<float4*>(orow + c) = v4;
-      } else {
-        if (c < L.Dv) orow[c] = v4.x;
-        if (c + 1 < L.Dv) orow[c + 1] = v4.y;
-        if (c + 2 < L.Dv) orow[c + 2] = v4.z;
-        if (c + 3 < L.Dv) orow[c + 3] = v4.w;
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(&so[l32 * 36 + 8 * g + 4 * hf]) =
+          make_float4(oacc[vb][4 * g] * inv, oacc[vb][4 * g + 1] * inv, oacc[vb][4 * g + 2] * inv,
+                      oacc[vb][4 * g + 3] * inv);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int qq = 8 * x + (lane >> 3), iq = q0 + w * 32 + qq, c = 32 * vb + 4 * cq;
+      const float4 v4 = *reinterpret_cast<const float4*>(&so[qq * 36 + 4 * cq]);
+      if (iq < L.N && c < L.Dv) {
+        float* orow = o + (((size_t)b * L.N + iq) * L.H + h) * L.Dv;
+        if ((L.Dv & 3) == 0) {
+          *reinterpret_cast<float4*>(orow + c) = v4;
+        } else {
+          orow[c] = v4.x;
+          if (c + 1 < L.Dv) orow[c + 1] = v4.y;
+          if (c + 2 < L.Dv) orow[c + 2] = v4.z;
+          if (c + 3 < L.Dv) orow[c + 3] = v4.w;
+        }
       }
     }
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 template <int NQS, int NVB>
@@ -372,17 +428,17 @@ hipError_t launch_bias_attention(const ipa_bias_shape* s, const void* q, const v
   if (!make_bias_layout(s, &L)) return hipErrorInvalidValue;
   char* w = reinterpret_cast<char*>(ws);
   const long nq = (long)L.B * L.H * L.Npad * (L.W / 8), nk = (long)L.B * L.H * L.Mpad * (L.W / 8);
-  const long nv = (long)L.B * L.H * L.MT * L.DVP * 8, nm = (long)L.B * L.MT * 2;
+  const long nv = (long)L.B * L.H * L.MT * (L.DVP / 32), nm = (long)L.B * L.MT * 2;
   auto rows = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, L, 0, q, phi_q, w);
     hipLaunchKernelGGL(kern, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, st, L, 1, k, phi_k, w);
   };
   if (L.bf) {
     if (L.bfp) rows(bias_lift_rows_kernel<true, true>); else rows(bias_lift_rows_kernel<true, false>);
-    hipLaunchKernelGGL(bias_lift_v_kernel<true>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, L, v, w);
+    hipLaunchKernelGGL(bias_lift_v_kernel<true>, dim3((unsigned)nv), dim3(256), 0, st, L, v, w);
   } else {
     if (L.bfp) rows(bias_lift_rows_kernel<false, true>); else rows(bias_lift_rows_kernel<false, false>);
-    hipLaunchKernelGGL(bias_lift_v_kernel<false>, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, L, v, w);
+    hipLaunchKernelGGL(bias_lift_v_kernel<false>, dim3((unsigned)nv), dim3(256), 0, st, L, v, w);
   }
   hipLaunchKernelGGL(bias_mask_kernel, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, st, L, key_mask, w);
   bool ok = false;
