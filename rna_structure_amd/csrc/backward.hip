@@ -610,6 +610,164 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
   if (hf == 0) wsf(a, L.off_lse)[rq] = empty ? -INFINITY : m + logf(lsum);
 }
 
+// ------------------------------------------------------------------ matrix-core query pass
+// dQV, dA and the per-row d gamma sums on fp32 matrix cores (standard
+// widths).  Same work split as the matrix-core recomputation: four
+// wavefronts x 32 queries of one (b, h), key tiles of 32 in LDS.  Per tile:
+//   S^T  = KV_t QV^T and dP^T = VV_t dO^T   (their K-steps interleaved, so
+//                                            that the two chains of dependent
+//                                            MFMAs overlap)
+//   p = exp(S - gamma |A - B|^2 - lse), dS = p (dP - Dsum)   vector ALU, the
+//   point term from coordinate differences as in the recomputation, with
+//   dA += -2 gamma dS (A - B) and dgamma_i += -dS |A - B|^2 per lane
+//   dQV^T += KV_t^T dS^T                     dS straight from the accumulator
+//                                            layout (lane half h supplies
+//                                            key kappa(s, h) at step s)
+// KV and VV are staged transposed with a pitch of 33 floats, so that both the
+// row reads (S, dP: one key per lane) and the column reads (dQV: one feature
+// per lane) are free of bank conflicts.
+template <int DKH, int DVH, int NKB, int P3C>
+__global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
+  const BwLayout& L = a.L;
+  constexpr int DKp = 2 * DKH, DVp = 2 * DVH;
+  static_assert(32 * NKB >= DKp, "dQV blocks cover the key row");
+  __shared__ float sKT[32 * NKB][kBwKT + 1];
+  __shared__ float sVT[DVp][kBwKT + 1];
+  __shared__ __align__(16) float sBp[kBwKT][16];
+  __shared__ float sM[kBwKT];
+  __shared__ float sQ[4][32][DKp + 1];  // each wavefront's 32 query rows QV
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int q = blockIdx.x * 128 + 32 * w + l32;
+  const bool qin = q < L.N;
+  const int qc = qin ? q : L.N - 1;
+  const size_t rq = rowidx(L, b, h, qc);
+  const float gam = wsf(a, L.off_gam)[h];
+  const float lse = wsf(a, L.off_lse)[rq];
+  const float dsum = wsf(a, L.off_dd)[rq];
+  const bool mq = qin && a.mask[(size_t)b * L.N + qc] != 0 && lse > -INFINITY;
+  // rows of the dQV blocks past DKp read zeros
+  for (int e = tid; e < (32 * NKB - DKp) * (kBwKT + 1); e += 256) sKT[DKp + e / (kBwKT + 1)][e % (kBwKT + 1)] = 0.f;
+  // B operands: QV[q][s + DKH hf] from LDS, dO[q][s + DVH hf] in registers
+  for (int e = lane; e < 32 * (DKp / 4); e += 64) {
+    const int qq = e / (DKp / 4), c4 = e - qq * (DKp / 4);
+    const int qr = min(blockIdx.x * 128 + 32 * w + qq, L.N - 1);
+    const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_qv) + rowidx(L, b, h, qr) * L.DKp)[c4];
+    sQ[w][qq][4 * c4] = v.x; sQ[w][qq][4 * c4 + 1] = v.y; sQ[w][qq][4 * c4 + 2] = v.z; sQ[w][qq][4 * c4 + 3] = v.w;
+  }
+  const float* qrow = &sQ[w][l32][DKH * hf];
+  float dov[DVH];
+  {
+    const float* drow = wsf(a, L.off_do) + rq * L.DVp + DVH * hf;
+#pragma unroll
+    for (int s4 = 0; s4 < DVH / 4; ++s4) {
+      const float4 v = reinterpret_cast<const float4*>(drow)[s4];
+      dov[4 * s4] = v.x; dov[4 * s4 + 1] = v.y; dov[4 * s4 + 2] = v.z; dov[4 * s4 + 3] = v.w;
+    }
+  }
+  float qa[P3C];  // coordinates past 3P are zero on both sides
+  {
+    const float* row = wsf(a, L.off_qa) + rq * 16;
+#pragma unroll
+    for (int u = 0; u < P3C; ++u) qa[u] = row[u];
+  }
+  f32x16_t dq[NKB];
+#pragma unroll
+  for (int c = 0; c < NKB; ++c) dq[c] = f32x16_t{};
+  float da[P3C];
+#pragma unroll
+  for (int u = 0; u < P3C; ++u) da[u] = 0.f;
+  float dg = 0.f;
+  const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + qc) * L.N : nullptr;
+  for (int j0 = 0; j0 < L.N; j0 += kBwKT) {
+    __syncthreads();
+    for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
+      const int jj = e / (DKp / 4), c4 = e - jj * (DKp / 4);
+      const int j = min(j0 + jj, L.N - 1);
+      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, j) * L.DKp)[c4];
+      sKT[4 * c4][jj] = v.x; sKT[4 * c4 + 1][jj] = v.y; sKT[4 * c4 + 2][jj] = v.z; sKT[4 * c4 + 3][jj] = v.w;
+    }
+    for (int e = tid; e < kBwKT * (DVp / 4); e += 256) {
+      const int jj = e / (DVp / 4), c4 = e - jj * (DVp / 4);
+      const int j = min(j0 + jj, L.N - 1);
+      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_vv) + rowidx(L, b, h, j) * L.DVp)[c4];
+      sVT[4 * c4][jj] = v.x; sVT[4 * c4 + 1][jj] = v.y; sVT[4 * c4 + 2][jj] = v.z; sVT[4 * c4 + 3][jj] = v.w;
+    }
+    for (int e = tid; e < kBwKT * 4; e += 256) {
+      const int jj = e >> 2, c4 = e & 3;
+      const int j = min(j0 + jj, L.N - 1);
+      reinterpret_cast<float4*>(&sBp[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_kb) + rowidx(L, b, h, j) * 16)[c4];
+    }
+    if (tid < kBwKT) {
+      const int j = j0 + tid;
+      sM[tid] = (j < L.N && a.mask[(size_t)b * L.N + j] != 0) ? 1.f : 0.f;
+    }
+    __syncthreads();
+    // S and dP steps interleaved: two independent chains of dependent MFMAs
+    f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < (DKH > DVH ? DKH : DVH); ++s) {
+      if (s < DKH) sa = __builtin_amdgcn_mfma_f32_32x32x2f32(sKT[s + DKH * hf][l32], qrow[s], sa, 0, 0, 0);
+      if (s < DVH) pa = __builtin_amdgcn_mfma_f32_32x32x2f32(sVT[s + DVH * hf][l32], dov[s], pa, 0, 0, 0);
+    }
+    const int nj = min(kBwKT, L.N - j0);
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kappa(r, hf);
+      const bool ok = mq && kk < nj && sM[kk] != 0.f && (!pmrow || pmrow[j0 + kk] != 0);
+      float dif[P3C];
+      float d2 = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < P3C / 4; ++c4) {
+        const float4 y = reinterpret_cast<const float4*>(&sBp[kk][0])[c4];
+        dif[4 * c4] = qa[4 * c4] - y.x; dif[4 * c4 + 1] = qa[4 * c4 + 1] - y.y;
+        dif[4 * c4 + 2] = qa[4 * c4 + 2] - y.z; dif[4 * c4 + 3] = qa[4 * c4 + 3] - y.w;
+        d2 += dif[4 * c4] * dif[4 * c4] + dif[4 * c4 + 1] * dif[4 * c4 + 1] + dif[4 * c4 + 2] * dif[4 * c4 + 2] +
+              dif[4 * c4 + 3] * dif[4 * c4 + 3];
+      }
+      const float p = ok ? expf(sa[r] - gam * d2 - lse) : 0.f;
+      ds[r] = p * (pa[r] - dsum);
+#pragma unroll
+      for (int u = 0; u < P3C; ++u) da[u] = fmaf(ds[r], dif[u], da[u]);
+      dg = fmaf(-ds[r], d2, dg);
+    }
+    // dQV^T += KV_t^T dS^T
+#pragma unroll
+    for (int c = 0; c < NKB; ++c)
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        dq[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sKT[32 * c + l32][kappa(s, hf)], ds[s], dq[c], 0, 0, 0);
+  }
+  // the two halves of the wavefront hold the same queries' two halves of each tile
+#pragma unroll
+  for (int u = 0; u < P3C; ++u) da[u] += __shfl_xor(da[u], 32);
+  dg += __shfl_xor(dg, 32);
+  if (!qin) return;
+  float* orow = wsf(a, L.off_dqv) + rq * L.DKp;
+#pragma unroll
+  for (int c = 0; c < NKB; ++c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int f = 32 * c + 8 * g + 4 * hf;
+      if (f < DKp)
+        *reinterpret_cast<float4*>(orow + f) = make_float4(dq[c][4 * g], dq[c][4 * g + 1], dq[c][4 * g + 2], dq[c][4 * g + 3]);
+    }
+  if (hf == 0) {
+    float* arow = wsf(a, L.off_dqa) + rq * 16;
+#pragma unroll
+    for (int u4 = 0; u4 < 4; ++u4) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * u4 < P3C)
+        v = make_float4(-2.f * gam * da[4 * u4], -2.f * gam * da[4 * u4 + 1], -2.f * gam * da[4 * u4 + 2],
+                        -2.f * gam * da[4 * u4 + 3]);
+      reinterpret_cast<float4*>(arow)[u4] = v;
+    }
+    wsf(a, L.off_dgam)[rq] = dg;
+  }
+}
+
 // ------------------------------------------------------------------ GEMM
 // C[m][n] (+)= sum_k A(m,k) B(k,n), fp32, 64x64 tiles, 256 threads x 4x4.
 // A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn].  blockIdx.z splits K
@@ -974,6 +1132,10 @@ hipError_t launch_pairs_inst(const BwArgs& a, int which, hipStream_t st) {
   if (which == 0 && L.NK4 == 9) {
     // standard shape (D + R Cz <= 144, Dv + R Cz + 3Q <= 176): matrix cores
     hipLaunchKernelGGL((bw_fwd_mfma_kernel<72, 6>), dim3((L.N + 127) / 128, L.H, L.B), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  if (which == 1 && L.NK4 == 9 && L.DVp == 176 && L.P3 == 12) {
+    hipLaunchKernelGGL((bw_query_mfma_kernel<72, 88, 5, 12>), dim3((L.N + 127) / 128, L.H, L.B), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (L.NK4 == 1) return launch_pairs<1, 2>(a, which, st);
