@@ -768,6 +768,191 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ matrix-core key pass
+// dKV, dB and dVV on fp32 matrix cores (standard widths), in two launches
+// (below): four wavefronts x
+// 32 keys of one (b, h), query tiles of 32 in LDS.  The accumulator layout
+// gives every lane one key and 16 queries.  Per tile:
+//   S = QV_t KV^T and dP = dO_t VV^T        K-steps interleaved; the keys'
+//                                            KV rows sit in LDS, their VV rows
+//                                            in registers
+//   p = exp(S - gamma |A - B|^2 - lse_i), dS = p (dP - Dsum_i), and
+//   dB += 2 gamma dS (A - B) on the vector ALU
+//   dKV^T += QV_t^T dS, dVV^T += dO_t^T P   the probabilities and dS straight
+//                                            from the accumulator registers
+// The query tile's QV and dO are staged transposed (pitch 33 floats): the S
+// and dP products read them one query per lane, the dKV and dVV products one
+// feature per lane, both without bank conflicts.
+// MODE 0: S and dP, accumulating dKV and dB; MODE 1: S only, accumulating dVV
+// (one launch each: together they would hold more registers than a lane has).
+template <int DKH, int DVH, int NKB, int NVB, int P3C, int MODE>
+__global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
+  const BwLayout& L = a.L;
+  constexpr bool kDS = MODE == 0, kDV = MODE == 1;
+  constexpr int DKp = 2 * DKH, DVp = 2 * DVH;
+  static_assert(32 * NKB >= DKp && 32 * NVB >= DVp, "blocks cover the rows");
+  __shared__ float sK[4][32][DKp + 1];  // each wavefront's 32 key rows KV
+  __shared__ float sQT[32 * NKB][kBwKT + 1];
+  __shared__ float sDT[32 * NVB][kBwKT + 1];
+  __shared__ __align__(16) float sA[kBwKT][16];
+  __shared__ float sL[kBwKT], sS[kBwKT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int j = blockIdx.x * 128 + 32 * w + l32;
+  const bool kin = j < L.N;
+  const int jc = kin ? j : L.N - 1;
+  const size_t rj = rowidx(L, b, h, jc);
+  const float gam = wsf(a, L.off_gam)[h];
+  const bool mk = kin && a.mask[(size_t)b * L.N + jc] != 0;
+  // rows of the last blocks past DKp / DVp read zeros
+  for (int e = tid; e < (32 * NKB - DKp) * (kBwKT + 1); e += 256) sQT[DKp + e / (kBwKT + 1)][e % (kBwKT + 1)] = 0.f;
+  for (int e = tid; e < (32 * NVB - DVp) * (kBwKT + 1); e += 256) sDT[DVp + e / (kBwKT + 1)][e % (kBwKT + 1)] = 0.f;
+  for (int e = lane; e < 32 * (DKp / 4); e += 64) {
+    const int kk = e / (DKp / 4), c4 = e - kk * (DKp / 4);
+    const int kr = min(blockIdx.x * 128 + 32 * w + kk, L.N - 1);
+    const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, kr) * L.DKp)[c4];
+    sK[w][kk][4 * c4] = v.x; sK[w][kk][4 * c4 + 1] = v.y; sK[w][kk][4 * c4 + 2] = v.z; sK[w][kk][4 * c4 + 3] = v.w;
+  }
+  const float* krow = &sK[w][l32][DKH * hf];
+  float vv[kDS ? DVH : 1];
+  if constexpr (kDS) {
+    const float* row = wsf(a, L.off_vv) + rj * L.DVp + DVH * hf;
+#pragma unroll
+    for (int s4 = 0; s4 < DVH / 4; ++s4) {
+      const float4 v = reinterpret_cast<const float4*>(row)[s4];
+      vv[4 * s4] = v.x; vv[4 * s4 + 1] = v.y; vv[4 * s4 + 2] = v.z; vv[4 * s4 + 3] = v.w;
+    }
+  }
+  float kb[P3C];
+  {
+    const float* row = wsf(a, L.off_kb) + rj * 16;
+#pragma unroll
+    for (int u = 0; u < P3C; ++u) kb[u] = row[u];
+  }
+  f32x16_t dk[kDS ? NKB : 1], dv[kDV ? NVB : 1];
+#pragma unroll
+  for (int c = 0; c < (kDS ? NKB : 1); ++c) dk[c] = f32x16_t{};
+#pragma unroll
+  for (int c = 0; c < (kDV ? NVB : 1); ++c) dv[c] = f32x16_t{};
+  float db[P3C];
+#pragma unroll
+  for (int u = 0; u < P3C; ++u) db[u] = 0.f;
+  for (int i0 = 0; i0 < L.N; i0 += kBwKT) {
+    __syncthreads();
+    for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
+      const int ii = e / (DKp / 4), c4 = e - ii * (DKp / 4);
+      const int i = min(i0 + ii, L.N - 1);
+      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_qv) + rowidx(L, b, h, i) * L.DKp)[c4];
+      sQT[4 * c4][ii] = v.x; sQT[4 * c4 + 1][ii] = v.y; sQT[4 * c4 + 2][ii] = v.z; sQT[4 * c4 + 3][ii] = v.w;
+    }
+    for (int e = tid; e < kBwKT * (DVp / 4); e += 256) {
+      const int ii = e / (DVp / 4), c4 = e - ii * (DVp / 4);
+      const int i = min(i0 + ii, L.N - 1);
+      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_do) + rowidx(L, b, h, i) * L.DVp)[c4];
+      sDT[4 * c4][ii] = v.x; sDT[4 * c4 + 1][ii] = v.y; sDT[4 * c4 + 2][ii] = v.z; sDT[4 * c4 + 3][ii] = v.w;
+    }
+    for (int e = tid; e < kBwKT * 4; e += 256) {
+      const int ii = e >> 2, c4 = e & 3;
+      const int i = min(i0 + ii, L.N - 1);
+      reinterpret_cast<float4*>(&sA[ii][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_qa) + rowidx(L, b, h, i) * 16)[c4];
+    }
+    if (tid < kBwKT) {
+      const int i = i0 + tid;
+      const int icl = min(i, L.N - 1);
+      const float lse = wsf(a, L.off_lse)[rowidx(L, b, h, icl)];
+      const bool ok = i < L.N && a.mask[(size_t)b * L.N + icl] != 0 && lse > -INFINITY;
+      sL[tid] = ok ? lse : INFINITY;  // +inf marks a query that takes no key
+      sS[tid] = wsf(a, L.off_dd)[rowidx(L, b, h, icl)];
+    }
+    __syncthreads();
+    f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
+    if constexpr (kDS) {
+#pragma unroll
+      for (int s = 0; s < (DKH > DVH ? DKH : DVH); ++s) {
+        if (s < DKH) sa = __builtin_amdgcn_mfma_f32_32x32x2f32(sQT[s + DKH * hf][l32], krow[s], sa, 0, 0, 0);
+        if (s < DVH) pa = __builtin_amdgcn_mfma_f32_32x32x2f32(sDT[s + DVH * hf][l32], vv[s], pa, 0, 0, 0);
+      }
+    } else {
+      // one chain: two accumulators over even and odd K-steps
+#pragma unroll
+      for (int s = 0; s < DKH; s += 2) {
+        sa = __builtin_amdgcn_mfma_f32_32x32x2f32(sQT[s + DKH * hf][l32], krow[s], sa, 0, 0, 0);
+        if (s + 1 < DKH) pa = __builtin_amdgcn_mfma_f32_32x32x2f32(sQT[s + 1 + DKH * hf][l32], krow[s + 1], pa, 0, 0, 0);
+      }
+      sa += pa;
+    }
+    float ds[16], pr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = kappa(r, hf);
+      const int i = i0 + qq;
+      const bool ok = mk && sL[qq] < INFINITY && (!a.pmask || a.pmask[((size_t)b * L.N + i) * L.N + jc] != 0);
+      float dif[P3C];
+      float d2 = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < P3C / 4; ++c4) {
+        const float4 x = reinterpret_cast<const float4*>(&sA[qq][0])[c4];
+        dif[4 * c4] = x.x - kb[4 * c4]; dif[4 * c4 + 1] = x.y - kb[4 * c4 + 1];
+        dif[4 * c4 + 2] = x.z - kb[4 * c4 + 2]; dif[4 * c4 + 3] = x.w - kb[4 * c4 + 3];
+        d2 += dif[4 * c4] * dif[4 * c4] + dif[4 * c4 + 1] * dif[4 * c4 + 1] + dif[4 * c4 + 2] * dif[4 * c4 + 2] +
+              dif[4 * c4 + 3] * dif[4 * c4 + 3];
+      }
+      pr[r] = ok ? expf(sa[r] - gam * d2 - sL[qq]) : 0.f;
+      if constexpr (kDS) {
+        ds[r] = pr[r] * (pa[r] - sS[qq]);
+#pragma unroll
+        for (int u = 0; u < P3C; ++u) db[u] = fmaf(ds[r], dif[u], db[u]);
+      }
+    }
+    // dKV^T += QV_t^T dS, dVV^T += dO_t^T P
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if constexpr (kDS) {
+#pragma unroll
+        for (int c = 0; c < NKB; ++c)
+          dk[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sQT[32 * c + l32][kappa(s, hf)], ds[s], dk[c], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NVB; ++c)
+          dv[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sDT[32 * c + l32][kappa(s, hf)], pr[s], dv[c], 0, 0, 0);
+      }
+    }
+  }
+  // the two halves of the wavefront hold the same keys' two halves of each tile
+#pragma unroll
+  for (int u = 0; u < P3C; ++u) db[u] += __shfl_xor(db[u], 32);
+  if (!kin) return;
+  float* krw = wsf(a, L.off_dkv) + rj * L.DKp;
+  float* vrw = wsf(a, L.off_dvv) + rj * L.DVp;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+#pragma unroll
+    for (int c = 0; c < (kDS ? NKB : 0); ++c) {
+      const int f = 32 * c + 8 * g + 4 * hf;
+      if (f < DKp)
+        *reinterpret_cast<float4*>(krw + f) = make_float4(dk[c][4 * g], dk[c][4 * g + 1], dk[c][4 * g + 2], dk[c][4 * g + 3]);
+    }
+#pragma unroll
+    for (int c = 0; c < (kDV ? NVB : 0); ++c) {
+      const int f = 32 * c + 8 * g + 4 * hf;
+      if (f < DVp)
+        *reinterpret_cast<float4*>(vrw + f) = make_float4(dv[c][4 * g], dv[c][4 * g + 1], dv[c][4 * g + 2], dv[c][4 * g + 3]);
+    }
+  }
+  if (kDS && hf == 0) {
+    float* brow = wsf(a, L.off_dkb) + rj * 16;
+#pragma unroll
+    for (int u4 = 0; u4 < 4; ++u4) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * u4 < P3C)
+        v = make_float4(2.f * gam * db[4 * u4], 2.f * gam * db[4 * u4 + 1], 2.f * gam * db[4 * u4 + 2],
+                        2.f * gam * db[4 * u4 + 3]);
+      reinterpret_cast<float4*>(brow)[u4] = v;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ GEMM
 // C[m][n] (+)= sum_k A(m,k) B(k,n), fp32, 64x64 tiles, 256 threads x 4x4.
 // A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn].  blockIdx.z splits K
@@ -1132,6 +1317,12 @@ hipError_t launch_pairs_inst(const BwArgs& a, int which, hipStream_t st) {
   if (which == 0 && L.NK4 == 9) {
     // standard shape (D + R Cz <= 144, Dv + R Cz + 3Q <= 176): matrix cores
     hipLaunchKernelGGL((bw_fwd_mfma_kernel<72, 6>), dim3((L.N + 127) / 128, L.H, L.B), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  if (which == 2 && L.NK4 == 9 && L.DVp == 176 && L.P3 == 12) {
+    const dim3 grid((L.N + 127) / 128, L.H, L.B);
+    hipLaunchKernelGGL((bw_key_mfma_kernel<72, 88, 5, 6, 12, 0>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bw_key_mfma_kernel<72, 88, 5, 6, 12, 1>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (which == 1 && L.NK4 == 9 && L.DVp == 176 && L.P3 == 12) {
