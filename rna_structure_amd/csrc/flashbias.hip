@@ -31,6 +31,7 @@
 // The next tile's global loads are issued before the current tile's
 // arithmetic and land in LDS after it.  Causal attention stops at the tile
 // that holds the workgroup's last query.
+#include "lds_copy.h"
 #include "mfma_tile.h"
 
 namespace fipa {
@@ -44,7 +45,7 @@ constexpr float kBiasLn2 = 0.6931471805599453f;
 struct BiasLayout {
   int B, N, M, H, D, Dv, R, causal, bf, bfp;
   float scale;
-  int NQS, NVB, W, DVP, Npad, Mpad, MT;
+  int NQS, NVB, W, KP, DVP, Npad, Mpad, MT;  // KP: key row pitch (W + 8, as in LDS)
   size_t off_q, off_k, off_v, off_m, total;
 };
 
@@ -74,6 +75,7 @@ bool make_bias_layout(const ipa_bias_shape* s, BiasLayout* L) {
   L->NVB = pick_nvb((L->Dv + 31) / 32);
   if (L->NQS == 0 || L->NVB == 0) return false;
   L->W = 16 * L->NQS;
+  L->KP = L->W + 8;
   L->DVP = 32 * L->NVB;
   L->Npad = (s->N + 127) / 128 * 128;
   L->Mpad = (s->M + 63) / 64 * 64;
@@ -81,11 +83,20 @@ bool make_bias_layout(const ipa_bias_shape* s, BiasLayout* L) {
   const size_t BH = (size_t)s->B * s->H;
   size_t off = 0;
   L->off_q = off; off = al256(off + BH * L->Npad * L->W * 2);
-  L->off_k = off; off = al256(off + BH * L->Mpad * L->W * 2);
-  L->off_v = off; off = al256(off + BH * L->Mpad * L->DVP * 2);
+  L->off_k = off; off = al256(off + BH * L->Mpad * L->KP * 2);
+  L->off_v = off; off = al256(off + BH * L->Mpad * L->DVP * 72 / 64 * 2);
   L->off_m = off; off = al256(off + (size_t)s->B * L->MT * 2 * 4);
   L->total = off;
   return true;
+}
+
+// A uniform word through a scalar load (constant address space): it is not
+// counted by the vector-memory counter that the tile copies are waited on with.
+__device__ __forceinline__ uint32_t ld_scalar_u32(const uint32_t* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return *(const __attribute__((address_space(4))) uint32_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(256) void bias_lift_rows_kernel(BiasLayout L, int s
                                                              char* ws) {
   // 32-bit indices: B H rows c8 < 2^31 (checked on the host)
   const uint32_t rows = side == 0 ? L.Npad : L.Mpad, n = side == 0 ? L.N : L.M;
-  const uint32_t c8 = L.W / 8;
+  const uint32_t c8 = (side == 0 ? L.W : L.KP) / 8;  // key rows carry the 8 pad columns of the LDS tile
   const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
   if (idx >= (uint32_t)L.B * L.H * rows * c8) return;
   const uint32_t rr = idx / c8, cc = idx - rr * c8;
@@ -155,7 +166,8 @@ __global__ __launch_bounds__(256) void bias_lift_rows_kernel(BiasLayout L, int s
   reinterpret_cast<uint4*>(base)[idx] = out;
 }
 
-// Transposed value tiles [b][h][t][c][64], keys permuted within every 16
+// Transposed value tiles [b][h][t][c][72] (64 keys and 8 pad columns, the
+// LDS tile's layout), keys permuted within every 16
 // (column kappa holds key vt_key_of_col(kappa)).  A workgroup takes one
 // 64-key tile and 32 value columns of one (b, h): it reads the 64 rows'
 // 32-column pieces, transposes them in LDS and writes 32 rows of 64 keys
@@ -179,8 +191,10 @@ __global__ __launch_bounds__(256) void bias_lift_v_kernel(BiasLayout L, const vo
   float f[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = sT[vt_key_of_col(8 * k8 + e)][cl];
-  uint4* dst = reinterpret_cast<uint4*>(ws + L.off_v) + (((size_t)bh * L.MT + t) * L.DVP + 32 * cb + cl) * 8 + k8;
-  *dst = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
+  // rows of 72 keys' width: 64 keys and the 8 pad columns of the LDS tile
+  uint4* dst = reinterpret_cast<uint4*>(ws + L.off_v) + (((size_t)bh * L.MT + t) * L.DVP + 32 * cb + cl) * 9;
+  dst[k8] = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
+  if (k8 == 0) dst[8] = make_uint4(0, 0, 0, 0);
 }
 
 // Key-mask words: per (b, tile) two words; bit kb*16 + r of word h is key
@@ -203,7 +217,8 @@ __global__ __launch_bounds__(256) void bias_mask_kernel(BiasLayout L, const uint
 }
 
 // Three wavefronts per SIMD where the instance's registers fit (168 each)
-// without spilling, else no occupancy constraint.
+// without spilling, else no occupancy constraint (four, at 128 registers,
+// measured slower for the D = 64 instance).
 constexpr int bias_waves(int nqs, int nvb) {
   return ((nvb <= 2 && nqs <= 5) || (nvb == 1 && nqs <= 9) || (nvb == 4 && nqs == 2)) ? 3 : 1;
 }
@@ -214,13 +229,12 @@ void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
   constexpr int W = 16 * NQS, DVP = 32 * NVB;
   constexpr int KP = W + 8;   // LDS row pitch of the key tile (bf16)
   constexpr int VP = 64 + 8;  // LDS row pitch of the transposed value tile (bf16)
-  constexpr int KCH = 64 * W / 8, VCH = DVP * 8;  // 16-byte chunks per tile
-  constexpr int KPT = (KCH + 255) / 256, VPT = VCH / 256;
-  // key tile, value tile; after the last tile, 32x36-float output blocks per wavefront
-  constexpr int KB = 64 * KP * 2, VB = DVP * VP * 2, SB = 4 * 32 * 36 * 4;
-  __shared__ __align__(16) char smem[KB + VB > SB ? KB + VB : SB];
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + KB);
+  // key and value tiles are copied global -> LDS as they lie in the workspace
+  // (rows already at the LDS pitches), into two buffers
+  constexpr int KT_BYTES = 64 * KP * 2, VT_BYTES = DVP * VP * 2;
+  constexpr int KT_LDS = (KT_BYTES + 1023) / 1024 * 1024, VT_LDS = (VT_BYTES + 1023) / 1024 * 1024;
+  constexpr int BUF = KT_LDS + VT_LDS, SB = 4 * 32 * 36 * 4;  // SB: output blocks after the last tile
+  __shared__ __align__(1024) char smem[2 * BUF > SB ? 2 * BUF : SB];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -234,20 +248,10 @@ void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
 #pragma unroll
   for (int ks = 0; ks < NQS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8_t, qrow[2 * ks + hf]);
 
-  const u32x4_t* kg = reinterpret_cast<const u32x4_t*>(ws + L.off_k) + bh * L.Mpad * (W / 8);
-  const u32x4_t* vg = reinterpret_cast<const u32x4_t*>(ws + L.off_v) + bh * L.MT * (DVP * 8);
+  const char* ktg = ws + L.off_k + bh * L.MT * (size_t)KT_BYTES;
+  const char* vtg = ws + L.off_v + bh * L.MT * (size_t)VT_BYTES;
   const uint32_t* mw = reinterpret_cast<const uint32_t*>(ws + L.off_m) + (size_t)b * L.MT * 2;
   const int tend = L.causal ? min(L.MT, (min(q0 + 127, L.N - 1) >> 6) + 1) : L.MT;
-
-  u32x4_t pk[KPT], pv[VPT];
-  // tile 0 into registers
-#pragma unroll
-  for (int x = 0; x < KPT; ++x) {
-    const int ch = tid + 256 * x;
-    pk[x] = kg[ch < KCH ? ch : 0];
-  }
-#pragma unroll
-  for (int x = 0; x < VPT; ++x) pv[x] = vg[tid + 256 * x];
 
   f32x16_t oacc[NVB];
 #pragma unroll
@@ -256,29 +260,20 @@ void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
     for (int r = 0; r < 16; ++r) oacc[vb][r] = 0.f;
   float m = -INFINITY, l = 0.f;
 
+  dma_tile<KT_BYTES, 4>(ktg, smem, w, lane);
+  dma_tile<VT_BYTES, 4>(vtg, smem + KT_LDS, w, lane);
   for (int t = 0; t < tend; ++t) {
-    __syncthreads();  // every wavefront is done with the previous tile
-#pragma unroll
-    for (int x = 0; x < KPT; ++x) {
-      const int ch = tid + 256 * x;
-      if (ch < KCH) *reinterpret_cast<u32x4_t*>(&sK[(ch / (W / 8)) * KP + (ch % (W / 8)) * 8]) = pk[x];
-    }
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) {
-      const int ch = tid + 256 * x;
-      *reinterpret_cast<u32x4_t*>(&sV[(ch >> 3) * VP + (ch & 7) * 8]) = pv[x];
-    }
+    // tile t has landed (every wavefront waits for its own copies) and every
+    // wavefront is done with tile t - 1, whose buffer the next copies refill
+    wait_vmcnt<0>();
     __syncthreads();
     if (t + 1 < tend) {
-      // the next tile's loads run during this tile's arithmetic
-#pragma unroll
-      for (int x = 0; x < KPT; ++x) {
-        const int ch = tid + 256 * x;
-        pk[x] = kg[(size_t)(t + 1) * KCH + (ch < KCH ? ch : 0)];
-      }
-#pragma unroll
-      for (int x = 0; x < VPT; ++x) pv[x] = vg[(size_t)(t + 1) * VCH + tid + 256 * x];
+      char* nb = smem + ((t + 1) & 1) * BUF;
+      dma_tile<KT_BYTES, 4>(ktg + (size_t)(t + 1) * KT_BYTES, nb, w, lane);
+      dma_tile<VT_BYTES, 4>(vtg + (size_t)(t + 1) * VT_BYTES, nb + KT_LDS, w, lane);
     }
+    const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + (t & 1) * BUF);
+    const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + (t & 1) * BUF + KT_LDS);
 
     // causal: a tile whose first key is past the wavefront's last query adds nothing
     if (L.causal && t * 64 > q0 + w * 32 + 31) continue;
@@ -297,7 +292,7 @@ void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
     }
 
     // masks: key mask word of this lane half; causal keys beyond the query
-    const uint32_t w0 = __builtin_amdgcn_readfirstlane(mw[2 * t]), w1 = __builtin_amdgcn_readfirstlane(mw[2 * t + 1]);
+    const uint32_t w0 = ld_scalar_u32(mw + 2 * t), w1 = ld_scalar_u32(mw + 2 * t + 1);
     const uint32_t word = hf ? w1 : w0;
     const bool diag = L.causal && t * 64 + 63 > q0 + w * 32;
     float s[32];
@@ -362,6 +357,7 @@ void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
   // O^T (value columns x this wavefront's 32 queries) through LDS, one block
   // of 32 columns at a time, so that every query row is written as whole
   // 128-byte pieces of consecutive columns
+  wait_vmcnt<0>();
   __syncthreads();  // the last tile's LDS reads are done in every wavefront
   float* so = reinterpret_cast<float*>(smem) + w * 32 * 36;
   const int cq = lane & 7;  // 16-byte piece of a row
@@ -427,7 +423,8 @@ hipError_t launch_bias_attention(const ipa_bias_shape* s, const void* q, const v
   BiasLayout L;
   if (!make_bias_layout(s, &L)) return hipErrorInvalidValue;
   char* w = reinterpret_cast<char*>(ws);
-  const long nq = (long)L.B * L.H * L.Npad * (L.W / 8), nk = (long)L.B * L.H * L.Mpad * (L.W / 8);
+  // one thread per 16-byte piece: query rows W wide, key rows KP wide (with the LDS pad columns)
+  const long nq = (long)L.B * L.H * L.Npad * (L.W / 8), nk = (long)L.B * L.H * L.Mpad * (L.KP / 8);
   const long nv = (long)L.B * L.H * L.MT * (L.DVP / 32), nm = (long)L.B * L.MT * 2;
   auto rows = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, L, 0, q, phi_q, w);

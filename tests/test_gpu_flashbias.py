@@ -8,7 +8,9 @@ magnitude (bf16 hi/lo pairs), and probabilities are rounded to bf16 against
 bf16 values (2^-9).  Bar: max |o - ref| / max |ref| <= 2e-2 per case (the
 bf16 bar of the IPA forward), |lse - ref| <= 2e-2 max(1, |ref|), and the same
 empty rows (O = 0, lse = -inf).  At the benchmark sizes the oracle computes
-sampled rows, tile edges and the last row included."""
+sampled rows, tile edges and the last row included.  The workspace is
+filled with all-ones bytes (NaN) before every call, so a region the lift
+leaves unwritten cannot pass on stale data."""
 import numpy as np
 import pytest
 
@@ -33,6 +35,9 @@ def _run(inp, scale, causal, f=None):
     if f is None:
         f = _lib.BiasAttention(d["B"], d["N"], d["M"], d["H"], d["D"], d["Dv"], d["R"], scale, causal,
                                d["dtype"], d["phi_dtype"])
+    # every byte of the workspace that the kernels read must have been written
+    # by this call: start from all-ones bytes (NaN as bf16 or fp32)
+    f.workspace.fill_(255)
     out = f(q, k, v, pq, pk, km)
     torch.cuda.synchronize()
     return f, {n: t.cpu().numpy().astype(np.float64) for n, t in out.items()}
