@@ -236,7 +236,9 @@ void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
   constexpr int BUF = KT_LDS + VT_LDS, SB = 4 * 32 * 36 * 4;  // SB: output blocks after the last tile
   __shared__ __align__(1024) char smem[2 * BUF > SB ? 2 * BUF : SB];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  // the wavefront index is uniform: say so, so that the copy offsets live in scalar registers
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
+            hf = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
   // causal: the query tiles with the most key tiles are launched first
   const int qt = L.causal ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
