@@ -6,7 +6,9 @@
 //
 //   L_ij = scale q_i . k_j + phi_q(i) . phi_k(j),  O_i = softmax_j(L_ij) v_j
 //
-// Lift (one pass over the inputs, written to the workspace):
+// Lifted rows (the key side written to the workspace by a lift pass, the
+// query side built in the attention kernel's prologue, each query row being
+// read once):
 //   Q~_i = [scale log2(e) q_i | per factor r: hi, hi, lo of log2(e) phi_q,r(i)]
 //   K~_j = [k_j               | per factor r: hi, lo, hi of phi_k,r(j)]
 // in bf16, zero-padded to W = 16 NQS columns, so that Q~_i . K~_j is L_ij in
@@ -46,7 +48,7 @@ struct BiasLayout {
   int B, N, M, H, D, Dv, R, causal, bf, bfp;
   float scale;
   int NQS, NVB, W, KP, DVP, Npad, Mpad, MT;  // KP: key row pitch (W + 8, as in LDS)
-  size_t off_q, off_k, off_v, off_m, total;
+  size_t off_k, off_v, off_m, total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -82,7 +84,6 @@ bool make_bias_layout(const ipa_bias_shape* s, BiasLayout* L) {
   L->MT = L->Mpad / 64;
   const size_t BH = (size_t)s->B * s->H;
   size_t off = 0;
-  L->off_q = off; off = al256(off + BH * L->Npad * L->W * 2);
   L->off_k = off; off = al256(off + BH * L->Mpad * L->KP * 2);
   L->off_v = off; off = al256(off + BH * L->Mpad * L->DVP * 72 / 64 * 2);
   L->off_m = off; off = al256(off + (size_t)s->B * L->MT * 2 * 4);
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256) void bias_lift_rows_kernel(BiasLayout L, int s
     }
     out = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
   }
-  char* base = ws + (side == 0 ? L.off_q : L.off_k);
+  char* base = ws + L.off_k;  // (side 0, query rows, is lifted inside the attention kernel)
   reinterpret_cast<uint4*>(base)[idx] = out;
 }
 
@@ -225,7 +226,7 @@ constexpr int bias_waves(int nqs, int nvb) {
 
 template <int NQS, int NVB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bias_waves(NQS, NVB))))
-void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
+void bias_attn_kernel(BiasLayout L, const char* ws, const void* qin, const void* pqin, float* o, float* lse) {
   constexpr int W = 16 * NQS, DVP = 32 * NVB;
   constexpr int KP = W + 8;   // LDS row pitch of the key tile (bf16)
   constexpr int VP = 64 + 8;  // LDS row pitch of the transposed value tile (bf16)
@@ -245,10 +246,26 @@ void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
   const int q0 = qt * 128, i = q0 + w * 32 + l32;
   const size_t bh = (size_t)b * L.H + h;
 
-  const uint4* qrow = reinterpret_cast<const uint4*>(ws + L.off_q) + (bh * L.Npad + i) * (W / 8);
+  // query operand (B of S^T), lifted here from q and phi_q: lane (query i, half
+  // hf) holds columns 16 ks + 8 hf .. +7 of [scale log2e q_i | hi hi lo of
+  // log2e phi_q(i) per factor], zero for padding rows
   bf16x8_t bq[NQS];
+  {
+    const size_t xrow = (((size_t)b * L.N + i) * L.H + h) * L.D;
+    const size_t prow = (((size_t)b * L.N + i) * L.H + h) * L.R;
 #pragma unroll
-  for (int ks = 0; ks < NQS; ++ks) bq[ks] = __builtin_bit_cast(bf16x8_t, qrow[2 * ks + hf]);
+    for (int ks = 0; ks < NQS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 16 * ks + 8 * hf + e;
+        float f = 0.f;
+        if (i < L.N) {
+          if (L.bf) f = L.bfp ? lifted<true, true>(L, 0, qin, pqin, xrow, prow, c) : lifted<true, false>(L, 0, qin, pqin, xrow, prow, c);
+          else f = L.bfp ? lifted<false, true>(L, 0, qin, pqin, xrow, prow, c) : lifted<false, false>(L, 0, qin, pqin, xrow, prow, c);
+        }
+        bq[ks][e] = (__bf16)f;
+      }
+  }
 
   const char* ktg = ws + L.off_k + bh * L.MT * (size_t)KT_BYTES;
   const char* vtg = ws + L.off_v + bh * L.MT * (size_t)VT_BYTES;
@@ -392,17 +409,19 @@ void bias_attn_kernel(BiasLayout L, const char* ws, float* o, float* lse) {
 }
 
 template <int NQS, int NVB>
-void launch_attn(const BiasLayout& L, const char* ws, float* o, float* lse, hipStream_t st) {
-  hipLaunchKernelGGL((bias_attn_kernel<NQS, NVB>), dim3(L.Npad / 128, L.H, L.B), dim3(256), 0, st, L, ws, o, lse);
+void launch_attn(const BiasLayout& L, const char* ws, const void* q, const void* pq, float* o, float* lse,
+                 hipStream_t st) {
+  hipLaunchKernelGGL((bias_attn_kernel<NQS, NVB>), dim3(L.Npad / 128, L.H, L.B), dim3(256), 0, st, L, ws, q, pq, o, lse);
 }
 
 template <int NQS>
-bool dispatch_nvb(const BiasLayout& L, const char* ws, float* o, float* lse, hipStream_t st) {
+bool dispatch_nvb(const BiasLayout& L, const char* ws, const void* q, const void* pq, float* o, float* lse,
+                  hipStream_t st) {
   switch (L.NVB) {
-    case 1: launch_attn<NQS, 1>(L, ws, o, lse, st); return true;
-    case 2: launch_attn<NQS, 2>(L, ws, o, lse, st); return true;
-    case 4: launch_attn<NQS, 4>(L, ws, o, lse, st); return true;
-    case 8: launch_attn<NQS, 8>(L, ws, o, lse, st); return true;
+    case 1: launch_attn<NQS, 1>(L, ws, q, pq, o, lse, st); return true;
+    case 2: launch_attn<NQS, 2>(L, ws, q, pq, o, lse, st); return true;
+    case 4: launch_attn<NQS, 4>(L, ws, q, pq, o, lse, st); return true;
+    case 8: launch_attn<NQS, 8>(L, ws, q, pq, o, lse, st); return true;
   }
   return false;
 }
@@ -425,11 +444,10 @@ hipError_t launch_bias_attention(const ipa_bias_shape* s, const void* q, const v
   BiasLayout L;
   if (!make_bias_layout(s, &L)) return hipErrorInvalidValue;
   char* w = reinterpret_cast<char*>(ws);
-  // one thread per 16-byte piece: query rows W wide, key rows KP wide (with the LDS pad columns)
-  const long nq = (long)L.B * L.H * L.Npad * (L.W / 8), nk = (long)L.B * L.H * L.Mpad * (L.KP / 8);
+  // one thread per 16-byte piece of the key rows, KP wide (with the LDS pad columns)
+  const long nk = (long)L.B * L.H * L.Mpad * (L.KP / 8);
   const long nv = (long)L.B * L.H * L.MT * (L.DVP / 32), nm = (long)L.B * L.MT * 2;
-  auto rows = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, L, 0, q, phi_q, w);
+  auto rows = [&](auto kern) {  // key rows (the query rows are lifted inside the attention kernel)
     hipLaunchKernelGGL(kern, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, st, L, 1, k, phi_k, w);
   };
   if (L.bf) {
@@ -442,13 +460,13 @@ hipError_t launch_bias_attention(const ipa_bias_shape* s, const void* q, const v
   hipLaunchKernelGGL(bias_mask_kernel, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, st, L, key_mask, w);
   bool ok = false;
   switch (L.NQS) {
-    case 2: ok = dispatch_nvb<2>(L, w, o, lse, st); break;
-    case 3: ok = dispatch_nvb<3>(L, w, o, lse, st); break;
-    case 4: ok = dispatch_nvb<4>(L, w, o, lse, st); break;
-    case 5: ok = dispatch_nvb<5>(L, w, o, lse, st); break;
-    case 8: ok = dispatch_nvb<8>(L, w, o, lse, st); break;
-    case 9: ok = dispatch_nvb<9>(L, w, o, lse, st); break;
-    case 16: ok = dispatch_nvb<16>(L, w, o, lse, st); break;
+    case 2: ok = dispatch_nvb<2>(L, w, q, phi_q, o, lse, st); break;
+    case 3: ok = dispatch_nvb<3>(L, w, q, phi_q, o, lse, st); break;
+    case 4: ok = dispatch_nvb<4>(L, w, q, phi_q, o, lse, st); break;
+    case 5: ok = dispatch_nvb<5>(L, w, q, phi_q, o, lse, st); break;
+    case 8: ok = dispatch_nvb<8>(L, w, q, phi_q, o, lse, st); break;
+    case 9: ok = dispatch_nvb<9>(L, w, q, phi_q, o, lse, st); break;
+    case 16: ok = dispatch_nvb<16>(L, w, q, phi_q, o, lse, st); break;
   }
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
