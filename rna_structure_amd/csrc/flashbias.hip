@@ -181,11 +181,32 @@ __global__ __launch_bounds__(256) void bias_lift_v_kernel(BiasLayout L, const vo
   const int bh = blockIdx.x / ((L.DVP / 32) * L.MT);
   const int h = bh % L.H, b = bh / L.H;
   const int tid = threadIdx.x;
+  {
+    // thread: 8 consecutive columns of one key (one 16-byte bf16 or two
+    // 16-byte fp32 loads when the row allows it)
+    const int jj = tid >> 2, c0 = 8 * (tid & 3), j = t * 64 + jj, cg = 32 * cb + c0;
+    float f[8];
+    const size_t vrow = (((size_t)b * L.M + min(j, L.M - 1)) * L.H + h) * L.Dv;
+    if ((L.Dv & 7) == 0 && cg + 8 <= L.Dv && j < L.M) {
+      if constexpr (BF) {
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(v) + vrow + cg);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int e = tid + 256 * x;  // 64 keys x 32 columns, columns fastest
-    const int jj = e >> 5, c = 32 * cb + (e & 31), j = t * 64 + jj;
-    sT[jj][e & 31] = (c < L.Dv && j < L.M) ? ld<BF>(v, (((size_t)b * L.M + j) * L.H + h) * L.Dv + c) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = __uint_as_float(w4[e] << 16);
+          f[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+        }
+      } else {
+        const float4 x0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(v) + vrow + cg);
+        const float4 x1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(v) + vrow + cg + 4);
+        f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w; f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = (cg + e < L.Dv && j < L.M) ? ld<BF>(v, vrow + cg + e) : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sT[jj][c0 + e] = f[e];
   }
   __syncthreads();
   const int cl = tid >> 3, k8 = tid & 7;
@@ -253,18 +274,41 @@ void bias_attn_kernel(BiasLayout L, const char* ws, const void* qin, const void*
   {
     const size_t xrow = (((size_t)b * L.N + i) * L.H + h) * L.D;
     const size_t prow = (((size_t)b * L.N + i) * L.H + h) * L.R;
+    const float mul = L.scale * kBiasLog2e;
 #pragma unroll
-    for (int ks = 0; ks < NQS; ++ks)
+    for (int ks = 0; ks < NQS; ++ks) {
+      const int c0 = 16 * ks + 8 * hf;
+      float f[8];
+      if (i < L.N && (L.D & 7) == 0 && c0 + 8 <= L.D) {
+        // eight q columns: one 16-byte (bf16) or two 16-byte (fp32) loads
+        if (L.bf) {
+          const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(qin) + xrow + c0);
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 16 * ks + 8 * hf + e;
-        float f = 0.f;
-        if (i < L.N) {
-          if (L.bf) f = L.bfp ? lifted<true, true>(L, 0, qin, pqin, xrow, prow, c) : lifted<true, false>(L, 0, qin, pqin, xrow, prow, c);
-          else f = L.bfp ? lifted<false, true>(L, 0, qin, pqin, xrow, prow, c) : lifted<false, false>(L, 0, qin, pqin, xrow, prow, c);
+          for (int e = 0; e < 4; ++e) {
+            f[2 * e] = __uint_as_float(w4[e] << 16) * mul;
+            f[2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u) * mul;
+          }
+        } else {
+          const float4 a0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qin) + xrow + c0);
+          const float4 a1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(qin) + xrow + c0 + 4);
+          f[0] = a0.x * mul; f[1] = a0.y * mul; f[2] = a0.z * mul; f[3] = a0.w * mul;
+          f[4] = a1.x * mul; f[5] = a1.y * mul; f[6] = a1.z * mul; f[7] = a1.w * mul;
         }
-        bq[ks][e] = (__bf16)f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = c0 + e;
+          f[e] = 0.f;
+          if (i < L.N) {
+            if (L.bf) f[e] = L.bfp ? lifted<true, true>(L, 0, qin, pqin, xrow, prow, c) : lifted<true, false>(L, 0, qin, pqin, xrow, prow, c);
+            else f[e] = L.bfp ? lifted<false, true>(L, 0, qin, pqin, xrow, prow, c) : lifted<false, false>(L, 0, qin, pqin, xrow, prow, c);
+          }
+        }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bq[ks][e] = (__bf16)f[e];
+    }
   }
 
   const char* ktg = ws + L.off_k + bh * L.MT * (size_t)KT_BYTES;
