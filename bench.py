@@ -254,13 +254,37 @@ def time_backward(name, B, N, kw, steps, min_warm_ms=40.0):
             "workspace_mb": round(ws_mb, 1)}
 
 
+def backward_cpu_baseline(N=1024):
+    """The float64 autograd oracle for a whole backward at a bounded length
+    (same widths, B=1, H=8), as algorithmic TFLOP/s (the flops of backward_flops)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle.ipa_backward import ipa_gradients
+    from rna_structure_amd.synth import IPAShape, make_inputs
+    sh = IPAShape(B=1, N=N, H=8, dtype="f32")
+    inp = make_inputs(sh, 9000 + N, frames="walk", step=3.8)
+    rng = np.random.default_rng(1)
+    du = rng.standard_normal((1, N, sh.Cout))
+    dl = rng.standard_normal((1, N, sh.H, sh.Q, 3))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ipa_gradients(inp, du, dl)
+        el = time.perf_counter() - t0
+    flops = backward_flops(sh, inp["mask"])
+    return dict(value=round(flops / el / 1e12, 6), unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"whole backward at N={N} (B1 H8, standard widths), float64 autograd oracle, {el:.1f} s")
+
+
 def backward_section(args):
     res = []
     for name, B, N, kw, steps in BACKWARD_WORKLOADS:
         res.append(time_backward(name, B, N, kw, steps))
         print(f"# backward {res[-1]}", file=sys.stderr, flush=True)
-    return {"peak_fp32_mfma_tflops": PEAK_FP32_MFMA_TFLOPS, "peak_fp32_fma_tflops": round(PEAK_FP32_FMA_TFLOPS, 1),
-            "inputs": "fp32", "runs": res}
+    sec = {"peak_fp32_mfma_tflops": PEAK_FP32_MFMA_TFLOPS, "peak_fp32_fma_tflops": round(PEAK_FP32_FMA_TFLOPS, 1),
+           "inputs": "fp32", "runs": res}
+    if not args.no_cpu_baseline:
+        sec["cpu_baseline"] = backward_cpu_baseline()
+    return sec
 
 
 def knn_cpu_baseline(N=16384, budget_s=3.0):
@@ -402,12 +426,43 @@ def time_flashbias(name, dims, kind, causal, steps, min_warm_ms=40.0):
             "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
+def flashbias_cpu_baseline(budget_s=10.0):
+    """The float64 oracle on a sample of query rows of the squared-distance
+    workload, scaled by N/rows to a whole call (algorithmic TFLOP/s)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import flashbias_rows
+    from rna_structure_amd.synth import make_bias_inputs
+    name, dims, kind, causal, _ = FLASHBIAS_WORKLOADS[1]
+    inp = make_bias_inputs(**dims, seed=8000 + dims["N"], kind=kind)
+    scale = 1.0 / math.sqrt(dims["D"])
+    N = dims["N"]
+    rng = np.random.default_rng(2)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        flashbias_rows(inp["q"], inp["k"], inp["v"], inp["phi_q"], inp["phi_k"], scale, np.arange(4))
+        per_row = (time.perf_counter() - t0) / 4
+        n = int(max(4, min(N, budget_s / max(per_row, 1e-9))))
+        rows = np.sort(rng.choice(N, size=n, replace=False))
+        t0 = time.perf_counter()
+        flashbias_rows(inp["q"], inp["k"], inp["v"], inp["phi_q"], inp["phi_k"], scale, rows)
+        el = time.perf_counter() - t0
+    per_call = el * N / n
+    flops = dims["B"] * dims["H"] * N * dims["M"] * (2 * (dims["D"] + dims["R"]) + 2 * dims["Dv"])
+    return dict(value=round(flops / per_call / 1e12, 6), unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"{n} of {N} query rows of {name}, float64 NumPy oracle, {el:.1f} s measured, "
+                       f"scaled by N/rows to {per_call:.0f} s per call")
+
+
 def flashbias_section(args):
     res = []
     for name, dims, kind, causal, steps in FLASHBIAS_WORKLOADS:
         res.append(time_flashbias(name, dims, kind, causal, max(steps, args.steps // 2)))
         print(f"# flashbias {res[-1]}", file=sys.stderr, flush=True)
-    return {"peak_bf16_tflops": PEAK_BF16_TFLOPS, "runs": res}
+    sec = {"peak_bf16_tflops": PEAK_BF16_TFLOPS, "runs": res}
+    if not args.no_cpu_baseline:
+        sec["cpu_baseline"] = flashbias_cpu_baseline()
+    return sec
 
 
 def knn_section(args):
