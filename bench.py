@@ -254,7 +254,7 @@ def time_backward(name, B, N, kw, steps, min_warm_ms=40.0):
             "workspace_mb": round(ws_mb, 1)}
 
 
-def backward_cpu_baseline(N=1024):
+def backward_cpu_baseline(N=2048):
     """The float64 autograd oracle for a whole backward at a bounded length
     (same widths, B=1, H=8), as algorithmic TFLOP/s (the flops of backward_flops)."""
     import numpy as np

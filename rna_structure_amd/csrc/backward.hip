@@ -631,11 +631,15 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   const BwLayout& L = a.L;
   constexpr int DKp = 2 * DKH, DVp = 2 * DVH;
   static_assert(32 * NKB >= DKp, "dQV blocks cover the key row");
-  __shared__ float sKT[32 * NKB][kBwKT + 1];
-  __shared__ float sVT[DVp][kBwKT + 1];
+  // row-major tiles; the pitches (floats) make 16-byte reads of 8 consecutive
+  // lanes' rows fall on distinct banks, and the key rows run to 32 NKB columns
+  // so that the dQV blocks read zeros past DKp
+  constexpr int KPI = 32 * NKB + 4, VPI = DVp + 4, QPI = DKp + 4;
+  __shared__ __align__(16) float sK[kBwKT][KPI];
+  __shared__ __align__(16) float sV[kBwKT][VPI];
   __shared__ __align__(16) float sBp[kBwKT][16];
   __shared__ float sM[kBwKT];
-  __shared__ float sQ[4][32][DKp + 1];  // each wavefront's 32 query rows QV
+  __shared__ __align__(16) float sQ[4][32][QPI];  // each wavefront's 32 query rows QV
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -647,14 +651,14 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   const float lse = wsf(a, L.off_lse)[rq];
   const float dsum = wsf(a, L.off_dd)[rq];
   const bool mq = qin && a.mask[(size_t)b * L.N + qc] != 0 && lse > -INFINITY;
-  // rows of the dQV blocks past DKp read zeros
-  for (int e = tid; e < (32 * NKB - DKp) * (kBwKT + 1); e += 256) sKT[DKp + e / (kBwKT + 1)][e % (kBwKT + 1)] = 0.f;
+  // key-row columns past DKp read zeros (the tile copies never write them)
+  for (int e = tid; e < kBwKT * (KPI - DKp); e += 256) sK[e / (KPI - DKp)][DKp + e % (KPI - DKp)] = 0.f;
   // B operands: QV[q][s + DKH hf] from LDS, dO[q][s + DVH hf] in registers
   for (int e = lane; e < 32 * (DKp / 4); e += 64) {
     const int qq = e / (DKp / 4), c4 = e - qq * (DKp / 4);
     const int qr = min(blockIdx.x * 128 + 32 * w + qq, L.N - 1);
     const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_qv) + rowidx(L, b, h, qr) * L.DKp)[c4];
-    sQ[w][qq][4 * c4] = v.x; sQ[w][qq][4 * c4 + 1] = v.y; sQ[w][qq][4 * c4 + 2] = v.z; sQ[w][qq][4 * c4 + 3] = v.w;
+    *reinterpret_cast<float4*>(&sQ[w][qq][4 * c4]) = v;
   }
   const float* qrow = &sQ[w][l32][DKH * hf];
   float dov[DVH];
@@ -685,14 +689,14 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
     for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
       const int jj = e / (DKp / 4), c4 = e - jj * (DKp / 4);
       const int j = min(j0 + jj, L.N - 1);
-      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, j) * L.DKp)[c4];
-      sKT[4 * c4][jj] = v.x; sKT[4 * c4 + 1][jj] = v.y; sKT[4 * c4 + 2][jj] = v.z; sKT[4 * c4 + 3][jj] = v.w;
+      *reinterpret_cast<float4*>(&sK[jj][4 * c4]) =
+          reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, j) * L.DKp)[c4];
     }
     for (int e = tid; e < kBwKT * (DVp / 4); e += 256) {
       const int jj = e / (DVp / 4), c4 = e - jj * (DVp / 4);
       const int j = min(j0 + jj, L.N - 1);
-      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_vv) + rowidx(L, b, h, j) * L.DVp)[c4];
-      sVT[4 * c4][jj] = v.x; sVT[4 * c4 + 1][jj] = v.y; sVT[4 * c4 + 2][jj] = v.z; sVT[4 * c4 + 3][jj] = v.w;
+      *reinterpret_cast<float4*>(&sV[jj][4 * c4]) =
+          reinterpret_cast<const float4*>(wsf(a, L.off_vv) + rowidx(L, b, h, j) * L.DVp)[c4];
     }
     for (int e = tid; e < kBwKT * 4; e += 256) {
       const int jj = e >> 2, c4 = e & 3;
@@ -706,10 +710,28 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
     __syncthreads();
     // S and dP steps interleaved: two independent chains of dependent MFMAs
     f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
+    {
+      // four K-steps per 16-byte read of the key row (A) and the query row (B)
+      const float* ka = &sK[l32][DKH * hf];
+      const float* va = &sV[l32][DVH * hf];
 #pragma unroll
-    for (int s = 0; s < (DKH > DVH ? DKH : DVH); ++s) {
-      if (s < DKH) sa = __builtin_amdgcn_mfma_f32_32x32x2f32(sKT[s + DKH * hf][l32], qrow[s], sa, 0, 0, 0);
-      if (s < DVH) pa = __builtin_amdgcn_mfma_f32_32x32x2f32(sVT[s + DVH * hf][l32], dov[s], pa, 0, 0, 0);
+      for (int s4 = 0; s4 < (DKH > DVH ? DKH : DVH) / 4; ++s4) {
+        if (4 * s4 < DKH) {
+          const float4 x = *reinterpret_cast<const float4*>(ka + 4 * s4);
+          const float4 y = *reinterpret_cast<const float4*>(qrow + 4 * s4);
+          sa = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, y.x, sa, 0, 0, 0);
+          sa = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, y.y, sa, 0, 0, 0);
+          sa = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, y.z, sa, 0, 0, 0);
+          sa = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, y.w, sa, 0, 0, 0);
+        }
+        if (4 * s4 < DVH) {
+          const float4 x = *reinterpret_cast<const float4*>(va + 4 * s4);
+          pa = __builtin_amdgcn_mfma_f32_32x32x2f32(x.x, dov[4 * s4], pa, 0, 0, 0);
+          pa = __builtin_amdgcn_mfma_f32_32x32x2f32(x.y, dov[4 * s4 + 1], pa, 0, 0, 0);
+          pa = __builtin_amdgcn_mfma_f32_32x32x2f32(x.z, dov[4 * s4 + 2], pa, 0, 0, 0);
+          pa = __builtin_amdgcn_mfma_f32_32x32x2f32(x.w, dov[4 * s4 + 3], pa, 0, 0, 0);
+        }
+      }
     }
     const int nj = min(kBwKT, L.N - j0);
     float ds[16];
@@ -738,7 +760,7 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
     for (int c = 0; c < NKB; ++c)
 #pragma unroll
       for (int s = 0; s < 16; ++s)
-        dq[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sKT[32 * c + l32][kappa(s, hf)], ds[s], dq[c], 0, 0, 0);
+        dq[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[kappa(s, hf)][32 * c + l32], ds[s], dq[c], 0, 0, 0);
   }
   // the two halves of the wavefront hold the same queries' two halves of each tile
 #pragma unroll
