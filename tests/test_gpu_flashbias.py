@@ -71,6 +71,9 @@ CASES = [
     ("no-bias-d128", dict(B=1, N=150, M=150, H=1, D=128, Dv=64, R=0), 10, "random", True, dict()),
     ("bf16-factors", dict(B=1, N=129, M=129, H=2, D=32, Dv=32, R=3), 8, "random", False, dict(phi_dtype="bf16")),
     ("one-query", dict(B=1, N=1, M=1, H=1, D=4, Dv=4, R=1), 9, "random", True, dict(dtype="f32")),
+    # causal with a batch, masked keys (one of them a query's only causal key) and an empty sample
+    ("batch-causal-masks", dict(B=3, N=200, M=200, H=2, D=32, Dv=20, R=3), 12, "random", True,
+     dict(dtype="f32", masked_keys=(0, 63, 64, 199), empty_sample=True)),
 ]
 
 
