@@ -323,20 +323,25 @@ void bias_attn_kernel(BiasLayout L, const char* ws, const void* qin, const void*
     for (int r = 0; r < 16; ++r) oacc[vb][r] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  dma_tile<KT_BYTES, 4>(ktg, smem, w, lane);
-  dma_tile<VT_BYTES, 4>(vtg, smem + KT_LDS, w, lane);
-  for (int t = 0; t < tend; ++t) {
+  // causal attention walks the key tiles from the diagonal back to the first:
+  // a bias that grows with the key index (ALiBi) then sets the running maximum
+  // on the first tile and hardly ever raises it again
+  const int t0 = L.causal ? tend - 1 : 0, dt = L.causal ? -1 : 1;
+  dma_tile<KT_BYTES, 4>(ktg + (size_t)t0 * KT_BYTES, smem, w, lane);
+  dma_tile<VT_BYTES, 4>(vtg + (size_t)t0 * VT_BYTES, smem + KT_LDS, w, lane);
+  for (int it = 0; it < tend; ++it) {
+    const int t = t0 + dt * it;
     // tile t has landed (every wavefront waits for its own copies) and every
-    // wavefront is done with tile t - 1, whose buffer the next copies refill
+    // wavefront is done with the previous tile, whose buffer the next copies refill
     wait_vmcnt<0>();
     __syncthreads();
-    if (t + 1 < tend) {
-      char* nb = smem + ((t + 1) & 1) * BUF;
-      dma_tile<KT_BYTES, 4>(ktg + (size_t)(t + 1) * KT_BYTES, nb, w, lane);
-      dma_tile<VT_BYTES, 4>(vtg + (size_t)(t + 1) * VT_BYTES, nb + KT_LDS, w, lane);
+    if (it + 1 < tend) {
+      char* nb = smem + ((it + 1) & 1) * BUF;
+      dma_tile<KT_BYTES, 4>(ktg + (size_t)(t + dt) * KT_BYTES, nb, w, lane);
+      dma_tile<VT_BYTES, 4>(vtg + (size_t)(t + dt) * VT_BYTES, nb + KT_LDS, w, lane);
     }
-    const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + (t & 1) * BUF);
-    const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + (t & 1) * BUF + KT_LDS);
+    const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + (it & 1) * BUF);
+    const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + (it & 1) * BUF + KT_LDS);
 
     // causal: a tile whose first key is past the wavefront's last query adds nothing
     if (L.causal && t * 64 > q0 + w * 32 + 31) continue;
