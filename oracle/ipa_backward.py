@@ -37,21 +37,36 @@ GRAD_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "tra
              "point_weight_raw", "w_pair", "zl", "zr", "w_out", "b_out")
 
 
-def ipa_forward_torch(t: dict, mask: torch.Tensor, pair_mask, eps: float = 1e-8) -> dict:
+def ipa_forward_torch(t: dict, mask: torch.Tensor, pair_mask, eps: float = 1e-8, rows=None) -> dict:
     """The forward on float64 tensors t[key] for key in GRAD_KEYS; mask [B,N]
     bool, pair_mask [B,N,N] bool or None.  Returns update [B,N,Cout] and
-    local_points [B,N,H,Q,3]."""
+    local_points [B,N,H,Q,3].
+
+    rows (optional, a list of query indices): only those query rows are
+    formed, each against all N keys, and the outputs are [B,len(rows),...].
+    A query row depends on its own query-side inputs and on every key, so
+    the gradient of a loss that reads only these rows is the same as that of
+    the full forward with zero upstream gradients on the other rows."""
     q, k, v = t["q"], t["k"], t["v"]
     B, N, H, D = q.shape
     P = t["q_points"].shape[3]
     R = t["rotation"]
     tr = t["translation"]
 
-    def to_global(x):                                   # T_i(x) = R_i @ x + t_i
-        return torch.einsum("bnxy,bnhpy->bnhpx", R, x) + tr[:, :, None, None, :]
+    def to_global(x, Rm, tm):                           # T_i(x) = R_i @ x + t_i
+        return torch.einsum("bnxy,bnhpy->bnhpx", Rm, x) + tm[:, :, None, None, :]
 
-    Xq, Xk, Xv = to_global(t["q_points"]), to_global(t["k_points"]), to_global(t["v_points"])
-    z = torch.einsum("birc,bjrc->bijc", t["zl"], t["zr"])               # [B,N,N,Cz]
+    # query side: the selected rows only
+    sel = slice(None) if rows is None else torch.as_tensor(rows, dtype=torch.long)
+    Ri, ti = R[:, sel], tr[:, sel]
+    Xq = to_global(t["q_points"][:, sel], Ri, ti)
+    Xk, Xv = to_global(t["k_points"], R, tr), to_global(t["v_points"], R, tr)
+    q, zl = q[:, sel], t["zl"][:, sel]
+    mask_i = mask[:, sel]
+    if pair_mask is not None:
+        pair_mask = pair_mask[:, sel]
+    Nq = q.shape[1]
+    z = torch.einsum("birc,bjrc->bijc", zl, t["zr"])                    # [B,Nq,N,Cz]
     pair_bias = torch.einsum("bijc,hc->bhij", z, t["w_pair"])
     scalar = torch.einsum("bihd,bjhd->bhij", q, k) / math.sqrt(3.0 * D)
     diff = Xq[:, :, None] - Xk[:, None, :]                               # [B,N,N,H,P,3]
@@ -59,7 +74,7 @@ def ipa_forward_torch(t: dict, mask: torch.Tensor, pair_mask, eps: float = 1e-8)
     gamma = 0.5 * torch.nn.functional.softplus(t["point_weight_raw"]) * math.sqrt(2.0 / (27.0 * P))
     logits = scalar + pair_bias / math.sqrt(3.0) - gamma[None, :, None, None] * dist
 
-    permitted = mask[:, :, None] & mask[:, None, :]
+    permitted = mask_i[:, :, None] & mask[:, None, :]
     if pair_mask is not None:
         permitted = permitted & pair_mask
     perm_h = permitted[:, None].expand_as(logits)
@@ -73,25 +88,30 @@ def ipa_forward_torch(t: dict, mask: torch.Tensor, pair_mask, eps: float = 1e-8)
     o_scalar = torch.einsum("bhij,bjhd->bihd", attention, v)
     o_pair = torch.einsum("bhij,bijc->bihc", attention, z)
     g = torch.einsum("bhij,bjhqx->bihqx", attention, Xv)
-    local = torch.einsum("biyx,bihqy->bihqx", R, g - tr[:, :, None, None, :])
+    local = torch.einsum("biyx,bihqy->bihqx", Ri, g - ti[:, :, None, None, :])
     keep = (~empty)[:, :, None, None, None].to(local.dtype)
     local = local * keep
     length = torch.sqrt((local * local).sum(-1) + eps) * keep[..., 0]
-    features = torch.cat([o_scalar.reshape(B, N, -1), local[..., 0].reshape(B, N, -1),
-                          local[..., 1].reshape(B, N, -1), local[..., 2].reshape(B, N, -1),
-                          length.reshape(B, N, -1), o_pair.reshape(B, N, -1)], dim=-1)
+    features = torch.cat([o_scalar.reshape(B, Nq, -1), local[..., 0].reshape(B, Nq, -1),
+                          local[..., 1].reshape(B, Nq, -1), local[..., 2].reshape(B, Nq, -1),
+                          length.reshape(B, Nq, -1), o_pair.reshape(B, Nq, -1)], dim=-1)
     update = (features @ t["w_out"] + t["b_out"]) * (~empty)[:, :, None].to(features.dtype)
     return dict(update=update, local_points=local)
 
 
-def ipa_gradients(inp: dict, d_update, d_local, keys=GRAD_KEYS) -> dict:
+def ipa_gradients(inp: dict, d_update, d_local, keys=GRAD_KEYS, rows=None) -> dict:
     """Gradients (float64 NumPy) of <update, d_update> + <local_points, d_local>
-    with respect to the inputs of a synth.make_inputs() set."""
+    with respect to the inputs of a synth.make_inputs() set.
+
+    With rows given, d_update [B,len(rows),Cout] and d_local
+    [B,len(rows),H,Q,3] are the upstream gradients of those query rows and
+    every other row's are zero; only the selected rows' forward is formed
+    (memory O(len(rows) N) instead of O(N^2))."""
     t = {key: torch.tensor(inp[key], dtype=torch.float64, requires_grad=key in keys) for key in GRAD_KEYS}
     mask = torch.tensor(inp["mask"], dtype=torch.bool)
     pm = inp.get("pair_mask")
     pm = None if pm is None else torch.tensor(pm, dtype=torch.bool)
-    out = ipa_forward_torch(t, mask, pm, inp["eps"])
+    out = ipa_forward_torch(t, mask, pm, inp["eps"], rows=rows)
     loss = (out["update"] * torch.tensor(d_update, dtype=torch.float64)).sum() + \
            (out["local_points"] * torch.tensor(d_local, dtype=torch.float64)).sum()
     loss.backward()

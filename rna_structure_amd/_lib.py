@@ -302,6 +302,14 @@ class FlashIPA:
         self.update = torch.empty(B, N, shape.Cout, dtype=torch.float32, device=device)
         self.local_points = torch.empty(B, N, H, Q, 3, dtype=torch.float32, device=device)
 
+    def poison(self):
+        """Fill the workspace with 0xFF bytes and the outputs with NaN (for
+        tests: whatever a kernel fails to write, or reads before it is
+        written, then shows up)."""
+        self.lifted.fill_(255)
+        for buf in (self.o, self.lse, self.update, self.local_points):
+            buf.fill_(float("nan"))
+
     def lift(self, t: dict, stream=None):
         ipa_lift(self.s, t, self.lifted, stream)
 

@@ -202,6 +202,44 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
   return true;
 }
 
+// Byte offsets of the records of the lifted workspace, used by the kernels
+// that write and read them and by the host-side bounds check of the tests.
+// Region sizes (make_layout): QL B H NQpad QW e, QA B H NQpad 64, KT B H NT
+// (64 KROW e), VT B H NT (VROWS kVCols 2 | NKpad/NT 64 VROWS 4), CK B NT 16,
+// KM B NT 8, PART KS B H NQpad PREC 4, PM B NQpad NT 8 (e = 2 on the
+// matrix-core path, 4 on the fp32 path).
+__host__ __device__ __forceinline__ size_t lifted_elem(const Layout& L) { return L.mfma ? 2 : 4; }
+__host__ __device__ __forceinline__ size_t kt_tile_bytes(const Layout& L) {
+  return (size_t)kKeyTile * L.KROW * lifted_elem(L);
+}
+__host__ __device__ __forceinline__ size_t vt_tile_bytes(const Layout& L) {
+  return L.mfma ? (size_t)L.VROWS * kVCols * 2 : (size_t)kKeyTile * L.VROWS * 4;
+}
+__host__ __device__ __forceinline__ size_t kt_tile_off(const Layout& L, int b, int h, int t) {
+  return L.off_kt + (((size_t)b * L.H + h) * L.NT + t) * kt_tile_bytes(L);
+}
+__host__ __device__ __forceinline__ size_t vt_tile_off(const Layout& L, int b, int h, int t) {
+  return L.off_vt + (((size_t)b * L.H + h) * L.NT + t) * vt_tile_bytes(L);
+}
+__host__ __device__ __forceinline__ size_t ql_row_off(const Layout& L, int b, int h, int i) {
+  return L.off_ql + (((size_t)b * L.H + h) * L.NQpad + i) * (size_t)L.QW * lifted_elem(L);
+}
+__host__ __device__ __forceinline__ size_t qa_row_off(const Layout& L, int b, int h, int i) {
+  return L.off_qa + (((size_t)b * L.H + h) * L.NQpad + i) * 64;
+}
+__host__ __device__ __forceinline__ size_t ck_off(const Layout& L, int b, int t) {
+  return L.off_ck + ((size_t)b * L.NT + t) * 16;
+}
+__host__ __device__ __forceinline__ size_t km_word_off(const Layout& L, int b, int t, int half) {
+  return L.off_km + (((size_t)b * L.NT + t) * 2 + half) * 4;
+}
+__host__ __device__ __forceinline__ size_t pm_word_off(const Layout& L, int b, int i, int t, int half) {
+  return L.off_pm + ((((size_t)b * L.NQpad + i) * L.NT + t) * 2 + half) * 4;
+}
+__host__ __device__ __forceinline__ size_t part_rec_off(const Layout& L, int s, int b, int h, int i) {
+  return L.off_part + ((((size_t)s * L.B + b) * L.H + h) * L.NQpad + i) * (size_t)L.PREC * 4;
+}
+
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) {
   return __uint_as_float(((uint32_t)u) << 16);

@@ -61,7 +61,7 @@ __device__ __forceinline__ T ld_uniform(const T* p) {
   const uint64_t a = (uint64_t)(uintptr_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return *(const __attribute__((address_space(4))) T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return *(const __attribute__((address_space(4))) T*)(uintptr_t)join_addr(hi, lo);
 }
 __device__ __forceinline__ float4 ld_uniform4(const float4* p) {
   const float* f = reinterpret_cast<const float*>(p);
@@ -184,8 +184,7 @@ __device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, 
   if (a.ks > 1) {
     // partial result: empty statistics (the combine reads no values then)
     if (lane < 32 && i0 + lane < N) {
-      float* rec = reinterpret_cast<float*>(const_cast<char*>(a.ws) + L.off_part) +
-                   ((((size_t)s * L.B + b) * H + h) * L.NQpad + i0 + lane) * L.PREC + DO;
+      float* rec = reinterpret_cast<float*>(const_cast<char*>(a.ws) + part_rec_off(L, s, b, h, i0 + lane)) + DO;
       rec[0] = -INFINITY; rec[1] = 0.f; rec[2] = 0.f; rec[3] = 0.f;
     }
     return;
@@ -236,8 +235,8 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   float m = 0.f, l = 0.f;
   bool init = false;
 
-  const char* ktg0 = a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)KT_BYTES;
-  const char* vtg0 = a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES;
+  const char* ktg0 = a.ws + kt_tile_off(L, b, h, 0);
+  const char* vtg0 = a.ws + vt_tile_off(L, b, h, 0);
   const uint32_t* kmb = km + (size_t)b * NT * 2;
   int buf = 0;
   // a wavefront without a valid query keeps copying tiles and meeting the
@@ -316,8 +315,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   // its statistics; the combine normalises
   const float ib = nonempty ? (partial ? 1.0f : (1.0f / kVScale) / lbf) : 0.f;  // the value rows hold v 2^-8
   const float ih = nonempty ? (partial ? 1.0f : 1.0f / lh) : 0.f;
-  float* prec = reinterpret_cast<float*>(const_cast<char*>(a.ws) + L.off_part) +
-                (((size_t)sp * L.B + b) * H + h) * L.NQpad * L.PREC;
+  float* prec = reinterpret_cast<float*>(const_cast<char*>(a.ws) + part_rec_off(L, sp, b, h, 0));
   if (partial && qin && half == 0) {
     float* st = prec + (size_t)i * L.PREC + DO;
     st[0] = nonempty ? m : -INFINITY;
@@ -431,8 +429,7 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   const int tb = (int)(((long)NT * sp) / a.ks), te = (int)(((long)NT * (sp + 1)) / a.ks);
   const int t0 = next_valid_tile(kmb, tb - 1, te);
   if (t0 < te)
-    copy_kv_tile<NQS, NVB, GS, W>(a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)KT_BYTES,
-                                  a.ws + L.off_vt + ((size_t)b * H + h) * NT * (size_t)VT_BYTES, sk, sv, t0, 0, w,
+    copy_kv_tile<NQS, NVB, GS, W>(a.ws + kt_tile_off(L, b, h, 0), a.ws + vt_tile_off(L, b, h, 0), sk, sv, t0, 0, w,
                                   lane);
   {
     // a workgroup none of whose queries is valid (padding) only writes zeros
@@ -453,14 +450,13 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
 
   // query operand (B of S^T): lane holds query l32, columns half*8 .. +7 of each K-step
   bf16x8_t bq[NQS];
-  load_q_frag<NQS>(reinterpret_cast<const uint4*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + i) * (QW / 8),
-                   qin, half, bq);
+  load_q_frag<NQS>(reinterpret_cast<const uint4*>(a.ws + ql_row_off(L, b, h, qin ? i : 0)), qin, half, bq);
   const bool qvalid = query_valid(L, a.ws, b, i, qin);
   f16x8_t bg[GS];
   QueryGeo qg;
   {
     float av[15];
-    load_qa(reinterpret_cast<const float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + i) * 4, qin, av);
+    load_qa(reinterpret_cast<const float4*>(a.ws + qa_row_off(L, b, h, qin ? i : 0)), qin, av);
     build_geo<GS>(L.P, av, qvalid, gl, half, bg, &qg);
   }
 

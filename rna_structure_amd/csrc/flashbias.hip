@@ -97,7 +97,7 @@ __device__ __forceinline__ uint32_t ld_scalar_u32(const uint32_t* p) {
   const uint64_t a = (uint64_t)(uintptr_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return *(const __attribute__((address_space(4))) uint32_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return *(const __attribute__((address_space(4))) uint32_t*)(uintptr_t)join_addr(hi, lo);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {

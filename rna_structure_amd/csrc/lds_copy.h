@@ -12,6 +12,28 @@ namespace fipa {
 template <int BYTES, int W>
 constexpr int dma_per_wave() { return ((BYTES + 1023) / 1024 + W - 1) / W; }
 
+// LDS bytes a copied tile occupies: whole KiB chunks (the lanes of a partial
+// last chunk land in the rounding).
+__host__ __device__ constexpr int dma_lds_bytes(int bytes) { return (bytes + 1023) / 1024 * 1024; }
+
+// The chunk that copy instruction k of wavefront w moves (a wavefront with
+// fewer chunks repeats the tile's last one), and, for lane `lane`, the byte
+// offset it reads within the tile (clamped to the tile's last 16 bytes) and
+// the byte offset it writes within the LDS buffer.
+__host__ __device__ constexpr int dma_chunk(int bytes, int W, int w, int k) {
+  return w + W * k < (bytes + 1023) / 1024 ? w + W * k : (bytes + 1023) / 1024 - 1;
+}
+__host__ __device__ constexpr uint32_t dma_src_off(int bytes, int ch, int lane) {
+  return (uint32_t)ch * 1024u + (uint32_t)lane * 16u < (uint32_t)bytes ? (uint32_t)ch * 1024u + (uint32_t)lane * 16u
+                                                                        : (uint32_t)(bytes - 16);
+}
+__host__ __device__ constexpr uint32_t dma_dst_off(int ch, int lane) { return (uint32_t)ch * 1024u + (uint32_t)lane * 16u; }
+
+// A 64-bit address from its two 32-bit halves.  Both halves must be unsigned:
+// readfirstlane returns int, and an int low word with bit 31 set would be
+// sign-extended by the join and fill the high word with ones.
+__host__ __device__ constexpr uint64_t join_addr(uint32_t hi, uint32_t lo) { return ((uint64_t)hi << 32) | (uint64_t)lo; }
+
 // Copy a tile (BYTES, a multiple of 16) global -> LDS with
 // global_load_lds_dwordx4: lane l of a wavefront moves bytes 16l .. 16l+15 of
 // one KiB chunk to M0 + 16l.  Every wavefront issues the same number of
@@ -22,22 +44,19 @@ constexpr int dma_per_wave() { return ((BYTES + 1023) / 1024 + W - 1) / W; }
 // explicitly (vmcnt) before the barrier that precedes the LDS reads.
 template <int BYTES, int W>
 __device__ __forceinline__ void dma_tile(const char* g, const char* s, int w, int lane) {
-  constexpr int nch = (BYTES + 1023) / 1024;
   const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(s);
   // the tile address is uniform; make that explicit for the SGPR operand
-  // (readfirstlane returns int: each half goes through uint32_t so that the
-  // low word is zero-extended, not sign-extended, when the halves are joined)
   const uint64_t ga = (uint64_t)(uintptr_t)g;
   const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ga);
   const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
-  g = (const char*)(uintptr_t)(((uint64_t)ghi << 32) | (uint64_t)glo);
+  g = (const char*)(uintptr_t)join_addr(ghi, glo);
 #pragma unroll
   for (int k = 0; k < dma_per_wave<BYTES, W>(); ++k) {
-    int ch = w + W * k;
-    ch = ch < nch ? ch : nch - 1;
-    const uint32_t off = (uint32_t)ch * 1024u + (uint32_t)lane * 16u;
-    const uint32_t voff = off < (uint32_t)BYTES ? off : (uint32_t)(BYTES - 16);
-    const uint32_t m0 = lbase + (uint32_t)ch * 1024u;
+    const int ch = dma_chunk(BYTES, W, w, k);
+    const uint32_t voff = dma_src_off(BYTES, ch, lane);
+    // the instruction writes lane l's 16 bytes to M0 + 16 l, i.e. at
+    // dma_dst_off(ch, l) within the buffer
+    const uint32_t m0 = lbase + dma_dst_off(ch, 0);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(g), "s"(m0)
                  : "memory", "m0");
   }

@@ -564,8 +564,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   if (tid == 64) {
     if (b == 0 && t == 0) reinterpret_cast<float*>(a.ws + L.off_gam)[h] = gam;
     if (h == 0) {
-      float4* ck = reinterpret_cast<float4*>(a.ws + L.off_ck);
-      ck[(size_t)b * L.NT + t] = make_float4(cx, cy, cz, 0.f);
+      *reinterpret_cast<float4*>(a.ws + ck_off(L, b, t)) = make_float4(cx, cy, cz, 0.f);
       if (b == 0 && t == 0) {
         Header* hd = reinterpret_cast<Header*>(a.ws);
         hd->magic = kMagic;
@@ -581,7 +580,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     uint32_t w = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) w |= (uint32_t)((vm >> (4 * (2 * k + hw))) & 0xFu) << (4 * k);
-    reinterpret_cast<uint32_t*>(a.ws + L.off_km)[((size_t)b * L.NT + t) * 2 + hw] = w;
+    *reinterpret_cast<uint32_t*>(a.ws + km_word_off(L, b, t, hw)) = w;
   }
   // a tile without a valid residue is never read: the fused kernel skips
   // key tiles without a valid key and writes padding queries as zeros
@@ -627,7 +626,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       }
     }
     __syncthreads();  // the raw point rows are read; the staging array is free
-    uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * L.KROW;
+    uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + kt_tile_off(L, b, h, t));
     auto vh = [](uint16_t bits) { return f32_to_f16_bits(bf16_bits_to_f32(bits) * kVScale); };
 #pragma unroll
     for (int k = 0; k < kFastZ; ++k) {
@@ -659,7 +658,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     {
       const float sq = kLog2e / sqrtf(3.0f * (float)D);
       const float sp = kLog2e / sqrtf(3.0f);
-      uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + (size_t)t * 64) * QW;
+      uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + ql_row_off(L, b, h, t * 64));
 #pragma unroll
       for (int k = 0; k < kFastZ; ++k) {
         const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
@@ -748,7 +747,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     }
     // query global points: 16 floats per (b, h, i)
     {
-      float4* qa = reinterpret_cast<float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + (size_t)t * 64) * 4;
+      float4* qa = reinterpret_cast<float4*>(a.ws + qa_row_off(L, b, h, t * 64));
       const int row = tid / 4, c = (tid % 4) * 4;
       float v[4];
 #pragma unroll
@@ -757,7 +756,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     }
     // transposed value tile: rows d, columns kappa; columns k0 .. k0+7 hold keys
     // j0 .. j0+3 and j0+8 .. j0+11 (j0 = vt_key_of_col(k0)), columns 64 .. 71 are zero
-    uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + L.off_vt) + (((size_t)b * H + h) * L.NT + t) * VROWS * kVCols;
+    uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + vt_tile_off(L, b, h, t));
     const uint32_t vm0 = s_vmask[0], vm1 = s_vmask[1];
     // rows [v | zr]: 8 column chunks each, straight from the transposed LDS copy
     for (int x = tid; x < DZ * 8; x += 256) {
@@ -798,7 +797,6 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   // ---- 5. permitted-key words of every query row for this key tile
   // (the H workgroups of the tile share the query rows: rows h, h + H, ...)
   if (a.pm != nullptr) {
-    uint32_t* pmw = reinterpret_cast<uint32_t*>(a.ws + L.off_pm);
     for (int i = tid * H + h; i < L.NQpad; i += 256 * H) {
       uint32_t w[2] = {0u, 0u};
       if (tile_any && i < N && a.mask[(size_t)b * N + i]) {
@@ -831,8 +829,8 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
           }
         }
       }
-      pmw[(((size_t)b * L.NQpad + i) * L.NT + t) * 2] = w[0];
-      pmw[(((size_t)b * L.NQpad + i) * L.NT + t) * 2 + 1] = w[1];
+      *reinterpret_cast<uint32_t*>(a.ws + pm_word_off(L, b, i, t, 0)) = w[0];
+      *reinterpret_cast<uint32_t*>(a.ws + pm_word_off(L, b, i, t, 1)) = w[1];
     }
   }
 }

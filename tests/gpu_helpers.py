@@ -17,11 +17,15 @@ def say(msg: str):
 
 
 def run_gpu(inp: dict, eps=None):
+    """One forward on fresh buffers that are poisoned first (workspace bytes
+    0xFF, outputs NaN), so a region the kernels skip, or read unwritten,
+    cannot pass on values left behind by an earlier call."""
     import torch
     from rna_structure_amd import _lib
     shape = inp["shape"]
     t = _lib.device_inputs(inp, "cuda")
     f = _lib.FlashIPA(shape, eps=inp["eps"] if eps is None else eps, with_pair_mask=t["pair_mask"] is not None)
+    f.poison()
     out = f.forward(t)
     torch.cuda.synchronize()
     return f, t, {k: v.detach().cpu().numpy().astype(np.float64) for k, v in out.items()}
@@ -65,8 +69,9 @@ def compare(inp: dict, gpu: dict, rows=None, tol=2e-2, lse_tol=None, verbose=Tru
         bi = np.nonzero(empty)
         assert np.all(gpu["update"][:, rows][bi] == 0.0)
         assert np.all(gpu["local_points"][:, rows][bi] == 0.0)
-    for key in ("update", "local_points"):
+    for key in ("update", "local_points", "o"):
         assert np.all(np.isfinite(gpu[key])), key
+    assert not np.any(np.isnan(gpu["lse"])), "lse"
     if verbose:
         say("  max-abs-rel " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     lt = tol if lse_tol is None else lse_tol

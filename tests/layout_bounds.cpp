@@ -1,0 +1,255 @@
+// Host-side bounds check of the lifted workspace and of the direct
+// global -> LDS tile copies, built from the library's own headers (the same
+// offset functions and copy arithmetic the kernels use) and run on the CPU.
+//
+//  1. Copy arithmetic (lds_copy.h) for every tile size the kernels copy: each
+//     lane reads inside the tile, writes inside the KiB-rounded LDS buffer,
+//     every byte of the tile is copied to the same offset, and a lane whose
+//     read is clamped to the tile's last 16 bytes writes past the tile (it
+//     never overwrites tile data).
+//  2. Address join: a 64-bit address rebuilt from its two 32-bit halves is
+//     the address itself, also when bit 31 of the low half is set.  Joining
+//     an int low half instead sign-extends it and fills the high word with
+//     ones, i.e. a wild address.
+//  3. Workspace layout (common.h make_layout) for the benchmark
+//     configurations and ragged or odd shapes: the regions are disjoint and
+//     in order, inside the total size, and the last record of every region
+//     that the lift writes or the fused kernel reads (key and value tiles,
+//     query rows and points, centroids, mask words, partial results, pair
+//     mask words) ends inside its region; the tile sizes the fused kernel
+//     compiles in equal the layout's; key ranges hold at least one tile each;
+//     the workgroup remap of the fused kernel is a permutation.
+// Prints "layout bounds: N checks ok" and exits 0, or names the first
+// failure and exits 1.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "../rna_structure_amd/csrc/common.h"
+#include "../rna_structure_amd/csrc/lds_copy.h"
+
+using namespace fipa;
+
+static long g_checks = 0;
+#define CHECK(cond, ...)                                           \
+  do {                                                             \
+    ++g_checks;                                                    \
+    if (!(cond)) {                                                 \
+      std::printf("FAIL %s:%d: %s -- ", __FILE__, __LINE__, #cond); \
+      std::printf(__VA_ARGS__);                                    \
+      std::printf("\n");                                           \
+      std::exit(1);                                                \
+    }                                                              \
+  } while (0)
+
+// ---------------------------------------------------------------- 1. copies
+static void check_copy(int bytes, int W, int per_wave, const char* what) {
+  CHECK(bytes % 16 == 0 && bytes >= 16, "%s: %d bytes", what, bytes);
+  const int lds = dma_lds_bytes(bytes);
+  std::vector<int> hit(bytes, 0);
+  for (int w = 0; w < W; ++w)
+    for (int k = 0; k < per_wave; ++k) {
+      const int ch = dma_chunk(bytes, W, w, k);
+      CHECK(ch >= 0 && ch * 1024 < bytes, "%s: chunk %d of %d bytes", what, ch, bytes);
+      for (int lane = 0; lane < 64; ++lane) {
+        const uint32_t src = dma_src_off(bytes, ch, lane), dst = dma_dst_off(ch, lane);
+        CHECK(src + 16 <= (uint32_t)bytes, "%s: read %u of %d", what, src, bytes);
+        CHECK(dst + 16 <= (uint32_t)lds, "%s: write %u of %d", what, dst, lds);
+        if (src == dst) {
+          for (int e = 0; e < 16; ++e) hit[src + e] = 1;
+        } else {
+          CHECK(dst >= (uint32_t)bytes, "%s: clamped lane writes tile byte %u", what, dst);
+        }
+      }
+    }
+  for (int x = 0; x < bytes; ++x) CHECK(hit[x], "%s: byte %d of %d never copied", what, x, bytes);
+}
+
+template <int BYTES, int W>
+static void check_copy_inst(const char* what) {
+  check_copy(BYTES, W, dma_per_wave<BYTES, W>(), what);
+}
+
+template <int NQS, int NVB, int GS, int W>
+static void check_fused_inst() {
+  // the tile sizes of flash_mfma_kernel<NQS, NVB, GS, W>
+  constexpr int KT_BYTES = 64 * (16 * NQS + 16 * GS + kRowPad) * 2;
+  constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
+  check_copy_inst<KT_BYTES, W>("fused key tile");
+  check_copy_inst<VT_BYTES, W>("fused value tile");
+}
+
+template <int NQS>
+static void check_bias_inst() {
+  // the tile sizes of bias_attn_kernel<NQS, NVB> (4 wavefronts)
+  constexpr int KP = 16 * NQS + 8;
+  check_copy_inst<64 * KP * 2, 4>("bias key tile");
+  check_copy_inst<32 * 1 * 72 * 2, 4>("bias value tile");
+  check_copy_inst<32 * 2 * 72 * 2, 4>("bias value tile");
+  check_copy_inst<32 * 4 * 72 * 2, 4>("bias value tile");
+  check_copy_inst<32 * 8 * 72 * 2, 4>("bias value tile");
+}
+
+static void check_copies() {
+  check_fused_inst<3, 2, 3, 4>(); check_fused_inst<3, 2, 3, 8>(); check_fused_inst<3, 2, 4, 4>();
+  check_fused_inst<3, 2, 4, 8>(); check_fused_inst<5, 3, 3, 4>(); check_fused_inst<5, 3, 3, 8>();
+  check_fused_inst<5, 3, 4, 4>(); check_fused_inst<5, 3, 4, 8>(); check_fused_inst<9, 5, 3, 4>();
+  check_fused_inst<9, 5, 3, 8>(); check_fused_inst<9, 5, 4, 4>(); check_fused_inst<9, 5, 4, 8>();
+  check_fused_inst<13, 7, 3, 4>(); check_fused_inst<13, 7, 4, 4>();
+  // epilogue: W_h of Cout rows at the head-feature pitch, 4 wavefronts
+  check_copy_inst<32 * kHeadFeatPitch * 2, 4>("epilogue w_out head");
+  check_copy_inst<64 * kHeadFeatPitch * 2, 4>("epilogue w_out head");
+  check_copy_inst<96 * kHeadFeatPitch * 2, 4>("epilogue w_out head");
+  check_copy_inst<128 * kHeadFeatPitch * 2, 4>("epilogue w_out head");
+  check_bias_inst<2>(); check_bias_inst<3>(); check_bias_inst<4>(); check_bias_inst<5>();
+  check_bias_inst<8>(); check_bias_inst<9>(); check_bias_inst<16>();
+  // every size a copy can have, on 4 and 8 wavefronts
+  for (int bytes = 16; bytes <= 40 * 1024; bytes += 16) {
+    check_copy(bytes, 4, ((bytes + 1023) / 1024 + 3) / 4, "any size, W=4");
+    check_copy(bytes, 8, ((bytes + 1023) / 1024 + 7) / 8, "any size, W=8");
+  }
+}
+
+// ---------------------------------------------------------------- 2. join
+static void check_join() {
+  const uint64_t addrs[] = {0x00007f0000000000ull, 0x00007f1234567890ull, 0x00007f12ffffff00ull,
+                            0x00007f1280000000ull, 0x00007f12fffffff0ull, 0x0000000100000000ull,
+                            0x000000017fffffffull, 0x0000000180000000ull};
+  for (uint64_t a : addrs) {
+    const uint32_t lo = (uint32_t)a, hi = (uint32_t)(a >> 32);
+    CHECK(join_addr(hi, lo) == a, "join of %llx", (unsigned long long)a);
+    // the pitfall: a signed low half
+    const int slo = (int)lo;
+    const uint64_t wrong = ((uint64_t)hi << 32) | (uint64_t)(int64_t)slo;
+    if (lo & 0x80000000u)
+      CHECK((wrong >> 32) == 0xffffffffull, "sign extension of %llx", (unsigned long long)a);
+    else
+      CHECK(wrong == a, "no sign extension for %llx", (unsigned long long)a);
+  }
+}
+
+// ---------------------------------------------------------------- 3. layout
+struct Region {
+  const char* name;
+  size_t start, end;  // [start, end), end = start of the next region
+};
+
+static void check_layout(const ipa_shape& s, int with_pm) {
+  Layout L;
+  if (!make_layout(&s, with_pm, &L)) return;  // unsupported shape: nothing to check
+  char tag[160];
+  std::snprintf(tag, sizeof tag, "B%lld N%lld H%lld D%lld Dv%lld P%lld Q%lld Cz%lld R%lld Cout%lld %s pm%d",
+                (long long)s.B, (long long)s.N, (long long)s.H, (long long)s.D, (long long)s.Dv, (long long)s.P,
+                (long long)s.Q, (long long)s.Cz, (long long)s.R, (long long)s.Cout,
+                s.dtype == IPA_BF16 ? "bf16" : "f32", with_pm);
+  const int B = L.B, H = L.H, NT = L.NT;
+  const size_t e = lifted_elem(L);
+  CHECK(L.NKpad == NT * 64 && L.NKpad <= L.NQpad, "%s: padded rows", tag);
+  // region order and sizes
+  const Region reg[] = {
+      {"QL", L.off_ql, L.off_qa}, {"QA", L.off_qa, L.off_kt},   {"KT", L.off_kt, L.off_vt},
+      {"VT", L.off_vt, L.off_ck}, {"CK", L.off_ck, L.off_gam},  {"GAM", L.off_gam, L.off_km},
+      {"KM", L.off_km, L.off_wt}, {"WT", L.off_wt, L.off_part}, {"PART", L.off_part, L.off_pm},
+      {"PM", L.off_pm, L.total}};
+  CHECK(L.off_ql >= sizeof(Header), "%s: header", tag);
+  for (const Region& r : reg) CHECK(r.start <= r.end && r.start % 256 == 0, "%s: region %s", tag, r.name);
+  auto inside = [&](const Region& r, size_t off, size_t bytes, const char* what) {
+    CHECK(off >= r.start && off + bytes <= r.end, "%s: %s [%zu, %zu) outside %s [%zu, %zu)", tag, what, off,
+          off + bytes, r.name, r.start, r.end);
+  };
+  // per-region sizes the layout reserves, against the records
+  CHECK(L.off_qa - L.off_ql >= (size_t)B * H * L.NQpad * L.QW * e, "%s: QL size", tag);
+  const size_t ktb = kt_tile_bytes(L), vtb = vt_tile_bytes(L);
+  for (int b : {0, B - 1})
+    for (int h : {0, H - 1}) {
+      for (int t : {0, NT - 1}) {
+        inside(reg[2], kt_tile_off(L, b, h, t), ktb, "key tile");
+        inside(reg[3], vt_tile_off(L, b, h, t), vtb, "value tile");
+      }
+      // the lift writes query rows of every key-tile residue (< NKpad), the
+      // fused kernel reads rows < N
+      for (int i : {0, L.N - 1, L.NKpad - 1, L.NQpad - 1}) {
+        inside(reg[0], ql_row_off(L, b, h, i), (size_t)L.QW * e, "query row");
+        inside(reg[1], qa_row_off(L, b, h, i), 64, "query points");
+      }
+    }
+  for (int b : {0, B - 1})
+    for (int t : {0, NT - 1}) {
+      inside(reg[4], ck_off(L, b, t), 16, "centroid");
+      for (int hf = 0; hf < 2; ++hf) inside(reg[6], km_word_off(L, b, t, hf), 4, "key-mask word");
+      if (with_pm)
+        for (int i : {0, L.NQpad - 1})
+          for (int hf = 0; hf < 2; ++hf) inside(reg[9], pm_word_off(L, b, i, t, hf), 4, "pair-mask word");
+    }
+  inside(reg[5], L.off_gam, (size_t)H * 4, "point weights");
+  if (L.mfma) {
+    // the tile sizes of the fused kernel instance picked for this layout
+    const size_t KT_BYTES = 64 * (size_t)(16 * L.NQS + 16 * L.GS + kRowPad) * 2;
+    const size_t VT_BYTES = 32 * (size_t)(L.NVB + 1) * kVCols * 2;
+    CHECK(ktb == KT_BYTES && vtb == VT_BYTES, "%s: tile bytes %zu %zu vs %zu %zu", tag, ktb, vtb, KT_BYTES, VT_BYTES);
+    // packed w_out of the epilogue (per head or transposed)
+    const size_t wt = (size_t)L.H * L.Cout * kHeadFeatPitch * 2, wt2 = (size_t)L.Cout * L.FP * 2;
+    inside(reg[7], L.off_wt, wt > wt2 ? wt : wt2, "packed w_out");
+    // key ranges of the fused kernel: [NT s / KS, NT (s + 1) / KS), each nonempty
+    CHECK(L.KS >= 1 && L.KS <= 4, "%s: KS %d", tag, L.KS);
+    for (int sp = 0; sp < L.KS; ++sp) {
+      const int tb = (int)(((long)NT * sp) / L.KS), te = (int)(((long)NT * (sp + 1)) / L.KS);
+      CHECK(te > tb, "%s: empty key range %d", tag, sp);
+    }
+    if (L.KS > 1)
+      for (int i : {0, L.NQpad - 1})
+        inside(reg[8], part_rec_off(L, L.KS - 1, B - 1, H - 1, i), (size_t)L.PREC * 4, "partial record");
+    CHECK(L.PREC >= L.DO + 4 && L.PREC % 4 == 0, "%s: PREC", tag);
+    // workgroup remap of the fused kernel (8 or 4 wavefronts per workgroup)
+    for (int W : {4, 8}) {
+      const int qtiles = (L.N + 32 * W - 1) / (32 * W);
+      const long nwg = (long)qtiles * H * B * L.KS;
+      if (nwg > (1 << 22) || nwg % 8) continue;
+      std::vector<char> seen(nwg, 0);
+      for (long wg = 0; wg < nwg; ++wg) {
+        const long logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
+        CHECK(logical >= 0 && logical < nwg && !seen[logical], "%s: remap %ld", tag, wg);
+        seen[logical] = 1;
+      }
+    }
+  }
+  CHECK(L.total == (with_pm ? align256(L.off_pm + (size_t)B * L.NQpad * NT * 8) : L.off_pm), "%s: total", tag);
+}
+
+static ipa_shape shape(long B, long N, long H, long D, long Dv, long P, long Q, long Cz, long R, long Cout, int dt) {
+  ipa_shape s;
+  s.B = B; s.N = N; s.H = H; s.D = D; s.Dv = Dv; s.P = P; s.Q = Q; s.Cz = Cz; s.R = R; s.Cout = Cout;
+  s.dtype = dt;
+  s.eps = 1e-8f;
+  return s;
+}
+
+static void check_layouts() {
+  std::vector<ipa_shape> v;
+  // the benchmark configurations
+  v.push_back(shape(1, 16, 4, 16, 16, 4, 8, 16, 2, 128, IPA_F32));
+  v.push_back(shape(8, 256, 8, 16, 16, 4, 8, 64, 2, 128, IPA_BF16));
+  v.push_back(shape(1, 2048, 8, 16, 16, 4, 8, 64, 2, 128, IPA_BF16));
+  v.push_back(shape(39, 512, 12, 16, 16, 4, 8, 64, 2, 128, IPA_BF16));
+  for (long n : {4096L, 8192L, 16384L, 32768L}) v.push_back(shape(1, n, 8, 16, 16, 4, 8, 64, 2, 128, IPA_BF16));
+  // ragged lengths, ranks 1..3, every point count, small and odd widths, both paths
+  for (long n : {1L, 2L, 63L, 64L, 65L, 127L, 128L, 129L, 200L, 255L, 256L, 257L, 600L, 1000L, 1024L, 1100L, 5000L})
+    for (int dt : {IPA_F32, IPA_BF16}) {
+      v.push_back(shape(1, n, 8, 16, 16, 4, 8, 64, 2, 128, dt));
+      v.push_back(shape(3, n, 3, 16, 16, 4, 8, 64, 3, 128, dt));
+      v.push_back(shape(2, n, 2, 8, 8, 5, 9, 48, 1, 64, dt));
+      v.push_back(shape(2, n, 3, 4, 3, 2, 2, 5, 2, 6, dt));
+      for (long P = 1; P <= 5; ++P) v.push_back(shape(1, n, 2, 8, 16, P, 4, 40, 2, 64, dt));
+      v.push_back(shape(2, n, 12, 16, 16, 4, 8, 64, 2, 96, dt));
+    }
+  for (const ipa_shape& s : v)
+    for (int pm : {0, 1}) check_layout(s, pm);
+}
+
+int main() {
+  check_copies();
+  check_join();
+  check_layouts();
+  std::printf("layout bounds: %ld checks ok\n", g_checks);
+  return 0;
+}

@@ -141,3 +141,30 @@ def test_empty_rows_pass_no_gradient():
     g1 = ipa_gradients(inp, du2, dl2)
     for key in GRAD_KEYS:
         np.testing.assert_allclose(g1[key], g0[key], rtol=0, atol=1e-12, err_msg=key)
+
+
+def test_row_restricted_gradients_equal_full_with_zero_upstream_elsewhere():
+    """The row-restricted forward (only the selected query rows, against all
+    keys) gives the full oracle's gradients when the upstream gradients of
+    every other row are zero: masks, a pair mask and the empty row included,
+    rows in any order, a repeated row counted twice."""
+    inp = _small(13, B=2, N=9, H=3, masked_keys=(2,), pair_dropout=0.2, empty_row=True)
+    du, dl = _upstream(inp, 14)
+    for rows in ([0, 4, 8], [7, 1], [3, 3, 5]):
+        du_full, dl_full = np.zeros_like(du), np.zeros_like(dl)
+        for k, i in enumerate(rows):
+            du_full[:, i] += du[:, k]
+            dl_full[:, i] += dl[:, k]
+        g_full = ipa_gradients(inp, du_full, dl_full)
+        g_rows = ipa_gradients(inp, du[:, :len(rows)], dl[:, :len(rows)], rows=rows)
+        for key in GRAD_KEYS:
+            np.testing.assert_allclose(g_rows[key], g_full[key], rtol=1e-12, atol=1e-13, err_msg=f"{rows} {key}")
+    # the restricted forward's outputs are the full forward's rows
+    t = _tensors(inp)
+    mask = torch.tensor(inp["mask"], dtype=torch.bool)
+    pm = torch.tensor(inp["pair_mask"], dtype=torch.bool)
+    full = ipa_forward_torch(t, mask, pm, inp["eps"])
+    part = ipa_forward_torch(t, mask, pm, inp["eps"], rows=[8, 2, 5])
+    for key in ("update", "local_points"):
+        np.testing.assert_allclose(part[key].detach().numpy(), full[key].detach().numpy()[:, [8, 2, 5]],
+                                   rtol=1e-13, atol=1e-14)

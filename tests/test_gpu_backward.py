@@ -29,6 +29,10 @@ def _run(inp, du, dl):
     shape = inp["shape"]
     t = _lib.device_inputs(inp, "cuda")
     bw = _lib.IPABackward(shape, eps=inp["eps"])
+    # NaN in the workspace and in every gradient buffer: a region the
+    # kernels fail to write shows up in the comparison
+    bw.ws.fill_(255)
+    bw.grads = {n: torch.full_like(t[n], float("nan"), dtype=torch.float32) for n in GRAD_KEYS}
     g = bw(t, torch.from_numpy(du).cuda(), torch.from_numpy(dl).cuda())
     torch.cuda.synchronize()
     return {key: v.cpu().numpy().astype(np.float64) for key, v in g.items()}
@@ -90,3 +94,47 @@ def test_backward_properties_at_length_4096():
     scale = np.sum(np.abs(np.einsum("nxy,nzy->nxz", g["rotation"][0], R))) + np.sum(np.abs(np.einsum("nx,nz->nxz", dt, t)))
     assert np.max(np.abs(M - M.T)) <= 1e-4 * scale, "common rotation"
     np.testing.assert_allclose(g["b_out"], du[0].astype(np.float64).sum(axis=0), rtol=1e-5, atol=1e-3)
+
+
+def _compare(got, ref, label):
+    errs = {}
+    for key in GRAD_KEYS:
+        scale = np.max(np.abs(ref[key]))
+        errs[key] = np.max(np.abs(got[key] - ref[key])) / scale if scale > 0 else np.max(np.abs(got[key]))
+    say(f"  {label} max-abs-rel " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    for key, v in errs.items():
+        assert v <= 1e-4, (key, v)
+
+
+def test_backward_full_at_length_2048():
+    """The RNA-like length with the standard widths (B1 N2048 H8, 6 A walk,
+    the backward workload the benchmark times first): all 14 gradients
+    against the dense float64 autograd oracle, every upstream row nonzero."""
+    shape = IPAShape(B=1, N=2048, H=8, dtype="f32")
+    say(f"case backward full {shape}")
+    inp = make_inputs(shape, 2048, frames="walk", step=6.0)
+    du, dl = _upstream(shape, 2049)
+    got = _run(inp, du, dl)
+    ref = ipa_gradients(inp, du.astype(np.float64), dl.astype(np.float64))
+    _compare(got, ref, "N=2048")
+
+
+@pytest.mark.parametrize("n,dtype", [(4096, "bf16"), (16384, "f32")])
+def test_backward_sampled_rows_at_benchmark_lengths(n, dtype):
+    """The lengths the benchmark times the backward at: upstream gradients
+    zero except on 16 sampled query rows (tile edges and the last row
+    included), so every input gradient is exact in the row-restricted float64
+    oracle (those rows against all keys).  Key-side gradients (k, v, points,
+    zr, frames) still collect contributions from every key of the chain."""
+    shape = IPAShape(B=1, N=n, H=8, dtype=dtype)
+    say(f"case backward sampled rows {shape}")
+    inp = make_inputs(shape, n + 5, frames="walk", step=3.8)
+    rng = np.random.default_rng(n)
+    rows = sorted(set(rng.choice(n, 12, replace=False).tolist()) | {0, 63, 64, n - 1})
+    du_r, dl_r = _upstream(IPAShape(B=1, N=len(rows), H=8), n + 1)
+    du = np.zeros((1, n, shape.Cout), np.float32)
+    dl = np.zeros((1, n, shape.H, shape.Q, 3), np.float32)
+    du[:, rows], dl[:, rows] = du_r, dl_r
+    got = _run(inp, du, dl)
+    ref = ipa_gradients(inp, du_r.astype(np.float64), dl_r.astype(np.float64), rows=rows)
+    _compare(got, ref, f"N={n} rows={len(rows)}")

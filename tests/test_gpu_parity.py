@@ -150,9 +150,10 @@ def test_deterministic():
     inp = make_config("protein")
     say("case determinism")
     _, _, g1 = run_gpu(inp)
-    _, _, g2 = run_gpu(inp)
+    _, _, g2 = run_gpu(inp)  # run_gpu poisons the buffers again before the second forward
     for k in ("update", "local_points", "o", "lse"):
-        assert np.array_equal(g1[k], g2[k], equal_nan=True), k
+        assert not np.any(np.isnan(g1[k])), k
+        assert np.array_equal(g1[k], g2[k]), k
 
 
 def test_rigid_invariance_gpu_f32():
@@ -172,5 +173,6 @@ def test_rigid_invariance_gpu_f32():
     moved["translation"] = (np.einsum("xy,bny->bnx", G, inp["translation"]) + 100.0).astype(np.float32).astype(np.float64)
     _, _, g2 = run_gpu(moved)
     for k in ("update", "local_points"):
+        assert np.all(np.isfinite(g1[k])) and np.all(np.isfinite(g2[k])), k
         err = np.max(np.abs(g1[k] - g2[k])) / np.max(np.abs(g1[k]))
         assert err <= 1e-4, (k, err)
