@@ -16,6 +16,10 @@
  *   ipa_flash_fwd fused masked online-softmax attention over lifted rows
  *   ipa_epilogue  inverse frame transform, pair expansion, point lengths,
  *                 head-major feature concat and the output projection
+ * Their buffers: the lifted workspace (ipa_lifted_bytes; written by
+ * ipa_lift, read by ipa_flash_fwd), the attention output o and lse (written
+ * by ipa_flash_fwd, read by ipa_epilogue) and the epilogue's workspace
+ * (ipa_epilogue_workspace_bytes), all caller-owned.
  *
  * Conventions shared by every call
  *  - All device pointers refer to memory of the current HIP device; tensors
@@ -115,7 +119,8 @@ typedef struct {
 
 /* Size in bytes of the opaque "lifted" workspace that ipa_lift fills and
  * ipa_flash_fwd reads (lifted query rows, key/value tiles, per-tile
- * centroids, point weights, packed masks).  with_pair_mask != 0 reserves
+ * centroids, point weights, packed masks, and the partial results of the
+ * fused kernel's key ranges when it splits them).  with_pair_mask != 0 reserves
  * room for a bit-packed pair mask (B*N*ceil(N/64)*8 bytes, the only part
  * that grows as N^2/8); pass 0 when ipa_lift will get pair_mask == NULL.
  * Returns 0 for an invalid or unsupported shape. */
@@ -153,21 +158,31 @@ ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, siz
  * MFMA for the centred point columns, fp32 softmax and accumulation. */
 ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream);
 
+/* Bytes of the epilogue's own workspace for this shape (the output
+ * projection packed for the matrix-core product: per head or transposed,
+ * bf16); at least 16.  0 for an invalid shape or one the epilogue does not
+ * support. */
+size_t ipa_epilogue_workspace_bytes(const ipa_shape* s);
+
 /* Kernel 3 (epilogue).  Per residue i: local_points = R_i^T (g - t_i) for
  * every head and value point, lengths sqrt(|local|^2 + eps), pair features
  * o_pair = sum_r zl_ir * o_zr_r, head-major concat
  * [scalar (H,Dv) | x (H,Q) | y | z | length (H,Q) | pair (H,Cz)], and
  * update = features @ w_out + b_out; everything zero for an empty
  * neighbourhood (IPA page, "Required behavior").
- *   lifted       the workspace of ipa_lift (a region of it receives w_out
- *                transposed; the lifted rows are not touched)
+ *   workspace    caller-owned, workspace_bytes >= ipa_epilogue_workspace_bytes(s);
+ *                overwritten with w_out packed for the product (may be NULL
+ *                on the fp32 path, which packs nothing).  The lifted rows of
+ *                ipa_lift are not an argument: the epilogue reads only o, lse
+ *                and the inputs below.
  *   o, lse       from ipa_flash_fwd
  *   update       [B,N,Cout] fp32 (written)
  *   local_points [B,N,H,Q,3] fp32 (written)
  * IPA_ERR_UNSUPPORTED if the feature row F does not fit the kernel's LDS
- * staging (bf16 path: F <= 2544; fp32 path: F <= 2559). */
-ipa_status ipa_epilogue(const ipa_shape* s, void* lifted, const float* o, const float* lse, const ipa_epi_in* in,
-                        float* update, float* local_points, void* stream);
+ * staging (bf16 path: F <= 2544; fp32 path: F <= 2559); IPA_ERR_SHAPE if
+ * the workspace is too small. */
+ipa_status ipa_epilogue(const ipa_shape* s, void* workspace, size_t workspace_bytes, const float* o, const float* lse,
+                        const ipa_epi_in* in, float* update, float* local_points, void* stream);
 
 /* Diagnostic (tests only): the logits the fused kernel uses, for query rows
  * row0 .. row0+nrows-1 of (b, h), recomputed from the lifted rows with the

@@ -19,7 +19,8 @@ LIB_PATH = os.environ.get("FLASHIPA_LIBRARY", os.path.join(HERE, "libflashipa.so
 IPA_F32, IPA_BF16 = 0, 1
 STATUS = {0: "IPA_OK", 1: "IPA_ERR_NULL", 2: "IPA_ERR_SHAPE", 3: "IPA_ERR_UNSUPPORTED",
           4: "IPA_ERR_ALIGN", 5: "IPA_ERR_LAUNCH", 6: "IPA_ERR_DEVICE"}
-EXPORTS = ("ipa_lifted_bytes", "ipa_o_width", "ipa_lift", "ipa_flash_fwd", "ipa_epilogue",
+EXPORTS = ("ipa_lifted_bytes", "ipa_o_width", "ipa_lift", "ipa_flash_fwd", "ipa_epilogue_workspace_bytes",
+           "ipa_epilogue",
            "ipa_logit_rows", "ipa_backward_workspace_bytes", "ipa_backward", "ipa_knn_distogram",
            "ipa_bias_workspace_bytes", "ipa_bias_attention", "ipa_status_string", "ipa_version")
 GRAD_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "translation",
@@ -83,7 +84,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipa_lift.restype = ctypes.c_int
     lib.ipa_flash_fwd.argtypes = [sp, vp, vp, vp, vp]
     lib.ipa_flash_fwd.restype = ctypes.c_int
-    lib.ipa_epilogue.argtypes = [sp, vp, vp, vp, ctypes.POINTER(IpaEpiIn), vp, vp, vp]
+    lib.ipa_epilogue_workspace_bytes.argtypes = [sp]
+    lib.ipa_epilogue_workspace_bytes.restype = sz
+    lib.ipa_epilogue.argtypes = [sp, vp, sz, vp, vp, ctypes.POINTER(IpaEpiIn), vp, vp, vp]
     lib.ipa_epilogue.restype = ctypes.c_int
     lib.ipa_logit_rows.argtypes = [sp, vp, i64, i64, i64, i64, vp, vp]
     lib.ipa_logit_rows.restype = ctypes.c_int
@@ -150,10 +153,15 @@ def ipa_flash_fwd(s: IpaShape, lifted, o, lse, stream=None):
                                                  _stream(stream)))
 
 
-def ipa_epilogue(s: IpaShape, lifted, o, lse, t: dict, update, local_points, stream=None):
+def epilogue_workspace_bytes(s: IpaShape) -> int:
+    return int(load().ipa_epilogue_workspace_bytes(ctypes.byref(s)))
+
+
+def ipa_epilogue(s: IpaShape, workspace, o, lse, t: dict, update, local_points, stream=None):
     ei = IpaEpiIn(*[_ptr(t[n]) for n in ("zl", "rotation", "translation", "w_out", "b_out")])
-    _check("ipa_epilogue", load().ipa_epilogue(ctypes.byref(s), _ptr(lifted), _ptr(o), _ptr(lse), ctypes.byref(ei),
-                                               _ptr(update), _ptr(local_points), _stream(stream)))
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("ipa_epilogue", load().ipa_epilogue(ctypes.byref(s), _ptr(workspace), nbytes, _ptr(o), _ptr(lse),
+                                               ctypes.byref(ei), _ptr(update), _ptr(local_points), _stream(stream)))
 
 
 def ipa_logit_rows(s: IpaShape, lifted, b: int, h: int, row0: int, nrows: int, out, stream=None):
@@ -296,6 +304,10 @@ class FlashIPA:
         if nbytes == 0:
             raise IPAError("ipa_lifted_bytes", 3)
         self.lifted = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ebytes = epilogue_workspace_bytes(self.s)
+        if ebytes == 0:
+            raise IPAError("ipa_epilogue_workspace_bytes", 3)
+        self.epi_ws = torch.empty(ebytes, dtype=torch.uint8, device=device)
         B, N, H, Q = shape.B, shape.N, shape.H, shape.Q
         self.o = torch.empty(B, N, H, o_width(self.s), dtype=torch.float32, device=device)
         self.lse = torch.empty(B, H, N, dtype=torch.float32, device=device)
@@ -307,6 +319,7 @@ class FlashIPA:
         tests: whatever a kernel fails to write, or reads before it is
         written, then shows up)."""
         self.lifted.fill_(255)
+        self.epi_ws.fill_(255)
         for buf in (self.o, self.lse, self.update, self.local_points):
             buf.fill_(float("nan"))
 
@@ -317,7 +330,7 @@ class FlashIPA:
         ipa_flash_fwd(self.s, self.lifted, self.o, self.lse, stream)
 
     def epilogue(self, t: dict, stream=None):
-        ipa_epilogue(self.s, self.lifted, self.o, self.lse, t, self.update, self.local_points, stream)
+        ipa_epilogue(self.s, self.epi_ws, self.o, self.lse, t, self.update, self.local_points, stream)
 
     def forward(self, t: dict, stream=None):
         self.lift(t, stream)

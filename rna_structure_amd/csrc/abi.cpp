@@ -84,21 +84,30 @@ ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float
                               : fipa::launch_flash_f32(L, lifted, o, lse, hs));
 }
 
-ipa_status ipa_epilogue(const ipa_shape* s, void* lifted, const float* o, const float* lse, const ipa_epi_in* in,
-                        float* update, float* local_points, void* stream) {
-  if (!s || !lifted || !o || !lse || !in || !update || !local_points) return IPA_ERR_NULL;
+size_t ipa_epilogue_workspace_bytes(const ipa_shape* s) {
+  Layout L;
+  if (shape_status(s, 0, &L) != IPA_OK || !fipa::epilogue_supported(L)) return 0;
+  return L.epi_ws > 0 ? L.epi_ws : 16;
+}
+
+ipa_status ipa_epilogue(const ipa_shape* s, void* workspace, size_t workspace_bytes, const float* o, const float* lse,
+                        const ipa_epi_in* in, float* update, float* local_points, void* stream) {
+  if (!s || !o || !lse || !in || !update || !local_points) return IPA_ERR_NULL;
   Layout L;
   ipa_status st = shape_status(s, 0, &L);
   if (st != IPA_OK) return st;
   const void* req[] = {in->zl, in->rotation, in->translation, in->w_out, in->b_out};
   for (const void* p : req)
     if (!p) return IPA_ERR_NULL;
+  if (L.epi_ws > 0 && !workspace) return IPA_ERR_NULL;
   for (const void* p : req)
     if (!aligned16(p)) return IPA_ERR_ALIGN;
-  if (!aligned16(lifted) || !aligned16(o) || !aligned16(lse) || !aligned16(update) || !aligned16(local_points))
+  if ((workspace && !aligned16(workspace)) || !aligned16(o) || !aligned16(lse) || !aligned16(update) ||
+      !aligned16(local_points))
     return IPA_ERR_ALIGN;
   if (!fipa::epilogue_supported(L)) return IPA_ERR_UNSUPPORTED;
-  return launch_status(fipa::launch_epilogue(L, lifted, o, lse, in, s->eps, update, local_points,
+  if (workspace_bytes < L.epi_ws) return IPA_ERR_SHAPE;
+  return launch_status(fipa::launch_epilogue(L, workspace, o, lse, in, s->eps, update, local_points,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 

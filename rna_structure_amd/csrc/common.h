@@ -80,7 +80,8 @@ struct Layout {
   int F, FP;  // epilogue feature count, padded to 16
   int KS;     // matrix-core path: key ranges the fused kernel splits a query tile over
   int PREC;   // floats per partial-result record (KS > 1): DO values + 4 statistics, padded to 4
-  size_t off_ql, off_qa, off_kt, off_vt, off_ck, off_gam, off_km, off_wt, off_part, off_pm, total;
+  size_t off_ql, off_qa, off_kt, off_vt, off_ck, off_gam, off_km, off_part, off_pm, total;
+  size_t epi_ws;  // bytes of the epilogue's own workspace (packed w_out)
 };
 
 // Key ranges per query tile of the fused kernel: when (b, h, 256-query tile)
@@ -184,13 +185,6 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
   off = align256(off + H * 4);
   L->off_km = off;
   off = align256(off + B * NT * 2 * 4);
-  // output projection transposed to [Cout][FP] bf16, or per head to
-  // [H][Cout][kHeadFeatPitch] bf16 (matrix-core path)
-  L->off_wt = off;
-  if (L->mfma) {
-    const size_t a1 = (size_t)L->Cout * L->FP, a2 = (size_t)L->H * L->Cout * kHeadFeatPitch;
-    off = align256(off + (a1 > a2 ? a1 : a2) * 2);
-  }
   // partial results of the key ranges: [KS][B][H][NQpad][PREC] fp32 (before
   // the pair-mask region, whose presence does not move it)
   L->PREC = round_up(L->DO + 4, 4);
@@ -199,6 +193,13 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
   L->off_pm = off;
   if (with_pm) off = align256(off + B * NQ * NT * 2 * 4);
   L->total = off;
+  // the epilogue's workspace (separate from the lifted rows): the output
+  // projection transposed to [Cout][FP] bf16, or per head to
+  // [H][Cout][kHeadFeatPitch] bf16 (matrix-core path); none on the fp32 path
+  {
+    const size_t a1 = (size_t)L->Cout * L->FP, a2 = (size_t)L->H * L->Cout * kHeadFeatPitch;
+    L->epi_ws = L->mfma ? align256((a1 > a2 ? a1 : a2) * 2) : 0;
+  }
   return true;
 }
 

@@ -659,7 +659,7 @@ hipError_t launch_epilogue(const Layout& L, void* ws, const float* o, const floa
   a.wt = nullptr;
   const int total = L.B * L.N;
   if (head_path(L)) {
-    uint16_t* wh = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.off_wt);
+    uint16_t* wh = reinterpret_cast<uint16_t*>(ws);
     const long n = (long)L.H * L.Cout * kHeadFeatPitch;
     hipLaunchKernelGGL(pack_wout_heads_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(in->w_out), wh, L.H, L.Cout);
@@ -679,7 +679,7 @@ hipError_t launch_epilogue(const Layout& L, void* ws, const float* o, const floa
       }
     }
   } else if (L.mfma) {
-    uint16_t* wt = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.off_wt);
+    uint16_t* wt = reinterpret_cast<uint16_t*>(ws);
     hipLaunchKernelGGL(transpose_wout_kernel, dim3((L.FP + 63) / 64, (L.Cout + 63) / 64), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(in->w_out), wt, L.F, L.FP, L.Cout);
     a.wt = wt;

@@ -76,6 +76,13 @@ __device__ __forceinline__ int next_valid_tile(const uint32_t* kmb, int t, int N
   return __builtin_amdgcn_readfirstlane(t);
 }
 
+// Key/value tile buffers of an instance.
+// (Three buffers with the copies two tiles ahead, where they fit in the 160
+// KiB of LDS, measured no faster than two at N = 16384: the copies land
+// within one tile.  The loop keeps both forms.)
+template <int NQS, int NVB, int GS>
+constexpr int kv_buffers() { return 2; }
+
 // Key and value tile t of one (batch, head) into LDS buffer buf.
 template <int NQS, int NVB, int GS, int W>
 __device__ __forceinline__ void copy_kv_tile(const char* ktg0, const char* vtg0, char* sk0, char* sv0, int t, int buf,
@@ -109,12 +116,13 @@ __device__ __forceinline__ float exp_tile(float* s, f16x8_t* ph) {
 // O^T += V~^T P^T over one 64-key value tile in LDS: 4 K-steps x (NVB + 1)
 // value blocks, consecutive MFMAs on different blocks (independent), value
 // fragments fetched DEPTH MFMAs ahead of their use so that the LDS latency
-// hides behind the preceding MFMAs.
-template <int NVB>
-__device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* pc, f32x16_t* oacc) {
+// hides behind the preceding MFMAs.  pv_tile_ops emits the reads and MFMAs,
+// pv_tile_sched their order (with up to VPER vector-ALU instructions of other
+// work after each MFMA).
+template <int NVB, int DEPTH>
+__device__ __forceinline__ void pv_tile_ops(const char* vrow, const f16x8_t* pc, f32x16_t* oacc) {
   constexpr int NB = NVB + 1;
   constexpr int NS = 4 * NB;
-  constexpr int DEPTH = 4;
   auto off = [](int st) { return (size_t)((st % NB) * 32 * kVCols) * 2 + (st / NB) * 32; };
   uint4 f[DEPTH];
 #pragma unroll
@@ -126,12 +134,23 @@ __device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* pc, f32
     oacc[st % NB] =
         __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c), pc[st / NB], oacc[st % NB], 0, 0, 0);
   }
+}
+
+template <int NS, int DEPTH, int VPER>
+__device__ __forceinline__ void pv_tile_sched() {
   __builtin_amdgcn_sched_group_barrier(0x100, DEPTH, 0);
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (st + DEPTH < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (VPER > 0) __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
   }
+}
+
+template <int NVB>
+__device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* pc, f32x16_t* oacc) {
+  pv_tile_ops<NVB, 4>(vrow, pc, oacc);
+  pv_tile_sched<4 * (NVB + 1), 4, 0>();
 }
 
 // First half of the online softmax of one tile for the 32 queries of a
@@ -205,19 +224,17 @@ __device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, 
   }
 }
 
-// Main loop over the key tiles [t, tend) of key range sp and the final
-// normalisation (or, with several key ranges, the partial result) for one
-// wavefront's 32 queries.  The copy of the first tile t (into buffer 0) was
-// issued by the caller.  Key/value tiles alternate between two LDS buffers:
-// at the top of tile t the copies of t (issued one tile earlier) are waited
-// for, one barrier makes them visible and frees the other buffer, and the
-// copies of the next tile go out before the products of t start.  PM selects
-// the per-query pair-mask words (a vector load per tile); without a pair mask
-// the key mask is inside the key product.
-template <int NQS, int NVB, int GS, int W, bool PM>
-__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* sv0, int t, int tend, int sp, int b,
-                                       int h, int i, bool qin, bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
-                                       const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
+// Final normalisation (or, with several key ranges, the partial result) of
+// one block of 32 queries i - l32 .. i - l32 + 31 after its last key tile:
+// log-sum-exp, O divided by the ones-row sums, the centroid added back to the
+// value points, written through an LDS slot of the (then free) tile buffers.
+// `w` names the slot (0 .. W-1): W/2 slots in each of the two buffer arrays.
+// Every wavefront of the workgroup calls it the same number of times (it
+// contains a barrier).
+template <int NQS, int NVB, int GS, int W>
+__device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* sk0, char* sv0, int sp, int b, int h, int i,
+                                            bool qin, bool qvalid, int w, int lane, int l32, int half,
+                                            const f32x16_t* oacc, float m, float l, bool init) {
   constexpr int QW = 16 * NQS;
   constexpr int KROW = QW + 16 * GS + kRowPad;
   constexpr int KT_BYTES = 64 * KROW * 2;
@@ -226,62 +243,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   constexpr int KT_LDS = (KT_BYTES + 1023) / 1024 * 1024;
   constexpr int VT_LDS = (VT_BYTES + 1023) / 1024 * 1024;
   const Layout& L = a.L;
-  const int N = L.N, H = L.H, NT = L.NT;
-  const uint32_t* km = reinterpret_cast<const uint32_t*>(a.ws + L.off_km);
-  const float4* ck = reinterpret_cast<const float4*>(a.ws + L.off_ck);
-  f32x16_t oacc[NVB + 1];
-#pragma unroll
-  for (int vb = 0; vb <= NVB; ++vb) oacc[vb] = f32x16_t{};
-  float m = 0.f, l = 0.f;
-  bool init = false;
-
-  const char* ktg0 = a.ws + kt_tile_off(L, b, h, 0);
-  const char* vtg0 = a.ws + vt_tile_off(L, b, h, 0);
-  const uint32_t* kmb = km + (size_t)b * NT * 2;
-  int buf = 0;
-  // a wavefront without a valid query keeps copying tiles and meeting the
-  // barriers, but does no products
-  const bool active = __any(qvalid);
-  while (t < tend) {
-    const int tn = next_valid_tile(kmb, t, tend);
-    uint32_t mw = 0xFFFFFFFFu;
-    if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
-    geo_tile<GS>(qg, ld_uniform4(ck + (size_t)b * NT + t), gl, Pf, m, half, bg);
-    // tile t in LDS buffer buf; every wave is done with tile t-1 (buffer buf^1)
-    wait_vmcnt<0>();
-    __syncthreads();
-    if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
-    if (tn < tend) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, tn, buf ^ 1, w, lane);
-    const char* sk = sk0 + buf * KT_LDS;
-    const char* sv = sv0 + buf * VT_LDS;
-    if (!active) {
-      buf ^= 1;
-      t = tn;
-      continue;
-    }
-
-    f32x16_t sacc[2];
-    __builtin_amdgcn_s_setprio(1);
-    s_tile<NQS, GS>(sk, bq, bg, l32, half, sacc);
-    __builtin_amdgcn_s_setprio(0);
-
-    float s32[32];
-    const float alpha = softmax_max<PM>(sacc, mw, m, init, s32);
-    f16x8_t ph[4];
-    const float ps = exp_tile(s32, ph);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int vb = 0; vb <= NVB; ++vb) oacc[vb] *= alpha;
-    }
-    l = l * alpha + ps;
-
-    __builtin_amdgcn_s_setprio(1);
-    pv_tile<NVB>(sv + (size_t)(l32 * kVCols) * 2 + half * 16, ph, oacc);
-    __builtin_amdgcn_s_setprio(0);
-    buf ^= 1;
-    t = tn;
-  }
-  // ---- finalise
+  const int N = L.N, H = L.H;
   const float ltot = l + __shfl_xor(l, 32);
   const bool nonempty = qvalid && init && ltot > 0.f;
   const bool partial = a.ks > 1;
@@ -393,6 +355,131 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   }
 }
 
+// Main loop over the key tiles [t, tend) of key range sp and the final
+// normalisation (or, with several key ranges, the partial result) for one
+// wavefront's 32 queries.  The copy of the first tile t (into buffer 0) was
+// issued by the caller.  Key/value tiles alternate between two LDS buffers:
+// at the top of tile t the copies of t (issued one tile earlier) are waited
+// for, one barrier makes them visible and frees the other buffer, and the
+// copies of the next tile go out before the products of t start.  PM selects
+// the per-query pair-mask words (a vector load per tile); without a pair mask
+// the key mask is inside the key product.
+// One key tile t of the main loop, held in LDS buffer BUF of NBUF (a
+// compile-time index, so that every LDS offset is a constant): the point
+// operand with the current running maximum, the barrier that makes tile t
+// visible and frees the previous tile's buffer, the copies of the tile
+// NBUF - 1 ahead into that buffer, and the products and softmax of tile t.
+// Returns the next tile with a valid key (tend if none).
+template <int NQS, int NVB, int GS, int W, bool PM, int NBUF, int BUF>
+__device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const char* ktg0, const char* vtg0, char* sk0,
+                                           char* sv0, const uint32_t* kmb, const float4* ckb, int t, int tend, int b,
+                                           int i, bool qin, bool qvalid, bool active, int w, int lane, int l32,
+                                           int half, float gl, float Pf, const bf16x8_t* bq, f16x8_t* bg,
+                                           const QueryGeo& qg, f32x16_t* oacc, float& m, float& l, bool& init) {
+  constexpr int QW = 16 * NQS;
+  constexpr int KROW = QW + 16 * GS + kRowPad;
+  constexpr int KT_BYTES = 64 * KROW * 2;
+  constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
+  constexpr int KT_LDS = (KT_BYTES + 1023) / 1024 * 1024;
+  constexpr int VT_LDS = (VT_BYTES + 1023) / 1024 * 1024;
+  constexpr int DPW = dma_per_wave<KT_BYTES, W>() + dma_per_wave<VT_BYTES, W>();
+  constexpr int PREV = (BUF + NBUF - 1) % NBUF;  // the buffer the copies refill
+  const Layout& L = a.L;
+  const int tn = next_valid_tile(kmb, t, tend);
+  uint32_t mw = 0xFFFFFFFFu;
+  if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
+  geo_tile<GS>(qg, ld_uniform4(ckb + t), gl, Pf, m, half, bg);
+  // tile t has landed (the copies of the next tile, with three buffers, may
+  // still be in flight); every wave is done with the previous tile
+  if constexpr (NBUF == 3) {
+    if (tn < tend) wait_vmcnt<DPW>();
+    else wait_vmcnt<0>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
+  {
+    const int tc = NBUF == 3 ? (tn < tend ? next_valid_tile(kmb, tn, tend) : tend) : tn;
+    if (tc < tend) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, tc, PREV, w, lane);
+  }
+  if (!active) return tn;
+  const char* sk = sk0 + BUF * KT_LDS;
+  const char* sv = sv0 + BUF * VT_LDS;
+  f32x16_t sacc[2];
+  __builtin_amdgcn_s_setprio(1);
+  s_tile<NQS, GS>(sk, bq, bg, l32, half, sacc);
+  __builtin_amdgcn_s_setprio(0);
+
+  float s32[32];
+  const float alpha = softmax_max<PM>(sacc, mw, m, init, s32);
+  f16x8_t ph[4];
+  const float ps = exp_tile(s32, ph);
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int vb = 0; vb <= NVB; ++vb) oacc[vb] *= alpha;
+  }
+  l = l * alpha + ps;
+
+  __builtin_amdgcn_s_setprio(1);
+  pv_tile<NVB>(sv + (size_t)(l32 * kVCols) * 2 + half * 16, ph, oacc);
+  __builtin_amdgcn_s_setprio(0);
+  return tn;
+}
+
+// Main loop over the key tiles [t, tend) of key range sp and the final
+// normalisation (or, with several key ranges, the partial result) for one
+// wavefront's 32 queries.  The copy of the first tile t (into buffer 0) was
+// issued by the caller.  Key/value tiles rotate through NBUF buffers and the
+// copies of a tile go out NBUF - 1 tiles before its turn: three buffers
+// where they fit in LDS and without a pair mask (whose words are vector loads
+// that the compiler would wait for with the copies still in flight), else
+// two.  The loop is unrolled by NBUF so that buffer offsets are constants.
+// PM selects the per-query pair-mask words (a vector load per tile); without
+// a pair mask the key mask is inside the key product.
+template <int NQS, int NVB, int GS, int W, bool PM>
+__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* sv0, int t, int tend, int sp, int b,
+                                       int h, int i, bool qin, bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
+                                       const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
+  const Layout& L = a.L;
+  const int NT = L.NT;
+  const float4* ckb = reinterpret_cast<const float4*>(a.ws + L.off_ck) + (size_t)b * NT;
+  const uint32_t* kmb = reinterpret_cast<const uint32_t*>(a.ws + L.off_km) + (size_t)b * NT * 2;
+  const char* ktg0 = a.ws + kt_tile_off(L, b, h, 0);
+  const char* vtg0 = a.ws + vt_tile_off(L, b, h, 0);
+  f32x16_t oacc[NVB + 1];
+#pragma unroll
+  for (int vb = 0; vb <= NVB; ++vb) oacc[vb] = f32x16_t{};
+  float m = 0.f, l = 0.f;
+  bool init = false;
+  // a wavefront without a valid query keeps copying tiles and meeting the
+  // barriers, but does no products
+  const bool active = __any(qvalid);
+  constexpr int NBUF = (!PM && kv_buffers<NQS, NVB, GS>() == 3) ? 3 : 2;
+#define FIPA_TILE(BUFI)                                                                                             \
+  attend_tile<NQS, NVB, GS, W, PM, NBUF, BUFI>(a, ktg0, vtg0, sk0, sv0, kmb, ckb, t, tend, b, i, qin, qvalid, active, \
+                                               w, lane, l32, half, gl, Pf, bq, bg, qg, oacc, m, l, init)
+  if constexpr (NBUF == 3) {
+    const int t1 = next_valid_tile(kmb, t, tend);
+    if (t1 < tend) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, t1, 1, w, lane);
+    while (t < tend) {
+      t = FIPA_TILE(0);
+      if (t >= tend) break;
+      t = FIPA_TILE(1);
+      if (t >= tend) break;
+      t = FIPA_TILE(2);
+    }
+  } else {
+    while (t < tend) {
+      t = FIPA_TILE(0);
+      if (t >= tend) break;
+      t = FIPA_TILE(1);
+    }
+  }
+#undef FIPA_TILE
+  finish_rows<NQS, NVB, GS, W>(a, sk0, sv0, sp, b, h, i, qin, qvalid, w, lane, l32, half, oacc, m, l, init);
+}
+
 template <int NQS, int NVB, int GS, int W>
 __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   constexpr int QW = 16 * NQS;
@@ -401,8 +488,9 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
   // two buffers each, rounded up to whole KiB: the last copy chunk of a
   // tile may be partial and its upper lanes then land in this padding
-  __shared__ __attribute__((aligned(1024))) char sk[2 * ((KT_BYTES + 1023) / 1024 * 1024)];
-  __shared__ __attribute__((aligned(1024))) char sv[2 * ((VT_BYTES + 1023) / 1024 * 1024)];
+  // (three buffers each where they fit, see attend)
+  __shared__ __attribute__((aligned(1024))) char sk[kv_buffers<NQS, NVB, GS>() * ((KT_BYTES + 1023) / 1024 * 1024)];
+  __shared__ __attribute__((aligned(1024))) char sv[kv_buffers<NQS, NVB, GS>() * ((VT_BYTES + 1023) / 1024 * 1024)];
 
   const Layout& L = a.L;
   const int N = L.N, H = L.H;

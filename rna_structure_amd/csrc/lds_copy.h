@@ -50,15 +50,29 @@ __device__ __forceinline__ void dma_tile(const char* g, const char* s, int w, in
   const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ga);
   const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
   g = (const char*)(uintptr_t)join_addr(ghi, glo);
+  if constexpr (BYTES % 1024 == 0) {
+    // whole chunks: no lane is clamped, so one lane offset (16 l) serves
+    // every chunk and the chunk offset goes into the scalar address
+    const uint32_t voff = dma_src_off(BYTES, 0, lane);
 #pragma unroll
-  for (int k = 0; k < dma_per_wave<BYTES, W>(); ++k) {
-    const int ch = dma_chunk(BYTES, W, w, k);
-    const uint32_t voff = dma_src_off(BYTES, ch, lane);
-    // the instruction writes lane l's 16 bytes to M0 + 16 l, i.e. at
-    // dma_dst_off(ch, l) within the buffer
-    const uint32_t m0 = lbase + dma_dst_off(ch, 0);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(g), "s"(m0)
-                 : "memory", "m0");
+    for (int k = 0; k < dma_per_wave<BYTES, W>(); ++k) {
+      const int ch = dma_chunk(BYTES, W, w, k);
+      const char* gc = g + (size_t)dma_dst_off(ch, 0);
+      const uint32_t m0 = lbase + dma_dst_off(ch, 0);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gc), "s"(m0)
+                   : "memory", "m0");
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < dma_per_wave<BYTES, W>(); ++k) {
+      const int ch = dma_chunk(BYTES, W, w, k);
+      const uint32_t voff = dma_src_off(BYTES, ch, lane);
+      // the instruction writes lane l's 16 bytes to M0 + 16 l, i.e. at
+      // dma_dst_off(ch, l) within the buffer
+      const uint32_t m0 = lbase + dma_dst_off(ch, 0);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(g), "s"(m0)
+                   : "memory", "m0");
+    }
   }
 }
 

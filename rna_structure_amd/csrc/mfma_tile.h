@@ -159,14 +159,15 @@ __device__ __forceinline__ void geo_tile(const QueryGeo& qg, float4 ct, float gl
 // ktile points at 64 rows of KROW 16-bit elements (LDS or global memory).
 // The two key blocks are interleaved so consecutive MFMAs are independent,
 // and the operand fragments are fetched DEPTH K-steps ahead of their MFMA so
-// that the reads' latency hides behind the preceding MFMAs.
-template <int NQS, int GS>
-__device__ __forceinline__ void s_tile(const char* ktile, const bf16x8_t* bq, const f16x8_t* bg, int l32, int half,
-                                       f32x16_t* sacc) {
+// that the reads' latency hides behind the preceding MFMAs.  s_tile_ops
+// emits the reads and MFMAs only; the caller orders them (s_tile_sched), so
+// that other work can be placed between them.
+template <int NQS, int GS, int DEPTH>
+__device__ __forceinline__ void s_tile_ops(const char* ktile, const bf16x8_t* bq, const f16x8_t* bg, int l32, int half,
+                                           f32x16_t* sacc) {
   constexpr int QW = 16 * NQS;
   constexpr int KROW = QW + 16 * GS + kRowPad;
   constexpr int NS = NQS + GS;
-  constexpr int DEPTH = 3;
   const char* k0 = ktile + (size_t)(l32 * KROW) * 2 + half * 16;
   const char* k1 = k0 + (size_t)(32 * KROW) * 2;
   auto off = [](int st) { return st < NQS ? st * 32 : (QW + (st - NQS) * 16) * 2; };
@@ -193,14 +194,27 @@ __device__ __forceinline__ void s_tile(const char* ktile, const bf16x8_t* bq, co
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c1), bg[st - NQS], sacc[1], 0, 0, 0);
     }
   }
-  // keep the fetch-ahead order through scheduling: the first DEPTH steps'
-  // reads, then per step two MFMAs followed by the reads DEPTH steps ahead
+}
+
+// Instruction order for s_tile_ops: the first DEPTH steps' reads, then per
+// step its two MFMAs, the reads DEPTH steps ahead and up to VPER vector-ALU
+// instructions of independent work placed in the same region.
+template <int NS, int DEPTH, int VPER>
+__device__ __forceinline__ void s_tile_sched() {
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * DEPTH, 0);
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     if (st + DEPTH < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (VPER > 0) __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
   }
+}
+
+template <int NQS, int GS, int DEPTH = 3>
+__device__ __forceinline__ void s_tile(const char* ktile, const bf16x8_t* bq, const f16x8_t* bg, int l32, int half,
+                                       f32x16_t* sacc) {
+  s_tile_ops<NQS, GS, DEPTH>(ktile, bq, bg, l32, half, sacc);
+  s_tile_sched<NQS + GS, DEPTH, 0>();
 }
 
 // Permitted-key word of a lane for key tile t (bit kb*16 + r <-> key

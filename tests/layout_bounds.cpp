@@ -17,7 +17,8 @@
 //     that the lift writes or the fused kernel reads (key and value tiles,
 //     query rows and points, centroids, mask words, partial results, pair
 //     mask words) ends inside its region; the tile sizes the fused kernel
-//     compiles in equal the layout's; key ranges hold at least one tile each;
+//     compiles in equal the layout's; the epilogue's workspace holds the
+//     packed output projection; key ranges hold at least one tile each;
 //     the workgroup remap of the fused kernel is a permutation.
 // Prints "layout bounds: N checks ok" and exits 0, or names the first
 // failure and exits 1.
@@ -149,8 +150,7 @@ static void check_layout(const ipa_shape& s, int with_pm) {
   const Region reg[] = {
       {"QL", L.off_ql, L.off_qa}, {"QA", L.off_qa, L.off_kt},   {"KT", L.off_kt, L.off_vt},
       {"VT", L.off_vt, L.off_ck}, {"CK", L.off_ck, L.off_gam},  {"GAM", L.off_gam, L.off_km},
-      {"KM", L.off_km, L.off_wt}, {"WT", L.off_wt, L.off_part}, {"PART", L.off_part, L.off_pm},
-      {"PM", L.off_pm, L.total}};
+      {"KM", L.off_km, L.off_part}, {"PART", L.off_part, L.off_pm}, {"PM", L.off_pm, L.total}};
   CHECK(L.off_ql >= sizeof(Header), "%s: header", tag);
   for (const Region& r : reg) CHECK(r.start <= r.end && r.start % 256 == 0, "%s: region %s", tag, r.name);
   auto inside = [&](const Region& r, size_t off, size_t bytes, const char* what) {
@@ -179,7 +179,7 @@ static void check_layout(const ipa_shape& s, int with_pm) {
       for (int hf = 0; hf < 2; ++hf) inside(reg[6], km_word_off(L, b, t, hf), 4, "key-mask word");
       if (with_pm)
         for (int i : {0, L.NQpad - 1})
-          for (int hf = 0; hf < 2; ++hf) inside(reg[9], pm_word_off(L, b, i, t, hf), 4, "pair-mask word");
+          for (int hf = 0; hf < 2; ++hf) inside(reg[8], pm_word_off(L, b, i, t, hf), 4, "pair-mask word");
     }
   inside(reg[5], L.off_gam, (size_t)H * 4, "point weights");
   if (L.mfma) {
@@ -187,9 +187,10 @@ static void check_layout(const ipa_shape& s, int with_pm) {
     const size_t KT_BYTES = 64 * (size_t)(16 * L.NQS + 16 * L.GS + kRowPad) * 2;
     const size_t VT_BYTES = 32 * (size_t)(L.NVB + 1) * kVCols * 2;
     CHECK(ktb == KT_BYTES && vtb == VT_BYTES, "%s: tile bytes %zu %zu vs %zu %zu", tag, ktb, vtb, KT_BYTES, VT_BYTES);
-    // packed w_out of the epilogue (per head or transposed)
+    // packed w_out of the epilogue (per head or transposed), in the
+    // epilogue's own workspace
     const size_t wt = (size_t)L.H * L.Cout * kHeadFeatPitch * 2, wt2 = (size_t)L.Cout * L.FP * 2;
-    inside(reg[7], L.off_wt, wt > wt2 ? wt : wt2, "packed w_out");
+    CHECK(L.epi_ws >= (wt > wt2 ? wt : wt2), "%s: epilogue workspace %zu", tag, L.epi_ws);
     // key ranges of the fused kernel: [NT s / KS, NT (s + 1) / KS), each nonempty
     CHECK(L.KS >= 1 && L.KS <= 4, "%s: KS %d", tag, L.KS);
     for (int sp = 0; sp < L.KS; ++sp) {
@@ -198,7 +199,7 @@ static void check_layout(const ipa_shape& s, int with_pm) {
     }
     if (L.KS > 1)
       for (int i : {0, L.NQpad - 1})
-        inside(reg[8], part_rec_off(L, L.KS - 1, B - 1, H - 1, i), (size_t)L.PREC * 4, "partial record");
+        inside(reg[7], part_rec_off(L, L.KS - 1, B - 1, H - 1, i), (size_t)L.PREC * 4, "partial record");
     CHECK(L.PREC >= L.DO + 4 && L.PREC % 4 == 0, "%s: PREC", tag);
     // workgroup remap of the fused kernel (8 or 4 wavefronts per workgroup)
     for (int W : {4, 8}) {

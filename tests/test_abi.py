@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert lib.ipa_version().startswith(b"flashipa")
     for code in range(7):
-        assert lib.ipa_status_string(code)
+        assert lib.ipa_status_string(code) != b"unknown status"
     assert lib.ipa_status_string(99) == b"unknown status"
 
 
@@ -111,15 +111,25 @@ def test_validation_before_launch(lib):
     assert lib.ipa_flash_fwd(ctypes.byref(s), None, 4096, 4096, None) == 1
     assert lib.ipa_flash_fwd(ctypes.byref(s), 4096, 4100, 4096, None) == 4
     ei = _lib.IpaEpiIn(4096, 4096, 4096, 4096, None)
-    assert lib.ipa_epilogue(ctypes.byref(s), 4096, 4096, 4096, ctypes.byref(ei), 4096, 4096, None) == 1
+    assert lib.ipa_epilogue(ctypes.byref(s), 4096, 1 << 30, 4096, 4096, ctypes.byref(ei), 4096, 4096, None) == 1
     ei2 = _lib.IpaEpiIn(4096, 4096, 4096, 4096, 4096)
-    assert lib.ipa_epilogue(ctypes.byref(s), None, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 1
-    assert lib.ipa_epilogue(ctypes.byref(s), 4096, 4096, 4100, ctypes.byref(ei2), 4096, 4096, None) == 4
+    # the bf16 path needs the epilogue workspace (packed w_out)
+    assert lib.ipa_epilogue(ctypes.byref(s), None, 1 << 30, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 1
+    assert lib.ipa_epilogue(ctypes.byref(s), 4096, 1 << 30, None, 4096, ctypes.byref(ei2), 4096, 4096, None) == 1
+    assert lib.ipa_epilogue(ctypes.byref(s), 4096, 1 << 30, 4100, 4096, ctypes.byref(ei2), 4096, 4096, None) == 4
+    assert lib.ipa_epilogue(ctypes.byref(s), 4104, 1 << 30, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 4
+    need = lib.ipa_epilogue_workspace_bytes(ctypes.byref(s))
+    assert need >= 8 * 128 * 120 * 2        # per-head packed w_out at H=8, Cout=128
+    assert lib.ipa_epilogue(ctypes.byref(s), 4096, need - 1, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 2
     # F = 40*(16+32+56) = 4160 with non-standard dimensions: beyond the LDS
     # staging of the general epilogue (the per-head path takes any H, but only
     # Dv=16, Q=8, Cz=64, R=2)
     big = _shape(H=40, Cz=56)
-    assert lib.ipa_epilogue(ctypes.byref(big), 4096, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 3
+    assert lib.ipa_epilogue_workspace_bytes(ctypes.byref(big)) == 0
+    assert lib.ipa_epilogue(ctypes.byref(big), 4096, 1 << 30, 4096, 4096, ctypes.byref(ei2), 4096, 4096, None) == 3
+    # the fp32 path packs nothing: no workspace needed
+    f32 = _shape(dtype="f32", N=100, H=4)
+    assert lib.ipa_epilogue_workspace_bytes(ctypes.byref(f32)) == 16
     assert lib.ipa_logit_rows(ctypes.byref(s), 4096, 5, 0, 0, 1, 4096, None) == 2   # b out of range
     assert lib.ipa_logit_rows(ctypes.byref(s), 4096, 0, 0, 299, 2, 4096, None) == 2  # rows past N
 
@@ -225,3 +235,4 @@ def test_bias_attention_validation_before_launch(lib):
     for name in ("q", "k", "v", "pq", "pk", "o", "lse", "w"):
         assert call(bs(), **{name: 4100}) == 4, name
     assert call(bs(), km=4097) == 4
+
