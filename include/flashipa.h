@@ -54,7 +54,8 @@ typedef enum {
   IPA_ERR_UNSUPPORTED = 3, /* dims beyond the compiled kernel limits, or unknown dtype */
   IPA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   IPA_ERR_LAUNCH = 5,      /* a kernel launch failed (hipGetLastError) */
-  IPA_ERR_DEVICE = 6       /* HIP runtime / device query failed */
+  IPA_ERR_DEVICE = 6,      /* HIP runtime / device query failed */
+  IPA_ERR_SCRATCH = 7      /* ipa_forward_noalloc: the shape needs more than its static scratch */
 } ipa_status;
 
 typedef enum { IPA_F32 = 0, IPA_BF16 = 1 } ipa_dtype;
@@ -183,6 +184,26 @@ size_t ipa_epilogue_workspace_bytes(const ipa_shape* s);
  * the workspace is too small. */
 ipa_status ipa_epilogue(const ipa_shape* s, void* workspace, size_t workspace_bytes, const float* o, const float* lse,
                         const ipa_epi_in* in, float* update, float* local_points, void* stream);
+
+/* The whole forward (ipa_lift, ipa_flash_fwd, ipa_epilogue) in one call
+ * that allocates nothing, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Inputs and outputs as for the three calls (in, epi, update
+ * [B,N,Cout] fp32, local_points [B,N,H,Q,3] fp32); every other buffer (the
+ * lifted rows, o, lse, the packed output projection) lives in a static
+ * device array of 128 MiB per GPU, held from the library's first use on that
+ * GPU until the process ends.  The shape must fit in it:
+ *   align256(ipa_lifted_bytes(s, pm)) + align256(4 B N H ipa_o_width(s))
+ *     + align256(4 B H N) + ipa_epilogue_workspace_bytes(s) <= 128 MiB
+ * (B=8, N=256: 29 MiB; B=1, N=2048: 72 MiB, at H=8 and the standard
+ * widths), else
+ * IPA_ERR_SCRATCH before anything is enqueued.  Results are those of the
+ * three calls.  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other host threads) race.  Other errors
+ * as for the three calls; IPA_ERR_DEVICE if the array's device address
+ * cannot be found. */
+ipa_status ipa_forward_noalloc(const ipa_shape* s, const ipa_lift_in* in, const ipa_epi_in* epi, float* update,
+                               float* local_points, void* stream);
 
 /* Diagnostic (tests only): the logits the fused kernel uses, for query rows
  * row0 .. row0+nrows-1 of (b, h), recomputed from the lifted rows with the

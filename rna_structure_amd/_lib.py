@@ -18,11 +18,12 @@ LIB_PATH = os.environ.get("FLASHIPA_LIBRARY", os.path.join(HERE, "libflashipa.so
 
 IPA_F32, IPA_BF16 = 0, 1
 STATUS = {0: "IPA_OK", 1: "IPA_ERR_NULL", 2: "IPA_ERR_SHAPE", 3: "IPA_ERR_UNSUPPORTED",
-          4: "IPA_ERR_ALIGN", 5: "IPA_ERR_LAUNCH", 6: "IPA_ERR_DEVICE"}
+          4: "IPA_ERR_ALIGN", 5: "IPA_ERR_LAUNCH", 6: "IPA_ERR_DEVICE", 7: "IPA_ERR_SCRATCH"}
 EXPORTS = ("ipa_lifted_bytes", "ipa_o_width", "ipa_lift", "ipa_flash_fwd", "ipa_epilogue_workspace_bytes",
            "ipa_epilogue",
            "ipa_logit_rows", "ipa_backward_workspace_bytes", "ipa_backward", "ipa_knn_distogram",
-           "ipa_bias_workspace_bytes", "ipa_bias_attention", "ipa_status_string", "ipa_version")
+           "ipa_bias_workspace_bytes", "ipa_bias_attention", "ipa_forward_noalloc", "ipa_status_string",
+           "ipa_version")
 GRAD_KEYS = ("q", "k", "v", "q_points", "k_points", "v_points", "rotation", "translation",
              "point_weight_raw", "w_pair", "zl", "zr", "w_out", "b_out")
 
@@ -101,6 +102,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipa_bias_workspace_bytes.restype = sz
     lib.ipa_bias_attention.argtypes = [ctypes.POINTER(IpaBiasShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ipa_bias_attention.restype = ctypes.c_int
+    lib.ipa_forward_noalloc.argtypes = [sp, ctypes.POINTER(IpaLiftIn), ctypes.POINTER(IpaEpiIn), vp, vp, vp]
+    lib.ipa_forward_noalloc.restype = ctypes.c_int
     lib.ipa_status_string.argtypes = [ctypes.c_int]
     lib.ipa_status_string.restype = ctypes.c_char_p
     lib.ipa_version.argtypes = []
@@ -162,6 +165,16 @@ def ipa_epilogue(s: IpaShape, workspace, o, lse, t: dict, update, local_points, 
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("ipa_epilogue", load().ipa_epilogue(ctypes.byref(s), _ptr(workspace), nbytes, _ptr(o), _ptr(lse),
                                                ctypes.byref(ei), _ptr(update), _ptr(local_points), _stream(stream)))
+
+
+def ipa_forward_noalloc(s: IpaShape, t: dict, update, local_points, stream=None):
+    """The whole forward in one call that allocates nothing (static scratch)."""
+    li = IpaLiftIn(*[_ptr(t.get(n)) for n in ("q", "k", "v", "q_points", "k_points", "v_points", "rotation",
+                                              "translation", "point_weight_raw", "w_pair", "zl", "zr",
+                                              "mask", "pair_mask")])
+    ei = IpaEpiIn(*[_ptr(t[n]) for n in ("zl", "rotation", "translation", "w_out", "b_out")])
+    _check("ipa_forward_noalloc", load().ipa_forward_noalloc(ctypes.byref(s), ctypes.byref(li), ctypes.byref(ei),
+                                                             _ptr(update), _ptr(local_points), _stream(stream)))
 
 
 def ipa_logit_rows(s: IpaShape, lifted, b: int, h: int, row0: int, nrows: int, out, stream=None):

@@ -226,6 +226,7 @@ const char* ipa_status_string(int status) {
     case IPA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case IPA_ERR_LAUNCH: return "kernel launch failed";
     case IPA_ERR_DEVICE: return "HIP runtime error";
+    case IPA_ERR_SCRATCH: return "the shape needs more than the static scratch of ipa_forward_noalloc";
     default: return "unknown status";
   }
 }

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.ipa_version().startswith(b"flashipa")
-    for code in range(7):
+    for code in range(8):
         assert lib.ipa_status_string(code) != b"unknown status"
     assert lib.ipa_status_string(99) == b"unknown status"
 
@@ -236,3 +236,16 @@ def test_bias_attention_validation_before_launch(lib):
         assert call(bs(), **{name: 4100}) == 4, name
     assert call(bs(), km=4097) == 4
 
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """ipa_forward_noalloc checks the shape against its static 128 MiB before
+    any device call: N = 16384 (H = 8) needs ~280 MB."""
+    s = _shape(B=1, N=16384)
+    fields = [n for n, _ in _lib.IpaLiftIn._fields_ if n != "pair_mask"]
+    li = _lib.IpaLiftIn(**{n: 4096 for n in fields})
+    ei = _lib.IpaEpiIn(4096, 4096, 4096, 4096, 4096)
+    assert lib.ipa_forward_noalloc(ctypes.byref(s), ctypes.byref(li), ctypes.byref(ei), 4096, 4096, None) == 7
+    assert lib.ipa_forward_noalloc(ctypes.byref(s), ctypes.byref(li), ctypes.byref(ei), None, 4096, None) == 1
+    li.q = 4100
+    assert lib.ipa_forward_noalloc(ctypes.byref(_shape(B=1, N=100)), ctypes.byref(li), ctypes.byref(ei), 4096, 4096,
+                                   None) == 4
