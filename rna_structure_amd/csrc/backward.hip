@@ -19,7 +19,18 @@
 //   dKV_j = sum_i dS_ij QV_i,   dB_j = +2 gamma sum_i dS_ij (A_i - B_j)
 //   dVV_j = sum_i p_ij dO_i,    dgamma = -sum_ij dS_ij |A_i - B_j|^2
 // in two passes (one over keys per query, one over queries per key), after a
-// forward pass that yields O and the log-sum-exp.  Four lanes share a row:
+// forward pass that yields O and the log-sum-exp.
+// Precision: dO_i . VV_j - Dsum_i cancels, and for long chains the global
+// value points in VV and O are hundreds of angstroms from the origin, so in
+// fp32 the two products would carry absolute errors far above their
+// difference.  Every 32-residue block k of a sample therefore has a
+// reference point c_k (its first residue's translation rounded to whole
+// angstroms, so that differences of references are exact): VV_j holds its
+// points relative to c of j's block and O_i relative to c of i's block
+// (O'_i), and with S_i = sum_q dO_i of the point part (3 components)
+//   dO_i . VV_j - Dsum_i = dO_i . VV'_j - (Dsum'_i + S_i . (c_i - c_j))
+// where Dsum'_i = dO_i . O'_i.  All products then involve coordinates of the
+// size of a block or of the attention's reach.  Four lanes share a row:
 // each holds a quarter of the columns and the dot products are summed over
 // the quad with DPP.  The epilogue's backward and the weight gradients use a
 // tiled fp32 GEMM; a last pass maps the row gradients back to the inputs
@@ -40,7 +51,7 @@ struct BwLayout {
   int B, N, H, D, Dv, P, Q, Cz, R, Cout, F;
   int DK, DV, P3, NK4, NV4, DKp, DVp;
   int ksplit;
-  size_t off_gam, off_qv, off_kv, off_vv, off_qa, off_kb, off_o, off_lse, off_do, off_dd, off_feat, off_dfeat,
+  size_t off_gam, off_qv, off_kv, off_vv, off_qa, off_kb, off_o, off_lse, off_do, off_dd, off_ds, off_feat, off_dfeat,
       off_dqv, off_dqa, off_dgam, off_dkv, off_dkb, off_dvv, off_dzle, off_dre, off_dte, off_dwpart, off_ppart,
       total;
   int bf16;               // inputs are bf16: converted into fp32 copies first
@@ -71,6 +82,14 @@ __device__ __forceinline__ float quad_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
   return x;
+}
+
+// Reference point of the 32-residue block holding residue n of sample b: the
+// block's first translation rounded to whole angstroms (differences of two
+// references are exact in fp32).
+__device__ __forceinline__ float3 blk_ref(const BwArgs& a, int b, int n) {
+  const float* t = a.tr + ((size_t)b * a.L.N + (size_t)(n & ~31)) * 3;
+  return make_float3(rintf(t[0]), rintf(t[1]), rintf(t[2]));
 }
 
 __device__ __forceinline__ float softplusf(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
@@ -115,9 +134,14 @@ __global__ __launch_bounds__(256) void bw_prep_kernel(BwArgs a) {
   c = 0;
   for (int d = 0; d < L.Dv; ++d) vv[c++] = vrow[d];
   for (int e = 0; e < L.R * L.Cz; ++e) vv[c++] = zrr[e];
-  for (int qq = 0; qq < L.Q; ++qq) {
-    const float* x = a.vp + ((bn * L.H + h) * L.Q + qq) * 3;
-    for (int m = 0; m < 3; ++m) vv[c++] = R[m * 3 + 0] * x[0] + R[m * 3 + 1] * x[1] + R[m * 3 + 2] * x[2] + t[m];
+  {
+    // value points relative to the block reference (t - c first: exact)
+    const float3 cr = blk_ref(a, b, n);
+    const float tc[3] = {t[0] - cr.x, t[1] - cr.y, t[2] - cr.z};
+    for (int qq = 0; qq < L.Q; ++qq) {
+      const float* x = a.vp + ((bn * L.H + h) * L.Q + qq) * 3;
+      for (int m = 0; m < 3; ++m) vv[c++] = R[m * 3 + 0] * x[0] + R[m * 3 + 1] * x[1] + R[m * 3 + 2] * x[2] + tc[m];
+    }
   }
   for (; c < L.DVp; ++c) vv[c] = 0.f;
   for (int p = 0; p < 16; ++p) qa[p] = kb[p] = 0.f;
@@ -217,6 +241,9 @@ __global__ __launch_bounds__(4 * ROWS) void bw_fwd_kernel(BwArgs a) {
 #pragma unroll
   for (int u = 0; u < NV4; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   float m = -INFINITY, l = 0.f;
+  // sum_j p_ij (c_j - c_i): the key blocks' references relative to the query's
+  const float3 cq = blk_ref(a, b, ic);
+  float cx = 0.f, cy = 0.f, cz = 0.f;
   const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + ic) * L.N : nullptr;
   for (int j0 = 0; j0 < L.N; j0 += kBwTile) {
     __syncthreads();
@@ -241,6 +268,8 @@ __global__ __launch_bounds__(4 * ROWS) void bw_fwd_kernel(BwArgs a) {
     }
     __syncthreads();
     const int nj = min(kBwTile, L.N - j0);
+    const float3 ct = blk_ref(a, b, j0);
+    const float dcx = ct.x - cq.x, dcy = ct.y - cq.y, dcz = ct.z - cq.z;
     for (int jj = 0; jj < nj; ++jj) {
       float d2;
       const float lg = logit_q<NK4>(qv, &sK[jj][part * 4 * NK4], qa, &sB[jj][part * 4], gam, true, d2);
@@ -249,6 +278,9 @@ __global__ __launch_bounds__(4 * ROWS) void bw_fwd_kernel(BwArgs a) {
       if (lg > m) {
         const float c = expf(m - lg);
         l *= c;
+        cx *= c;
+        cy *= c;
+        cz *= c;
 #pragma unroll
         for (int u = 0; u < NV4; ++u) {
           o[u].x *= c;
@@ -260,18 +292,27 @@ __global__ __launch_bounds__(4 * ROWS) void bw_fwd_kernel(BwArgs a) {
       }
       const float p = expf(lg - m);
       l += p;
+      cx = fmaf(p, dcx, cx);
+      cy = fmaf(p, dcy, cy);
+      cz = fmaf(p, dcz, cz);
       axpy_quarter<NV4>(o, p, &sV[jj][0], part);
     }
   }
   if (!qin) return;
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.f / l;
+  // O' : the value points relative to the query's block reference
+  const int pbase = L.Dv + L.R * L.Cz, pend = pbase + 3 * L.Q;
+  const float cc[3] = {cx, cy, cz};
 #pragma unroll
   for (int u = 0; u < NV4; ++u) {
-    o[u].x *= inv;
-    o[u].y *= inv;
-    o[u].z *= inv;
-    o[u].w *= inv;
+    float* e4 = reinterpret_cast<float*>(&o[u]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int col = part * 4 * NV4 + 4 * u + e;
+      const float add = (col >= pbase && col < pend) ? cc[(col - pbase) % 3] : 0.f;
+      e4[e] = (e4[e] + add) * inv;
+    }
   }
   store_quarter<NV4>(wsf(a, L.off_o) + ri * L.DVp, part, o);
   if (part == 0) wsf(a, L.off_lse)[ri] = empty ? -INFINITY : m + logf(l);
@@ -295,6 +336,8 @@ __global__ __launch_bounds__(4 * ROWS) void bw_query_kernel(BwArgs a) {
   const float gam = wsf(a, L.off_gam)[h];
   const float lse = wsf(a, L.off_lse)[ri];
   const float dsum = wsf(a, L.off_dd)[ri];
+  const float4 sv = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + ri * 4)[0];
+  const float3 cq = blk_ref(a, b, ic);
   const bool mq = qin && a.mask[(size_t)b * L.N + ic] != 0 && lse > -INFINITY;
   float4 qv[NK4], dq[NK4];
   load_quarter<NK4>(wsf(a, L.off_qv) + ri * L.DKp, part, qv);
@@ -329,6 +372,9 @@ __global__ __launch_bounds__(4 * ROWS) void bw_query_kernel(BwArgs a) {
     }
     __syncthreads();
     const int nj = min(kBwTile, L.N - j0);
+    // Dsum'_i + S_i . (c_i - c_t) for this key block
+    const float3 ct = blk_ref(a, b, j0);
+    const float corr = fmaf(sv.x, cq.x - ct.x, fmaf(sv.y, cq.y - ct.y, fmaf(sv.z, cq.z - ct.z, dsum)));
     for (int jj = 0; jj < nj; ++jj) {
       float d2;
       const float lg = logit_q<NK4>(qv, &sK[jj][part * 4 * NK4], qa, &sB[jj][part * 4], gam, true, d2);
@@ -336,7 +382,7 @@ __global__ __launch_bounds__(4 * ROWS) void bw_query_kernel(BwArgs a) {
       const bool ok = mq && sM[jj] != 0.f && (!pmrow || pmrow[j0 + jj] != 0);
       if (!ok) continue;
       const float p = expf(lg - lse);
-      const float ds = p * (dp - dsum);
+      const float ds = p * (dp - corr);
       axpy_quarter<NK4>(dq, ds, &sK[jj][0], part);
       const float4 y = *reinterpret_cast<const float4*>(&sB[jj][part * 4]);
       const float w = -2.f * gam * ds;
@@ -366,7 +412,7 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
   __shared__ __align__(16) float sQ[kBwTile][KW];
   __shared__ __align__(16) float sA[kBwTile][16];
   __shared__ __align__(16) float sD[kBwTile][VW];
-  __shared__ float sL[kBwTile], sS[kBwTile];
+  __shared__ float sL[kBwTile], sS[kBwTile], sSx[kBwTile], sSy[kBwTile], sSz[kBwTile];
   __shared__ uint8_t sPM[kBwTile][ROWS];
   const int tid = threadIdx.x, part = tid & 3, r = tid >> 2;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -376,6 +422,7 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
   const size_t rj = rowidx(L, b, h, jc);
   const float gam = wsf(a, L.off_gam)[h];
   const bool mk = kin && a.mask[(size_t)b * L.N + jc] != 0;
+  const float3 ckey = blk_ref(a, b, jc);
   constexpr bool kDS = MODE != 1, kDV = MODE != 0;
   float4 kv[NK4], dk[kDS ? NK4 : 1];
   load_quarter<NK4>(wsf(a, L.off_kv) + rj * L.DKp, part, kv);
@@ -416,6 +463,10 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
       const bool ok = i < L.N && a.mask[(size_t)b * L.N + icl] != 0 && lse > -INFINITY;
       sL[tid] = ok ? lse : INFINITY;  // +inf marks a query that takes no key
       sS[tid] = wsf(a, L.off_dd)[rowidx(L, b, h, icl)];
+      const float4 sv = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + rowidx(L, b, h, icl) * 4)[0];
+      sSx[tid] = sv.x;
+      sSy[tid] = sv.y;
+      sSz[tid] = sv.z;
     }
     for (int e = tid; e < kBwTile * ROWS; e += 4 * ROWS) {
       const int ii = e / ROWS, jj = e - ii * ROWS;
@@ -424,6 +475,9 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
     }
     __syncthreads();
     const int ni = min(kBwTile, L.N - i0);
+    // the query block's reference relative to this key's
+    const float3 cqb = blk_ref(a, b, i0);
+    const float dcx = cqb.x - ckey.x, dcy = cqb.y - ckey.y, dcz = cqb.z - ckey.z;
     for (int ii = 0; ii < ni; ++ii) {
       float d2;
       const float lg = logit_q<NK4>(kv, &sQ[ii][part * 4 * NK4], kb, &sA[ii][part * 4], gam, false, d2);
@@ -432,7 +486,8 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
         const bool ok = mk && sL[ii] < INFINITY && sPM[ii][r] != 0;
         if (!ok) continue;
         const float p = expf(lg - sL[ii]);
-        const float ds = p * (dp - sS[ii]);
+        const float corr = fmaf(sSx[ii], dcx, fmaf(sSy[ii], dcy, fmaf(sSz[ii], dcz, sS[ii])));
+        const float ds = p * (dp - corr);
         axpy_quarter<NK4>(dk, ds, &sQ[ii][0], part);
         if constexpr (kDV) axpy_quarter<NV4>(dv, p, &sD[ii][0], part);
         const float4 x = *reinterpret_cast<const float4*>(&sA[ii][part * 4]);
@@ -517,6 +572,10 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
 #pragma unroll
   for (int v = 0; v < NVB; ++v) oacc[v] = f32x16_t{};
   float m = -INFINITY, lsum = 0.f;
+  // sum_j p_ij (c_j - c_i) over this lane's keys (the wavefront's 32 queries
+  // are one block: one reference)
+  const float3 cq = blk_ref(a, b, qc);
+  float cx = 0.f, cy = 0.f, cz = 0.f;
   const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + qc) * L.N : nullptr;
   const int P3 = L.P3;  // coordinates past 3P are zero on both sides
   for (int j0 = 0; j0 < L.N; j0 += kBwKT) {
@@ -576,15 +635,26 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
     if (tmax > m + 5.0f) {  // raise the running maximum (lazily: values up to e^5 are fine)
       const float c = expf(m - tmax);
       lsum *= c;
+      cx *= c;
+      cy *= c;
+      cz *= c;
 #pragma unroll
       for (int v = 0; v < NVB; ++v) oacc[v] *= c;
       m = tmax;
     }
     float pr[16];
+    float tsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       pr[r] = lg[r] > -INFINITY ? expf(lg[r] - m) : 0.f;
-      lsum += pr[r];
+      tsum += pr[r];
+    }
+    lsum += tsum;
+    {
+      const float3 ct = blk_ref(a, b, j0);
+      cx = fmaf(tsum, ct.x - cq.x, cx);
+      cy = fmaf(tsum, ct.y - cq.y, cy);
+      cz = fmaf(tsum, ct.z - cq.z, cz);
     }
     // O^T += VV^T P^T
 #pragma unroll
@@ -594,18 +664,31 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
         oacc[v] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[kappa(s, hf)][32 * v + l32], pr[s], oacc[v], 0, 0, 0);
   }
   lsum += __shfl_xor(lsum, 32);
+  cx += __shfl_xor(cx, 32);
+  cy += __shfl_xor(cy, 32);
+  cz += __shfl_xor(cz, 32);
   if (!qin) return;
   const bool empty = !(lsum > 0.f);
   const float inv = empty ? 0.f : 1.f / lsum;
+  // O' : the value points relative to the query's block reference
+  const int pbase = L.Dv + L.R * L.Cz, pend = pbase + 3 * L.Q;
+  const float cc[3] = {cx, cy, cz};
   float* orow = wsf(a, L.off_o) + rq * L.DVp;
 #pragma unroll
   for (int v = 0; v < NVB; ++v)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int c = 32 * v + 8 * g + 4 * hf;
-      if (c < L.DVp)
-        *reinterpret_cast<float4*>(orow + c) =
-            make_float4(oacc[v][4 * g] * inv, oacc[v][4 * g + 1] * inv, oacc[v][4 * g + 2] * inv, oacc[v][4 * g + 3] * inv);
+      if (c < L.DVp) {
+        float e4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = c + e;
+          const float add = (col >= pbase && col < pend) ? cc[(col - pbase) % 3] : 0.f;
+          e4[e] = (oacc[v][4 * g + e] + add) * inv;
+        }
+        *reinterpret_cast<float4*>(orow + c) = make_float4(e4[0], e4[1], e4[2], e4[3]);
+      }
     }
   if (hf == 0) wsf(a, L.off_lse)[rq] = empty ? -INFINITY : m + logf(lsum);
 }
@@ -650,6 +733,8 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   const float gam = wsf(a, L.off_gam)[h];
   const float lse = wsf(a, L.off_lse)[rq];
   const float dsum = wsf(a, L.off_dd)[rq];
+  const float4 sv = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + rq * 4)[0];
+  const float3 cq = blk_ref(a, b, qc);
   const bool mq = qin && a.mask[(size_t)b * L.N + qc] != 0 && lse > -INFINITY;
   // key-row columns past DKp read zeros (the tile copies never write them)
   for (int e = tid; e < kBwKT * (KPI - DKp); e += 256) sK[e / (KPI - DKp)][DKp + e % (KPI - DKp)] = 0.f;
@@ -734,6 +819,9 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
       }
     }
     const int nj = min(kBwKT, L.N - j0);
+    // Dsum'_i + S_i . (c_i - c_t) for this key block
+    const float3 ct = blk_ref(a, b, j0);
+    const float corr = fmaf(sv.x, cq.x - ct.x, fmaf(sv.y, cq.y - ct.y, fmaf(sv.z, cq.z - ct.z, dsum)));
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -750,7 +838,7 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
               dif[4 * c4 + 3] * dif[4 * c4 + 3];
       }
       const float p = ok ? expf(sa[r] - gam * d2 - lse) : 0.f;
-      ds[r] = p * (pa[r] - dsum);
+      ds[r] = p * (pa[r] - corr);
 #pragma unroll
       for (int u = 0; u < P3C; ++u) da[u] = fmaf(ds[r], dif[u], da[u]);
       dg = fmaf(-ds[r], d2, dg);
@@ -817,7 +905,7 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
   __shared__ float sQT[32 * NKB][kBwKT + 1];
   __shared__ float sDT[32 * NVB][kBwKT + 1];
   __shared__ __align__(16) float sA[kBwKT][16];
-  __shared__ float sL[kBwKT], sS[kBwKT];
+  __shared__ float sL[kBwKT], sS[kBwKT], sSx[kBwKT], sSy[kBwKT], sSz[kBwKT];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -827,6 +915,7 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
   const size_t rj = rowidx(L, b, h, jc);
   const float gam = wsf(a, L.off_gam)[h];
   const bool mk = kin && a.mask[(size_t)b * L.N + jc] != 0;
+  const float3 ckey = blk_ref(a, b, jc);
   // rows of the last blocks past DKp / DVp read zeros
   for (int e = tid; e < (32 * NKB - DKp) * (kBwKT + 1); e += 256) sQT[DKp + e / (kBwKT + 1)][e % (kBwKT + 1)] = 0.f;
   for (int e = tid; e < (32 * NVB - DVp) * (kBwKT + 1); e += 256) sDT[DVp + e / (kBwKT + 1)][e % (kBwKT + 1)] = 0.f;
@@ -886,8 +975,15 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
       const bool ok = i < L.N && a.mask[(size_t)b * L.N + icl] != 0 && lse > -INFINITY;
       sL[tid] = ok ? lse : INFINITY;  // +inf marks a query that takes no key
       sS[tid] = wsf(a, L.off_dd)[rowidx(L, b, h, icl)];
+      const float4 sv = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + rowidx(L, b, h, icl) * 4)[0];
+      sSx[tid] = sv.x;
+      sSy[tid] = sv.y;
+      sSz[tid] = sv.z;
     }
     __syncthreads();
+    // the query block's reference relative to this key's
+    const float3 cqb = blk_ref(a, b, i0);
+    const float dcx = cqb.x - ckey.x, dcy = cqb.y - ckey.y, dcz = cqb.z - ckey.z;
     f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
     if constexpr (kDS) {
 #pragma unroll
@@ -922,7 +1018,8 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
       }
       pr[r] = ok ? expf(sa[r] - gam * d2 - sL[qq]) : 0.f;
       if constexpr (kDS) {
-        ds[r] = pr[r] * (pa[r] - sS[qq]);
+        const float corr = fmaf(sSx[qq], dcx, fmaf(sSy[qq], dcy, fmaf(sSz[qq], dcz, sS[qq])));
+        ds[r] = pr[r] * (pa[r] - corr);
 #pragma unroll
         for (int u = 0; u < P3C; ++u) db[u] = fmaf(ds[r], dif[u], db[u]);
       }
@@ -1070,6 +1167,7 @@ __global__ __launch_bounds__(64) void bw_epi_kernel(BwArgs a) {
       const size_t ri = rowidx(L, b, h, i);
       for (int e = lane; e < L.DVp; e += 64) wsf(a, L.off_do)[ri * L.DVp + e] = 0.f;
       if (lane == 0) wsf(a, L.off_dd)[ri] = 0.f;
+      if (lane < 4) wsf(a, L.off_ds)[ri * 4 + lane] = 0.f;
     }
     for (int e = lane; e < R * Cz; e += 64) dzle[e] = 0.f;
     if (lane < 9) wsf(a, L.off_dre)[(size_t)bn * 9 + lane] = 0.f;
@@ -1103,14 +1201,17 @@ __global__ __launch_bounds__(64) void bw_epi_kernel(BwArgs a) {
     for (int h = 0; h < H; ++h) s += wsf(a, L.off_o)[rowidx(L, b, h, i) * L.DVp + Dv + r * Cz + c] * dfeat[oP + h * Cz + c];
     dzle[e] = s;
   }
-  // points: one lane per (h, q)
+  // points: one lane per (h, q); O holds them relative to the block
+  // reference c of residue i, so g - t = O' - (t - c)
+  const float3 cr = blk_ref(a, b, i);
+  const float tc[3] = {tv[0] - cr.x, tv[1] - cr.y, tv[2] - cr.z};
   float dr[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float dt[3] = {0.f, 0.f, 0.f};
   for (int e = lane; e < H * Q; e += 64) {
     const int h = e / Q, qq = e - h * Q;
     const size_t ri = rowidx(L, b, h, i);
     const float* g = wsf(a, L.off_o) + ri * L.DVp + Dv + R * Cz + 3 * qq;
-    const float rel[3] = {g[0] - tv[0], g[1] - tv[1], g[2] - tv[2]};
+    const float rel[3] = {g[0] - tc[0], g[1] - tc[1], g[2] - tc[2]};
     float loc[3];
     for (int x = 0; x < 3; ++x) loc[x] = Rm[0 * 3 + x] * rel[0] + Rm[1 * 3 + x] * rel[1] + Rm[2 * 3 + x] * rel[2];
     const float len = sqrtf(loc[0] * loc[0] + loc[1] * loc[1] + loc[2] * loc[2] + a.eps);
@@ -1146,7 +1247,8 @@ __global__ __launch_bounds__(64) void bw_epi_kernel(BwArgs a) {
     for (int e = 0; e < 3; ++e) wsf(a, L.off_dte)[(size_t)bn * 3 + e] = dt[e];
   }
   __syncthreads();
-  // Dsum_h = dO_h . O_h
+  // Dsum'_h = dO_h . O'_h, and S_h = the sum of dO_h's point part over the
+  // value points (per coordinate)
   for (int h = 0; h < H; ++h) {
     const size_t ri = rowidx(L, b, h, i);
     const float* O = wsf(a, L.off_o) + ri * L.DVp;
@@ -1155,6 +1257,12 @@ __global__ __launch_bounds__(64) void bw_epi_kernel(BwArgs a) {
     for (int e = lane; e < L.DV; e += 64) s += O[e] * dO[e];
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
     if (lane == 0) wsf(a, L.off_dd)[ri] = s;
+    if (lane < 4) {
+      float sc = 0.f;
+      if (lane < 3)
+        for (int qq = 0; qq < Q; ++qq) sc += dO[Dv + R * Cz + 3 * qq + lane];
+      wsf(a, L.off_ds)[ri * 4 + lane] = sc;
+    }
   }
 }
 
@@ -1410,6 +1518,7 @@ bool bw_layout(const ipa_shape* s, BwLayout* L) {
   L->off_lse = take(rows);
   L->off_do = take(rows * L->DVp);
   L->off_dd = take(rows);
+  L->off_ds = take(rows * 4);
   L->off_feat = take(bn * (L->F + 1));
   L->off_dfeat = take(bn * L->F);
   L->off_dqv = take(rows * L->DKp);
