@@ -33,6 +33,25 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_mfma_traffic.json")
 KERNEL_SOURCES = ("flash_mfma.hip", "mfma_tile.h", "common.h")
 
 
+def host_cores() -> dict:
+    """Host CPU the oracle baselines run on: the cores this process may use
+    (at most 16, one GPU's share of a box), nproc and the CPU model."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cores": max(1, min(usable, 16)), "nproc": os.cpu_count(), "cpu_model": model}
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
@@ -256,23 +275,21 @@ def time_backward(name, B, N, kw, steps, min_warm_ms=40.0):
 
 def backward_cpu_baseline(N=2048):
     """The float64 autograd oracle for a whole backward at a bounded length
-    (same widths, B=1, H=8), as algorithmic TFLOP/s (the flops of backward_flops)."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-    from oracle.ipa_backward import ipa_gradients
+    (same widths, B=1, H=8) on the host's cores: the upstream rows split into
+    one block per process (the gradients of the blocks add up to the whole),
+    as algorithmic TFLOP/s (the flops of backward_flops)."""
     from rna_structure_amd.synth import IPAShape, make_inputs
     sh = IPAShape(B=1, N=N, H=8, dtype="f32")
     inp = make_inputs(sh, 9000 + N, frames="walk", step=3.8)
-    rng = np.random.default_rng(1)
-    du = rng.standard_normal((1, N, sh.Cout))
-    dl = rng.standard_normal((1, N, sh.H, sh.Q, 3))
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        ipa_gradients(inp, du, dl)
-        el = time.perf_counter() - t0
+    # The backward oracle's workers import torch, and a process that has
+    # loaded torch counts as one that holds the GPU: keep those workers, this
+    # process and the child within the 16 processes one GPU may have.
+    r = _run_cpu_oracle("backward", str(N), 0.0, max_workers=12)
     flops = backward_flops(sh, inp["mask"])
-    return dict(value=round(flops / el / 1e12, 6), unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"whole backward at N={N} (B1 H8, standard widths), float64 autograd oracle, {el:.1f} s")
+    return dict(value=round(flops / r["seconds_per_call"] / 1e12, 6), unit="TFLOP/s", cores=r["workers"],
+                kind="oracle", nproc=r["nproc"], cpu_model=r["cpu_model"],
+                sample=f"whole backward at N={N} (B1 H8, standard widths), float64 autograd oracle, upstream rows "
+                       f"in {r['workers']} blocks on as many processes, {r['wall_s']:.1f} s wall")
 
 
 def backward_section(args):
@@ -288,28 +305,119 @@ def backward_section(args):
 
 
 def knn_cpu_baseline(N=16384, budget_s=3.0):
-    """The kNN oracle on a sample of rows of the N-residue walk, scaled to all rows."""
+    """The kNN oracle on a sample of rows of the N-residue walk on the host's
+    cores (rows split over one process per core), scaled to all rows."""
+    r = _run_cpu_oracle("knn", str(N), budget_s)
+    return {"workload": f"knn_{N}", "ms_per_call": round(r["seconds_per_call"] * 1e3, 1), "cores": r["workers"],
+            "nproc": r["nproc"], "cpu_model": r["cpu_model"], "kind": "oracle",
+            "sample": f"{r['rows']} of {N} rows, fp32 NumPy oracle in {r['workers']} processes, "
+                      f"{r['wall_s']:.1f} s wall, scaled by N/rows"}
+
+
+# ---------------------------------------------------------------- CPU oracle baselines
+# The oracles are plain NumPy / PyTorch code whose einsums run on one core.
+# To time them on the host's cores, a child process (started with
+# --cpu-oracle, never touching the GPU) splits independent query rows over
+# worker processes, one BLAS thread each: forward rows are independent, and
+# the backward's gradient is a sum over upstream rows, so row blocks of the
+# row-restricted gradient oracle add up to the whole backward.
+_ORACLE = {}
+
+
+def _oracle_job(rows):
     import numpy as np
     from threadpoolctl import threadpool_limits
-
-    from oracle import knn_distogram
-    from rna_structure_amd.synth import make_positions
-    pos = make_positions(1, N, 7000 + N, frames="walk", step=3.8)
+    kind = _ORACLE["kind"]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        knn_distogram(pos["translation"], pos["mask"], k=20, rows=np.arange(16))
-        per_row = (time.perf_counter() - t0) / 16
-        n = int(max(16, min(N, budget_s / max(per_row, 1e-9))))
+        if kind == "forward":
+            from oracle import ipa_factored
+            ipa_factored(_ORACLE["inp"], rows=rows, keep=("update", "local_points"))
+        elif kind == "backward":
+            import torch
+            torch.set_num_threads(1)
+            from oracle.ipa_backward import ipa_gradients
+            du, dl = _ORACLE["du"], _ORACLE["dl"]
+            ipa_gradients(_ORACLE["inp"], du[:, rows], dl[:, rows], rows=list(rows))
+        elif kind == "knn":
+            from oracle import knn_distogram
+            pos = _ORACLE["inp"]
+            knn_distogram(pos["translation"], pos["mask"], k=20, rows=np.asarray(rows))
+        else:
+            from oracle import flashbias_rows
+            inp = _ORACLE["inp"]
+            flashbias_rows(inp["q"], inp["k"], inp["v"], inp["phi_q"], inp["phi_k"], _ORACLE["scale"],
+                           np.asarray(rows))
+        return time.perf_counter() - t0
+
+
+def cpu_oracle_main(kind: str, arg: str, budget_s: float, workers: int) -> None:
+    """Child process: time an oracle on `workers` processes (one BLAS thread
+    each) over a bounded sample of rows; print one JSON line."""
+    import concurrent.futures
+    import multiprocessing
+    import numpy as np
+    _ORACLE["kind"] = kind
+    if kind == "forward":
+        inp = make_workload(arg)
+        N, nb = inp["shape"].N, inp["shape"].B
+    elif kind == "backward":
+        from rna_structure_amd.synth import IPAShape, make_inputs
+        N = int(arg)
+        sh = IPAShape(B=1, N=N, H=8, dtype="f32")
+        inp = make_inputs(sh, 9000 + N, frames="walk", step=3.8)
+        rng = np.random.default_rng(1)
+        _ORACLE["du"] = rng.standard_normal((1, N, sh.Cout))
+        _ORACLE["dl"] = rng.standard_normal((1, N, sh.H, sh.Q, 3))
+    elif kind == "knn":
+        from rna_structure_amd.synth import make_positions
+        N = int(arg)
+        inp = make_positions(1, N, 7000 + N, frames="walk", step=3.8)
+    else:
+        from rna_structure_amd.synth import make_bias_inputs
+        name, dims, bkind, causal, _ = FLASHBIAS_WORKLOADS[1]
+        inp = make_bias_inputs(**dims, seed=8000 + dims["N"], kind=bkind)
+        _ORACLE["scale"] = 1.0 / math.sqrt(dims["D"])
+        N = dims["N"]
+    _ORACLE["inp"] = inp
+    rng = np.random.default_rng(0)
+    if kind == "backward":
+        n = N  # the whole backward, split into row blocks
+    else:
+        probe = np.sort(rng.choice(N, size=min(N, 16), replace=False))
+        per_row = _oracle_job(probe) / len(probe)
+        n = int(max(workers, min(N, budget_s * workers / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(N, size=n, replace=False))
+    chunks = [c for c in np.array_split(rows, workers) if len(c)]
+    ctx = multiprocessing.get_context("fork")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=len(chunks), mp_context=ctx) as ex:
+        list(ex.map(_oracle_job, [chunks[0][:1]] * len(chunks)))  # start the workers
         t0 = time.perf_counter()
-        knn_distogram(pos["translation"], pos["mask"], k=20, rows=np.arange(n))
-        el = time.perf_counter() - t0
-    return {"workload": f"knn_{N}", "ms_per_call": round(el * N / n * 1e3, 1), "cores": 1, "kind": "oracle",
-            "sample": f"{n} of {N} rows, fp32 NumPy oracle, {el:.1f} s measured, scaled by N/rows"}
+        list(ex.map(_oracle_job, chunks))
+        wall = time.perf_counter() - t0
+    print(json.dumps({"seconds_per_call": wall * N / n, "rows": n, "N": N, "wall_s": wall,
+                      "workers": len(chunks)}), flush=True)
 
 
-def cpu_baseline(inp, flops, budget_s=12.0):
-    """Time the float64 oracle on a bounded sample of query rows and scale to
-    the whole forward (per-row cost is the same for every row at fixed N)."""
+def _run_cpu_oracle(kind: str, arg: str, budget_s: float, max_workers: int = 16) -> dict:
+    """Run cpu_oracle_main in a child process (which never touches the GPU)."""
+    import subprocess
+    host = host_cores()
+    workers = min(host["cores"], max_workers)
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-oracle", kind, arg, str(budget_s), str(workers)]
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600, env=env)
+    if r.returncode != 0:
+        raise RuntimeError(f"cpu oracle child failed: {r.stderr[-2000:]}")
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    out.update(host)
+    return out
+
+
+def _oracle_rate(inp, threads, budget_s):
+    """Seconds per whole forward of the float64 oracle with `threads` BLAS
+    threads, from a bounded sample of query rows scaled by N/rows (the per-row
+    cost is the same for every row at fixed N); also the sample size."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -317,21 +425,33 @@ def cpu_baseline(inp, flops, budget_s=12.0):
     shape = inp["shape"]
     N = shape.N
     rng = np.random.default_rng(0)
-    with threadpool_limits(limits=1):
-        rows = np.sort(rng.choice(N, size=4, replace=False))
+    with threadpool_limits(limits=threads):
+        rows = np.sort(rng.choice(N, size=min(N, 16), replace=False))
         t0 = time.perf_counter()
         ipa_factored(inp, rows=rows, keep=("update", "local_points"))
-        per_row = (time.perf_counter() - t0) / (len(rows) * shape.B)
-        n = int(max(4, min(N, budget_s / max(per_row * shape.B, 1e-9))))
+        per_row = (time.perf_counter() - t0) / len(rows)
+        n = int(max(16, min(N, budget_s / max(per_row, 1e-9))))
         rows = np.sort(rng.choice(N, size=n, replace=False))
         t0 = time.perf_counter()
         ipa_factored(inp, rows=rows, keep=("update", "local_points"))
         el = time.perf_counter() - t0
-    per_call_s = el * N / n
-    return dict(value=flops / per_call_s / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"{n} of {N} query rows x all {shape.B} samples, float64 NumPy oracle, "
-                       f"{el:.1f} s measured, scaled by N/rows to {per_call_s:.1f} s per forward",
-                seconds_per_call=per_call_s)
+    return el * N / n, n, el
+
+
+def cpu_baseline(workload, inp, flops, budget_s=12.0):
+    """The float64 oracle on the host's cores (query rows split over one
+    process per core), timed on a bounded sample of query rows and scaled to
+    the whole forward; the one-thread rate beside it."""
+    shape = inp["shape"]
+    r = _run_cpu_oracle("forward", workload, budget_s)
+    one_s, n1, el1 = _oracle_rate(inp, 1, budget_s / 4)
+    return dict(value=flops / r["seconds_per_call"] / 1e12, unit="TFLOP/s", cores=r["workers"], kind="oracle",
+                sample=f"{r['rows']} of {shape.N} query rows x all {shape.B} samples, float64 NumPy oracle in "
+                       f"{r['workers']} processes (one BLAS thread each), {r['wall_s']:.1f} s wall, scaled by "
+                       f"N/rows to {r['seconds_per_call']:.1f} s per forward",
+                seconds_per_call=r["seconds_per_call"], nproc=r["nproc"], cpu_model=r["cpu_model"],
+                one_thread={"value": flops / one_s / 1e12, "seconds_per_call": one_s,
+                            "sample": f"{n1} rows on one thread, {el1:.1f} s measured"})
 
 
 def copy_calibration(mib: int, reps: int = 3) -> None:
@@ -428,30 +548,16 @@ def time_flashbias(name, dims, kind, causal, steps, min_warm_ms=40.0):
 
 def flashbias_cpu_baseline(budget_s=10.0):
     """The float64 oracle on a sample of query rows of the squared-distance
-    workload, scaled by N/rows to a whole call (algorithmic TFLOP/s)."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-    from oracle import flashbias_rows
-    from rna_structure_amd.synth import make_bias_inputs
+    workload on the host's cores (rows split over one process per core),
+    scaled by N/rows to a whole call (algorithmic TFLOP/s)."""
     name, dims, kind, causal, _ = FLASHBIAS_WORKLOADS[1]
-    inp = make_bias_inputs(**dims, seed=8000 + dims["N"], kind=kind)
-    scale = 1.0 / math.sqrt(dims["D"])
+    r = _run_cpu_oracle("flashbias", name, budget_s)
     N = dims["N"]
-    rng = np.random.default_rng(2)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        flashbias_rows(inp["q"], inp["k"], inp["v"], inp["phi_q"], inp["phi_k"], scale, np.arange(4))
-        per_row = (time.perf_counter() - t0) / 4
-        n = int(max(4, min(N, budget_s / max(per_row, 1e-9))))
-        rows = np.sort(rng.choice(N, size=n, replace=False))
-        t0 = time.perf_counter()
-        flashbias_rows(inp["q"], inp["k"], inp["v"], inp["phi_q"], inp["phi_k"], scale, rows)
-        el = time.perf_counter() - t0
-    per_call = el * N / n
     flops = dims["B"] * dims["H"] * N * dims["M"] * (2 * (dims["D"] + dims["R"]) + 2 * dims["Dv"])
-    return dict(value=round(flops / per_call / 1e12, 6), unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"{n} of {N} query rows of {name}, float64 NumPy oracle, {el:.1f} s measured, "
-                       f"scaled by N/rows to {per_call:.0f} s per call")
+    return dict(value=round(flops / r["seconds_per_call"] / 1e12, 6), unit="TFLOP/s", cores=r["workers"],
+                kind="oracle", nproc=r["nproc"], cpu_model=r["cpu_model"],
+                sample=f"{r['rows']} of {N} query rows of {name}, float64 NumPy oracle in {r['workers']} processes, "
+                       f"{r['wall_s']:.1f} s wall, scaled by N/rows to {r['seconds_per_call']:.0f} s per call")
 
 
 def flashbias_section(args):
@@ -497,7 +603,13 @@ def main():
                     help="run only plain copies of MIB MiB (counter calibration) and exit")
     ap.add_argument("--hbm-calibration", action="store_true",
                     help="print the fill / copy / sum rates of plain device kernels and exit")
+    ap.add_argument("--cpu-oracle", nargs=4, metavar=("KIND", "ARG", "BUDGET_S", "WORKERS"),
+                    help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_oracle:
+        kind, arg, budget, workers = args.cpu_oracle
+        cpu_oracle_main(kind, arg, float(budget), int(workers))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -565,7 +677,8 @@ def main():
     print(json.dumps({"partial": out}), file=sys.stderr, flush=True)
     if not args.no_sweep:
         sweep = []
-        for name in ("short_batch", "sweep_4096", "sweep_8192", "sweep_16384", "sweep_32768"):
+        for name in ("tiny", "protein", "rna", "short_batch", "sweep_4096", "sweep_8192", "sweep_16384",
+                     "sweep_32768"):
             if name == args.workload:
                 rr, sh, fl = r, shape, flops
             else:
@@ -573,7 +686,7 @@ def main():
                 sh = w["shape"]
                 fl = eff_flops(sh, w["mask"])
                 rr = time_forward(w, max(3, args.steps // 4), 2)
-            sweep.append({"workload": name, "B": sh.B, "N": sh.N, "H": sh.H, "ms": round(rr["ms"], 4),
+            sweep.append({"workload": name, "B": sh.B, "N": sh.N, "H": sh.H, "dtype": sh.dtype, "ms": round(rr["ms"], 4),
                           "eff_tflops": round(fl / (rr["ms"] * 1e-3) / 1e12, 2),
                           "flash_ms": round(rr["flash_ms"], 4),
                           "flash_frac_mfma": round(fl / (rr["flash_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -612,7 +725,7 @@ def main():
         out["flashbias"] = flashbias_section(args)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, flops)
+        out["cpu_baseline"] = cpu_baseline(args.workload, inp, flops)
     print(json.dumps(out), flush=True)
 
 
