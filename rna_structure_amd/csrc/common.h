@@ -49,8 +49,10 @@ constexpr int kVCols = kKeyTile + kRowPad;  // 72 elements = 144 bytes
 constexpr uint32_t kMagic = 0x46495041u;    // "FIPA"
 
 // Matrix-core kernel instances: (NQS, NVB, GS) = number of 16-wide bf16
-// K-steps of the scalar+pair query columns, number of 32-row bf16 value
-// blocks, number of fp16 geometric K-steps.
+// K-steps of the scalar+pair query columns (one for the scalar part, NQS - 1
+// for the pair part), number of 32-row value blocks besides the one of the
+// value points (one for the values, NVB - 1 for the pair part), number of
+// fp16 geometric K-steps.
 struct MfmaDims {
   int NQS, NVB, GS;
 };
@@ -72,15 +74,17 @@ struct Layout {
   int mfma;  // 1: matrix-core path (bf16 input), 0: fp32 path
   int NQS, NVB, GS;
   int QW;     // query scalar+pair width (elements)
-  int KROW;   // elements per key row (mfma: QW + 16 GS + pad; fp32: DKP)
-  int VROWS;  // mfma: rows of the transposed value tile; fp32: DVP (row stride)
+  int KROW;   // elements per key row (mfma: head part 16 + 16 GS + pad; fp32: DKP)
+  int VROWS;  // mfma: rows of the head part of the transposed value tile (64); fp32: DVP (row stride)
+  int KZROW;  // mfma: elements per row of the shared pair-factor key tile, 16 (NQS - 1) + pad
+  int VZROWS; // mfma: rows of the shared pair-factor value tile, 32 (NVB - 1)
   int DQP;    // fp32 path: padded query row width
   int DO;     // attention output width Dv + R*Cz + 3Q
   int has_pm;
   int F, FP;  // epilogue feature count, padded to 16
   int KS;     // matrix-core path: key ranges the fused kernel splits a query tile over
   int PREC;   // floats per partial-result record (KS > 1): DO values + 4 statistics, padded to 4
-  size_t off_ql, off_qa, off_kt, off_vt, off_ck, off_gam, off_km, off_part, off_pm, total;
+  size_t off_ql, off_qa, off_kt, off_vt, off_ktz, off_vtz, off_ck, off_gam, off_km, off_part, off_pm, total;
   size_t epi_ws;  // bytes of the epilogue's own workspace (packed w_out)
 };
 
@@ -100,14 +104,17 @@ static inline int key_splits(int B, int N, int H, int NT) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// Choose the smallest compiled matrix-core instance that holds the shape.
+// Choose the smallest compiled matrix-core instance that holds the shape:
+// the scalar query/key columns fit one K-step (D <= 16), the values and
+// their ones row one value block (Dv + 1 <= 32), the value points, ones row
+// and centroid another (3Q + 4 <= 32), and the R Cz pair columns the rest.
 // Returns false when none does.
 static inline bool pick_mfma_dims(int D, int Dv, int RCz, int P, int Q, MfmaDims* out) {
   static const MfmaDims inst[] = {{3, 2, 0}, {5, 3, 0}, {9, 5, 0}, {13, 7, 0}};
   if (P > 5) return false;
-  if (3 * Q + 4 > 32) return false;
+  if (3 * Q + 4 > 32 || D > 16 || Dv + 1 > 32) return false;
   for (const MfmaDims& m : inst) {
-    if (D + RCz <= 16 * m.NQS && Dv + RCz + 1 <= 32 * m.NVB) {
+    if (RCz <= 16 * (m.NQS - 1) && RCz <= 32 * (m.NVB - 1)) {
       *out = m;
       out->GS = geo_steps(P);
       return true;
@@ -151,8 +158,10 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
     L->mfma = 1;
     L->NQS = md.NQS; L->NVB = md.NVB; L->GS = md.GS;
     L->QW = 16 * md.NQS;
-    L->KROW = L->QW + 16 * md.GS + kRowPad;
-    L->VROWS = 32 * (md.NVB + 1);
+    L->KROW = 16 + 16 * md.GS + kRowPad;
+    L->VROWS = 64;
+    L->KZROW = 16 * (md.NQS - 1) + kRowPad;
+    L->VZROWS = 32 * (md.NVB - 1);
     L->DQP = L->QW;
     L->KS = key_splits(L->B, L->N, L->H, L->NT);
   } else if (s->dtype == IPA_F32) {
@@ -164,6 +173,7 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
     L->QW = L->DQP;
     L->KROW = round_up(L->D + L->RCz + 3 * L->P, 4);
     L->VROWS = round_up(L->DO, 4);
+    L->KZROW = L->VZROWS = 0;
   } else {
     return false;
   }
@@ -179,6 +189,11 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
     off = align256(off + B * H * NT * (size_t)L->VROWS * kVCols * 2);
   else
     off = align256(off + B * H * NK * (size_t)L->VROWS * 4);
+  // pair-factor key and value tiles, shared by the H heads (matrix-core path)
+  L->off_ktz = off;
+  if (L->mfma) off = align256(off + B * NT * (size_t)kKeyTile * L->KZROW * 2);
+  L->off_vtz = off;
+  if (L->mfma) off = align256(off + B * NT * (((size_t)L->VZROWS * kVCols * 2 + 1023) / 1024 * 1024));
   L->off_ck = off;
   off = align256(off + B * NT * 4 * 4);
   L->off_gam = off;
@@ -206,15 +221,37 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
 // Byte offsets of the records of the lifted workspace, used by the kernels
 // that write and read them and by the host-side bounds check of the tests.
 // Region sizes (make_layout): QL B H NQpad QW e, QA B H NQpad 64, KT B H NT
-// (64 KROW e), VT B H NT (VROWS kVCols 2 | NKpad/NT 64 VROWS 4), CK B NT 16,
+// (64 KROW e), VT B H NT (VROWS kVCols 2 | NKpad/NT 64 VROWS 4), KTZ B NT
+// (64 KZROW 2), VTZ B NT (VZROWS kVCols 2 rounded up to KiB), CK B NT 16,
 // KM B NT 8, PART KS B H NQpad PREC 4, PM B NQpad NT 8 (e = 2 on the
-// matrix-core path, 4 on the fp32 path).
+// matrix-core path, 4 on the fp32 path; KTZ and VTZ empty on the fp32 path).
+//
+// Matrix-core path, one key tile of 64 keys:
+//   KT  (per head)   rows [k (D, zero to 16) | geometric 16 GS | pad 8], bf16 / fp16
+//   KTZ (shared)     rows [zr (R Cz, zero to 16 (NQS - 1)) | pad 8], bf16
+//   VT  (per head)   64 rows x kVCols, fp16, transposed (one column per key):
+//                    rows 0..31  [v 2^-8 (Dv) | 1 | 0 ...]
+//                    rows 32..63 [x - c_t (3Q) | 1 | c_t (3) | 0 ...]
+//   VTZ (shared)     VZROWS rows x kVCols, fp16 [zr 2^-8 (R Cz) | 0 ...]
+// The four parts are whole KiB each, and the fused kernel copies them into
+// one LDS buffer in this order; the value part then reads as one tile of
+// 64 + VZROWS rows (value blocks 0 and 1 per head, 2 .. NVB pair factors).
 __host__ __device__ __forceinline__ size_t lifted_elem(const Layout& L) { return L.mfma ? 2 : 4; }
 __host__ __device__ __forceinline__ size_t kt_tile_bytes(const Layout& L) {
   return (size_t)kKeyTile * L.KROW * lifted_elem(L);
 }
 __host__ __device__ __forceinline__ size_t vt_tile_bytes(const Layout& L) {
   return L.mfma ? (size_t)L.VROWS * kVCols * 2 : (size_t)kKeyTile * L.VROWS * 4;
+}
+__host__ __device__ __forceinline__ size_t ktz_tile_bytes(const Layout& L) { return (size_t)kKeyTile * L.KZROW * 2; }
+__host__ __device__ __forceinline__ size_t vtz_tile_bytes(const Layout& L) {
+  return ((size_t)L.VZROWS * kVCols * 2 + 1023) / 1024 * 1024;
+}
+__host__ __device__ __forceinline__ size_t ktz_tile_off(const Layout& L, int b, int t) {
+  return L.off_ktz + ((size_t)b * L.NT + t) * ktz_tile_bytes(L);
+}
+__host__ __device__ __forceinline__ size_t vtz_tile_off(const Layout& L, int b, int t) {
+  return L.off_vtz + ((size_t)b * L.NT + t) * vtz_tile_bytes(L);
 }
 __host__ __device__ __forceinline__ size_t kt_tile_off(const Layout& L, int b, int h, int t) {
   return L.off_kt + (((size_t)b * L.H + h) * L.NT + t) * kt_tile_bytes(L);

@@ -1,9 +1,12 @@
 // Diagnostic kernel (tests only): the logits the fused kernel forms, for a
 // few query rows, in natural-log units, -inf where the key is not permitted.
 // The matrix-core variant runs the fused kernel's own MFMA fragment sequence
-// (mfma_tile.h) on the same lifted operands and the same query grouping, so
-// its logits are bit-identical to the ones the fused kernel exponentiates; together with the fused
-// kernel's log-sum-exp they give the attention rows exp(L - lse).  The fp32
+// (mfma_tile.h) on the same lifted operands and the same query grouping; the
+// fused kernel folds its running maximum into the per-tile row term, which is
+// zero here, so the two differ only in the rounding of that term (three fp16
+// parts of the row term over 16: a few units of 2^-22 relative).  Together
+// with the fused kernel's log-sum-exp these logits give the attention rows
+// exp(L - lse).  The fp32
 // variant repeats the fp32 kernel's expressions in the same order.
 #include "mfma_tile.h"
 
@@ -21,7 +24,6 @@ struct DiagArgs {
 template <int NQS, int GS>
 __global__ __launch_bounds__(64) void logit_rows_mfma_kernel(DiagArgs a) {
   constexpr int QW = 16 * NQS;
-  constexpr int KROW = QW + 16 * GS + kRowPad;
   const Layout& L = a.L;
   const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
   const int b = a.b, h = a.h, N = L.N, H = L.H, NT = L.NT;
@@ -43,12 +45,11 @@ __global__ __launch_bounds__(64) void logit_rows_mfma_kernel(DiagArgs a) {
     load_qa(reinterpret_cast<const float4*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + i) * 4, qin, av);
     build_geo<GS>(L.P, av, qvalid, gl, half, bg, &qg);
   }
-  const char* kt0 = a.ws + L.off_kt + ((size_t)b * H + h) * NT * (size_t)(64 * KROW * 2);
   for (int t = 0; t < NT; ++t) {
     const uint32_t mw = perm_word(L, a.ws, has_pm, b, i, qin, qvalid, t, half);
     geo_tile<GS>(qg, ck[(size_t)b * NT + t], gl, (float)L.P, 0.f, half, bg);
     f32x16_t sacc[2];
-    s_tile<NQS, GS>(kt0 + (size_t)t * 64 * KROW * 2, bq, bg, l32, half, sacc);
+    s_tile<NQS, GS>(a.ws + kt_tile_off(L, b, h, t), a.ws + ktz_tile_off(L, b, t), bq, bg, l32, half, sacc);
     if (!out_row) continue;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)

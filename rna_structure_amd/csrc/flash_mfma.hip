@@ -17,9 +17,11 @@
 //   raised when it grows by more than 8 (probabilities stay below 2^8) and
 //   an fp32 row sum for the log-sum-exp
 //   O^T += V~^T P^T                       fp16 probabilities against the fp16
-//                                         value tile: values and pair factors
-//                                         (times 2^-8), centred value points,
-//                                         the centroid and ones rows
+//                                         value tile: values (times 2^-8), the
+//                                         centred value points, the centroid
+//                                         and ones rows (per head), and the
+//                                         pair factors (times 2^-8, shared by
+//                                         the heads)
 // The accumulator layout of S^T gives every lane one query and 16 keys, so
 // the probabilities feed the value product from registers; the value tile is
 // stored transposed with its keys permuted to match (lift kernel).
@@ -28,7 +30,9 @@
 // values sum to one to fp32 rounding and the centroid cancels exactly.
 // Key and value tiles are copied global -> LDS with direct-to-LDS loads into
 // two buffers: the copies of the next tile run during the whole of the
-// current tile, and one barrier per tile separates the two.
+// current tile, and one barrier per tile separates the two.  A tile has four
+// parts (common.h): the head's key rows and value rows, and the pair-factor
+// key and value rows that the H heads of a batch element share.
 #include "lds_copy.h"
 #include "mfma_tile.h"
 
@@ -76,23 +80,30 @@ __device__ __forceinline__ int next_valid_tile(const uint32_t* kmb, int t, int N
   return __builtin_amdgcn_readfirstlane(t);
 }
 
-// Key/value tile buffers of an instance.
-// (Three buffers with the copies two tiles ahead, where they fit in the 160
-// KiB of LDS, measured no faster than two at N = 16384: the copies land
-// within one tile.  The loop keeps both forms.)
+// Byte sizes of the four parts of a key/value tile (common.h) and of one LDS
+// tile buffer, which holds them back to back in this order.
 template <int NQS, int NVB, int GS>
-constexpr int kv_buffers() { return 2; }
+struct TileDims {
+  static constexpr int KH = 64 * (16 + 16 * GS + kRowPad) * 2;    // head key rows
+  static constexpr int KZ = 64 * (16 * (NQS - 1) + kRowPad) * 2;  // pair-factor key rows
+  static constexpr int VH = 64 * kVCols * 2;                      // head value rows (blocks 0, 1)
+  static constexpr int VZ = (32 * (NVB - 1) * kVCols * 2 + 1023) / 1024 * 1024;  // pair-factor value rows
+  static constexpr int TB = KH + KZ + VH + VZ;
+};
 
-// Key and value tile t of one (batch, head) into LDS buffer buf.
+// Global addresses of key/value tile 0 of one (batch, head): the head's own
+// parts and the shared pair-factor parts.
+struct TileSrc {
+  const char *kh, *kz, *vh, *vz;
+};
+
+// Key and value tile t into LDS buffer buf.
 template <int NQS, int NVB, int GS, int W>
-__device__ __forceinline__ void copy_kv_tile(const char* ktg0, const char* vtg0, char* sk0, char* sv0, int t, int buf,
-                                             int w, int lane) {
-  constexpr int KT_BYTES = 64 * (16 * NQS + 16 * GS + kRowPad) * 2;
-  constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
-  constexpr int KT_LDS = (KT_BYTES + 1023) / 1024 * 1024;
-  constexpr int VT_LDS = (VT_BYTES + 1023) / 1024 * 1024;
-  dma_tile<KT_BYTES, W>(ktg0 + (size_t)t * KT_BYTES, sk0 + buf * KT_LDS, w, lane);
-  dma_tile<VT_BYTES, W>(vtg0 + (size_t)t * VT_BYTES, sv0 + buf * VT_LDS, w, lane);
+__device__ __forceinline__ void copy_kv_tile(const TileSrc& src, char* skv, int t, int buf, int w, int lane) {
+  using T = TileDims<NQS, NVB, GS>;
+  dma_parts<T::KH, T::KZ, T::VH, T::VZ, W>(src.kh + (size_t)t * T::KH, src.kz + (size_t)t * T::KZ,
+                                           src.vh + (size_t)t * T::VH, src.vz + (size_t)t * T::VZ,
+                                           skv + buf * T::TB, w, lane);
 }
 
 
@@ -228,20 +239,20 @@ __device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, 
 // one block of 32 queries i - l32 .. i - l32 + 31 after its last key tile:
 // log-sum-exp, O divided by the ones-row sums, the centroid added back to the
 // value points, written through an LDS slot of the (then free) tile buffers.
-// `w` names the slot (0 .. W-1): W/2 slots in each of the two buffer arrays.
-// Every wavefront of the workgroup calls it the same number of times (it
-// contains a barrier).
+// `w` names the slot (0 .. W-1).  Every wavefront of the workgroup calls it
+// the same number of times (it contains a barrier).
+// Value blocks: 0 = [v 2^-8 (Dv) | 1 | 0], 1 = [x - c_t (3Q) | 1 | c_t | 0],
+// 2 .. NVB = pair factors 2^-8 (R Cz rows).  The output row is
+// [v (Dv) | pair (R Cz) | points (3Q)], i.e. the blocks in the order
+// 0, 2, 3, .., NVB, 1 ("positions" 0 .. NVB below).
+template <int NVB>
+__device__ __forceinline__ constexpr int block_at(int pos) { return pos == 0 ? 0 : (pos == NVB ? 1 : pos + 1); }
+
 template <int NQS, int NVB, int GS, int W>
-__device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* sk0, char* sv0, int sp, int b, int h, int i,
+__device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* skv, int sp, int b, int h, int i,
                                             bool qin, bool qvalid, int w, int lane, int l32, int half,
                                             const f32x16_t* oacc, float m, float l, bool init) {
-  constexpr int QW = 16 * NQS;
-  constexpr int KROW = QW + 16 * GS + kRowPad;
-  constexpr int KT_BYTES = 64 * KROW * 2;
-  constexpr int VROWS = 32 * (NVB + 1);
-  constexpr int VT_BYTES = VROWS * kVCols * 2;
-  constexpr int KT_LDS = (KT_BYTES + 1023) / 1024 * 1024;
-  constexpr int VT_LDS = (VT_BYTES + 1023) / 1024 * 1024;
+  using T = TileDims<NQS, NVB, GS>;
   const Layout& L = a.L;
   const int N = L.N, H = L.H;
   const float ltot = l + __shfl_xor(l, 32);
@@ -254,23 +265,14 @@ __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* sk0, c
   const int Dv = L.Dv, RCz = L.RCz, Q3 = 3 * L.Q, DO = L.DO;
   const int d1 = Dv + RCz;
   float lbf, lh, cxyz[3];
-  {
-    const int vb1 = d1 >> 5, rr = d1 & 31;
-    float v = 0.f;
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      const float pv = pick16(oacc[vb], 4 * (rr >> 3) + (rr & 3));
-      v = (vb == vb1) ? pv : v;
-    }
-    lbf = __shfl(v, l32 + 32 * ((rr & 7) >> 2));
-  }
+  lbf = __shfl(pick16(oacc[0], 4 * (Dv >> 3) + (Dv & 3)), l32 + 32 * ((Dv & 7) >> 2));
   {
     int rr = Q3;
-    lh = __shfl(pick16(oacc[NVB], 4 * (rr >> 3) + (rr & 3)), l32 + 32 * ((rr & 7) >> 2));
+    lh = __shfl(pick16(oacc[1], 4 * (rr >> 3) + (rr & 3)), l32 + 32 * ((rr & 7) >> 2));
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
       rr = Q3 + 1 + x;
-      cxyz[x] = __shfl(pick16(oacc[NVB], 4 * (rr >> 3) + (rr & 3)), l32 + 32 * ((rr & 7) >> 2));
+      cxyz[x] = __shfl(pick16(oacc[1], 4 * (rr >> 3) + (rr & 3)), l32 + 32 * ((rr & 7) >> 2));
     }
   }
   // a partial result keeps the unnormalised sums (values times 2^-8) and
@@ -285,52 +287,54 @@ __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* sk0, c
     st[2] = nonempty ? lbf : 0.f;
     st[3] = nonempty ? lh : 0.f;
   }
-  // O is written through LDS (the tile buffers are free now), BPP
-  // accumulator blocks per pass: every wavefront stores its 32 queries x
-  // 32 BPP rows (scaled) in a slot of its own, register by register, then
-  // writes the pass's output columns, one contiguous range, 16 bytes per lane
-  // with consecutive lanes on consecutive addresses.
+  // first and one-past-last output column of position p
+  auto col_start = [&](int p) { return p == 0 ? 0 : (p == NVB ? d1 : min(Dv + 32 * (p - 1), d1)); };
+  auto col_end = [&](int p) { return p == 0 ? Dv : (p == NVB ? d1 + Q3 : min(Dv + 32 * p, d1)); };
+  // O is written through LDS (the tile buffers are free now), BPP positions
+  // per pass: every wavefront stores its 32 queries x 32 BPP rows (scaled) in
+  // a slot of its own, register by register, then writes the pass's output
+  // columns, one contiguous range, 16 bytes per lane with consecutive lanes
+  // on consecutive addresses.
   constexpr int NB = NVB + 1;
-  constexpr int SLOTS = W / 2;  // slots per buffer array
-  constexpr int BUF = KT_LDS * 2 < VT_LDS * 2 ? KT_LDS * 2 : VT_LDS * 2;
-  constexpr int BPP0 = (BUF / (SLOTS * 32 * 4) - 1) / 32;
+  constexpr int SLOT = 2 * T::TB / W;  // bytes per slot
+  constexpr int BPP0 = (SLOT / (32 * 4) - 1) / 32;
   constexpr int BPP = BPP0 < NB ? BPP0 : NB;
   static_assert(BPP >= 1, "LDS slots too small for the output staging");
   constexpr int PITCH = 32 * BPP + 1;  // floats per staged query row
-  float* slot = reinterpret_cast<float*>((w < SLOTS ? sk0 : sv0) + (size_t)(w % SLOTS) * 32 * PITCH * 4);
+  static_assert(32 * PITCH * 4 <= SLOT, "output staging slot");
+  float* slot = reinterpret_cast<float*>(skv + (size_t)w * SLOT);
   const int i0 = i - l32;  // first query of this wavefront
   __syncthreads();  // every wave is done with the tile buffers
 #pragma unroll
   for (int p = 0; p < (NB + BPP - 1) / BPP; ++p) {
-    const int vb0 = p * BPP;
-    const int vb1 = vb0 + BPP < NB ? vb0 + BPP : NB;
+    const int p0 = p * BPP;
+    const int p1 = p0 + BPP < NB ? p0 + BPP : NB;
 #pragma unroll
     for (int j = 0; j < BPP; ++j) {
-      const int vb = vb0 + j;
-      if (vb < NB) {
+      const int pos = p0 + j;
+      if (pos < NB) {
+        const int vb = block_at<NVB>(pos);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           // row of register r in a 32-row block: 8 (r/4) + 4 half + r%4
           const int rb = 8 * (r >> 2) + (r & 3);
           float v;
-          if (vb < NVB) {
+          if (vb != 1) {
             v = oacc[vb][r] * ib;
           } else {
             // value-point row dd = rb + 4 half: add back the centroid coordinate dd % 3
             const int x0 = rb % 3, x1 = (rb + 4) % 3;
             const float c0 = x0 == 0 ? cxyz[0] : (x0 == 1 ? cxyz[1] : cxyz[2]);
             const float c1 = x1 == 0 ? cxyz[0] : (x1 == 1 ? cxyz[1] : cxyz[2]);
-            v = (oacc[NVB][r] + (half ? c1 : c0)) * ih;
+            v = (oacc[1][r] + (half ? c1 : c0)) * ih;
           }
           slot[l32 * PITCH + 32 * j + rb + 4 * half] = v;
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // output columns of this pass: values [32 vb0, min(32 vb1, d1)), then the
-    // value points [d1, d1 + 3Q) if the point block is in the pass
-    const int cs = vb0 < NVB ? min(32 * vb0, d1) : d1;
-    const int ce = vb1 > NVB ? d1 + Q3 : min(32 * vb1, d1);
+    // output columns of this pass: [col_start(p0), col_end(p1 - 1))
+    const int cs = col_start(p0), ce = col_end(p1 - 1);
     const int nc = ce - cs, n4 = (nc + 3) >> 2;
     const bool vec = (((partial ? L.PREC : DO) | cs) & 3) == 0;
     for (int x = lane; x < 32 * n4; x += 64) {
@@ -341,8 +345,10 @@ __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* sk0, c
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = cs + 4 * jj + e;
-        const int loc = c < d1 ? c - 32 * vb0 : 32 * (NVB - vb0) + (c - d1);
-        e4[e] = c < ce ? sr[loc] : 0.f;
+        // position and row of output column c
+        const int pos = c < Dv ? 0 : (c < d1 ? 1 + (c - Dv) / 32 : NVB);
+        const int row = c < Dv ? c : (c < d1 ? (c - Dv) % 32 : c - d1);
+        e4[e] = c < ce ? sr[32 * (pos - p0) + row] : 0.f;
       }
       float* dst = (partial ? prec + (size_t)iq * L.PREC : a.o + (((size_t)b * N + iq) * H + h) * DO) + cs + 4 * jj;
       if (vec && 4 * jj + 4 <= nc) {
@@ -355,60 +361,35 @@ __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* sk0, c
   }
 }
 
-// Main loop over the key tiles [t, tend) of key range sp and the final
-// normalisation (or, with several key ranges, the partial result) for one
-// wavefront's 32 queries.  The copy of the first tile t (into buffer 0) was
-// issued by the caller.  Key/value tiles alternate between two LDS buffers:
-// at the top of tile t the copies of t (issued one tile earlier) are waited
-// for, one barrier makes them visible and frees the other buffer, and the
-// copies of the next tile go out before the products of t start.  PM selects
-// the per-query pair-mask words (a vector load per tile); without a pair mask
-// the key mask is inside the key product.
-// One key tile t of the main loop, held in LDS buffer BUF of NBUF (a
-// compile-time index, so that every LDS offset is a constant): the point
-// operand with the current running maximum, the barrier that makes tile t
-// visible and frees the previous tile's buffer, the copies of the tile
-// NBUF - 1 ahead into that buffer, and the products and softmax of tile t.
-// Returns the next tile with a valid key (tend if none).
-template <int NQS, int NVB, int GS, int W, bool PM, int NBUF, int BUF>
-__device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const char* ktg0, const char* vtg0, char* sk0,
-                                           char* sv0, const uint32_t* kmb, const float4* ckb, int t, int tend, int b,
-                                           int i, bool qin, bool qvalid, bool active, int w, int lane, int l32,
-                                           int half, float gl, float Pf, const bf16x8_t* bq, f16x8_t* bg,
-                                           const QueryGeo& qg, f32x16_t* oacc, float& m, float& l, bool& init) {
-  constexpr int QW = 16 * NQS;
-  constexpr int KROW = QW + 16 * GS + kRowPad;
-  constexpr int KT_BYTES = 64 * KROW * 2;
-  constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
-  constexpr int KT_LDS = (KT_BYTES + 1023) / 1024 * 1024;
-  constexpr int VT_LDS = (VT_BYTES + 1023) / 1024 * 1024;
-  constexpr int DPW = dma_per_wave<KT_BYTES, W>() + dma_per_wave<VT_BYTES, W>();
-  constexpr int PREV = (BUF + NBUF - 1) % NBUF;  // the buffer the copies refill
+// One key tile t of the main loop, held in LDS buffer BUF (a compile-time
+// index, so that every LDS offset is a constant): the point operand with the
+// current running maximum, the wait for the tile's copies (issued one tile
+// earlier) and the barrier that makes them visible and frees the other
+// buffer, the copies of the next valid tile into that buffer, and the
+// products and softmax of tile t.  Returns the next tile with a valid key
+// (tend if none).
+template <int NQS, int NVB, int GS, int W, bool PM, int BUF>
+__device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc& src, char* skv,
+                                           const uint32_t* kmb, const float4* ckb, int t, int tend, int b, int i,
+                                           bool qin, bool qvalid, bool active, int w, int lane, int l32, int half,
+                                           float gl, float Pf, const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg,
+                                           f32x16_t* oacc, float& m, float& l, bool& init) {
+  using T = TileDims<NQS, NVB, GS>;
   const Layout& L = a.L;
   const int tn = next_valid_tile(kmb, t, tend);
   uint32_t mw = 0xFFFFFFFFu;
   if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
   geo_tile<GS>(qg, ld_uniform4(ckb + t), gl, Pf, m, half, bg);
-  // tile t has landed (the copies of the next tile, with three buffers, may
-  // still be in flight); every wave is done with the previous tile
-  if constexpr (NBUF == 3) {
-    if (tn < tend) wait_vmcnt<DPW>();
-    else wait_vmcnt<0>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  // tile t has landed; every wave is done with the previous tile
+  wait_vmcnt<0>();
   __syncthreads();
   if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
-  {
-    const int tc = NBUF == 3 ? (tn < tend ? next_valid_tile(kmb, tn, tend) : tend) : tn;
-    if (tc < tend) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, tc, PREV, w, lane);
-  }
+  if (tn < tend) copy_kv_tile<NQS, NVB, GS, W>(src, skv, tn, 1 - BUF, w, lane);
   if (!active) return tn;
-  const char* sk = sk0 + BUF * KT_LDS;
-  const char* sv = sv0 + BUF * VT_LDS;
+  const char* kt = skv + BUF * T::TB;
   f32x16_t sacc[2];
   __builtin_amdgcn_s_setprio(1);
-  s_tile<NQS, GS>(sk, bq, bg, l32, half, sacc);
+  s_tile<NQS, GS>(kt, kt + T::KH, bq, bg, l32, half, sacc);
   __builtin_amdgcn_s_setprio(0);
 
   float s32[32];
@@ -422,7 +403,7 @@ __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const char* k
   l = l * alpha + ps;
 
   __builtin_amdgcn_s_setprio(1);
-  pv_tile<NVB>(sv + (size_t)(l32 * kVCols) * 2 + half * 16, ph, oacc);
+  pv_tile<NVB>(kt + T::KH + T::KZ + (size_t)(l32 * kVCols) * 2 + half * 16, ph, oacc);
   __builtin_amdgcn_s_setprio(0);
   return tn;
 }
@@ -430,23 +411,18 @@ __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const char* k
 // Main loop over the key tiles [t, tend) of key range sp and the final
 // normalisation (or, with several key ranges, the partial result) for one
 // wavefront's 32 queries.  The copy of the first tile t (into buffer 0) was
-// issued by the caller.  Key/value tiles rotate through NBUF buffers and the
-// copies of a tile go out NBUF - 1 tiles before its turn: three buffers
-// where they fit in LDS and without a pair mask (whose words are vector loads
-// that the compiler would wait for with the copies still in flight), else
-// two.  The loop is unrolled by NBUF so that buffer offsets are constants.
-// PM selects the per-query pair-mask words (a vector load per tile); without
-// a pair mask the key mask is inside the key product.
+// issued by the caller.  Key/value tiles alternate between two LDS buffers
+// (the loop is unrolled by two so that buffer offsets are constants).  PM
+// selects the per-query pair-mask words (a vector load per tile); without a
+// pair mask the key mask is inside the key product.
 template <int NQS, int NVB, int GS, int W, bool PM>
-__device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* sv0, int t, int tend, int sp, int b,
-                                       int h, int i, bool qin, bool qvalid, int w, int lane, int l32, int half, float gl, float Pf,
-                                       const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
+__device__ __forceinline__ void attend(const FlashMfmaArgs& a, const TileSrc& src, char* skv, int t, int tend, int sp,
+                                       int b, int h, int i, bool qin, bool qvalid, int w, int lane, int l32, int half,
+                                       float gl, float Pf, const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
   const Layout& L = a.L;
   const int NT = L.NT;
   const float4* ckb = reinterpret_cast<const float4*>(a.ws + L.off_ck) + (size_t)b * NT;
   const uint32_t* kmb = reinterpret_cast<const uint32_t*>(a.ws + L.off_km) + (size_t)b * NT * 2;
-  const char* ktg0 = a.ws + kt_tile_off(L, b, h, 0);
-  const char* vtg0 = a.ws + vt_tile_off(L, b, h, 0);
   f32x16_t oacc[NVB + 1];
 #pragma unroll
   for (int vb = 0; vb <= NVB; ++vb) oacc[vb] = f32x16_t{};
@@ -455,42 +431,24 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, char* sk0, char* 
   // a wavefront without a valid query keeps copying tiles and meeting the
   // barriers, but does no products
   const bool active = __any(qvalid);
-  constexpr int NBUF = (!PM && kv_buffers<NQS, NVB, GS>() == 3) ? 3 : 2;
-#define FIPA_TILE(BUFI)                                                                                             \
-  attend_tile<NQS, NVB, GS, W, PM, NBUF, BUFI>(a, ktg0, vtg0, sk0, sv0, kmb, ckb, t, tend, b, i, qin, qvalid, active, \
-                                               w, lane, l32, half, gl, Pf, bq, bg, qg, oacc, m, l, init)
-  if constexpr (NBUF == 3) {
-    const int t1 = next_valid_tile(kmb, t, tend);
-    if (t1 < tend) copy_kv_tile<NQS, NVB, GS, W>(ktg0, vtg0, sk0, sv0, t1, 1, w, lane);
-    while (t < tend) {
-      t = FIPA_TILE(0);
-      if (t >= tend) break;
-      t = FIPA_TILE(1);
-      if (t >= tend) break;
-      t = FIPA_TILE(2);
-    }
-  } else {
-    while (t < tend) {
-      t = FIPA_TILE(0);
-      if (t >= tend) break;
-      t = FIPA_TILE(1);
-    }
+#define FIPA_TILE(BUFI)                                                                                              \
+  attend_tile<NQS, NVB, GS, W, PM, BUFI>(a, src, skv, kmb, ckb, t, tend, b, i, qin, qvalid, active, w, lane, l32, half, \
+                                         gl, Pf, bq, bg, qg, oacc, m, l, init)
+  while (t < tend) {
+    t = FIPA_TILE(0);
+    if (t >= tend) break;
+    t = FIPA_TILE(1);
   }
 #undef FIPA_TILE
-  finish_rows<NQS, NVB, GS, W>(a, sk0, sv0, sp, b, h, i, qin, qvalid, w, lane, l32, half, oacc, m, l, init);
+  finish_rows<NQS, NVB, GS, W>(a, skv, sp, b, h, i, qin, qvalid, w, lane, l32, half, oacc, m, l, init);
 }
 
 template <int NQS, int NVB, int GS, int W>
 __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
-  constexpr int QW = 16 * NQS;
-  constexpr int KROW = QW + 16 * GS + kRowPad;
-  constexpr int KT_BYTES = 64 * KROW * 2;
-  constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
-  // two buffers each, rounded up to whole KiB: the last copy chunk of a
-  // tile may be partial and its upper lanes then land in this padding
-  // (three buffers each where they fit, see attend)
-  __shared__ __attribute__((aligned(1024))) char sk[kv_buffers<NQS, NVB, GS>() * ((KT_BYTES + 1023) / 1024 * 1024)];
-  __shared__ __attribute__((aligned(1024))) char sv[kv_buffers<NQS, NVB, GS>() * ((VT_BYTES + 1023) / 1024 * 1024)];
+  using T = TileDims<NQS, NVB, GS>;
+  // two tile buffers, each [head key rows | pair key rows | head value rows |
+  // pair value rows]
+  __shared__ __attribute__((aligned(1024))) char skv[2 * T::TB];
 
   const Layout& L = a.L;
   const int N = L.N, H = L.H;
@@ -512,13 +470,13 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
 
   const int NT = L.NT;
   const uint32_t* kmb = reinterpret_cast<const uint32_t*>(a.ws + L.off_km) + (size_t)b * NT * 2;
+  const TileSrc src{a.ws + kt_tile_off(L, b, h, 0), a.ws + ktz_tile_off(L, b, 0), a.ws + vt_tile_off(L, b, h, 0),
+                    a.ws + vtz_tile_off(L, b, 0)};
   // key tiles [tb, te) of key range sp; the copy of the first goes out
   // before anything else is loaded
   const int tb = (int)(((long)NT * sp) / a.ks), te = (int)(((long)NT * (sp + 1)) / a.ks);
   const int t0 = next_valid_tile(kmb, tb - 1, te);
-  if (t0 < te)
-    copy_kv_tile<NQS, NVB, GS, W>(a.ws + kt_tile_off(L, b, h, 0), a.ws + vt_tile_off(L, b, h, 0), sk, sv, t0, 0, w,
-                                  lane);
+  if (t0 < te) copy_kv_tile<NQS, NVB, GS, W>(src, skv, t0, 0, w, lane);
   {
     // a workgroup none of whose queries is valid (padding) only writes zeros
     const int tq0 = (qt * W * 32) >> 6, tq1 = min(NT, tq0 + W / 2);
@@ -549,9 +507,9 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   }
 
   if (has_pm)
-    attend<NQS, NVB, GS, W, true>(a, sk, sv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, true>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
   else
-    attend<NQS, NVB, GS, W, false>(a, sk, sv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, false>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
 }
 
 // Merge the partial results of the KS key ranges of every (b, h, query):

@@ -76,6 +76,46 @@ __device__ __forceinline__ void dma_tile(const char* g, const char* s, int w, in
   }
 }
 
+// Copy a tile made of four parts, each a whole number of KiB and each from a
+// source of its own, into one LDS buffer (the parts back to back in order):
+// chunk c of the C = (B0 + B1 + B2 + B3) / 1024 chunks goes to s + 1024 c.
+// Wavefront w moves chunks w, w + W, ... (every wavefront issues
+// dma_per_wave<1024 C, W> instructions, repeating the last chunk where it has
+// fewer), lane l bytes 16 l .. 16 l + 15 of each.  Which part a chunk comes
+// from is decided on scalar registers (uniform per wavefront).
+__host__ __device__ constexpr int dma_part_of_chunk(int c, int C0, int C1, int C2) {
+  return c < C0 ? 0 : (c < C0 + C1 ? 1 : (c < C0 + C1 + C2 ? 2 : 3));
+}
+template <int B0, int B1, int B2, int B3, int W>
+__device__ __forceinline__ void dma_parts(const char* g0, const char* g1, const char* g2, const char* g3,
+                                          const char* s, int w, int lane) {
+  static_assert(B0 % 1024 == 0 && B1 % 1024 == 0 && B2 % 1024 == 0 && B3 % 1024 == 0, "parts of whole KiB");
+  constexpr int C0 = B0 / 1024, C1 = B1 / 1024, C2 = B2 / 1024, C3 = B3 / 1024;
+  constexpr int C = C0 + C1 + C2 + C3;
+  __builtin_assume(w >= 0 && w < W);
+  const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(s);
+  auto uni = [](const char* g) {
+    const uint64_t ga = (uint64_t)(uintptr_t)g;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ga);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
+    return (const char*)(uintptr_t)join_addr(hi, lo);
+  };
+  g0 = uni(g0); g1 = uni(g1); g2 = uni(g2); g3 = uni(g3);
+  const uint32_t voff = (uint32_t)lane * 16u;
+#pragma unroll
+  for (int k = 0; k < dma_per_wave<C * 1024, W>(); ++k) {
+    const int c = w + W * k < C ? w + W * k : C - 1;
+    const char* gc;
+    if (c < C0) gc = g0 + (size_t)c * 1024;
+    else if (c < C0 + C1) gc = g1 + (size_t)(c - C0) * 1024;
+    else if (c < C0 + C1 + C2) gc = g2 + (size_t)(c - C0 - C1) * 1024;
+    else gc = g3 + (size_t)(c - C0 - C1 - C2) * 1024;
+    const uint32_t m0 = lbase + (uint32_t)c * 1024u;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gc), "s"(m0)
+                 : "memory", "m0");
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -165,13 +165,13 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
   const float sp = kLog2e / sqrtf(3.0f);
 
   if constexpr (BF) {
-    // ---------------- matrix-core layouts
+    // ---------------- matrix-core layouts (common.h)
     const int QW = L.QW, KROW = L.KROW, P3 = 3 * P, GS = L.GS;
-    // key rows of tile (b,h,t): [k | zr | 0 | geo(48) | pad]
-    uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + L.off_kt) + (((size_t)b * H + h) * L.NT + t) * 64 * KROW;
     const uint16_t* k16 = reinterpret_cast<const uint16_t*>(a.k);
     const uint16_t* zr16 = reinterpret_cast<const uint16_t*>(a.zr);
     const uint16_t* v16 = reinterpret_cast<const uint16_t*>(a.v);
+    // head key rows of tile (b,h,t): [k | 0 | geometric 16 GS | pad]
+    uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + kt_tile_off(L, b, h, t));
     const int kchunks = KROW / 8;
     for (int ch = tid; ch < 64 * kchunks; ch += 256) {
       const int row = ch / kchunks, c0 = (ch % kchunks) * 8;
@@ -183,11 +183,9 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
         if (s_valid[row]) {
           if (c < D) {
             val = k16[(((size_t)b * N + j) * H + h) * D + c];
-          } else if (c < D + RCz) {
-            val = zr16[((size_t)b * N + j) * RCz + (c - D)];
-          } else if (c >= QW && c < QW + 16 * GS) {
+          } else if (c >= 16 && c < 16 + 16 * GS) {
             // geometric columns, layout in common.h
-            const int g = c - QW, base = 16 * (GS - 1);
+            const int g = c - 16, base = 16 * (GS - 1);
             if (g < base + 4) {
               if (g < P3) val = hi16(s_w[row][g]);
               else if (g < 2 * P3) val = lo16(s_w[row][g - P3]);
@@ -201,7 +199,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
               else if (x >= 9 && x <= 11) val = 0x4C00;  // fp16 16.0, multiplies the query's t'/16 parts
             }
           }
-        } else if (c == QW + 16 * (GS - 1) + 8) {
+        } else if (c == 16 + 16 * (GS - 1) + 8) {
           val = 0xFBFF;  // fp16 -65504 in the key-mask column of a masked key
         }
         out[e] = val;
@@ -213,11 +211,11 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
       pk.w = out[6] | ((uint32_t)out[7] << 16);
       reinterpret_cast<uint4*>(kt + (size_t)row * KROW + c0)[0] = pk;
     }
-    // transposed value tile (b,h,t): rows d, columns kappa (permuted keys)
-    const int VROWS = L.VROWS, NVB = L.NVB;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + L.off_vt) + (((size_t)b * H + h) * L.NT + t) * VROWS * kVCols;
+    // head value rows of tile (b,h,t), transposed (rows d, columns kappa =
+    // permuted keys): [v 2^-8 | 1 | 0] and [x - c | 1 | c | 0]
+    uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + vt_tile_off(L, b, h, t));
     const int vchunks = kVCols / 8;
-    for (int ch = tid; ch < VROWS * vchunks; ch += 256) {
+    for (int ch = tid; ch < 64 * vchunks; ch += 256) {
       const int d = ch / vchunks, k0 = (ch % vchunks) * 8;
       uint16_t out[8];
       for (int e = 0; e < 8; ++e) {
@@ -227,12 +225,11 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
           const int jj = vt_key_of_col(kappa);
           const int j = t * 64 + jj;
           if (s_valid[jj]) {
-            if (d < 32 * NVB) {
+            if (d < 32) {
               if (d < Dv) val = f32_to_f16_bits(bf16_bits_to_f32(v16[(((size_t)b * N + j) * H + h) * Dv + d]) * kVScale);
-              else if (d < Dv + RCz) val = f32_to_f16_bits(bf16_bits_to_f32(zr16[((size_t)b * N + j) * RCz + (d - Dv)]) * kVScale);
-              else if (d == Dv + RCz) val = 0x3C00;  // fp16 1.0: weight sum
+              else if (d == Dv) val = 0x3C00;  // fp16 1.0: weight sum
             } else {
-              const int dd = d - 32 * NVB;
+              const int dd = d - 32;
               if (dd < 3 * Q) val = hi16(s_x[jj][dd]);
               else if (dd == 3 * Q) val = 0x3C00;  // fp16 1.0: weight sum
               else if (dd <= 3 * Q + 3) val = hi16(s_c[dd - 3 * Q - 1]);
@@ -248,7 +245,29 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
       pk.w = out[6] | ((uint32_t)out[7] << 16);
       reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + k0)[0] = pk;
     }
-    // lifted query rows: [q sq | w_pair * zl * sp | 0] for the tile's residues
+    if (h == 0) {
+      // pair-factor key rows [zr | 0 | pad] and transposed value rows
+      // [zr 2^-8 | 0] of tile (b,t), shared by the heads
+      uint16_t* kz = reinterpret_cast<uint16_t*>(a.ws + ktz_tile_off(L, b, t));
+      const int KZROW = L.KZROW;
+      for (int x = tid; x < 64 * KZROW; x += 256) {
+        const int row = x / KZROW, c = x % KZROW;
+        kz[x] = (s_valid[row] && c < RCz) ? zr16[((size_t)b * N + t * 64 + row) * RCz + c] : (uint16_t)0;
+      }
+      uint16_t* vz = reinterpret_cast<uint16_t*>(a.ws + vtz_tile_off(L, b, t));
+      const int vzn = (int)(vtz_tile_bytes(L) / 2);
+      for (int x = tid; x < vzn; x += 256) {
+        const int d = x / kVCols, kappa = x % kVCols;
+        uint16_t val = 0;
+        if (d < RCz && kappa < 64) {
+          const int jj = vt_key_of_col(kappa);
+          if (s_valid[jj])
+            val = f32_to_f16_bits(bf16_bits_to_f32(zr16[((size_t)b * N + t * 64 + jj) * RCz + d]) * kVScale);
+        }
+        vz[x] = val;
+      }
+    }
+    // lifted query rows: [q sq | 0 | w_pair * zl * sp | 0] for the tile's residues
     uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql);
     const int qchunks = QW / 8;
     for (int ch = tid; ch < 64 * qchunks; ch += 256) {
@@ -261,9 +280,9 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
         if (i < N) {
           if (c < D) {
             val = ld<true>(a.q, (((size_t)b * N + i) * H + h) * D + c) * sq;
-          } else if (c < D + RCz) {
-            const int cc = (c - D) % Cz;
-            val = ld<true>(a.wpair, (size_t)h * Cz + cc) * ld<true>(a.zl, ((size_t)b * N + i) * RCz + (c - D)) * sp;
+          } else if (c >= 16 && c < 16 + RCz) {
+            const int cc = (c - 16) % Cz;
+            val = ld<true>(a.wpair, (size_t)h * Cz + cc) * ld<true>(a.zl, ((size_t)b * N + i) * RCz + (c - 16)) * sp;
           }
         }
         out[e] = f32_to_bf16_bits(val);
@@ -351,19 +370,22 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
 // ---------------------------------------------------------------- vectorised matrix-core lift
 // Same output as lift_kernel<true> for shapes whose D, Dv and Cz are
 // multiples of 8, so that every 8-column chunk of a lifted row comes from one
-// 16-byte piece of one input row.  Every global load of a workgroup is issued
-// up front into registers (one memory latency per workgroup instead of one
-// per loop trip); key and pair rows are then copied with 16-byte stores, the
-// value tile is transposed through LDS, the query rows are scaled and rounded
-// 8 columns at a time, and one thread per key writes that key's geometric
-// columns (their layout is fixed by P at compile time).  LDS rows are padded
-// to odd word strides where lanes walk down a column.  Units (b, t, h) are
-// handed out so that the H heads of one key tile run back to back on one XCD
-// and share its L2 for zr, zl and the frames.
-constexpr int kFastVRows = 160;      // Dv + R Cz <= 32 NVB - 1 <= 159
+// 16-byte piece of one input row.  Per key tile there are H + 1 units: one
+// per head (key rows [k | geometric], value rows [v | points], query rows,
+// query points) and one for the pair-factor rows the heads share (zr key
+// rows, zr value rows).  Every global load of a unit is issued up front into
+// registers (one memory latency per workgroup instead of one per loop trip);
+// rows are then written with 16-byte stores, value tiles are transposed
+// through LDS, the query rows are scaled and rounded 8 columns at a time, and
+// one thread per key writes that key's geometric columns (their layout is
+// fixed by P at compile time).  LDS rows are padded to odd word strides where
+// lanes walk down a column.  Units (b, t, u) are handed out so that the H + 1
+// units of one key tile run back to back on one XCD and share its L2 for zl
+// and the frames.
+constexpr int kFastVRows = 96;       // transposed rows per pass: Dv <= 24 (head unit), R Cz in passes of 96 (pair unit)
 constexpr int kFastVPitch = 66;      // 16-bit elements per transposed LDS row (33 words)
-constexpr int kFastZ = 5;            // 16-byte pieces of a zr / zl tile per thread: 64 R Cz/8 <= 1280
-constexpr int kFastK = 2;            // pieces of a k / v / q tile per thread: 64 D/8 <= 512
+constexpr int kFastZ = 6;            // 16-byte pieces of a zr / zl tile per thread: 64 R Cz/8 <= 1536
+constexpr int kFastK = 1;            // pieces of a k / v / q tile per thread: 64 D/8 <= 256 (D <= 16, Dv <= 24)
 constexpr int kFastPts = 5;          // points per thread: 64 (2P + Q) <= 1280
 constexpr int kFastPc = 4;           // 8-byte point pieces per thread: 64 (6 + 3Q/4) <= 1024
 constexpr int kPrPitch = 13;         // 8-byte pieces per staged point row (odd: rows spread over banks)
@@ -391,7 +413,7 @@ __device__ __forceinline__ uint4 pack8(const uint16_t* v) {
 struct LiftFastArgs {
   int units, per_xcd, pm_vec;
   int pts_vec;  // P = 4 and Q % 4 == 0: points loaded as 8-byte pieces of whole rows
-  FastDiv nz, nk, nv, npc;
+  FastDiv nz, nk, nv, npc, nkz;
 };
 
 // Two floats to packed bf16 (round to nearest even, the hardware conversion).
@@ -402,9 +424,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 static inline bool lift_fast_fits(const Layout& L) {
-  return L.mfma && L.D % 8 == 0 && L.Dv % 8 == 0 && L.Cz % 8 == 0 && L.Dv + L.RCz <= kFastVRows &&
-         L.Cz <= 160 && 64 * (L.RCz / 8) <= 256 * kFastZ && 64 * (L.D / 8) <= 256 * kFastK &&
-         64 * (L.Dv / 8) <= 256 * kFastK && 64 * (2 * L.P + L.Q) <= 256 * kFastPts;
+  return L.mfma && L.D % 8 == 0 && L.Dv % 8 == 0 && L.Cz % 8 == 0 && L.Dv <= kFastVRows && L.Cz <= 192 &&
+         64 * (L.RCz / 8) <= 256 * kFastZ && 64 * (L.D / 8) <= 256 * kFastK && 64 * (L.Dv / 8) <= 256 * kFastK &&
+         64 * (2 * L.P + L.Q) <= 256 * kFastPts;
+}
+
+// Transposed value rows out of LDS: row d of the transposed copy `src`
+// (one 16-bit element per key, pitch kFastVPitch) as 8 column chunks of the
+// tile row (columns k0 .. k0+7 hold keys j0 .. j0+3 and j0+8 .. j0+11,
+// j0 = vt_key_of_col(k0)) plus the 8 zero pad columns 64 .. 71.
+__device__ __forceinline__ void store_vt_rows(uint16_t* vt, const uint16_t (*src)[kFastVPitch], int rows, int tid) {
+  for (int x = tid; x < rows * 9; x += 256) {
+    const int d = x / 9, c = x - 9 * d;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (c < 8) {
+      const int j0 = vt_key_of_col(8 * c);
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(&src[d][0]);
+      val = make_uint4(row[j0 / 2], row[j0 / 2 + 1], row[j0 / 2 + 4], row[j0 / 2 + 5]);
+    }
+    *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * c) = val;
+  }
 }
 
 template <int P>
@@ -415,11 +454,13 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   const int N = L.N, H = L.H, Q = L.Q, D = L.D, Dv = L.Dv, RCz = L.RCz, Cz = L.Cz;
   const int u = (int)(blockIdx.x % 8) * f.per_xcd + (int)(blockIdx.x / 8);
   if (u >= f.units) return;
-  const int h = u % H, t = (u / H) % L.NT, b = u / (H * L.NT);
+  const int h = u % (H + 1), t = (u / (H + 1)) % L.NT, b = u / ((H + 1) * L.NT);
   const int tid = threadIdx.x;
   const int nk = D / 8, nz = RCz / 8, nv = Dv / 8;
   const int QW = L.QW;
   const int npt = 2 * P + Q;
+  const size_t row0 = (size_t)b * N + (size_t)t * 64;     // first residue of the tile
+  const int nrow = min(64, N - t * 64);                    // residues of the tile inside the chain
 
   __shared__ float s_rot[64][9];
   __shared__ float s_tr[64][3];
@@ -428,25 +469,75 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   __shared__ float s_w[64][P3 % 2 ? P3 : P3 + 1];  // b - c (key points, centred), odd row stride
   __shared__ float s_a[64][P3 % 2 ? P3 : P3 + 1];  // a (query points, global), odd row stride
   __shared__ __attribute__((aligned(16))) float s_xT[32][64];  // x - c of valid keys, coordinate-major
-  __shared__ float s_wp[160];          // w_pair[h, :]
-  __shared__ __attribute__((aligned(16))) uint16_t s_vzT[kFastVRows][kFastVPitch];  // [v | zr] 2^-8 (fp16) of valid keys
+  __shared__ float s_wp[192];          // w_pair[h, :]
+  __shared__ __attribute__((aligned(16))) uint16_t s_vzT[kFastVRows][kFastVPitch];  // transposed rows 2^-8 (fp16)
   __shared__ float s_c[4];
   __shared__ float s_gam;
 
-  // ---- 1. every global load of the workgroup.  Addresses: one 64-bit base
-  // per tensor for the tile's first residue (uniform), plus 32-bit offsets
-  // within the tile.
-  const size_t row0 = (size_t)b * N + (size_t)t * 64;     // first residue of the tile
+  if (h == H) {
+    // ---- pair-factor unit: zr key rows [zr | 0 | pad] and transposed value
+    // rows [zr 2^-8 | 0] of tile (b, t), zero for keys that are masked or
+    // past the end
+    const uint4* zrb4 = reinterpret_cast<const uint4*>(a.zr) + row0 * nz;
+    uint4 zr_r[kFastZ];
+#pragma unroll
+    for (int k = 0; k < kFastZ; ++k) {
+      const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+      zr_r[k] = (x < 64 * nz && r < nrow) ? zrb4[r * nz + c] : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 64) s_valid[tid] = tid < nrow && a.mask[row0 + tid] != 0;
+    __syncthreads();
+    const int KZROW = L.KZROW;
+    uint16_t* kz = reinterpret_cast<uint16_t*>(a.ws + ktz_tile_off(L, b, t));
+    auto vh = [](uint16_t bits) { return f32_to_f16_bits(bf16_bits_to_f32(bits) * kVScale); };
+#pragma unroll
+    for (int k = 0; k < kFastZ; ++k) {
+      const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+      if (x < 64 * nz) {
+        if (!s_valid[r]) zr_r[k] = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(kz + (size_t)r * KZROW + 8 * c) = zr_r[k];
+      }
+    }
+    // zero columns [R Cz, KZROW) of the key rows
+    const int nzero = (KZROW - RCz) / 8;
+    for (int x = tid; x < 64 * nzero; x += 256) {
+      const int r = fdiv(x, f.nkz);
+      *reinterpret_cast<uint4*>(kz + (size_t)r * KZROW + RCz + 8 * (x - r * nzero)) = make_uint4(0, 0, 0, 0);
+    }
+    // value rows: zr 2^-8 transposed through LDS, kFastVRows channels a pass
+    uint16_t* vz = reinterpret_cast<uint16_t*>(a.ws + vtz_tile_off(L, b, t));
+    for (int d0 = 0; d0 < RCz; d0 += kFastVRows) {
+#pragma unroll
+      for (int k = 0; k < kFastZ; ++k) {
+        const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+        if (x < 64 * nz && 8 * c >= d0 && 8 * c < d0 + kFastVRows) {
+          const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&zr_r[k]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s_vzT[8 * c + e - d0][r] = vh(e16[e]);
+        }
+      }
+      __syncthreads();
+      store_vt_rows(vz + (size_t)d0 * kVCols, s_vzT, min(kFastVRows, RCz - d0), tid);
+      __syncthreads();
+    }
+    // zero rows [R Cz, VZROWS) and the KiB rounding of the tile
+    const int zrows_end = (int)(vtz_tile_bytes(L) / 16);
+    for (int x = RCz * (kVCols / 8) + tid; x < zrows_end; x += 256)
+      reinterpret_cast<uint4*>(vz)[x] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+
+  // ---- head unit.  1. every global load of the workgroup.  Addresses: one
+  // 64-bit base per tensor for the tile's first residue (uniform), plus
+  // 32-bit offsets within the tile.
   const size_t rh0 = row0 * H + h;                         // its (residue, head) row
   const uint4* kb4 = reinterpret_cast<const uint4*>(a.k) + rh0 * nk;
   const uint4* vb4 = reinterpret_cast<const uint4*>(a.v) + rh0 * nv;
   const uint4* qb4 = reinterpret_cast<const uint4*>(a.q) + rh0 * nk;
-  const uint4* zrb4 = reinterpret_cast<const uint4*>(a.zr) + row0 * nz;
   const uint4* zlb4 = reinterpret_cast<const uint4*>(a.zl) + row0 * nz;
   const uint16_t* kpb = reinterpret_cast<const uint16_t*>(a.kp) + rh0 * (3 * P);
   const uint16_t* qpb = reinterpret_cast<const uint16_t*>(a.qp) + rh0 * (3 * P);
   const uint16_t* vpb = reinterpret_cast<const uint16_t*>(a.vp) + rh0 * (3 * Q);
-  const int nrow = min(64, N - t * 64);                    // residues of the tile inside the chain
   float fr[13];  // threads 0..63: translation, rotation, mask of residue tid
   if (tid < 64) {
     if (tid < nrow) {
@@ -466,13 +557,11 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   const float pwr = ld<true>(a.pwr, h);
   // each loop below covers one tensor, so the lanes of a wavefront never
   // diverge over which tensor a piece comes from
-  uint4 zr_r[kFastZ], zl_r[kFastZ];
+  uint4 zl_r[kFastZ];
 #pragma unroll
   for (int k = 0; k < kFastZ; ++k) {
     const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
-    const bool in = x < 64 * nz && r < nrow;
-    zr_r[k] = in ? zrb4[r * nz + c] : make_uint4(0, 0, 0, 0);
-    zl_r[k] = in ? zlb4[r * nz + c] : make_uint4(0, 0, 0, 0);
+    zl_r[k] = (x < 64 * nz && r < nrow) ? zlb4[r * nz + c] : make_uint4(0, 0, 0, 0);
   }
   uint4 k_r[kFastK], q_r[kFastK], v_r[kFastK];
 #pragma unroll
@@ -501,19 +590,19 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     }
   } else {
 #pragma unroll
-  for (int k = 0; k < kFastPts; ++k) {
-    const int x = tid + 256 * k, r = x % 64, it = x / 64;
-    pts[k][0] = pts[k][1] = pts[k][2] = 0.f;
-    if (x < 64 * npt && r < nrow) {
-      const uint16_t* src;
-      if (it < P) src = kpb + r * H * 3 * P + 3 * it;
-      else if (it < 2 * P) src = qpb + r * H * 3 * P + 3 * (it - P);
-      else src = vpb + r * H * 3 * Q + 3 * (it - 2 * P);
-      pts[k][0] = bf16_bits_to_f32(src[0]);
-      pts[k][1] = bf16_bits_to_f32(src[1]);
-      pts[k][2] = bf16_bits_to_f32(src[2]);
+    for (int k = 0; k < kFastPts; ++k) {
+      const int x = tid + 256 * k, r = x % 64, it = x / 64;
+      pts[k][0] = pts[k][1] = pts[k][2] = 0.f;
+      if (x < 64 * npt && r < nrow) {
+        const uint16_t* src;
+        if (it < P) src = kpb + r * H * 3 * P + 3 * it;
+        else if (it < 2 * P) src = qpb + r * H * 3 * P + 3 * (it - P);
+        else src = vpb + r * H * 3 * Q + 3 * (it - 2 * P);
+        pts[k][0] = bf16_bits_to_f32(src[0]);
+        pts[k][1] = bf16_bits_to_f32(src[1]);
+        pts[k][2] = bf16_bits_to_f32(src[2]);
+      }
     }
-  }
   }
 
   // ---- 2. frames, validity and the tile centroid (wavefront 0)
@@ -546,8 +635,8 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       s_gam = 0.5f * softplus_f(pwr) * sqrtf(2.0f / (27.0f * (float)P));
     }
   }
-  // raw point rows in LDS (the value-tile staging array is free until the
-  // points are done): row r at s_praw + kPrPitch r, as bf16 [kp | qp | vp]
+  // raw point rows in LDS (the transposition array is free until the points
+  // are done): row r at s_praw + kPrPitch r, as bf16 [kp | qp | vp]
   uint2* s_praw = reinterpret_cast<uint2*>(&s_vzT[0][0]);
   if (P == 4 && f.pts_vec) {
 #pragma unroll
@@ -586,10 +675,9 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   // key tiles without a valid key and writes padding queries as zeros
   const bool tile_any = (s_vmask[0] | s_vmask[1]) != 0u;
   if (tile_any) {
-    // ---- 3. points, then [k | zr] straight into the key tile and [v | zr]
-    // transposed into LDS
-    // global points: key points (centred), query points, value points (centred,
-    // zero for keys that are masked or past the end)
+    // ---- 3. points, then k straight into the key rows and v transposed
+    // into LDS.  Global points: key points (centred), query points, value
+    // points (centred, zero for keys that are masked or past the end)
 #pragma unroll
     for (int k = 0; k < kFastPts; ++k) {
       const int x = tid + 256 * k, r = x % 64, it = x / 64;
@@ -629,18 +717,6 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     uint16_t* kt = reinterpret_cast<uint16_t*>(a.ws + kt_tile_off(L, b, h, t));
     auto vh = [](uint16_t bits) { return f32_to_f16_bits(bf16_bits_to_f32(bits) * kVScale); };
 #pragma unroll
-    for (int k = 0; k < kFastZ; ++k) {
-      const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
-      if (x < 64 * nz) {
-        const uint4 val = s_valid[r] ? zr_r[k] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(kt + (size_t)r * L.KROW + D + 8 * c) = val;
-        // value-tile entries: fp16 of the bf16 input times 2^-8
-        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&val);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_vzT[Dv + 8 * c + e][r] = vh(e16[e]);
-      }
-    }
-#pragma unroll
     for (int k = 0; k < kFastK; ++k) {
       const int x = tid + 256 * k;
       const int rk = fdiv(x, f.nk), ck = x - rk * nk;
@@ -654,7 +730,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
         for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][rv] = vh(e16[e]);
       }
     }
-    // lifted query rows [q sq | w_pair zl sp | 0]
+    // lifted query rows [q sq | 0 | w_pair zl sp | 0]
     {
       const float sq = kLog2e / sqrtf(3.0f * (float)D);
       const float sp = kLog2e / sqrtf(3.0f);
@@ -670,7 +746,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
           pk.y = pack_bf16x2(wp[2] * bf16_bits_to_f32(e16[2]) * sp, wp[3] * bf16_bits_to_f32(e16[3]) * sp);
           pk.z = pack_bf16x2(wp[4] * bf16_bits_to_f32(e16[4]) * sp, wp[5] * bf16_bits_to_f32(e16[5]) * sp);
           pk.w = pack_bf16x2(wp[6] * bf16_bits_to_f32(e16[6]) * sp, wp[7] * bf16_bits_to_f32(e16[7]) * sp);
-          *reinterpret_cast<uint4*>(ql + (size_t)r * QW + D + 8 * c) = pk;
+          *reinterpret_cast<uint4*>(ql + (size_t)r * QW + 16 + 8 * c) = pk;
         }
       }
 #pragma unroll
@@ -686,19 +762,22 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
           *reinterpret_cast<uint4*>(ql + (size_t)r * QW + 8 * c) = pk;
         }
       }
-      // zero columns [D + R Cz, QW)
-      const int nzero = (QW - D - RCz) / 8;
-      for (int x = tid; x < 64 * nzero; x += 256)
-        *reinterpret_cast<uint4*>(ql + (size_t)(x / nzero) * QW + D + RCz + 8 * (x % nzero)) = make_uint4(0, 0, 0, 0);
+      // zero columns [D, 16) and [16 + R Cz, QW)
+      const int nz0 = (16 - D) / 8, nz1 = (QW - 16 - RCz) / 8, nzt = nz0 + nz1;
+      if (nzt > 0)
+        for (int x = tid; x < 64 * nzt; x += 256) {
+          const int r = x / nzt, c = x - r * nzt;
+          const int col = c < nz0 ? D + 8 * c : 16 + RCz + 8 * (c - nz0);
+          *reinterpret_cast<uint4*>(ql + (size_t)r * QW + col) = make_uint4(0, 0, 0, 0);
+        }
     }
     __syncthreads();
 
-    // ---- 4. key rows past [k | zr] (one thread per key): zeros up to QW, the
+    // ---- 4. key rows past k (one thread per key): zeros up to 16, the
     // geometric columns (layout in common.h), 8 pad columns
-    const int VROWS = L.VROWS, NVB = L.NVB, DZ = Dv + RCz;
     {
       // every wavefront: lane = key, chunks w, w + 4, ... of the 16 GS + 8
-      // columns after QW; each lane recomputes its key's point sums
+      // columns after 16; each lane recomputes its key's point sums
       const int r = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
       const bool valid = s_valid[r] != 0;
       float w[P3];
@@ -714,7 +793,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       const float ww[3] = {2.f * gl * Wx, 2.f * gl * Wy, 2.f * gl * Wz};
       uint16_t* krow = kt + (size_t)r * L.KROW;
       if (wv == 0)
-        for (int c = D + RCz; c < QW; c += 8) *reinterpret_cast<uint4*>(krow + c) = make_uint4(0, 0, 0, 0);
+        for (int c = D; c < 16; c += 8) *reinterpret_cast<uint4*>(krow + c) = make_uint4(0, 0, 0, 0);
       constexpr int base = 16 * (GS - 1);
       constexpr int NCH = (16 * GS + 8) / 8;
       // value of geometric column g of this key (layout in common.h)
@@ -742,7 +821,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
         uint16_t g16[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) g16[e] = geo(8 * c + e);
-        *reinterpret_cast<uint4*>(krow + QW + 8 * c) = pack8(g16);
+        *reinterpret_cast<uint4*>(krow + 16 + 8 * c) = pack8(g16);
       }
     }
     // query global points: 16 floats per (b, h, i)
@@ -754,27 +833,19 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       for (int e = 0; e < 4; ++e) v[e] = (row < nrow && c + e < P3) ? s_a[row][c + e] : 0.f;
       qa[tid] = make_float4(v[0], v[1], v[2], v[3]);
     }
-    // transposed value tile: rows d, columns kappa; columns k0 .. k0+7 hold keys
-    // j0 .. j0+3 and j0+8 .. j0+11 (j0 = vt_key_of_col(k0)), columns 64 .. 71 are zero
+    // head value rows, transposed: rows [0, Dv) from the LDS copy of v, the
+    // rest computed (ones rows, centred value points, centroid)
     uint16_t* vt = reinterpret_cast<uint16_t*>(a.ws + vt_tile_off(L, b, h, t));
+    store_vt_rows(vt, s_vzT, Dv, tid);
     const uint32_t vm0 = s_vmask[0], vm1 = s_vmask[1];
-    // rows [v | zr]: 8 column chunks each, straight from the transposed LDS copy
-    for (int x = tid; x < DZ * 8; x += 256) {
-      const int d = x >> 3, j0 = vt_key_of_col(8 * (x & 7));
-      const uint32_t* row = reinterpret_cast<const uint32_t*>(&s_vzT[d][0]);
-      *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * (x & 7)) =
-          make_uint4(row[j0 / 2], row[j0 / 2 + 1], row[j0 / 2 + 4], row[j0 / 2 + 5]);
-    }
-    // the other rows: the weight-sum row, zero rows, centred value points, the
-    // ones row and the centroid (valid keys only)
-    for (int x = tid; x < (VROWS - DZ) * 8; x += 256) {
-      const int d = DZ + (x >> 3), j0 = vt_key_of_col(8 * (x & 7));
+    for (int x = tid; x < (64 - Dv) * 8; x += 256) {
+      const int d = Dv + (x >> 3), j0 = vt_key_of_col(8 * (x & 7));
       // valid bits of the 8 keys, in column order
       const uint32_t word = j0 < 32 ? vm0 : vm1;
       const uint32_t bits = ((word >> (j0 & 31)) & 0xFu) | (((word >> ((j0 & 31) + 8)) & 0xFu) << 4);
       uint16_t one = 0;
-      const int dd = d - 32 * NVB;
-      if (d == DZ) one = 0x3C00;                          // fp16 1.0: weight sum
+      const int dd = d - 32;
+      if (d == Dv) one = 0x3C00;                          // fp16 1.0: weight sum
       else if (dd == 3 * Q) one = 0x3C00;                 // fp16 1.0: weight sum
       else if (dd > 3 * Q && dd <= 3 * Q + 3) one = hi16(s_c[dd - 3 * Q - 1]);  // centroid
       uint16_t out[8];
@@ -789,8 +860,8 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       }
       *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 8 * (x & 7)) = pack8(out);
     }
-    // pad columns 64 .. 71 of every row
-    for (int d = tid; d < VROWS; d += 256)
+    // pad columns 64 .. 71 of the computed rows
+    for (int d = Dv + tid; d < 64; d += 256)
       *reinterpret_cast<uint4*>(vt + (size_t)d * kVCols + 64) = make_uint4(0, 0, 0, 0);
   }
 
@@ -850,7 +921,7 @@ hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStre
                         reinterpret_cast<uintptr_t>(in->zr)) % 16 == 0;
   if (aligned && lift_fast_fits(L)) {
     LiftFastArgs f;
-    f.units = L.B * L.NT * L.H;
+    f.units = L.B * L.NT * (L.H + 1);
     f.per_xcd = (f.units + 7) / 8;
     f.pm_vec = in->pair_mask != nullptr && L.N % 16 == 0 && reinterpret_cast<uintptr_t>(in->pair_mask) % 16 == 0;
     f.nz = make_fastdiv(L.RCz / 8);
@@ -858,6 +929,7 @@ hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStre
     f.nv = make_fastdiv(L.Dv / 8);
     f.pts_vec = L.P == 4 && L.Q % 4 == 0 && 6 + 3 * L.Q / 4 <= kPrPitch;
     f.npc = make_fastdiv(6 + 3 * L.Q / 4);
+    f.nkz = make_fastdiv((L.KZROW - L.RCz) / 8 > 0 ? (L.KZROW - L.RCz) / 8 : 1);
     const dim3 g(8 * f.per_xcd), blk(256);
     switch (L.P) {
       case 1: hipLaunchKernelGGL(lift_fast_kernel<1>, g, blk, 0, st, a, f); break;

@@ -1,6 +1,8 @@
 // MFMA fragment code of the fused kernel, shared with the diagnostic logit
-// kernel so that both evaluate every logit with the identical instruction
-// sequence (and hence bit-identical results).
+// kernel so that both evaluate every logit with the identical sequence of
+// matrix instructions on the same operands (the diagnostic kernel passes a
+// running maximum of zero, so only the rounding of the per-tile row term
+// differs between the two).
 #pragma once
 
 #include "common.h"
@@ -156,26 +158,36 @@ __device__ __forceinline__ void geo_tile(const QueryGeo& qg, float4 ct, float gl
 }
 
 // S^T for one 64-key tile: sacc[kb] (keys kb*32 .. +31) x 32 queries.
-// ktile points at 64 rows of KROW 16-bit elements (LDS or global memory).
-// The two key blocks are interleaved so consecutive MFMAs are independent,
-// and the operand fragments are fetched DEPTH K-steps ahead of their MFMA so
-// that the reads' latency hides behind the preceding MFMAs.  s_tile_ops
-// emits the reads and MFMAs only; the caller orders them (s_tile_sched), so
-// that other work can be placed between them.
+// khead points at the tile's 64 head rows of KROW = 16 + 16 GS + pad 16-bit
+// elements ([k | geometric | pad]), kpair at its 64 shared pair-factor rows
+// of KZROW = 16 (NQS - 1) + pad elements (LDS or global memory).  K-step 0
+// is the scalar part, K-steps 1 .. NQS-1 the pair part, then GS geometric
+// K-steps.  The two key blocks are interleaved so consecutive MFMAs are
+// independent, and the operand fragments are fetched DEPTH K-steps ahead of
+// their MFMA so that the reads' latency hides behind the preceding MFMAs.
+// s_tile_ops emits the reads and MFMAs only; the caller orders them
+// (s_tile_sched), so that other work can be placed between them.
 template <int NQS, int GS, int DEPTH>
-__device__ __forceinline__ void s_tile_ops(const char* ktile, const bf16x8_t* bq, const f16x8_t* bg, int l32, int half,
-                                           f32x16_t* sacc) {
-  constexpr int QW = 16 * NQS;
-  constexpr int KROW = QW + 16 * GS + kRowPad;
+__device__ __forceinline__ void s_tile_ops(const char* khead, const char* kpair, const bf16x8_t* bq,
+                                           const f16x8_t* bg, int l32, int half, f32x16_t* sacc) {
+  constexpr int KROW = 16 + 16 * GS + kRowPad;
+  constexpr int KZROW = 16 * (NQS - 1) + kRowPad;
   constexpr int NS = NQS + GS;
-  const char* k0 = ktile + (size_t)(l32 * KROW) * 2 + half * 16;
-  const char* k1 = k0 + (size_t)(32 * KROW) * 2;
-  auto off = [](int st) { return st < NQS ? st * 32 : (QW + (st - NQS) * 16) * 2; };
+  const char* h0 = khead + (size_t)(l32 * KROW) * 2 + half * 16;
+  const char* h1 = h0 + (size_t)(32 * KROW) * 2;
+  const char* z0 = kpair + (size_t)(l32 * KZROW) * 2 + half * 16;
+  const char* z1 = z0 + (size_t)(32 * KZROW) * 2;
+  // fragment of K-step st for key block kb
+  auto frag = [&](int st, int kb) {
+    const char* p = st == 0 ? (kb ? h1 : h0)
+                            : (st < NQS ? (kb ? z1 : z0) + (st - 1) * 32 : (kb ? h1 : h0) + (16 + (st - NQS) * 16) * 2);
+    return *reinterpret_cast<const uint4*>(p);
+  };
   uint4 f0[DEPTH], f1[DEPTH];
 #pragma unroll
   for (int st = 0; st < DEPTH && st < NS; ++st) {
-    f0[st] = *reinterpret_cast<const uint4*>(k0 + off(st));
-    f1[st] = *reinterpret_cast<const uint4*>(k1 + off(st));
+    f0[st] = frag(st, 0);
+    f1[st] = frag(st, 1);
   }
   sacc[0] = f32x16_t{};
   sacc[1] = f32x16_t{};
@@ -183,8 +195,8 @@ __device__ __forceinline__ void s_tile_ops(const char* ktile, const bf16x8_t* bq
   for (int st = 0; st < NS; ++st) {
     const uint4 c0 = f0[st % DEPTH], c1 = f1[st % DEPTH];
     if (st + DEPTH < NS) {
-      f0[st % DEPTH] = *reinterpret_cast<const uint4*>(k0 + off(st + DEPTH));
-      f1[st % DEPTH] = *reinterpret_cast<const uint4*>(k1 + off(st + DEPTH));
+      f0[st % DEPTH] = frag(st + DEPTH, 0);
+      f1[st % DEPTH] = frag(st + DEPTH, 1);
     }
     if (st < NQS) {
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c0), bq[st], sacc[0], 0, 0, 0);
@@ -211,9 +223,9 @@ __device__ __forceinline__ void s_tile_sched() {
 }
 
 template <int NQS, int GS, int DEPTH = 3>
-__device__ __forceinline__ void s_tile(const char* ktile, const bf16x8_t* bq, const f16x8_t* bg, int l32, int half,
-                                       f32x16_t* sacc) {
-  s_tile_ops<NQS, GS, DEPTH>(ktile, bq, bg, l32, half, sacc);
+__device__ __forceinline__ void s_tile(const char* khead, const char* kpair, const bf16x8_t* bq, const f16x8_t* bg,
+                                       int l32, int half, f32x16_t* sacc) {
+  s_tile_ops<NQS, GS, DEPTH>(khead, kpair, bq, bg, l32, half, sacc);
   s_tile_sched<NQS + GS, DEPTH, 0>();
 }
 

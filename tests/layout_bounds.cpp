@@ -6,7 +6,11 @@
 //     lane reads inside the tile, writes inside the KiB-rounded LDS buffer,
 //     every byte of the tile is copied to the same offset, and a lane whose
 //     read is clamped to the tile's last 16 bytes writes past the tile (it
-//     never overwrites tile data).
+//     never overwrites tile data).  For the fused kernel's four-part tiles
+//     (head key rows, shared pair-factor key rows, head value rows, shared
+//     pair-factor value rows): every chunk is read inside its part, every
+//     LDS byte of the buffer is written exactly from its part, and the
+//     operand reads of the key and value products stay inside their parts.
 //  2. Address join: a 64-bit address rebuilt from its two 32-bit halves is
 //     the address itself, also when bit 31 of the low half is set.  Joining
 //     an int low half instead sign-extends it and fills the high word with
@@ -71,13 +75,75 @@ static void check_copy_inst(const char* what) {
   check_copy(BYTES, W, dma_per_wave<BYTES, W>(), what);
 }
 
+// The part sizes of flash_mfma_kernel<NQS, NVB, GS, W> (TileDims there).
+template <int NQS, int NVB, int GS>
+struct FusedParts {
+  static constexpr int KH = 64 * (16 + 16 * GS + kRowPad) * 2;
+  static constexpr int KZ = 64 * (16 * (NQS - 1) + kRowPad) * 2;
+  static constexpr int VH = 64 * kVCols * 2;
+  static constexpr int VZ = (32 * (NVB - 1) * kVCols * 2 + 1023) / 1024 * 1024;
+};
+
+static void check_parts(const int* bytes, int W, int per_wave, const char* what) {
+  int C = 0, start[5];
+  for (int p = 0; p < 4; ++p) {
+    CHECK(bytes[p] % 1024 == 0 && bytes[p] > 0, "%s: part %d of %d bytes", what, p, bytes[p]);
+    start[p] = C;
+    C += bytes[p] / 1024;
+  }
+  start[4] = C;
+  CHECK(per_wave == (C + W - 1) / W, "%s: %d copies per wave", what, per_wave);
+  std::vector<int> hit(C * 1024, 0);
+  for (int w = 0; w < W; ++w)
+    for (int k = 0; k < per_wave; ++k) {
+      const int c = w + W * k < C ? w + W * k : C - 1;  // as in dma_parts
+      const int p = dma_part_of_chunk(c, start[1], start[2] - start[1], start[3] - start[2]);
+      CHECK(c >= start[p] && c < start[p + 1], "%s: chunk %d in part %d", what, c, p);
+      for (int lane = 0; lane < 64; ++lane) {
+        const uint32_t src = (uint32_t)(c - start[p]) * 1024u + 16u * lane, dst = (uint32_t)c * 1024u + 16u * lane;
+        CHECK(src + 16 <= (uint32_t)bytes[p], "%s: read %u of part %d (%d bytes)", what, src, p, bytes[p]);
+        CHECK(dst + 16 <= (uint32_t)C * 1024u, "%s: write %u", what, dst);
+        CHECK(dst - (uint32_t)start[p] * 1024u == src, "%s: part %d lands at its place", what, p);
+        for (int e = 0; e < 16; ++e) hit[dst + e] = 1;
+      }
+    }
+  for (int x = 0; x < C * 1024; ++x) CHECK(hit[x], "%s: LDS byte %d never written", what, x);
+}
+
 template <int NQS, int NVB, int GS, int W>
 static void check_fused_inst() {
-  // the tile sizes of flash_mfma_kernel<NQS, NVB, GS, W>
-  constexpr int KT_BYTES = 64 * (16 * NQS + 16 * GS + kRowPad) * 2;
-  constexpr int VT_BYTES = 32 * (NVB + 1) * kVCols * 2;
-  check_copy_inst<KT_BYTES, W>("fused key tile");
-  check_copy_inst<VT_BYTES, W>("fused value tile");
+  using T = FusedParts<NQS, NVB, GS>;
+  const int parts[4] = {T::KH, T::KZ, T::VH, T::VZ};
+  constexpr int TB = T::KH + T::KZ + T::VH + T::VZ;
+  check_parts(parts, W, dma_per_wave<TB, W>(), "fused tile");
+  CHECK(2 * TB <= 160 * 1024, "fused tile buffers %d bytes", 2 * TB);
+  // key operand reads (s_tile_ops): lane (l32, half), key block kb; head
+  // part at row pitch 16 + 16 GS + pad, pair part at 16 (NQS - 1) + pad
+  constexpr int KROW = 16 + 16 * GS + kRowPad, KZROW = 16 * (NQS - 1) + kRowPad;
+  for (int st = 0; st < NQS + GS; ++st)
+    for (int kb = 0; kb < 2; ++kb)
+      for (int l32 : {0, 31})
+        for (int half = 0; half < 2; ++half) {
+          const int row = 32 * kb + l32;
+          if (st >= 1 && st < NQS) {
+            const int off = row * KZROW * 2 + half * 16 + (st - 1) * 32;
+            CHECK(off >= 0 && off + 16 <= T::KZ, "pair key read %d of %d", off, T::KZ);
+            CHECK((st - 1) * 16 + half * 8 + 8 <= 16 * (NQS - 1), "pair key column past the pair part");
+          } else {
+            const int col = st == 0 ? half * 8 : 16 + (st - NQS) * 16 + half * 8;
+            const int off = row * KROW * 2 + col * 2;
+            CHECK(off + 16 <= T::KH && col + 8 <= 16 + 16 * GS, "head key read %d of %d", off, T::KH);
+          }
+        }
+  // value operand reads (pv_tile_ops): block vb, K-step ks, lane (l32, half)
+  for (int vb = 0; vb <= NVB; ++vb)
+    for (int ks = 0; ks < 4; ++ks)
+      for (int l32 : {0, 31})
+        for (int half = 0; half < 2; ++half) {
+          const int off = (l32 * kVCols) * 2 + half * 16 + vb * 32 * kVCols * 2 + ks * 32;
+          CHECK(off + 16 <= T::VH + T::VZ, "value read %d of %d", off, T::VH + T::VZ);
+          CHECK((ks * 32 + half * 16) / 2 + 8 <= 64, "value read past the 64 key columns");
+        }
 }
 
 template <int NQS>
@@ -148,9 +214,11 @@ static void check_layout(const ipa_shape& s, int with_pm) {
   CHECK(L.NKpad == NT * 64 && L.NKpad <= L.NQpad, "%s: padded rows", tag);
   // region order and sizes
   const Region reg[] = {
-      {"QL", L.off_ql, L.off_qa}, {"QA", L.off_qa, L.off_kt},   {"KT", L.off_kt, L.off_vt},
-      {"VT", L.off_vt, L.off_ck}, {"CK", L.off_ck, L.off_gam},  {"GAM", L.off_gam, L.off_km},
-      {"KM", L.off_km, L.off_part}, {"PART", L.off_part, L.off_pm}, {"PM", L.off_pm, L.total}};
+      {"QL", L.off_ql, L.off_qa},   {"QA", L.off_qa, L.off_kt},       {"KT", L.off_kt, L.off_vt},
+      {"VT", L.off_vt, L.off_ktz},  {"KTZ", L.off_ktz, L.off_vtz},    {"VTZ", L.off_vtz, L.off_ck},
+      {"CK", L.off_ck, L.off_gam},  {"GAM", L.off_gam, L.off_km},     {"KM", L.off_km, L.off_part},
+      {"PART", L.off_part, L.off_pm}, {"PM", L.off_pm, L.total}};
+  enum { rQL, rQA, rKT, rVT, rKTZ, rVTZ, rCK, rGAM, rKM, rPART, rPM };
   CHECK(L.off_ql >= sizeof(Header), "%s: header", tag);
   for (const Region& r : reg) CHECK(r.start <= r.end && r.start % 256 == 0, "%s: region %s", tag, r.name);
   auto inside = [&](const Region& r, size_t off, size_t bytes, const char* what) {
@@ -163,30 +231,37 @@ static void check_layout(const ipa_shape& s, int with_pm) {
   for (int b : {0, B - 1})
     for (int h : {0, H - 1}) {
       for (int t : {0, NT - 1}) {
-        inside(reg[2], kt_tile_off(L, b, h, t), ktb, "key tile");
-        inside(reg[3], vt_tile_off(L, b, h, t), vtb, "value tile");
+        inside(reg[rKT], kt_tile_off(L, b, h, t), ktb, "key tile");
+        inside(reg[rVT], vt_tile_off(L, b, h, t), vtb, "value tile");
+        if (L.mfma) {
+          inside(reg[rKTZ], ktz_tile_off(L, b, t), ktz_tile_bytes(L), "pair key tile");
+          inside(reg[rVTZ], vtz_tile_off(L, b, t), vtz_tile_bytes(L), "pair value tile");
+        }
       }
       // the lift writes query rows of every key-tile residue (< NKpad), the
       // fused kernel reads rows < N
       for (int i : {0, L.N - 1, L.NKpad - 1, L.NQpad - 1}) {
-        inside(reg[0], ql_row_off(L, b, h, i), (size_t)L.QW * e, "query row");
-        inside(reg[1], qa_row_off(L, b, h, i), 64, "query points");
+        inside(reg[rQL], ql_row_off(L, b, h, i), (size_t)L.QW * e, "query row");
+        inside(reg[rQA], qa_row_off(L, b, h, i), 64, "query points");
       }
     }
   for (int b : {0, B - 1})
     for (int t : {0, NT - 1}) {
-      inside(reg[4], ck_off(L, b, t), 16, "centroid");
-      for (int hf = 0; hf < 2; ++hf) inside(reg[6], km_word_off(L, b, t, hf), 4, "key-mask word");
+      inside(reg[rCK], ck_off(L, b, t), 16, "centroid");
+      for (int hf = 0; hf < 2; ++hf) inside(reg[rKM], km_word_off(L, b, t, hf), 4, "key-mask word");
       if (with_pm)
         for (int i : {0, L.NQpad - 1})
-          for (int hf = 0; hf < 2; ++hf) inside(reg[8], pm_word_off(L, b, i, t, hf), 4, "pair-mask word");
+          for (int hf = 0; hf < 2; ++hf) inside(reg[rPM], pm_word_off(L, b, i, t, hf), 4, "pair-mask word");
     }
-  inside(reg[5], L.off_gam, (size_t)H * 4, "point weights");
+  inside(reg[rGAM], L.off_gam, (size_t)H * 4, "point weights");
   if (L.mfma) {
-    // the tile sizes of the fused kernel instance picked for this layout
-    const size_t KT_BYTES = 64 * (size_t)(16 * L.NQS + 16 * L.GS + kRowPad) * 2;
-    const size_t VT_BYTES = 32 * (size_t)(L.NVB + 1) * kVCols * 2;
-    CHECK(ktb == KT_BYTES && vtb == VT_BYTES, "%s: tile bytes %zu %zu vs %zu %zu", tag, ktb, vtb, KT_BYTES, VT_BYTES);
+    // the part sizes of the fused kernel instance picked for this layout
+    const size_t KH = 64 * (size_t)(16 + 16 * L.GS + kRowPad) * 2, KZ = 64 * (size_t)(16 * (L.NQS - 1) + kRowPad) * 2;
+    const size_t VH = 64 * (size_t)kVCols * 2, VZ = (32 * (size_t)(L.NVB - 1) * kVCols * 2 + 1023) / 1024 * 1024;
+    CHECK(ktb == KH && vtb == VH && ktz_tile_bytes(L) == KZ && vtz_tile_bytes(L) == VZ, "%s: tile part bytes", tag);
+    // the columns and rows the lift fills fit the parts
+    CHECK(L.D <= 16 && L.RCz <= 16 * (L.NQS - 1) && L.RCz <= L.VZROWS && L.Dv + 1 <= 32 && 3 * L.Q + 4 <= 32,
+          "%s: widths vs instance", tag);
     // packed w_out of the epilogue (per head or transposed), in the
     // epilogue's own workspace
     const size_t wt = (size_t)L.H * L.Cout * kHeadFeatPitch * 2, wt2 = (size_t)L.Cout * L.FP * 2;
@@ -199,7 +274,7 @@ static void check_layout(const ipa_shape& s, int with_pm) {
     }
     if (L.KS > 1)
       for (int i : {0, L.NQpad - 1})
-        inside(reg[7], part_rec_off(L, L.KS - 1, B - 1, H - 1, i), (size_t)L.PREC * 4, "partial record");
+        inside(reg[rPART], part_rec_off(L, L.KS - 1, B - 1, H - 1, i), (size_t)L.PREC * 4, "partial record");
     CHECK(L.PREC >= L.DO + 4 && L.PREC % 4 == 0, "%s: PREC", tag);
     // workgroup remap of the fused kernel (8 or 4 wavefronts per workgroup)
     for (int W : {4, 8}) {
