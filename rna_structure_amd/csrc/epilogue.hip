@@ -377,8 +377,12 @@ __global__ __launch_bounds__(RPW * 8) void epilogue_mfma_kernel(EpiArgs a) {
 // cache lines), build its 112 features in LDS, and the wavefronts multiply
 // them by W_h on MFMA.  O is loaded two heads ahead, W_h one head ahead.
 constexpr int kHeadCoutMax = 128;
+// The per-head kernel: Dv = 16, Cz = 64, Q = 8 (112 features per head, for
+// any rank R of the pair factors: the pair expansion contracts r), R = 1..3;
+// any Cout in 32 .. 128 for R = 2, Cout = 128 for R = 1 and 3.
 __host__ __device__ __forceinline__ bool head_path(const Layout& L) {
-  return L.mfma && fast_dims(L) && L.Cout % 32 == 0 && L.Cout <= kHeadCoutMax;
+  if (!(L.mfma && L.Dv == kFDv && L.Cz == kFCz && L.Q == kFQ && L.R >= 1 && L.R <= 3)) return false;
+  return L.R == 2 ? (L.Cout % 32 == 0 && L.Cout <= kHeadCoutMax) : L.Cout == 128;
 }
 
 // wh[h][c][k] = w_out[f(h, k)][c] (bf16 bits), zero in the pitch padding.
@@ -402,8 +406,16 @@ __global__ __launch_bounds__(256) void pack_wout_heads_kernel(const uint16_t* w,
 
 // HT > 0: H = HT at compile time (the head loop is unrolled completely, and
 // the compiler's waits for the O loads then follow the two-head prefetch).
-template <int M, int COUT, int HT>
+// R: rank of the pair factors.  The attention-output row of a (residue, head)
+// is DO = 16 + 64 R + 24 floats = 4 + 16 R + 6 pieces of 16 bytes; lane j of
+// the residue's 8 loads pieces j, j + 8, .., i.e. NPC = 2 R + 2 of them:
+// scalar pieces 0..3 (lanes 0..3, k = 0), pair chunk c of rank r at piece
+// 4 + 16 r + c, point pieces 4 + 16 R .. 9 + 16 R (lanes 4..7 at k = 2 R,
+// lanes 0, 1 at k = 2 R + 1).
+template <int M, int COUT, int HT, int R>
 __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
+  constexpr int DOR = kFDv + R * kFCz + 3 * kFQ;        // floats per attention-output row
+  constexpr int NPC = 2 * R + 2;                         // 16-byte pieces per lane
   constexpr int NT_ = 8 * M;  // threads
   constexpr int NW = NT_ / 64;
   constexpr int KP = kHeadFeatPitch;
@@ -441,10 +453,12 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
   const bool empty = s_empty[r] != 0;  // also true past the end
 
   // per-residue constants, the same for every head: frame, and the zl values
-  // of this lane's two pair chunks (chunks qa, qb of 4 channels)
+  // of this lane's two pair chunks (chunks qa, qb of 4 channels) for every r
   float Rm[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, tr[3] = {0.f, 0.f, 0.f};
   const int qa = j >= 4 ? j - 4 : j + 12, qb = j + 4;
-  uint2 zla0 = make_uint2(0, 0), zla1 = make_uint2(0, 0), zlb0 = make_uint2(0, 0), zlb1 = make_uint2(0, 0);
+  uint2 zla[R], zlb[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) zla[rr] = zlb[rr] = make_uint2(0, 0);
   if (!empty) {
     const uint16_t* rt = reinterpret_cast<const uint16_t*>(a.rot) + (size_t)row * 9;
     const uint16_t* tt = reinterpret_cast<const uint16_t*>(a.trans) + (size_t)row * 3;
@@ -452,9 +466,12 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
     for (int e = 0; e < 9; ++e) Rm[e] = bf16_bits_to_f32(rt[e]);
 #pragma unroll
     for (int e = 0; e < 3; ++e) tr[e] = bf16_bits_to_f32(tt[e]);
-    const uint2* z2 = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.zl) + (size_t)row * kFR * kFCz);
-    zla0 = z2[qa]; zla1 = z2[16 + qa];  // channel 4q of r = 0 and r = 1
-    zlb0 = z2[qb]; zlb1 = z2[16 + qb];
+    const uint2* z2 = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.zl) + (size_t)row * R * kFCz);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      zla[rr] = z2[16 * rr + qa];  // channels 4 qa .. 4 qa + 3 of rank rr
+      zlb[rr] = z2[16 * rr + qb];
+    }
   }
   // W_h straight into LDS buffer h&1 (direct copies, waited for explicitly);
   // O of a head: this lane's 16-byte pieces j, j+8, ..., j+40 of the
@@ -464,9 +481,9 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
   auto copy_w = [&](int h) { dma_tile<WBYTES, NW>(whg + (size_t)h * WBYTES, sW + (h & 1) * WLDS, w, lane); };
   const int rowc = min(row, total - 1);
   auto load_o = [&](int h, float4* v) {
-    const float4* o4 = reinterpret_cast<const float4*>(a.o + ((size_t)rowc * H + h) * kFDO);
+    const float4* o4 = reinterpret_cast<const float4*>(a.o + ((size_t)rowc * H + h) * DOR);
 #pragma unroll
-    for (int k = 0; k < 6; ++k) v[k] = o4[min(j + 8 * k, kFDO / 4 - 1)];
+    for (int k = 0; k < NPC; ++k) v[k] = o4[min(j + 8 * k, DOR / 4 - 1)];
   };
   auto zl4 = [](uint2 u, int e) {
     const uint32_t wd = (e >> 1) ? u.y : u.x;
@@ -479,13 +496,13 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
   // head h: O in cur (loaded two heads ahead), W_h in LDS buffer h&1 (copy
   // issued one head ahead); issues the copy of W_(h+1), then O of head h+2
   // into nb
-  auto step = [&](int h, float4(&cur)[6], float4(&nb)[6]) {
+  auto step = [&](int h, float4(&cur)[NPC], float4(&nb)[NPC]) {
     if (h + 1 < H) copy_w(h + 1);
     if (h + 2 < H) load_o(h + 2, nb);
     // ---- features of head h for residue r (8 lanes); an empty row's O is zero
     if (empty) {
 #pragma unroll
-      for (int k = 0; k < 6; ++k) cur[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < NPC; ++k) cur[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (j < 4) {  // scalar: piece j
       uint2 u;
@@ -494,16 +511,20 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
       *reinterpret_cast<uint2*>(frow + 4 * j) = u;
     }
     {
-      // pair chunk qa: pieces 4+qa (r=0) and 20+qa (r=1); chunk qb: 4+qb, 20+qb
-      const float4& a0 = j >= 4 ? cur[0] : cur[2];
-      const float4& a1 = j >= 4 ? cur[2] : cur[4];
-      const float4& b0 = cur[1];
-      const float4& b1 = cur[3];
-      float pa[4], pb[4];
+      // pair chunk qa of rank r: piece 4 + 16 r + qa, i.e. k = 2 r (lanes 4..7)
+      // or 2 r + 2 (lanes 0..3); chunk qb: piece 8 + 16 r + j, k = 2 r + 1
+      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pa[e] = fmaf(zl4(zla1, e), f4(a1, e), zl4(zla0, e) * f4(a0, e));
-        pb[e] = fmaf(zl4(zlb1, e), f4(b1, e), zl4(zlb0, e) * f4(b0, e));
+      for (int rr = 0; rr < R; ++rr) {
+        const float4 c0 = cur[2 * rr], c2 = cur[2 * rr + 2];
+        const bool hi = j >= 4;
+        const float4 ar = make_float4(hi ? c0.x : c2.x, hi ? c0.y : c2.y, hi ? c0.z : c2.z, hi ? c0.w : c2.w);
+        const float4 br = cur[2 * rr + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pa[e] = fmaf(zl4(zla[rr], e), f4(ar, e), pa[e]);
+          pb[e] = fmaf(zl4(zlb[rr], e), f4(br, e), pb[e]);
+        }
       }
       uint2 u;
       u.x = pack_bf16(pa[0], pa[1]); u.y = pack_bf16(pa[2], pa[3]);
@@ -511,9 +532,9 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
       u.x = pack_bf16(pb[0], pb[1]); u.y = pack_bf16(pb[2], pb[3]);
       *reinterpret_cast<uint2*>(frow + 48 + 4 * qb) = u;
     }
-    // points: pieces 36..41 through LDS, then lane j takes point j
-    if (j >= 4) *reinterpret_cast<float4*>(&sP[r][4 * (j - 4)]) = cur[4];
-    if (j < 2) *reinterpret_cast<float4*>(&sP[r][16 + 4 * j]) = cur[5];
+    // points: pieces 4 + 16 R .. 9 + 16 R through LDS, then lane j takes point j
+    if (j >= 4) *reinterpret_cast<float4*>(&sP[r][4 * (j - 4)]) = cur[2 * R];
+    if (j < 2) *reinterpret_cast<float4*>(&sP[r][16 + 4 * j]) = cur[2 * R + 1];
     __builtin_amdgcn_wave_barrier();
     {
       const float gx = sP[r][3 * j] - tr[0], gy = sP[r][3 * j + 1] - tr[1], gz = sP[r][3 * j + 2] - tr[2];
@@ -534,8 +555,8 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
     }
     // W_h has landed: at most the copies and loads issued after it (O of
     // h+1, the copy of W_(h+1), O of h+2) may still be in flight
-    if (h + 2 < H) wait_vmcnt<12 + WDMA>();
-    else if (h + 1 < H) wait_vmcnt<6 + WDMA>();
+    if (h + 2 < H) wait_vmcnt<2 * NPC + WDMA>();
+    else if (h + 1 < H) wait_vmcnt<NPC + WDMA>();
     else wait_vmcnt<0>();
     __syncthreads();  // features of head h and W_h visible
     // ---- update += features_h @ W_h
@@ -555,7 +576,7 @@ __global__ __launch_bounds__(8 * M) void epilogue_head_kernel(EpiArgs a) {
     }
     __syncthreads();  // everyone done with the features of head h and W buffer h&1
   };
-  float4 oa[6], ob[6], oc[6];
+  float4 oa[NPC], ob[NPC], oc[NPC];
   copy_w(0);
   load_o(0, oa);
   if (H > 1) load_o(1, ob);
@@ -666,16 +687,22 @@ hipError_t launch_epilogue(const Layout& L, void* ws, const float* o, const floa
     a.wt = wh;
     a.FP = kHeadFeatPitch;
     const dim3 g((total + 31) / 32), blk(256);
-    if (L.Cout == 128 && L.H == 8) {
-      hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 8>), g, blk, 0, st, a);
+    if (L.R == 1) {
+      if (L.H == 8) hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 8, 1>), g, blk, 0, st, a);
+      else hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 0, 1>), g, blk, 0, st, a);
+    } else if (L.R == 3) {
+      if (L.H == 8) hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 8, 3>), g, blk, 0, st, a);
+      else hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 0, 3>), g, blk, 0, st, a);
+    } else if (L.Cout == 128 && L.H == 8) {
+      hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 8, 2>), g, blk, 0, st, a);
     } else if (L.Cout == 128 && L.H == 12) {
-      hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 12>), g, blk, 0, st, a);
+      hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 12, 2>), g, blk, 0, st, a);
     } else {
       switch (L.Cout) {
-        case 32: hipLaunchKernelGGL((epilogue_head_kernel<32, 32, 0>), g, blk, 0, st, a); break;
-        case 64: hipLaunchKernelGGL((epilogue_head_kernel<32, 64, 0>), g, blk, 0, st, a); break;
-        case 96: hipLaunchKernelGGL((epilogue_head_kernel<32, 96, 0>), g, blk, 0, st, a); break;
-        default: hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 0>), g, blk, 0, st, a); break;
+        case 32: hipLaunchKernelGGL((epilogue_head_kernel<32, 32, 0, 2>), g, blk, 0, st, a); break;
+        case 64: hipLaunchKernelGGL((epilogue_head_kernel<32, 64, 0, 2>), g, blk, 0, st, a); break;
+        case 96: hipLaunchKernelGGL((epilogue_head_kernel<32, 96, 0, 2>), g, blk, 0, st, a); break;
+        default: hipLaunchKernelGGL((epilogue_head_kernel<32, 128, 0, 2>), g, blk, 0, st, a); break;
       }
     }
   } else if (L.mfma) {

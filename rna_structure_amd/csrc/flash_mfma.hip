@@ -168,10 +168,13 @@ __device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* pc, f32
 // wavefront.  S arrives relative to the running maximum m of each query (m
 // rides in the row term of the last geometric K-step); keys that are masked
 // out arrive as -16 x 65504 (key-mask column) or are set to -inf here
-// (pair-mask bits).  m is raised only when a row maximum exceeds it by more
-// than 8 (log2 units), so the probabilities stay below 2^8 and rescaling is
-// rare.  Leaves s relative to the new m and returns the factor by which O
-// and l are to be scaled.
+// (pair-mask bits).  m starts at the maximum of the first tile that holds a
+// permitted key of the row: without a pair mask every tile the loop visits
+// holds a valid key, which every valid query may attend to; with one, the
+// row's permitted keys are exactly its finite entries.  After that m is
+// raised only when a row maximum exceeds it by more than 8 (log2 units), so
+// the probabilities stay below 2^8 and rescaling is rare.  Leaves s relative
+// to the new m and returns the factor by which O and l are to be scaled.
 template <bool PM>
 __device__ __forceinline__ float softmax_max(const f32x16_t* sacc, uint32_t mw, float& m, bool& init, float* s) {
 #pragma unroll
@@ -192,9 +195,9 @@ __device__ __forceinline__ float softmax_max(const f32x16_t* sacc, uint32_t mw, 
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
     mt = fmaxf(mt, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
   }
-  // first permitted key of the row (masked keys are below -1e6), or a
-  // maximum that grew by more than 8
-  const bool need = init ? (mt > 8.0f) : (mt > -5.0e5f);
+  // the first tile with a permitted key of the row, or a maximum that grew
+  // by more than 8
+  const bool need = init ? (mt > 8.0f) : (PM ? (mt > -INFINITY) : true);
   const float shift = need ? mt : 0.f;
   const float alpha = (need && init) ? __builtin_amdgcn_exp2f(-mt) : 1.0f;
   if (__any(need)) {

@@ -398,15 +398,26 @@ void bias_attn_kernel(BiasLayout L, const char* ws, const void* qin, const void*
     // while no key of the row has been permitted, m is -inf and so is every s:
     // subtracting 0 instead keeps exp2(-inf) = 0
     const float ms = m == -INFINITY ? 0.f : m;
+    // l sums the bf16-rounded weights that the value product multiplies
+    // (two at a time, v_dot2 against ones, fp32 accumulation), so the weights
+    // applied to V sum to one to fp32 rounding; the log-sum-exp then carries
+    // their rounding (below 2^-9 relative in l)
     bf16x8_t pb[4];
-    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      const float p = __builtin_amdgcn_exp2f(s[x] - ms);
-      if (x & 1) ps1 += p; else ps0 += p;
-      pb[x >> 3][x & 7] = (__bf16)p;
+    for (int x = 0; x < 32; ++x) pb[x >> 3][x & 7] = (__bf16)__builtin_amdgcn_exp2f(s[x] - ms);
+    {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 0, 1), one2, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 2, 3), one2, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 4, 5), one2, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 6, 7), one2, ps1, false);
+      }
+      l += ps0 + ps1;
     }
-    l += ps0 + ps1;
 
     // O^T += V~^T P^T: K-step j covers keys 16 j .. 16 j + 15 of the tile
 #pragma unroll

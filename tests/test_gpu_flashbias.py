@@ -105,3 +105,20 @@ def test_bias_attention_full_size_sampled_rows(name, dims, kind, causal, opts):
     # a second call on the same buffers gives the same bits
     _, again = _run(inp, scale, causal, f)
     assert np.array_equal(again["o"], got["o"]) and np.array_equal(again["lse"], got["lse"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_weights_applied_to_values_sum_to_one(causal):
+    """With every value equal to 1 the output is the sum of the weights the
+    value product applies: 1 within fp32 rounding (1e-5) on every non-empty
+    row, not just within the bf16 rounding of the weights."""
+    dims = dict(B=2, N=300, M=300, H=3, D=32, Dv=16, R=2)
+    inp = make_bias_inputs(**dims, seed=13, kind="random", masked_keys=(7, 64, 299), empty_sample=True)
+    inp["v"] = np.ones_like(inp["v"])
+    say(f"case bias attention unit values causal={causal}")
+    _, got = _run(inp, 1.0 / np.sqrt(dims["D"]), causal)
+    fin = np.isfinite(got["lse"]).transpose(0, 2, 1)  # [B, N, H]
+    assert fin.any() and not fin.all()
+    o = got["o"]
+    assert np.max(np.abs(o[fin] - 1.0)) <= 1e-5, np.max(np.abs(o[fin] - 1.0))
+    assert np.all(o[~fin] == 0.0)

@@ -56,6 +56,9 @@ SMALL = [
     _case("rank3-bf16", IPAShape(B=2, N=300, H=3, R=3), 22, frames="walk", step=3.8, lengths=(200, 300),
           pair_dropout=0.05, empty_row=True),
     _case("rank3-split-bf16", IPAShape(B=1, N=1100, H=2, R=3), 23, frames="walk", step=3.8),
+    # rank 1 at the standard widths (the per-head epilogue's rank-1 instance)
+    _case("rank1-std-bf16", IPAShape(B=2, N=260, H=8, R=1), 24, frames="walk", step=3.8, lengths=(150, 260),
+          pair_dropout=0.05, empty_row=True),
 ]
 
 
@@ -113,6 +116,61 @@ def test_parity_sweep_sampled(n):
     say(f"config sweep N={n}")
     _, _, gpu = run_gpu(inp)
     compare(inp, gpu, rows=_sample_rows(n, 6, 3, extra=(n // 2, n - 64, 63, 64)), tol=TOL["bf16"])
+
+
+@pytest.mark.parametrize("R", [1, 3])
+def test_parity_rank_sweep_sampled(R):
+    """The rank sweep's shapes (B1 N8192 H8, pair factors of rank 1 and 3) at
+    full size, on sampled rows."""
+    inp = make_inputs(IPAShape(B=1, N=8192, H=8, R=R), 8100 + R, frames="walk", step=3.8)
+    say(f"case rank sweep R={R} N=8192")
+    _, _, gpu = run_gpu(inp)
+    compare(inp, gpu, rows=_sample_rows(8192, 6, 4, extra=(63, 64, 4096, 8191)), tol=TOL["bf16"])
+
+
+def _far_cluster_inputs(dtype):
+    """B1 N192 H4: keys 128..191 (the third key tile) moved 180 A away along
+    x; query row 10 may attend to those keys only (pair mask); the point
+    weights 60, -60, 30, 0.5 (softplus of large arguments of both signs).  On
+    the head with weight 60 every permitted logit of row 10 lies between
+    -9.4e5 and -6.4e5 in log2 units: the page's softmax still normalises over
+    those keys, and the row is not an empty neighbourhood."""
+    from rna_structure_amd.synth import round_to
+    s = IPAShape(B=1, N=192, H=4, dtype=dtype)
+    inp = make_inputs(s, 41, frames="walk", step=3.8)
+    tr = inp["translation"].astype(np.float64).copy()
+    tr[0, 128:, 0] += 180.0
+    inp["translation"] = round_to(tr, dtype)
+    inp["point_weight_raw"] = round_to(np.array([60.0, -60.0, 30.0, 0.5]), dtype)
+    pm = np.ones((1, 192, 192), dtype=bool)
+    pm[0, 10, :128] = False
+    inp["pair_mask"] = pm
+    return inp
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_far_keys_and_extreme_point_weights(dtype):
+    inp = _far_cluster_inputs(dtype)
+    ref = ipa_factored(inp, rows=np.array([10]), keep=("logits", "lse", "empty"))
+    permitted = ref["logits"][0, 0, 0, 128:] / math.log(2)
+    assert permitted.max() < -5e5 and not ref["empty"][0, 0]
+    say(f"case far keys {dtype}")
+    _, _, gpu = run_gpu(inp)
+    assert np.all(np.isfinite(gpu["lse"][0, :, 10]))
+    compare(inp, gpu, rows=np.array([0, 5, 10, 11, 127, 128, 150, 191]), tol=TOL[dtype])
+
+
+def test_chain_far_from_origin_bf16():
+    """Every translation moved by (2e4, -1.5e4, 3e4) A before the bf16 rounding
+    (spacing 128 A there): the centroids and centred points stay small."""
+    from rna_structure_amd.synth import round_to
+    s = IPAShape(B=2, N=300, H=4)
+    inp = make_inputs(s, 43, frames="walk", step=3.8, lengths=(200, 300))
+    tr = inp["translation"].astype(np.float64) + np.array([2e4, -1.5e4, 3e4])
+    inp["translation"] = round_to(tr, "bf16")
+    say("case chain far from the origin")
+    _, _, gpu = run_gpu(inp)
+    compare(inp, gpu, tol=TOL["bf16"])
 
 
 @pytest.mark.parametrize("dtype,N", [("bf16", 300), ("f32", 300), ("bf16", 1100)])
