@@ -156,7 +156,15 @@ ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, siz
  * is a_hij = exp(L_ijh - lse_hi).
  * `lifted` must come from ipa_lift with the same shape, mask and pair_mask.
  * bf16 path: bf16 MFMA for the scalar and pair columns, fp16 hi/lo split
- * MFMA for the centred point columns, fp32 softmax and accumulation. */
+ * MFMA for the centred point columns, fp32 softmax and accumulation.  Its
+ * shapes: D <= 16, Dv <= 31, P <= 5, Q <= 9, R*Cz <= 192 (else
+ * IPA_ERR_UNSUPPORTED from ipa_lifted_bytes and the calls).  Its range: the
+ * point term of a query against the centroid of a key tile, minus the row's
+ * running maximum (the maximum over the permitted keys of the tiles seen so
+ * far; zero before the first tile with a permitted key), is held in fp16
+ * parts and must stay within 16 * 65504 in log2 units, i.e. gamma_h
+ * sum_p |T_i q_p - c_t|^2 below about 7e5 at a row's first tile with a
+ * permitted key; beyond that it is clamped (finite results, no NaN). */
 ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream);
 
 /* Bytes of the epilogue's own workspace for this shape (the output
@@ -195,7 +203,7 @@ ipa_status ipa_epilogue(const ipa_shape* s, void* workspace, size_t workspace_by
  * GPU until the process ends.  The shape must fit in it:
  *   align256(ipa_lifted_bytes(s, pm)) + align256(4 B N H ipa_o_width(s))
  *     + align256(4 B H N) + ipa_epilogue_workspace_bytes(s) <= 128 MiB
- * (B=8, N=256: 29 MiB; B=1, N=2048: 72 MiB, at H=8 and the standard
+ * (B=8, N=256: 22 MiB; B=1, N=2048: 65 MiB, at H=8 and the standard
  * widths), else
  * IPA_ERR_SCRATCH before anything is enqueued.  Results are those of the
  * three calls.  Every call on a GPU shares that GPU's array: calls that
