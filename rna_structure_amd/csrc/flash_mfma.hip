@@ -28,11 +28,17 @@
 // Normalisation uses the ones rows, i.e. the sums of the rounded
 // probabilities actually multiplied into O, so the weights applied to the
 // values sum to one to fp32 rounding and the centroid cancels exactly.
-// Key and value tiles are copied global -> LDS with direct-to-LDS loads into
-// two buffers: the copies of the next tile run during the whole of the
-// current tile, and one barrier per tile separates the two.  A tile has four
-// parts (common.h): the head's key rows and value rows, and the pair-factor
-// key and value rows that the H heads of a batch element share.
+// Key and value tiles are copied global -> LDS with direct-to-LDS loads.  A
+// tile has four parts (common.h): the head's key rows and value rows, and the
+// pair-factor key and value rows that the H heads of a batch element share.
+// Two schemes (NBUF): with two buffers the copies of the next tile run
+// during the whole of the current tile and one barrier per tile separates
+// the two (8 wavefronts, one workgroup per CU: long key ranges); with one
+// buffer the copies of a tile go out when every wavefront is done with the
+// previous one, and the latency is hidden by a second workgroup on the CU
+// (4 wavefronts, two workgroups per CU: short key ranges, where the
+// per-workgroup prologue and output also overlap with the other
+// workgroup's tiles).
 #include "lds_copy.h"
 #include "mfma_tile.h"
 
@@ -251,7 +257,7 @@ __device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, 
 template <int NVB>
 __device__ __forceinline__ constexpr int block_at(int pos) { return pos == 0 ? 0 : (pos == NVB ? 1 : pos + 1); }
 
-template <int NQS, int NVB, int GS, int W>
+template <int NQS, int NVB, int GS, int W, int NBUF>
 __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* skv, int sp, int b, int h, int i,
                                             bool qin, bool qvalid, int w, int lane, int l32, int half,
                                             const f32x16_t* oacc, float m, float l, bool init) {
@@ -299,7 +305,7 @@ __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* skv, i
   // columns, one contiguous range, 16 bytes per lane with consecutive lanes
   // on consecutive addresses.
   constexpr int NB = NVB + 1;
-  constexpr int SLOT = 2 * T::TB / W;  // bytes per slot
+  constexpr int SLOT = NBUF * T::TB / W;  // bytes per slot
   constexpr int BPP0 = (SLOT / (32 * 4) - 1) / 32;
   constexpr int BPP = BPP0 < NB ? BPP0 : NB;
   static_assert(BPP >= 1, "LDS slots too small for the output staging");
@@ -366,28 +372,41 @@ __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* skv, i
 
 // One key tile t of the main loop, held in LDS buffer BUF (a compile-time
 // index, so that every LDS offset is a constant): the point operand with the
-// current running maximum, the wait for the tile's copies (issued one tile
-// earlier) and the barrier that makes them visible and frees the other
-// buffer, the copies of the next valid tile into that buffer, and the
-// products and softmax of tile t.  Returns the next tile with a valid key
+// current running maximum; with two buffers the wait for the tile's copies
+// (issued one tile earlier), the barrier that makes them visible and frees
+// the other buffer, and the copies of the next valid tile into that buffer;
+// with one buffer a barrier (every wavefront is done with the previous tile,
+// unless t is the first), the copies of tile t, the wait and a barrier; then
+// the products and softmax of tile t.  Returns the next tile with a valid key
 // (tend if none).
-template <int NQS, int NVB, int GS, int W, bool PM, int BUF>
+template <int NQS, int NVB, int GS, int W, bool PM, int NBUF, int BUF>
 __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc& src, char* skv,
                                            const uint32_t* kmb, const float4* ckb, int t, int tend, int b, int i,
                                            bool qin, bool qvalid, bool active, int w, int lane, int l32, int half,
                                            float gl, float Pf, const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg,
-                                           f32x16_t* oacc, float& m, float& l, bool& init) {
+                                           f32x16_t* oacc, float& m, float& l, bool& init, int t_first) {
   using T = TileDims<NQS, NVB, GS>;
   const Layout& L = a.L;
   const int tn = next_valid_tile(kmb, t, tend);
   uint32_t mw = 0xFFFFFFFFu;
   if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
   geo_tile<GS>(qg, ld_uniform4(ckb + t), gl, Pf, m, half, bg);
-  // tile t has landed; every wave is done with the previous tile
-  wait_vmcnt<0>();
-  __syncthreads();
-  if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
-  if (tn < tend) copy_kv_tile<NQS, NVB, GS, W>(src, skv, tn, 1 - BUF, w, lane);
+  if constexpr (NBUF == 2) {
+    // tile t has landed; every wave is done with the previous tile
+    wait_vmcnt<0>();
+    __syncthreads();
+    if constexpr (PM) asm volatile("" ::"v"(mw));  // in registers before the next copies are issued
+    if (tn < tend) copy_kv_tile<NQS, NVB, GS, W>(src, skv, tn, 1 - BUF, w, lane);
+  } else {
+    // the first tile's copies went out before the loop
+    if (t != t_first) {
+      __syncthreads();  // every wave is done with the previous tile
+      copy_kv_tile<NQS, NVB, GS, W>(src, skv, t, 0, w, lane);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    if constexpr (PM) asm volatile("" ::"v"(mw));
+  }
   if (!active) return tn;
   const char* kt = skv + BUF * T::TB;
   f32x16_t sacc[2];
@@ -418,7 +437,7 @@ __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc
 // (the loop is unrolled by two so that buffer offsets are constants).  PM
 // selects the per-query pair-mask words (a vector load per tile); without a
 // pair mask the key mask is inside the key product.
-template <int NQS, int NVB, int GS, int W, bool PM>
+template <int NQS, int NVB, int GS, int W, int NBUF, bool PM>
 __device__ __forceinline__ void attend(const FlashMfmaArgs& a, const TileSrc& src, char* skv, int t, int tend, int sp,
                                        int b, int h, int i, bool qin, bool qvalid, int w, int lane, int l32, int half,
                                        float gl, float Pf, const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
@@ -434,24 +453,30 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, const TileSrc& sr
   // a wavefront without a valid query keeps copying tiles and meeting the
   // barriers, but does no products
   const bool active = __any(qvalid);
-#define FIPA_TILE(BUFI)                                                                                              \
-  attend_tile<NQS, NVB, GS, W, PM, BUFI>(a, src, skv, kmb, ckb, t, tend, b, i, qin, qvalid, active, w, lane, l32, half, \
-                                         gl, Pf, bq, bg, qg, oacc, m, l, init)
-  while (t < tend) {
-    t = FIPA_TILE(0);
-    if (t >= tend) break;
-    t = FIPA_TILE(1);
+  const int t_first = t;
+#define FIPA_TILE(BUFI)                                                                                             \
+  attend_tile<NQS, NVB, GS, W, PM, NBUF, BUFI>(a, src, skv, kmb, ckb, t, tend, b, i, qin, qvalid, active, w, lane,   \
+                                               l32, half, gl, Pf, bq, bg, qg, oacc, m, l, init, t_first)
+  if constexpr (NBUF == 2) {
+    while (t < tend) {
+      t = FIPA_TILE(0);
+      if (t >= tend) break;
+      t = FIPA_TILE(1);
+    }
+  } else {
+    while (t < tend) t = FIPA_TILE(0);
   }
 #undef FIPA_TILE
-  finish_rows<NQS, NVB, GS, W>(a, skv, sp, b, h, i, qin, qvalid, w, lane, l32, half, oacc, m, l, init);
+  finish_rows<NQS, NVB, GS, W, NBUF>(a, skv, sp, b, h, i, qin, qvalid, w, lane, l32, half, oacc, m, l, init);
 }
 
-template <int NQS, int NVB, int GS, int W>
-__global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
+// NBUF tile buffers, each [head key rows | pair key rows | head value rows |
+// pair value rows]; with one buffer two workgroups share a CU (registers
+// capped at 256 a lane).
+template <int NQS, int NVB, int GS, int W, int NBUF>
+__global__ __launch_bounds__(W * 64, NBUF == 1 ? 2 : 1) void flash_mfma_kernel(FlashMfmaArgs a) {
   using T = TileDims<NQS, NVB, GS>;
-  // two tile buffers, each [head key rows | pair key rows | head value rows |
-  // pair value rows]
-  __shared__ __attribute__((aligned(1024))) char skv[2 * T::TB];
+  __shared__ __attribute__((aligned(1024))) char skv[NBUF * T::TB];
 
   const Layout& L = a.L;
   const int N = L.N, H = L.H;
@@ -510,9 +535,11 @@ __global__ __launch_bounds__(W * 64) void flash_mfma_kernel(FlashMfmaArgs a) {
   }
 
   if (has_pm)
-    attend<NQS, NVB, GS, W, true>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, NBUF, true>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq,
+                                        bg, qg);
   else
-    attend<NQS, NVB, GS, W, false>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq, bg, qg);
+    attend<NQS, NVB, GS, W, NBUF, false>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq,
+                                         bg, qg);
 }
 
 // Merge the partial results of the KS key ranges of every (b, h, query):
@@ -563,9 +590,15 @@ __global__ __launch_bounds__(256) void combine_kernel(Layout L, const float* par
   if (c4 == 0) lse[((size_t)b * H + h) * N + i] = nonempty ? (m + log2f(ls)) * kLn2 : -INFINITY;
 }
 
-// 8 wavefronts (256 queries) per workgroup when that still gives every CU a
-// workgroup, or when the keys are split into ranges (then KS workgroups per
-// query tile and the combine kernel after); else 4 (128 queries).
+// Short chains whose keys are not split (KS = 1, at most kShortRange tiles
+// per query tile: the protein-like and short-chain batches) run on one tile
+// buffer, four wavefronts (128 queries) per workgroup and two workgroups per
+// CU; everything else on two buffers with 8 wavefronts (256 queries), one
+// workgroup per CU.  Whole forwards measured 2% faster with one buffer on
+// the two batches, 1.5-4% slower at N = 2048 and 4096 (key ranges split over
+// more workgroups) and the same at N = 8192.  KS > 1 splits the keys of a
+// query tile into ranges (one workgroup each, the combine kernel after).
+constexpr int kShortRange = 16;
 template <int NQS, int NVB, int GS>
 static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st) {
   FlashMfmaArgs a;
@@ -574,22 +607,21 @@ static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* 
   a.o = o;
   a.lse = lse;
   a.ks = L.KS;
-  const int q8 = (L.N + 255) / 256;
   if constexpr (NQS > 9) {
     // the widest rows (rank-3 pair factors): four wavefronts, one per SIMD,
     // with the whole register file each
     a.qtiles = (L.N + 127) / 128;
     a.nwg = a.qtiles * L.H * L.B * L.KS;
-    hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4>), dim3(a.nwg), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4, 2>), dim3(a.nwg), dim3(256), 0, st, a);
   } else {
-    if ((long)q8 * L.H * L.B >= 256 || L.KS > 1) {
-      a.qtiles = q8;
-      a.nwg = a.qtiles * L.H * L.B * L.KS;
-      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 8>), dim3(a.nwg), dim3(512), 0, st, a);
-    } else {
+    if (L.KS == 1 && L.NT <= kShortRange) {
       a.qtiles = (L.N + 127) / 128;
-      a.nwg = a.qtiles * L.H * L.B;
-      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4>), dim3(a.nwg), dim3(256), 0, st, a);
+      a.nwg = a.qtiles * L.H * L.B * L.KS;
+      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4, 1>), dim3(a.nwg), dim3(256), 0, st, a);
+    } else {
+      a.qtiles = (L.N + 255) / 256;
+      a.nwg = a.qtiles * L.H * L.B * L.KS;
+      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 8, 2>), dim3(a.nwg), dim3(512), 0, st, a);
     }
   }
   if (L.KS > 1) {
