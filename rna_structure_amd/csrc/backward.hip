@@ -526,17 +526,89 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
 // lane half h supplies key kappa(s, h) = 8 (s / 4) + 4 h + s % 4, the key its
 // register s holds, and reads the value row of that key.
 constexpr int kBwKT = 32;  // keys per tile of the matrix-core passes
+constexpr int kStageC = 2;  // loads per thread in flight at once where registers are short
 
 __device__ __forceinline__ int kappa(int s, int h) { return 8 * (s >> 2) + 4 * h + (s & 3); }
+
+// One tile of 32 rows of F4 float4 pieces, staged through registers by the
+// 256 threads of a workgroup: `load` issues every global load of the tile at
+// once (so a tile costs one memory round trip, not one per loop trip; and a
+// tile can be loaded one step ahead while the current one is in use),
+// `store` hands each piece to the caller's LDS write.  Rows past the end
+// repeat row N - 1; pieces at or past `valid` read as zero.  Every load
+// address is clamped into the rows and pieces of the tensor.
+template <int F4>
+struct Tile4 {
+  static constexpr int K = (32 * F4 + 255) / 256;
+  float4 v[K];
+  __device__ __forceinline__ void load(const float* base, int stride, int j0, int N, int tid, int valid) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int e = min(tid + 256 * k, 32 * F4 - 1);
+      const int jj = e / F4, c4 = e - jj * F4;
+      const int j = min(j0 + jj, N - 1);
+      // a 32-bit index from the uniform base (scalar base + vector offset)
+      const uint32_t idx = (uint32_t)j * (uint32_t)(stride >> 2) + (uint32_t)min(c4, valid - 1);
+      const float4 x = reinterpret_cast<const float4*>(base)[idx];
+      v[k] = c4 < valid ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  template <typename Fn>
+  __device__ __forceinline__ void store(int tid, Fn fn) const {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int e = tid + 256 * k;
+      if (e < 32 * F4) {
+        const int jj = e / F4, c4 = e - jj * F4;
+        fn(jj, c4, v[k]);
+      }
+    }
+  }
+};
+
+// The same staging for kernels without the registers for a whole tensor's
+// pieces: loads in groups of C per thread, each group written to LDS before
+// the next is loaded.
+template <int F4, int C, typename Fn>
+__device__ __forceinline__ void stage_tile(const float* base, int stride, int j0, int N, int tid, int valid, Fn fn) {
+  constexpr int K = (32 * F4 + 255) / 256;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += C) {
+    float4 v[C];
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      const int e = min(tid + 256 * (k0 + k), 32 * F4 - 1);
+      const int jj = e / F4, c4 = e - jj * F4;
+      const int j = min(j0 + jj, N - 1);
+      const uint32_t idx = (uint32_t)j * (uint32_t)(stride >> 2) + (uint32_t)min(c4, valid - 1);
+      const float4 x = reinterpret_cast<const float4*>(base)[idx];
+      v[k] = c4 < valid ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      const int e = tid + 256 * (k0 + k);
+      if (k0 + k < K && e < 32 * F4) {
+        const int jj = e / F4, c4 = e - jj * F4;
+        fn(jj, c4, v[k]);
+      }
+    }
+  }
+}
 
 template <int DKH, int NVB>
 __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
   const BwLayout& L = a.L;
   constexpr int DKp = 2 * DKH;
   constexpr int VW = 32 * NVB;  // value columns staged (DVp padded with zeros)
-  __shared__ float sKT[DKp][kBwKT];
+  // Pitches: KV is written transposed by threads walking its columns, so a
+  // row pitch of 33 words spreads consecutive columns over the banks (32
+  // would put them all in one); the value rows are read at rows kappa(s, 0)
+  // and kappa(s, 1) = +4 by the two halves of a wavefront, so a pitch of
+  // VW + 8 words (4 (VW + 8) = 32 mod 64) gives the halves different banks.
+  constexpr int VWP = VW + 8;
+  __shared__ float sKT[DKp][kBwKT + 1];
   __shared__ __align__(16) float sBp[kBwKT][16];
-  __shared__ float sV[kBwKT][VW];
+  __shared__ __align__(16) float sV[kBwKT][VWP];
   __shared__ float sM[kBwKT];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -578,34 +650,36 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
   float cx = 0.f, cy = 0.f, cz = 0.f;
   const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + qc) * L.N : nullptr;
   const int P3 = L.P3;  // coordinates past 3P are zero on both sides
+  // key tiles: KV (transposed into LDS), VV rows (zero past DVp), centred key
+  // points, key mask; the next tile's loads are in flight during the
+  // products of the current one
+  const float* kvb = wsf(a, L.off_kv) + rowidx(L, b, h, 0) * L.DKp;
+  const float* vvb = wsf(a, L.off_vv) + rowidx(L, b, h, 0) * L.DVp;
+  const float* kbb = wsf(a, L.off_kb) + rowidx(L, b, h, 0) * 16;
+  Tile4<DKp / 4> tk;
+  Tile4<VW / 4> tv;
+  Tile4<4> tb;
+  float tm = 0.f;
+  auto issue = [&](int j0) {
+    tk.load(kvb, L.DKp, j0, L.N, tid, DKp / 4);
+    tv.load(vvb, L.DVp, j0, L.N, tid, L.DVp / 4);
+    tb.load(kbb, 16, j0, L.N, tid, 4);
+    const int j = min(j0 + (tid & 31), L.N - 1);
+    tm = (j0 + (tid & 31) < L.N && a.mask[(size_t)b * L.N + j] != 0) ? 1.f : 0.f;
+  };
+  issue(0);
   for (int j0 = 0; j0 < L.N; j0 += kBwKT) {
     __syncthreads();
-    // stage the tile: KV transposed, VV rows (zero past DVp), centred key points
-    for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
-      const int jj = e / (DKp / 4), c4 = e - jj * (DKp / 4);
-      const int j = min(j0 + jj, L.N - 1);
-      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, j) * L.DKp)[c4];
+    tk.store(tid, [&](int jj, int c4, float4 v) {
       sKT[4 * c4][jj] = v.x;
       sKT[4 * c4 + 1][jj] = v.y;
       sKT[4 * c4 + 2][jj] = v.z;
       sKT[4 * c4 + 3][jj] = v.w;
-    }
-    for (int e = tid; e < kBwKT * (VW / 4); e += 256) {
-      const int jj = e / (VW / 4), c4 = e - jj * (VW / 4);
-      const int j = min(j0 + jj, L.N - 1);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (4 * c4 < L.DVp) v = reinterpret_cast<const float4*>(wsf(a, L.off_vv) + rowidx(L, b, h, j) * L.DVp)[c4];
-      reinterpret_cast<float4*>(&sV[jj][0])[c4] = v;
-    }
-    for (int e = tid; e < kBwKT * 4; e += 256) {
-      const int jj = e >> 2, c4 = e & 3;
-      const int j = min(j0 + jj, L.N - 1);
-      reinterpret_cast<float4*>(&sBp[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_kb) + rowidx(L, b, h, j) * 16)[c4];
-    }
-    if (tid < kBwKT) {
-      const int j = j0 + tid;
-      sM[tid] = (j < L.N && a.mask[(size_t)b * L.N + j] != 0) ? 1.f : 0.f;
-    }
+    });
+    tv.store(tid, [&](int jj, int c4, float4 v) { reinterpret_cast<float4*>(&sV[jj][0])[c4] = v; });
+    tb.store(tid, [&](int jj, int c4, float4 v) { reinterpret_cast<float4*>(&sBp[jj][0])[c4] = v; });
+    if (tid < kBwKT) sM[tid] = tm;
+    if (j0 + kBwKT < L.N) issue(j0 + kBwKT);
     __syncthreads();
     // S^T: A = key tile (row = key l32, k = hf), B = query (k = hf, column = query l32)
     f32x16_t sacc = f32x16_t{};
@@ -769,28 +843,23 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   for (int u = 0; u < P3C; ++u) da[u] = 0.f;
   float dg = 0.f;
   const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + qc) * L.N : nullptr;
+  const float* kvb = wsf(a, L.off_kv) + rowidx(L, b, h, 0) * L.DKp;
+  const float* vvb = wsf(a, L.off_vv) + rowidx(L, b, h, 0) * L.DVp;
+  const float* kbb = wsf(a, L.off_kb) + rowidx(L, b, h, 0) * 16;
   for (int j0 = 0; j0 < L.N; j0 += kBwKT) {
     __syncthreads();
-    for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
-      const int jj = e / (DKp / 4), c4 = e - jj * (DKp / 4);
-      const int j = min(j0 + jj, L.N - 1);
-      *reinterpret_cast<float4*>(&sK[jj][4 * c4]) =
-          reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, j) * L.DKp)[c4];
-    }
-    for (int e = tid; e < kBwKT * (DVp / 4); e += 256) {
-      const int jj = e / (DVp / 4), c4 = e - jj * (DVp / 4);
-      const int j = min(j0 + jj, L.N - 1);
-      *reinterpret_cast<float4*>(&sV[jj][4 * c4]) =
-          reinterpret_cast<const float4*>(wsf(a, L.off_vv) + rowidx(L, b, h, j) * L.DVp)[c4];
-    }
-    for (int e = tid; e < kBwKT * 4; e += 256) {
-      const int jj = e >> 2, c4 = e & 3;
-      const int j = min(j0 + jj, L.N - 1);
-      reinterpret_cast<float4*>(&sBp[jj][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_kb) + rowidx(L, b, h, j) * 16)[c4];
-    }
-    if (tid < kBwKT) {
-      const int j = j0 + tid;
-      sM[tid] = (j < L.N && a.mask[(size_t)b * L.N + j] != 0) ? 1.f : 0.f;
+    {
+      // one tensor at a time: its loads together, then its LDS writes (the
+      // whole tile at once would not fit beside the accumulators)
+      const int jm = min(j0 + (tid & 31), L.N - 1);
+      const float tm = (j0 + (tid & 31) < L.N && a.mask[(size_t)b * L.N + jm] != 0) ? 1.f : 0.f;
+      stage_tile<4, 1>(kbb, 16, j0, L.N, tid, 4,
+                       [&](int jj, int c4, float4 v) { reinterpret_cast<float4*>(&sBp[jj][0])[c4] = v; });
+      stage_tile<DKp / 4, kStageC>(kvb, L.DKp, j0, L.N, tid, DKp / 4,
+                                   [&](int jj, int c4, float4 v) { *reinterpret_cast<float4*>(&sK[jj][4 * c4]) = v; });
+      stage_tile<DVp / 4, kStageC>(vvb, L.DVp, j0, L.N, tid, DVp / 4,
+                                   [&](int jj, int c4, float4 v) { *reinterpret_cast<float4*>(&sV[jj][4 * c4]) = v; });
+      if (tid < kBwKT) sM[tid] = tm;
     }
     __syncthreads();
     // S and dP steps interleaved: two independent chains of dependent MFMAs
@@ -949,37 +1018,75 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
   float db[P3C];
 #pragma unroll
   for (int u = 0; u < P3C; ++u) db[u] = 0.f;
+  // query tiles: QV and dO (transposed into LDS), query points, per-query
+  // statistics; the tile's loads go out together, and in mode 1 (which has
+  // the registers for it) one tile ahead, in flight during the products
+  constexpr bool kPre = MODE == 1;
+  const float* qvb = wsf(a, L.off_qv) + rowidx(L, b, h, 0) * L.DKp;
+  const float* dob = wsf(a, L.off_do) + rowidx(L, b, h, 0) * L.DVp;
+  const float* qab = wsf(a, L.off_qa) + rowidx(L, b, h, 0) * 16;
+  Tile4<DKp / 4> tq;
+  Tile4<DVp / 4> td;
+  Tile4<4> ta;
+  float t_lse = 0.f, t_dd = 0.f;
+  float4 t_ds = make_float4(0.f, 0.f, 0.f, 0.f);
+  bool t_ok = false;
+  auto issue = [&](int i0) {
+    tq.load(qvb, L.DKp, i0, L.N, tid, DKp / 4);
+    td.load(dob, L.DVp, i0, L.N, tid, DVp / 4);
+    ta.load(qab, 16, i0, L.N, tid, 4);
+    const int i = i0 + (tid & 31);
+    const int icl = min(i, L.N - 1);
+    t_lse = wsf(a, L.off_lse)[rowidx(L, b, h, icl)];
+    t_ok = i < L.N && a.mask[(size_t)b * L.N + icl] != 0;
+    t_dd = wsf(a, L.off_dd)[rowidx(L, b, h, icl)];
+    t_ds = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + rowidx(L, b, h, icl) * 4)[0];
+  };
+  auto put_q = [&](int ii, int c4, float4 v) {
+    sQT[4 * c4][ii] = v.x; sQT[4 * c4 + 1][ii] = v.y; sQT[4 * c4 + 2][ii] = v.z; sQT[4 * c4 + 3][ii] = v.w;
+  };
+  auto put_d = [&](int ii, int c4, float4 v) {
+    sDT[4 * c4][ii] = v.x; sDT[4 * c4 + 1][ii] = v.y; sDT[4 * c4 + 2][ii] = v.z; sDT[4 * c4 + 3][ii] = v.w;
+  };
+  auto put_a = [&](int ii, int c4, float4 v) { reinterpret_cast<float4*>(&sA[ii][0])[c4] = v; };
+  if (kPre) issue(0);
   for (int i0 = 0; i0 < L.N; i0 += kBwKT) {
     __syncthreads();
-    for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
-      const int ii = e / (DKp / 4), c4 = e - ii * (DKp / 4);
-      const int i = min(i0 + ii, L.N - 1);
-      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_qv) + rowidx(L, b, h, i) * L.DKp)[c4];
-      sQT[4 * c4][ii] = v.x; sQT[4 * c4 + 1][ii] = v.y; sQT[4 * c4 + 2][ii] = v.z; sQT[4 * c4 + 3][ii] = v.w;
-    }
-    for (int e = tid; e < kBwKT * (DVp / 4); e += 256) {
-      const int ii = e / (DVp / 4), c4 = e - ii * (DVp / 4);
-      const int i = min(i0 + ii, L.N - 1);
-      const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_do) + rowidx(L, b, h, i) * L.DVp)[c4];
-      sDT[4 * c4][ii] = v.x; sDT[4 * c4 + 1][ii] = v.y; sDT[4 * c4 + 2][ii] = v.z; sDT[4 * c4 + 3][ii] = v.w;
-    }
-    for (int e = tid; e < kBwKT * 4; e += 256) {
-      const int ii = e >> 2, c4 = e & 3;
-      const int i = min(i0 + ii, L.N - 1);
-      reinterpret_cast<float4*>(&sA[ii][0])[c4] = reinterpret_cast<const float4*>(wsf(a, L.off_qa) + rowidx(L, b, h, i) * 16)[c4];
+    if constexpr (kPre) {
+      tq.store(tid, put_q);
+      td.store(tid, put_d);
+      ta.store(tid, put_a);
+    } else {
+      // mode 0 holds more accumulators: a piece at a time (measured faster
+      // here than the grouped loads, which made the compiler spill)
+      const int i = i0 + (tid & 31);
+      const int icl = min(i, L.N - 1);
+      t_lse = wsf(a, L.off_lse)[rowidx(L, b, h, icl)];
+      t_ok = i < L.N && a.mask[(size_t)b * L.N + icl] != 0;
+      t_dd = wsf(a, L.off_dd)[rowidx(L, b, h, icl)];
+      t_ds = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + rowidx(L, b, h, icl) * 4)[0];
+      for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
+        const int ii = e / (DKp / 4), c4 = e - ii * (DKp / 4);
+        put_q(ii, c4, reinterpret_cast<const float4*>(qvb + (size_t)min(i0 + ii, L.N - 1) * L.DKp)[c4]);
+      }
+      for (int e = tid; e < kBwKT * (DVp / 4); e += 256) {
+        const int ii = e / (DVp / 4), c4 = e - ii * (DVp / 4);
+        put_d(ii, c4, reinterpret_cast<const float4*>(dob + (size_t)min(i0 + ii, L.N - 1) * L.DVp)[c4]);
+      }
+      for (int e = tid; e < kBwKT * 4; e += 256) {
+        const int ii = e >> 2, c4 = e & 3;
+        put_a(ii, c4, reinterpret_cast<const float4*>(qab + (size_t)min(i0 + ii, L.N - 1) * 16)[c4]);
+      }
     }
     if (tid < kBwKT) {
-      const int i = i0 + tid;
-      const int icl = min(i, L.N - 1);
-      const float lse = wsf(a, L.off_lse)[rowidx(L, b, h, icl)];
-      const bool ok = i < L.N && a.mask[(size_t)b * L.N + icl] != 0 && lse > -INFINITY;
-      sL[tid] = ok ? lse : INFINITY;  // +inf marks a query that takes no key
-      sS[tid] = wsf(a, L.off_dd)[rowidx(L, b, h, icl)];
-      const float4 sv = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + rowidx(L, b, h, icl) * 4)[0];
-      sSx[tid] = sv.x;
-      sSy[tid] = sv.y;
-      sSz[tid] = sv.z;
+      const bool ok = t_ok && t_lse > -INFINITY;
+      sL[tid] = ok ? t_lse : INFINITY;  // +inf marks a query that takes no key
+      sS[tid] = t_dd;
+      sSx[tid] = t_ds.x;
+      sSy[tid] = t_ds.y;
+      sSz[tid] = t_ds.z;
     }
+    if (kPre && i0 + kBwKT < L.N) issue(i0 + kBwKT);
     __syncthreads();
     // the query block's reference relative to this key's
     const float3 cqb = blk_ref(a, b, i0);
