@@ -545,7 +545,9 @@ __global__ __launch_bounds__(W * 64, NBUF == 1 ? 2 : 1) void flash_mfma_kernel(F
 // Merge the partial results of the KS key ranges of every (b, h, query):
 // weights 2^(m_s - m) for the range maxima m_s, values divided by the merged
 // ones-row sums, log-sum-exp from the merged fp32 sums.  One thread per four
-// output columns of a row.
+// output columns of a row; every load of a thread (the statistics and four
+// values of each range) is issued before any is used, the ranges past KS
+// reading range KS - 1 and weighing nothing.
 __global__ __launch_bounds__(256) void combine_kernel(Layout L, const float* part, float* o, float* lse) {
   const int DO = L.DO, n4 = (DO + 3) >> 2, H = L.H, N = L.N, KS = L.KS;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -555,24 +557,35 @@ __global__ __launch_bounds__(256) void combine_kernel(Layout L, const float* par
   const int h = (int)(row % H), i = (int)((row / H) % N), b = (int)(row / ((long)H * N));
   const size_t sstride = (size_t)L.B * H * L.NQpad * L.PREC;
   const float* rec0 = part + (((size_t)b * H + h) * L.NQpad + i) * L.PREC;
-  float m = -INFINITY;
-  for (int s = 0; s < KS; ++s) {
-    const float* st = rec0 + s * sstride + DO;
-    if (st[1] > 0.f) m = fmaxf(m, st[0]);
+  float sm[4], sl[4], sb[4], sh[4];
+  float4 v[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float* rec = rec0 + (size_t)min(s, KS - 1) * sstride;
+    sm[s] = rec[DO];
+    sl[s] = rec[DO + 1];
+    sb[s] = rec[DO + 2];
+    sh[s] = rec[DO + 3];
+    v[s] = *reinterpret_cast<const float4*>(rec + 4 * c4);
   }
+  float m = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    if (s < KS && sl[s] > 0.f) m = fmaxf(m, sm[s]);
   float ls = 0.f, lbf = 0.f, lh = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (m > -INFINITY) {
-    for (int s = 0; s < KS; ++s) {
-      const float* rec = rec0 + s * sstride;
-      const float* st = rec + DO;
-      if (!(st[1] > 0.f)) continue;  // an empty range holds no values
-      const float wgt = __builtin_amdgcn_exp2f(st[0] - m);
-      ls = fmaf(wgt, st[1], ls);
-      lbf = fmaf(wgt, st[2], lbf);
-      lh = fmaf(wgt, st[3], lh);
-      const float4 v = *reinterpret_cast<const float4*>(rec + 4 * c4);
-      acc[0] = fmaf(wgt, v.x, acc[0]); acc[1] = fmaf(wgt, v.y, acc[1]);
-      acc[2] = fmaf(wgt, v.z, acc[2]); acc[3] = fmaf(wgt, v.w, acc[3]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // an empty range (or one past KS) holds no values
+      // (its records may be unwritten: selected away, never multiplied)
+      if (s < KS && sl[s] > 0.f) {
+        const float wgt = __builtin_amdgcn_exp2f(sm[s] - m);
+        ls = fmaf(wgt, sl[s], ls);
+        lbf = fmaf(wgt, sb[s], lbf);
+        lh = fmaf(wgt, sh[s], lh);
+        acc[0] = fmaf(wgt, v[s].x, acc[0]); acc[1] = fmaf(wgt, v[s].y, acc[1]);
+        acc[2] = fmaf(wgt, v[s].z, acc[2]); acc[3] = fmaf(wgt, v[s].w, acc[3]);
+      }
     }
   }
   const bool nonempty = ls > 0.f;
