@@ -36,6 +36,13 @@
  *    IPA_OK or an ipa_status code without enqueuing anything; kernel launch
  *    failures are reported as IPA_ERR_LAUNCH.  Finite inputs are a
  *    precondition and are not checked.
+ *  - Tracing: every call that enqueues work is bracketed by a roctx range
+ *    named after the call (rocprofv3 --marker-trace).
+ *  - Debugging: with the environment variable FLASHIPA_DEBUG set to a
+ *    non-zero value (read once per process), every call also waits for its
+ *    kernels and returns IPA_ERR_LAUNCH, naming the call on stderr, when one
+ *    of them failed.  Calls then synchronise their stream, so this mode is
+ *    not for graph capture or timing.
  */
 #ifndef FLASHIPA_H
 #define FLASHIPA_H

@@ -1,7 +1,14 @@
 // C ABI of the FlashIPA library: argument validation, workspace layout and
 // kernel launches.  No allocation, no synchronisation: every kernel is
-// enqueued on the caller's stream.
+// enqueued on the caller's stream.  Each call is bracketed by a roctx range
+// named after it (rocprofv3 --marker-trace shows them); with the environment
+// variable FLASHIPA_DEBUG set to a non-zero value every call also waits for
+// its kernels and reports a failing one on stderr.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
+
+#include <cstdio>
+#include <cstdlib>
 
 #include "common.h"
 
@@ -39,7 +46,31 @@ static ipa_status shape_status(const ipa_shape* s, int with_pm, Layout* L) {
   return IPA_OK;
 }
 
-static ipa_status launch_status(hipError_t e) { return e == hipSuccess ? IPA_OK : IPA_ERR_LAUNCH; }
+// roctx range over one ABI call
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+};
+
+static bool debug_mode() {
+  static const bool on = [] {
+    const char* v = std::getenv("FLASHIPA_DEBUG");
+    return v != nullptr && v[0] != '\0' && v[0] != '0';
+  }();
+  return on;
+}
+
+// Status of a call whose kernels were enqueued with launch error e.  In debug
+// mode the call also waits for its kernels on `stream`, so that an error of a
+// kernel (not only of its launch) is reported here, with the call's name.
+static ipa_status launch_status(hipError_t e, const char* what, void* stream) {
+  if (e == hipSuccess && debug_mode()) {
+    e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess && debug_mode()) std::fprintf(stderr, "flashipa: %s: %s\n", what, hipGetErrorString(e));
+  return e == hipSuccess ? IPA_OK : IPA_ERR_LAUNCH;
+}
 
 extern "C" {
 
@@ -68,7 +99,8 @@ ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, siz
     if (!aligned16(p)) return IPA_ERR_ALIGN;
   if (!aligned16(lifted) || (in->pair_mask && !aligned16(in->pair_mask))) return IPA_ERR_ALIGN;
   if (lifted_bytes < L.total) return IPA_ERR_SHAPE;
-  return launch_status(fipa::launch_lift(L, in, lifted, reinterpret_cast<hipStream_t>(stream)));
+  const Range range("ipa_lift");
+  return launch_status(fipa::launch_lift(L, in, lifted, reinterpret_cast<hipStream_t>(stream)), "ipa_lift", stream);
 }
 
 ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream) {
@@ -80,8 +112,9 @@ ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float
   if (st != IPA_OK) return st;
   if (!aligned16(lifted) || !aligned16(o) || !aligned16(lse)) return IPA_ERR_ALIGN;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const Range range("ipa_flash_fwd");
   return launch_status(L.mfma ? fipa::launch_flash_mfma(L, lifted, o, lse, hs)
-                              : fipa::launch_flash_f32(L, lifted, o, lse, hs));
+                              : fipa::launch_flash_f32(L, lifted, o, lse, hs), "ipa_flash_fwd", stream);
 }
 
 size_t ipa_epilogue_workspace_bytes(const ipa_shape* s) {
@@ -107,8 +140,9 @@ ipa_status ipa_epilogue(const ipa_shape* s, void* workspace, size_t workspace_by
     return IPA_ERR_ALIGN;
   if (!fipa::epilogue_supported(L)) return IPA_ERR_UNSUPPORTED;
   if (workspace_bytes < L.epi_ws) return IPA_ERR_SHAPE;
+  const Range range("ipa_epilogue");
   return launch_status(fipa::launch_epilogue(L, workspace, o, lse, in, s->eps, update, local_points,
-                                             reinterpret_cast<hipStream_t>(stream)));
+                                             reinterpret_cast<hipStream_t>(stream)), "ipa_epilogue", stream);
 }
 
 ipa_status ipa_logit_rows(const ipa_shape* s, const void* lifted, int64_t b, int64_t h, int64_t row0, int64_t nrows,
@@ -120,8 +154,9 @@ ipa_status ipa_logit_rows(const ipa_shape* s, const void* lifted, int64_t b, int
   if (b < 0 || b >= s->B || h < 0 || h >= s->H || row0 < 0 || nrows <= 0 || row0 + nrows > s->N || nrows > 65535)
     return IPA_ERR_SHAPE;
   if (!aligned16(lifted) || !aligned16(out)) return IPA_ERR_ALIGN;
+  const Range range("ipa_logit_rows");
   return launch_status(fipa::launch_logit_rows(L, lifted, (int)b, (int)h, (int)row0, (int)nrows, out,
-                                               reinterpret_cast<hipStream_t>(stream)));
+                                               reinterpret_cast<hipStream_t>(stream)), "ipa_logit_rows", stream);
 }
 
 static ipa_status bw_shape_status(const ipa_shape* s) {
@@ -160,8 +195,9 @@ ipa_status ipa_backward(const ipa_shape* s, const ipa_lift_in* in, const ipa_epi
       (in->pair_mask && !aligned16(in->pair_mask)))
     return IPA_ERR_ALIGN;
   if (workspace_bytes < need) return IPA_ERR_SHAPE;
+  const Range range("ipa_backward");
   return launch_status(
-      fipa::launch_backward(s, in, epi, d_update, d_local, workspace, g, (hipStream_t)stream));
+      fipa::launch_backward(s, in, epi, d_update, d_local, workspace, g, (hipStream_t)stream), "ipa_backward", stream);
 }
 
 ipa_status ipa_knn_distogram(const ipa_knn_shape* s, const float* translation, const uint8_t* mask,
@@ -176,7 +212,8 @@ ipa_status ipa_knn_distogram(const ipa_knn_shape* s, const float* translation, c
   if (!aligned16(translation) || !aligned16(nn_index) || (mask && !aligned16(mask)) ||
       (nn_dist && !aligned16(nn_dist)) || (dgram && !aligned16(dgram)))
     return IPA_ERR_ALIGN;
-  return launch_status(fipa::launch_knn(s, translation, mask, nn_index, nn_dist, dgram, (hipStream_t)stream));
+  const Range range("ipa_knn_distogram");
+  return launch_status(fipa::launch_knn(s, translation, mask, nn_index, nn_dist, dgram, (hipStream_t)stream), "ipa_knn_distogram", stream);
 }
 
 static ipa_status bias_shape_status(const ipa_bias_shape* s) {
@@ -213,8 +250,9 @@ ipa_status ipa_bias_attention(const ipa_bias_shape* s, const void* q, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
       (phi_q && !aligned16(phi_q)) || (phi_k && !aligned16(phi_k)) || (key_mask && !aligned16(key_mask)))
     return IPA_ERR_ALIGN;
+  const Range range("ipa_bias_attention");
   return launch_status(fipa::launch_bias_attention(s, q, k, v, phi_q, phi_k, key_mask, o, lse, workspace,
-                                                   (hipStream_t)stream));
+                                                   (hipStream_t)stream), "ipa_bias_attention", stream);
 }
 
 const char* ipa_status_string(int status) {

@@ -14,6 +14,7 @@
 // GPU (different streams or host threads) race.  No kernel needs the array
 // cleared: each launch writes every byte it later reads.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <mutex>
 
@@ -61,6 +62,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+static ipa_status enqueue(const fipa::Layout& L, const ipa_lift_in* in, const ipa_epi_in* epi, float eps, char* base,
+                          size_t off_o, size_t off_lse, size_t off_epi, float* update, float* local_points,
+                          void* stream);
+
 extern "C" ipa_status ipa_forward_noalloc(const ipa_shape* s, const ipa_lift_in* in, const ipa_epi_in* epi,
                                           float* update, float* local_points, void* stream) {
   if (!s || !in || !epi || !update || !local_points) return IPA_ERR_NULL;
@@ -88,13 +93,22 @@ extern "C" ipa_status ipa_forward_noalloc(const ipa_shape* s, const ipa_lift_in*
 
   char* base = nullptr;
   if (scratch_address(&base) != hipSuccess) return IPA_ERR_DEVICE;
+  roctxRangePushA("ipa_forward_noalloc");
+  const ipa_status st = enqueue(L, in, epi, s->eps, base, off_o, off_lse, off_epi, update, local_points, stream);
+  roctxRangePop();
+  return st;
+}
+
+static ipa_status enqueue(const fipa::Layout& L, const ipa_lift_in* in, const ipa_epi_in* epi, float eps, char* base,
+                          size_t off_o, size_t off_lse, size_t off_epi, float* update, float* local_points,
+                          void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* o = reinterpret_cast<float*>(base + off_o);
   float* lse = reinterpret_cast<float*>(base + off_lse);
   if (fipa::launch_lift(L, in, base, st) != hipSuccess) return IPA_ERR_LAUNCH;
   const hipError_t e = L.mfma ? fipa::launch_flash_mfma(L, base, o, lse, st) : fipa::launch_flash_f32(L, base, o, lse, st);
   if (e != hipSuccess) return IPA_ERR_LAUNCH;
-  if (fipa::launch_epilogue(L, base + off_epi, o, lse, epi, s->eps, update, local_points, st) != hipSuccess)
+  if (fipa::launch_epilogue(L, base + off_epi, o, lse, epi, eps, update, local_points, st) != hipSuccess)
     return IPA_ERR_LAUNCH;
   return IPA_OK;
 }
