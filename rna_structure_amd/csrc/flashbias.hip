@@ -43,6 +43,7 @@ namespace {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kBiasLog2e = 1.4426950408889634f;
 constexpr float kBiasLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 16777216.0f;  // 2^24: largest per-lane tile weight sum kept without a new maximum
 
 struct BiasLayout {
   int B, N, M, H, D, Dv, R, causal, bf, bfp;
@@ -381,31 +382,21 @@ void bias_attn_kernel(BiasLayout L, const char* ws, const void* qin, const void*
         for (int r = 0; r < 16; ++r)
           s[kb * 16 + r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= lim) ? s[kb * 16 + r] : -INFINITY;
     }
-    float mt = s[0];
-#pragma unroll
-    for (int x = 1; x < 32; ++x) mt = fmaxf(mt, s[x]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    if (mt > m + 8.0f) {
-      // first permitted key of the row, or a maximum that grew by more than 8
-      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mt);
-      m = mt;
-      l *= alpha;
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[vb][r] *= alpha;
-    }
-    // while no key of the row has been permitted, m is -inf and so is every s:
-    // subtracting 0 instead keeps exp2(-inf) = 0
-    const float ms = m == -INFINITY ? 0.f : m;
+    // Probabilities against the running maximum m as it stands; the row
+    // maximum of the tile is only computed (and m raised) when a row has no
+    // reference yet (m = -inf) or when the tile's weights of a lane sum to
+    // more than kLazyMax (a weight above it, or infinite): the weights then
+    // stay below 2^24, which bf16 operands and fp32 sums hold, and most tiles
+    // need neither the maximum nor its exchange between the lane halves.
     // l sums the bf16-rounded weights that the value product multiplies
     // (two at a time, v_dot2 against ones, fp32 accumulation), so the weights
     // applied to V sum to one to fp32 rounding; the log-sum-exp then carries
     // their rounding (below 2^-9 relative in l)
     bf16x8_t pb[4];
+    float ps;
+    auto weights = [&](float ref) {
 #pragma unroll
-    for (int x = 0; x < 32; ++x) pb[x >> 3][x & 7] = (__bf16)__builtin_amdgcn_exp2f(s[x] - ms);
-    {
+      for (int x = 0; x < 32; ++x) pb[x >> 3][x & 7] = (__bf16)__builtin_amdgcn_exp2f(s[x] - ref);
       typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
       const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
       float ps0 = 0.f, ps1 = 0.f;
@@ -416,8 +407,37 @@ void bias_attn_kernel(BiasLayout L, const char* ws, const void* qin, const void*
         ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 4, 5), one2, ps0, false);
         ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[j], pb[j], 6, 7), one2, ps1, false);
       }
-      l += ps0 + ps1;
+      ps = ps0 + ps1;
+    };
+    bool exact = m == -INFINITY;
+    if (!__any(exact)) {
+      weights(m);
+      exact = !(ps <= kLazyMax);
     }
+    if (__any(exact)) {
+      float mt = s[0];
+#pragma unroll
+      for (int x = 1; x < 32; ++x) mt = fmaxf(mt, s[x]);
+      {
+        // the other lane half holds the same queries' other 32 keys
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(mt, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+      }
+      if (mt > m + 8.0f) {
+        // first permitted key of the row, or a maximum that grew by more than 8
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mt);
+        m = mt;
+        l *= alpha;
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[vb][r] *= alpha;
+      }
+      // while no key of the row has been permitted, m is -inf and so is every
+      // s: subtracting 0 instead keeps exp2(-inf) = 0
+      weights(m == -INFINITY ? 0.f : m);
+    }
+    l += ps;
 
     // O^T += V~^T P^T: K-step j covers keys 16 j .. 16 j + 15 of the tile
 #pragma unroll
