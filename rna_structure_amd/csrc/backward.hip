@@ -51,6 +51,8 @@ struct BwLayout {
   int B, N, H, D, Dv, P, Q, Cz, R, Cout, F;
   int DK, DV, P3, NK4, NV4, DKp, DVp;
   int ksplit;
+  int psplit;  // inner-loop ranges of the matrix-core pair passes (one workgroup each)
+  size_t off_opart, off_xqv, off_xqa, off_xgam, off_xkv, off_xkb, off_xvv;  // their partial results (psplit > 1)
   size_t off_gam, off_qv, off_kv, off_vv, off_qa, off_kb, off_o, off_lse, off_do, off_dd, off_ds, off_feat, off_dfeat,
       off_dqv, off_dqa, off_dgam, off_dkv, off_dkb, off_dvv, off_dzle, off_dre, off_dte, off_dwpart, off_ppart,
       total;
@@ -526,6 +528,72 @@ __global__ __launch_bounds__(4 * ROWS) void bw_key_kernel(BwArgs a) {
 // lane half h supplies key kappa(s, h) = 8 (s / 4) + 4 h + s % 4, the key its
 // register s holds, and reads the value row of that key.
 constexpr int kBwKT = 32;  // keys per tile of the matrix-core passes
+
+// Partner rows [*lo, *hi) of inner-loop range sp of the matrix-core pair
+// passes: the N / kBwKT partner tiles split into psplit ranges of whole tiles.
+__device__ __forceinline__ void split_range(const BwLayout& L, int sp, int* lo, int* hi) {
+  const int nt = (L.N + kBwKT - 1) / kBwKT;
+  *lo = (int)((long)nt * sp / L.psplit) * kBwKT;
+  *hi = min(L.N, (int)((long)nt * (sp + 1) / L.psplit) * kBwKT);
+}
+
+// Merge the psplit partial recomputations of a row (one thread per four
+// columns): weights e^(m_s - M) over the ranges with a nonzero sum, O' the
+// merged values (plus the merged reference offsets on the value points) over
+// the merged sum, lse = M + log(sum).  Rows without a permitted key get
+// zeros and -inf, as in the unsplit pass.
+__global__ __launch_bounds__(256) void bw_merge_o_kernel(BwArgs a) {
+  const BwLayout& L = a.L;
+  const size_t rows = (size_t)L.B * L.H * L.N;
+  const int n4 = L.DVp / 4, REC = L.DVp + 8;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * n4) return;
+  const size_t r = idx / n4;
+  const int c4 = (int)(idx - r * n4);
+  const float* part = wsf(a, L.off_opart);
+  float M = -INFINITY;
+  for (int s = 0; s < L.psplit; ++s) {
+    const float* rec = part + ((size_t)s * rows + r) * REC;
+    if (rec[L.DVp + 1] > 0.f) M = fmaxf(M, rec[L.DVp]);
+  }
+  float lsum = 0.f, cc[3] = {0.f, 0.f, 0.f}, o[4] = {0.f, 0.f, 0.f, 0.f};
+  if (M > -INFINITY) {
+    for (int s = 0; s < L.psplit; ++s) {
+      const float* rec = part + ((size_t)s * rows + r) * REC;
+      const float ls = rec[L.DVp + 1];
+      if (!(ls > 0.f)) continue;  // an empty range holds no values
+      const float wgt = expf(rec[L.DVp] - M);
+      lsum = fmaf(wgt, ls, lsum);
+      cc[0] = fmaf(wgt, rec[L.DVp + 2], cc[0]);
+      cc[1] = fmaf(wgt, rec[L.DVp + 3], cc[1]);
+      cc[2] = fmaf(wgt, rec[L.DVp + 4], cc[2]);
+      const float4 v = reinterpret_cast<const float4*>(rec)[c4];
+      o[0] = fmaf(wgt, v.x, o[0]); o[1] = fmaf(wgt, v.y, o[1]); o[2] = fmaf(wgt, v.z, o[2]); o[3] = fmaf(wgt, v.w, o[3]);
+    }
+  }
+  const bool empty = !(lsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / lsum;
+  const int pbase = L.Dv + L.R * L.Cz, pend = pbase + 3 * L.Q;
+  float e4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int col = 4 * c4 + e;
+    const float add = (col >= pbase && col < pend) ? cc[(col - pbase) % 3] : 0.f;
+    e4[e] = (o[e] + add) * inv;
+  }
+  reinterpret_cast<float4*>(wsf(a, L.off_o) + r * L.DVp)[c4] = make_float4(e4[0], e4[1], e4[2], e4[3]);
+  if (c4 == 0) wsf(a, L.off_lse)[r] = empty ? -INFINITY : M + logf(lsum);
+}
+
+// out[i] += sum of the ns slabs extra[z n + i] (the partial sums of the
+// inner-loop ranges 1 .. psplit-1 of a pair pass).
+__global__ __launch_bounds__(256) void bw_add_slabs_kernel(float* out, const float* extra, size_t n, int ns) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = out[i];
+  for (int z = 0; z < ns; ++z) v += extra[(size_t)z * n + i];
+  out[i] = v;
+}
 constexpr int kStageC = 2;  // loads per thread in flight at once where registers are short
 
 __device__ __forceinline__ int kappa(int s, int h) { return 8 * (s >> 2) + 4 * h + (s & 3); }
@@ -613,12 +681,15 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int q = blockIdx.x * 128 + 32 * w + l32;
+  const int qt = blockIdx.x / L.psplit, sp = blockIdx.x - qt * L.psplit;
+  const int q = qt * 128 + 32 * w + l32;
   const bool qin = q < L.N;
   const int qc = qin ? q : L.N - 1;
   const size_t rq = rowidx(L, b, h, qc);
   const float gam = wsf(a, L.off_gam)[h];
   const bool mq = qin && a.mask[(size_t)b * L.N + qc] != 0;
+  int jb, je;
+  split_range(L, sp, &jb, &je);
   // query operand: QV[q][s + DKH hf], s < DKH; point coordinates 8 hf .. +7
   float qv[DKH];
   {
@@ -667,8 +738,8 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
     const int j = min(j0 + (tid & 31), L.N - 1);
     tm = (j0 + (tid & 31) < L.N && a.mask[(size_t)b * L.N + j] != 0) ? 1.f : 0.f;
   };
-  issue(0);
-  for (int j0 = 0; j0 < L.N; j0 += kBwKT) {
+  issue(jb);
+  for (int j0 = jb; j0 < je; j0 += kBwKT) {
     __syncthreads();
     tk.store(tid, [&](int jj, int c4, float4 v) {
       sKT[4 * c4][jj] = v.x;
@@ -679,7 +750,7 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
     tv.store(tid, [&](int jj, int c4, float4 v) { reinterpret_cast<float4*>(&sV[jj][0])[c4] = v; });
     tb.store(tid, [&](int jj, int c4, float4 v) { reinterpret_cast<float4*>(&sBp[jj][0])[c4] = v; });
     if (tid < kBwKT) sM[tid] = tm;
-    if (j0 + kBwKT < L.N) issue(j0 + kBwKT);
+    if (j0 + kBwKT < je) issue(j0 + kBwKT);
     __syncthreads();
     // S^T: A = key tile (row = key l32, k = hf), B = query (k = hf, column = query l32)
     f32x16_t sacc = f32x16_t{};
@@ -742,6 +813,25 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
   cy += __shfl_xor(cy, 32);
   cz += __shfl_xor(cz, 32);
   if (!qin) return;
+  if (L.psplit > 1) {
+    // partial result of this key range: unnormalised O (value points without
+    // the reference offset), then m, the sum, and the offset sums
+    float* rec = wsf(a, L.off_opart) + ((size_t)sp * L.B * L.H * L.N + rq) * (L.DVp + 8);
+#pragma unroll
+    for (int v = 0; v < NVB; ++v)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * v + 8 * g + 4 * hf;
+        if (c < L.DVp)
+          *reinterpret_cast<float4*>(rec + c) =
+              make_float4(oacc[v][4 * g], oacc[v][4 * g + 1], oacc[v][4 * g + 2], oacc[v][4 * g + 3]);
+      }
+    if (hf == 0) {
+      *reinterpret_cast<float4*>(rec + L.DVp) = make_float4(m, lsum, cx, cy);
+      rec[L.DVp + 4] = cz;
+    }
+    return;
+  }
   const bool empty = !(lsum > 0.f);
   const float inv = empty ? 0.f : 1.f / lsum;
   // O' : the value points relative to the query's block reference
@@ -800,12 +890,15 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int q = blockIdx.x * 128 + 32 * w + l32;
+  const int qt = blockIdx.x / L.psplit, sp = blockIdx.x - qt * L.psplit;
+  const int q = qt * 128 + 32 * w + l32;
   const bool qin = q < L.N;
   const int qc = qin ? q : L.N - 1;
   const size_t rq = rowidx(L, b, h, qc);
   const float gam = wsf(a, L.off_gam)[h];
   const float lse = wsf(a, L.off_lse)[rq];
+  int jb, je;
+  split_range(L, sp, &jb, &je);
   const float dsum = wsf(a, L.off_dd)[rq];
   const float4 sv = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + rq * 4)[0];
   const float3 cq = blk_ref(a, b, qc);
@@ -815,7 +908,7 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   // B operands: QV[q][s + DKH hf] from LDS, dO[q][s + DVH hf] in registers
   for (int e = lane; e < 32 * (DKp / 4); e += 64) {
     const int qq = e / (DKp / 4), c4 = e - qq * (DKp / 4);
-    const int qr = min(blockIdx.x * 128 + 32 * w + qq, L.N - 1);
+    const int qr = min(qt * 128 + 32 * w + qq, L.N - 1);
     const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_qv) + rowidx(L, b, h, qr) * L.DKp)[c4];
     *reinterpret_cast<float4*>(&sQ[w][qq][4 * c4]) = v;
   }
@@ -846,7 +939,7 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   const float* kvb = wsf(a, L.off_kv) + rowidx(L, b, h, 0) * L.DKp;
   const float* vvb = wsf(a, L.off_vv) + rowidx(L, b, h, 0) * L.DVp;
   const float* kbb = wsf(a, L.off_kb) + rowidx(L, b, h, 0) * 16;
-  for (int j0 = 0; j0 < L.N; j0 += kBwKT) {
+  for (int j0 = jb; j0 < je; j0 += kBwKT) {
     __syncthreads();
     {
       // one tensor at a time: its loads together, then its LDS writes (the
@@ -924,7 +1017,9 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   for (int u = 0; u < P3C; ++u) da[u] += __shfl_xor(da[u], 32);
   dg += __shfl_xor(dg, 32);
   if (!qin) return;
-  float* orow = wsf(a, L.off_dqv) + rq * L.DKp;
+  // key range sp > 0 writes its partial sums to a slab of its own
+  const size_t rows = (size_t)L.B * L.H * L.N, xs = (size_t)(sp - 1);
+  float* orow = (sp == 0 ? wsf(a, L.off_dqv) : wsf(a, L.off_xqv) + xs * rows * L.DKp) + rq * L.DKp;
 #pragma unroll
   for (int c = 0; c < NKB; ++c)
 #pragma unroll
@@ -934,7 +1029,7 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
         *reinterpret_cast<float4*>(orow + f) = make_float4(dq[c][4 * g], dq[c][4 * g + 1], dq[c][4 * g + 2], dq[c][4 * g + 3]);
     }
   if (hf == 0) {
-    float* arow = wsf(a, L.off_dqa) + rq * 16;
+    float* arow = (sp == 0 ? wsf(a, L.off_dqa) : wsf(a, L.off_xqa) + xs * rows * 16) + rq * 16;
 #pragma unroll
     for (int u4 = 0; u4 < 4; ++u4) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -943,7 +1038,7 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
                         -2.f * gam * da[4 * u4 + 3]);
       reinterpret_cast<float4*>(arow)[u4] = v;
     }
-    wsf(a, L.off_dgam)[rq] = dg;
+    (sp == 0 ? wsf(a, L.off_dgam) : wsf(a, L.off_xgam) + xs * rows)[rq] = dg;
   }
 }
 
@@ -978,8 +1073,11 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int j = blockIdx.x * 128 + 32 * w + l32;
+  const int kt = blockIdx.x / L.psplit, sp = blockIdx.x - kt * L.psplit;
+  const int j = kt * 128 + 32 * w + l32;
   const bool kin = j < L.N;
+  int ib, ie;
+  split_range(L, sp, &ib, &ie);
   const int jc = kin ? j : L.N - 1;
   const size_t rj = rowidx(L, b, h, jc);
   const float gam = wsf(a, L.off_gam)[h];
@@ -990,7 +1088,7 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
   for (int e = tid; e < (32 * NVB - DVp) * (kBwKT + 1); e += 256) sDT[DVp + e / (kBwKT + 1)][e % (kBwKT + 1)] = 0.f;
   for (int e = lane; e < 32 * (DKp / 4); e += 64) {
     const int kk = e / (DKp / 4), c4 = e - kk * (DKp / 4);
-    const int kr = min(blockIdx.x * 128 + 32 * w + kk, L.N - 1);
+    const int kr = min(kt * 128 + 32 * w + kk, L.N - 1);
     const float4 v = reinterpret_cast<const float4*>(wsf(a, L.off_kv) + rowidx(L, b, h, kr) * L.DKp)[c4];
     sK[w][kk][4 * c4] = v.x; sK[w][kk][4 * c4 + 1] = v.y; sK[w][kk][4 * c4 + 2] = v.z; sK[w][kk][4 * c4 + 3] = v.w;
   }
@@ -1049,8 +1147,8 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
     sDT[4 * c4][ii] = v.x; sDT[4 * c4 + 1][ii] = v.y; sDT[4 * c4 + 2][ii] = v.z; sDT[4 * c4 + 3][ii] = v.w;
   };
   auto put_a = [&](int ii, int c4, float4 v) { reinterpret_cast<float4*>(&sA[ii][0])[c4] = v; };
-  if (kPre) issue(0);
-  for (int i0 = 0; i0 < L.N; i0 += kBwKT) {
+  if (kPre) issue(ib);
+  for (int i0 = ib; i0 < ie; i0 += kBwKT) {
     __syncthreads();
     if constexpr (kPre) {
       tq.store(tid, put_q);
@@ -1086,7 +1184,7 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
       sSy[tid] = t_ds.y;
       sSz[tid] = t_ds.z;
     }
-    if (kPre && i0 + kBwKT < L.N) issue(i0 + kBwKT);
+    if (kPre && i0 + kBwKT < ie) issue(i0 + kBwKT);
     __syncthreads();
     // the query block's reference relative to this key's
     const float3 cqb = blk_ref(a, b, i0);
@@ -1149,8 +1247,10 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
 #pragma unroll
   for (int u = 0; u < P3C; ++u) db[u] += __shfl_xor(db[u], 32);
   if (!kin) return;
-  float* krw = wsf(a, L.off_dkv) + rj * L.DKp;
-  float* vrw = wsf(a, L.off_dvv) + rj * L.DVp;
+  // query range sp > 0 writes its partial sums to a slab of its own
+  const size_t rows = (size_t)L.B * L.H * L.N, xs = (size_t)(sp - 1);
+  float* krw = (sp == 0 ? wsf(a, L.off_dkv) : wsf(a, L.off_xkv) + xs * rows * L.DKp) + rj * L.DKp;
+  float* vrw = (sp == 0 ? wsf(a, L.off_dvv) : wsf(a, L.off_xvv) + xs * rows * L.DVp) + rj * L.DVp;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
 #pragma unroll
@@ -1167,7 +1267,7 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
     }
   }
   if (kDS && hf == 0) {
-    float* brow = wsf(a, L.off_dkb) + rj * 16;
+    float* brow = (sp == 0 ? wsf(a, L.off_dkb) : wsf(a, L.off_xkb) + xs * rows * 16) + rj * 16;
 #pragma unroll
     for (int u4 = 0; u4 < 4; ++u4) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1551,19 +1651,39 @@ hipError_t launch_pairs(const BwArgs& a, int which, hipStream_t st) {
 
 hipError_t launch_pairs_inst(const BwArgs& a, int which, hipStream_t st) {
   const BwLayout& L = a.L;
+  // the matrix-core passes take psplit workgroups per row tile, one per
+  // inner-loop range (psplit > 1 only with every pass on the matrix cores)
+  const dim3 grid((L.N + 127) / 128 * L.psplit, L.H, L.B);
+  const size_t rows = (size_t)L.B * L.H * L.N;
+  const int xs = L.psplit - 1;
+  auto add = [&](size_t out, size_t extra, size_t n) {
+    hipLaunchKernelGGL(bw_add_slabs_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<float*>(a.ws + out), reinterpret_cast<const float*>(a.ws + extra), n, xs);
+  };
   if (which == 0 && L.NK4 == 9) {
     // standard shape (D + R Cz <= 144, Dv + R Cz + 3Q <= 176): matrix cores
-    hipLaunchKernelGGL((bw_fwd_mfma_kernel<72, 6>), dim3((L.N + 127) / 128, L.H, L.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bw_fwd_mfma_kernel<72, 6>), grid, dim3(256), 0, st, a);
+    if (L.psplit > 1)
+      hipLaunchKernelGGL(bw_merge_o_kernel, dim3((unsigned)((rows * (L.DVp / 4) + 255) / 256)), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (which == 2 && L.NK4 == 9 && L.DVp == 176 && L.P3 == 12) {
-    const dim3 grid((L.N + 127) / 128, L.H, L.B);
     hipLaunchKernelGGL((bw_key_mfma_kernel<72, 88, 5, 6, 12, 0>), grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((bw_key_mfma_kernel<72, 88, 5, 6, 12, 1>), grid, dim3(256), 0, st, a);
+    if (L.psplit > 1) {
+      add(L.off_dkv, L.off_xkv, rows * L.DKp);
+      add(L.off_dkb, L.off_xkb, rows * 16);
+      add(L.off_dvv, L.off_xvv, rows * L.DVp);
+    }
     return hipGetLastError();
   }
   if (which == 1 && L.NK4 == 9 && L.DVp == 176 && L.P3 == 12) {
-    hipLaunchKernelGGL((bw_query_mfma_kernel<72, 88, 5, 12>), dim3((L.N + 127) / 128, L.H, L.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bw_query_mfma_kernel<72, 88, 5, 12>), grid, dim3(256), 0, st, a);
+    if (L.psplit > 1) {
+      add(L.off_dqv, L.off_xqv, rows * L.DKp);
+      add(L.off_dqa, L.off_xqa, rows * 16);
+      add(L.off_dgam, L.off_xgam, rows);
+    }
     return hipGetLastError();
   }
   if (L.NK4 == 1) return launch_pairs<1, 2>(a, which, st);
@@ -1609,6 +1729,16 @@ bool bw_layout(const ipa_shape* s, BwLayout* L) {
   L->DVp = 16 * L->NV4;
   const size_t rows = (size_t)L->B * L->H * L->N, bn = (size_t)L->B * L->N;
   L->ksplit = (int)std::min<size_t>(64, std::max<size_t>(1, bn / 256));
+  // Short chains: the pair passes' grids (128-row tiles x H x B) would leave
+  // CUs idle, so each row tile's inner loop is split into psplit ranges of at
+  // least 8 partner tiles (up to 4 ranges, while the grid stays within 256
+  // workgroups), the partial results merged by small kernels.  Only when all
+  // three passes run on the matrix cores (standard widths).
+  const bool mfma_all = L->NK4 == 9 && L->DVp == 176 && L->P3 == 12;
+  const size_t row_tiles = (size_t)((L->N + 127) / 128) * L->H * L->B;
+  L->psplit = 1;
+  while (mfma_all && L->psplit < 4 && row_tiles * L->psplit * 2 <= 256 && (size_t)L->N >= (size_t)512 * L->psplit)
+    L->psplit *= 2;
   size_t off = 256;
   auto take = [&](size_t floats) {
     const size_t o = off;
@@ -1639,6 +1769,14 @@ bool bw_layout(const ipa_shape* s, BwLayout* L) {
   L->off_dte = take(bn * 3);
   L->off_dwpart = take((size_t)L->ksplit * (L->F + 1) * L->Cout);
   L->off_ppart = take((size_t)L->H * kBwParamChunks * (L->Cz + 1));
+  const size_t xs = (size_t)(L->psplit - 1);
+  L->off_opart = L->psplit > 1 ? take((size_t)L->psplit * rows * (L->DVp + 8)) : 0;
+  L->off_xqv = xs ? take(xs * rows * L->DKp) : 0;
+  L->off_xqa = xs ? take(xs * rows * 16) : 0;
+  L->off_xgam = xs ? take(xs * rows) : 0;
+  L->off_xkv = xs ? take(xs * rows * L->DKp) : 0;
+  L->off_xkb = xs ? take(xs * rows * 16) : 0;
+  L->off_xvv = xs ? take(xs * rows * L->DVp) : 0;
   L->bf16 = s->dtype == IPA_BF16;
   const size_t bnh = bn * L->H;
   const size_t cn[14] = {bnh * L->D, bnh * L->D, bnh * L->Dv, bnh * L->P * 3, bnh * L->P * 3, bnh * L->Q * 3, bn * 9,

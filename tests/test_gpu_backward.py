@@ -54,6 +54,13 @@ CASES = [
     # bf16 inputs: widened to fp32 inside, gradients at the bf16 values
     ("standard-bf16-inputs", IPAShape(B=1, N=120, H=4, dtype="bf16"), 10,
      dict(frames="walk", step=3.8, pair_dropout=0.05, empty_row=True)),
+    # short chains at the standard widths: each pair pass splits its inner
+    # loop over keys or queries into 4 (N=1024) or 2 (B2 N600, ragged ranges)
+    # workgroups per row tile, the partial results merged afterwards
+    ("split4-n1024", IPAShape(B=1, N=1024, H=8, dtype="f32"), 11,
+     dict(frames="walk", step=3.8, masked_keys=(1023,), pair_dropout=0.05)),
+    ("split2-ragged-b2", IPAShape(B=2, N=600, H=8, dtype="f32"), 12,
+     dict(frames="walk", step=3.8, lengths=(431, 600), pair_dropout=0.05, empty_row=True)),
     # 512 workgroups per pass: the key pass runs as two launches (dK/dB, then dV)
     ("split-key-pass", IPAShape(B=16, N=256, H=8, D=4, Dv=3, P=2, Q=2, Cz=5, R=2, Cout=6, dtype="f32"), 9,
      dict(frames="walk", step=3.8, lengths=(200, 256), pair_dropout=0.05)),
