@@ -97,63 +97,91 @@ __device__ __forceinline__ float3 blk_ref(const BwArgs& a, int b, int n) {
 __device__ __forceinline__ float softplusf(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
 
 // ------------------------------------------------------------------ prep
-// One thread per (b, h, residue): the plain rows QV, KV, VV, A, B.
+// The plain rows QV, KV, VV, A, B of 32 residues of one (b, h) per
+// workgroup.  Threads walk the 4-float pieces of the rows, so that
+// consecutive lanes read consecutive inputs and store consecutive addresses.
+constexpr int kPrepRows = 32;
 __global__ __launch_bounds__(256) void bw_prep_kernel(BwArgs a) {
   const BwLayout& L = a.L;
-  const int n = blockIdx.x * 256 + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  if (b == 0 && n == 0 && h == 0) {
+  const int n0 = blockIdx.x * kPrepRows, nr = min(kPrepRows, L.N - n0);
+  if (b == 0 && blockIdx.x == 0 && h == 0 && threadIdx.x == 0) {
     for (int hh = 0; hh < L.H; ++hh)
       wsf(a, L.off_gam)[hh] = 0.5f * softplusf(a.wraw[hh]) * sqrtf(2.0f / (27.0f * (float)L.P));
   }
-  if (n >= L.N) return;
-  const size_t ri = rowidx(L, b, h, n);
-  const size_t bn = (size_t)b * L.N + n;
-  const float* R = a.rot + bn * 9;
-  const float* t = a.tr + bn * 3;
   const float sq = 1.0f / sqrtf(3.0f * (float)L.D), s3 = 1.0f / sqrtf(3.0f);
-  float* qv = wsf(a, L.off_qv) + ri * L.DKp;
-  float* kv = wsf(a, L.off_kv) + ri * L.DKp;
-  float* vv = wsf(a, L.off_vv) + ri * L.DVp;
-  float* qa = wsf(a, L.off_qa) + ri * 16;
-  float* kb = wsf(a, L.off_kb) + ri * 16;
-  const float* qrow = a.q + (bn * L.H + h) * L.D;
-  const float* krow = a.k + (bn * L.H + h) * L.D;
-  const float* vrow = a.v + (bn * L.H + h) * L.Dv;
-  const float* zlr = a.zl + bn * L.R * L.Cz;
-  const float* zrr = a.zr + bn * L.R * L.Cz;
-  int c = 0;
-  for (int d = 0; d < L.D; ++d, ++c) {
-    qv[c] = qrow[d] * sq;
-    kv[c] = krow[d];
+  const int RCz = L.R * L.Cz;
+  // QV = [q / sqrt(3D) | w_pair zl / sqrt(3) | 0], KV = [k | zr | 0]
+  const int k4 = L.DKp / 4;
+  for (int x = threadIdx.x; x < nr * k4; x += 256) {
+    const int rr = x / k4, c4 = x - rr * k4, n = n0 + rr;
+    const size_t bn = (size_t)b * L.N + n, ri = rowidx(L, b, h, n);
+    float qv[4], kv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 4 * c4 + e;
+      if (c < L.D) {
+        qv[e] = a.q[(bn * L.H + h) * L.D + c] * sq;
+        kv[e] = a.k[(bn * L.H + h) * L.D + c];
+      } else if (c < L.D + RCz) {
+        const int idx = c - L.D, z = idx % L.Cz;
+        qv[e] = a.wpair[h * L.Cz + z] * a.zl[bn * RCz + idx] * s3;
+        kv[e] = a.zr[bn * RCz + idx];
+      } else {
+        qv[e] = kv[e] = 0.f;
+      }
+    }
+    reinterpret_cast<float4*>(wsf(a, L.off_qv) + ri * L.DKp)[c4] = make_float4(qv[0], qv[1], qv[2], qv[3]);
+    reinterpret_cast<float4*>(wsf(a, L.off_kv) + ri * L.DKp)[c4] = make_float4(kv[0], kv[1], kv[2], kv[3]);
   }
-  for (int r = 0; r < L.R; ++r)
-    for (int z = 0; z < L.Cz; ++z, ++c) {
-      qv[c] = a.wpair[h * L.Cz + z] * zlr[r * L.Cz + z] * s3;
-      kv[c] = zrr[r * L.Cz + z];
+  // VV = [v | zr | T(v_points) relative to the block reference (t - c
+  // first: exact) | 0]
+  const int v4 = L.DVp / 4, pbase = L.Dv + RCz, pend = pbase + 3 * L.Q;
+  for (int x = threadIdx.x; x < nr * v4; x += 256) {
+    const int rr = x / v4, c4 = x - rr * v4, n = n0 + rr;
+    const size_t bn = (size_t)b * L.N + n, ri = rowidx(L, b, h, n);
+    float vv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 4 * c4 + e;
+      if (c < L.Dv) {
+        vv[e] = a.v[(bn * L.H + h) * L.Dv + c];
+      } else if (c < pbase) {
+        vv[e] = a.zr[bn * RCz + (c - L.Dv)];
+      } else if (c < pend) {
+        const int qq = (c - pbase) / 3, m = (c - pbase) - 3 * qq;
+        const float* R = a.rot + bn * 9;
+        const float* x3 = a.vp + ((bn * L.H + h) * L.Q + qq) * 3;
+        const float3 cr = blk_ref(a, b, n);
+        const float tc = a.tr[bn * 3 + m] - (m == 0 ? cr.x : (m == 1 ? cr.y : cr.z));
+        vv[e] = R[m * 3 + 0] * x3[0] + R[m * 3 + 1] * x3[1] + R[m * 3 + 2] * x3[2] + tc;
+      } else {
+        vv[e] = 0.f;
+      }
     }
-  for (; c < L.DKp; ++c) qv[c] = kv[c] = 0.f;
-  c = 0;
-  for (int d = 0; d < L.Dv; ++d) vv[c++] = vrow[d];
-  for (int e = 0; e < L.R * L.Cz; ++e) vv[c++] = zrr[e];
-  {
-    // value points relative to the block reference (t - c first: exact)
-    const float3 cr = blk_ref(a, b, n);
-    const float tc[3] = {t[0] - cr.x, t[1] - cr.y, t[2] - cr.z};
-    for (int qq = 0; qq < L.Q; ++qq) {
-      const float* x = a.vp + ((bn * L.H + h) * L.Q + qq) * 3;
-      for (int m = 0; m < 3; ++m) vv[c++] = R[m * 3 + 0] * x[0] + R[m * 3 + 1] * x[1] + R[m * 3 + 2] * x[2] + tc[m];
-    }
+    reinterpret_cast<float4*>(wsf(a, L.off_vv) + ri * L.DVp)[c4] = make_float4(vv[0], vv[1], vv[2], vv[3]);
   }
-  for (; c < L.DVp; ++c) vv[c] = 0.f;
-  for (int p = 0; p < 16; ++p) qa[p] = kb[p] = 0.f;
-  for (int p = 0; p < L.P; ++p) {
-    const float* xq = a.qp + ((bn * L.H + h) * L.P + p) * 3;
-    const float* xk = a.kp + ((bn * L.H + h) * L.P + p) * 3;
-    for (int m = 0; m < 3; ++m) {
-      qa[3 * p + m] = R[m * 3 + 0] * xq[0] + R[m * 3 + 1] * xq[1] + R[m * 3 + 2] * xq[2] + t[m];
-      kb[3 * p + m] = R[m * 3 + 0] * xk[0] + R[m * 3 + 1] * xk[1] + R[m * 3 + 2] * xk[2] + t[m];
+  // A = T(q_points), B = T(k_points), 16 coordinates each (zero past 3P)
+  for (int x = threadIdx.x; x < nr * 4; x += 256) {
+    const int rr = x >> 2, c4 = x & 3, n = n0 + rr;
+    const size_t bn = (size_t)b * L.N + n, ri = rowidx(L, b, h, n);
+    const float* R = a.rot + bn * 9;
+    const float* t = a.tr + bn * 3;
+    float qa[4], kb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 4 * c4 + e;
+      qa[e] = kb[e] = 0.f;
+      if (c < 3 * L.P) {
+        const int p = c / 3, m = c - 3 * p;
+        const float* xq = a.qp + ((bn * L.H + h) * L.P + p) * 3;
+        const float* xk = a.kp + ((bn * L.H + h) * L.P + p) * 3;
+        qa[e] = R[m * 3 + 0] * xq[0] + R[m * 3 + 1] * xq[1] + R[m * 3 + 2] * xq[2] + t[m];
+        kb[e] = R[m * 3 + 0] * xk[0] + R[m * 3 + 1] * xk[1] + R[m * 3 + 2] * xk[2] + t[m];
+      }
     }
+    reinterpret_cast<float4*>(wsf(a, L.off_qa) + ri * 16)[c4] = make_float4(qa[0], qa[1], qa[2], qa[3]);
+    reinterpret_cast<float4*>(wsf(a, L.off_kb) + ri * 16)[c4] = make_float4(kb[0], kb[1], kb[2], kb[3]);
   }
 }
 
@@ -1850,7 +1878,7 @@ hipError_t launch_backward(const ipa_shape* s, const ipa_lift_in* in, const ipa_
   a.gbout = gr->b_out;
   hipError_t e;
   const int BN = L.B * L.N;
-  hipLaunchKernelGGL(bw_prep_kernel, dim3((L.N + 255) / 256, L.H, L.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bw_prep_kernel, dim3((L.N + kPrepRows - 1) / kPrepRows, L.H, L.B), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_pairs_inst(a, 0, st)) != hipSuccess) return e;
   // DFEAT[bn][f] = sum_c dU[bn][c] w_out[f][c]
