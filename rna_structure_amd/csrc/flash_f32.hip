@@ -25,9 +25,13 @@ struct FlashF32Args {
 };
 
 constexpr int kF32Keys = 32;  // keys staged per step
-constexpr int kF32DvPer = kF32MaxDV / 4;
 
+// MDQ, MDV: compile-time bounds on D + R Cz and on the output row width, so
+// that the per-key loops run over the columns a shape has (two instances:
+// narrow rows, and up to kF32MaxDQ / kF32MaxDV)
+template <int MDQ, int MDV>
 __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
+  constexpr int kF32DvPer = MDV / 4;
   const Layout& L = a.L;
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -46,10 +50,10 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
   const float gl = gam * kLog2e;
   const bool qin = i < N;
 
-  float qv[kF32MaxDQ];
+  float qv[MDQ];
   const float* qrow = reinterpret_cast<const float*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + i) * L.DQP;
 #pragma unroll
-  for (int d = 0; d < kF32MaxDQ; ++d) qv[d] = (qin && d < DQ) ? qrow[d] : 0.f;
+  for (int d = 0; d < MDQ; ++d) qv[d] = (qin && d < DQ) ? qrow[d] : 0.f;
   float av[15];
   const float* arow = reinterpret_cast<const float*>(a.ws + L.off_qa) + (((size_t)b * H + h) * L.NQpad + i) * 16;
 #pragma unroll
@@ -112,17 +116,18 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
       const bool perm = (((hf ? w1 : w0) >> bit) & 1u) != 0;
       if (!perm) continue;
       const float* kr = sk + jl * KROW;
+      // branch-free column loops (the LDS reads then go out together):
+      // columns past DQ read column 0 against a zero query column, point
+      // coordinates past 3P give a zero difference
       float s = 0.f;
 #pragma unroll
-      for (int d = 0; d < kF32MaxDQ; ++d)
-        if (d < DQ) s = fmaf(qv[d], kr[d], s);
+      for (int d = 0; d < MDQ; ++d) s = fmaf(qv[d], kr[d < DQ ? d : 0], s);
       float dist = 0.f;
 #pragma unroll
-      for (int g = 0; g < 15; ++g)
-        if (g < P3) {
-          const float df = dA[g] - kr[DQ + g];
-          dist = fmaf(df, df, dist);
-        }
+      for (int g = 0; g < 15; ++g) {
+        const float df = g < P3 ? dA[g] - kr[DQ + (g < P3 ? g : 0)] : 0.f;
+        dist = fmaf(df, df, dist);
+      }
       s = fmaf(-gl, dist, s);
       if (s > m) {
         const float alpha = exp2f(m - s);  // m = -inf -> 0
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
 #pragma unroll
       for (int e = 0; e < kF32DvPer; ++e) {
         const int d = e * 4 + part;
-        if (d < DO) ov[e] = fmaf(p, vr[d], ov[e]);
+        ov[e] = fmaf(d < DO ? p : 0.f, vr[d < DO ? d : 0], ov[e]);
       }
       cs0 = fmaf(p, c4.x, cs0); cs1 = fmaf(p, c4.y, cs1); cs2 = fmaf(p, c4.z, cs2);
     }
@@ -170,7 +175,10 @@ hipError_t launch_flash_f32(const Layout& L, const void* ws, float* o, float* ls
   a.lse = lse;
   const size_t shm = (size_t)kF32Keys * (L.KROW + L.VROWS) * sizeof(float);
   dim3 grid((L.N + 63) / 64, L.H, L.B);
-  hipLaunchKernelGGL(flash_f32_kernel, grid, dim3(256), shm, st, a);
+  if (L.D + L.RCz <= 64 && L.DO <= 96)
+    hipLaunchKernelGGL((flash_f32_kernel<64, 96>), grid, dim3(256), shm, st, a);
+  else
+    hipLaunchKernelGGL((flash_f32_kernel<kF32MaxDQ, kF32MaxDV>), grid, dim3(256), shm, st, a);
   return hipGetLastError();
 }
 
