@@ -91,6 +91,23 @@ def lift_bytes(shape, with_pm: bool) -> float:
     return shape.B * shape.N * per_res + extra
 
 
+def lift_method_bytes(shape, with_pm: bool) -> float:
+    """HBM bytes of the lift as the method lays its rows out (Flash IPA page,
+    the factorised logit): the same inputs read once, and per head a query
+    row and a key row of d_qk = D + 3P + 2 + R Cz columns and a value row of
+    d_v = Dv + 3Q + R Cz columns written in 16-bit, the pair factors inside
+    every head's rows.  The lift here shares the pair-factor rows among the
+    heads and moves fewer bytes (lift_bytes); this count is the work of the
+    method, as flops count the method's products."""
+    H, R, Cz = shape.H, shape.R, shape.Cz
+    rd = 2 * H * (2 * shape.D + shape.Dv) + 2 * 3 * H * (2 * shape.P + shape.Q) + 2 * 12 + 2 * 2 * R * Cz + 1
+    d_qk = shape.D + 3 * shape.P + 2 + R * Cz
+    d_v = shape.Dv + 3 * shape.Q + R * Cz
+    wr = H * (2 * d_qk + d_v) * 2
+    extra = shape.B * shape.N * shape.N if with_pm else 0
+    return shape.B * shape.N * (rd + wr) + extra
+
+
 def epilogue_bytes(shape) -> float:
     """Algorithmic HBM bytes of the epilogue: O, lse, zl and frames read, the
     update and local points written, per residue (w_out once)."""
@@ -613,7 +630,7 @@ def main():
         cpu_oracle_main(kind, arg, float(budget), int(workers))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
@@ -672,6 +689,11 @@ def main():
                    "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
             for name, nb, ms in (("lift", lift_bytes(shape, inp["pair_mask"] is not None), r["lift_ms"]),
                                  ("epilogue", epilogue_bytes(shape), r["epilogue_ms"]))},
+        "lift_method_layout": {
+            "bytes": round(lift_method_bytes(shape, inp["pair_mask"] is not None)),
+            "achieved_GBs": round(lift_method_bytes(shape, inp["pair_mask"] is not None) / (r["lift_ms"] * 1e-3) / 1e9, 1),
+            "frac": round(lift_method_bytes(shape, inp["pair_mask"] is not None) / (r["lift_ms"] * 1e-3) / 1e9
+                          / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "kernel": "flash_mfma_kernel", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
