@@ -94,6 +94,14 @@ __device__ __forceinline__ float3 blk_ref(const BwArgs& a, int b, int n) {
   return make_float3(rintf(t[0]), rintf(t[1]), rintf(t[2]));
 }
 
+// e^x as 2^(x log2 e) on v_exp_f32 (two instructions; expf's range reduction
+// and special-case selects take about twelve).  The rounding of the product
+// adds a relative error of about |x| 2^-24: below 1e-6 for every argument
+// whose result is not negligible against the others of its row.  Used by the
+// matrix-core passes, whose vector-ALU work does not overlap their fp32
+// matrix instructions.
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
 __device__ __forceinline__ float softplusf(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
 
 // ------------------------------------------------------------------ prep
@@ -806,7 +814,7 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     if (tmax > m + 5.0f) {  // raise the running maximum (lazily: values up to e^5 are fine)
-      const float c = expf(m - tmax);
+      const float c = exp_fast(m - tmax);
       lsum *= c;
       cx *= c;
       cy *= c;
@@ -819,7 +827,7 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
     float tsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pr[r] = lg[r] > -INFINITY ? expf(lg[r] - m) : 0.f;
+      pr[r] = lg[r] > -INFINITY ? exp_fast(lg[r] - m) : 0.f;
       tsum += pr[r];
     }
     lsum += tsum;
@@ -1027,7 +1035,7 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
         d2 += dif[4 * c4] * dif[4 * c4] + dif[4 * c4 + 1] * dif[4 * c4 + 1] + dif[4 * c4 + 2] * dif[4 * c4 + 2] +
               dif[4 * c4 + 3] * dif[4 * c4 + 3];
       }
-      const float p = ok ? expf(sa[r] - gam * d2 - lse) : 0.f;
+      const float p = ok ? exp_fast(sa[r] - gam * d2 - lse) : 0.f;
       ds[r] = p * (pa[r] - corr);
 #pragma unroll
       for (int u = 0; u < P3C; ++u) da[u] = fmaf(ds[r], dif[u], da[u]);
@@ -1249,7 +1257,7 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
         d2 += dif[4 * c4] * dif[4 * c4] + dif[4 * c4 + 1] * dif[4 * c4 + 1] + dif[4 * c4 + 2] * dif[4 * c4 + 2] +
               dif[4 * c4 + 3] * dif[4 * c4 + 3];
       }
-      pr[r] = ok ? expf(sa[r] - gam * d2 - sL[qq]) : 0.f;
+      pr[r] = ok ? exp_fast(sa[r] - gam * d2 - sL[qq]) : 0.f;
       if constexpr (kDS) {
         const float corr = fmaf(sSx[qq], dcx, fmaf(sSy[qq], dcy, fmaf(sSz[qq], dcz, sS[qq])));
         ds[r] = pr[r] * (pa[r] - corr);
