@@ -699,7 +699,30 @@ __device__ __forceinline__ void stage_tile(const float* base, int stride, int j0
   }
 }
 
-template <int DKH, int NVB>
+// Permission bits of one 32-key tile for a query lane: bit r for key
+// kappa(r, hf) of the tile (keys past the chain's end, masked keys, and with
+// a pair mask the pairs it removes are 0).  Computed once per tile so that
+// the per-element work has no branches; the pair-mask loads of a tile go out
+// together (their index clamped into the row; the clamped ones are masked
+// by the key bits).
+__device__ __forceinline__ uint32_t tile_permitted(const float* sM, int nj, const uint8_t* pmrow, int j0, int N,
+                                                   int hf) {
+  uint32_t okm = 0u;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kk = kappa(r, hf);
+    okm |= (kk < nj && sM[kk] != 0.f) ? (1u << r) : 0u;
+  }
+  if (pmrow) {
+    uint32_t pm = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pm |= pmrow[min(j0 + kappa(r, hf), N - 1)] != 0 ? (1u << r) : 0u;
+    okm &= pm;
+  }
+  return okm;
+}
+
+template <int DKH, int NVB, int P3C>
 __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
   const BwLayout& L = a.L;
   constexpr int DKp = 2 * DKH;
@@ -756,7 +779,6 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
   const float3 cq = blk_ref(a, b, qc);
   float cx = 0.f, cy = 0.f, cz = 0.f;
   const uint8_t* pmrow = a.pmask ? a.pmask + ((size_t)b * L.N + qc) * L.N : nullptr;
-  const int P3 = L.P3;  // coordinates past 3P are zero on both sides
   // key tiles: KV (transposed into LDS), VV rows (zero past DVp), centred key
   // points, key mask; the next tile's loads are in flight during the
   // products of the current one
@@ -797,19 +819,18 @@ __global__ __launch_bounds__(256) void bw_fwd_mfma_kernel(BwArgs a) {
     float lg[16];
     float tmax = -INFINITY;
     const int nj = min(kBwKT, L.N - j0);
+    const uint32_t okm = mq ? tile_permitted(sM, nj, pmrow, j0, L.N, hf) : 0u;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kappa(r, hf);
-      const bool ok = mq && kk < nj && sM[kk] != 0.f && (!pmrow || pmrow[j0 + kk] != 0);
       float d2 = 0.f;
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        if (4 * c4 >= P3) break;
+      for (int c4 = 0; c4 < P3C / 4; ++c4) {
         const float4 y = reinterpret_cast<const float4*>(&sBp[kk][0])[c4];
         const float dx = qa[4 * c4] - y.x, dy = qa[4 * c4 + 1] - y.y, dz = qa[4 * c4 + 2] - y.z, dw = qa[4 * c4 + 3] - y.w;
         d2 += dx * dx + dy * dy + dz * dz + dw * dw;
       }
-      lg[r] = ok ? sacc[r] - gam * d2 : -INFINITY;
+      lg[r] = ((okm >> r) & 1u) ? sacc[r] - gam * d2 : -INFINITY;
       tmax = fmaxf(tmax, lg[r]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -975,21 +996,27 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
   const float* kvb = wsf(a, L.off_kv) + rowidx(L, b, h, 0) * L.DKp;
   const float* vvb = wsf(a, L.off_vv) + rowidx(L, b, h, 0) * L.DVp;
   const float* kbb = wsf(a, L.off_kb) + rowidx(L, b, h, 0) * 16;
+  // key tiles: the next tile's loads are in flight during the products of
+  // the current one
+  Tile4<4> tb;
+  Tile4<DKp / 4> tk;
+  Tile4<DVp / 4> tv;
+  float tm = 0.f;
+  auto issue = [&](int j0) {
+    tb.load(kbb, 16, j0, L.N, tid, 4);
+    tk.load(kvb, L.DKp, j0, L.N, tid, DKp / 4);
+    tv.load(vvb, L.DVp, j0, L.N, tid, DVp / 4);
+    const int jm = min(j0 + (tid & 31), L.N - 1);
+    tm = (j0 + (tid & 31) < L.N && a.mask[(size_t)b * L.N + jm] != 0) ? 1.f : 0.f;
+  };
+  if (jb < je) issue(jb);
   for (int j0 = jb; j0 < je; j0 += kBwKT) {
     __syncthreads();
-    {
-      // one tensor at a time: its loads together, then its LDS writes (the
-      // whole tile at once would not fit beside the accumulators)
-      const int jm = min(j0 + (tid & 31), L.N - 1);
-      const float tm = (j0 + (tid & 31) < L.N && a.mask[(size_t)b * L.N + jm] != 0) ? 1.f : 0.f;
-      stage_tile<4, 1>(kbb, 16, j0, L.N, tid, 4,
-                       [&](int jj, int c4, float4 v) { reinterpret_cast<float4*>(&sBp[jj][0])[c4] = v; });
-      stage_tile<DKp / 4, kStageC>(kvb, L.DKp, j0, L.N, tid, DKp / 4,
-                                   [&](int jj, int c4, float4 v) { *reinterpret_cast<float4*>(&sK[jj][4 * c4]) = v; });
-      stage_tile<DVp / 4, kStageC>(vvb, L.DVp, j0, L.N, tid, DVp / 4,
-                                   [&](int jj, int c4, float4 v) { *reinterpret_cast<float4*>(&sV[jj][4 * c4]) = v; });
-      if (tid < kBwKT) sM[tid] = tm;
-    }
+    tb.store(tid, [&](int jj, int c4, float4 v) { reinterpret_cast<float4*>(&sBp[jj][0])[c4] = v; });
+    tk.store(tid, [&](int jj, int c4, float4 v) { *reinterpret_cast<float4*>(&sK[jj][4 * c4]) = v; });
+    tv.store(tid, [&](int jj, int c4, float4 v) { *reinterpret_cast<float4*>(&sV[jj][4 * c4]) = v; });
+    if (tid < kBwKT) sM[tid] = tm;
+    if (j0 + kBwKT < je) issue(j0 + kBwKT);
     __syncthreads();
     // S and dP steps interleaved: two independent chains of dependent MFMAs
     f32x16_t sa = f32x16_t{}, pa = f32x16_t{};
@@ -1021,25 +1048,35 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
     const float3 ct = blk_ref(a, b, j0);
     const float corr = fmaf(sv.x, cq.x - ct.x, fmaf(sv.y, cq.y - ct.y, fmaf(sv.z, cq.z - ct.z, dsum)));
     float ds[16];
+    const uint32_t okm = mq ? tile_permitted(sM, nj, pmrow, j0, L.N, hf) : 0u;
+    // dS first (the coordinate differences recomputed below rather than held:
+    // sixteen keys' differences would not fit beside the accumulators)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kk = kappa(r, hf);
-      const bool ok = mq && kk < nj && sM[kk] != 0.f && (!pmrow || pmrow[j0 + kk] != 0);
-      float dif[P3C];
       float d2 = 0.f;
 #pragma unroll
       for (int c4 = 0; c4 < P3C / 4; ++c4) {
         const float4 y = reinterpret_cast<const float4*>(&sBp[kk][0])[c4];
-        dif[4 * c4] = qa[4 * c4] - y.x; dif[4 * c4 + 1] = qa[4 * c4 + 1] - y.y;
-        dif[4 * c4 + 2] = qa[4 * c4 + 2] - y.z; dif[4 * c4 + 3] = qa[4 * c4 + 3] - y.w;
-        d2 += dif[4 * c4] * dif[4 * c4] + dif[4 * c4 + 1] * dif[4 * c4 + 1] + dif[4 * c4 + 2] * dif[4 * c4 + 2] +
-              dif[4 * c4 + 3] * dif[4 * c4 + 3];
+        const float dx = qa[4 * c4] - y.x, dy = qa[4 * c4 + 1] - y.y, dz = qa[4 * c4 + 2] - y.z, dw = qa[4 * c4 + 3] - y.w;
+        d2 += dx * dx + dy * dy + dz * dz + dw * dw;
       }
-      const float p = ok ? exp_fast(sa[r] - gam * d2 - lse) : 0.f;
+      const float p = ((okm >> r) & 1u) ? exp_fast(sa[r] - gam * d2 - lse) : 0.f;
       ds[r] = p * (pa[r] - corr);
-#pragma unroll
-      for (int u = 0; u < P3C; ++u) da[u] = fmaf(ds[r], dif[u], da[u]);
       dg = fmaf(-ds[r], d2, dg);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = kappa(r, hf);
+#pragma unroll
+      for (int c4 = 0; c4 < P3C / 4; ++c4) {
+        const float4 y = reinterpret_cast<const float4*>(&sBp[kk][0])[c4];
+        da[4 * c4] = fmaf(ds[r], qa[4 * c4] - y.x, da[4 * c4]);
+        da[4 * c4 + 1] = fmaf(ds[r], qa[4 * c4 + 1] - y.y, da[4 * c4 + 1]);
+        da[4 * c4 + 2] = fmaf(ds[r], qa[4 * c4 + 2] - y.z, da[4 * c4 + 2]);
+        da[4 * c4 + 3] = fmaf(ds[r], qa[4 * c4 + 3] - y.w, da[4 * c4 + 3]);
+      }
     }
     // dQV^T += KV_t^T dS^T
 #pragma unroll
@@ -1155,7 +1192,7 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
   // query tiles: QV and dO (transposed into LDS), query points, per-query
   // statistics; the tile's loads go out together, and in mode 1 (which has
   // the registers for it) one tile ahead, in flight during the products
-  constexpr bool kPre = MODE == 1;
+  constexpr bool kPre = true;
   const float* qvb = wsf(a, L.off_qv) + rowidx(L, b, h, 0) * L.DKp;
   const float* dob = wsf(a, L.off_do) + rowidx(L, b, h, 0) * L.DVp;
   const float* qab = wsf(a, L.off_qa) + rowidx(L, b, h, 0) * 16;
@@ -1242,27 +1279,53 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
       sa += pa;
     }
     float ds[16], pr[16];
+    // permission bits of the tile's queries for this key (bit r: query
+    // kappa(r, hf)), once per tile; the pair-mask loads go out together, their
+    // row clamped into the chain (queries past it have sL = +inf)
+    uint32_t okm = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) okm |= sL[kappa(r, hf)] < INFINITY ? (1u << r) : 0u;
+    if (a.pmask) {
+      uint32_t pm = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = min(i0 + kappa(r, hf), L.N - 1);
+        pm |= a.pmask[((size_t)b * L.N + i) * L.N + jc] != 0 ? (1u << r) : 0u;
+      }
+      okm &= pm;
+    }
+    okm = mk ? okm : 0u;
+    // probabilities (and dS) first; the coordinate differences are
+    // recomputed for dB below rather than held for sixteen queries
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qq = kappa(r, hf);
-      const int i = i0 + qq;
-      const bool ok = mk && sL[qq] < INFINITY && (!a.pmask || a.pmask[((size_t)b * L.N + i) * L.N + jc] != 0);
-      float dif[P3C];
       float d2 = 0.f;
 #pragma unroll
       for (int c4 = 0; c4 < P3C / 4; ++c4) {
         const float4 x = reinterpret_cast<const float4*>(&sA[qq][0])[c4];
-        dif[4 * c4] = x.x - kb[4 * c4]; dif[4 * c4 + 1] = x.y - kb[4 * c4 + 1];
-        dif[4 * c4 + 2] = x.z - kb[4 * c4 + 2]; dif[4 * c4 + 3] = x.w - kb[4 * c4 + 3];
-        d2 += dif[4 * c4] * dif[4 * c4] + dif[4 * c4 + 1] * dif[4 * c4 + 1] + dif[4 * c4 + 2] * dif[4 * c4 + 2] +
-              dif[4 * c4 + 3] * dif[4 * c4 + 3];
+        const float dx = x.x - kb[4 * c4], dy = x.y - kb[4 * c4 + 1], dz = x.z - kb[4 * c4 + 2], dw = x.w - kb[4 * c4 + 3];
+        d2 += dx * dx + dy * dy + dz * dz + dw * dw;
       }
-      pr[r] = ok ? exp_fast(sa[r] - gam * d2 - sL[qq]) : 0.f;
+      pr[r] = ((okm >> r) & 1u) ? exp_fast(sa[r] - gam * d2 - sL[qq]) : 0.f;
       if constexpr (kDS) {
         const float corr = fmaf(sSx[qq], dcx, fmaf(sSy[qq], dcy, fmaf(sSz[qq], dcz, sS[qq])));
         ds[r] = pr[r] * (pa[r] - corr);
+      }
+    }
+    if constexpr (kDS) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < P3C; ++u) db[u] = fmaf(ds[r], dif[u], db[u]);
+      for (int r = 0; r < 16; ++r) {
+        const int qq = kappa(r, hf);
+#pragma unroll
+        for (int c4 = 0; c4 < P3C / 4; ++c4) {
+          const float4 x = reinterpret_cast<const float4*>(&sA[qq][0])[c4];
+          db[4 * c4] = fmaf(ds[r], x.x - kb[4 * c4], db[4 * c4]);
+          db[4 * c4 + 1] = fmaf(ds[r], x.y - kb[4 * c4 + 1], db[4 * c4 + 1]);
+          db[4 * c4 + 2] = fmaf(ds[r], x.z - kb[4 * c4 + 2], db[4 * c4 + 2]);
+          db[4 * c4 + 3] = fmaf(ds[r], x.w - kb[4 * c4 + 3], db[4 * c4 + 3]);
+        }
       }
     }
     // dKV^T += QV_t^T dS, dVV^T += dO_t^T P
@@ -1698,7 +1761,11 @@ hipError_t launch_pairs_inst(const BwArgs& a, int which, hipStream_t st) {
   };
   if (which == 0 && L.NK4 == 9) {
     // standard shape (D + R Cz <= 144, Dv + R Cz + 3Q <= 176): matrix cores
-    hipLaunchKernelGGL((bw_fwd_mfma_kernel<72, 6>), grid, dim3(256), 0, st, a);
+    // coordinates past 3P are zero on both sides: P < 4 takes the 12-coordinate instance as well
+    if (L.P3 <= 12)
+      hipLaunchKernelGGL((bw_fwd_mfma_kernel<72, 6, 12>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((bw_fwd_mfma_kernel<72, 6, 16>), grid, dim3(256), 0, st, a);
     if (L.psplit > 1)
       hipLaunchKernelGGL(bw_merge_o_kernel, dim3((unsigned)((rows * (L.DVp / 4) + 255) / 256)), dim3(256), 0, st, a);
     return hipGetLastError();
