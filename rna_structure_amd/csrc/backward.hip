@@ -1065,25 +1065,24 @@ __global__ __launch_bounds__(256) void bw_query_mfma_kernel(BwArgs a) {
       ds[r] = p * (pa[r] - corr);
       dg = fmaf(-ds[r], d2, dg);
     }
+    // dQV^T += KV_t^T dS^T, with the point term dA (vector ALU, independent
+    // of these products) a piece after each matrix instruction
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = kappa(r, hf);
+    for (int s = 0; s < 16; ++s) {
+      const int kk = kappa(s, hf);
 #pragma unroll
-      for (int c4 = 0; c4 < P3C / 4; ++c4) {
-        const float4 y = reinterpret_cast<const float4*>(&sBp[kk][0])[c4];
-        da[4 * c4] = fmaf(ds[r], qa[4 * c4] - y.x, da[4 * c4]);
-        da[4 * c4 + 1] = fmaf(ds[r], qa[4 * c4 + 1] - y.y, da[4 * c4 + 1]);
-        da[4 * c4 + 2] = fmaf(ds[r], qa[4 * c4 + 2] - y.z, da[4 * c4 + 2]);
-        da[4 * c4 + 3] = fmaf(ds[r], qa[4 * c4 + 3] - y.w, da[4 * c4 + 3]);
+      for (int c = 0; c < NKB; ++c) {
+        dq[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[kk][32 * c + l32], ds[s], dq[c], 0, 0, 0);
+        if (c < P3C / 4) {
+          const float4 y = reinterpret_cast<const float4*>(&sBp[kk][0])[c];
+          da[4 * c] = fmaf(ds[s], qa[4 * c] - y.x, da[4 * c]);
+          da[4 * c + 1] = fmaf(ds[s], qa[4 * c + 1] - y.y, da[4 * c + 1]);
+          da[4 * c + 2] = fmaf(ds[s], qa[4 * c + 2] - y.z, da[4 * c + 2]);
+          da[4 * c + 3] = fmaf(ds[s], qa[4 * c + 3] - y.w, da[4 * c + 3]);
+        }
       }
     }
-    // dQV^T += KV_t^T dS^T
-#pragma unroll
-    for (int c = 0; c < NKB; ++c)
-#pragma unroll
-      for (int s = 0; s < 16; ++s)
-        dq[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[kappa(s, hf)][32 * c + l32], ds[s], dq[c], 0, 0, 0);
   }
   // the two halves of the wavefront hold the same queries' two halves of each tile
 #pragma unroll
@@ -1313,28 +1312,26 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
         ds[r] = pr[r] * (pa[r] - corr);
       }
     }
-    if constexpr (kDS) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = kappa(r, hf);
-#pragma unroll
-        for (int c4 = 0; c4 < P3C / 4; ++c4) {
-          const float4 x = reinterpret_cast<const float4*>(&sA[qq][0])[c4];
-          db[4 * c4] = fmaf(ds[r], x.x - kb[4 * c4], db[4 * c4]);
-          db[4 * c4 + 1] = fmaf(ds[r], x.y - kb[4 * c4 + 1], db[4 * c4 + 1]);
-          db[4 * c4 + 2] = fmaf(ds[r], x.z - kb[4 * c4 + 2], db[4 * c4 + 2]);
-          db[4 * c4 + 3] = fmaf(ds[r], x.w - kb[4 * c4 + 3], db[4 * c4 + 3]);
-        }
-      }
-    }
-    // dKV^T += QV_t^T dS, dVV^T += dO_t^T P
+    // dKV^T += QV_t^T dS, dVV^T += dO_t^T P; in mode 0 the point term dB
+    // (vector ALU, independent of these products) is placed between the
+    // matrix instructions
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       if constexpr (kDS) {
+        const int qq = kappa(s, hf);
 #pragma unroll
-        for (int c = 0; c < NKB; ++c)
-          dk[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sQT[32 * c + l32][kappa(s, hf)], ds[s], dk[c], 0, 0, 0);
+        for (int c = 0; c < NKB; ++c) {
+          dk[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(sQT[32 * c + l32][qq], ds[s], dk[c], 0, 0, 0);
+          if (c < P3C / 4) {
+            // a piece of dB for query qq (coordinates 4c .. 4c+3)
+            const float4 x = reinterpret_cast<const float4*>(&sA[qq][0])[c];
+            db[4 * c] = fmaf(ds[s], x.x - kb[4 * c], db[4 * c]);
+            db[4 * c + 1] = fmaf(ds[s], x.y - kb[4 * c + 1], db[4 * c + 1]);
+            db[4 * c + 2] = fmaf(ds[s], x.z - kb[4 * c + 2], db[4 * c + 2]);
+            db[4 * c + 3] = fmaf(ds[s], x.w - kb[4 * c + 3], db[4 * c + 3]);
+          }
+        }
       } else {
 #pragma unroll
         for (int c = 0; c < NVB; ++c)
