@@ -630,7 +630,6 @@ __global__ __launch_bounds__(256) void bw_add_slabs_kernel(float* out, const flo
   for (int z = 0; z < ns; ++z) v += extra[(size_t)z * n + i];
   out[i] = v;
 }
-constexpr int kStageC = 2;  // loads per thread in flight at once where registers are short
 
 __device__ __forceinline__ int kappa(int s, int h) { return 8 * (s >> 2) + 4 * h + (s & 3); }
 
@@ -669,35 +668,6 @@ struct Tile4 {
     }
   }
 };
-
-// The same staging for kernels without the registers for a whole tensor's
-// pieces: loads in groups of C per thread, each group written to LDS before
-// the next is loaded.
-template <int F4, int C, typename Fn>
-__device__ __forceinline__ void stage_tile(const float* base, int stride, int j0, int N, int tid, int valid, Fn fn) {
-  constexpr int K = (32 * F4 + 255) / 256;
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += C) {
-    float4 v[C];
-#pragma unroll
-    for (int k = 0; k < C; ++k) {
-      const int e = min(tid + 256 * (k0 + k), 32 * F4 - 1);
-      const int jj = e / F4, c4 = e - jj * F4;
-      const int j = min(j0 + jj, N - 1);
-      const uint32_t idx = (uint32_t)j * (uint32_t)(stride >> 2) + (uint32_t)min(c4, valid - 1);
-      const float4 x = reinterpret_cast<const float4*>(base)[idx];
-      v[k] = c4 < valid ? x : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int k = 0; k < C; ++k) {
-      const int e = tid + 256 * (k0 + k);
-      if (k0 + k < K && e < 32 * F4) {
-        const int jj = e / F4, c4 = e - jj * F4;
-        fn(jj, c4, v[k]);
-      }
-    }
-  }
-}
 
 // Permission bits of one 32-key tile for a query lane: bit r for key
 // kappa(r, hf) of the tile (keys past the chain's end, masked keys, and with
@@ -1189,9 +1159,8 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
 #pragma unroll
   for (int u = 0; u < P3C; ++u) db[u] = 0.f;
   // query tiles: QV and dO (transposed into LDS), query points, per-query
-  // statistics; the tile's loads go out together, and in mode 1 (which has
-  // the registers for it) one tile ahead, in flight during the products
-  constexpr bool kPre = true;
+  // statistics; the tile's loads go out together one tile ahead, in flight
+  // during the products of the current one
   const float* qvb = wsf(a, L.off_qv) + rowidx(L, b, h, 0) * L.DKp;
   const float* dob = wsf(a, L.off_do) + rowidx(L, b, h, 0) * L.DVp;
   const float* qab = wsf(a, L.off_qa) + rowidx(L, b, h, 0) * 16;
@@ -1219,35 +1188,12 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
     sDT[4 * c4][ii] = v.x; sDT[4 * c4 + 1][ii] = v.y; sDT[4 * c4 + 2][ii] = v.z; sDT[4 * c4 + 3][ii] = v.w;
   };
   auto put_a = [&](int ii, int c4, float4 v) { reinterpret_cast<float4*>(&sA[ii][0])[c4] = v; };
-  if (kPre) issue(ib);
+  if (ib < ie) issue(ib);
   for (int i0 = ib; i0 < ie; i0 += kBwKT) {
     __syncthreads();
-    if constexpr (kPre) {
-      tq.store(tid, put_q);
-      td.store(tid, put_d);
-      ta.store(tid, put_a);
-    } else {
-      // mode 0 holds more accumulators: a piece at a time (measured faster
-      // here than the grouped loads, which made the compiler spill)
-      const int i = i0 + (tid & 31);
-      const int icl = min(i, L.N - 1);
-      t_lse = wsf(a, L.off_lse)[rowidx(L, b, h, icl)];
-      t_ok = i < L.N && a.mask[(size_t)b * L.N + icl] != 0;
-      t_dd = wsf(a, L.off_dd)[rowidx(L, b, h, icl)];
-      t_ds = reinterpret_cast<const float4*>(wsf(a, L.off_ds) + rowidx(L, b, h, icl) * 4)[0];
-      for (int e = tid; e < kBwKT * (DKp / 4); e += 256) {
-        const int ii = e / (DKp / 4), c4 = e - ii * (DKp / 4);
-        put_q(ii, c4, reinterpret_cast<const float4*>(qvb + (size_t)min(i0 + ii, L.N - 1) * L.DKp)[c4]);
-      }
-      for (int e = tid; e < kBwKT * (DVp / 4); e += 256) {
-        const int ii = e / (DVp / 4), c4 = e - ii * (DVp / 4);
-        put_d(ii, c4, reinterpret_cast<const float4*>(dob + (size_t)min(i0 + ii, L.N - 1) * L.DVp)[c4]);
-      }
-      for (int e = tid; e < kBwKT * 4; e += 256) {
-        const int ii = e >> 2, c4 = e & 3;
-        put_a(ii, c4, reinterpret_cast<const float4*>(qab + (size_t)min(i0 + ii, L.N - 1) * 16)[c4]);
-      }
-    }
+    tq.store(tid, put_q);
+    td.store(tid, put_d);
+    ta.store(tid, put_a);
     if (tid < kBwKT) {
       const bool ok = t_ok && t_lse > -INFINITY;
       sL[tid] = ok ? t_lse : INFINITY;  // +inf marks a query that takes no key
@@ -1256,7 +1202,7 @@ __global__ __launch_bounds__(256) void bw_key_mfma_kernel(BwArgs a) {
       sSy[tid] = t_ds.y;
       sSz[tid] = t_ds.z;
     }
-    if (kPre && i0 + kBwKT < ie) issue(i0 + kBwKT);
+    if (i0 + kBwKT < ie) issue(i0 + kBwKT);
     __syncthreads();
     // the query block's reference relative to this key's
     const float3 cqb = blk_ref(a, b, i0);
