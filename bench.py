@@ -123,10 +123,11 @@ def make_workload(name):
     return make_config(name)
 
 
-def time_forward(inp, steps, warmup, per_kernel=True, min_warm_ms=40.0):
+def time_forward(inp, steps, warmup, per_kernel=True, min_warm_ms=40.0, stacked=False):
     """Forward time with inputs resident: `warmup` untimed forwards, continued
     until at least min_warm_ms of GPU time has passed (the clock ramps up over
-    the first tens of milliseconds of load), then `steps` timed forwards."""
+    the first tens of milliseconds of load), then `steps` timed forwards.
+    stacked=True times the pages' stacked point layout (comparison calls)."""
     import torch
     from rna_structure_amd import _lib
     shape = inp["shape"]
@@ -134,7 +135,7 @@ def time_forward(inp, steps, warmup, per_kernel=True, min_warm_ms=40.0):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base_mem = torch.cuda.memory_allocated()
-    f = _lib.FlashIPA(shape, eps=inp["eps"], with_pair_mask=t["pair_mask"] is not None)
+    f = _lib.FlashIPA(shape, eps=inp["eps"], with_pair_mask=t["pair_mask"] is not None, stacked=stacked)
     w0 = torch.cuda.Event(enable_timing=True)
     w1 = torch.cuda.Event(enable_timing=True)
     w0.record()
@@ -622,6 +623,9 @@ def main():
                     help="run only plain copies of MIB MiB (counter calibration) and exit")
     ap.add_argument("--hbm-calibration", action="store_true",
                     help="print the fill / copy / sum rates of plain device kernels and exit")
+    ap.add_argument("--stacked-layout", action="store_true",
+                    help="time the headline workload with the pages' stacked point layout (comparison calls "
+                         "ipa_lift_stacked / ipa_flash_fwd_stacked) instead of the centred split")
     ap.add_argument("--cpu-oracle", nargs=4, metavar=("KIND", "ARG", "BUDGET_S", "WORKERS"),
                     help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -654,14 +658,14 @@ def main():
     shape = inp["shape"]
     flops = eff_flops(shape, inp["mask"])
     print(f"# workload {args.workload} {shape}", file=sys.stderr, flush=True)
-    r = time_forward(inp, args.steps, args.warmup, min_warm_ms=0.0)
+    r = time_forward(inp, args.steps, args.warmup, min_warm_ms=0.0, stacked=args.stacked_layout)
     value = flops / (r["ms"] * 1e-3) / 1e12
     achieved = flops / (r["flash_ms"] * 1e-3) / 1e12
     traffic = None
     try:
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
-        if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == args.workload:
+        if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == args.workload and not args.stacked_layout:
             traffic = tr["fetch_bytes"] + tr["write_bytes"]
     except (OSError, ValueError, KeyError):
         traffic = None
@@ -680,7 +684,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"long-sequence IPA forward {args.workload}", "B": shape.B, "N": shape.N,
                    "H": shape.H, "D": shape.D, "Dv": shape.Dv, "P": shape.P, "Q": shape.Q, "Cz": shape.Cz,
-                   "R": shape.R, "Cout": shape.Cout, "inputs": "bf16", "accumulate": "fp32"},
+                   "R": shape.R, "Cout": shape.Cout, "inputs": "bf16", "accumulate": "fp32",
+                   **({"layout": "stacked bf16 point columns (comparison)"} if args.stacked_layout else {})},
         "kernels_ms": {"lift": round(r["lift_ms"], 4), "flash": round(r["flash_ms"], 4),
                        "epilogue": round(r["epilogue_ms"], 4)},
         "peak_mem_mb": round(r["peak_mem_mb"], 1),
@@ -741,6 +746,24 @@ def main():
                           "lift_ms": round(rr["lift_ms"], 4), "epilogue_ms": round(rr["epilogue_ms"], 4)})
             print(f"# rank sweep {ranks[-1]}", file=sys.stderr, flush=True)
         out["rank_sweep"] = ranks
+        # the pages' stacked point layout (five bf16 columns per point, global
+        # coordinates, two geometric K-steps) against the centred fp16 hi/lo
+        # split (three), same inputs; the flops counted are the algorithmic
+        # ones of both (their accuracy is compared in the GPU tests)
+        layouts = []
+        for N in (8192, 16384):
+            sh = IPAShape(B=1, N=N, H=8)
+            w = make_inputs(sh, 7000 + N, frames="walk", step=3.8)
+            fl = eff_flops(sh, w["mask"])
+            for stk in (False, True):
+                rr = time_forward(w, max(3, args.steps // 4), 2, stacked=stk)
+                layouts.append({"layout": "stacked bf16 (pages)" if stk else "centred fp16 hi/lo", "N": N,
+                                "geometric_ksteps": 2 if stk else 3, "ms": round(rr["ms"], 4),
+                                "flash_ms": round(rr["flash_ms"], 4),
+                                "flash_frac_mfma": round(fl / (rr["flash_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                "lift_ms": round(rr["lift_ms"], 4)})
+                print(f"# layout comparison {layouts[-1]}", file=sys.stderr, flush=True)
+        out["layout_comparison"] = layouts
     if not args.no_sweep and not args.no_knn:
         out["knn_distogram"] = knn_section(args)
     if not args.no_sweep and not args.no_backward:

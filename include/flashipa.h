@@ -174,6 +174,28 @@ ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, siz
  * permitted key; beyond that it is clamped (finite results, no NaN). */
 ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream);
 
+/* Comparison only: the pages' own stacked point layout (FlashIPA rebuttal,
+ * Q3: the point term as stacked vectors of five columns per point fed to
+ * the same attention kernel).  Identical to ipa_lift / ipa_flash_fwd except
+ * that the point term of L_ijh is evaluated as the inner product of
+ *   query [T_i q_p (3) | |T_i q_p|^2 | 1]  and
+ *   key   [2 gamma_h T_j k_p (3) | -gamma_h | -gamma_h |T_j k_p|^2]
+ * per point, in bf16 and in global coordinates (two bf16 K-steps instead of
+ * three fp16 hi/lo K-steps about centroids).  The squared norms of global
+ * coordinates are then rounded to 8 significant bits, so on chains far from
+ * the origin the logits, and with them o and lse, carry errors far beyond
+ * the bf16 path's tolerance; these calls exist to measure that error and
+ * the layout's speed beside the standard path, not to replace it.  The
+ * lifted buffer (ipa_lifted_bytes_stacked bytes) is only valid for
+ * ipa_flash_fwd_stacked; o and lse have the layouts of ipa_flash_fwd and
+ * may be passed to ipa_epilogue.  Shapes: bf16 only, D <= 16, Dv <= 31,
+ * P = 4, Q <= 9, 64 < R*Cz <= 128, D, Dv and Cz multiples of 8 (else
+ * IPA_ERR_UNSUPPORTED, or 0 bytes). */
+size_t ipa_lifted_bytes_stacked(const ipa_shape* s, int with_pair_mask);
+ipa_status ipa_lift_stacked(const ipa_shape* s, const ipa_lift_in* in, void* lifted, size_t lifted_bytes,
+                            void* stream);
+ipa_status ipa_flash_fwd_stacked(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream);
+
 /* Bytes of the epilogue's own workspace for this shape (the output
  * projection packed for the matrix-core product: per head or transposed,
  * bf16); at least 16.  0 for an invalid shape or one the epilogue does not

@@ -20,7 +20,7 @@ IPA_F32, IPA_BF16 = 0, 1
 STATUS = {0: "IPA_OK", 1: "IPA_ERR_NULL", 2: "IPA_ERR_SHAPE", 3: "IPA_ERR_UNSUPPORTED",
           4: "IPA_ERR_ALIGN", 5: "IPA_ERR_LAUNCH", 6: "IPA_ERR_DEVICE", 7: "IPA_ERR_SCRATCH"}
 EXPORTS = ("ipa_lifted_bytes", "ipa_o_width", "ipa_lift", "ipa_flash_fwd", "ipa_epilogue_workspace_bytes",
-           "ipa_epilogue",
+           "ipa_epilogue", "ipa_lifted_bytes_stacked", "ipa_lift_stacked", "ipa_flash_fwd_stacked",
            "ipa_logit_rows", "ipa_backward_workspace_bytes", "ipa_backward", "ipa_knn_distogram",
            "ipa_bias_workspace_bytes", "ipa_bias_attention", "ipa_forward_noalloc", "ipa_status_string",
            "ipa_version")
@@ -85,6 +85,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ipa_lift.restype = ctypes.c_int
     lib.ipa_flash_fwd.argtypes = [sp, vp, vp, vp, vp]
     lib.ipa_flash_fwd.restype = ctypes.c_int
+    lib.ipa_lifted_bytes_stacked.argtypes = [sp, ctypes.c_int]
+    lib.ipa_lifted_bytes_stacked.restype = sz
+    lib.ipa_lift_stacked.argtypes = [sp, ctypes.POINTER(IpaLiftIn), vp, sz, vp]
+    lib.ipa_lift_stacked.restype = ctypes.c_int
+    lib.ipa_flash_fwd_stacked.argtypes = [sp, vp, vp, vp, vp]
+    lib.ipa_flash_fwd_stacked.restype = ctypes.c_int
     lib.ipa_epilogue_workspace_bytes.argtypes = [sp]
     lib.ipa_epilogue_workspace_bytes.restype = sz
     lib.ipa_epilogue.argtypes = [sp, vp, sz, vp, vp, ctypes.POINTER(IpaEpiIn), vp, vp, vp]
@@ -134,26 +140,28 @@ def _check(fn, code):
         raise IPAError(fn, code)
 
 
-def lifted_bytes(s: IpaShape, with_pair_mask: bool) -> int:
-    return int(load().ipa_lifted_bytes(ctypes.byref(s), int(bool(with_pair_mask))))
+def lifted_bytes(s: IpaShape, with_pair_mask: bool, stacked: bool = False) -> int:
+    fn = load().ipa_lifted_bytes_stacked if stacked else load().ipa_lifted_bytes
+    return int(fn(ctypes.byref(s), int(bool(with_pair_mask))))
 
 
 def o_width(s: IpaShape) -> int:
     return int(load().ipa_o_width(ctypes.byref(s)))
 
 
-def ipa_lift(s: IpaShape, t: dict, lifted, stream=None):
+def ipa_lift(s: IpaShape, t: dict, lifted, stream=None, stacked: bool = False):
     lib = load()
     li = IpaLiftIn(*[_ptr(t.get(n)) for n in ("q", "k", "v", "q_points", "k_points", "v_points", "rotation",
                                               "translation", "point_weight_raw", "w_pair", "zl", "zr",
                                               "mask", "pair_mask")])
-    _check("ipa_lift", lib.ipa_lift(ctypes.byref(s), ctypes.byref(li), _ptr(lifted), lifted.numel() *
+    name = "ipa_lift_stacked" if stacked else "ipa_lift"
+    _check(name, getattr(lib, name)(ctypes.byref(s), ctypes.byref(li), _ptr(lifted), lifted.numel() *
                                     lifted.element_size(), _stream(stream)))
 
 
-def ipa_flash_fwd(s: IpaShape, lifted, o, lse, stream=None):
-    _check("ipa_flash_fwd", load().ipa_flash_fwd(ctypes.byref(s), _ptr(lifted), _ptr(o), _ptr(lse),
-                                                 _stream(stream)))
+def ipa_flash_fwd(s: IpaShape, lifted, o, lse, stream=None, stacked: bool = False):
+    name = "ipa_flash_fwd_stacked" if stacked else "ipa_flash_fwd"
+    _check(name, getattr(load(), name)(ctypes.byref(s), _ptr(lifted), _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def epilogue_workspace_bytes(s: IpaShape) -> int:
@@ -306,16 +314,19 @@ def device_inputs(inp: dict, device="cuda") -> dict:
 
 
 class FlashIPA:
-    """Buffers and the three calls of one forward for a fixed problem shape."""
+    """Buffers and the three calls of one forward for a fixed problem shape.
+    stacked=True runs the lift and the fused attention with the pages' stacked
+    point layout (ipa_lift_stacked / ipa_flash_fwd_stacked, a comparison)."""
 
-    def __init__(self, shape, eps: float = 1e-8, with_pair_mask: bool = False, device="cuda"):
+    def __init__(self, shape, eps: float = 1e-8, with_pair_mask: bool = False, device="cuda", stacked: bool = False):
         import torch
         load()
         self.shape = shape
+        self.stacked = stacked
         self.s = make_shape(shape, eps)
-        nbytes = lifted_bytes(self.s, with_pair_mask)
+        nbytes = lifted_bytes(self.s, with_pair_mask, stacked)
         if nbytes == 0:
-            raise IPAError("ipa_lifted_bytes", 3)
+            raise IPAError("ipa_lifted_bytes_stacked" if stacked else "ipa_lifted_bytes", 3)
         self.lifted = torch.empty(nbytes, dtype=torch.uint8, device=device)
         ebytes = epilogue_workspace_bytes(self.s)
         if ebytes == 0:
@@ -337,10 +348,10 @@ class FlashIPA:
             buf.fill_(float("nan"))
 
     def lift(self, t: dict, stream=None):
-        ipa_lift(self.s, t, self.lifted, stream)
+        ipa_lift(self.s, t, self.lifted, stream, self.stacked)
 
     def attend(self, stream=None):
-        ipa_flash_fwd(self.s, self.lifted, self.o, self.lse, stream)
+        ipa_flash_fwd(self.s, self.lifted, self.o, self.lse, stream, self.stacked)
 
     def epilogue(self, t: dict, stream=None):
         ipa_epilogue(self.s, self.epi_ws, self.o, self.lse, t, self.update, self.local_points, stream)
@@ -353,6 +364,8 @@ class FlashIPA:
 
     def logit_rows(self, b: int, h: int, row0: int, nrows: int, stream=None):
         import torch
+        if self.stacked:
+            raise ValueError("ipa_logit_rows reads the standard layout only")
         out = torch.empty(nrows, self.shape.N, dtype=torch.float32, device=self.o.device)
         ipa_logit_rows(self.s, self.lifted, b, h, row0, nrows, out, stream)
         return out

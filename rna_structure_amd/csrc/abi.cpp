@@ -36,13 +36,13 @@ using fipa::Layout;
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-static ipa_status shape_status(const ipa_shape* s, int with_pm, Layout* L) {
+static ipa_status shape_status(const ipa_shape* s, int with_pm, Layout* L, int stacked = 0) {
   if (!s) return IPA_ERR_NULL;
   if (s->B <= 0 || s->N <= 0 || s->H <= 0 || s->D <= 0 || s->Dv <= 0 || s->P <= 0 || s->Q <= 0 || s->Cz <= 0 ||
       s->R <= 0 || s->Cout <= 0 || !(s->eps > 0.0f))
     return IPA_ERR_SHAPE;
   if (s->dtype != IPA_F32 && s->dtype != IPA_BF16) return IPA_ERR_UNSUPPORTED;
-  if (!fipa::make_layout(s, with_pm, L)) return IPA_ERR_UNSUPPORTED;
+  if (!fipa::make_layout(s, with_pm, L, stacked)) return IPA_ERR_UNSUPPORTED;
   return IPA_OK;
 }
 
@@ -85,11 +85,16 @@ int64_t ipa_o_width(const ipa_shape* s) {
   return s->Dv + s->R * s->Cz + 3 * s->Q;
 }
 
-ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, size_t lifted_bytes, void* stream) {
+}  // extern "C"
+
+// ipa_lift and ipa_lift_stacked (which differ only in the point columns of
+// the key rows), ipa_flash_fwd and ipa_flash_fwd_stacked
+static ipa_status lift_call(const ipa_shape* s, const ipa_lift_in* in, void* lifted, size_t lifted_bytes,
+                            void* stream, int stacked, const char* name) {
   if (!s || !in || !lifted) return IPA_ERR_NULL;
   Layout L;
   const int with_pm = in->pair_mask != nullptr;
-  ipa_status st = shape_status(s, with_pm, &L);
+  ipa_status st = shape_status(s, with_pm, &L, stacked);
   if (st != IPA_OK) return st;
   const void* req[] = {in->q, in->k, in->v, in->q_points, in->k_points, in->v_points, in->rotation,
                        in->translation, in->point_weight_raw, in->w_pair, in->zl, in->zr, in->mask};
@@ -99,22 +104,48 @@ ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, siz
     if (!aligned16(p)) return IPA_ERR_ALIGN;
   if (!aligned16(lifted) || (in->pair_mask && !aligned16(in->pair_mask))) return IPA_ERR_ALIGN;
   if (lifted_bytes < L.total) return IPA_ERR_SHAPE;
-  const Range range("ipa_lift");
-  return launch_status(fipa::launch_lift(L, in, lifted, reinterpret_cast<hipStream_t>(stream)), "ipa_lift", stream);
+  const Range range(name);
+  return launch_status(fipa::launch_lift(L, in, lifted, reinterpret_cast<hipStream_t>(stream)), name, stream);
 }
 
-ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream) {
+static ipa_status flash_call(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream, int stacked,
+                             const char* name) {
   if (!s || !lifted || !o || !lse) return IPA_ERR_NULL;
   Layout L;
   // the pair-mask region is at the end of the workspace; its presence is
-  // recorded in the workspace header by ipa_lift
-  ipa_status st = shape_status(s, 0, &L);
+  // recorded in the workspace header by the lift
+  ipa_status st = shape_status(s, 0, &L, stacked);
   if (st != IPA_OK) return st;
   if (!aligned16(lifted) || !aligned16(o) || !aligned16(lse)) return IPA_ERR_ALIGN;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const Range range("ipa_flash_fwd");
+  const Range range(name);
   return launch_status(L.mfma ? fipa::launch_flash_mfma(L, lifted, o, lse, hs)
-                              : fipa::launch_flash_f32(L, lifted, o, lse, hs), "ipa_flash_fwd", stream);
+                              : fipa::launch_flash_f32(L, lifted, o, lse, hs), name, stream);
+}
+
+extern "C" {
+
+ipa_status ipa_lift(const ipa_shape* s, const ipa_lift_in* in, void* lifted, size_t lifted_bytes, void* stream) {
+  return lift_call(s, in, lifted, lifted_bytes, stream, 0, "ipa_lift");
+}
+
+ipa_status ipa_flash_fwd(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream) {
+  return flash_call(s, lifted, o, lse, stream, 0, "ipa_flash_fwd");
+}
+
+size_t ipa_lifted_bytes_stacked(const ipa_shape* s, int with_pair_mask) {
+  Layout L;
+  if (shape_status(s, with_pair_mask, &L, 1) != IPA_OK) return 0;
+  return L.total;
+}
+
+ipa_status ipa_lift_stacked(const ipa_shape* s, const ipa_lift_in* in, void* lifted, size_t lifted_bytes,
+                            void* stream) {
+  return lift_call(s, in, lifted, lifted_bytes, stream, 1, "ipa_lift_stacked");
+}
+
+ipa_status ipa_flash_fwd_stacked(const ipa_shape* s, const void* lifted, float* o, float* lse, void* stream) {
+  return flash_call(s, lifted, o, lse, stream, 1, "ipa_flash_fwd_stacked");
 }
 
 size_t ipa_epilogue_workspace_bytes(const ipa_shape* s) {

@@ -32,6 +32,15 @@ constexpr int kQueryTile = 128;
 //   base+9..11: (t' - m)/16 in three fp16 parts x 16 (m: the query's running
 //               maximum in the fused kernel, 0 for plain logits)
 // so that the MFMA itself returns the complete logit.
+//
+// Stacked layout (the comparison of the pages' own scheme, Layout::stacked):
+// the point term as five bf16 columns per point in global coordinates, no
+// centring and no hi/lo split, GS = 2 bf16 K-steps.  Key side, point p:
+// [2 gl b_p (3) | -gl | -gl |b_p|^2] at columns 5p .. 5p+4; query side
+// [a_p (3) | |a_p|^2 | 1], so the product is -gl |a_p - b_p|^2.  Column 28 is
+// the key-mask column (key -65536 when masked, query 16) and columns 29..31
+// carry the query's -m/16 in three bf16 parts against a key value of 16.
+constexpr int kStkMaskCol = 28;
 constexpr int kCentGrid = 4;  // angstrom
 constexpr float kNormScale = 16.0f;
 // The value tile is fp16 throughout (the probabilities multiply it as fp16).
@@ -72,6 +81,7 @@ struct Layout {
   int NKpad; // NT*64 key rows
   int NQpad; // query rows rounded up to 128
   int mfma;  // 1: matrix-core path (bf16 input), 0: fp32 path
+  int stacked;  // 1: the pages' stacked point columns (bf16, global coordinates), comparison only
   int NQS, NVB, GS;
   int QW;     // query scalar+pair width (elements)
   int KROW;   // elements per key row (mfma: head part 16 + 16 GS + pad; fp32: DKP)
@@ -134,8 +144,9 @@ constexpr int kF32MaxDV = 192;   // Dv + R*Cz + 3Q (4 threads x 48)
 constexpr int kMaxP = 5;   // 3P <= 15 point coordinates per lifted row
 constexpr int kMaxQ = 10;  // 3Q <= 30 value-point coordinates
 
-static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
+static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L, int stacked = 0) {
   if (!s) return false;
+  L->stacked = stacked ? 1 : 0;
   if (s->B <= 0 || s->N <= 0 || s->H <= 0 || s->D <= 0 || s->Dv <= 0 || s->P <= 0 || s->Q <= 0 ||
       s->Cz <= 0 || s->R <= 0 || s->Cout <= 0)
     return false;
@@ -156,6 +167,11 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
     MfmaDims md;
     if (!pick_mfma_dims(L->D, L->Dv, L->RCz, L->P, L->Q, &md)) return false;
     L->mfma = 1;
+    // the stacked comparison is compiled for the standard widths only
+    if (stacked) {
+      if (md.NQS != 9 || md.NVB != 5 || L->P != 4 || L->D % 8 || L->Dv % 8 || L->Cz % 8) return false;
+      md.GS = 2;
+    }
     L->NQS = md.NQS; L->NVB = md.NVB; L->GS = md.GS;
     L->QW = 16 * md.NQS;
     L->KROW = 16 + 16 * md.GS + kRowPad;
@@ -165,6 +181,7 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L) {
     L->DQP = L->QW;
     L->KS = key_splits(L->B, L->N, L->H, L->NT);
   } else if (s->dtype == IPA_F32) {
+    if (stacked) return false;
     if (L->D + L->RCz > kF32MaxDQ || L->DO > kF32MaxDV) return false;
     L->mfma = 0;
     L->NQS = L->NVB = L->GS = 0;

@@ -379,7 +379,7 @@ __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* skv, i
 // unless t is the first), the copies of tile t, the wait and a barrier; then
 // the products and softmax of tile t.  Returns the next tile with a valid key
 // (tend if none).
-template <int NQS, int NVB, int GS, int W, bool PM, int NBUF, int BUF>
+template <int NQS, int NVB, int GS, int W, bool PM, int NBUF, int BUF, bool STK>
 __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc& src, char* skv,
                                            const uint32_t* kmb, const float4* ckb, int t, int tend, int b, int i,
                                            bool qin, bool qvalid, bool active, int w, int lane, int l32, int half,
@@ -390,7 +390,10 @@ __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc
   const int tn = next_valid_tile(kmb, t, tend);
   uint32_t mw = 0xFFFFFFFFu;
   if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
-  geo_tile<GS>(qg, ld_uniform4(ckb + t), gl, Pf, m, half, bg);
+  if constexpr (STK)
+    geo_tile_stacked(qg, m, half, bg);
+  else
+    geo_tile<GS>(qg, ld_uniform4(ckb + t), gl, Pf, m, half, bg);
   if constexpr (NBUF == 2) {
     // tile t has landed; every wave is done with the previous tile
     wait_vmcnt<0>();
@@ -411,7 +414,7 @@ __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc
   const char* kt = skv + BUF * T::TB;
   f32x16_t sacc[2];
   __builtin_amdgcn_s_setprio(1);
-  s_tile<NQS, GS>(kt, kt + T::KH, bq, bg, l32, half, sacc);
+  s_tile<NQS, GS, 3, STK>(kt, kt + T::KH, bq, bg, l32, half, sacc);
   __builtin_amdgcn_s_setprio(0);
 
   float s32[32];
@@ -437,7 +440,7 @@ __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc
 // (the loop is unrolled by two so that buffer offsets are constants).  PM
 // selects the per-query pair-mask words (a vector load per tile); without a
 // pair mask the key mask is inside the key product.
-template <int NQS, int NVB, int GS, int W, int NBUF, bool PM>
+template <int NQS, int NVB, int GS, int W, int NBUF, bool PM, bool STK>
 __device__ __forceinline__ void attend(const FlashMfmaArgs& a, const TileSrc& src, char* skv, int t, int tend, int sp,
                                        int b, int h, int i, bool qin, bool qvalid, int w, int lane, int l32, int half,
                                        float gl, float Pf, const bf16x8_t* bq, f16x8_t* bg, const QueryGeo& qg) {
@@ -455,7 +458,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, const TileSrc& sr
   const bool active = __any(qvalid);
   const int t_first = t;
 #define FIPA_TILE(BUFI)                                                                                             \
-  attend_tile<NQS, NVB, GS, W, PM, NBUF, BUFI>(a, src, skv, kmb, ckb, t, tend, b, i, qin, qvalid, active, w, lane,   \
+  attend_tile<NQS, NVB, GS, W, PM, NBUF, BUFI, STK>(a, src, skv, kmb, ckb, t, tend, b, i, qin, qvalid, active, w, lane,   \
                                                l32, half, gl, Pf, bq, bg, qg, oacc, m, l, init, t_first)
   if constexpr (NBUF == 2) {
     while (t < tend) {
@@ -473,7 +476,7 @@ __device__ __forceinline__ void attend(const FlashMfmaArgs& a, const TileSrc& sr
 // NBUF tile buffers, each [head key rows | pair key rows | head value rows |
 // pair value rows]; with one buffer two workgroups share a CU (registers
 // capped at 256 a lane).
-template <int NQS, int NVB, int GS, int W, int NBUF>
+template <int NQS, int NVB, int GS, int W, int NBUF, bool STK = false>
 __global__ __launch_bounds__(W * 64, NBUF == 1 ? 2 : 1) void flash_mfma_kernel(FlashMfmaArgs a) {
   using T = TileDims<NQS, NVB, GS>;
   __shared__ __attribute__((aligned(1024))) char skv[NBUF * T::TB];
@@ -531,14 +534,17 @@ __global__ __launch_bounds__(W * 64, NBUF == 1 ? 2 : 1) void flash_mfma_kernel(F
   {
     float av[15];
     load_qa(reinterpret_cast<const float4*>(a.ws + qa_row_off(L, b, h, qin ? i : 0)), qin, av);
-    build_geo<GS>(L.P, av, qvalid, gl, half, bg, &qg);
+    if constexpr (STK)
+      build_geo_stacked<4>(av, half, bg, &qg);
+    else
+      build_geo<GS>(L.P, av, qvalid, gl, half, bg, &qg);
   }
 
   if (has_pm)
-    attend<NQS, NVB, GS, W, NBUF, true>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq,
+    attend<NQS, NVB, GS, W, NBUF, true, STK>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq,
                                         bg, qg);
   else
-    attend<NQS, NVB, GS, W, NBUF, false>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq,
+    attend<NQS, NVB, GS, W, NBUF, false, STK>(a, src, skv, t0, te, sp, b, h, i, qin, qvalid, w, lane, l32, half, gl, Pf, bq,
                                          bg, qg);
 }
 
@@ -612,7 +618,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Layout L, const float* par
 // more workgroups) and the same at N = 8192.  KS > 1 splits the keys of a
 // query tile into ranges (one workgroup each, the combine kernel after).
 constexpr int kShortRange = 16;
-template <int NQS, int NVB, int GS>
+template <int NQS, int NVB, int GS, bool STK = false>
 static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st) {
   FlashMfmaArgs a;
   a.L = L;
@@ -630,11 +636,11 @@ static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* 
     if (L.KS == 1 && L.NT <= kShortRange) {
       a.qtiles = (L.N + 127) / 128;
       a.nwg = a.qtiles * L.H * L.B * L.KS;
-      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4, 1>), dim3(a.nwg), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 4, 1, STK>), dim3(a.nwg), dim3(256), 0, st, a);
     } else {
       a.qtiles = (L.N + 255) / 256;
       a.nwg = a.qtiles * L.H * L.B * L.KS;
-      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 8, 2>), dim3(a.nwg), dim3(512), 0, st, a);
+      hipLaunchKernelGGL((flash_mfma_kernel<NQS, NVB, GS, 8, 2, STK>), dim3(a.nwg), dim3(512), 0, st, a);
     }
   }
   if (L.KS > 1) {
@@ -646,6 +652,11 @@ static hipError_t launch_inst(const Layout& L, const void* ws, float* o, float* 
 }
 
 hipError_t launch_flash_mfma(const Layout& L, const void* ws, float* o, float* lse, hipStream_t st) {
+  if (L.stacked) {
+    // the pages' stacked point columns (comparison): standard widths only
+    if (L.GS == 2 && L.NQS == 9 && L.NVB == 5) return launch_inst<9, 5, 2, true>(L, ws, o, lse, st);
+    return hipErrorInvalidValue;
+  }
   if (L.GS == 3) {
     if (L.NQS == 3 && L.NVB == 2) return launch_inst<3, 2, 3>(L, ws, o, lse, st);
     if (L.NQS == 5 && L.NVB == 3) return launch_inst<5, 3, 3>(L, ws, o, lse, st);

@@ -446,10 +446,10 @@ __device__ __forceinline__ void store_vt_rows(uint16_t* vt, const uint16_t (*src
   }
 }
 
-template <int P>
+template <int P, bool STK = false>
 __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastArgs f) {
   constexpr int P3 = 3 * P;
-  constexpr int GS = P <= 4 ? 3 : 4;
+  constexpr int GS = STK ? 2 : (P <= 4 ? 3 : 4);
   const Layout& L = a.L;
   const int N = L.N, H = L.H, Q = L.Q, D = L.D, Dv = L.Dv, RCz = L.RCz, Cz = L.Cz;
   const int u = (int)(blockIdx.x % 8) * f.per_xcd + (int)(blockIdx.x / 8);
@@ -799,6 +799,20 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       // value of geometric column g of this key (layout in common.h)
       auto geo = [&](int g) -> uint16_t {
         uint16_t val = 0;
+        if constexpr (STK) {
+          // stacked comparison: global key points b = w + c in bf16
+          if (g < 5 * P) {
+            const int p = g / 5, e = g % 5;
+            const float bx = w[3 * p] + cx, by = w[3 * p + 1] + cy, bz = w[3 * p + 2] + cz;
+            if (e < 3) val = f32_to_bf16_bits(2.f * gl * (e == 0 ? bx : (e == 1 ? by : bz)));
+            else if (e == 3) val = f32_to_bf16_bits(-gl);
+            else val = f32_to_bf16_bits(-gl * (bx * bx + by * by + bz * bz));
+          } else if (g > kStkMaskCol && g < 32) {
+            val = 0x4180;  // bf16 16.0, multiplies the query's -m/16 parts
+          }
+          if (!valid) val = g == kStkMaskCol ? (uint16_t)0xC780 : (g > kStkMaskCol && g < 32 ? val : (uint16_t)0);
+          return val;
+        }
         if (g < base + 4) {
           if (g < P3) val = hi16(w[g]);
           else if (g < 2 * P3) val = lo16(w[g - P3]);
@@ -919,6 +933,11 @@ hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStre
   const bool aligned = (reinterpret_cast<uintptr_t>(in->q) | reinterpret_cast<uintptr_t>(in->k) |
                         reinterpret_cast<uintptr_t>(in->v) | reinterpret_cast<uintptr_t>(in->zl) |
                         reinterpret_cast<uintptr_t>(in->zr)) % 16 == 0;
+  if (L.stacked) {
+    // the stacked comparison runs on the fast kernel only (P = 4, checked by
+    // the caller)
+    if (!aligned || !lift_fast_fits(L) || L.P != 4) return hipErrorInvalidValue;
+  }
   if (aligned && lift_fast_fits(L)) {
     LiftFastArgs f;
     f.units = L.B * L.NT * (L.H + 1);
@@ -935,7 +954,12 @@ hipError_t launch_lift(const Layout& L, const ipa_lift_in* in, void* ws, hipStre
       case 1: hipLaunchKernelGGL(lift_fast_kernel<1>, g, blk, 0, st, a, f); break;
       case 2: hipLaunchKernelGGL(lift_fast_kernel<2>, g, blk, 0, st, a, f); break;
       case 3: hipLaunchKernelGGL(lift_fast_kernel<3>, g, blk, 0, st, a, f); break;
-      case 4: hipLaunchKernelGGL(lift_fast_kernel<4>, g, blk, 0, st, a, f); break;
+      case 4:
+        if (L.stacked)
+          hipLaunchKernelGGL((lift_fast_kernel<4, true>), g, blk, 0, st, a, f);
+        else
+          hipLaunchKernelGGL(lift_fast_kernel<4>, g, blk, 0, st, a, f);
+        break;
       default: hipLaunchKernelGGL(lift_fast_kernel<5>, g, blk, 0, st, a, f); break;
     }
   } else if (L.mfma)

@@ -57,6 +57,7 @@ struct QueryGeo {
   float U[3];
   float SA;
   uint32_t fix0, fix1;  // fixed first two dwords of the last geometric K-step
+  uint32_t fix2, fix3;  // stacked layout: its last two dwords (half 0)
 };
 
 template <int P, int GS>
@@ -133,6 +134,54 @@ __device__ __forceinline__ void build_geo(int P, const float* av, bool qvalid, f
   }
 }
 
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Query side of the stacked comparison layout (common.h): per point
+// [a_p (3) | |a_p|^2 | 1] in bf16 from the global query points, 16 in the
+// key-mask column; the -m/16 columns are set per key tile (geo_tile_stacked).
+template <int P>
+__device__ __forceinline__ void build_geo_stacked(const float* av, int half, f16x8_t* bg, QueryGeo* qg) {
+  auto qval = [&](int g) -> float {
+    if (g < 5 * P) {
+      const int p = g / 5, e = g % 5;
+      const float x = av[3 * p], y = av[3 * p + 1], z = av[3 * p + 2];
+      return e == 0 ? x : (e == 1 ? y : (e == 2 ? z : (e == 3 ? x * x + y * y + z * z : 1.0f)));
+    }
+    return g == kStkMaskCol ? 16.0f : 0.f;
+  };
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    uint32_t d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int g0 = 16 * s + 8 * half + 2 * e;
+      d[e] = pack_bf16(qval(g0), qval(g0 + 1));
+    }
+    bg[s] = __builtin_bit_cast(f16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+  }
+  const uint4 last = __builtin_bit_cast(uint4, bg[1]);
+  qg->fix0 = last.x; qg->fix1 = last.y; qg->fix2 = last.z; qg->fix3 = last.w;
+}
+
+// Per key tile (stacked layout): -msub/16 in three bf16 parts in columns
+// 29..31 (half 1, elements 5..7), so that the product returns the logit
+// minus msub.
+__device__ __forceinline__ void geo_tile_stacked(const QueryGeo& qg, float msub, int half, f16x8_t* bg) {
+  const float x = -msub * (1.0f / 16.0f);
+  const float h1 = bf16_bits_to_f32(f32_to_bf16_bits(x));
+  const float r1 = x - h1;
+  const float h2 = bf16_bits_to_f32(f32_to_bf16_bits(r1));
+  const float h3 = r1 - h2;
+  uint4 last = make_uint4(qg.fix0, qg.fix1, qg.fix2, qg.fix3);
+  if (half) {
+    last.z = (qg.fix2 & 0xFFFFu) | ((uint32_t)f32_to_bf16_bits(h1) << 16);
+    last.w = pack_bf16(h2, h3);
+  }
+  bg[1] = __builtin_bit_cast(f16x8_t, last);
+}
+
 // Per key tile: -delta (exact in fp16) in the last K-step, and the row term
 // t' - msub (three fp16 parts of (t' - msub)/16) in the slots of half 1, so
 // that the product returns the logit minus msub (the running maximum of the
@@ -167,7 +216,7 @@ __device__ __forceinline__ void geo_tile(const QueryGeo& qg, float4 ct, float gl
 // their MFMA so that the reads' latency hides behind the preceding MFMAs.
 // s_tile_ops emits the reads and MFMAs only; the caller orders them
 // (s_tile_sched), so that other work can be placed between them.
-template <int NQS, int GS, int DEPTH>
+template <int NQS, int GS, int DEPTH, bool STK = false>
 __device__ __forceinline__ void s_tile_ops(const char* khead, const char* kpair, const bf16x8_t* bq,
                                            const f16x8_t* bg, int l32, int half, f32x16_t* sacc) {
   constexpr int KROW = 16 + 16 * GS + kRowPad;
@@ -201,6 +250,11 @@ __device__ __forceinline__ void s_tile_ops(const char* khead, const char* kpair,
     if (st < NQS) {
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c0), bq[st], sacc[0], 0, 0, 0);
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c1), bq[st], sacc[1], 0, 0, 0);
+    } else if constexpr (STK) {
+      // stacked comparison layout: bf16 point columns
+      const bf16x8_t g = __builtin_bit_cast(bf16x8_t, bg[st - NQS]);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c0), g, sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c1), g, sacc[1], 0, 0, 0);
     } else {
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c0), bg[st - NQS], sacc[0], 0, 0, 0);
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, c1), bg[st - NQS], sacc[1], 0, 0, 0);
@@ -222,10 +276,10 @@ __device__ __forceinline__ void s_tile_sched() {
   }
 }
 
-template <int NQS, int GS, int DEPTH = 3>
+template <int NQS, int GS, int DEPTH = 3, bool STK = false>
 __device__ __forceinline__ void s_tile(const char* khead, const char* kpair, const bf16x8_t* bq, const f16x8_t* bg,
                                        int l32, int half, f32x16_t* sacc) {
-  s_tile_ops<NQS, GS, DEPTH>(khead, kpair, bq, bg, l32, half, sacc);
+  s_tile_ops<NQS, GS, DEPTH, STK>(khead, kpair, bq, bg, l32, half, sacc);
   s_tile_sched<NQS + GS, DEPTH, 0>();
 }
 

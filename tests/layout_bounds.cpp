@@ -163,6 +163,8 @@ static void check_copies() {
   check_fused_inst<5, 3, 4, 4>(); check_fused_inst<5, 3, 4, 8>(); check_fused_inst<9, 5, 3, 4>();
   check_fused_inst<9, 5, 3, 8>(); check_fused_inst<9, 5, 4, 4>(); check_fused_inst<9, 5, 4, 8>();
   check_fused_inst<13, 7, 3, 4>(); check_fused_inst<13, 7, 4, 4>();
+  // the stacked point layout (comparison): two bf16 geometric K-steps
+  check_fused_inst<9, 5, 2, 4>(); check_fused_inst<9, 5, 2, 8>();
   // epilogue: W_h of Cout rows at the head-feature pitch, 4 wavefronts
   check_copy_inst<32 * kHeadFeatPitch * 2, 4>("epilogue w_out head");
   check_copy_inst<64 * kHeadFeatPitch * 2, 4>("epilogue w_out head");
@@ -201,14 +203,15 @@ struct Region {
   size_t start, end;  // [start, end), end = start of the next region
 };
 
-static void check_layout(const ipa_shape& s, int with_pm) {
+static void check_layout(const ipa_shape& s, int with_pm, int stacked = 0) {
   Layout L;
-  if (!make_layout(&s, with_pm, &L)) return;  // unsupported shape: nothing to check
+  if (!make_layout(&s, with_pm, &L, stacked)) return;  // unsupported shape: nothing to check
   char tag[160];
-  std::snprintf(tag, sizeof tag, "B%lld N%lld H%lld D%lld Dv%lld P%lld Q%lld Cz%lld R%lld Cout%lld %s pm%d",
+  std::snprintf(tag, sizeof tag, "B%lld N%lld H%lld D%lld Dv%lld P%lld Q%lld Cz%lld R%lld Cout%lld %s pm%d%s",
                 (long long)s.B, (long long)s.N, (long long)s.H, (long long)s.D, (long long)s.Dv, (long long)s.P,
                 (long long)s.Q, (long long)s.Cz, (long long)s.R, (long long)s.Cout,
-                s.dtype == IPA_BF16 ? "bf16" : "f32", with_pm);
+                s.dtype == IPA_BF16 ? "bf16" : "f32", with_pm, stacked ? " stacked" : "");
+  if (stacked) CHECK(L.GS == 2 && L.NQS == 9 && L.NVB == 5 && L.KROW == 56, "%s: stacked instance", tag);
   const int B = L.B, H = L.H, NT = L.NT;
   const size_t e = lifted_elem(L);
   CHECK(L.NKpad == NT * 64 && L.NKpad <= L.NQpad, "%s: padded rows", tag);
@@ -319,7 +322,8 @@ static void check_layouts() {
       v.push_back(shape(2, n, 12, 16, 16, 4, 8, 64, 2, 96, dt));
     }
   for (const ipa_shape& s : v)
-    for (int pm : {0, 1}) check_layout(s, pm);
+    for (int pm : {0, 1})
+      for (int stk : {0, 1}) check_layout(s, pm, stk);
 }
 
 int main() {

@@ -250,3 +250,29 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     li.q = 4100
     assert lib.ipa_forward_noalloc(ctypes.byref(_shape(B=1, N=100)), ctypes.byref(li), ctypes.byref(ei), 4096, 4096,
                                    None) == 4
+
+
+def test_stacked_layout_shapes_and_validation(lib):
+    """The stacked point-layout comparison: standard widths on the bf16 path
+    only, a smaller lifted buffer (two geometric K-steps of 16 instead of
+    three), the same validation as ipa_lift / ipa_flash_fwd."""
+    s = _shape()
+    std, stk = _lib.lifted_bytes(s, False), _lib.lifted_bytes(s, False, stacked=True)
+    assert 0 < stk < std
+    # the key rows lose 16 elements of 2 bytes per residue and head
+    assert std - stk >= 2 * 8 * 320 * 16 * 2 - 4 * 256
+    assert _lib.lifted_bytes(_shape(dtype="f32"), False, stacked=True) == 0
+    assert _lib.lifted_bytes(_shape(P=3), False, stacked=True) == 0
+    assert _lib.lifted_bytes(_shape(R=3), False, stacked=True) == 0
+    assert _lib.lifted_bytes(_shape(Cz=32), False, stacked=True) == 0
+    fields = [n for n, _ in _lib.IpaLiftIn._fields_ if n != "pair_mask"]
+    li = _lib.IpaLiftIn(**{n: 4096 for n in fields})
+    assert lib.ipa_lift_stacked(None, ctypes.byref(li), 4096, 1 << 40, None) == 1
+    assert lib.ipa_lift_stacked(ctypes.byref(s), ctypes.byref(li), 4096, stk - 1, None) == 2
+    li.k = 4100
+    assert lib.ipa_lift_stacked(ctypes.byref(s), ctypes.byref(li), 4096, 1 << 40, None) == 4
+    assert lib.ipa_lift_stacked(ctypes.byref(_shape(P=3)), ctypes.byref(li), 4096, 1 << 40, None) == 3
+    assert lib.ipa_flash_fwd_stacked(ctypes.byref(s), None, 4096, 4096, None) == 1
+    assert lib.ipa_flash_fwd_stacked(ctypes.byref(s), 4096, 4100, 4096, None) == 4
+    assert lib.ipa_flash_fwd_stacked(ctypes.byref(_shape(dtype="f32")), 4096, 4096, 4096, None) == 3
+

@@ -1,0 +1,118 @@
+"""The pages' stacked point layout as a GPU path (ipa_lift_stacked /
+ipa_flash_fwd_stacked), beside this build's centred fp16 hi/lo layout.
+
+The FlashIPA rebuttal (paperhub page, Q3) feeds the point term to the
+attention kernel as stacked vectors of five columns per point.  In 16-bit
+operands that layout rounds the squared norms of global coordinates, so its
+logit error grows with the distance of the chain from the origin.  The first
+test pins the stacked path to the oracle within the error its own bf16
+operands allow (a bound computed from the inputs, small when the
+coordinates are small), so that the second test's error figures measure the
+layout and not a fault of the kernel; the second measures both paths against
+the float64 oracle on sampled rows of an N = 16384 random walk."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ipa_factored, point_weight, to_global
+from rna_structure_amd import _lib
+from rna_structure_amd.synth import IPAShape, make_inputs
+
+from gpu_helpers import compare, run_gpu, say, split_o
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_stacked(inp):
+    shape = inp["shape"]
+    t = _lib.device_inputs(inp, "cuda")
+    f = _lib.FlashIPA(shape, eps=inp["eps"], with_pair_mask=t["pair_mask"] is not None, stacked=True)
+    f.poison()
+    out = f.forward(t)
+    torch.cuda.synchronize()
+    return {k: v.detach().cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+def _stacked_logit_bound(inp):
+    """Upper bound (natural-log units) on the logit error of the stacked bf16
+    operands, per (b, h, i, j): every operand carries a relative rounding
+    error of at most 2^-9 (round to nearest), so a product of two carries at
+    most 2^-8 (1 + 2^-10), summed over the point columns in absolute value;
+    plus the bf16 bar of the scalar and pair columns (shared with the
+    standard path) and the fp32 accumulation."""
+    s = inp["shape"]
+    gam = point_weight(inp["point_weight_raw"], s.P)                          # [H]
+    A = to_global(inp["rotation"], inp["translation"], inp["q_points"])       # [B,N,H,P,3]
+    Bk = to_global(inp["rotation"], inp["translation"], inp["k_points"])
+    # query [a | |a|^2 | 1] against key [2 gamma b | -gamma | -gamma |b|^2]
+    # (the kernel's log2 e scaling cancels in natural-log units)
+    cross = 2.0 * np.einsum("bihpc,bjhpc->bhij", np.abs(A), np.abs(Bk))
+    na = np.sum(A ** 2, axis=(-1, -2)).transpose(0, 2, 1)[..., :, None]     # [B,H,N,1]
+    nb = np.sum(Bk ** 2, axis=(-1, -2)).transpose(0, 2, 1)[..., None, :]    # [B,H,1,N]
+    rel = 2.0 ** -8 * (1 + 2.0 ** -10)
+    return rel * gam[None, :, None, None] * (cross + na + nb)
+
+
+def test_stacked_layout_matches_oracle_within_its_rounding():
+    """Coordinates within a few angstrom of the origin: the stacked path's
+    own rounding is small, and its lse and outputs must follow the oracle
+    within the bound that rounding allows."""
+    s = IPAShape(B=2, N=300, H=8, dtype="bf16")
+    inp = make_inputs(s, 4242, frames="gauss", trans_sigma=0.5, lengths=(200, 300), masked_keys=(7,),
+                      pair_dropout=0.05)
+    say(f"case stacked small coordinates {s}")
+    got = _run_stacked(inp)
+    ref = ipa_factored(inp, keep=("update", "local_points", "lse", "empty", "o_scalar", "g"))
+    mask = inp["mask"].astype(bool)
+    perm = mask[:, :, None] & mask[:, None, :]
+    if inp["pair_mask"] is not None:
+        perm &= inp["pair_mask"].astype(bool)
+    bound = _stacked_logit_bound(inp)                                         # [B,H,N,N]
+    beta = np.max(np.where(perm[:, None], bound, 0.0), axis=-1)             # [B,H,N] worst permitted key
+    lse_r, lse_g = ref["lse"], got["lse"]
+    fin = np.isfinite(lse_r)
+    assert np.array_equal(np.isfinite(lse_g), fin), "empty-neighbourhood rows differ"
+    err = np.abs(lse_g[fin] - lse_r[fin])
+    allow = (beta + 2e-2 * np.maximum(1.0, np.abs(lse_r)))[fin]
+    say(f"  lse: max error {err.max():.3e}, max allowed {allow.max():.3e} (rounding bound up to {beta[fin].max():.3e})")
+    assert np.all(err <= allow)
+    # attention output: weights perturbed by at most a factor exp(+-2 beta)
+    o = split_o(got["o"], s)
+    vmax = np.max(np.abs(inp["v"]))
+    w = np.exp(2.0 * beta.transpose(0, 2, 1)) - 1.0                           # [B,N,H]
+    e_o = np.abs(o["o_scalar"] - ref["o_scalar"]).max(axis=-1)
+    assert np.all(e_o <= w * 2 * vmax + 2e-2 * np.max(np.abs(ref["o_scalar"])))
+    assert beta[fin].max() < 0.2, "the case no longer has small coordinates"
+    for key in ("update", "local_points"):
+        assert np.all(np.isfinite(got[key]))
+    empty = ref["empty"]
+    assert empty.any()
+    assert np.all(got["update"][np.nonzero(empty)] == 0.0)
+
+
+def test_stacked_layout_against_centred_split_long_chain():
+    """N = 16384 random walk (3.8 A steps): both layouts against the float64
+    oracle on sampled rows.  The centred split stays within the bf16 path's
+    bar; the stacked layout's global squared norms carry errors orders of
+    magnitude larger."""
+    s = IPAShape(B=1, N=16384, H=8, dtype="bf16")
+    inp = make_inputs(s, 9161, frames="walk", step=3.8)
+    rows = np.array([0, 3000, 8191, 12000, 16383])
+    say(f"case stacked vs centred long chain {s} rows {rows.tolist()}")
+    _, _, std = run_gpu(inp)
+    e_std = compare(inp, std, rows=rows, tol=2e-2)
+    stk = _run_stacked(inp)
+    ref = ipa_factored(inp, rows=rows, keep=("lse", "o_scalar", "g", "update"))
+    o = split_o(stk["o"], s)
+    e_stk = {"lse": float(np.max(np.abs(stk["lse"][:, :, rows] - ref["lse"]))),
+             "o_scalar": float(np.max(np.abs(o["o_scalar"][:, rows] - ref["o_scalar"])) / np.max(np.abs(ref["o_scalar"]))),
+             "update": float(np.max(np.abs(stk["update"][:, rows] - ref["update"])) / np.max(np.abs(ref["update"])))}
+    lse_std = float(np.max(np.abs(std["lse"][:, :, rows] - ref["lse"])))
+    say(f"  stacked bf16 layout: |lse error| {e_stk['lse']:.3g}, o_scalar {e_stk['o_scalar']:.3g}, "
+        f"update {e_stk['update']:.3g} (max-abs-rel); centred split: |lse error| {lse_std:.3g}, "
+        f"o_scalar {e_std['o_scalar']:.3g}, update {e_std['update']:.3g}")
+    assert np.all(np.isfinite(stk["o"])) and np.all(np.isfinite(stk["update"]))
+    assert e_stk["lse"] > 100 * lse_std
+    assert e_stk["update"] > 10 * e_std["update"]
