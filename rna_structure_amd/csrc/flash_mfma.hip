@@ -34,11 +34,12 @@
 // Two schemes (NBUF): with two buffers the copies of the next tile run
 // during the whole of the current tile and one barrier per tile separates
 // the two (8 wavefronts, one workgroup per CU: long key ranges); with one
-// buffer the next tile's key parts are copied during the current softmax and
-// value product, its value parts during the next key product, and the
-// remaining latency is hidden by a second workgroup on the CU (4 wavefronts,
-// two workgroups per CU: short key ranges, where the per-workgroup prologue
-// and output also overlap with the other workgroup's tiles).
+// buffer the copies of a tile go out when every wavefront is done with the
+// previous one, and the latency is hidden by a second workgroup on the CU
+// (4 wavefronts, two workgroups per CU: short key ranges, where the
+// per-workgroup prologue and output also overlap with the other
+// workgroup's tiles).  (Refilling the key and value parts of the one buffer
+// in turn, so that copies overlap the products, measured no faster.)
 #include "lds_copy.h"
 #include "mfma_tile.h"
 
@@ -110,29 +111,6 @@ __device__ __forceinline__ void copy_kv_tile(const TileSrc& src, char* skv, int 
   dma_parts<T::KH, T::KZ, T::VH, T::VZ, W>(src.kh + (size_t)t * T::KH, src.kz + (size_t)t * T::KZ,
                                            src.vh + (size_t)t * T::VH, src.vz + (size_t)t * T::VZ,
                                            skv + buf * T::TB, w, lane);
-}
-
-// The key parts (head and pair-factor key rows) and the value parts of tile t
-// separately, into the single buffer of the one-buffer scheme: the key parts
-// of the next tile go out once every wavefront is done with the current
-// key rows, the value parts once it is done with the current value rows.
-template <int NQS, int NVB, int GS, int W>
-__device__ __forceinline__ void copy_k_part(const TileSrc& src, char* skv, int t, int w, int lane) {
-  using T = TileDims<NQS, NVB, GS>;
-  dma_parts<T::KH, T::KZ, 0, 0, W>(src.kh + (size_t)t * T::KH, src.kz + (size_t)t * T::KZ, src.kz, src.kz, skv, w,
-                                   lane);
-}
-template <int NQS, int NVB, int GS, int W>
-__device__ __forceinline__ void copy_v_part(const TileSrc& src, char* skv, int t, int w, int lane) {
-  using T = TileDims<NQS, NVB, GS>;
-  dma_parts<T::VH, T::VZ, 0, 0, W>(src.vh + (size_t)t * T::VH, src.vz + (size_t)t * T::VZ, src.vz, src.vz,
-                                   skv + T::KH + T::KZ, w, lane);
-}
-// copies each wavefront issues for the value parts of a tile
-template <int NQS, int NVB, int GS, int W>
-constexpr int v_part_copies() {
-  using T = TileDims<NQS, NVB, GS>;
-  return dma_per_wave<T::VH + T::VZ, W>();
 }
 
 // Second half of the online softmax: p = 2^s (s already relative to the
@@ -444,14 +422,11 @@ __device__ __forceinline__ void finish_rows(const FlashMfmaArgs& a, char* skv, i
 // index, so that every LDS offset is a constant): the point operand with the
 // current running maximum; with two buffers the wait for the tile's copies
 // (issued one tile earlier), the barrier that makes them visible and frees
-// the other buffer, and the copies of the next valid tile into that buffer,
-// then the products and softmax of tile t; with one buffer the key and value
-// parts are refilled in turn: wait for the key parts of tile t and a
-// barrier, the key product, wait for its value parts and a barrier (every
-// wavefront is done with the key rows), the copies of the next tile's key
-// parts, the softmax and value product, a barrier (every wavefront is done
-// with the value rows) and the copies of the next tile's value parts.
-// Returns the next tile with a valid key (tend if none).
+// the other buffer, and the copies of the next valid tile into that buffer;
+// with one buffer a barrier (every wavefront is done with the previous tile,
+// unless t is the first), the copies of tile t, the wait and a barrier; then
+// the products and softmax of tile t.  Returns the next tile with a valid key
+// (tend if none).
 template <int NQS, int NVB, int GS, int W, bool PM, int NBUF, int BUF, bool STK>
 __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc& src, char* skv,
                                            const uint32_t* kmb, const float4* ckb, int t, int tend, int b, int i,
@@ -461,47 +436,6 @@ __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc
   using T = TileDims<NQS, NVB, GS>;
   const Layout& L = a.L;
   const int tn = next_valid_tile(kmb, t, tend);
-  if constexpr (NBUF == 1) {
-    // one buffer, its key and value parts refilled in turn: the key parts
-    // of tile t have landed (its value parts may still be in flight)
-    wait_vmcnt<v_part_copies<NQS, NVB, GS, W>()>();
-    __syncthreads();
-    uint32_t mw = 0xFFFFFFFFu;
-    if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
-    if constexpr (STK)
-      geo_tile_stacked(qg, m, half, bg);
-    else
-      geo_tile<GS>(qg, ld_uniform4(ckb + t), gl, Pf, m, half, bg);
-    f32x16_t sacc[2];
-    if (active) {
-      __builtin_amdgcn_s_setprio(1);
-      s_tile<NQS, GS, 3, STK>(skv, skv + T::KH, bq, bg, l32, half, sacc);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    // the value parts (and the pair-mask word) have landed; every wave is
-    // done with the key rows, which now take the next tile's
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (tn < tend) copy_k_part<NQS, NVB, GS, W>(src, skv, tn, w, lane);
-    if (active) {
-      float s32[32];
-      const float alpha = softmax_max<PM>(sacc, mw, m, init, s32);
-      f16x8_t ph[4];
-      const float ps = exp_tile(s32, ph);
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int vb = 0; vb <= NVB; ++vb) oacc[vb] *= alpha;
-      }
-      l = l * alpha + ps;
-      __builtin_amdgcn_s_setprio(1);
-      pv_tile<NVB>(skv + T::KH + T::KZ + (size_t)(l32 * kVCols) * 2 + half * 16, ph, oacc);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    // every wave is done with the value rows, which now take the next tile's
-    __syncthreads();
-    if (tn < tend) copy_v_part<NQS, NVB, GS, W>(src, skv, tn, w, lane);
-    return tn;
-  }
   uint32_t mw = 0xFFFFFFFFu;
   if constexpr (PM) mw = perm_word(L, a.ws, true, b, i, qin, qvalid, t, half);
   if constexpr (STK)
@@ -621,15 +555,7 @@ __global__ __launch_bounds__(W * 64, NBUF == 1 ? 2 : 1) void flash_mfma_kernel(F
   // before anything else is loaded
   const int tb = (int)(((long)NT * sp) / a.ks), te = (int)(((long)NT * (sp + 1)) / a.ks);
   const int t0 = next_valid_tile(kmb, tb - 1, te);
-  if (t0 < te) {
-    if constexpr (NBUF == 1) {
-      // key parts first, then value parts (the tile loop waits for them in turn)
-      copy_k_part<NQS, NVB, GS, W>(src, skv, t0, w, lane);
-      copy_v_part<NQS, NVB, GS, W>(src, skv, t0, w, lane);
-    } else {
-      copy_kv_tile<NQS, NVB, GS, W>(src, skv, t0, 0, w, lane);
-    }
-  }
+  if (t0 < te) copy_kv_tile<NQS, NVB, GS, W>(src, skv, t0, 0, w, lane);
   {
     // a workgroup none of whose queries is valid (padding) only writes zeros
     const int tq0 = (qt * W * 32) >> 6, tq1 = min(NT, tq0 + W / 2);

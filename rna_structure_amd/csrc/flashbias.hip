@@ -453,10 +453,28 @@ void bias_attn_kernel(BiasLayout L, const char* ws, const void* qin, const void*
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.0f / l;
   if (hf == 0 && i < L.N) lse[bh * L.N + i] = empty ? -INFINITY : (m + log2f(l)) * kBiasLn2;
-  // O^T (value columns x this wavefront's 32 queries) through LDS, one block
-  // of 32 columns at a time, so that every query row is written as whole
-  // 128-byte pieces of consecutive columns
-  wait_vmcnt<0>();
+  wait_vmcnt<0>();  // no tile copy is still in flight when the workgroup ends
+  if ((L.Dv & 3) == 0) {
+    // registers 4g .. 4g+3 of a block are value columns 8g + 4 hf .. +3 of
+    // the lane's query: one 16-byte store each, straight from the registers
+    // (uniform condition: no wavefront takes the barrier below)
+    if (i < L.N) {
+      float* orow = o + (((size_t)b * L.N + i) * L.H + h) * L.Dv;
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = 32 * vb + 8 * g + 4 * hf;
+          if (c < L.Dv)
+            *reinterpret_cast<float4*>(orow + c) = make_float4(oacc[vb][4 * g] * inv, oacc[vb][4 * g + 1] * inv,
+                                                               oacc[vb][4 * g + 2] * inv, oacc[vb][4 * g + 3] * inv);
+        }
+    }
+    return;
+  }
+  // other widths: O^T (value columns x this wavefront's 32 queries) through
+  // LDS, one block of 32 columns at a time, so that every query row is
+  // written as whole 128-byte pieces of consecutive columns
   __syncthreads();  // the last tile's LDS reads are done in every wavefront
   float* so = reinterpret_cast<float*>(smem) + w * 32 * 36;
   const int cq = lane & 7;  // 16-byte piece of a row

@@ -87,7 +87,7 @@ struct FusedParts {
 static void check_parts(const int* bytes, int W, int per_wave, const char* what) {
   int C = 0, start[5];
   for (int p = 0; p < 4; ++p) {
-    CHECK(bytes[p] % 1024 == 0 && (bytes[p] > 0 || p >= 2), "%s: part %d of %d bytes", what, p, bytes[p]);
+    CHECK(bytes[p] % 1024 == 0 && bytes[p] > 0, "%s: part %d of %d bytes", what, p, bytes[p]);
     start[p] = C;
     C += bytes[p] / 1024;
   }
@@ -116,12 +116,6 @@ static void check_fused_inst() {
   const int parts[4] = {T::KH, T::KZ, T::VH, T::VZ};
   constexpr int TB = T::KH + T::KZ + T::VH + T::VZ;
   check_parts(parts, W, dma_per_wave<TB, W>(), "fused tile");
-  // the one-buffer scheme copies the key parts and the value parts apart
-  // (dma_parts with two empty parts), each at its own place in the buffer
-  const int kparts[4] = {T::KH, T::KZ, 0, 0}, vparts[4] = {T::VH, T::VZ, 0, 0};
-  check_parts(kparts, W, dma_per_wave<T::KH + T::KZ, W>(), "fused key parts");
-  check_parts(vparts, W, dma_per_wave<T::VH + T::VZ, W>(), "fused value parts");
-  CHECK(T::KH + T::KZ + T::VH + T::VZ == TB && (T::KH + T::KZ) % 1024 == 0, "value parts start on a KiB");
   CHECK(2 * TB <= 160 * 1024, "fused tile buffers %d bytes", 2 * TB);
   // key operand reads (s_tile_ops): lane (l32, half), key block kb; head
   // part at row pitch 16 + 16 GS + pad, pair part at 16 (NQS - 1) + pad
