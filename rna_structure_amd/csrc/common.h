@@ -41,6 +41,9 @@ constexpr int kQueryTile = 128;
 // the key-mask column (key -65536 when masked, query 16) and columns 29..31
 // carry the query's -m/16 in three bf16 parts against a key value of 16.
 constexpr int kStkMaskCol = 28;
+// log2(e) / sqrt(3): the pair bias enters the logit divided by sqrt(3), in
+// log2 units
+constexpr float kPairScale = (float)(1.4426950408889634 / 1.7320508075688772);
 constexpr int kCentGrid = 4;  // angstrom
 constexpr float kNormScale = 16.0f;
 // The value tile is fp16 throughout (the probabilities multiply it as fp16).
@@ -83,7 +86,8 @@ struct Layout {
   int mfma;  // 1: matrix-core path (bf16 input), 0: fp32 path
   int stacked;  // 1: the pages' stacked point columns (bf16, global coordinates), comparison only
   int NQS, NVB, GS;
-  int QW;     // query scalar+pair width (elements)
+  int QW;     // per-head query row width (elements): mfma 16 (the scalar columns); fp32 D + R Cz padded
+  int ZW;     // mfma: query pair columns 16 (NQS - 1), shared by the heads (QZ rows, WP rows)
   int KROW;   // elements per key row (mfma: head part 16 + 16 GS + pad; fp32: DKP)
   int VROWS;  // mfma: rows of the head part of the transposed value tile (64); fp32: DVP (row stride)
   int KZROW;  // mfma: elements per row of the shared pair-factor key tile, 16 (NQS - 1) + pad
@@ -94,7 +98,8 @@ struct Layout {
   int F, FP;  // epilogue feature count, padded to 16
   int KS;     // matrix-core path: key ranges the fused kernel splits a query tile over
   int PREC;   // floats per partial-result record (KS > 1): DO values + 4 statistics, padded to 4
-  size_t off_ql, off_qa, off_kt, off_vt, off_ktz, off_vtz, off_ck, off_gam, off_km, off_part, off_pm, total;
+  size_t off_ql, off_qz, off_wp, off_qa, off_kt, off_vt, off_ktz, off_vtz, off_ck, off_gam, off_km, off_part, off_pm,
+      total;
   size_t epi_ws;  // bytes of the epilogue's own workspace (packed w_out)
 };
 
@@ -173,12 +178,13 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L, int s
       md.GS = 2;
     }
     L->NQS = md.NQS; L->NVB = md.NVB; L->GS = md.GS;
-    L->QW = 16 * md.NQS;
+    L->QW = 16;
+    L->ZW = 16 * (md.NQS - 1);
     L->KROW = 16 + 16 * md.GS + kRowPad;
     L->VROWS = 64;
     L->KZROW = 16 * (md.NQS - 1) + kRowPad;
     L->VZROWS = 32 * (md.NVB - 1);
-    L->DQP = L->QW;
+    L->DQP = 16 * md.NQS;
     L->KS = key_splits(L->B, L->N, L->H, L->NT);
   } else if (s->dtype == IPA_F32) {
     if (stacked) return false;
@@ -188,6 +194,7 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L, int s
     L->KS = 1;
     L->DQP = round_up(L->D + L->RCz, 4);
     L->QW = L->DQP;
+    L->ZW = 0;
     L->KROW = round_up(L->D + L->RCz + 3 * L->P, 4);
     L->VROWS = round_up(L->DO, 4);
     L->KZROW = L->VZROWS = 0;
@@ -197,6 +204,13 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L, int s
   size_t off = 256;  // header
   L->off_ql = off;
   off = align256(off + B * H * NQ * L->QW * (L->mfma ? 2 : 4));
+  // matrix-core path: the query pair factors zl, shared by the heads, and the
+  // per-head pair weights w_pair, each padded to ZW columns (bf16); the fused
+  // kernel forms the pair part of its query operand from them
+  L->off_qz = off;
+  off = align256(off + B * NQ * (size_t)L->ZW * 2);
+  L->off_wp = off;
+  off = align256(off + H * (size_t)L->ZW * 2);
   L->off_qa = off;
   off = align256(off + B * H * NQ * 16 * 4);
   L->off_kt = off;
@@ -237,12 +251,18 @@ static inline bool make_layout(const ipa_shape* s, int with_pm, Layout* L, int s
 
 // Byte offsets of the records of the lifted workspace, used by the kernels
 // that write and read them and by the host-side bounds check of the tests.
-// Region sizes (make_layout): QL B H NQpad QW e, QA B H NQpad 64, KT B H NT
+// Region sizes (make_layout): QL B H NQpad QW e, QZ B NQpad ZW 2, WP H ZW 2,
+// QA B H NQpad 64, KT B H NT
 // (64 KROW e), VT B H NT (VROWS kVCols 2 | NKpad/NT 64 VROWS 4), KTZ B NT
 // (64 KZROW 2), VTZ B NT (VZROWS kVCols 2 rounded up to KiB), CK B NT 16,
 // KM B NT 8, PART KS B H NQpad PREC 4, PM B NQpad NT 8 (e = 2 on the
 // matrix-core path, 4 on the fp32 path; KTZ and VTZ empty on the fp32 path).
 //
+// Matrix-core path, query side:
+//   QL  (per head)   rows [q log2e/sqrt(3D) (D, zero to 16)], bf16
+//   QZ  (shared)     rows [zl (R Cz, zero to ZW)], bf16, the inputs as given
+//   WP  (per head)   [w_pair[h, c % Cz] for c < R Cz, zero to ZW], bf16
+// the fused kernel's query operand is QL and bf16((WP x QZ) x kPairScale).
 // Matrix-core path, one key tile of 64 keys:
 //   KT  (per head)   rows [k (D, zero to 16) | geometric 16 GS | pad 8], bf16 / fp16
 //   KTZ (shared)     rows [zr (R Cz, zero to 16 (NQS - 1)) | pad 8], bf16
@@ -278,6 +298,12 @@ __host__ __device__ __forceinline__ size_t vt_tile_off(const Layout& L, int b, i
 }
 __host__ __device__ __forceinline__ size_t ql_row_off(const Layout& L, int b, int h, int i) {
   return L.off_ql + (((size_t)b * L.H + h) * L.NQpad + i) * (size_t)L.QW * lifted_elem(L);
+}
+__host__ __device__ __forceinline__ size_t qz_row_off(const Layout& L, int b, int i) {
+  return L.off_qz + ((size_t)b * L.NQpad + i) * (size_t)L.ZW * 2;
+}
+__host__ __device__ __forceinline__ size_t wp_row_off(const Layout& L, int h) {
+  return L.off_wp + (size_t)h * L.ZW * 2;
 }
 __host__ __device__ __forceinline__ size_t qa_row_off(const Layout& L, int b, int h, int i) {
   return L.off_qa + (((size_t)b * L.H + h) * L.NQpad + i) * 64;

@@ -23,7 +23,6 @@ struct DiagArgs {
 // fused kernel's wavefronts, which sets the query centroid), all key tiles.
 template <int NQS, int GS>
 __global__ __launch_bounds__(64) void logit_rows_mfma_kernel(DiagArgs a) {
-  constexpr int QW = 16 * NQS;
   const Layout& L = a.L;
   const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
   const int b = a.b, h = a.h, N = L.N, H = L.H, NT = L.NT;
@@ -35,8 +34,7 @@ __global__ __launch_bounds__(64) void logit_rows_mfma_kernel(DiagArgs a) {
   const float gl = reinterpret_cast<const float*>(a.ws + L.off_gam)[h] * kLog2e;
   const float4* ck = reinterpret_cast<const float4*>(a.ws + L.off_ck);
   bf16x8_t bq[NQS];
-  load_q_frag<NQS>(reinterpret_cast<const uint4*>(a.ws + L.off_ql) + (((size_t)b * H + h) * L.NQpad + i) * (QW / 8),
-                   qin, half, bq);
+  load_q_operand<NQS>(L, a.ws, b, h, i, qin, half, bq);
   const bool qvalid = query_valid(L, a.ws, b, i, qin);
   f16x8_t bg[GS];
   QueryGeo qg;

@@ -575,7 +575,7 @@ __global__ __launch_bounds__(W * 64, NBUF == 1 ? 2 : 1) void flash_mfma_kernel(F
 
   // query operand (B of S^T): lane holds query l32, columns half*8 .. +7 of each K-step
   bf16x8_t bq[NQS];
-  load_q_frag<NQS>(reinterpret_cast<const uint4*>(a.ws + ql_row_off(L, b, h, qin ? i : 0)), qin, half, bq);
+  load_q_operand<NQS>(L, a.ws, b, h, i, qin, half, bq);
   const bool qvalid = query_valid(L, a.ws, b, i, qin);
   f16x8_t bg[GS];
   QueryGeo qg;

@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
         vz[x] = val;
       }
     }
-    // lifted query rows: [q sq | 0 | w_pair * zl * sp | 0] for the tile's residues
+    // lifted query rows [q sq | 0] for the tile's residues
     uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + L.off_ql);
     const int qchunks = QW / 8;
     for (int ch = tid; ch < 64 * qchunks; ch += 256) {
@@ -276,16 +276,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
       uint16_t out[8];
       for (int e = 0; e < 8; ++e) {
         const int c = c0 + e;
-        float val = 0.f;
-        if (i < N) {
-          if (c < D) {
-            val = ld<true>(a.q, (((size_t)b * N + i) * H + h) * D + c) * sq;
-          } else if (c >= 16 && c < 16 + RCz) {
-            const int cc = (c - 16) % Cz;
-            val = ld<true>(a.wpair, (size_t)h * Cz + cc) * ld<true>(a.zl, ((size_t)b * N + i) * RCz + (c - 16)) * sp;
-          }
-        }
-        out[e] = f32_to_bf16_bits(val);
+        out[e] = f32_to_bf16_bits(i < N && c < D ? ld<true>(a.q, (((size_t)b * N + i) * H + h) * D + c) * sq : 0.f);
       }
       uint4 pk;
       pk.x = out[0] | ((uint32_t)out[1] << 16);
@@ -293,6 +284,22 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
       pk.z = out[4] | ((uint32_t)out[5] << 16);
       pk.w = out[6] | ((uint32_t)out[7] << 16);
       reinterpret_cast<uint4*>(ql + (((size_t)b * H + h) * L.NQpad + i) * QW + c0)[0] = pk;
+    }
+    // the query pair factors [zl | 0] (shared by the heads: head 0 writes
+    // them) and this head's pair weights [w_pair[h, c % Cz] | 0]
+    const uint16_t* zl16 = reinterpret_cast<const uint16_t*>(a.zl);
+    const uint16_t* wp16 = reinterpret_cast<const uint16_t*>(a.wpair);
+    const int ZW = L.ZW;
+    if (h == 0) {
+      uint16_t* qz = reinterpret_cast<uint16_t*>(a.ws + qz_row_off(L, b, t * 64));
+      for (int x = tid; x < 64 * ZW; x += 256) {
+        const int row = x / ZW, c = x - row * ZW, i = t * 64 + row;
+        if (i < N) qz[(size_t)row * ZW + c] = c < RCz ? zl16[((size_t)b * N + i) * RCz + c] : (uint16_t)0;
+      }
+    }
+    if (b == 0 && t == 0) {
+      uint16_t* wp = reinterpret_cast<uint16_t*>(a.ws + wp_row_off(L, h));
+      for (int c = tid; c < ZW; c += 256) wp[c] = c < RCz ? wp16[(size_t)h * Cz + c % Cz] : (uint16_t)0;
     }
   } else {
     // ---------------- fp32 layouts (row-major per key / query)
@@ -469,7 +476,6 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   __shared__ float s_w[64][P3 % 2 ? P3 : P3 + 1];  // b - c (key points, centred), odd row stride
   __shared__ float s_a[64][P3 % 2 ? P3 : P3 + 1];  // a (query points, global), odd row stride
   __shared__ __attribute__((aligned(16))) float s_xT[32][64];  // x - c of valid keys, coordinate-major
-  __shared__ float s_wp[192];          // w_pair[h, :]
   __shared__ __attribute__((aligned(16))) uint16_t s_vzT[kFastVRows][kFastVPitch];  // transposed rows 2^-8 (fp16)
   __shared__ float s_c[4];
   __shared__ float s_gam;
@@ -484,6 +490,28 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
     for (int k = 0; k < kFastZ; ++k) {
       const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
       zr_r[k] = (x < 64 * nz && r < nrow) ? zrb4[r * nz + c] : make_uint4(0, 0, 0, 0);
+    }
+    // the query pair factors of the tile's residues, [zl | 0] (read by the
+    // fused kernel for every head)
+    {
+      const uint4* zlb4 = reinterpret_cast<const uint4*>(a.zl) + row0 * nz;
+      uint4 zl_r[kFastZ];
+#pragma unroll
+      for (int k = 0; k < kFastZ; ++k) {
+        const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+        zl_r[k] = (x < 64 * nz && r < nrow) ? zlb4[r * nz + c] : make_uint4(0, 0, 0, 0);
+      }
+      uint16_t* qz = reinterpret_cast<uint16_t*>(a.ws + qz_row_off(L, b, t * 64));
+#pragma unroll
+      for (int k = 0; k < kFastZ; ++k) {
+        const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
+        if (x < 64 * nz && r < nrow) *reinterpret_cast<uint4*>(qz + (size_t)r * L.ZW + 8 * c) = zl_r[k];
+      }
+      const int nzq = (L.ZW - RCz) / 8;
+      for (int x = tid; x < nrow * nzq; x += 256) {
+        const int r = x / nzq;
+        *reinterpret_cast<uint4*>(qz + (size_t)r * L.ZW + RCz + 8 * (x - r * nzq)) = make_uint4(0, 0, 0, 0);
+      }
     }
     if (tid < 64) s_valid[tid] = tid < nrow && a.mask[row0 + tid] != 0;
     __syncthreads();
@@ -534,7 +562,6 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   const uint4* kb4 = reinterpret_cast<const uint4*>(a.k) + rh0 * nk;
   const uint4* vb4 = reinterpret_cast<const uint4*>(a.v) + rh0 * nv;
   const uint4* qb4 = reinterpret_cast<const uint4*>(a.q) + rh0 * nk;
-  const uint4* zlb4 = reinterpret_cast<const uint4*>(a.zl) + row0 * nz;
   const uint16_t* kpb = reinterpret_cast<const uint16_t*>(a.kp) + rh0 * (3 * P);
   const uint16_t* qpb = reinterpret_cast<const uint16_t*>(a.qp) + rh0 * (3 * P);
   const uint16_t* vpb = reinterpret_cast<const uint16_t*>(a.vp) + rh0 * (3 * Q);
@@ -553,16 +580,9 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
       for (int e = 0; e < 13; ++e) fr[e] = 0.f;
     }
   }
-  const float wp_raw = tid < Cz ? ld<true>(a.wpair, (size_t)h * Cz + tid) : 0.f;
   const float pwr = ld<true>(a.pwr, h);
   // each loop below covers one tensor, so the lanes of a wavefront never
   // diverge over which tensor a piece comes from
-  uint4 zl_r[kFastZ];
-#pragma unroll
-  for (int k = 0; k < kFastZ; ++k) {
-    const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
-    zl_r[k] = (x < 64 * nz && r < nrow) ? zlb4[r * nz + c] : make_uint4(0, 0, 0, 0);
-  }
   uint4 k_r[kFastK], q_r[kFastK], v_r[kFastK];
 #pragma unroll
   for (int k = 0; k < kFastK; ++k) {
@@ -606,7 +626,6 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   }
 
   // ---- 2. frames, validity and the tile centroid (wavefront 0)
-  if (tid < Cz) s_wp[tid] = wp_raw;
   if (tid < 64) {
     const int valid = fr[12] != 0.f;
     const float tx = fr[0], ty = fr[1], tz = fr[2];
@@ -650,6 +669,12 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   const float gam = s_gam;
   const float gl = gam * kLog2e;
 
+  if (b == 0 && t == 0) {
+    // this head's pair weights [w_pair[h, c % Cz] | 0], bf16 as given
+    uint16_t* wp = reinterpret_cast<uint16_t*>(a.ws + wp_row_off(L, h));
+    for (int c = tid; c < L.ZW; c += 256)
+      wp[c] = c < RCz ? reinterpret_cast<const uint16_t*>(a.wpair)[(size_t)h * Cz + c % Cz] : (uint16_t)0;
+  }
   if (tid == 64) {
     if (b == 0 && t == 0) reinterpret_cast<float*>(a.ws + L.off_gam)[h] = gam;
     if (h == 0) {
@@ -730,25 +755,11 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
         for (int e = 0; e < 8; ++e) s_vzT[8 * cv + e][rv] = vh(e16[e]);
       }
     }
-    // lifted query rows [q sq | 0 | w_pair zl sp | 0]
+    // lifted query rows [q sq | 0] (the pair part of the query operand is
+    // formed by the fused kernel from the shared zl rows and w_pair)
     {
       const float sq = kLog2e / sqrtf(3.0f * (float)D);
-      const float sp = kLog2e / sqrtf(3.0f);
       uint16_t* ql = reinterpret_cast<uint16_t*>(a.ws + ql_row_off(L, b, h, t * 64));
-#pragma unroll
-      for (int k = 0; k < kFastZ; ++k) {
-        const int x = tid + 256 * k, r = fdiv(x, f.nz), c = x - r * nz;
-        if (x < 64 * nz) {
-          const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&zl_r[k]);
-          const float* wp = s_wp + (8 * c) % Cz;
-          uint4 pk;
-          pk.x = pack_bf16x2(wp[0] * bf16_bits_to_f32(e16[0]) * sp, wp[1] * bf16_bits_to_f32(e16[1]) * sp);
-          pk.y = pack_bf16x2(wp[2] * bf16_bits_to_f32(e16[2]) * sp, wp[3] * bf16_bits_to_f32(e16[3]) * sp);
-          pk.z = pack_bf16x2(wp[4] * bf16_bits_to_f32(e16[4]) * sp, wp[5] * bf16_bits_to_f32(e16[5]) * sp);
-          pk.w = pack_bf16x2(wp[6] * bf16_bits_to_f32(e16[6]) * sp, wp[7] * bf16_bits_to_f32(e16[7]) * sp);
-          *reinterpret_cast<uint4*>(ql + (size_t)r * QW + 16 + 8 * c) = pk;
-        }
-      }
 #pragma unroll
       for (int k = 0; k < kFastK; ++k) {
         const int x = tid + 256 * k, r = fdiv(x, f.nk), c = x - r * nk;
@@ -762,13 +773,12 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
           *reinterpret_cast<uint4*>(ql + (size_t)r * QW + 8 * c) = pk;
         }
       }
-      // zero columns [D, 16) and [16 + R Cz, QW)
-      const int nz0 = (16 - D) / 8, nz1 = (QW - 16 - RCz) / 8, nzt = nz0 + nz1;
-      if (nzt > 0)
-        for (int x = tid; x < 64 * nzt; x += 256) {
-          const int r = x / nzt, c = x - r * nzt;
-          const int col = c < nz0 ? D + 8 * c : 16 + RCz + 8 * (c - nz0);
-          *reinterpret_cast<uint4*>(ql + (size_t)r * QW + col) = make_uint4(0, 0, 0, 0);
+      // zero columns [D, 16)
+      const int nz0 = (16 - D) / 8;
+      if (nz0 > 0)
+        for (int x = tid; x < 64 * nz0; x += 256) {
+          const int r = x / nz0, c = x - r * nz0;
+          *reinterpret_cast<uint4*>(ql + (size_t)r * QW + D + 8 * c) = make_uint4(0, 0, 0, 0);
         }
     }
     __syncthreads();

@@ -27,13 +27,37 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 }
 
 // Query operand of S^T = K~ Q~^T (B operand): lane (l32, half) holds columns
-// half*8 .. +7 of every 16-wide K-step of query row `qrow`.
+// half*8 .. +7 of every 16-wide K-step of query row i.  K-step 0 holds the
+// head's scalar columns
+// (QL), K-steps 1 .. NQS-1 the pair columns bf16((w_pair[h] x zl) x
+// kPairScale), formed here from the shared zl rows (QZ) and the head's pair
+// weights (WP), both bf16 as given, in fp32 and rounded to nearest.
 template <int NQS>
-__device__ __forceinline__ void load_q_frag(const uint4* qrow, bool qin, int half, bf16x8_t* bq) {
+__device__ __forceinline__ void load_q_operand(const Layout& L, const char* ws, int b, int h, int i, bool qin,
+                                               int half, bf16x8_t* bq) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const uint4* qrow = reinterpret_cast<const uint4*>(ws + ql_row_off(L, b, h, qin ? i : 0));
+  const uint4* zrow = reinterpret_cast<const uint4*>(ws + qz_row_off(L, b, qin ? i : 0));
+  const uint4* wrow = reinterpret_cast<const uint4*>(ws + wp_row_off(L, h));
+  uint4 z[NQS], wv[NQS];
+  z[0] = qin ? qrow[half] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-  for (int ks = 0; ks < NQS; ++ks) {
-    uint4 v = qin ? qrow[ks * 2 + half] : make_uint4(0, 0, 0, 0);
-    bq[ks] = __builtin_bit_cast(bf16x8_t, v);
+  for (int ks = 1; ks < NQS; ++ks) {
+    z[ks] = qin ? zrow[(ks - 1) * 2 + half] : make_uint4(0, 0, 0, 0);
+    wv[ks] = wrow[(ks - 1) * 2 + half];
+  }
+  bq[0] = __builtin_bit_cast(bf16x8_t, z[0]);
+  auto prod = [](uint32_t w2, uint32_t z2) {
+    const float w0 = __uint_as_float(w2 << 16), w1 = __uint_as_float(w2 & 0xFFFF0000u);
+    const float z0 = __uint_as_float(z2 << 16), z1 = __uint_as_float(z2 & 0xFFFF0000u);
+    const bf16x2_t v = {(__bf16)(w0 * z0 * kPairScale), (__bf16)(w1 * z1 * kPairScale)};
+    return __builtin_bit_cast(uint32_t, v);
+  };
+#pragma unroll
+  for (int ks = 1; ks < NQS; ++ks) {
+    const uint4 p = make_uint4(prod(wv[ks].x, z[ks].x), prod(wv[ks].y, z[ks].y), prod(wv[ks].z, z[ks].z),
+                               prod(wv[ks].w, z[ks].w));
+    bq[ks] = __builtin_bit_cast(bf16x8_t, p);
   }
 }
 

@@ -217,11 +217,12 @@ static void check_layout(const ipa_shape& s, int with_pm, int stacked = 0) {
   CHECK(L.NKpad == NT * 64 && L.NKpad <= L.NQpad, "%s: padded rows", tag);
   // region order and sizes
   const Region reg[] = {
-      {"QL", L.off_ql, L.off_qa},   {"QA", L.off_qa, L.off_kt},       {"KT", L.off_kt, L.off_vt},
+      {"QL", L.off_ql, L.off_qz},   {"QZ", L.off_qz, L.off_wp},       {"WP", L.off_wp, L.off_qa},
+      {"QA", L.off_qa, L.off_kt},   {"KT", L.off_kt, L.off_vt},
       {"VT", L.off_vt, L.off_ktz},  {"KTZ", L.off_ktz, L.off_vtz},    {"VTZ", L.off_vtz, L.off_ck},
       {"CK", L.off_ck, L.off_gam},  {"GAM", L.off_gam, L.off_km},     {"KM", L.off_km, L.off_part},
       {"PART", L.off_part, L.off_pm}, {"PM", L.off_pm, L.total}};
-  enum { rQL, rQA, rKT, rVT, rKTZ, rVTZ, rCK, rGAM, rKM, rPART, rPM };
+  enum { rQL, rQZ, rWP, rQA, rKT, rVT, rKTZ, rVTZ, rCK, rGAM, rKM, rPART, rPM };
   CHECK(L.off_ql >= sizeof(Header), "%s: header", tag);
   for (const Region& r : reg) CHECK(r.start <= r.end && r.start % 256 == 0, "%s: region %s", tag, r.name);
   auto inside = [&](const Region& r, size_t off, size_t bytes, const char* what) {
@@ -229,7 +230,18 @@ static void check_layout(const ipa_shape& s, int with_pm, int stacked = 0) {
           off + bytes, r.name, r.start, r.end);
   };
   // per-region sizes the layout reserves, against the records
-  CHECK(L.off_qa - L.off_ql >= (size_t)B * H * L.NQpad * L.QW * e, "%s: QL size", tag);
+  CHECK(L.off_qz - L.off_ql >= (size_t)B * H * L.NQpad * L.QW * e, "%s: QL size", tag);
+  if (L.mfma) {
+    // the query operand: 16 scalar columns per head row, the pair columns
+    // (NQS - 1 K-steps of 16) in the shared rows and the weights
+    CHECK(L.QW == 16 && L.ZW == 16 * (L.NQS - 1) && L.ZW >= L.RCz && L.ZW % 8 == 0, "%s: query widths", tag);
+    for (int b : {0, B - 1})
+      for (int i : {0, L.N - 1, L.NKpad - 1, L.NQpad - 1})
+        inside(reg[rQZ], qz_row_off(L, b, i), (size_t)L.ZW * 2, "query pair row");
+    for (int h : {0, H - 1}) inside(reg[rWP], wp_row_off(L, h), (size_t)L.ZW * 2, "pair weights");
+  } else {
+    CHECK(L.off_wp == L.off_qz && L.off_qa == L.off_wp, "%s: no shared query rows on the fp32 path", tag);
+  }
   const size_t ktb = kt_tile_bytes(L), vtb = vt_tile_bytes(L);
   for (int b : {0, B - 1})
     for (int h : {0, H - 1}) {
