@@ -77,15 +77,16 @@ def _mfma_dims(shape):
 def lift_bytes(shape, with_pm: bool) -> float:
     """Algorithmic HBM bytes of the lift kernel: every input read once, every
     lifted row written once (per residue: q, k, v, the points, frames, zl, zr,
-    mask; per head key rows, transposed value rows, query rows, query points;
-    once the pair-factor key and value rows the heads share)."""
+    mask; per head key rows, transposed value rows, the 16 scalar query
+    columns, query points; once the pair-factor key and value rows and the
+    query pair-factor row that the heads share)."""
     nqs, nvb, gs = _mfma_dims(shape)
     H, R, Cz = shape.H, shape.R, shape.Cz
     rd = 2 * H * (2 * shape.D + shape.Dv) + 2 * 3 * H * (2 * shape.P + shape.Q) + 2 * 12 + 2 * 2 * R * Cz + 1
     kt = H * (16 + 16 * gs + 8) * 2 + (16 * (nqs - 1) + 8) * 2  # head key rows + shared pair-factor rows
     vz = (32 * (nvb - 1) * 72 * 2 + 1023) // 1024 * 1024
     vt = H * 64 * 72 * 2 / 64 + vz / 64                      # head value rows + shared pair-factor rows
-    wr = kt + vt + H * 16 * nqs * 2 + H * 16 * 4
+    wr = kt + vt + H * 16 * 2 + 16 * (nqs - 1) * 2 + H * 16 * 4
     per_res = rd + wr
     extra = shape.B * shape.N * shape.N if with_pm else 0
     return shape.B * shape.N * per_res + extra
