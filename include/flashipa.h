@@ -232,7 +232,7 @@ ipa_status ipa_epilogue(const ipa_shape* s, void* workspace, size_t workspace_by
  * GPU until the process ends.  The shape must fit in it:
  *   align256(ipa_lifted_bytes(s, pm)) + align256(4 B N H ipa_o_width(s))
  *     + align256(4 B H N) + ipa_epilogue_workspace_bytes(s) <= 128 MiB
- * (B=8, N=256: 22 MiB; B=1, N=2048: 65 MiB, at H=8 and the standard
+ * (B=8, N=256: 18 MiB; B=1, N=2048: 61 MiB, at H=8 and the standard
  * widths), else
  * IPA_ERR_SCRATCH before anything is enqueued.  Results are those of the
  * three calls.  Every call on a GPU shares that GPU's array: calls that
