@@ -170,6 +170,53 @@ __device__ __forceinline__ void pv_tile(const char* vrow, const f16x8_t* pc, f32
   pv_tile_sched<4 * (NVB + 1), 4, 0>();
 }
 
+// Second half of the online softmax and the value product of one tile in
+// one block of instructions: p = 2^s for the first 32-key block (registers
+// 0..15 of s) before a scheduling barrier, then the exponentials, row sum
+// and fp16 conversion of the second block placed between the 2 (NVB + 1)
+// value MFMAs of K-steps 0 and 1 (which need only the first block), then
+// the MFMAs of K-steps 2 and 3.  Returns the fp32 row sum.
+template <int NVB>
+__device__ __forceinline__ float exp_pv_interleaved(const char* vrow, float* s, f16x8_t* ph, f32x16_t* oacc) {
+  constexpr int NB = NVB + 1;
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    s[x] = __builtin_amdgcn_exp2f(s[x]);
+    ps[x & 3] += s[x];
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ph[ks][e] = (_Float16)s[ks * 8 + e];
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  // the second block's softmax (independent of K-steps 0 and 1), then the
+  // value product; the scheduling groups below interleave the two
+#pragma unroll
+  for (int x = 16; x < 32; ++x) {
+    s[x] = __builtin_amdgcn_exp2f(s[x]);
+    ps[x & 3] += s[x];
+  }
+#pragma unroll
+  for (int ks = 2; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ph[ks][e] = (_Float16)s[16 + (ks - 2) * 8 + e];
+  pv_tile_ops<NVB, 4>(vrow, ph, oacc);
+  // order: the first DEPTH fragment reads, then per MFMA of K-steps 0 and 1
+  // its read DEPTH ahead and two or three vector instructions of the second
+  // block's softmax, then the remaining MFMAs with their reads
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int st = 0; st < 4 * NB; ++st) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (st + 4 < 4 * NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (st < 2 * NB) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+
 // First half of the online softmax of one tile for the 32 queries of a
 // wavefront.  S arrives relative to the running maximum m of each query (m
 // rides in the row term of the last geometric K-step); keys that are masked
@@ -467,12 +514,22 @@ __device__ __forceinline__ int attend_tile(const FlashMfmaArgs& a, const TileSrc
 
   float s32[32];
   const float alpha = softmax_max<PM>(sacc, mw, m, init, s32);
-  f16x8_t ph[4];
-  const float ps = exp_tile(s32, ph);
   if (__any(alpha != 1.0f)) {
 #pragma unroll
     for (int vb = 0; vb <= NVB; ++vb) oacc[vb] *= alpha;
   }
+  f16x8_t ph[4];
+  if constexpr (W == 4) {
+    // one wavefront per SIMD (the widest rows): no second wavefront hides
+    // the softmax behind its matrix work, so the exponentials of the second
+    // 32-key block are issued between the value-product MFMAs of the first
+    // (K-steps 0 and 1 use only the first block's probabilities)
+    const float ps = exp_pv_interleaved<NVB>(kt + T::KH + T::KZ + (size_t)(l32 * kVCols) * 2 + half * 16, s32, ph,
+                                             oacc);
+    l = l * alpha + ps;
+    return tn;
+  }
+  const float ps = exp_tile(s32, ph);
   l = l * alpha + ps;
 
   __builtin_amdgcn_s_setprio(1);
