@@ -55,13 +55,17 @@ def _stacked_logit_bound(inp):
     return rel * gam[None, :, None, None] * (cross + na + nb)
 
 
-def test_stacked_layout_matches_oracle_within_its_rounding():
+@pytest.mark.parametrize("shape,lengths", [
+    (IPAShape(B=2, N=300, H=8, dtype="bf16"), (200, 300)),   # one tile buffer, keys not split
+    (IPAShape(B=1, N=1024, H=2, dtype="bf16"), None),        # keys split over workgroups, merged after
+], ids=["batch", "split"])
+def test_stacked_layout_matches_oracle_within_its_rounding(shape, lengths):
     """Coordinates within a few angstrom of the origin: the stacked path's
     own rounding is small, and its lse and outputs must follow the oracle
     within the bound that rounding allows."""
-    s = IPAShape(B=2, N=300, H=8, dtype="bf16")
-    inp = make_inputs(s, 4242, frames="gauss", trans_sigma=0.5, lengths=(200, 300), masked_keys=(7,),
-                      pair_dropout=0.05)
+    s = shape
+    inp = make_inputs(s, 4242, frames="gauss", trans_sigma=0.5, lengths=lengths, masked_keys=(7,),
+                      pair_dropout=0.05, empty_row=True)
     say(f"case stacked small coordinates {s}")
     got = _run_stacked(inp)
     ref = ipa_factored(inp, keep=("update", "local_points", "lse", "empty", "o_scalar", "g"))
