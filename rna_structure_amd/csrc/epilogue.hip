@@ -629,25 +629,37 @@ __global__ __launch_bounds__(256) void epilogue_f32_kernel(EpiArgs a) {
   const int Cout = L.Cout;
   const float* wo = reinterpret_cast<const float*>(a.w_out);
   const float* bo = reinterpret_cast<const float*>(a.b_out);
-  const int r = tid % kEpiRowsF32, cg = tid / kEpiRowsF32;
-  const int row = row0 + r;
-  if (row >= total) return;
-  for (int col = cg; col < Cout; col += 256 / kEpiRowsF32) {
-    // 16 features a step, their w_out loads issued together (one memory
-    // round trip per step instead of one per feature), four partial sums
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* fr = ffeat + (size_t)r * FP;
+  // thread = (column, half of the 16 rows): consecutive threads on
+  // consecutive columns, so the w_out loads of a feature are one coalesced
+  // row piece and independent of each other from feature to feature; each
+  // thread accumulates its 8 rows from LDS broadcasts of the features
+  constexpr int RH = kEpiRowsF32 / 2;
+  for (int cb = 0; cb < Cout; cb += 128) {
+    const int col = cb + (tid & 127), r0 = (tid >> 7) * RH;
+    if (col >= Cout) continue;
+    float acc[RH];
+#pragma unroll
+    for (int q = 0; q < RH; ++q) acc[q] = 0.f;
     int f = 0;
-    for (; f + 16 <= F; f += 16) {
-      float w[16];
+    for (; f + 8 <= F; f += 8) {
+      float w[8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) w[e] = wo[(size_t)(f + e) * Cout + col];
+      for (int e = 0; e < 8; ++e) w[e] = wo[(size_t)(f + e) * Cout + col];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e & 3] = fmaf(fr[f + e], w[e], acc[e & 3]);
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int q = 0; q < RH; ++q) acc[q] = fmaf(ffeat[(size_t)(r0 + q) * FP + f + e], w[e], acc[q]);
     }
-    for (; f < F; ++f) acc[0] = fmaf(fr[f], wo[(size_t)f * Cout + col], acc[0]);
-    const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    a.update[(size_t)row * Cout + col] = s_empty[r] ? 0.f : sum + bo[col];
+    for (; f < F; ++f) {
+      const float w = wo[(size_t)f * Cout + col];
+#pragma unroll
+      for (int q = 0; q < RH; ++q) acc[q] = fmaf(ffeat[(size_t)(r0 + q) * FP + f], w, acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < RH; ++q) {
+      const int row = row0 + r0 + q;
+      if (row < total) a.update[(size_t)row * Cout + col] = s_empty[r0 + q] ? 0.f : acc[q] + bo[col];
+    }
   }
 }
 

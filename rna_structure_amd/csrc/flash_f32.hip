@@ -119,16 +119,18 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
       // branch-free column loops (the LDS reads then go out together):
       // columns past DQ read column 0 against a zero query column, point
       // coordinates past 3P give a zero difference
-      float s = 0.f;
+      // four and three independent partial sums (short dependency chains)
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int d = 0; d < MDQ; ++d) s = fmaf(qv[d], kr[d < DQ ? d : 0], s);
-      float dist = 0.f;
+      for (int d = 0; d < MDQ; ++d) s4[d & 3] = fmaf(qv[d], kr[d < DQ ? d : 0], s4[d & 3]);
+      float d3[3] = {0.f, 0.f, 0.f};
 #pragma unroll
       for (int g = 0; g < 15; ++g) {
         const float df = g < P3 ? dA[g] - kr[DQ + (g < P3 ? g : 0)] : 0.f;
-        dist = fmaf(df, df, dist);
+        d3[g % 3] = fmaf(df, df, d3[g % 3]);
       }
-      s = fmaf(-gl, dist, s);
+      float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      s = fmaf(-gl, (d3[0] + d3[1]) + d3[2], s);
       if (s > m) {
         const float alpha = exp2f(m - s);  // m = -inf -> 0
         l *= alpha;
