@@ -12,7 +12,10 @@
 // style); value points are aggregated relative to the tile centroid and the
 // centroid term sum_j p_j c_t is carried separately.
 //
-// Grid (ceil(N/64), H, B), 256 threads: 64 queries x 4 column groups.
+// Grid (ceil(N/64), H, B), 256 threads: 64 queries x 4 column groups; per
+// step of 32 keys the four threads of a query form 8 logits each and share
+// them through LDS, then each runs the softmax over all 32 and accumulates
+// its own output columns.
 #include "common.h"
 
 namespace fipa {
@@ -43,6 +46,7 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
   extern __shared__ float smem[];
   float* sk = smem;                       // [32][KROW]
   float* sv = smem + kF32Keys * KROW;     // [32][DVP]
+  float* slog = sv + kF32Keys * DVP;      // [64][33] logits of the step's keys
 
   const Header* hd = reinterpret_cast<const Header*>(a.ws);
   const bool has_pm = hd->has_pair_mask != 0;
@@ -109,28 +113,39 @@ __global__ __launch_bounds__(256) void flash_f32_kernel(FlashF32Args a) {
     for (int x = tid; x < kF32Keys * DVP / 4; x += 256)
       reinterpret_cast<float4*>(sv)[x] = reinterpret_cast<const float4*>(vt)[x];
     __syncthreads();
-    for (int jl = 0; jl < kF32Keys; ++jl) {
+    // logits of the step's 32 keys for this thread's query, 8 keys per
+    // column group (keys part, part + 4, ...), shared through LDS; -inf for
+    // a key that is not permitted
+    for (int jl = part; jl < kF32Keys; jl += 4) {
       const int jj = (st & 1) * kF32Keys + jl;
       int hf;
       const int bit = mask_bit_of_key(jj, &hf);
       const bool perm = (((hf ? w1 : w0) >> bit) & 1u) != 0;
-      if (!perm) continue;
-      const float* kr = sk + jl * KROW;
-      // branch-free column loops (the LDS reads then go out together):
-      // columns past DQ read column 0 against a zero query column, point
-      // coordinates past 3P give a zero difference
-      // four and three independent partial sums (short dependency chains)
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      float s = -INFINITY;
+      if (perm) {
+        const float* kr = sk + jl * KROW;
+        // branch-free column loops (the LDS reads then go out together):
+        // columns past DQ read column 0 against a zero query column, point
+        // coordinates past 3P give a zero difference; four and three
+        // independent partial sums
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int d = 0; d < MDQ; ++d) s4[d & 3] = fmaf(qv[d], kr[d < DQ ? d : 0], s4[d & 3]);
-      float d3[3] = {0.f, 0.f, 0.f};
+        for (int d = 0; d < MDQ; ++d) s4[d & 3] = fmaf(qv[d], kr[d < DQ ? d : 0], s4[d & 3]);
+        float d3[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < 15; ++g) {
-        const float df = g < P3 ? dA[g] - kr[DQ + (g < P3 ? g : 0)] : 0.f;
-        d3[g % 3] = fmaf(df, df, d3[g % 3]);
+        for (int g = 0; g < 15; ++g) {
+          const float df = g < P3 ? dA[g] - kr[DQ + (g < P3 ? g : 0)] : 0.f;
+          d3[g % 3] = fmaf(df, df, d3[g % 3]);
+        }
+        s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        s = fmaf(-gl, (d3[0] + d3[1]) + d3[2], s);
       }
-      float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      s = fmaf(-gl, (d3[0] + d3[1]) + d3[2], s);
+      slog[qi * (kF32Keys + 1) + jl] = s;
+    }
+    __syncthreads();
+    for (int jl = 0; jl < kF32Keys; ++jl) {
+      const float s = slog[qi * (kF32Keys + 1) + jl];
+      if (s == -INFINITY) continue;  // not permitted
       if (s > m) {
         const float alpha = exp2f(m - s);  // m = -inf -> 0
         l *= alpha;
@@ -175,7 +190,7 @@ hipError_t launch_flash_f32(const Layout& L, const void* ws, float* o, float* ls
   a.ws = reinterpret_cast<const char*>(ws);
   a.o = o;
   a.lse = lse;
-  const size_t shm = (size_t)kF32Keys * (L.KROW + L.VROWS) * sizeof(float);
+  const size_t shm = ((size_t)kF32Keys * (L.KROW + L.VROWS) + 64 * (kF32Keys + 1)) * sizeof(float);
   dim3 grid((L.N + 63) / 64, L.H, L.B);
   if (L.D + L.RCz <= 64 && L.DO <= 96)
     hipLaunchKernelGGL((flash_f32_kernel<64, 96>), grid, dim3(256), shm, st, a);
