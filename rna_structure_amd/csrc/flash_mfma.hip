@@ -294,9 +294,11 @@ __device__ __forceinline__ void zero_rows(const FlashMfmaArgs& a, int b, int h, 
 // Final normalisation (or, with several key ranges, the partial result) of
 // one block of 32 queries i - l32 .. i - l32 + 31 after its last key tile:
 // log-sum-exp, O divided by the ones-row sums, the centroid added back to the
-// value points, written through an LDS slot of the (then free) tile buffers.
-// `w` names the slot (0 .. W-1).  Every wavefront of the workgroup calls it
-// the same number of times (it contains a barrier).
+// value points.  Widths that are multiples of 4 are written straight from
+// the accumulator registers; others through an LDS slot of the (then free)
+// tile buffers, `w` naming the slot (0 .. W-1).  Every wavefront of the
+// workgroup calls it the same number of times (the staged path contains a
+// barrier; which path runs depends only on the shape).
 // Value blocks: 0 = [v 2^-8 (Dv) | 1 | 0], 1 = [x - c_t (3Q) | 1 | c_t | 0],
 // 2 .. NVB = pair factors 2^-8 (R Cz rows).  The output row is
 // [v (Dv) | pair (R Cz) | points (3Q)], i.e. the blocks in the order

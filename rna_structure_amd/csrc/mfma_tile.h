@@ -28,10 +28,10 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 
 // Query operand of S^T = K~ Q~^T (B operand): lane (l32, half) holds columns
 // half*8 .. +7 of every 16-wide K-step of query row i.  K-step 0 holds the
-// head's scalar columns
-// (QL), K-steps 1 .. NQS-1 the pair columns bf16((w_pair[h] x zl) x
-// kPairScale), formed here from the shared zl rows (QZ) and the head's pair
-// weights (WP), both bf16 as given, in fp32 and rounded to nearest.
+// head's scalar columns (QL), K-steps 1 .. NQS-1 the pair columns
+// bf16((w_pair[h] x zl) x kPairScale), formed here from the shared zl rows
+// (QZ) and the head's pair weights (WP), both bf16 as given, in fp32 and
+// rounded to nearest.
 template <int NQS>
 __device__ __forceinline__ void load_q_operand(const Layout& L, const char* ws, int b, int h, int i, bool qin,
                                                int half, bf16x8_t* bq) {
