@@ -214,6 +214,36 @@ def test_deterministic():
         assert np.array_equal(g1[k], g2[k]), k
 
 
+@pytest.mark.parametrize("shape", [IPAShape(B=2, N=300, H=8), IPAShape(B=1, N=1024, H=2), IPAShape(B=1, N=100, H=2, dtype="f32")],
+                         ids=["one-buffer", "split-keys", "f32"])
+def test_repeated_calls_on_one_lift(shape):
+    """ipa_flash_fwd and ipa_epilogue are functions of the lifted buffer and
+    the inputs: called again on the same lift (outputs poisoned in between)
+    they give the same bits, also where the keys are split over workgroups
+    and merged."""
+    import torch
+    from rna_structure_amd import _lib
+    inp = make_inputs(shape, 77, frames="walk", step=3.8, pair_dropout=0.05)
+    say(f"case repeated calls {shape}")
+    t = _lib.device_inputs(inp, "cuda")
+    f = _lib.FlashIPA(shape, eps=inp["eps"], with_pair_mask=True)
+    f.poison()
+    f.lift(t)
+    outs = []
+    for _ in range(3):
+        for buf in (f.o, f.lse, f.update, f.local_points):
+            buf.fill_(float("nan"))
+        f.attend()
+        f.epilogue(t)
+        torch.cuda.synchronize()
+        outs.append({k: v.detach().cpu().numpy().copy() for k, v in
+                     dict(o=f.o, lse=f.lse, update=f.update, local_points=f.local_points).items()})
+    for k in outs[0]:
+        assert not np.any(np.isnan(outs[0][k])), k
+        for o in outs[1:]:
+            assert np.array_equal(outs[0][k], o[k]), k
+
+
 def test_rigid_invariance_gpu_f32():
     s = IPAShape(B=1, N=150, H=4, dtype="f32")
     inp = make_inputs(s, 41, frames="walk", step=3.8)
