@@ -16,18 +16,56 @@ def say(msg: str):
     sys.stdout.flush()
 
 
+GUARD = 16384        # bytes of sentinel before and after every buffer of a forward
+GUARD_BYTE = 0xA5
+BUFFERS = ("lifted", "epi_ws", "o", "lse", "update", "local_points")
+
+
+def add_guards(f, names=BUFFERS):
+    """Move the named buffers of `f` into allocations GUARD bytes larger on
+    each side, the extra bytes holding GUARD_BYTE; `check_guards` then finds
+    any write past either end of a buffer."""
+    if not hasattr(f, "_guards"):
+        f._guards = []
+    for name in names:
+        inner, raw, nb = guarded_like(getattr(f, name))
+        setattr(f, name, inner)
+        f._guards.append((name, raw, nb))
+    return f
+
+
+def guarded_like(buf):
+    """A tensor shaped like `buf` inside an allocation with GUARD sentinel
+    bytes on each side: (tensor, whole allocation, bytes of the tensor)."""
+    import torch
+    nb = buf.numel() * buf.element_size()
+    raw = torch.full((nb + 2 * GUARD,), GUARD_BYTE, dtype=torch.uint8, device=buf.device)
+    return raw[GUARD:GUARD + nb].view(buf.dtype).view(buf.shape), raw, nb
+
+
+def check_guards(f):
+    for name, raw, nb in f._guards:
+        before = int((raw[:GUARD] != GUARD_BYTE).sum())
+        after = int((raw[GUARD + nb:] != GUARD_BYTE).sum())
+        assert before == 0 and after == 0, \
+            f"{name}: {before} sentinel bytes before and {after} after the buffer overwritten"
+
+
 def run_gpu(inp: dict, eps=None):
     """One forward on fresh buffers that are poisoned first (workspace bytes
     0xFF, outputs NaN), so a region the kernels skip, or read unwritten,
-    cannot pass on values left behind by an earlier call."""
+    cannot pass on values left behind by an earlier call; every buffer sits
+    between two guard bands of sentinel bytes, checked after the forward."""
     import torch
     from rna_structure_amd import _lib
     shape = inp["shape"]
     t = _lib.device_inputs(inp, "cuda")
     f = _lib.FlashIPA(shape, eps=inp["eps"] if eps is None else eps, with_pair_mask=t["pair_mask"] is not None)
+    add_guards(f)
     f.poison()
     out = f.forward(t)
     torch.cuda.synchronize()
+    check_guards(f)
     return f, t, {k: v.detach().cpu().numpy().astype(np.float64) for k, v in out.items()}
 
 

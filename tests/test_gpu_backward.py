@@ -12,7 +12,7 @@ import pytest
 from oracle.ipa_backward import GRAD_KEYS, ipa_gradients
 from rna_structure_amd.synth import IPAShape, make_inputs
 
-from gpu_helpers import say
+from gpu_helpers import add_guards, check_guards, guarded_like, say
 
 pytestmark = pytest.mark.gpu
 
@@ -28,13 +28,19 @@ def _run(inp, du, dl):
     from rna_structure_amd import _lib
     shape = inp["shape"]
     t = _lib.device_inputs(inp, "cuda")
-    bw = _lib.IPABackward(shape, eps=inp["eps"])
+    bw = add_guards(_lib.IPABackward(shape, eps=inp["eps"]), ("ws",))
     # NaN in the workspace and in every gradient buffer: a region the
-    # kernels fail to write shows up in the comparison
+    # kernels fail to write shows up in the comparison; guard bands of
+    # sentinel bytes around each show a write past its ends
     bw.ws.fill_(255)
-    bw.grads = {n: torch.full_like(t[n], float("nan"), dtype=torch.float32) for n in GRAD_KEYS}
+    bw.grads = {}
+    for n in GRAD_KEYS:
+        g_n, raw, nb = guarded_like(torch.empty_like(t[n], dtype=torch.float32))
+        bw.grads[n] = g_n.fill_(float("nan"))
+        bw._guards.append((n, raw, nb))
     g = bw(t, torch.from_numpy(du).cuda(), torch.from_numpy(dl).cuda())
     torch.cuda.synchronize()
+    check_guards(bw)
     return {key: v.cpu().numpy().astype(np.float64) for key, v in g.items()}
 
 

@@ -17,7 +17,7 @@ import pytest
 from oracle import flashbias_attention, flashbias_rows
 from rna_structure_amd.synth import make_bias_inputs
 
-from gpu_helpers import max_abs_rel, say
+from gpu_helpers import add_guards, check_guards, max_abs_rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -35,11 +35,13 @@ def _run(inp, scale, causal, f=None):
     if f is None:
         f = _lib.BiasAttention(d["B"], d["N"], d["M"], d["H"], d["D"], d["Dv"], d["R"], scale, causal,
                                d["dtype"], d["phi_dtype"])
+        add_guards(f, ("workspace", "o", "lse"))
     # every byte of the workspace that the kernels read must have been written
     # by this call: start from all-ones bytes (NaN as bf16 or fp32)
     f.workspace.fill_(255)
     out = f(q, k, v, pq, pk, km)
     torch.cuda.synchronize()
+    check_guards(f)
     return f, {n: t.cpu().numpy().astype(np.float64) for n, t in out.items()}
 
 

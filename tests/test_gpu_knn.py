@@ -8,7 +8,7 @@ import pytest
 from oracle import knn_distogram
 from rna_structure_amd.synth import make_positions
 
-from gpu_helpers import say
+from gpu_helpers import add_guards, check_guards, say
 
 pytestmark = pytest.mark.gpu
 
@@ -20,12 +20,14 @@ def _run(pos, k, nbins, dmax, dgram_dtype="f32", with_mask=True, prefill=True):
     t = torch.from_numpy(np.ascontiguousarray(pos["translation"])).cuda()
     m = torch.from_numpy(pos["mask"].astype(np.uint8)).cuda() if with_mask else None
     kd = _lib.KnnDistogram(B, N, k, nbins, dmax, dgram_dtype=dgram_dtype)
+    add_guards(kd, [n for n in ("nn_index", "nn_dist", "dgram") if getattr(kd, n) is not None])
     if prefill:   # every element must be written by the call
         kd.nn_index.fill_(12345)
         kd.nn_dist.fill_(-7.0)
         kd.dgram.fill_(3.0)
     out = kd(t, m)
     torch.cuda.synchronize()
+    check_guards(kd)
     return {key: v.float().cpu().numpy() if key == "dgram" else v.cpu().numpy() for key, v in out.items()}
 
 

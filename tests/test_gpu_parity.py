@@ -10,7 +10,7 @@ import pytest
 from oracle import ipa_factored
 from rna_structure_amd.synth import IPAShape, make_config, make_inputs
 
-from gpu_helpers import compare, run_gpu, say
+from gpu_helpers import add_guards, check_guards, compare, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -226,7 +226,7 @@ def test_repeated_calls_on_one_lift(shape):
     inp = make_inputs(shape, 77, frames="walk", step=3.8, pair_dropout=0.05)
     say(f"case repeated calls {shape}")
     t = _lib.device_inputs(inp, "cuda")
-    f = _lib.FlashIPA(shape, eps=inp["eps"], with_pair_mask=True)
+    f = add_guards(_lib.FlashIPA(shape, eps=inp["eps"], with_pair_mask=True))
     f.poison()
     f.lift(t)
     outs = []
@@ -242,6 +242,7 @@ def test_repeated_calls_on_one_lift(shape):
         assert not np.any(np.isnan(outs[0][k])), k
         for o in outs[1:]:
             assert np.array_equal(outs[0][k], o[k]), k
+    check_guards(f)
 
 
 def test_rigid_invariance_gpu_f32():

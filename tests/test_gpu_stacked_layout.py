@@ -20,7 +20,7 @@ from oracle import ipa_factored, point_weight, to_global
 from rna_structure_amd import _lib
 from rna_structure_amd.synth import IPAShape, make_inputs
 
-from gpu_helpers import compare, run_gpu, say, split_o
+from gpu_helpers import add_guards, check_guards, compare, run_gpu, say, split_o
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +29,11 @@ def _run_stacked(inp):
     shape = inp["shape"]
     t = _lib.device_inputs(inp, "cuda")
     f = _lib.FlashIPA(shape, eps=inp["eps"], with_pair_mask=t["pair_mask"] is not None, stacked=True)
+    add_guards(f)
     f.poison()
     out = f.forward(t)
     torch.cuda.synchronize()
+    check_guards(f)
     return {k: v.detach().cpu().numpy().astype(np.float64) for k, v in out.items()}
 
 

@@ -5,13 +5,15 @@ row, the second with a smaller input, so that whatever the first call left in
 the shared array cannot pass for the second's results.  The same kernels run
 in the same launch configurations, so the outputs are compared bit for bit
 (and against the oracle within the bf16 bar)."""
+import types
+
 import numpy as np
 import pytest
 
 from oracle import ipa_factored
 from rna_structure_amd.synth import IPAShape, make_inputs
 
-from gpu_helpers import max_abs_rel, run_gpu, say
+from gpu_helpers import add_guards, check_guards, max_abs_rel, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -22,10 +24,17 @@ def _noalloc(inp):
     shape = inp["shape"]
     t = _lib.device_inputs(inp, "cuda")
     s = _lib.make_shape(shape, inp["eps"])
-    update = torch.full((shape.B, shape.N, shape.Cout), float("nan"), dtype=torch.float32, device="cuda")
-    local = torch.full((shape.B, shape.N, shape.H, shape.Q, 3), float("nan"), dtype=torch.float32, device="cuda")
+    # outputs NaN-poisoned between guard bands of sentinel bytes
+    bufs = types.SimpleNamespace(
+        update=torch.full((shape.B, shape.N, shape.Cout), float("nan"), dtype=torch.float32, device="cuda"),
+        local=torch.full((shape.B, shape.N, shape.H, shape.Q, 3), float("nan"), dtype=torch.float32, device="cuda"))
+    add_guards(bufs, ("update", "local"))
+    bufs.update.fill_(float("nan"))
+    bufs.local.fill_(float("nan"))
+    update, local = bufs.update, bufs.local
     _lib.ipa_forward_noalloc(s, t, update, local)
     torch.cuda.synchronize()
+    check_guards(bufs)
     return update.cpu().numpy().astype(np.float64), local.cpu().numpy().astype(np.float64)
 
 
