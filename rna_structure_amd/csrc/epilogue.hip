@@ -30,6 +30,10 @@ struct EpiArgs {
   int FP;  // LDS row pitch of the features (elements)
 };
 
+// A residue's neighbourhood is empty when no key is permitted to it (key
+// mask, pair mask).  The attention kernels decide that from the mask bits
+// alone, the same for every head, and then give lse = -inf, so head 0's
+// log-sum-exp tells it for the residue.
 __device__ __forceinline__ bool row_empty(const EpiArgs& a, int row) {
   const Layout& L = a.L;
   const int b = row / L.N, i = row % L.N;
