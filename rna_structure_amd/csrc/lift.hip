@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256) void lift_kernel(LiftArgs a) {
 // lanes walk down a column.  Units (b, t, u) are handed out so that the H + 1
 // units of one key tile run back to back on one XCD and share its L2 for zl
 // and the frames.
-constexpr int kFastVRows = 96;       // transposed rows per pass: Dv <= 24 (head unit), R Cz in passes of 96 (pair unit)
+constexpr int kFastVRows = 64;       // transposed rows per pass: Dv <= 24 (head unit), R Cz in passes of 64 (pair unit)
 constexpr int kFastVPitch = 66;      // 16-bit elements per transposed LDS row (33 words)
 constexpr int kFastZ = 6;            // 16-byte pieces of a zr / zl tile per thread: 64 R Cz/8 <= 1536
 constexpr int kFastK = 1;            // pieces of a k / v / q tile per thread: 64 D/8 <= 256 (D <= 16, Dv <= 24)
@@ -454,7 +454,7 @@ __device__ __forceinline__ void store_vt_rows(uint16_t* vt, const uint16_t (*src
 }
 
 template <int P, bool STK = false>
-__global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastArgs f) {
+__global__ __launch_bounds__(256, 6) void lift_fast_kernel(LiftArgs a, LiftFastArgs f) {
   constexpr int P3 = 3 * P;
   constexpr int GS = STK ? 2 : (P <= 4 ? 3 : 4);
   const Layout& L = a.L;
@@ -656,6 +656,7 @@ __global__ __launch_bounds__(256, 4) void lift_fast_kernel(LiftArgs a, LiftFastA
   }
   // raw point rows in LDS (the transposition array is free until the points
   // are done): row r at s_praw + kPrPitch r, as bf16 [kp | qp | vp]
+  static_assert(64 * kPrPitch * sizeof(uint2) <= sizeof(s_vzT), "staged point rows overflow the transposition array");
   uint2* s_praw = reinterpret_cast<uint2*>(&s_vzT[0][0]);
   if (P == 4 && f.pts_vec) {
 #pragma unroll
